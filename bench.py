@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 MoE hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+routing align (topk_ids -> sorted_ids / expert_ids / num_tokens_padded), the
+gate/up W4A16 GEMM (per routed slot), and the down W4A16 GEMM with the
+top-k-weighted combine.  Inputs and packed weights are resident in HBM before
+the timed region.  Default workload: the EP8 decode share of a Kimi K2.x MoE
+layer (48 of 384 experts, top-8, 576 tokens, hidden 7168, intermediate 2048).
+
+Prints one JSON line (rank 0).  `value` is the step's weight+scale bytes
+(experts touched by the batch, both projections) over the step time, in GB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def weight_bytes(n_touched: int, N: int, K: int) -> int:
+    """Packed INT4 weights (K/2 bytes per row) + bf16 group-32 scales."""
+    return n_touched * (N * K // 2 + N * (K // 32) * 2)
+
+
+def cpu_baseline(sh, ids, wts, x, a, c1, s1, c2, s2, n_experts: int) -> dict:
+    """The oracle's fp32 path (dequantise, sgemm, combine), untuned, on the
+    first `n_experts` local experts and all rows routed to them."""
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    S = n_experts
+    t0 = time.perf_counter()
+    O.indexed_gate_up_fp32(x, c1[:S], s1[:S], ids, sh.first, S)
+    O.indexed_down_combine_fp32(a, c2[:S], s2[:S], ids, wts, sh.first, S)
+    dt = time.perf_counter() - t0
+    flat = ids.reshape(-1)
+    rows = int(((flat >= sh.first) & (flat < sh.first + S)).sum())
+    b = weight_bytes(S, sh.N1, sh.K1) + weight_bytes(S, sh.N2, sh.K2)
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"gate/up + down+combine for local experts 0..{S - 1} of {sh.E_loc} "
+                      f"({rows} routed rows), same inputs as the GPU step; GB/s of weight+scale bytes"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ep8_decode")
+    ap.add_argument("--block-m", type=int, default=0, help="override the selector's block_m")
+    ap.add_argument("--nr", type=int, default=0, help="override the selector's weight tiles per wave")
+    ap.add_argument("--cpu-experts", type=int, default=4, help="experts in the CPU-baseline sample (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(collectives and sharding are out of scope); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import w4a16_int4_mixture_moe_amd as M
+    from synth import workloads as W
+
+    sh = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    t_gen = time.perf_counter()
+    ids, wts = W.routing_for(sh)
+    x = W.activations(sh.seed, "x", sh.T, sh.K1)
+    a = W.activations(sh.seed, "a", sh.T * sh.topk, sh.K2)
+    c1 = W.weight_codes(sh.seed, "w1_codes", sh.E_loc, sh.N1, sh.K1)
+    s1 = W.weight_scales(sh.seed, "w1_scales", sh.E_loc, sh.N1, sh.K1)
+    c2 = W.weight_codes(sh.seed, "w2_codes", sh.E_loc, sh.N2, sh.K2)
+    s2 = W.weight_scales(sh.seed, "w2_scales", sh.E_loc, sh.N2, sh.K2)
+    log(f"inputs generated in {time.perf_counter() - t_gen:.1f}s")
+
+    def bf(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    p1 = M.pack_w4(torch.from_numpy(c1).to(dev), bf(s1))
+    p2 = M.pack_w4(torch.from_numpy(c2).to(dev), bf(s2))
+    d_ids = torch.from_numpy(ids).to(dev)
+    d_w = torch.from_numpy(wts).to(dev)
+    d_x, d_a = bf(x), bf(a)
+    cfg = M.select(sh.T, sh.topk, sh.E_glob, sh.E_loc, sh.N1, sh.K1)
+    if args.block_m:
+        cfg.block_m = args.block_m
+    if args.nr:
+        cfg.nr = args.nr
+    T, k = sh.T, sh.topk
+    cap = M.align_capacity(T, k, sh.E_loc, cfg.block_m)
+    sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+    expert_ids = torch.empty(cap // cfg.block_m, dtype=torch.int32, device=dev)
+    ntp = torch.empty(1, dtype=torch.int32, device=dev)
+    routing = M.Routing(sorted_ids, expert_ids, ntp, cfg.block_m, d_ids, sh.E_glob, sh.first, sh.E_loc)
+    h = torch.empty(T * k, sh.N1, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(T, sh.N2, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(M.workspace_bytes(T, k, sh.N2, True), dtype=torch.uint8, device=dev)
+    L = M.load()
+    stream = torch.cuda.current_stream(dev)
+    import ctypes
+    s_ptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def align():
+        M._lib.check(L.w4a16_moe_align(d_ids.data_ptr(), T, k, sh.E_glob, sh.first, sh.E_loc,
+                                       cfg.block_m, sorted_ids.data_ptr(), expert_ids.data_ptr(),
+                                       ntp.data_ptr(), cap, 0, s_ptr))
+
+    def gate_up():
+        M.moe_w4a16_gemm(d_x, p1, routing, cfg=cfg, out=h)
+
+    def down():
+        M.moe_w4a16_gemm(d_a, p2, routing, topk_weights=d_w, cfg=cfg, out=y, workspace=ws)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        align()
+        if ev is not None:
+            ev[1].record(stream)
+        gate_up()
+        if ev is not None:
+            ev[2].record(stream)
+        down()
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    us_align = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    us_gu = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+    us_dn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3
+
+    flat = ids.reshape(-1)
+    local = (flat >= sh.first) & (flat < sh.first + sh.E_loc)
+    n_local = int(local.sum())
+    touched = int(len(np.unique(flat[local])))
+    tokens_with_local = int(local.reshape(T, k).any(1).sum())
+    wb1 = weight_bytes(touched, sh.N1, sh.K1)
+    wb2 = weight_bytes(touched, sh.N2, sh.K2)
+    n_ntp = int(ntp.item())
+    # algorithmic bytes per gate/up launch: weights+scales of touched experts,
+    # one activation row read and one output row written per routed slot,
+    # the routing indices
+    alg1 = wb1 + n_local * sh.K1 * 2 + n_local * sh.N1 * 2 + n_ntp * 4 + (n_ntp // cfg.block_m) * 4
+    value = (wb1 + wb2) / (ms_step * 1e-3) / 1e9
+    gu_gbs = alg1 / (us_gu * 1e-6) / 1e9
+    flops1 = 2.0 * n_local * sh.N1 * sh.K1
+    flops2 = 2.0 * n_local * sh.N2 * sh.K2
+    out = {
+        "metric": "weight-HBM GB/s of one MoE layer step (align + gate/up + down+combine), "
+                  "with us/call per W4A16 GEMM",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": sh.name, "T": T, "topk": k, "E_glob": sh.E_glob, "E_loc": sh.E_loc,
+                   "K1": sh.K1, "N1": sh.N1, "K2": sh.K2, "N2": sh.N2, "block_m": cfg.block_m,
+                   "nr": cfg.nr, "waves": cfg.waves, "routed_rows": n_local,
+                   "experts_touched": touched, "num_tokens_padded": n_ntp},
+        "per_call_us": {"align": round(us_align, 2), "gate_up": round(us_gu, 2),
+                        "down_combine": round(us_dn, 2)},
+        "gemm_rates": {
+            "gate_up_weight_GBs": round(wb1 / (us_gu * 1e-6) / 1e9, 1),
+            "down_weight_GBs": round(wb2 / (us_dn * 1e-6) / 1e9, 1),
+            "gate_up_TFLOPs": round(flops1 / (us_gu * 1e-6) / 1e12, 2),
+            "down_TFLOPs": round(flops2 / (us_dn * 1e-6) / 1e12, 2),
+        },
+        "roofline": {"kernel": "moe_gemm_kernel (gate/up)", "bound": "hbm",
+                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": int(alg1)},
+    }
+    if args.cpu_experts > 0:
+        log("timing the CPU oracle baseline ...")
+        out["cpu_baseline"] = cpu_baseline(sh, ids, wts, x, a, c1, s1, c2, s2, args.cpu_experts)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,237 @@
+/*
+ * w4a16_moe.h -- C ABI of the W4A16 INT4 mixture-of-experts expert GEMM for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (Chord W4A16 MoE post, "vLLM x Novita AI: Chord, a faster
+ * INT4 MoE for Kimi K2.x"; summary and section "Kernel optimisation"):
+ * BF16 activations times INT4 weights that carry one BF16 scale per 32
+ * consecutive K elements.  A weight code q in 0..15 stands for
+ * bf16_rne((q - 8) * s) -- subtract, then scale, rounded once to BF16 (section
+ * "H200 and Blackwell indexed decode") -- and the products are summed in FP32
+ * (section "vLLM integration": FP16 accumulation is not offered).  Every
+ * output element is rounded once to BF16 (round to nearest even).
+ *
+ * Conventions for every call below
+ *  - Tensor pointers are DEVICE pointers unless stated.  The caller allocates
+ *    and owns all device memory (activations, packed weights, routing
+ *    buffers, outputs, workspace); the library never allocates or frees
+ *    device memory and keeps no device state.
+ *  - BF16 tensors are passed as uint16_t bit patterns, row-major, no padding
+ *    between rows unless a stride is given.
+ *  - Calls that take a stream enqueue work on it and return without waiting,
+ *    except where "synchronises" is stated.  A NULL stream is the default
+ *    stream.  No call reads device memory back to the host unless stated, so
+ *    the align + GEMM sequence can be captured in a HIP graph.
+ *  - Arguments are checked on the host before anything is enqueued.  On a
+ *    bad argument the call returns a negative w4a16_status, enqueues nothing,
+ *    and w4a16_last_error() describes the problem (thread-local string, valid
+ *    until the next failing call on the same thread).
+ *  - Calls that overlap on one stream are ordered by it; the library itself
+ *    is thread-safe (its only state is a mutex-guarded host cache).
+ */
+#ifndef W4A16_MOE_H
+#define W4A16_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t, kept opaque so this header needs no HIP include. */
+typedef void* w4a16_stream_t;
+
+typedef enum {
+  W4A16_OK = 0,
+  W4A16_ERR_ARG = -1,          /* NULL pointer, negative size, misaligned pointer */
+  W4A16_ERR_SHAPE = -2,        /* unsupported shape: K % 32 != 0, N % 16 != 0, ... */
+  W4A16_ERR_LAYOUT = -3,       /* weight descriptor corrupt or not matching the call */
+  W4A16_ERR_UNSUPPORTED = -4,  /* tile configuration not built into this library */
+  W4A16_ERR_CAPACITY = -5,     /* routing buffer smaller than the worst case needs */
+  W4A16_ERR_ROUTING = -6,      /* validation found an expert id outside [0, E_glob) */
+  W4A16_ERR_HIP = -7,          /* the HIP runtime reported an error */
+  W4A16_ERR_WORKSPACE = -8     /* workspace missing or smaller than required */
+} w4a16_status;
+
+/* Description of the last non-OK status on this thread ("" if none). */
+const char* w4a16_last_error(void);
+
+/* ABI version of this header (W4A16_ABI_VERSION). */
+#define W4A16_ABI_VERSION 1
+int32_t w4a16_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Packed weights.
+ *
+ * Input format (Chord post, section "Grouped SM90 kernels", operator listing):
+ * unsigned INT4 codes [E, N, K], here one code per byte (values 0..15; the
+ * upper four bits of each byte are ignored), and BF16 scales [E, N, K/32],
+ * scale index kk / 32 along K.  The post packs once at model load (section
+ * "Indexed kernels": configuration and layout are fixed before packing);
+ * here one packed layout serves every call and every tile configuration, so
+ * nothing about the call has to be known when packing.
+ *
+ * Packed layout (all little-endian), with NT = N / 16, KP = K rounded up to
+ * 128, KC = KP / 128, SC = KC rounded up to 8:
+ *   packed_w : uint32 words [E][NT][KC][64 lanes][4 words]
+ *     lane l = 16 * g + i holds row n = 16 * tile + i; word j of that lane
+ *     holds the 8 codes of K indices kk = 128 * c + 32 * g + 8 * j + e,
+ *     e = 0..7, code e at bit 4 * (e / 2) + 16 * (e % 2).  Codes for kk >= K
+ *     are 8 (weight 0).  Each lane's word is exactly one MFMA operand
+ *     fragment of 8 consecutive K values, and one lane's four words span one
+ *     32-wide scale group.
+ *   packed_s : bf16 [E][NT][64 lanes][SC]
+ *     entry c of lane l = 16 * g + i is scale[n = 16 * tile + i][4 * c + g]
+ *     (0 past K / 32).
+ *   packed_w is E * NT * KC * 1024 bytes, packed_s is E * NT * 64 * SC * 2.
+ * ---------------------------------------------------------------------- */
+#define W4A16_DESC_MAGIC 0x16A4B0E5u /* arbitrary tag */
+#define W4A16_DESC_VERSION 1u
+
+typedef struct {
+  uint32_t magic;       /* W4A16_DESC_MAGIC */
+  uint32_t version;     /* W4A16_DESC_VERSION */
+  int32_t E, N, K;      /* experts, output features, reduction length */
+  int32_t K_pad;        /* KP above */
+  int32_t scale_cols;   /* SC above */
+  int32_t group;        /* 32 */
+  uint64_t w_bytes;     /* size of packed_w */
+  uint64_t s_bytes;     /* size of packed_s */
+  uint64_t check;       /* checksum of the fields above */
+} w4a16_weight_desc;
+
+/* Fill *out for an [E, N, K] weight (host only, no device work).
+ * Errors: ERR_ARG (out NULL, E/N/K <= 0), ERR_SHAPE (K % 32 or N % 16). */
+w4a16_status w4a16_weight_desc_init(int32_t E, int32_t N, int32_t K, w4a16_weight_desc* out);
+
+/* Pack codes [E, N, K] (uint8) and scales [E, N, K/32] (bf16) into the
+ * layout above.  `desc` must come from w4a16_weight_desc_init for the same
+ * E, N, K; packed_w / packed_s must be 16-byte aligned and desc->w_bytes /
+ * desc->s_bytes long.  Inputs are read, outputs fully written.
+ * Errors: ERR_ARG, ERR_LAYOUT (bad desc), ERR_HIP. */
+w4a16_status w4a16_pack_w4(const uint8_t* codes, const uint16_t* scales,
+                           const w4a16_weight_desc* desc, void* packed_w, void* packed_s,
+                           w4a16_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Routing align: topk_ids -> sorted_ids / expert_ids / num_tokens_padded.
+ *
+ * (Chord post, section "Two kernel families": the indexed family consumes
+ * these three buffers; section "vLLM integration": they are over-allocated so
+ * no routed count is read back to the host; Figure 3: padding lives in
+ * sentinel index values, activations are not padded.)
+ *
+ * Slot s = t * topk + j.  A slot is local when first_expert <= topk_ids[t][j]
+ * < first_expert + E_loc; its local expert is the difference.  For each local
+ * expert e in order, its slot ids ascending, then the sentinel T * topk until
+ * the segment length is a multiple of block_m.  expert_ids[b] = local expert
+ * of block b (rows b*block_m .. b*block_m + block_m - 1), -1 for blocks past
+ * the padded total.  *num_tokens_padded = padded total (device int32).
+ * sorted_ids past the padded total hold the sentinel.  Ids outside
+ * [0, E_glob) are treated as not local.
+ *
+ * capacity = length of sorted_ids, >= w4a16_align_capacity(); expert_ids has
+ * capacity / block_m entries.  block_m in {16, 32, 64, 128}.  E_loc <= 1024.
+ * validate != 0 synchronises: topk_ids are copied to the host and checked
+ * to lie in [0, E_glob) before anything is enqueued (ERR_ROUTING otherwise).
+ * Errors: ERR_ARG, ERR_SHAPE, ERR_CAPACITY, ERR_ROUTING, ERR_HIP. */
+int64_t w4a16_align_capacity(int32_t T, int32_t topk, int32_t E_loc, int32_t block_m);
+
+w4a16_status w4a16_moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t E_glob,
+                             int32_t first_expert, int32_t E_loc, int32_t block_m,
+                             int32_t* sorted_ids, int32_t* expert_ids,
+                             int32_t* num_tokens_padded, int64_t capacity, int32_t validate,
+                             w4a16_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Tile configuration and its selection.
+ *
+ * The post picks block_m from tokens per expert, tok_e = routed rows /
+ * experts, not from total tokens (section "H200 prefill and TP8": below about
+ * 80 rows per expert a search over block counts on sampled routing, above it
+ * a fit of padded expert rows).  w4a16_select applies the same idea with
+ * gfx950 constants; a config may also be given explicitly.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t block_m;   /* rows per routed block: 16, 32, 64 or 128 */
+  int32_t nr;        /* 16-row weight tiles per wave: 1, 2 or 4 */
+  int32_t waves;     /* waves per workgroup: 4 */
+  int32_t split_k;   /* reserved, must be 1 */
+} w4a16_config;
+
+/* Choose a config for T tokens, top-k, E_glob model experts of which E_loc
+ * are held here, projection [N, K] (host only).  Memoised per argument set.
+ * Errors: ERR_ARG. */
+w4a16_status w4a16_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc,
+                          int32_t N, int32_t K, w4a16_config* out);
+
+/* ------------------------------------------------------------------------
+ * Indexed MoE GEMM (the post's indexed family).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const int32_t* sorted_ids;         /* from w4a16_moe_align */
+  const int32_t* expert_ids;
+  const int32_t* num_tokens_padded;  /* device scalar */
+  int64_t capacity;                  /* length of sorted_ids */
+  int32_t block_m;                   /* must equal the config's block_m */
+  int32_t T, topk;                   /* sentinel is T * topk */
+  const int32_t* topk_ids;           /* [T, topk]; read only by the combine */
+  int32_t first_expert, E_loc;       /* local expert range; read only by the combine */
+} w4a16_indexed_routing;
+
+/* Bytes of workspace w4a16_moe_gemm needs: 0 without combine,
+ * T * topk * N * 4 with combine. */
+size_t w4a16_moe_gemm_workspace_bytes(int32_t T, int32_t topk, int32_t N, int32_t combine);
+
+/* out = routed W4A16 product.
+ *  a          : bf16 activations, row stride K (desc->K).  a_per_slot = 0:
+ *               one row per token ([T, K], gate/up); a_per_slot = 1: one row
+ *               per slot ([T * topk, K], down).  a_rows = rows in `a`.
+ *  topk_weights == NULL: per-slot output out[T * topk, N]; only local slots
+ *               are written, other rows keep their contents.
+ *  topk_weights != NULL (float32 [T, topk]): top-k-weighted combine,
+ *               out[t] = bf16(sum over local j of w[t][j] * (a_row . W[e]^T))
+ *               with fp32 products, summed in j order, one rounding; tokens
+ *               without local slots get 0; every row of out[T, N] written.
+ *               Needs workspace (fp32 partials per slot).
+ *  cfg        : NULL selects one (w4a16_select).
+ * Pointers: packed_w, packed_s, a, out, workspace 16-byte aligned.
+ * Errors: ERR_ARG, ERR_LAYOUT, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP. */
+w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
+                            const void* packed_s, const uint16_t* a, int64_t a_rows,
+                            int32_t a_per_slot, const w4a16_indexed_routing* routing,
+                            const float* topk_weights, uint16_t* out,
+                            const w4a16_config* cfg, void* workspace, size_t workspace_bytes,
+                            w4a16_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Grouped layouts (the post's grouped family, section "Grouped SM90
+ * kernels": contiguous prefill and masked decode; same packed weights here).
+ * ---------------------------------------------------------------------- */
+
+/* Contiguous: a [m_rows, K] holds each expert's rows back to back, each
+ * expert's segment starting at a multiple of 128 rows; m_indices[r] is the
+ * expert of row r or -1 on padding.  out[m_rows, N]: rows with
+ * m_indices[r] >= 0 written as bf16(a[r] . W[m_indices[r]]^T); -1 rows are
+ * left unwritten.  cfg->block_m must divide 128 (NULL: 128).
+ * Errors: ERR_ARG, ERR_LAYOUT, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP. */
+w4a16_status w4a16_grouped_contiguous(const w4a16_weight_desc* desc, const void* packed_w,
+                                      const void* packed_s, const uint16_t* a, int64_t m_rows,
+                                      const int32_t* m_indices, uint16_t* out,
+                                      const w4a16_config* cfg, w4a16_stream_t stream);
+
+/* Masked: a [E, max_m, K]; masked_m[g] (device int32, E entries) valid rows
+ * of group g; out flat [E * max_m, N], row g * max_m + r written for
+ * r < min(masked_m[g], max_m), other rows unwritten.  expected_m (host, > 0)
+ * only steers the tile choice when cfg is NULL.
+ * Errors: ERR_ARG, ERR_LAYOUT, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP. */
+w4a16_status w4a16_grouped_masked(const w4a16_weight_desc* desc, const void* packed_w,
+                                  const void* packed_s, const uint16_t* a, int32_t max_m,
+                                  const int32_t* masked_m, int32_t expected_m, uint16_t* out,
+                                  const w4a16_config* cfg, w4a16_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4A16_MOE_H */

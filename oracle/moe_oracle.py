@@ -164,7 +164,7 @@ def moe_align(topk_ids: np.ndarray, E_glob: int, first: int, E_loc: int,
         g = first + e
         if g < 0 or g >= E_glob:
             continue
-        slots = [s for s in range(T * k) if flat[s] == g]
+        slots = np.nonzero(flat == g)[0]          # ascending slot ids of expert g
         n = len(slots)
         P = -(-n // block_m) * block_m
         assert pos + P <= cap, "capacity too small"

@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/w4a16_moe.h declares, and rejects bad arguments before
+touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w4a16_int4_mixture_moe_amd as W
+from w4a16_int4_mixture_moe_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16_moe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(W.lib_path()):
+        pytest.skip("library not built")
+    return W.load()
+
+
+def test_every_declared_function_is_exported_and_bound(L):
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in _lib.SIGNATURES, f"{n} has no ctypes signature"
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(_lib.WeightDesc) == 56
+    assert ctypes.sizeof(_lib.Config) == 16
+    assert _lib.IndexedRouting.capacity.offset == 24
+
+
+def test_version_and_desc(L):
+    assert L.w4a16_abi_version() == 1
+    d = W.weight_desc(48, 4096, 7168)
+    assert (d.K_pad, d.scale_cols, d.group) == (7168, 56, 32)
+    assert d.w_bytes == 48 * 4096 * 7168 // 2
+    assert d.s_bytes == 48 * 256 * 64 * 56 * 2
+    d = W.weight_desc(2, 32, 96)                         # ragged K: padded to one chunk
+    assert (d.K_pad, d.scale_cols) == (128, 8)
+
+
+@pytest.mark.parametrize("E,N,K,code", [(0, 16, 32, -1), (1, 16, 33, -2), (1, 24, 32, -2), (1, 16, -32, -1)])
+def test_desc_rejects_bad_shapes(L, E, N, K, code):
+    d = _lib.WeightDesc()
+    assert L.w4a16_weight_desc_init(E, N, K, ctypes.byref(d)) == code
+    assert L.w4a16_last_error()
+
+
+def test_corrupted_descriptor_is_rejected(L):
+    d = W.weight_desc(4, 64, 256)
+    d.N = 128                                           # shape changed after packing
+    st = L.w4a16_grouped_contiguous(ctypes.byref(d), 16, 16, 16, 128, 16, 16, None, None)
+    assert st == -3 and b"checksum" in L.w4a16_last_error()
+    d = W.weight_desc(4, 64, 256)
+    d.magic = 0
+    assert L.w4a16_pack_w4(16, 16, ctypes.byref(d), 16, 16, None) == -3
+
+
+def test_capacity_and_workspace(L):
+    assert W.align_capacity(576, 8, 48, 32) == ((4608 + 48 * 31 + 31) // 32) * 32
+    assert L.w4a16_align_capacity(4, 2, 3, 24) == -1
+    assert W.workspace_bytes(10, 8, 7168, True) == 10 * 8 * 7168 * 4
+    assert W.workspace_bytes(10, 8, 7168, False) == 0
+
+
+def test_align_argument_errors(L):
+    P = 16  # fake, aligned, never dereferenced: every case fails validation first
+    assert L.w4a16_moe_align(P, 4, 2, 8, 0, 8, 16, None, P, P, 1024, 0, None) == -1
+    assert L.w4a16_moe_align(P, 4, 2, 8, 4, 8, 16, P, P, P, 1024, 0, None) == -1     # range past E_glob
+    assert L.w4a16_moe_align(P, 4, 2, 8, 0, 8, 24, P, P, P, 1024, 0, None) == -2     # block_m
+    assert L.w4a16_moe_align(P, 4, 2, 8, 0, 8, 16, P, P, P, 64, 0, None) == -5       # capacity
+    assert L.w4a16_moe_align(P, 4, 2, 2000, 0, 1500, 16, P, P, P, 1 << 20, 0, None) == -2
+
+
+def test_gemm_argument_errors(L):
+    P = 16
+    d = W.weight_desc(8, 64, 256)
+    r = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 8)
+    cfg = W.config(32, 2)
+    call = lambda **kw: L.w4a16_moe_gemm(ctypes.byref(d), P, P, kw.get("a", P), kw.get("rows", 64), 0,
+                                         ctypes.byref(kw.get("r", r)), kw.get("w"), P,
+                                         kw.get("cfg", ctypes.byref(cfg)), kw.get("ws"),
+                                         kw.get("wsb", 0), None)
+    assert call(a=P + 2) == -1                                           # misaligned activations
+    assert call(rows=10) == -2                                           # too few activation rows
+    assert call(cfg=ctypes.byref(W.config(64, 2))) == -3                 # block_m disagrees with routing
+    assert call(cfg=ctypes.byref(W.config(32, 3))) == -4                 # tile config not built
+    assert call(w=P) == -8                                               # combine without workspace
+    bad = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 4)
+    assert call(r=bad) == -3                                             # E_loc != weight experts
+    assert L.w4a16_grouped_masked(ctypes.byref(d), P, P, P, 0, P, 4, P, None, None) == -1
+    assert L.w4a16_grouped_masked(ctypes.byref(d), P, P, P, 32, P, 0, P, None, None) == -1
+    assert L.w4a16_grouped_contiguous(ctypes.byref(d), P, P, P, 100, P, P, None, None) == -2
+
+
+def test_selector_follows_tokens_per_expert(L):
+    dec = W.select(576, 8, 384, 48, 4096, 7168)            # ~12 rows/expert
+    assert dec.block_m == 32 and dec.nr == 2
+    one = W.select(16, 8, 384, 384, 512, 7168)             # ~0.3 rows/expert
+    assert one.block_m == 16
+    pre = W.select(8192, 8, 384, 48, 4096, 7168)           # ~171 rows/expert
+    assert pre.block_m == 128 and pre.nr == 4
+    # tok_e, not total tokens: same T, 8x more experts -> decode side
+    assert W.select(8192, 8, 3072, 48, 4096, 7168).block_m < 128
+    assert W.select(576, 8, 384, 48, 4096, 7168).block_m == dec.block_m   # memoised, stable
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib._build, "lib_path", lambda: str(tmp_path / "nope.so"))
+    with pytest.raises(_lib.W4A16Error):
+        _lib.load()

@@ -1,0 +1,309 @@
+"""GPU parity of the HIP kernels against the CPU oracle on small and ragged
+shapes: routing align (bit-exact), weight packing (bit-exact round trip),
+the indexed GEMM with per-slot and combined outputs, the grouped layouts, and
+the invariants (padding contributes nothing, token order, tile configuration
+does not change bits, zero-row experts, empty inputs)."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from synth import workloads as W
+from tests.gpu_util import Problem, assert_close, bits, dev, log, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+import w4a16_int4_mixture_moe_amd as M  # noqa: E402  (fails loudly if the binding is broken)
+
+
+# ------------------------------------------------------------ routing align
+
+def _align_case(topk, E_glob, first, E_loc, bm):
+    T, k = topk.shape
+    r = M.moe_align(to_dev(topk.astype(np.int32)), E_glob, first, E_loc, bm)
+    si, ei, ntp = O.moe_align(topk, E_glob, first, E_loc, bm)
+    got_si = r.sorted_ids.cpu().numpy()
+    got_ei = r.expert_ids.cpu().numpy()[: len(ei)]
+    got_ntp = int(r.num_tokens_padded.cpu().item())
+    assert got_ntp == ntp, (T, k, E_glob, first, E_loc, bm)
+    np.testing.assert_array_equal(got_si, si)
+    np.testing.assert_array_equal(got_ei, ei)
+
+
+def test_align_bit_exact_small_random():
+    rng = np.random.default_rng(0)
+    n = 0
+    for T, k, E_glob in [(1, 1, 1), (3, 2, 5), (37, 3, 11), (64, 2, 8), (200, 8, 64), (513, 6, 7)]:
+        for (first, E_loc), bm in itertools.product([(0, E_glob), (E_glob // 3, max(1, E_glob // 2))],
+                                                    (16, 32, 64, 128)):
+            topk = rng.integers(0, E_glob, (T, k)).astype(np.int32)
+            _align_case(topk, E_glob, first, E_loc, bm)
+            n += 1
+    log(f"{n} align cases bit-exact")
+
+
+def test_align_out_of_range_ids_are_not_local_and_validate_rejects():
+    topk = np.array([[0, 5], [-1, 2], [9, 1]], np.int32)
+    _align_case(topk, 4, 0, 4, 16)
+    with pytest.raises(M.W4A16Error, match="ERR_ROUTING"):
+        M.moe_align(to_dev(topk), 4, 0, 4, 16, validate=True)
+
+
+def test_align_edge_cases():
+    _align_case(np.zeros((0, 4), np.int32), 8, 0, 8, 16)                       # no tokens
+    _align_case(np.full((50, 2), 7, np.int32), 8, 0, 4, 32)                   # no local slot
+    _align_case(np.full((300, 2), 3, np.int32), 8, 0, 8, 16)                  # all to one expert
+    _align_case(np.random.default_rng(1).integers(0, 1024, (256, 8)).astype(np.int32), 1024, 0, 1024, 16)
+
+
+@pytest.mark.parametrize("name", ["ep8_decode", "ep8_prefill", "tp8_t1", "tp8_t4096", "grouped_skewed"])
+def test_align_bit_exact_workloads(name):
+    sh = W.WORKLOADS[name]
+    topk, _ = W.routing_for(sh)
+    for bm in (16, 32, 128):
+        _align_case(topk, sh.E_glob, sh.first, sh.E_loc, bm)
+
+
+# ------------------------------------------------------------ packing
+
+def _unpack_cpu(w_bytes: np.ndarray, s_bytes: np.ndarray, E, N, K):
+    """Read the packed layout as documented in w4a16_moe.h back into codes
+    [E, N, K] and scales [E, N, K/32]."""
+    KP = -(-K // 128) * 128
+    KC, NT = KP // 128, N // 16
+    SC = -(-KC // 8) * 8
+    words = w_bytes.view(np.uint32).reshape(E, NT, KC, 64, 4)
+    codes = np.zeros((E, N, KP), np.uint8)
+    for l, j, e in itertools.product(range(64), range(4), range(8)):
+        g, i = divmod(l, 16)
+        shift = 4 * (e // 2) + 16 * (e % 2)
+        vals = (words[:, :, :, l, j] >> shift) & 0xF                     # [E, NT, KC]
+        kk = np.arange(KC) * 128 + 32 * g + 8 * j + e
+        codes[:, np.arange(NT)[:, None] * 16 + i, kk[None, :]] = vals
+    sc = s_bytes.view(np.uint16).reshape(E, NT, 64, SC)
+    scales = np.zeros((E, N, 4 * SC), np.uint16)
+    for l in range(64):
+        g, i = divmod(l, 16)
+        scales[:, (np.arange(NT) * 16 + i)[:, None], (4 * np.arange(SC) + g)[None, :]] = sc[:, :, l, :]
+    return codes, scales
+
+
+@pytest.mark.parametrize("E,N,K", [(3, 48, 96), (2, 32, 256), (1, 16, 7168)])
+def test_pack_round_trip_bit_exact(E, N, K):
+    rng = np.random.default_rng(E * N + K)
+    codes = rng.integers(0, 16, (E, N, K), dtype=np.uint8)
+    scales = rng.integers(0, 65536, (E, N, K // 32), dtype=np.uint16)
+    p = M.pack_w4(to_dev(codes), to_dev_bf16(scales))
+    c2, s2 = _unpack_cpu(p.w.cpu().numpy(), p.s.cpu().numpy(), E, N, K)
+    np.testing.assert_array_equal(c2[:, :, :K], codes)
+    assert (c2[:, :, K:] == 8).all()                       # K padding decodes to weight 0
+    np.testing.assert_array_equal(s2[:, :, : K // 32], scales)
+    assert (s2[:, :, K // 32:] == 0).all()
+
+
+# ------------------------------------------------------------ indexed GEMM
+
+def _run_indexed(P, bm, nr=None, first=None):
+    sh = P.sh
+    first = sh.first if first is None else first
+    r = M.moe_align(P.d_ids, sh.E_glob, first, sh.E_loc, bm)
+    cfg = M.config(bm, nr if nr else (4 if bm >= 64 else 2))
+    h = M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=cfg)
+    y = M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=cfg) if P.with_down else None
+    torch.cuda.synchronize()
+    return r, h, y
+
+
+def _check_indexed(P, h, y, what):
+    sh = P.sh
+    ref_h, ok = O.indexed_gate_up(P.x, P.c1, P.s1, P.topk_ids, sh.first, sh.E_loc)
+    gh = bits(h)
+    e1, x1 = assert_close(gh[ok], ref_h[ok], what + " gate/up")
+    assert not gh[~ok].any(), "non-local slot rows were written"
+    res = {"gate_up_max_err": e1, "gate_up_exact": x1}
+    if y is not None:
+        ref_y = O.indexed_down_combine(P.a, P.c2, P.s2, P.topk_ids, P.topk_w, sh.first, sh.E_loc)
+        e2, x2 = assert_close(bits(y), ref_y, what + " down+combine")
+        res.update(down_max_err=e2, down_exact=x2)
+    log(what, res)
+    return res
+
+
+def test_tiny_workload_all_tile_configs_match_oracle_and_each_other():
+    P = Problem(W.WORKLOADS["tiny"]).upload()
+    outs = {}
+    for bm, nr in itertools.product((16, 32, 64, 128), (2, 4)):
+        _, h, y = _run_indexed(P, bm, nr)
+        _check_indexed(P, h, y, f"tiny bm={bm} nr={nr}")
+        outs[(bm, nr)] = (bits(h), bits(y))
+    base = outs[(16, 2)]
+    for key, (h, y) in outs.items():          # tile configuration does not change bits
+        np.testing.assert_array_equal(h, base[0], err_msg=str(key))
+        np.testing.assert_array_equal(y, base[1], err_msg=str(key))
+
+
+def test_ragged_shapes():
+    """N not a multiple of the workgroup tile, K not a multiple of 128, odd T."""
+    sh = W.MoEShape(name="ragged", E_glob=9, E_loc=5, first=2, topk=3, T=37, K1=96, N1=48,
+                    K2=160, N2=80, seed=77)
+    P = Problem(sh).upload()
+    for bm in (16, 32, 128):
+        _, h, y = _run_indexed(P, bm)
+        _check_indexed(P, h, y, f"ragged bm={bm}")
+
+
+def test_one_hot_activations_return_dequantised_weights_bit_exact():
+    E, N, K = 3, 64, 256
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 16, (E, N, K), dtype=np.uint8)
+    sc = W.to_bf16_bits(rng.uniform(0.005, 0.02, (E, N, K // 32)).astype(np.float32))
+    x = W.to_bf16_bits(np.eye(K, dtype=np.float32))
+    ids = (np.arange(K) % E).astype(np.int32)[:, None]
+    p = M.pack_w4(to_dev(codes), to_dev_bf16(sc))
+    r = M.moe_align(to_dev(ids), E, 0, E, 16)
+    h = bits(M.moe_w4a16_gemm(to_dev_bf16(x), p, r))
+    Wd = O.f64_to_bf16(O.dequant(codes, sc))                          # [E, N, K]
+    want = np.stack([Wd[t % E, :, t] for t in range(K)])
+    np.testing.assert_array_equal(h, want)
+
+
+def test_zero_codes_give_zero_and_power_of_two_scaling_is_exact():
+    P = Problem(W.WORKLOADS["tiny"])
+    P.c1 = np.full_like(P.c1, 8)
+    P.upload()
+    _, h, _ = _run_indexed(P, 16)
+    assert not bits(h).any()
+    P = Problem(W.WORKLOADS["tiny"]).upload()
+    _, h1, y1 = _run_indexed(P, 32)
+    P.d_x = P.d_x * 4
+    P.d_w = P.d_w * 2
+    _, h2, y2 = _run_indexed(P, 32)
+    np.testing.assert_array_equal(O.bf16_to_f64(bits(h2)), 4 * O.bf16_to_f64(bits(h1)))
+    np.testing.assert_array_equal(O.bf16_to_f64(bits(y2)), 2 * O.bf16_to_f64(bits(y1)))
+
+
+def test_padding_contributes_nothing():
+    """Garbage past num_tokens_padded, canaries in non-local rows, NaN in
+    activation rows that no slot references: outputs unchanged."""
+    sh = W.scaled(W.WORKLOADS["tiny"], E_glob=16, E_loc=8, first=4)
+    P = Problem(sh).upload()
+    r, h, y = _run_indexed(P, 32)
+    ntp = int(r.num_tokens_padded.item())
+    r.sorted_ids[ntp:] = 3                     # valid-looking slot ids past the end
+    r.expert_ids[ntp // 32:] = 1
+    canary = torch.full_like(h, -7.0)
+    h2 = M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=M.config(32, 2), out=canary.clone())
+    y2 = M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=M.config(32, 2))
+    torch.cuda.synchronize()
+    ok = np.isin(P.topk_ids.reshape(-1), np.arange(4, 12))
+    hb, h2b = bits(h), bits(h2)
+    np.testing.assert_array_equal(h2b[ok], hb[ok])
+    assert (O.bf16_to_f64(h2b[~ok]) == -7.0).all()
+    np.testing.assert_array_equal(bits(y2), bits(y))
+    # NaN in every down-input row of a non-local slot: never read
+    a = P.a.copy()
+    a[~ok] = 0x7FC0
+    P.d_a = to_dev_bf16(a)
+    _, _, y3 = _run_indexed(P, 32)
+    np.testing.assert_array_equal(bits(y3), bits(y))
+
+
+def test_token_order_invariance_bit_exact():
+    P = Problem(W.WORKLOADS["tiny"]).upload()
+    _, h, y = _run_indexed(P, 16)
+    perm = np.random.default_rng(3).permutation(P.T)
+    Q = Problem(W.WORKLOADS["tiny"])
+    Q.topk_ids, Q.topk_w, Q.x = P.topk_ids[perm], P.topk_w[perm], P.x[perm]
+    Q.a = P.a.reshape(P.T, -1, P.a.shape[1])[perm].reshape(P.a.shape)
+    Q.upload()
+    _, hq, yq = _run_indexed(Q, 16)
+    k = P.sh.topk
+    np.testing.assert_array_equal(bits(hq).reshape(P.T, k, -1), bits(h).reshape(P.T, k, -1)[perm])
+    np.testing.assert_array_equal(bits(yq), bits(y)[perm])
+
+
+def test_zero_row_experts_and_no_local_tokens():
+    sh = W.scaled(W.WORKLOADS["tiny"], T=40)
+    P = Problem(sh)
+    P.topk_ids = np.where(P.topk_ids % 2 == 0, 1, 5).astype(np.int32)     # only experts 1, 5 used
+    P.upload()
+    _, h, y = _run_indexed(P, 16)
+    _check_indexed(P, h, y, "two experts only")
+    # EP share that receives nothing: ntp = 0, combine output all zero
+    Q = Problem(sh)
+    Q.topk_ids = np.full_like(Q.topk_ids, 7)
+    Q.upload()
+    r = M.moe_align(Q.d_ids, 8, 0, 7, 16)
+    sh7 = r
+    assert int(sh7.num_tokens_padded.item()) == 0
+    p7 = M.pack_w4(to_dev(Q.c2[:7]), to_dev_bf16(Q.s2[:7]))
+    y = M.moe_w4a16_gemm(Q.d_a, p7, r, topk_weights=Q.d_w, cfg=M.config(16, 2))
+    torch.cuda.synchronize()
+    assert not bits(y).any()
+
+
+def test_duplicate_expert_in_one_token():
+    sh = W.scaled(W.WORKLOADS["tiny"], T=24)
+    P = Problem(sh)
+    P.topk_ids[:, 1] = P.topk_ids[:, 0]
+    P.upload()
+    _, h, y = _run_indexed(P, 32)
+    _check_indexed(P, h, y, "duplicate experts")
+
+
+def test_empty_token_batch():
+    sh = W.scaled(W.WORKLOADS["tiny"], T=0)
+    p = M.pack_w4(torch.zeros((8, 512, 256), dtype=torch.uint8, device=dev()),
+                  torch.zeros((8, 512, 8), dtype=torch.bfloat16, device=dev()))
+    ids = torch.zeros((0, 2), dtype=torch.int32, device=dev())
+    r = M.moe_align(ids, 8, 0, 8, 16)
+    h = M.moe_w4a16_gemm(torch.zeros((0, 256), dtype=torch.bfloat16, device=dev()), p, r)
+    torch.cuda.synchronize()
+    assert h.shape == (0, 512)
+
+
+def test_dense_special_case_matches_library_matmul():
+    """E = 1, top-1, weight 1: the routed GEMM is a dense x . W^T; compare with
+    torch.matmul (hipBLASLt) on the dequantised weight, at K = 7168, N = 4096."""
+    T, N, K = 256, 4096, 7168
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 16, (1, N, K), dtype=np.uint8)
+    sc = W.to_bf16_bits(rng.uniform(0.005, 0.02, (1, N, K // 32)).astype(np.float32))
+    x = W.activations(9, "x", T, K)
+    dc, ds = to_dev(codes), to_dev_bf16(sc)
+    p = M.pack_w4(dc, ds)
+    r = M.moe_align(torch.zeros((T, 1), dtype=torch.int32, device=dev()), 1, 0, 1, 128)
+    dx = to_dev_bf16(x)
+    h = M.moe_w4a16_gemm(dx, p, r, cfg=M.config(128, 4))
+    Wd = ((dc[0].float() - 8.0) * ds[0].float().repeat_interleave(32, dim=1)).to(torch.bfloat16)
+    ref = torch.matmul(dx.float(), Wd.float().t().contiguous()).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    e, x_exact = assert_close(bits(h), bits(ref), "dense vs torch.matmul")
+    log("dense special case: max err", e, "bit-exact fraction", x_exact)
+
+
+# ------------------------------------------------------------ grouped layouts
+
+def test_grouped_contiguous_and_masked_small():
+    sh = W.scaled(W.WORKLOADS["grouped_skewed"], T=300, K1=256, N1=96, E_glob=24, E_loc=6,
+                  first=3, max_m=48, n_zero_experts=1)
+    P = Problem(sh, with_down=False).upload()
+    A, mi, slots = W.contiguous_layout(P.topk_ids, P.x, sh.first, sh.E_loc, pad=128, pad_fill=0x7FC0)
+    ref, valid = O.grouped_contiguous(A, P.c1, P.s1, mi)
+    for bm in (16, 64, 128):
+        out = bits(M.grouped_contiguous(to_dev_bf16(A), P.p1, to_dev(mi), cfg=M.config(bm, 4 if bm >= 64 else 2)))
+        assert_close(out[valid], ref[valid], f"contiguous bm={bm}")
+    A3, mm, sl3, dropped = W.masked_layout(P.topk_ids, P.x, sh.first, sh.E_loc, sh.max_m, pad_fill=0x7FC0)
+    log("masked dropped", dropped, "masked_m", mm.tolist())
+    ref, valid = O.grouped_masked(A3, P.c1, P.s1, mm)
+    for bm in (16, 32, 64):
+        out = bits(M.grouped_masked(to_dev_bf16(A3), P.p1, to_dev(mm), 32, cfg=M.config(bm, 2)))
+        assert_close(out[valid], ref[valid], f"masked bm={bm}")
+    out = bits(M.grouped_masked(to_dev_bf16(A3), P.p1, to_dev(mm), expected_m=max(1, int(mm.mean()))))
+    assert_close(out[valid], ref[valid], "masked auto config")
+    # grouped and indexed agree on the same rows
+    h, ok = O.indexed_gate_up(P.x, P.c1, P.s1, P.topk_ids, sh.first, sh.E_loc)
+    s = sl3.reshape(-1)
+    np.testing.assert_array_equal(ref[valid], h[s[valid]])

@@ -1,0 +1,232 @@
+"""Python binding of the W4A16 MoE C ABI: torch tensors in, device pointers and
+torch's current HIP stream out.  Argument marshalling only -- every step of
+the computation runs in the HIP library's kernels.
+
+    packed = pack_w4(codes_u8[E, N, K], scales_bf16[E, N, K/32])
+    routing = moe_align(topk_ids[T, k], E_glob, first_expert, E_loc, block_m)
+    h = moe_w4a16_gemm(x[T, K], packed, routing)                     # per slot
+    y = moe_w4a16_gemm(a[T*k, K2], packed2, routing, topk_weights)   # combined
+    out = grouped_contiguous(a2[m, K], packed, m_indices)
+    out = grouped_masked(a3[E, max_m, K], packed, masked_m, expected_m)
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import torch
+
+from ._lib import Config, IndexedRouting, W4A16Error, WeightDesc, check, load
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtypes, ndim: Optional[int] = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_BF16 = (torch.bfloat16, torch.int16)
+
+
+@dataclasses.dataclass
+class PackedW4:
+    desc: WeightDesc
+    w: torch.Tensor      # uint8 [w_bytes]
+    s: torch.Tensor      # uint8 [s_bytes]
+
+    @property
+    def E(self):
+        return self.desc.E
+
+    @property
+    def N(self):
+        return self.desc.N
+
+    @property
+    def K(self):
+        return self.desc.K
+
+
+def weight_desc(E: int, N: int, K: int) -> WeightDesc:
+    d = WeightDesc()
+    check(load().w4a16_weight_desc_init(E, N, K, ctypes.byref(d)))
+    return d
+
+
+def pack_w4(codes: torch.Tensor, scales: torch.Tensor) -> PackedW4:
+    """codes uint8 [E, N, K] (0..15), scales bf16 [E, N, K/32] -> packed weight."""
+    _need(codes, "codes", (torch.uint8,), 3)
+    _need(scales, "scales", _BF16, 3)
+    E, N, K = codes.shape
+    if tuple(scales.shape) != (E, N, K // 32) or K % 32:
+        raise ValueError(f"scales shape {tuple(scales.shape)} does not match codes {tuple(codes.shape)}")
+    d = weight_desc(E, N, K)
+    w = torch.empty(d.w_bytes, dtype=torch.uint8, device=codes.device)
+    s = torch.empty(d.s_bytes, dtype=torch.uint8, device=codes.device)
+    check(load().w4a16_pack_w4(codes.data_ptr(), scales.data_ptr(), ctypes.byref(d), w.data_ptr(),
+                               s.data_ptr(), _stream(codes.device)))
+    return PackedW4(d, w, s)
+
+
+@dataclasses.dataclass
+class Routing:
+    sorted_ids: torch.Tensor          # int32 [capacity]
+    expert_ids: torch.Tensor          # int32 [capacity / block_m]
+    num_tokens_padded: torch.Tensor   # int32 [1]
+    block_m: int
+    topk_ids: torch.Tensor            # int32 [T, k]
+    E_glob: int
+    first_expert: int
+    E_loc: int
+
+    @property
+    def T(self):
+        return self.topk_ids.shape[0]
+
+    @property
+    def topk(self):
+        return self.topk_ids.shape[1]
+
+    @property
+    def capacity(self):
+        return self.sorted_ids.numel()
+
+    def as_c(self) -> IndexedRouting:
+        return IndexedRouting(self.sorted_ids.data_ptr(), self.expert_ids.data_ptr(),
+                              self.num_tokens_padded.data_ptr(), self.capacity, self.block_m,
+                              self.T, self.topk, self.topk_ids.data_ptr(), self.first_expert,
+                              self.E_loc)
+
+
+def align_capacity(T: int, topk: int, E_loc: int, block_m: int) -> int:
+    c = load().w4a16_align_capacity(T, topk, E_loc, block_m)
+    if c < 0:
+        raise ValueError("bad arguments for align_capacity")
+    return int(c)
+
+
+def moe_align(topk_ids: torch.Tensor, E_glob: int, first_expert: int, E_loc: int, block_m: int,
+              validate: bool = False, capacity: Optional[int] = None) -> Routing:
+    """topk_ids int32 [T, k] -> sorted_ids / expert_ids / num_tokens_padded."""
+    _need(topk_ids, "topk_ids", (torch.int32,), 2)
+    T, k = topk_ids.shape
+    cap = align_capacity(T, k, E_loc, block_m) if capacity is None else int(capacity)
+    dev = topk_ids.device
+    sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+    expert_ids = torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev)
+    ntp = torch.empty(1, dtype=torch.int32, device=dev)
+    check(load().w4a16_moe_align(topk_ids.data_ptr(), T, k, E_glob, first_expert, E_loc, block_m,
+                                 sorted_ids.data_ptr(), expert_ids.data_ptr(), ntp.data_ptr(), cap,
+                                 int(bool(validate)), _stream(dev)))
+    return Routing(sorted_ids, expert_ids, ntp, block_m, topk_ids, E_glob, first_expert, E_loc)
+
+
+def select(T: int, topk: int, E_glob: int, E_loc: int, N: int, K: int) -> Config:
+    c = Config()
+    check(load().w4a16_select(T, topk, E_glob, E_loc, N, K, ctypes.byref(c)))
+    return c
+
+
+def config(block_m: int, nr: int, waves: int = 4, split_k: int = 1) -> Config:
+    return Config(block_m, nr, waves, split_k)
+
+
+def workspace_bytes(T: int, topk: int, N: int, combine: bool) -> int:
+    return int(load().w4a16_moe_gemm_workspace_bytes(T, topk, N, int(bool(combine))))
+
+
+def moe_w4a16_gemm(a: torch.Tensor, packed: PackedW4, routing: Routing,
+                   topk_weights: Optional[torch.Tensor] = None, a_per_slot: Optional[bool] = None,
+                   cfg: Optional[Config] = None, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Indexed MoE GEMM.  Without topk_weights: out[T*k, N] per routed slot
+    (only local slots written).  With topk_weights float32 [T, k]: out[T, N]
+    top-k-weighted combine.  a_per_slot defaults to (topk_weights given)."""
+    _need(a, "a", _BF16, 2)
+    T, k = routing.T, routing.topk
+    if a_per_slot is None:
+        a_per_slot = topk_weights is not None
+    if a.shape[1] != packed.K:
+        raise ValueError(f"a has K={a.shape[1]}, weight has K={packed.K}")
+    dev = a.device
+    combine = topk_weights is not None
+    if combine:
+        _need(topk_weights, "topk_weights", (torch.float32,), 2)
+        rows = T
+    else:
+        rows = T * k
+    if out is None:
+        out = (torch.zeros if not combine else torch.empty)(rows, packed.N, dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", _BF16, 2)
+        if out.shape[0] < rows or out.shape[1] != packed.N:
+            raise ValueError(f"out must be [{rows}, {packed.N}]")
+    nws = workspace_bytes(T, k, packed.N, combine)
+    if combine and workspace is None:
+        workspace = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+    r = routing.as_c()
+    check(load().w4a16_moe_gemm(ctypes.byref(packed.desc), packed.w.data_ptr(), packed.s.data_ptr(),
+                                a.data_ptr(), a.shape[0], int(bool(a_per_slot)), ctypes.byref(r),
+                                _ptr(topk_weights), out.data_ptr(),
+                                None if cfg is None else ctypes.byref(cfg),
+                                _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                _stream(dev)))
+    return out
+
+
+def grouped_contiguous(a: torch.Tensor, packed: PackedW4, m_indices: torch.Tensor,
+                       cfg: Optional[Config] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """a [m, K] (experts' rows back to back, 128-row aligned segments),
+    m_indices int32 [m] (-1 on padding) -> out [m, N]."""
+    _need(a, "a", _BF16, 2)
+    _need(m_indices, "m_indices", (torch.int32,), 1)
+    m = a.shape[0]
+    if m_indices.shape[0] != m or a.shape[1] != packed.K:
+        raise ValueError("a / m_indices / weight shapes disagree")
+    if out is None:
+        out = torch.zeros(m, packed.N, dtype=torch.bfloat16, device=a.device)
+    check(load().w4a16_grouped_contiguous(ctypes.byref(packed.desc), packed.w.data_ptr(),
+                                          packed.s.data_ptr(), a.data_ptr(), m, m_indices.data_ptr(),
+                                          out.data_ptr(), None if cfg is None else ctypes.byref(cfg),
+                                          _stream(a.device)))
+    return out
+
+
+def grouped_masked(a: torch.Tensor, packed: PackedW4, masked_m: torch.Tensor, expected_m: int,
+                   cfg: Optional[Config] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """a [E, max_m, K], masked_m int32 [E] -> out flat [E * max_m, N]."""
+    _need(a, "a", _BF16, 3)
+    _need(masked_m, "masked_m", (torch.int32,), 1)
+    G, max_m, K = a.shape
+    if G != packed.E or K != packed.K or masked_m.shape[0] != G:
+        raise ValueError("a / masked_m / weight shapes disagree")
+    if out is None:
+        out = torch.zeros(G * max_m, packed.N, dtype=torch.bfloat16, device=a.device)
+    check(load().w4a16_grouped_masked(ctypes.byref(packed.desc), packed.w.data_ptr(),
+                                      packed.s.data_ptr(), a.data_ptr(), max_m, masked_m.data_ptr(),
+                                      int(expected_m), out.data_ptr(),
+                                      None if cfg is None else ctypes.byref(cfg), _stream(a.device)))
+    return out
+
+
+__all__ = [
+    "W4A16Error", "PackedW4", "Routing", "Config", "weight_desc", "pack_w4", "align_capacity",
+    "moe_align", "select", "config", "workspace_bytes", "moe_w4a16_gemm", "grouped_contiguous",
+    "grouped_masked",
+]

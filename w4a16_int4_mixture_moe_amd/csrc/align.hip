@@ -1,0 +1,139 @@
+// Routing align for the indexed MoE GEMM: a stable counting sort of routed
+// slots by local expert, padded per expert to a multiple of block_m with a
+// sentinel slot id.
+//
+// Chord W4A16 MoE post (vLLM x Novita AI), section "Two kernel families": the
+// indexed family consumes sorted_ids / expert_ids / num_tokens_padded; section
+// "vLLM integration": the buffers are over-allocated so no count is read back
+// to the host and the call stays graph-capturable; section "Grouped SM90
+// kernels", Figure 3: indexed routing puts its padding in sentinel indices.
+//
+// One workgroup of 8 waves.  Wave w owns a contiguous range of slots, so the
+// order of slots inside an expert segment is ascending by construction:
+//   pass 1  each wave counts its slots per expert (LDS atomics);
+//   scan    per expert, exclusive prefix over waves, then an exclusive scan of
+//           the padded expert totals gives segment starts;
+//   fill    sentinels inside segment tails and after the padded total,
+//           expert_ids per block, the padded total itself;
+//   pass 2  each wave walks its range 64 slots at a time; lanes routed to the
+//           same expert find each other with one ballot per expert-id bit,
+//           take consecutive positions in lane order, and the group's lowest
+//           lane advances the wave's cursor for that expert.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace w4a16 {
+
+constexpr int kAlignWaves = 8;
+constexpr int kAlignThreads = kAlignWaves * kWave;
+
+__global__ __launch_bounds__(kAlignThreads) void align_kernel(
+    const int32_t* __restrict__ topk_ids, int32_t total, int32_t first, int32_t E_loc,
+    int32_t bm, int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
+    int32_t* __restrict__ ntp_out, int64_t capacity) {
+  extern __shared__ int smem[];
+  int* cnt = smem;                            // [kAlignWaves][E_loc]: counts, then cursors
+  int* seg = smem + kAlignWaves * E_loc;      // [E_loc + 1]: padded segment starts
+  int* num = seg + E_loc + 1;                 // [E_loc]: slots per expert
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = tid / kWave;
+
+  for (int i = tid; i < kAlignWaves * E_loc; i += kAlignThreads) cnt[i] = 0;
+  __syncthreads();
+
+  const int per = ((total + kAlignWaves - 1) / kAlignWaves + kWave - 1) & ~(kWave - 1);
+  const int beg = min(w * per, total);
+  const int end = min(beg + per, total);
+
+  // pass 1: per-wave expert histogram
+  for (int s = beg + lane; s < end; s += kWave) {
+    const int e = topk_ids[s] - first;
+    if ((unsigned)e < (unsigned)E_loc) atomicAdd(&cnt[w * E_loc + e], 1);
+  }
+  __syncthreads();
+
+  // per expert: exclusive prefix over waves, total count
+  for (int e = tid; e < E_loc; e += kAlignThreads) {
+    int run = 0;
+    for (int v = 0; v < kAlignWaves; ++v) {
+      const int c = cnt[v * E_loc + e];
+      cnt[v * E_loc + e] = run;
+      run += c;
+    }
+    num[e] = run;
+  }
+  __syncthreads();
+
+  // exclusive scan of padded totals (wave 0; each lane a run of experts)
+  if (w == 0) {
+    const int per_lane = (E_loc + kWave - 1) / kWave;
+    const int e0 = min(lane * per_lane, E_loc);
+    const int e1 = min(e0 + per_lane, E_loc);
+    int mine = 0;
+    for (int e = e0; e < e1; ++e) mine += (num[e] + bm - 1) / bm * bm;
+    int incl = mine;
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    int run = incl - mine;
+    for (int e = e0; e < e1; ++e) {
+      seg[e] = run;
+      run += (num[e] + bm - 1) / bm * bm;
+    }
+    if (lane == kWave - 1) seg[E_loc] = incl;
+  }
+  __syncthreads();
+
+  const int ntp = seg[E_loc];
+  const int sentinel = total;
+  for (int i = tid; i < kAlignWaves * E_loc; i += kAlignThreads) cnt[i] += seg[i % E_loc];
+  for (int e = tid; e < E_loc; e += kAlignThreads) {
+    const int o = seg[e], n = num[e], o_end = seg[e + 1];
+    for (int q = o + n; q < o_end; ++q) sorted_ids[q] = sentinel;
+    for (int b = o / bm; b < o_end / bm; ++b) expert_ids[b] = e;
+  }
+  for (int64_t q = ntp + tid; q < capacity; q += kAlignThreads) sorted_ids[q] = sentinel;
+  for (int64_t b = ntp / bm + tid; b < capacity / bm; b += kAlignThreads) expert_ids[b] = -1;
+  if (tid == 0) *ntp_out = ntp;
+  __syncthreads();
+
+  // pass 2: stable scatter
+  const int nbits = 32 - __clz(max(E_loc - 1, 1));
+  const uint64_t lanes_below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+  for (int base = beg; base < end; base += kWave) {
+    const int s = base + lane;
+    int e = -1;
+    if (s < end) e = topk_ids[s] - first;
+    const bool loc = (s < end) && ((unsigned)e < (unsigned)E_loc);
+    uint64_t peers = __ballot(loc);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = loc && ((e >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    int cur = 0;
+    if (loc) {
+      cur = cnt[w * E_loc + e];
+      sorted_ids[cur + __popcll(peers & lanes_below)] = s;
+    }
+    // every lane has read its cursor before any lane of this wave updates it
+    __builtin_amdgcn_wave_barrier();
+    if (loc && (peers & lanes_below) == 0) cnt[w * E_loc + e] = cur + __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+hipError_t launch_align(const int32_t* topk_ids, int32_t total_slots, int32_t first, int32_t E_loc,
+                        int32_t block_m, int32_t* sorted_ids, int32_t* expert_ids,
+                        int32_t* num_tokens_padded, int64_t capacity, hipStream_t stream) {
+  const size_t lds = sizeof(int) * ((size_t)kAlignWaves * E_loc + 2 * (size_t)E_loc + 1);
+  hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), lds, stream, topk_ids,
+                     total_slots, first, E_loc, block_m, sorted_ids, expert_ids,
+                     num_tokens_padded, capacity);
+  return hipGetLastError();
+}
+
+}  // namespace w4a16

@@ -1,0 +1,425 @@
+// C ABI of the W4A16 MoE expert GEMM (declared in include/w4a16_moe.h):
+// argument validation, tile-configuration selection and kernel dispatch.
+// Every check runs on the host before anything is enqueued; no entry point
+// allocates device memory.
+#include "w4a16_moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <random>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+w4a16_status fail(w4a16_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+w4a16_status hip_fail(hipError_t e, const char* what) {
+  return fail(W4A16_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+uint64_t desc_checksum(const w4a16_weight_desc& d) {
+  // FNV-1a over every field before `check`
+  const unsigned char* b = reinterpret_cast<const unsigned char*>(&d);
+  uint64_t h = 1469598103934665603ull;
+  for (size_t i = 0; i < offsetof(w4a16_weight_desc, check); ++i) {
+    h ^= b[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+w4a16_weight_desc make_desc(int32_t E, int32_t N, int32_t K) {
+  w4a16_weight_desc d;
+  std::memset(&d, 0, sizeof d);
+  d.magic = W4A16_DESC_MAGIC;
+  d.version = W4A16_DESC_VERSION;
+  d.E = E;
+  d.N = N;
+  d.K = K;
+  d.K_pad = (int32_t)round_up(K, 128);
+  const int64_t KC = d.K_pad / 128;
+  d.scale_cols = (int32_t)round_up(KC, 8);
+  d.group = 32;
+  const int64_t NT = N / 16;
+  d.w_bytes = (uint64_t)E * NT * KC * 1024;
+  d.s_bytes = (uint64_t)E * NT * 64 * d.scale_cols * 2;
+  d.check = desc_checksum(d);
+  return d;
+}
+
+w4a16_status check_shape(int32_t E, int32_t N, int32_t K) {
+  if (E <= 0 || N <= 0 || K <= 0) return fail(W4A16_ERR_ARG, "E, N, K must be positive (got %d, %d, %d)", E, N, K);
+  if (K % 32) return fail(W4A16_ERR_SHAPE, "K = %d is not a multiple of the scale group 32", K);
+  if (N % 16) return fail(W4A16_ERR_SHAPE, "N = %d is not a multiple of 16", N);
+  if ((int64_t)K * 2 > INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "K = %d too large", K);
+  return W4A16_OK;
+}
+
+w4a16_status check_desc(const w4a16_weight_desc* d) {
+  if (d == nullptr) return fail(W4A16_ERR_ARG, "weight descriptor is NULL");
+  if (d->magic != W4A16_DESC_MAGIC || d->version != W4A16_DESC_VERSION)
+    return fail(W4A16_ERR_LAYOUT, "weight descriptor has a wrong magic/version (not from w4a16_weight_desc_init?)");
+  if (d->check != desc_checksum(*d)) return fail(W4A16_ERR_LAYOUT, "weight descriptor checksum mismatch (corrupted)");
+  w4a16_status st = check_shape(d->E, d->N, d->K);
+  if (st != W4A16_OK) return fail(W4A16_ERR_LAYOUT, "weight descriptor shape invalid: %s", g_last_error.c_str());
+  const w4a16_weight_desc ref = make_desc(d->E, d->N, d->K);
+  if (std::memcmp(&ref, d, sizeof ref) != 0) return fail(W4A16_ERR_LAYOUT, "weight descriptor fields inconsistent");
+  return W4A16_OK;
+}
+
+bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+// ---------------------------------------------------------------- selection
+//
+// Chord W4A16 MoE post, section "H200 prefill and TP8": block_m is chosen from
+// tokens per expert tok_e = routed rows / experts; below about 80 a search
+// minimises the total number of blocks on sampled routing, above it the
+// padded expert rows are fitted under a maximum block_m.  On gfx950 the
+// kernel skips 16-row token tiles that hold no valid row, so MFMA work
+// follows valid rows whatever block_m is, while every extra block of an
+// expert re-reads and re-dequantises its weights.  So:
+//   - decode side (tok_e < kPrefillTokE): sample per-expert counts, pick the
+//     smallest block_m whose total block count is within 2 % of the minimum
+//     (smaller blocks keep fewer accumulators live and more waves resident);
+//   - prefill side: block_m 128 (largest tile the accumulators allow), 4
+//     weight tiles per wave so each staged activation fragment feeds 4 MFMAs.
+constexpr double kPrefillTokE = 48.0;
+
+std::mutex g_cache_mu;
+std::map<std::tuple<int, int, int, int, int, int>, w4a16_config> g_cache;
+
+int64_t sampled_blocks(const std::vector<int>& counts, int bm) {
+  int64_t b = 0;
+  for (int c : counts) b += (c + bm - 1) / bm;
+  return b;
+}
+
+w4a16_config select_config(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc) {
+  w4a16_config c;
+  c.waves = 4;
+  c.split_k = 1;
+  const double tok_e = (double)T * topk / std::max(E_glob, 1);
+  if (tok_e >= kPrefillTokE) {
+    c.block_m = 128;
+    c.nr = 4;
+    return c;
+  }
+  // sampled routing: each of T*topk slots lands on one of E_glob experts
+  // uniformly; keep the local ones (fixed seed: deterministic choice)
+  std::mt19937 rng(12345u);
+  std::vector<int> counts(std::max(E_loc, 1), 0);
+  std::binomial_distribution<int> bin(std::max(T, 0) * std::max(topk, 1), 1.0 / std::max(E_glob, 1));
+  for (int e = 0; e < E_loc; ++e) counts[e] = bin(rng);
+  const int cands[3] = {16, 32, 64};
+  int64_t best = INT64_MAX;
+  for (int bm : cands) best = std::min(best, sampled_blocks(counts, bm));
+  c.block_m = 64;
+  for (int bm : cands)
+    if (sampled_blocks(counts, bm) * 100 <= best * 102) {
+      c.block_m = bm;
+      break;
+    }
+  c.nr = 2;
+  return c;
+}
+
+const char* env_str(const char* name) {
+  const char* v = std::getenv(name);
+  return (v && *v) ? v : nullptr;
+}
+
+// W4A16_BLOCK_M / W4A16_NR override the selector (read on every call; the
+// memoised result is the selector's, overrides are applied on top).
+void apply_env_overrides(w4a16_config* c) {
+  if (const char* v = env_str("W4A16_BLOCK_M")) c->block_m = std::atoi(v);
+  if (const char* v = env_str("W4A16_NR")) c->nr = std::atoi(v);
+}
+
+w4a16_status check_config(const w4a16_config& c, int route, int epi) {
+  if (!valid_block_m(c.block_m)) return fail(W4A16_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128}", c.block_m);
+  if (c.split_k != 1) return fail(W4A16_ERR_UNSUPPORTED, "split_k %d: only 1 is built", c.split_k);
+  if (!w4a16::gemm_config_supported(route, epi, c.block_m / 16, c.nr, c.waves))
+    return fail(W4A16_ERR_UNSUPPORTED, "tile config block_m=%d nr=%d waves=%d not built", c.block_m, c.nr, c.waves);
+  return W4A16_OK;
+}
+
+w4a16::GemmParams base_params(const w4a16_weight_desc* d, const void* pw, const void* ps,
+                              const uint16_t* a, void* out, int nr, int waves) {
+  w4a16::GemmParams p;
+  std::memset(&p, 0, sizeof p);
+  p.packed_w = static_cast<const uint4*>(pw);
+  p.packed_s = static_cast<const uint16_t*>(ps);
+  p.a = a;
+  p.E = d->E;
+  p.N = d->N;
+  p.K = d->K;
+  p.NT = d->N / 16;
+  p.KC = d->K_pad / 128;
+  p.SC = d->scale_cols;
+  const int tiles_per_wg = nr * waves;
+  p.n_tiles = (p.NT + tiles_per_wg - 1) / tiles_per_wg;
+  p.out = out;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a16_last_error(void) { return g_last_error.c_str(); }
+
+int32_t w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+w4a16_status w4a16_weight_desc_init(int32_t E, int32_t N, int32_t K, w4a16_weight_desc* out) {
+  if (out == nullptr) return fail(W4A16_ERR_ARG, "out is NULL");
+  w4a16_status st = check_shape(E, N, K);
+  if (st != W4A16_OK) return st;
+  *out = make_desc(E, N, K);
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_pack_w4(const uint8_t* codes, const uint16_t* scales,
+                           const w4a16_weight_desc* desc, void* packed_w, void* packed_s,
+                           w4a16_stream_t stream) {
+  w4a16_status st = check_desc(desc);
+  if (st != W4A16_OK) return st;
+  if (!codes || !scales || !packed_w || !packed_s) return fail(W4A16_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(packed_w) || !aligned16(packed_s)) return fail(W4A16_ERR_ARG, "packed buffers must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(scales) & 1u) return fail(W4A16_ERR_ARG, "scales must be 2-byte aligned");
+  hipError_t e = w4a16::launch_pack(codes, scales, desc->E, desc->N, desc->K, desc->K_pad / 128,
+                                    desc->scale_cols, static_cast<uint32_t*>(packed_w),
+                                    static_cast<uint16_t*>(packed_s), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pack_w4 launch");
+  return W4A16_OK;
+}
+
+int64_t w4a16_align_capacity(int32_t T, int32_t topk, int32_t E_loc, int32_t block_m) {
+  if (T < 0 || topk <= 0 || E_loc <= 0 || !valid_block_m(block_m)) return -1;
+  return round_up((int64_t)T * topk + (int64_t)E_loc * (block_m - 1), block_m);
+}
+
+w4a16_status w4a16_moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t E_glob,
+                             int32_t first_expert, int32_t E_loc, int32_t block_m,
+                             int32_t* sorted_ids, int32_t* expert_ids,
+                             int32_t* num_tokens_padded, int64_t capacity, int32_t validate,
+                             w4a16_stream_t stream) {
+  if (!sorted_ids || !expert_ids || !num_tokens_padded || (T > 0 && !topk_ids))
+    return fail(W4A16_ERR_ARG, "NULL pointer argument");
+  if (T < 0 || topk <= 0 || E_glob <= 0 || E_loc <= 0 || first_expert < 0)
+    return fail(W4A16_ERR_ARG, "bad sizes T=%d topk=%d E_glob=%d first=%d E_loc=%d", T, topk, E_glob, first_expert, E_loc);
+  if ((int64_t)first_expert + E_loc > E_glob)
+    return fail(W4A16_ERR_ARG, "local experts [%d, %d) exceed E_glob=%d", first_expert, first_expert + E_loc, E_glob);
+  if (E_loc > 1024) return fail(W4A16_ERR_SHAPE, "E_loc=%d > 1024 not supported", E_loc);
+  if (!valid_block_m(block_m)) return fail(W4A16_ERR_SHAPE, "block_m %d not in {16, 32, 64, 128}", block_m);
+  if ((int64_t)T * topk >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "T*topk too large");
+  const int64_t need = w4a16_align_capacity(T, topk, E_loc, block_m);
+  if (capacity < need || capacity % block_m)
+    return fail(W4A16_ERR_CAPACITY, "capacity %lld < %lld needed (or not a multiple of block_m %d)",
+                (long long)capacity, (long long)need, block_m);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate && T > 0) {
+    std::vector<int32_t> h((size_t)T * topk);
+    hipError_t e = hipMemcpyAsync(h.data(), topk_ids, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "moe_align validate readback");
+    for (size_t i = 0; i < h.size(); ++i)
+      if (h[i] < 0 || h[i] >= E_glob)
+        return fail(W4A16_ERR_ROUTING, "topk_ids[%zu] = %d outside [0, %d)", i, h[i], E_glob);
+  }
+  hipError_t e = w4a16::launch_align(topk_ids, T * topk, first_expert, E_loc, block_m, sorted_ids,
+                                     expert_ids, num_tokens_padded, capacity, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_align launch");
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N,
+                          int32_t K, w4a16_config* out) {
+  if (!out) return fail(W4A16_ERR_ARG, "out is NULL");
+  if (T < 0 || topk <= 0 || E_glob <= 0 || E_loc <= 0 || N <= 0 || K <= 0)
+    return fail(W4A16_ERR_ARG, "bad sizes for select");
+  const auto key = std::make_tuple(T, topk, E_glob, E_loc, N, K);
+  {
+    std::lock_guard<std::mutex> g(g_cache_mu);
+    auto it = g_cache.find(key);
+    if (it != g_cache.end()) {
+      *out = it->second;
+      apply_env_overrides(out);
+      return W4A16_OK;
+    }
+  }
+  w4a16_config c = select_config(T, topk, E_glob, E_loc);
+  {
+    std::lock_guard<std::mutex> g(g_cache_mu);
+    g_cache[key] = c;
+  }
+  *out = c;
+  apply_env_overrides(out);
+  return W4A16_OK;
+}
+
+size_t w4a16_moe_gemm_workspace_bytes(int32_t T, int32_t topk, int32_t N, int32_t combine) {
+  if (!combine || T <= 0 || topk <= 0 || N <= 0) return 0;
+  return (size_t)T * topk * N * sizeof(float);
+}
+
+w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
+                            const void* packed_s, const uint16_t* a, int64_t a_rows,
+                            int32_t a_per_slot, const w4a16_indexed_routing* routing,
+                            const float* topk_weights, uint16_t* out,
+                            const w4a16_config* cfg, void* workspace, size_t workspace_bytes,
+                            w4a16_stream_t stream) {
+  w4a16_status st = check_desc(desc);
+  if (st != W4A16_OK) return st;
+  if (!routing) return fail(W4A16_ERR_ARG, "routing is NULL");
+  const w4a16_indexed_routing& r = *routing;
+  const bool combine = topk_weights != nullptr;
+  if (!packed_w || !packed_s || !r.sorted_ids || !r.expert_ids || !r.num_tokens_padded)
+    return fail(W4A16_ERR_ARG, "NULL pointer argument");
+  if (r.T < 0 || r.topk <= 0 || r.capacity < 0) return fail(W4A16_ERR_ARG, "bad routing sizes");
+  if (r.T > 0 && (!a || !out)) return fail(W4A16_ERR_ARG, "activations or output are NULL");
+  if (!aligned16(packed_w) || !aligned16(packed_s) || !aligned16(a) || !aligned16(out))
+    return fail(W4A16_ERR_ARG, "packed weights, activations and output must be 16-byte aligned");
+  if (r.E_loc != desc->E)
+    return fail(W4A16_ERR_LAYOUT, "routing has E_loc=%d but the packed weight holds %d experts", r.E_loc, desc->E);
+  const int64_t need_rows = a_per_slot ? (int64_t)r.T * r.topk : r.T;
+  if (a_rows < need_rows)
+    return fail(W4A16_ERR_SHAPE, "activations have %lld rows, need %lld", (long long)a_rows, (long long)need_rows);
+  if ((int64_t)r.T * r.topk >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "T*topk too large");
+  w4a16_config c;
+  if (cfg) {
+    c = *cfg;
+  } else {
+    // the routing buffers fix block_m; the rest follows from it
+    c.block_m = r.block_m;
+    c.nr = r.block_m >= 64 ? 4 : 2;
+    c.waves = 4;
+    c.split_k = 1;
+    apply_env_overrides(&c);
+  }
+  const int epi = combine ? w4a16::kEpiWeighted : w4a16::kEpiStore;
+  st = check_config(c, w4a16::kRouteIndexed, epi);
+  if (st != W4A16_OK) return st;
+  if (c.block_m != r.block_m)
+    return fail(W4A16_ERR_LAYOUT, "config block_m=%d differs from the routing's block_m=%d", c.block_m, r.block_m);
+  if (r.capacity % r.block_m) return fail(W4A16_ERR_CAPACITY, "capacity not a multiple of block_m");
+  if (combine) {
+    if (!r.topk_ids) return fail(W4A16_ERR_ARG, "combine needs routing.topk_ids");
+    const size_t need = w4a16_moe_gemm_workspace_bytes(r.T, r.topk, desc->N, 1);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+      return fail(W4A16_ERR_WORKSPACE, "combine needs %zu bytes of 16-byte aligned workspace, got %zu", need, workspace_bytes);
+  }
+  if (r.T == 0) return W4A16_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  w4a16::GemmParams p = base_params(desc, packed_w, packed_s, a, combine ? workspace : (void*)out, c.nr, c.waves);
+  p.sorted_ids = r.sorted_ids;
+  p.expert_ids = r.expert_ids;
+  p.num_tokens_padded = r.num_tokens_padded;
+  p.sentinel = r.T * r.topk;
+  p.a_row_div = a_per_slot ? 1 : r.topk;
+  p.slot_weight = topk_weights;
+  hipError_t e = w4a16::launch_gemm(w4a16::kRouteIndexed, epi, c.block_m / 16, c.nr, c.waves, p,
+                                    r.capacity / r.block_m, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_gemm launch");
+  if (combine) {
+    e = w4a16::launch_combine(static_cast<const float*>(workspace), r.topk_ids, r.T, r.topk,
+                              r.first_expert, r.E_loc, desc->N, out, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_grouped_contiguous(const w4a16_weight_desc* desc, const void* packed_w,
+                                      const void* packed_s, const uint16_t* a, int64_t m_rows,
+                                      const int32_t* m_indices, uint16_t* out,
+                                      const w4a16_config* cfg, w4a16_stream_t stream) {
+  w4a16_status st = check_desc(desc);
+  if (st != W4A16_OK) return st;
+  if (m_rows < 0) return fail(W4A16_ERR_ARG, "m_rows < 0");
+  if (m_rows > 0 && (!a || !m_indices || !out)) return fail(W4A16_ERR_ARG, "NULL pointer argument");
+  if (!packed_w || !packed_s) return fail(W4A16_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(packed_w) || !aligned16(packed_s) || !aligned16(a) || !aligned16(out))
+    return fail(W4A16_ERR_ARG, "packed weights, activations and output must be 16-byte aligned");
+  w4a16_config c;
+  if (cfg) {
+    c = *cfg;
+  } else {
+    c.block_m = 128; c.nr = 4; c.waves = 4; c.split_k = 1;
+    apply_env_overrides(&c);
+  }
+  st = check_config(c, w4a16::kRouteContiguous, w4a16::kEpiStore);
+  if (st != W4A16_OK) return st;
+  if (128 % c.block_m) return fail(W4A16_ERR_UNSUPPORTED, "contiguous layout needs block_m dividing 128");
+  if (m_rows % c.block_m) return fail(W4A16_ERR_SHAPE, "m_rows=%lld is not a multiple of block_m=%d (segments are 128-row aligned)", (long long)m_rows, c.block_m);
+  if (m_rows >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "m_rows too large");
+  if (m_rows == 0) return W4A16_OK;
+  w4a16::GemmParams p = base_params(desc, packed_w, packed_s, a, out, c.nr, c.waves);
+  p.m_indices = m_indices;
+  hipError_t e = w4a16::launch_gemm(w4a16::kRouteContiguous, w4a16::kEpiStore, c.block_m / 16, c.nr,
+                                    c.waves, p, m_rows / c.block_m, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "grouped_contiguous launch");
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_grouped_masked(const w4a16_weight_desc* desc, const void* packed_w,
+                                  const void* packed_s, const uint16_t* a, int32_t max_m,
+                                  const int32_t* masked_m, int32_t expected_m, uint16_t* out,
+                                  const w4a16_config* cfg, w4a16_stream_t stream) {
+  w4a16_status st = check_desc(desc);
+  if (st != W4A16_OK) return st;
+  if (max_m <= 0) return fail(W4A16_ERR_ARG, "max_m must be positive");
+  if (!a || !masked_m || !out || !packed_w || !packed_s) return fail(W4A16_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(packed_w) || !aligned16(packed_s) || !aligned16(a) || !aligned16(out))
+    return fail(W4A16_ERR_ARG, "packed weights, activations and output must be 16-byte aligned");
+  if ((int64_t)desc->E * max_m >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "E * max_m too large");
+  w4a16_config c;
+  if (cfg) {
+    c = *cfg;
+  } else {
+    if (expected_m <= 0) return fail(W4A16_ERR_ARG, "expected_m must be positive");
+    // chosen from the expected rows per group (post, section "Grouped SM90
+    // kernels": masked decode picks BLOCK_M from the expected tokens per expert)
+    const int want = (int)round_up(std::min(expected_m, 128), 16);
+    c.block_m = want <= 16 ? 16 : want <= 32 ? 32 : want <= 64 ? 64 : 128;
+    c.nr = c.block_m >= 64 ? 4 : 2;
+    c.waves = 4;
+    c.split_k = 1;
+    apply_env_overrides(&c);
+  }
+  st = check_config(c, w4a16::kRouteMasked, w4a16::kEpiStore);
+  if (st != W4A16_OK) return st;
+  w4a16::GemmParams p = base_params(desc, packed_w, packed_s, a, out, c.nr, c.waves);
+  p.masked_m = masked_m;
+  p.max_m = max_m;
+  p.blocks_per_group = (max_m + c.block_m - 1) / c.block_m;
+  hipError_t e = w4a16::launch_gemm(w4a16::kRouteMasked, w4a16::kEpiStore, c.block_m / 16, c.nr,
+                                    c.waves, p, (int64_t)desc->E * p.blocks_per_group,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "grouped_masked launch");
+  return W4A16_OK;
+}
+
+}  // extern "C"

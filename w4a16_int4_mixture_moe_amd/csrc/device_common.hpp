@@ -1,0 +1,64 @@
+// Device-side types and helpers shared by the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 32;        // K elements per scale
+constexpr int kChunk = 128;       // K elements per packed chunk (4 scale groups)
+constexpr int kRowTile = 16;      // weight rows per MFMA tile
+constexpr int kWave = 64;
+
+// Dequantise the 8 INT4 codes of one packed word into the bf16 MFMA operand
+// fragment, value e = bf16_rne((q_e - 8) * s).
+//
+// Subtract-then-scale with one BF16 rounding (Chord W4A16 MoE post, section
+// "H200 and Blackwell indexed decode": the fused dequant keeps the unfused
+// BF16 rounding order).  Code e sits at bit 4*(e/2) + 16*(e%2) of the word, so
+// one AND + OR turns two codes into the fp16 values 1024 + q (low nibble of a
+// half) or 1024 + 16 q (high nibble); v_fma_mix_f32 then forms, exactly,
+//   (1024 + q) * s - 1032 s  =  (q - 8) s
+//   (1024 + 16 q) * (s / 16) - 72 s  =  (q - 8) s
+// (the fma rounds once and (q - 8) s fits fp32 exactly: a 4-bit integer times
+// an 8-bit significand), and v_cvt_pk_bf16_f32 rounds that to bf16, nearest
+// even.  c0 = -1032 s, s16 = s / 16, c1 = -72 s are exact for any scale with
+// 2^-100 < |s| < 2^100.
+__device__ __forceinline__ bf16x8_t dequant8(uint32_t d, float s, float c0, float s16, float c1) {
+  const uint32_t magic = 0x64006400u;
+  const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u;
+  const uint32_t d8 = d >> 8;
+  const f16x2_t h0 = __builtin_bit_cast(f16x2_t, (d & lo) | magic);
+  const f16x2_t h1 = __builtin_bit_cast(f16x2_t, (d & hi) | magic);
+  const f16x2_t h2 = __builtin_bit_cast(f16x2_t, (d8 & lo) | magic);
+  const f16x2_t h3 = __builtin_bit_cast(f16x2_t, (d8 & hi) | magic);
+  bf16x8_t r;
+  r[0] = (__bf16)__builtin_fmaf((float)h0.x, s, c0);
+  r[1] = (__bf16)__builtin_fmaf((float)h0.y, s, c0);
+  r[2] = (__bf16)__builtin_fmaf((float)h1.x, s16, c1);
+  r[3] = (__bf16)__builtin_fmaf((float)h1.y, s16, c1);
+  r[4] = (__bf16)__builtin_fmaf((float)h2.x, s, c0);
+  r[5] = (__bf16)__builtin_fmaf((float)h2.y, s, c0);
+  r[6] = (__bf16)__builtin_fmaf((float)h3.x, s16, c1);
+  r[7] = (__bf16)__builtin_fmaf((float)h3.y, s16, c1);
+  return r;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) {
+  return __builtin_bit_cast(float, b16 << 16);
+}
+
+// Two fp32 -> packed bf16x2 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+}  // namespace w4a16

@@ -1,0 +1,58 @@
+// Host-side launchers of the gfx950 kernels (internal to the library; the
+// public entry points in api.cpp validate arguments before calling these).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+// ---- routing align (align.hip)
+hipError_t launch_align(const int32_t* topk_ids, int32_t total_slots, int32_t first, int32_t E_loc,
+                        int32_t block_m, int32_t* sorted_ids, int32_t* expert_ids,
+                        int32_t* num_tokens_padded, int64_t capacity, hipStream_t stream);
+
+// ---- packer (pack.hip)
+hipError_t launch_pack(const uint8_t* codes, const uint16_t* scales, int32_t E, int32_t N,
+                       int32_t K, int32_t KC, int32_t SC, uint32_t* packed_w,
+                       uint16_t* packed_s, hipStream_t stream);
+
+// ---- GEMM (gemm.hip)
+enum RouteKind : int { kRouteIndexed = 0, kRouteContiguous = 1, kRouteMasked = 2 };
+enum EpilogueKind : int { kEpiStore = 0, kEpiWeighted = 1 };
+
+struct GemmParams {
+  const uint4* packed_w;        // [E][NT][KC][64][4 words]
+  const uint16_t* packed_s;     // [E][NT][64][SC]
+  const uint16_t* a;            // bf16 activations, row stride K
+  int32_t E, N, K, NT, KC, SC;
+  int32_t n_tiles;              // workgroup tiles along N
+  // indexed
+  const int32_t* sorted_ids;
+  const int32_t* expert_ids;
+  const int32_t* num_tokens_padded;
+  int32_t sentinel;             // T * topk
+  int32_t a_row_div;            // topk (rows per token) or 1 (rows per slot)
+  const float* slot_weight;     // weighted epilogue: topk weights, one per slot
+  // contiguous
+  const int32_t* m_indices;
+  // masked
+  const int32_t* masked_m;
+  int32_t max_m;
+  int32_t blocks_per_group;
+  // output: bf16 [rows][N] (store) or fp32 [rows][N] (weighted)
+  void* out;
+};
+
+// m_tiles: 16-row token tiles per block (block_m / 16); nr: 16-row weight
+// tiles per wave; waves: waves per workgroup; grid_blocks: routed blocks.
+hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves,
+                       const GemmParams& p, int64_t grid_blocks, hipStream_t stream);
+bool gemm_config_supported(int route, int epilogue, int m_tiles, int nr, int waves);
+
+// ---- combine of weighted per-slot partials (gemm.hip)
+hipError_t launch_combine(const float* partial, const int32_t* topk_ids, int32_t T, int32_t topk,
+                          int32_t first, int32_t E_loc, int32_t N, uint16_t* out,
+                          hipStream_t stream);
+
+}  // namespace w4a16
