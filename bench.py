@@ -70,6 +70,7 @@ def main() -> int:
     ap.add_argument("--block-m", type=int, default=0, help="override the selector's block_m")
     ap.add_argument("--nr", type=int, default=0, help="override the selector's weight tiles per wave")
     ap.add_argument("--cpu-experts", type=int, default=4, help="experts in the CPU-baseline sample (0: skip)")
+    ap.add_argument("--eager", action="store_true", help="launch the step eagerly instead of replaying a HIP graph")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -118,9 +119,10 @@ def main() -> int:
     L = M.load()
     stream = torch.cuda.current_stream(dev)
     import ctypes
-    s_ptr = ctypes.c_void_p(stream.cuda_stream)
 
     def align():
+        # current stream looked up per call: under graph capture it is the capture stream
+        s_ptr = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         M._lib.check(L.w4a16_moe_align(d_ids.data_ptr(), T, k, sh.E_glob, sh.first, sh.E_loc,
                                        cfg.block_m, sorted_ids.data_ptr(), expert_ids.data_ptr(),
                                        ntp.data_ptr(), cap, 0, s_ptr))
@@ -131,35 +133,60 @@ def main() -> int:
     def down():
         M.moe_w4a16_gemm(d_a, p2, routing, topk_weights=d_w, cfg=cfg, out=y, workspace=ws)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step():
         align()
-        if ev is not None:
-            ev[1].record(stream)
         gate_up()
-        if ev is not None:
-            ev[2].record(stream)
         down()
-        if ev is not None:
-            ev[3].record(stream)
+
+    def graph_of(fn, n):
+        """Capture n back-to-back calls of fn in one HIP graph (torch's
+        capture stream is the current stream inside the context, so the
+        library's launches land in the graph)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        return g
+
+    def timed(g, reps, per):
+        """Average duration of one call: replay g `reps` times between two
+        events on the stream the kernels run on."""
+        s_ = torch.cuda.current_stream(dev)
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g.replay()
+        torch.cuda.synchronize()
+        a_.record(s_)
+        for _ in range(reps):
+            g.replay()
+        b_.record(s_)
+        torch.cuda.synchronize()
+        return a_.elapsed_time(b_) * 1e3 / (reps * per)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    use_graph = not args.eager
+    if use_graph:
+        g_step = graph_of(step, 1)
+        for _ in range(args.warmup):
+            g_step.replay()
+    torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
+    for _ in range(args.steps):
+        if use_graph:
+            g_step.replay()
+        else:
+            step()
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
-    us_align = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
-    us_gu = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
-    us_dn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3
+    # per-kernel averages: each call replayed back to back inside one graph
+    inner = 8
+    us_align = timed(graph_of(align, inner), max(2, args.steps // 4), inner)
+    us_gu = timed(graph_of(gate_up, inner), max(2, args.steps // 4), inner)
+    us_dn = timed(graph_of(down, inner), max(2, args.steps // 4), inner)
 
     flat = ids.reshape(-1)
     local = (flat >= sh.first) & (flat < sh.first + sh.E_loc)
@@ -186,6 +213,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "timing": "HIP graph replay of the step" if use_graph else "eager launches",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -73,7 +73,7 @@ int32_t w4a16_abi_version(void);
  * nothing about the call has to be known when packing.
  *
  * Packed layout (all little-endian), with NT = N / 16, KP = K rounded up to
- * 128, KC = KP / 128, SC = KC rounded up to 8:
+ * 128, KC = KP / 128:
  *   packed_w : uint32 words [E][NT][KC][64 lanes][4 words]
  *     lane l = 16 * g + i holds row n = 16 * tile + i; word j of that lane
  *     holds the 8 codes of K indices kk = 128 * c + 32 * g + 8 * j + e,
@@ -81,10 +81,11 @@ int32_t w4a16_abi_version(void);
  *     are 8 (weight 0).  Each lane's word is exactly one MFMA operand
  *     fragment of 8 consecutive K values, and one lane's four words span one
  *     32-wide scale group.
- *   packed_s : bf16 [E][NT][64 lanes][SC]
- *     entry c of lane l = 16 * g + i is scale[n = 16 * tile + i][4 * c + g]
- *     (0 past K / 32).
- *   packed_w is E * NT * KC * 1024 bytes, packed_s is E * NT * 64 * SC * 2.
+ *   packed_s : bf16 [E][NT][KC][64 lanes]
+ *     lane l = 16 * g + i of (tile, chunk c) holds scale[n = 16 * tile + i]
+ *     [4 * c + g] (0 past K / 32): the one scale its four words need, so a
+ *     wave's scales for one chunk are one 128-byte line.
+ *   packed_w is E * NT * KC * 1024 bytes, packed_s is E * NT * KC * 128.
  * ---------------------------------------------------------------------- */
 #define W4A16_DESC_MAGIC 0x16A4B0E5u /* arbitrary tag */
 #define W4A16_DESC_VERSION 1u
@@ -94,7 +95,7 @@ typedef struct {
   uint32_t version;     /* W4A16_DESC_VERSION */
   int32_t E, N, K;      /* experts, output features, reduction length */
   int32_t K_pad;        /* KP above */
-  int32_t scale_cols;   /* SC above */
+  int32_t chunks;       /* KC above */
   int32_t group;        /* 32 */
   uint64_t w_bytes;     /* size of packed_w */
   uint64_t s_bytes;     /* size of packed_s */

@@ -44,11 +44,11 @@ def test_struct_layouts_match_header():
 def test_version_and_desc(L):
     assert L.w4a16_abi_version() == 1
     d = W.weight_desc(48, 4096, 7168)
-    assert (d.K_pad, d.scale_cols, d.group) == (7168, 56, 32)
+    assert (d.K_pad, d.chunks, d.group) == (7168, 56, 32)
     assert d.w_bytes == 48 * 4096 * 7168 // 2
-    assert d.s_bytes == 48 * 256 * 64 * 56 * 2
+    assert d.s_bytes == 48 * 256 * 56 * 64 * 2
     d = W.weight_desc(2, 32, 96)                         # ragged K: padded to one chunk
-    assert (d.K_pad, d.scale_cols) == (128, 8)
+    assert (d.K_pad, d.chunks) == (128, 1)
 
 
 @pytest.mark.parametrize("E,N,K,code", [(0, 16, 32, -1), (1, 16, 33, -2), (1, 24, 32, -2), (1, 16, -32, -1)])

@@ -73,7 +73,6 @@ def _unpack_cpu(w_bytes: np.ndarray, s_bytes: np.ndarray, E, N, K):
     [E, N, K] and scales [E, N, K/32]."""
     KP = -(-K // 128) * 128
     KC, NT = KP // 128, N // 16
-    SC = -(-KC // 8) * 8
     words = w_bytes.view(np.uint32).reshape(E, NT, KC, 64, 4)
     codes = np.zeros((E, N, KP), np.uint8)
     for l, j, e in itertools.product(range(64), range(4), range(8)):
@@ -82,11 +81,11 @@ def _unpack_cpu(w_bytes: np.ndarray, s_bytes: np.ndarray, E, N, K):
         vals = (words[:, :, :, l, j] >> shift) & 0xF                     # [E, NT, KC]
         kk = np.arange(KC) * 128 + 32 * g + 8 * j + e
         codes[:, np.arange(NT)[:, None] * 16 + i, kk[None, :]] = vals
-    sc = s_bytes.view(np.uint16).reshape(E, NT, 64, SC)
-    scales = np.zeros((E, N, 4 * SC), np.uint16)
+    sc = s_bytes.view(np.uint16).reshape(E, NT, KC, 64)
+    scales = np.zeros((E, N, 4 * KC), np.uint16)
     for l in range(64):
         g, i = divmod(l, 16)
-        scales[:, (np.arange(NT) * 16 + i)[:, None], (4 * np.arange(SC) + g)[None, :]] = sc[:, :, l, :]
+        scales[:, (np.arange(NT) * 16 + i)[:, None], (4 * np.arange(KC) + g)[None, :]] = sc[:, :, :, l]
     return codes, scales
 
 
@@ -307,3 +306,56 @@ def test_grouped_contiguous_and_masked_small():
     h, ok = O.indexed_gate_up(P.x, P.c1, P.s1, P.topk_ids, sh.first, sh.E_loc)
     s = sl3.reshape(-1)
     np.testing.assert_array_equal(ref[valid], h[s[valid]])
+
+
+def test_hip_graph_capture_replays_match_eager():
+    """align + gate/up + down+combine captured in one HIP graph: no host
+    readback or allocation in the path, so replays reproduce the eager
+    outputs bit for bit, also with other eager work between replays."""
+    P = Problem(W.WORKLOADS["tiny"]).upload()
+    sh = P.sh
+    bm = 32
+    cap = M.align_capacity(sh.T, sh.topk, sh.E_loc, bm)
+    r = M.Routing(torch.empty(cap, dtype=torch.int32, device=dev()),
+                  torch.empty(cap // bm, dtype=torch.int32, device=dev()),
+                  torch.empty(1, dtype=torch.int32, device=dev()), bm, P.d_ids, sh.E_glob,
+                  sh.first, sh.E_loc)
+    h = torch.zeros(sh.T * sh.topk, sh.N1, dtype=torch.bfloat16, device=dev())
+    y = torch.empty(sh.T, sh.N2, dtype=torch.bfloat16, device=dev())
+    ws = torch.empty(M.workspace_bytes(sh.T, sh.topk, sh.N2, True), dtype=torch.uint8, device=dev())
+    cfg = M.config(bm, 2)
+
+    def step():
+        rr = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, bm, capacity=cap)
+        r.sorted_ids.copy_(rr.sorted_ids)        # (eager reference path only)
+        return rr
+
+    ref_r = step()
+    ref_h = bits(M.moe_w4a16_gemm(P.d_x, P.p1, ref_r, cfg=cfg))
+    ref_y = bits(M.moe_w4a16_gemm(P.d_a, P.p2, ref_r, topk_weights=P.d_w, cfg=cfg))
+
+    import ctypes
+    L = M.load()
+
+    def captured_step():
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        M._lib.check(L.w4a16_moe_align(P.d_ids.data_ptr(), sh.T, sh.topk, sh.E_glob, sh.first,
+                                       sh.E_loc, bm, r.sorted_ids.data_ptr(), r.expert_ids.data_ptr(),
+                                       r.num_tokens_padded.data_ptr(), cap, 0, s))
+        M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=cfg, out=h)
+        M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=cfg, out=y, workspace=ws)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        captured_step()
+    for rep in range(4):
+        r.sorted_ids.fill_(-5)
+        h.fill_(0)
+        y.fill_(1.0)
+        ws.fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(h), ref_h, err_msg=f"replay {rep}")
+        np.testing.assert_array_equal(bits(y), ref_y, err_msg=f"replay {rep}")
+        _ = (P.d_x.float() @ P.d_x.float().t()).sum().item()   # unrelated eager work

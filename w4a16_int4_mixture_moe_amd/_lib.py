@@ -27,7 +27,7 @@ class WeightDesc(ctypes.Structure):
     _fields_ = [
         ("magic", ctypes.c_uint32), ("version", ctypes.c_uint32),
         ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
-        ("K_pad", ctypes.c_int32), ("scale_cols", ctypes.c_int32), ("group", ctypes.c_int32),
+        ("K_pad", ctypes.c_int32), ("chunks", ctypes.c_int32), ("group", ctypes.c_int32),
         ("w_bytes", ctypes.c_uint64), ("s_bytes", ctypes.c_uint64), ("check", ctypes.c_uint64),
     ]
 

@@ -47,10 +47,19 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   const int beg = min(w * per, total);
   const int end = min(beg + per, total);
 
-  // pass 1: per-wave expert histogram
-  for (int s = beg + lane; s < end; s += kWave) {
-    const int e = topk_ids[s] - first;
-    if ((unsigned)e < (unsigned)E_loc) atomicAdd(&cnt[w * E_loc + e], 1);
+  // pass 1: per-wave expert histogram; 8 loads in flight per lane
+  for (int s0 = beg; s0 < end; s0 += 8 * kWave) {
+    int id[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u * kWave + lane;
+      id[u] = s < end ? topk_ids[s] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = id[u] - first;
+      if (id[u] >= 0 && (unsigned)e < (unsigned)E_loc) atomicAdd(&cnt[w * E_loc + e], 1);
+    }
   }
   __syncthreads();
 
@@ -103,26 +112,37 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   // pass 2: stable scatter
   const int nbits = 32 - __clz(max(E_loc - 1, 1));
   const uint64_t lanes_below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
-  for (int base = beg; base < end; base += kWave) {
-    const int s = base + lane;
-    int e = -1;
-    if (s < end) e = topk_ids[s] - first;
-    const bool loc = (s < end) && ((unsigned)e < (unsigned)E_loc);
-    uint64_t peers = __ballot(loc);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = loc && ((e >> b) & 1);
-      const uint64_t m = __ballot(bit);
-      peers &= bit ? m : ~m;
+  // ids of the next 8 sub-tiles are requested together, then consumed in order
+  for (int s0 = beg; s0 < end; s0 += 8 * kWave) {
+    int id8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u * kWave + lane;
+      id8[u] = s < end ? topk_ids[s] : -1;
     }
-    int cur = 0;
-    if (loc) {
-      cur = cnt[w * E_loc + e];
-      sorted_ids[cur + __popcll(peers & lanes_below)] = s;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int base = s0 + u * kWave;
+      if (base >= end) break;
+      const int s = base + lane;
+      const int e = id8[u] - first;
+      const bool loc = (s < end) && id8[u] >= 0 && ((unsigned)e < (unsigned)E_loc);
+      uint64_t peers = __ballot(loc);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = loc && ((e >> b) & 1);
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+      }
+      int cur = 0;
+      if (loc) {
+        cur = cnt[w * E_loc + e];
+        sorted_ids[cur + __popcll(peers & lanes_below)] = s;
+      }
+      // every lane has read its cursor before any lane of this wave updates it
+      __builtin_amdgcn_wave_barrier();
+      if (loc && (peers & lanes_below) == 0) cnt[w * E_loc + e] = cur + __popcll(peers);
+      __builtin_amdgcn_wave_barrier();
     }
-    // every lane has read its cursor before any lane of this wave updates it
-    __builtin_amdgcn_wave_barrier();
-    if (loc && (peers & lanes_below) == 0) cnt[w * E_loc + e] = cur + __popcll(peers);
-    __builtin_amdgcn_wave_barrier();
   }
 }
 

@@ -62,11 +62,11 @@ w4a16_weight_desc make_desc(int32_t E, int32_t N, int32_t K) {
   d.K = K;
   d.K_pad = (int32_t)round_up(K, 128);
   const int64_t KC = d.K_pad / 128;
-  d.scale_cols = (int32_t)round_up(KC, 8);
+  d.chunks = (int32_t)KC;
   d.group = 32;
   const int64_t NT = N / 16;
   d.w_bytes = (uint64_t)E * NT * KC * 1024;
-  d.s_bytes = (uint64_t)E * NT * 64 * d.scale_cols * 2;
+  d.s_bytes = (uint64_t)E * NT * KC * 64 * 2;
   d.check = desc_checksum(d);
   return d;
 }
@@ -179,7 +179,6 @@ w4a16::GemmParams base_params(const w4a16_weight_desc* d, const void* pw, const 
   p.K = d->K;
   p.NT = d->N / 16;
   p.KC = d->K_pad / 128;
-  p.SC = d->scale_cols;
   const int tiles_per_wg = nr * waves;
   p.n_tiles = (p.NT + tiles_per_wg - 1) / tiles_per_wg;
   p.out = out;
@@ -210,8 +209,8 @@ w4a16_status w4a16_pack_w4(const uint8_t* codes, const uint16_t* scales,
   if (!codes || !scales || !packed_w || !packed_s) return fail(W4A16_ERR_ARG, "NULL pointer argument");
   if (!aligned16(packed_w) || !aligned16(packed_s)) return fail(W4A16_ERR_ARG, "packed buffers must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(scales) & 1u) return fail(W4A16_ERR_ARG, "scales must be 2-byte aligned");
-  hipError_t e = w4a16::launch_pack(codes, scales, desc->E, desc->N, desc->K, desc->K_pad / 128,
-                                    desc->scale_cols, static_cast<uint32_t*>(packed_w),
+  hipError_t e = w4a16::launch_pack(codes, scales, desc->E, desc->N, desc->K, desc->chunks,
+                                    static_cast<uint32_t*>(packed_w),
                                     static_cast<uint16_t*>(packed_s), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pack_w4 launch");
   return W4A16_OK;

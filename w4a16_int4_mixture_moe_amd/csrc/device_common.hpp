@@ -14,28 +14,46 @@ constexpr int kChunk = 128;       // K elements per packed chunk (4 scale groups
 constexpr int kRowTile = 16;      // weight rows per MFMA tile
 constexpr int kWave = 64;
 
+// Constants the dequantiser combines with one v_and_or_b32 per pair of codes.
+// VOP3 encodings on gfx950 take no 32-bit literal, so the masks are pinned in
+// VGPRs once per thread (an opaque v_mov keeps the compiler from folding them
+// back into two-instruction AND + OR forms).
+struct DequantMasks {
+  uint32_t lo, hi, magic;
+};
+
+__device__ __forceinline__ uint32_t pin_vgpr(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
+__device__ __forceinline__ DequantMasks make_dequant_masks() {
+  return DequantMasks{pin_vgpr(0x000F000Fu), pin_vgpr(0x00F000F0u), pin_vgpr(0x64006400u)};
+}
+
 // Dequantise the 8 INT4 codes of one packed word into the bf16 MFMA operand
 // fragment, value e = bf16_rne((q_e - 8) * s).
 //
 // Subtract-then-scale with one BF16 rounding (Chord W4A16 MoE post, section
 // "H200 and Blackwell indexed decode": the fused dequant keeps the unfused
 // BF16 rounding order).  Code e sits at bit 4*(e/2) + 16*(e%2) of the word, so
-// one AND + OR turns two codes into the fp16 values 1024 + q (low nibble of a
+// one AND-OR turns two codes into the fp16 values 1024 + q (low nibble of a
 // half) or 1024 + 16 q (high nibble); v_fma_mix_f32 then forms, exactly,
 //   (1024 + q) * s - 1032 s  =  (q - 8) s
 //   (1024 + 16 q) * (s / 16) - 72 s  =  (q - 8) s
 // (the fma rounds once and (q - 8) s fits fp32 exactly: a 4-bit integer times
 // an 8-bit significand), and v_cvt_pk_bf16_f32 rounds that to bf16, nearest
 // even.  c0 = -1032 s, s16 = s / 16, c1 = -72 s are exact for any scale with
-// 2^-100 < |s| < 2^100.
-__device__ __forceinline__ bf16x8_t dequant8(uint32_t d, float s, float c0, float s16, float c1) {
-  const uint32_t magic = 0x64006400u;
-  const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u;
+// 2^-100 < |s| < 2^100.  Cost per 8 codes: 1 shift, 4 AND-OR, 8 fma_mix,
+// 4 cvt_pk.
+__device__ __forceinline__ bf16x8_t dequant8(uint32_t d, float s, float c0, float s16, float c1,
+                                             const DequantMasks& m) {
   const uint32_t d8 = d >> 8;
-  const f16x2_t h0 = __builtin_bit_cast(f16x2_t, (d & lo) | magic);
-  const f16x2_t h1 = __builtin_bit_cast(f16x2_t, (d & hi) | magic);
-  const f16x2_t h2 = __builtin_bit_cast(f16x2_t, (d8 & lo) | magic);
-  const f16x2_t h3 = __builtin_bit_cast(f16x2_t, (d8 & hi) | magic);
+  const f16x2_t h0 = __builtin_bit_cast(f16x2_t, (d & m.lo) | m.magic);
+  const f16x2_t h1 = __builtin_bit_cast(f16x2_t, (d & m.hi) | m.magic);
+  const f16x2_t h2 = __builtin_bit_cast(f16x2_t, (d8 & m.lo) | m.magic);
+  const f16x2_t h3 = __builtin_bit_cast(f16x2_t, (d8 & m.hi) | m.magic);
   bf16x8_t r;
   r[0] = (__bf16)__builtin_fmaf((float)h0.x, s, c0);
   r[1] = (__bf16)__builtin_fmaf((float)h0.y, s, c0);

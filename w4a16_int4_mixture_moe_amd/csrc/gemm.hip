@@ -40,6 +40,8 @@
 // Epilogues: bf16 store (round to nearest even) or, for the top-k combine,
 // fp32 partial = topk_weight(slot) * acc stored per slot; launch_combine then
 // sums a token's local slots in j order and rounds once.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -51,7 +53,9 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p
   constexpr int NTHR = NW * kWave;
   constexpr int XROW = kChunk + 8;                 // bf16 per staged row (272 B)
   constexpr int PIECES = BM * (kChunk / 8);        // 16-byte pieces per chunk
-  constexpr int PPT = (PIECES + NTHR - 1) / NTHR;  // pieces per thread
+  static_assert(PIECES % NTHR == 0, "block rows must cover the workgroup's threads");
+  constexpr int PPT = PIECES / NTHR;               // pieces per thread
+  constexpr int ROWS_PER_PASS = NTHR / 16;         // staged rows covered by one piece index
 
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][XROW];
   __shared__ int s_row[BM];
@@ -60,7 +64,7 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
   const int mb = blockIdx.x / p.n_tiles;
   const int nt = blockIdx.x - mb * p.n_tiles;
 
@@ -99,6 +103,7 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p
       s_out[i] = s_row[i];
     }
   }
+  expert = __builtin_amdgcn_readfirstlane(expert);
   __syncthreads();
 
   // wave-uniform mask of token tiles holding at least one valid row
@@ -107,19 +112,24 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p
   for (int t = 0; t < MT; ++t)
     if (__ballot(s_row[16 * t + (lane & 15)] >= 0)) tmask |= 1u << t;
 
-  // this thread's activation pieces: row pointer (nullptr = zero fill)
+  // Activation staging.  Piece i of this thread is row (tid / 16) +
+  // i * ROWS_PER_PASS, 16 bytes at column 8 * (tid % 16); the row's token
+  // tile is wave-uniform, so inactive tiles are skipped with a scalar branch.
+  // Padding rows read the block's first row (always valid) instead; their
+  // LDS columns only feed output columns that are never stored.
+  const int fallback_row = s_row[0];
+  const int xcol = (tid & 15) * 8;
   const uint16_t* xsrc[PPT];
-  int xrow[PPT], xcol[PPT];
 #pragma unroll
   for (int i = 0; i < PPT; ++i) {
-    const int q = tid + i * NTHR;
-    xrow[i] = q >> 4;
-    xcol[i] = (q & 15) * 8;
-    const int r = (q < PIECES) ? s_row[q >> 4] : -1;
-    xsrc[i] = r >= 0 ? p.a + (int64_t)r * p.K + xcol[i] : nullptr;
+    const int row = (tid >> 4) + i * ROWS_PER_PASS;
+    const int r = s_row[row];
+    xsrc[i] = p.a + (int64_t)(r >= 0 ? r : fallback_row) * p.K + xcol;
   }
+  auto piece_tile = [&](int i) { return (wave * kWave) / 256 + i * (ROWS_PER_PASS / 16); };
 
-  // this wave's weight tiles (clamped for loads; tiles past N do no work)
+  // this wave's weight tiles (clamped so loads stay in bounds; tiles past N
+  // compute throw-away values that are never stored)
   const int rt_base = nt * (NW * NR) + wave * NR;
   const int nr_valid = min(NR, p.NT - rt_base);
   const uint4* wptr[NR];
@@ -127,28 +137,38 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const int rt = min(rt_base + r, p.NT - 1);
-    const int64_t tile = (int64_t)expert * p.NT + rt;
-    wptr[r] = p.packed_w + tile * p.KC * kWave + lane;
-    sptr[r] = p.packed_s + (tile * kWave + lane) * p.SC;
+    const int64_t tile = ((int64_t)expert * p.NT + rt) * p.KC;
+    wptr[r] = p.packed_w + tile * kWave + lane;
+    sptr[r] = p.packed_s + tile * kWave + lane;
   }
 
   const int K = p.K;
   const int KC = p.KC;
-  auto load_x = [&](int c, uint4 (&xr)[PPT]) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int kk = c * kChunk + xcol[i];
-      if (xsrc[i] != nullptr && kk < K)
-        xr[i] = *reinterpret_cast<const uint4*>(xsrc[i] + (int64_t)c * kChunk);
-      else
-        xr[i] = make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_x = [&](int buf, const uint4 (&xr)[PPT]) {
+  auto issue_x = [&](int c, uint4 (&xr)[PPT]) {
+    // ragged K: a piece past K reads column 0 of its row instead (in bounds)
+    // and is replaced by zeros when stored; no select here, so the load's
+    // destination is never rewritten before it lands
+    const int64_t off = (c * kChunk + xcol < K) ? (int64_t)c * kChunk : 0;
 #pragma unroll
     for (int i = 0; i < PPT; ++i)
-      if (tid + i * NTHR < PIECES)
-        *reinterpret_cast<uint4*>(&xs[buf][xrow[i]][xcol[i]]) = xr[i];
+      if ((tmask >> piece_tile(i)) & 1u) xr[i] = *reinterpret_cast<const uint4*>(xsrc[i] + off);
+  };
+  // `tail`: the chunk may be the ragged last one, pieces past K become zeros
+  auto store_x = [&](int buf, int c, const uint4 (&xr)[PPT], bool tail) {
+    const bool kin = !tail || c * kChunk + xcol < K;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i)
+      if ((tmask >> piece_tile(i)) & 1u) {
+        const uint4 v = kin ? xr[i] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(&xs[buf][(tid >> 4) + i * ROWS_PER_PASS][xcol]) = v;
+      }
+  };
+  auto issue_w = [&](int c, uint4 (&w)[NR], uint32_t (&sc)[NR]) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      w[r] = wptr[r][(int64_t)c * kWave];
+      sc[r] = sptr[r][(int64_t)c * kWave];
+    }
   };
 
   f32x4_t acc[NR][MT];
@@ -157,67 +177,78 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 xr[PPT];
-  uint4 wcur[NR], wnxt[NR];
-  uint32_t scur[NR], snxt[NR];
+  // Two register sets: chunk c uses set c % 2.  At the top of chunk c the
+  // activation pieces of chunk c + 2 are requested into the set whose data
+  // (chunk c) already sits in LDS; weights and scales of chunk c + 2 are
+  // requested as soon as chunk c's have been dequantised; chunk c + 1's
+  // activations (requested one chunk earlier) are written to the other LDS
+  // buffer before the barrier.  So every global load has about two chunk
+  // times to land, and the barrier never waits on HBM.
+  const DequantMasks masks = make_dequant_masks();
+  uint4 xr[2][PPT];
+  uint4 wr[2][NR];
+  uint32_t sr[2][NR];
 
-  load_x(0, xr);
-  store_x(0, xr);
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    wcur[r] = wptr[r][0];
-    scur[r] = sptr[r][0];
+  issue_x(0, xr[0]);
+  issue_w(0, wr[0], sr[0]);
+  if (KC > 1) {
+    issue_x(1, xr[1]);
+    issue_w(1, wr[1], sr[1]);
   }
+  store_x(0, 0, xr[0], true);
   __syncthreads();
 
-  for (int c = 0; c < KC; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < KC;
-    if (more) {
-      load_x(c + 1, xr);
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        wnxt[r] = wptr[r][(int64_t)(c + 1) * kWave];
-        snxt[r] = sptr[r][c + 1];
-      }
-    }
-
-    float sc[NR], c0[NR], s16[NR], c1[NR];
+  // one chunk; STEADY: chunks c + 1 and c + 2 exist and c + 1 is not the
+  // ragged last chunk, so every prefetch and store is unconditional (no
+  // register phis, no selects)
+  auto chunk = [&](auto P_, auto STEADY_, int c) {
+    constexpr int P = decltype(P_)::value;
+    constexpr bool STEADY = decltype(STEADY_)::value;
+    const bool pf = STEADY || c + 2 < KC;
+    if (pf) issue_x(c + 2, xr[P]);
+    bf16x8_t A[NR][4];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      sc[r] = bf16_bits_to_float(scur[r]);
-      c0[r] = -1032.0f * sc[r];
-      s16[r] = 0.0625f * sc[r];
-      c1[r] = -72.0f * sc[r];
+      const float s = bf16_bits_to_float(sr[P][r] & 0xFFFFu);
+      const float c0 = -1032.0f * s, s16 = 0.0625f * s, c1 = -72.0f * s;
+      A[r][0] = dequant8(wr[P][r].x, s, c0, s16, c1, masks);
+      A[r][1] = dequant8(wr[P][r].y, s, c0, s16, c1, masks);
+      A[r][2] = dequant8(wr[P][r].z, s, c0, s16, c1, masks);
+      A[r][3] = dequant8(wr[P][r].w, s, c0, s16, c1, masks);
     }
+    if (pf) issue_w(c + 2, wr[P], sr[P]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bf16x8_t A[NR];
+      bf16x8_t B[MT];
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const uint32_t d = j == 0 ? wcur[r].x : j == 1 ? wcur[r].y : j == 2 ? wcur[r].z : wcur[r].w;
-        A[r] = dequant8(d, sc[r], c0[r], s16[r], c1[r]);
-      }
+      for (int t = 0; t < MT; ++t)
+        if ((tmask >> t) & 1u)
+          B[t] = *reinterpret_cast<const bf16x8_t*>(
+              &xs[P][16 * t + (lane & 15)][32 * (lane >> 4) + 8 * j]);
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        if (!((tmask >> t) & 1u)) continue;
-        const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(
-            &xs[buf][16 * t + (lane & 15)][32 * (lane >> 4) + 8 * j]);
+      for (int t = 0; t < MT; ++t)
+        if ((tmask >> t) & 1u)
 #pragma unroll
-        for (int r = 0; r < NR; ++r)
-          if (r < nr_valid)
-            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r], B, acc[r][t], 0, 0, 0);
-      }
+          for (int r = 0; r < NR; ++r)
+            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r][j], B[t], acc[r][t], 0, 0, 0);
     }
-
-    if (more) store_x(buf ^ 1, xr);
+    if (STEADY || c + 1 < KC) store_x(P ^ 1, c + 1, xr[P ^ 1], !STEADY);
     __syncthreads();
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      wcur[r] = wnxt[r];
-      scur[r] = snxt[r];
-    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using Steady = std::integral_constant<bool, true>;
+  using Tail = std::integral_constant<bool, false>;
+  int c = 0;
+  for (; c + 3 < KC; c += 2) {
+    chunk(I0{}, Steady{}, c);
+    chunk(I1{}, Steady{}, c + 1);
   }
+  // the last one to three chunks (c is even here)
+  if (c < KC) chunk(I0{}, Tail{}, c);
+  if (c + 1 < KC) chunk(I1{}, Tail{}, c + 1);
+  if (c + 2 < KC) chunk(I0{}, Tail{}, c + 2);
 
   // ---------------------------------------------------------------- epilogue
   // lane holds rows n = 16*tile + 4*(lane/16) + v (v = 0..3) of token

@@ -14,7 +14,7 @@ hipError_t launch_align(const int32_t* topk_ids, int32_t total_slots, int32_t fi
 
 // ---- packer (pack.hip)
 hipError_t launch_pack(const uint8_t* codes, const uint16_t* scales, int32_t E, int32_t N,
-                       int32_t K, int32_t KC, int32_t SC, uint32_t* packed_w,
+                       int32_t K, int32_t KC, uint32_t* packed_w,
                        uint16_t* packed_s, hipStream_t stream);
 
 // ---- GEMM (gemm.hip)
@@ -23,9 +23,9 @@ enum EpilogueKind : int { kEpiStore = 0, kEpiWeighted = 1 };
 
 struct GemmParams {
   const uint4* packed_w;        // [E][NT][KC][64][4 words]
-  const uint16_t* packed_s;     // [E][NT][64][SC]
+  const uint16_t* packed_s;     // [E][NT][KC][64]
   const uint16_t* a;            // bf16 activations, row stride K
-  int32_t E, N, K, NT, KC, SC;
+  int32_t E, N, K, NT, KC;
   int32_t n_tiles;              // workgroup tiles along N
   // indexed
   const int32_t* sorted_ids;

@@ -40,13 +40,15 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const uint8_t* __restrict__
 
 __global__ __launch_bounds__(256) void pack_s_kernel(const uint16_t* __restrict__ scales,
                                                      int32_t N, int32_t K, int32_t NT,
-                                                     int32_t SC, int64_t total,
+                                                     int32_t KC, int64_t total,
                                                      uint16_t* __restrict__ packed_s) {
+  // output index = ((e * NT + tile) * KC + c) * 64 + lane
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  const int c = (int)(idx % SC);
-  const int l = (int)((idx / SC) & 63);
-  const int64_t rest = idx / ((int64_t)SC * 64);
+  const int l = (int)(idx & 63);
+  int64_t rest = idx >> 6;
+  const int c = (int)(rest % KC);
+  rest /= KC;
   const int tile = (int)(rest % NT);
   const int64_t e = rest / NT;
   const int n = tile * kRowTile + (l & 15);
@@ -56,17 +58,17 @@ __global__ __launch_bounds__(256) void pack_s_kernel(const uint16_t* __restrict_
 }
 
 hipError_t launch_pack(const uint8_t* codes, const uint16_t* scales, int32_t E, int32_t N,
-                       int32_t K, int32_t KC, int32_t SC, uint32_t* packed_w,
+                       int32_t K, int32_t KC, uint32_t* packed_w,
                        uint16_t* packed_s, hipStream_t stream) {
   const int32_t NT = N / kRowTile;
   const int64_t words = (int64_t)E * NT * KC * 256;
-  const int64_t sents = (int64_t)E * NT * 64 * SC;
+  const int64_t sents = (int64_t)E * NT * KC * 64;
   hipLaunchKernelGGL(pack_w_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
                      codes, N, K, NT, KC, words, packed_w);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(pack_s_kernel, dim3((unsigned)((sents + 255) / 256)), dim3(256), 0, stream,
-                     scales, N, K, NT, SC, sents, packed_s);
+                     scales, N, K, NT, KC, sents, packed_s);
   return hipGetLastError();
 }
 
