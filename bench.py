@@ -69,6 +69,8 @@ def main() -> int:
     ap.add_argument("--workload", default="ep8_decode")
     ap.add_argument("--block-m", type=int, default=0, help="override the selector's block_m")
     ap.add_argument("--nr", type=int, default=0, help="override the selector's weight tiles per wave")
+    ap.add_argument("--split-k", type=int, default=-1, help="override: 0 stream-K, 1 one workgroup per tile")
+    ap.add_argument("--stages", type=int, default=0, help="override: K chunks of weights in flight per wave")
     ap.add_argument("--cpu-experts", type=int, default=4, help="experts in the CPU-baseline sample (0: skip)")
     ap.add_argument("--eager", action="store_true", help="launch the step eagerly instead of replaying a HIP graph")
     args = ap.parse_args()
@@ -107,6 +109,10 @@ def main() -> int:
         cfg.block_m = args.block_m
     if args.nr:
         cfg.nr = args.nr
+    if args.split_k >= 0:
+        cfg.split_k = args.split_k
+    if args.stages:
+        cfg.stages = args.stages
     T, k = sh.T, sh.topk
     cap = M.align_capacity(T, k, sh.E_loc, cfg.block_m)
     sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
@@ -115,7 +121,8 @@ def main() -> int:
     routing = M.Routing(sorted_ids, expert_ids, ntp, cfg.block_m, d_ids, sh.E_glob, sh.first, sh.E_loc)
     h = torch.empty(T * k, sh.N1, dtype=torch.bfloat16, device=dev)
     y = torch.empty(T, sh.N2, dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(M.workspace_bytes(T, k, sh.N2, True), dtype=torch.uint8, device=dev)
+    ws1 = torch.empty(max(16, M.workspace_bytes(p1, T, k, False, cfg)), dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(max(16, M.workspace_bytes(p2, T, k, True, cfg)), dtype=torch.uint8, device=dev)
     L = M.load()
     stream = torch.cuda.current_stream(dev)
     import ctypes
@@ -128,10 +135,10 @@ def main() -> int:
                                        ntp.data_ptr(), cap, 0, s_ptr))
 
     def gate_up():
-        M.moe_w4a16_gemm(d_x, p1, routing, cfg=cfg, out=h)
+        M.moe_w4a16_gemm(d_x, p1, routing, cfg=cfg, out=h, workspace=ws1)
 
     def down():
-        M.moe_w4a16_gemm(d_a, p2, routing, topk_weights=d_w, cfg=cfg, out=y, workspace=ws)
+        M.moe_w4a16_gemm(d_a, p2, routing, topk_weights=d_w, cfg=cfg, out=y, workspace=ws2)
 
     def step():
         align()
@@ -221,7 +228,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": sh.name, "T": T, "topk": k, "E_glob": sh.E_glob, "E_loc": sh.E_loc,
                    "K1": sh.K1, "N1": sh.N1, "K2": sh.K2, "N2": sh.N2, "block_m": cfg.block_m,
-                   "nr": cfg.nr, "waves": cfg.waves, "routed_rows": n_local,
+                   "nr": cfg.nr, "waves": cfg.waves, "split_k": cfg.split_k, "stages": cfg.stages, "routed_rows": n_local,
                    "experts_touched": touched, "num_tokens_padded": n_ntp},
         "per_call_us": {"align": round(us_align, 2), "gate_up": round(us_gu, 2),
                         "down_combine": round(us_dn, 2)},

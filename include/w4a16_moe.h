@@ -73,7 +73,7 @@ int32_t w4a16_abi_version(void);
  * nothing about the call has to be known when packing.
  *
  * Packed layout (all little-endian), with NT = N / 16, KP = K rounded up to
- * 128, KC = KP / 128:
+ * 128, KC = KP / 128, KC2 = ceil(KC / 2):
  *   packed_w : uint32 words [E][NT][KC][64 lanes][4 words]
  *     lane l = 16 * g + i holds row n = 16 * tile + i; word j of that lane
  *     holds the 8 codes of K indices kk = 128 * c + 32 * g + 8 * j + e,
@@ -81,11 +81,12 @@ int32_t w4a16_abi_version(void);
  *     are 8 (weight 0).  Each lane's word is exactly one MFMA operand
  *     fragment of 8 consecutive K values, and one lane's four words span one
  *     32-wide scale group.
- *   packed_s : bf16 [E][NT][KC][64 lanes]
- *     lane l = 16 * g + i of (tile, chunk c) holds scale[n = 16 * tile + i]
- *     [4 * c + g] (0 past K / 32): the one scale its four words need, so a
- *     wave's scales for one chunk are one 128-byte line.
- *   packed_w is E * NT * KC * 1024 bytes, packed_s is E * NT * KC * 128.
+ *   packed_s : uint32 words [E][NT][KC2][64 lanes]
+ *     lane l = 16 * g + i of (tile, chunk pair m) holds the bf16 scales
+ *     scale[n = 16 * tile + i][4 * c + g] for c = 2m (low half) and
+ *     c = 2m + 1 (high half), 0 past K / 32: the one scale each of its
+ *     chunks needs, so a wave's scales for a chunk pair are one 256-byte run.
+ *   packed_w is E * NT * KC * 1024 bytes, packed_s is E * NT * KC2 * 256.
  * ---------------------------------------------------------------------- */
 #define W4A16_DESC_MAGIC 0x16A4B0E5u /* arbitrary tag */
 #define W4A16_DESC_VERSION 1u
@@ -156,10 +157,23 @@ w4a16_status w4a16_moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, i
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t block_m;   /* rows per routed block: 16, 32, 64 or 128 */
-  int32_t nr;        /* 16-row weight tiles per wave: 1, 2 or 4 */
+  int32_t nr;        /* 16-row weight tiles per wave: 2 or 4 */
   int32_t waves;     /* waves per workgroup: 4 */
-  int32_t split_k;   /* reserved, must be 1 */
+  int32_t split_k;   /* 1: one workgroup per (block, N tile), whole K;
+                        0: stream-K -- the workgroups the device keeps resident
+                        each take an equal share of (tile, 128-K chunk) units;
+                        tiles cut between two workgroups are finished from
+                        fp32 partials in workspace, summed in K order (results
+                        then depend on the device's CU count, not on timing) */
+  int32_t stages;    /* K chunks of weights each wave keeps in flight: 2, or 3
+                        for block_m <= 32 with nr = 2 */
 } w4a16_config;
+
+/* The config w4a16_moe_gemm uses when its cfg is NULL, for routing buffers
+ * aligned to block_m: one workgroup per tile (host only; environment
+ * overrides W4A16_BLOCK_M, W4A16_NR, W4A16_SPLIT_K, W4A16_STAGES applied).
+ * Errors: ERR_ARG. */
+w4a16_status w4a16_indexed_config(int32_t block_m, w4a16_config* out);
 
 /* Choose a config for T tokens, top-k, E_glob model experts of which E_loc
  * are held here, projection [N, K] (host only).  Memoised per argument set.
@@ -181,9 +195,12 @@ typedef struct {
   int32_t first_expert, E_loc;       /* local expert range; read only by the combine */
 } w4a16_indexed_routing;
 
-/* Bytes of workspace w4a16_moe_gemm needs: 0 without combine,
- * T * topk * N * 4 with combine. */
-size_t w4a16_moe_gemm_workspace_bytes(int32_t T, int32_t topk, int32_t N, int32_t combine);
+/* Bytes of workspace w4a16_moe_gemm needs for this weight, T, topk, combine
+ * flag and config (NULL: w4a16_indexed_config(16)): the combine's fp32 per-slot partials (T * topk * N * 4)
+ * when combine != 0, plus, for split_k = 0, two partial tiles per resident
+ * workgroup of the current device.  Returns 0 on bad arguments. */
+size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, int32_t T, int32_t topk,
+                                      int32_t combine, const w4a16_config* cfg);
 
 /* out = routed W4A16 product.
  *  a          : bf16 activations, row stride K (desc->K).  a_per_slot = 0:
@@ -196,7 +213,9 @@ size_t w4a16_moe_gemm_workspace_bytes(int32_t T, int32_t topk, int32_t N, int32_
  *               with fp32 products, summed in j order, one rounding; tokens
  *               without local slots get 0; every row of out[T, N] written.
  *               Needs workspace (fp32 partials per slot).
- *  cfg        : NULL selects one (w4a16_select).
+ *  workspace  : w4a16_moe_gemm_workspace_bytes() bytes; contents need no
+ *               initialisation and are scratch for this call only.
+ *  cfg        : NULL: w4a16_indexed_config(routing->block_m).
  * Pointers: packed_w, packed_s, a, out, workspace 16-byte aligned.
  * Errors: ERR_ARG, ERR_LAYOUT, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP. */
 w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,

@@ -37,7 +37,7 @@ def test_every_declared_function_is_exported_and_bound(L):
 
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(_lib.WeightDesc) == 56
-    assert ctypes.sizeof(_lib.Config) == 16
+    assert ctypes.sizeof(_lib.Config) == 20
     assert _lib.IndexedRouting.capacity.offset == 24
 
 
@@ -46,7 +46,7 @@ def test_version_and_desc(L):
     d = W.weight_desc(48, 4096, 7168)
     assert (d.K_pad, d.chunks, d.group) == (7168, 56, 32)
     assert d.w_bytes == 48 * 4096 * 7168 // 2
-    assert d.s_bytes == 48 * 256 * 56 * 64 * 2
+    assert d.s_bytes == 48 * 256 * 28 * 64 * 4
     d = W.weight_desc(2, 32, 96)                         # ragged K: padded to one chunk
     assert (d.K_pad, d.chunks) == (128, 1)
 
@@ -71,8 +71,15 @@ def test_corrupted_descriptor_is_rejected(L):
 def test_capacity_and_workspace(L):
     assert W.align_capacity(576, 8, 48, 32) == ((4608 + 48 * 31 + 31) // 32) * 32
     assert L.w4a16_align_capacity(4, 2, 3, 24) == -1
-    assert W.workspace_bytes(10, 8, 7168, True) == 10 * 8 * 7168 * 4
-    assert W.workspace_bytes(10, 8, 7168, False) == 0
+    p = W.PackedW4(W.weight_desc(4, 7168, 2048), None, None)
+    one_wg_per_tile = W.config(32, 2, split_k=1)
+    assert W.workspace_bytes(p, 10, 8, True, one_wg_per_tile) == 10 * 8 * 7168 * 4
+    assert W.workspace_bytes(p, 10, 8, False, one_wg_per_tile) == 0
+    assert W.workspace_bytes(p, 10, 8, True, W.config(32, 3)) == 0          # unsupported config
+    d = W.indexed_config(64)
+    assert (d.block_m, d.nr, d.waves, d.split_k, d.stages) == (64, 2, 4, 1, 2)
+    assert W.workspace_bytes(p, 10, 8, True, W.config(32, 2, stages=3)) == 10 * 8 * 7168 * 4
+    assert W.workspace_bytes(p, 10, 8, True, W.config(64, 4, stages=3)) == 0   # not built
 
 
 def test_align_argument_errors(L):
@@ -98,6 +105,7 @@ def test_gemm_argument_errors(L):
     assert call(cfg=ctypes.byref(W.config(64, 2))) == -3                 # block_m disagrees with routing
     assert call(cfg=ctypes.byref(W.config(32, 3))) == -4                 # tile config not built
     assert call(w=P) == -8                                               # combine without workspace
+    assert call(cfg=ctypes.byref(W.config(32, 2, split_k=2))) == -4      # split_k must be 0 or 1
     bad = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 4)
     assert call(r=bad) == -3                                             # E_loc != weight experts
     assert L.w4a16_grouped_masked(ctypes.byref(d), P, P, P, 0, P, 4, P, None, None) == -1
@@ -111,7 +119,7 @@ def test_selector_follows_tokens_per_expert(L):
     one = W.select(16, 8, 384, 384, 512, 7168)             # ~0.3 rows/expert
     assert one.block_m == 16
     pre = W.select(8192, 8, 384, 48, 4096, 7168)           # ~171 rows/expert
-    assert pre.block_m == 128 and pre.nr == 4
+    assert pre.block_m == 128 and pre.nr == 2
     # tok_e, not total tokens: same T, 8x more experts -> decode side
     assert W.select(8192, 8, 3072, 48, 4096, 7168).block_m < 128
     assert W.select(576, 8, 384, 48, 4096, 7168).block_m == dec.block_m   # memoised, stable

@@ -81,11 +81,13 @@ def _unpack_cpu(w_bytes: np.ndarray, s_bytes: np.ndarray, E, N, K):
         vals = (words[:, :, :, l, j] >> shift) & 0xF                     # [E, NT, KC]
         kk = np.arange(KC) * 128 + 32 * g + 8 * j + e
         codes[:, np.arange(NT)[:, None] * 16 + i, kk[None, :]] = vals
-    sc = s_bytes.view(np.uint16).reshape(E, NT, KC, 64)
-    scales = np.zeros((E, N, 4 * KC), np.uint16)
+    KC2 = -(-KC // 2)
+    words = s_bytes.view(np.uint32).reshape(E, NT, KC2, 64)
+    sc = np.stack([words & 0xFFFF, words >> 16], axis=3).reshape(E, NT, 2 * KC2, 64).astype(np.uint16)
+    scales = np.zeros((E, N, 8 * KC2), np.uint16)
     for l in range(64):
         g, i = divmod(l, 16)
-        scales[:, (np.arange(NT) * 16 + i)[:, None], (4 * np.arange(KC) + g)[None, :]] = sc[:, :, :, l]
+        scales[:, (np.arange(NT) * 16 + i)[:, None], (4 * np.arange(2 * KC2) + g)[None, :]] = sc[:, :, :, l]
     return codes, scales
 
 
@@ -104,11 +106,11 @@ def test_pack_round_trip_bit_exact(E, N, K):
 
 # ------------------------------------------------------------ indexed GEMM
 
-def _run_indexed(P, bm, nr=None, first=None):
+def _run_indexed(P, bm, nr=None, first=None, stages=2):
     sh = P.sh
     first = sh.first if first is None else first
     r = M.moe_align(P.d_ids, sh.E_glob, first, sh.E_loc, bm)
-    cfg = M.config(bm, nr if nr else (4 if bm >= 64 else 2))
+    cfg = M.config(bm, nr if nr else (4 if bm >= 64 else 2), stages=stages)
     h = M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=cfg)
     y = M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=cfg) if P.with_down else None
     torch.cuda.synchronize()
@@ -131,13 +133,17 @@ def _check_indexed(P, h, y, what):
 
 
 def test_tiny_workload_all_tile_configs_match_oracle_and_each_other():
+    """Every built tile configuration, including the pipeline depth (2 or 3
+    chunks of weights in flight), gives the same output bits."""
     P = Problem(W.WORKLOADS["tiny"]).upload()
     outs = {}
-    for bm, nr in itertools.product((16, 32, 64, 128), (2, 4)):
-        _, h, y = _run_indexed(P, bm, nr)
-        _check_indexed(P, h, y, f"tiny bm={bm} nr={nr}")
-        outs[(bm, nr)] = (bits(h), bits(y))
-    base = outs[(16, 2)]
+    combos = [(bm, nr, 2) for bm, nr in itertools.product((16, 32, 64, 128), (2, 4))]
+    combos += [(16, 2, 3), (32, 2, 3)]
+    for bm, nr, st in combos:
+        _, h, y = _run_indexed(P, bm, nr, stages=st)
+        _check_indexed(P, h, y, f"tiny bm={bm} nr={nr} stages={st}")
+        outs[(bm, nr, st)] = (bits(h), bits(y))
+    base = outs[(16, 2, 2)]
     for key, (h, y) in outs.items():          # tile configuration does not change bits
         np.testing.assert_array_equal(h, base[0], err_msg=str(key))
         np.testing.assert_array_equal(y, base[1], err_msg=str(key))
@@ -151,6 +157,8 @@ def test_ragged_shapes():
     for bm in (16, 32, 128):
         _, h, y = _run_indexed(P, bm)
         _check_indexed(P, h, y, f"ragged bm={bm}")
+    _, h, y = _run_indexed(P, 32, stages=3)
+    _check_indexed(P, h, y, "ragged bm=32 stages=3")
 
 
 def test_one_hot_activations_return_dequantised_weights_bit_exact():
@@ -322,8 +330,10 @@ def test_hip_graph_capture_replays_match_eager():
                   sh.first, sh.E_loc)
     h = torch.zeros(sh.T * sh.topk, sh.N1, dtype=torch.bfloat16, device=dev())
     y = torch.empty(sh.T, sh.N2, dtype=torch.bfloat16, device=dev())
-    ws = torch.empty(M.workspace_bytes(sh.T, sh.topk, sh.N2, True), dtype=torch.uint8, device=dev())
-    cfg = M.config(bm, 2)
+    cfg = M.config(bm, 2, split_k=0)
+    ws = torch.empty(M.workspace_bytes(P.p2, sh.T, sh.topk, True, cfg), dtype=torch.uint8, device=dev())
+    ws1 = torch.empty(max(16, M.workspace_bytes(P.p1, sh.T, sh.topk, False, cfg)), dtype=torch.uint8,
+                      device=dev())
 
     def step():
         rr = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, bm, capacity=cap)
@@ -342,7 +352,7 @@ def test_hip_graph_capture_replays_match_eager():
         M._lib.check(L.w4a16_moe_align(P.d_ids.data_ptr(), sh.T, sh.topk, sh.E_glob, sh.first,
                                        sh.E_loc, bm, r.sorted_ids.data_ptr(), r.expert_ids.data_ptr(),
                                        r.num_tokens_padded.data_ptr(), cap, 0, s))
-        M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=cfg, out=h)
+        M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=cfg, out=h, workspace=ws1)
         M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=cfg, out=y, workspace=ws)
 
     g = torch.cuda.CUDAGraph()
@@ -359,3 +369,32 @@ def test_hip_graph_capture_replays_match_eager():
         np.testing.assert_array_equal(bits(h), ref_h, err_msg=f"replay {rep}")
         np.testing.assert_array_equal(bits(y), ref_y, err_msg=f"replay {rep}")
         _ = (P.d_x.float() @ P.d_x.float().t()).sum().item()   # unrelated eager work
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 64), ("ragged", 37), ("tiny", 300)])
+def test_streamk_matches_oracle_and_is_deterministic(name, T):
+    """Stream-K (split_k = 0) cuts tiles between persistent workgroups and
+    finishes them from fp32 partials: results within tolerance of the oracle,
+    identical across repeated calls, and within tolerance of the one-
+    workgroup-per-tile schedule."""
+    if name == "ragged":
+        sh = W.MoEShape(name="ragged", E_glob=9, E_loc=5, first=2, topk=3, T=T, K1=96, N1=48,
+                        K2=160, N2=80, seed=77)
+    else:
+        sh = W.scaled(W.WORKLOADS["tiny"], T=T)
+    P = Problem(sh).upload()
+    for bm in (16, 32, 128):
+        nr = 4 if bm >= 64 else 2
+        r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, bm)
+        outs = []
+        for rep in range(2):
+            cfg = M.config(bm, nr, split_k=0)
+            h = M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=cfg)
+            y = M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=cfg)
+            torch.cuda.synchronize()
+            outs.append((bits(h), bits(y)))
+        np.testing.assert_array_equal(outs[0][0], outs[1][0])
+        np.testing.assert_array_equal(outs[0][1], outs[1][1])
+        _check_indexed(P, torch.from_numpy(outs[0][0].view(np.int16)).view(torch.bfloat16),
+                       torch.from_numpy(outs[0][1].view(np.int16)).view(torch.bfloat16),
+                       f"stream-K {name} T={T} bm={bm}")

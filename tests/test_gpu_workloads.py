@@ -29,7 +29,7 @@ def _indexed_full(P, name):
     r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, cfg1.block_m)
     canary = torch.full((T * k, sh.N1), -3.0, dtype=torch.bfloat16, device="cuda")
     h = M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=cfg1, out=canary)
-    y = M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=M.config(cfg1.block_m, cfg1.nr))
+    y = M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=cfg1)
     torch.cuda.synchronize()
     log(name, "config", cfg1, "ntp", int(r.num_tokens_padded.item()))
     flat = P.topk_ids.reshape(-1)

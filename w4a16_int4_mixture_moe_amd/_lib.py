@@ -34,10 +34,11 @@ class WeightDesc(ctypes.Structure):
 
 class Config(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int32), ("nr", ctypes.c_int32),
-                ("waves", ctypes.c_int32), ("split_k", ctypes.c_int32)]
+                ("waves", ctypes.c_int32), ("split_k", ctypes.c_int32), ("stages", ctypes.c_int32)]
 
     def __repr__(self):
-        return f"Config(block_m={self.block_m}, nr={self.nr}, waves={self.waves}, split_k={self.split_k})"
+        return (f"Config(block_m={self.block_m}, nr={self.nr}, waves={self.waves}, "
+                f"split_k={self.split_k}, stages={self.stages})")
 
 
 class IndexedRouting(ctypes.Structure):
@@ -63,7 +64,9 @@ SIGNATURES = {
     "w4a16_align_capacity": (_I64, [_I32, _I32, _I32, _I32]),
     "w4a16_moe_align": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P]),
     "w4a16_select": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(Config)]),
-    "w4a16_moe_gemm_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "w4a16_indexed_config": (_I32, [_I32, ctypes.POINTER(Config)]),
+    "w4a16_moe_gemm_workspace_bytes": (_SZ, [ctypes.POINTER(WeightDesc), _I32, _I32, _I32,
+                                             ctypes.POINTER(Config)]),
     "w4a16_moe_gemm": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I64, _I32,
                               ctypes.POINTER(IndexedRouting), _P, _P, ctypes.POINTER(Config),
                               _P, _SZ, _P]),

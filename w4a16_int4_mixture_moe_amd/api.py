@@ -143,12 +143,24 @@ def select(T: int, topk: int, E_glob: int, E_loc: int, N: int, K: int) -> Config
     return c
 
 
-def config(block_m: int, nr: int, waves: int = 4, split_k: int = 1) -> Config:
-    return Config(block_m, nr, waves, split_k)
+def config(block_m: int, nr: int, waves: int = 4, split_k: int = 1, stages: int = 2) -> Config:
+    """split_k = 1: one workgroup per tile; 0: stream-K over resident workgroups.
+    stages: K chunks of weights in flight per wave (2, or 3 for small tiles)."""
+    return Config(block_m, nr, waves, split_k, stages)
 
 
-def workspace_bytes(T: int, topk: int, N: int, combine: bool) -> int:
-    return int(load().w4a16_moe_gemm_workspace_bytes(T, topk, N, int(bool(combine))))
+def indexed_config(block_m: int) -> Config:
+    """The config moe_w4a16_gemm uses by default for routing aligned to block_m."""
+    c = Config()
+    check(load().w4a16_indexed_config(block_m, ctypes.byref(c)))
+    return c
+
+
+def workspace_bytes(packed: PackedW4, T: int, topk: int, combine: bool,
+                    cfg: Optional[Config] = None) -> int:
+    return int(load().w4a16_moe_gemm_workspace_bytes(
+        ctypes.byref(packed.desc), T, topk, int(bool(combine)),
+        None if cfg is None else ctypes.byref(cfg)))
 
 
 def moe_w4a16_gemm(a: torch.Tensor, packed: PackedW4, routing: Routing,
@@ -177,9 +189,12 @@ def moe_w4a16_gemm(a: torch.Tensor, packed: PackedW4, routing: Routing,
         _need(out, "out", _BF16, 2)
         if out.shape[0] < rows or out.shape[1] != packed.N:
             raise ValueError(f"out must be [{rows}, {packed.N}]")
-    nws = workspace_bytes(T, k, packed.N, combine)
-    if combine and workspace is None:
-        workspace = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+    if cfg is None:
+        cfg = indexed_config(routing.block_m)
+    if workspace is None:
+        nws = workspace_bytes(packed, T, k, combine, cfg)
+        if nws:
+            workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
     r = routing.as_c()
     check(load().w4a16_moe_gemm(ctypes.byref(packed.desc), packed.w.data_ptr(), packed.s.data_ptr(),
                                 a.data_ptr(), a.shape[0], int(bool(a_per_slot)), ctypes.byref(r),
@@ -227,6 +242,6 @@ def grouped_masked(a: torch.Tensor, packed: PackedW4, masked_m: torch.Tensor, ex
 
 __all__ = [
     "W4A16Error", "PackedW4", "Routing", "Config", "weight_desc", "pack_w4", "align_capacity",
-    "moe_align", "select", "config", "workspace_bytes", "moe_w4a16_gemm", "grouped_contiguous",
+    "moe_align", "select", "config", "indexed_config", "workspace_bytes", "moe_w4a16_gemm", "grouped_contiguous",
     "grouped_masked",
 ]

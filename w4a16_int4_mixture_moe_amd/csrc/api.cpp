@@ -66,7 +66,7 @@ w4a16_weight_desc make_desc(int32_t E, int32_t N, int32_t K) {
   d.group = 32;
   const int64_t NT = N / 16;
   d.w_bytes = (uint64_t)E * NT * KC * 1024;
-  d.s_bytes = (uint64_t)E * NT * KC * 64 * 2;
+  d.s_bytes = (uint64_t)E * NT * ((KC + 1) / 2) * 64 * 4;
   d.check = desc_checksum(d);
   return d;
 }
@@ -118,32 +118,42 @@ int64_t sampled_blocks(const std::vector<int>& counts, int bm) {
   return b;
 }
 
-w4a16_config select_config(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc) {
+int resident_workgroups(const w4a16_config& c, int epi);
+
+w4a16_config select_config(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N) {
   w4a16_config c;
   c.waves = 4;
   c.split_k = 1;
+  c.stages = 2;
   const double tok_e = (double)T * topk / std::max(E_glob, 1);
-  if (tok_e >= kPrefillTokE) {
-    c.block_m = 128;
-    c.nr = 4;
-    return c;
-  }
   // sampled routing: each of T*topk slots lands on one of E_glob experts
   // uniformly; keep the local ones (fixed seed: deterministic choice)
   std::mt19937 rng(12345u);
   std::vector<int> counts(std::max(E_loc, 1), 0);
   std::binomial_distribution<int> bin(std::max(T, 0) * std::max(topk, 1), 1.0 / std::max(E_glob, 1));
   for (int e = 0; e < E_loc; ++e) counts[e] = bin(rng);
-  const int cands[3] = {16, 32, 64};
-  int64_t best = INT64_MAX;
-  for (int bm : cands) best = std::min(best, sampled_blocks(counts, bm));
-  c.block_m = 64;
-  for (int bm : cands)
-    if (sampled_blocks(counts, bm) * 100 <= best * 102) {
-      c.block_m = bm;
-      break;
-    }
-  c.nr = 2;
+  if (tok_e >= kPrefillTokE) {
+    c.block_m = 128;
+    c.nr = 2;  // measured: two 16-row weight tiles per wave beat four at 128 rows
+  } else {
+    const int cands[3] = {16, 32, 64};
+    int64_t best = INT64_MAX;
+    for (int bm : cands) best = std::min(best, sampled_blocks(counts, bm));
+    c.block_m = 64;
+    for (int bm : cands)
+      if (sampled_blocks(counts, bm) * 100 <= best * 102) {
+        c.block_m = bm;
+        break;
+      }
+    c.nr = 2;
+  }
+  // Stream-K only when the tile grid would leave resident workgroups idle
+  // (the post keeps stream-K where the plain grid under-fills the machine,
+  // section "H200 prefill and TP8"); otherwise one workgroup per tile keeps
+  // more waves resident, which the latency-bound decode tiles need more.
+  const int64_t tiles = sampled_blocks(counts, c.block_m) * ((N / 16 + 4 * c.nr - 1) / (4 * c.nr));
+  const int resident = resident_workgroups(c, w4a16::kEpiStore);
+  if (resident > 0 && tiles < resident) c.split_k = 0;
   return c;
 }
 
@@ -152,18 +162,22 @@ const char* env_str(const char* name) {
   return (v && *v) ? v : nullptr;
 }
 
-// W4A16_BLOCK_M / W4A16_NR override the selector (read on every call; the
+// W4A16_BLOCK_M / W4A16_NR / W4A16_SPLIT_K / W4A16_STAGES override the selector (read on every call; the
 // memoised result is the selector's, overrides are applied on top).
 void apply_env_overrides(w4a16_config* c) {
   if (const char* v = env_str("W4A16_BLOCK_M")) c->block_m = std::atoi(v);
   if (const char* v = env_str("W4A16_NR")) c->nr = std::atoi(v);
+  if (const char* v = env_str("W4A16_SPLIT_K")) c->split_k = std::atoi(v);
+  if (const char* v = env_str("W4A16_STAGES")) c->stages = std::atoi(v);
 }
 
 w4a16_status check_config(const w4a16_config& c, int route, int epi) {
   if (!valid_block_m(c.block_m)) return fail(W4A16_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128}", c.block_m);
-  if (c.split_k != 1) return fail(W4A16_ERR_UNSUPPORTED, "split_k %d: only 1 is built", c.split_k);
-  if (!w4a16::gemm_config_supported(route, epi, c.block_m / 16, c.nr, c.waves))
-    return fail(W4A16_ERR_UNSUPPORTED, "tile config block_m=%d nr=%d waves=%d not built", c.block_m, c.nr, c.waves);
+  if (c.split_k != 0 && c.split_k != 1)
+    return fail(W4A16_ERR_UNSUPPORTED, "split_k %d: 0 (stream-K) or 1 (one workgroup per tile)", c.split_k);
+  if (!w4a16::gemm_config_supported(route, epi, c.block_m / 16, c.nr, c.waves, c.stages))
+    return fail(W4A16_ERR_UNSUPPORTED, "tile config block_m=%d nr=%d waves=%d stages=%d not built", c.block_m,
+                c.nr, c.waves, c.stages);
   return W4A16_OK;
 }
 
@@ -172,7 +186,7 @@ w4a16::GemmParams base_params(const w4a16_weight_desc* d, const void* pw, const 
   w4a16::GemmParams p;
   std::memset(&p, 0, sizeof p);
   p.packed_w = static_cast<const uint4*>(pw);
-  p.packed_s = static_cast<const uint16_t*>(ps);
+  p.packed_s = static_cast<const uint32_t*>(ps);
   p.a = a;
   p.E = d->E;
   p.N = d->N;
@@ -183,6 +197,35 @@ w4a16::GemmParams base_params(const w4a16_weight_desc* d, const void* pw, const 
   p.n_tiles = (p.NT + tiles_per_wg - 1) / tiles_per_wg;
   p.out = out;
   return p;
+}
+
+// Workspace carve-up: [combine partials, fp32 T*topk*N][stream-K partial tiles]
+size_t combine_region(int32_t T, int32_t topk, int32_t N, bool combine) {
+  return combine ? (size_t)round_up((int64_t)T * topk * N * (int64_t)sizeof(float), 256) : 0;
+}
+
+size_t streamk_region(const w4a16_config& c, int epi) {
+  if (c.split_k != 0) return 0;
+  const int wgs = resident_workgroups(c, epi);
+  if (wgs <= 0) return 0;
+  return w4a16::streamk_partial_bytes(c.block_m / 16, c.nr, c.waves, wgs);
+}
+
+w4a16_config default_indexed_config(int32_t block_m) {
+  w4a16_config c;
+  c.block_m = block_m;
+  c.nr = 2;
+  c.waves = 4;
+  c.split_k = 1;
+  c.stages = 2;
+  apply_env_overrides(&c);
+  return c;
+}
+
+// Workgroups of this config the current device keeps resident (stream-K
+// grid); 0 when no device is visible or the config is not built.
+int resident_workgroups(const w4a16_config& c, int epi) {
+  return w4a16::streamk_workgroups(w4a16::kRouteIndexed, epi, c.block_m / 16, c.nr, c.waves, c.stages);
 }
 
 }  // namespace
@@ -211,7 +254,7 @@ w4a16_status w4a16_pack_w4(const uint8_t* codes, const uint16_t* scales,
   if (reinterpret_cast<uintptr_t>(scales) & 1u) return fail(W4A16_ERR_ARG, "scales must be 2-byte aligned");
   hipError_t e = w4a16::launch_pack(codes, scales, desc->E, desc->N, desc->K, desc->chunks,
                                     static_cast<uint32_t*>(packed_w),
-                                    static_cast<uint16_t*>(packed_s), static_cast<hipStream_t>(stream));
+                                    static_cast<uint32_t*>(packed_s), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pack_w4 launch");
   return W4A16_OK;
 }
@@ -255,6 +298,13 @@ w4a16_status w4a16_moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, i
   return W4A16_OK;
 }
 
+w4a16_status w4a16_indexed_config(int32_t block_m, w4a16_config* out) {
+  if (!out) return fail(W4A16_ERR_ARG, "out is NULL");
+  if (!valid_block_m(block_m)) return fail(W4A16_ERR_ARG, "block_m %d not in {16, 32, 64, 128}", block_m);
+  *out = default_indexed_config(block_m);
+  return W4A16_OK;
+}
+
 w4a16_status w4a16_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N,
                           int32_t K, w4a16_config* out) {
   if (!out) return fail(W4A16_ERR_ARG, "out is NULL");
@@ -270,7 +320,7 @@ w4a16_status w4a16_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc
       return W4A16_OK;
     }
   }
-  w4a16_config c = select_config(T, topk, E_glob, E_loc);
+  w4a16_config c = select_config(T, topk, E_glob, E_loc, N);
   {
     std::lock_guard<std::mutex> g(g_cache_mu);
     g_cache[key] = c;
@@ -280,9 +330,13 @@ w4a16_status w4a16_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc
   return W4A16_OK;
 }
 
-size_t w4a16_moe_gemm_workspace_bytes(int32_t T, int32_t topk, int32_t N, int32_t combine) {
-  if (!combine || T <= 0 || topk <= 0 || N <= 0) return 0;
-  return (size_t)T * topk * N * sizeof(float);
+size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, int32_t T, int32_t topk,
+                                      int32_t combine, const w4a16_config* cfg) {
+  if (check_desc(desc) != W4A16_OK || T < 0 || topk <= 0) return 0;
+  const w4a16_config c = cfg ? *cfg : default_indexed_config(16);
+  const int epi = combine ? w4a16::kEpiWeighted : w4a16::kEpiStore;
+  if (check_config(c, w4a16::kRouteIndexed, epi) != W4A16_OK) return 0;
+  return combine_region(T, topk, desc->N, combine != 0) + streamk_region(c, epi);
 }
 
 w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
@@ -308,40 +362,47 @@ w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
   if (a_rows < need_rows)
     return fail(W4A16_ERR_SHAPE, "activations have %lld rows, need %lld", (long long)a_rows, (long long)need_rows);
   if ((int64_t)r.T * r.topk >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "T*topk too large");
+  const int epi = combine ? w4a16::kEpiWeighted : w4a16::kEpiStore;
   w4a16_config c;
   if (cfg) {
     c = *cfg;
   } else {
-    // the routing buffers fix block_m; the rest follows from it
-    c.block_m = r.block_m;
-    c.nr = r.block_m >= 64 ? 4 : 2;
-    c.waves = 4;
-    c.split_k = 1;
-    apply_env_overrides(&c);
+    c = default_indexed_config(r.block_m);   // the routing buffers fix block_m
   }
-  const int epi = combine ? w4a16::kEpiWeighted : w4a16::kEpiStore;
   st = check_config(c, w4a16::kRouteIndexed, epi);
   if (st != W4A16_OK) return st;
   if (c.block_m != r.block_m)
     return fail(W4A16_ERR_LAYOUT, "config block_m=%d differs from the routing's block_m=%d", c.block_m, r.block_m);
   if (r.capacity % r.block_m) return fail(W4A16_ERR_CAPACITY, "capacity not a multiple of block_m");
-  if (combine) {
-    if (!r.topk_ids) return fail(W4A16_ERR_ARG, "combine needs routing.topk_ids");
-    const size_t need = w4a16_moe_gemm_workspace_bytes(r.T, r.topk, desc->N, 1);
-    if (!workspace || workspace_bytes < need || !aligned16(workspace))
-      return fail(W4A16_ERR_WORKSPACE, "combine needs %zu bytes of 16-byte aligned workspace, got %zu", need, workspace_bytes);
-  }
+  if (combine && !r.topk_ids) return fail(W4A16_ERR_ARG, "combine needs routing.topk_ids");
+  const size_t comb_bytes = combine_region(r.T, r.topk, desc->N, combine);
+  const size_t sk_bytes = streamk_region(c, epi);
+  if (c.split_k == 0 && sk_bytes == 0)
+    return fail(W4A16_ERR_HIP, "stream-K: could not query the device's resident workgroups");
+  const size_t need = comb_bytes + sk_bytes;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(W4A16_ERR_WORKSPACE, "this call needs %zu bytes of 16-byte aligned workspace, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
   if (r.T == 0) return W4A16_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  w4a16::GemmParams p = base_params(desc, packed_w, packed_s, a, combine ? workspace : (void*)out, c.nr, c.waves);
+  char* ws = static_cast<char*>(workspace);
+  w4a16::GemmParams p = base_params(desc, packed_w, packed_s, a, combine ? (void*)ws : (void*)out, c.nr, c.waves);
   p.sorted_ids = r.sorted_ids;
   p.expert_ids = r.expert_ids;
   p.num_tokens_padded = r.num_tokens_padded;
   p.sentinel = r.T * r.topk;
   p.a_row_div = a_per_slot ? 1 : r.topk;
   p.slot_weight = topk_weights;
-  hipError_t e = w4a16::launch_gemm(w4a16::kRouteIndexed, epi, c.block_m / 16, c.nr, c.waves, p,
-                                    r.capacity / r.block_m, s);
+  p.grid_blocks = (int32_t)(r.capacity / r.block_m);
+  hipError_t e;
+  if (c.split_k == 0) {
+    p.sk_partial = reinterpret_cast<float*>(ws + comb_bytes);
+    const int wgs = resident_workgroups(c, epi);
+    e = w4a16::launch_gemm_streamk(w4a16::kRouteIndexed, epi, c.block_m / 16, c.nr, c.waves, c.stages, p,
+                                   wgs, s);
+  } else {
+    e = w4a16::launch_gemm(w4a16::kRouteIndexed, epi, c.block_m / 16, c.nr, c.waves, c.stages, p, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "moe_gemm launch");
   if (combine) {
     e = w4a16::launch_combine(static_cast<const float*>(workspace), r.topk_ids, r.T, r.topk,
@@ -366,19 +427,21 @@ w4a16_status w4a16_grouped_contiguous(const w4a16_weight_desc* desc, const void*
   if (cfg) {
     c = *cfg;
   } else {
-    c.block_m = 128; c.nr = 4; c.waves = 4; c.split_k = 1;
+    c.block_m = 128; c.nr = 2; c.waves = 4; c.split_k = 1; c.stages = 2;
     apply_env_overrides(&c);
   }
   st = check_config(c, w4a16::kRouteContiguous, w4a16::kEpiStore);
   if (st != W4A16_OK) return st;
+  if (c.split_k != 1) return fail(W4A16_ERR_UNSUPPORTED, "grouped calls run split_k = 1 only");
   if (128 % c.block_m) return fail(W4A16_ERR_UNSUPPORTED, "contiguous layout needs block_m dividing 128");
   if (m_rows % c.block_m) return fail(W4A16_ERR_SHAPE, "m_rows=%lld is not a multiple of block_m=%d (segments are 128-row aligned)", (long long)m_rows, c.block_m);
   if (m_rows >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "m_rows too large");
   if (m_rows == 0) return W4A16_OK;
   w4a16::GemmParams p = base_params(desc, packed_w, packed_s, a, out, c.nr, c.waves);
   p.m_indices = m_indices;
+  p.grid_blocks = (int32_t)(m_rows / c.block_m);
   hipError_t e = w4a16::launch_gemm(w4a16::kRouteContiguous, w4a16::kEpiStore, c.block_m / 16, c.nr,
-                                    c.waves, p, m_rows / c.block_m, static_cast<hipStream_t>(stream));
+                                    c.waves, c.stages, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "grouped_contiguous launch");
   return W4A16_OK;
 }
@@ -403,20 +466,22 @@ w4a16_status w4a16_grouped_masked(const w4a16_weight_desc* desc, const void* pac
     // kernels": masked decode picks BLOCK_M from the expected tokens per expert)
     const int want = (int)round_up(std::min(expected_m, 128), 16);
     c.block_m = want <= 16 ? 16 : want <= 32 ? 32 : want <= 64 ? 64 : 128;
-    c.nr = c.block_m >= 64 ? 4 : 2;
+    c.nr = 2;
     c.waves = 4;
     c.split_k = 1;
+    c.stages = 2;
     apply_env_overrides(&c);
   }
   st = check_config(c, w4a16::kRouteMasked, w4a16::kEpiStore);
   if (st != W4A16_OK) return st;
+  if (c.split_k != 1) return fail(W4A16_ERR_UNSUPPORTED, "grouped calls run split_k = 1 only");
   w4a16::GemmParams p = base_params(desc, packed_w, packed_s, a, out, c.nr, c.waves);
   p.masked_m = masked_m;
   p.max_m = max_m;
   p.blocks_per_group = (max_m + c.block_m - 1) / c.block_m;
+  p.grid_blocks = desc->E * p.blocks_per_group;
   hipError_t e = w4a16::launch_gemm(w4a16::kRouteMasked, w4a16::kEpiStore, c.block_m / 16, c.nr,
-                                    c.waves, p, (int64_t)desc->E * p.blocks_per_group,
-                                    static_cast<hipStream_t>(stream));
+                                    c.waves, c.stages, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "grouped_masked launch");
   return W4A16_OK;
 }

@@ -66,6 +66,31 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t d, float s, float c0, floa
   return r;
 }
 
+// Global-memory byte pointer (address space 1: loads through it are
+// global_load, never flat_load).
+typedef const char __attribute__((address_space(1)))* gptr_t;
+
+// A pointer the caller knows to be the same in every lane, moved to SGPRs so
+// address arithmetic on it stays scalar.
+template <typename T>
+__device__ __forceinline__ gptr_t uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<gptr_t>(((uint64_t)hi << 32) | lo);
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 gload_u32x4(gptr_t p) {
+  const u32x4_t v = *reinterpret_cast<const u32x4_t __attribute__((address_space(1)))*>(p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint32_t gload_u32(gptr_t p) {
+  return *reinterpret_cast<const uint32_t __attribute__((address_space(1)))*>(p);
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) {
   return __builtin_bit_cast(float, b16 << 16);
 }

@@ -11,21 +11,31 @@
 // 16-row token tiles per weight fragment, so every weight element is
 // dequantised once per workgroup however many rows share it.
 //
-// Workgroup tile: one routed block of BM = 16 * MT rows (one expert) times
-// BN = NW * NR * 16 weight rows; each wave owns NR 16-row weight tiles and
-// every token tile of the block.  Per 128-wide K chunk:
+// Tile: one routed block of BM = 16 * MT rows (one expert) times BN = NW * NR
+// * 16 weight rows; each wave owns NR 16-row weight tiles and every token
+// tile of the block.  Per 128-wide K chunk:
 //   - activations: BM rows x 256 B staged global -> registers -> LDS
 //     (double buffered, rows padded to 272 B so the 16-byte operand reads
 //     of 16 different rows fall in different LDS banks);
 //   - weights: one 16-byte load per lane per weight tile straight from HBM
-//     into registers (the packed layout is the operand layout), issued one
-//     chunk ahead; the lane's bf16 scale rides along;
-//   - dequant (dequant8) -> 4 MFMAs per (weight tile, token tile).
-// Token tiles without a valid row are skipped (wave-uniform), so padding rows
-// of a block cost neither MFMA work nor activation loads past the first
-// check.  Summation order per output: chunks in K order, and inside a chunk
-// the hardware's order over its 32 K -- independent of BM, NR, NW, so the
-// output bits do not depend on the tile configuration.
+//     into registers (the packed layout is the operand layout) plus the
+//     lane's one bf16 scale, both requested two or three chunks ahead;
+//   - dequant (dequant8) -> 4 MFMAs per (weight tile, active token tile).
+// Token tiles without a valid row are skipped (wave-uniform).  Summation
+// order per output: chunks in K order, and inside a chunk the hardware's
+// order over its 32 K; with one workgroup per tile this is independent of
+// BM, NR, NW, so the output bits do not depend on the tile configuration.
+//
+// Two schedules (the post gates stream-K by shape, section "H200 prefill and
+// TP8"; its decode section reports a semi-static tile schedule beating a
+// fully dynamic one):
+//   classic   one workgroup per (routed block, N tile);
+//   stream-K  as many workgroups as the device keeps resident, each taking
+//             an equal contiguous range of (tile, chunk) units, so a grid of
+//             1.5 "waves" of tiles no longer idles half the machine at the
+//             end; a tile cut by a range boundary leaves fp32 partials
+//             (one slot per contributor) that streamk_fixup_kernel sums in
+//             range order -- deterministic for a given device and config.
 //
 // Row sources (the post's two families, sections "Two kernel families" and
 // "Grouped SM90 kernels"):
@@ -40,6 +50,7 @@
 // Epilogues: bf16 store (round to nearest even) or, for the top-k combine,
 // fp32 partial = topk_weight(slot) * acc stored per slot; launch_combine then
 // sums a token's local slots in j order and rounds once.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -47,212 +58,257 @@
 
 namespace w4a16 {
 
-template <int MT, int NR, int NW, int ROUTE, int EPI>
-__global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p) {
+template <int MT>
+struct TileSmem {
+  uint16_t xs[2][16 * MT][kChunk + 8];  // staged activation chunk, 272-byte rows
+  int row[16 * MT];                     // activation row per block row, -1 = padding
+  int out[16 * MT];                     // output row per block row, -1 = not stored
+  float w[16 * MT];                     // top-k weight per block row (weighted epilogue)
+};
+
+// Number of routed blocks with work (indexed: from the device-side padded
+// total; grouped: the launch's block count).
+template <int MT, int ROUTE>
+__device__ __forceinline__ int live_blocks(const GemmParams& p) {
+  if constexpr (ROUTE == kRouteIndexed)
+    return min(*p.num_tokens_padded / (16 * MT), p.grid_blocks);
+  else
+    return p.grid_blocks;
+}
+
+// Fill the block's row tables; returns the block's expert (wave-uniform) or
+// -1 when the block has no work.  The caller synchronises afterwards.
+template <int MT, int NW, int ROUTE, int EPI>
+__device__ __forceinline__ int setup_rows(const GemmParams& p, int mb, TileSmem<MT>& sm) {
   constexpr int BM = 16 * MT;
   constexpr int NTHR = NW * kWave;
-  constexpr int XROW = kChunk + 8;                 // bf16 per staged row (272 B)
-  constexpr int PIECES = BM * (kChunk / 8);        // 16-byte pieces per chunk
-  static_assert(PIECES % NTHR == 0, "block rows must cover the workgroup's threads");
-  constexpr int PPT = PIECES / NTHR;               // pieces per thread
-  constexpr int ROWS_PER_PASS = NTHR / 16;         // staged rows covered by one piece index
-
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][XROW];
-  __shared__ int s_row[BM];
-  __shared__ int s_out[BM];
-  __shared__ float s_w[EPI == kEpiWeighted ? BM : 1];
-
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
-  const int mb = blockIdx.x / p.n_tiles;
-  const int nt = blockIdx.x - mb * p.n_tiles;
-
-  // ---------------------------------------------------------------- rows
   int expert;
   if constexpr (ROUTE == kRouteIndexed) {
-    if (mb * BM >= *p.num_tokens_padded) return;
+    if (mb * BM >= *p.num_tokens_padded) return -1;
     expert = p.expert_ids[mb];
-    if ((unsigned)expert >= (unsigned)p.E) return;   // -1 (unused block) or foreign id
+    if ((unsigned)expert >= (unsigned)p.E) return -1;   // -1 (unused block) or foreign id
     for (int i = tid; i < BM; i += NTHR) {
       const int s = p.sorted_ids[(int64_t)mb * BM + i];
       const bool v = (unsigned)s < (unsigned)p.sentinel;
-      s_row[i] = v ? s / p.a_row_div : -1;
-      s_out[i] = v ? s : -1;
-      if constexpr (EPI == kEpiWeighted) s_w[i] = v ? p.slot_weight[s] : 0.f;
+      sm.row[i] = v ? s / p.a_row_div : -1;
+      sm.out[i] = v ? s : -1;
+      if constexpr (EPI == kEpiWeighted) sm.w[i] = v ? p.slot_weight[s] : 0.f;
     }
   } else if constexpr (ROUTE == kRouteContiguous) {
     const int r0 = mb * BM;
     expert = p.m_indices[r0];
-    if ((unsigned)expert >= (unsigned)p.E) return;   // padding block (-1) or foreign id
+    if ((unsigned)expert >= (unsigned)p.E) return -1;   // padding block (-1) or foreign id
     for (int i = tid; i < BM; i += NTHR) {
       const bool v = p.m_indices[r0 + i] == expert;
-      s_row[i] = v ? r0 + i : -1;
-      s_out[i] = s_row[i];
+      sm.row[i] = v ? r0 + i : -1;
+      sm.out[i] = sm.row[i];
     }
   } else {
     const int g = mb / p.blocks_per_group;
     const int r0 = (mb - g * p.blocks_per_group) * BM;
     const int cnt = min(p.masked_m[g], p.max_m);
-    if (r0 >= cnt) return;
+    if (r0 >= cnt) return -1;
     expert = g;
     for (int i = tid; i < BM; i += NTHR) {
       const int r = r0 + i;
       const bool v = r < cnt;
-      s_row[i] = v ? g * p.max_m + r : -1;
-      s_out[i] = s_row[i];
+      sm.row[i] = v ? g * p.max_m + r : -1;
+      sm.out[i] = sm.row[i];
     }
   }
-  expert = __builtin_amdgcn_readfirstlane(expert);
-  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(expert);
+}
 
-  // wave-uniform mask of token tiles holding at least one valid row
+// Wave-uniform mask of token tiles holding at least one valid row.
+template <int MT>
+__device__ __forceinline__ uint32_t active_tiles(const TileSmem<MT>& sm) {
+  const int lane = threadIdx.x & (kWave - 1);
   uint32_t tmask = 0;
 #pragma unroll
   for (int t = 0; t < MT; ++t)
-    if (__ballot(s_row[16 * t + (lane & 15)] >= 0)) tmask |= 1u << t;
+    if (__ballot(sm.row[16 * t + (lane & 15)] >= 0)) tmask |= 1u << t;
+  return tmask;
+}
+
+// acc += this wave's weight tiles x the block's rows over K chunks [c0, c1).
+// Starts and ends with the workgroup synchronised.
+template <int MT, int NR, int NW, int D>
+__device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, int expert, int nt,
+                                         uint32_t tmask, int c0, int c1, f32x4_t (&acc)[NR][MT]) {
+  constexpr int NTHR = NW * kWave;
+  constexpr int PIECES = 16 * MT * (kChunk / 8);   // 16-byte pieces per chunk
+  static_assert(PIECES % NTHR == 0, "block rows must cover the workgroup's threads");
+  constexpr int PPT = PIECES / NTHR;                // pieces per thread
+  constexpr int ROWS_PER_PASS = NTHR / 16;          // staged rows covered by one piece index
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
   // Activation staging.  Piece i of this thread is row (tid / 16) +
   // i * ROWS_PER_PASS, 16 bytes at column 8 * (tid % 16); the row's token
   // tile is wave-uniform, so inactive tiles are skipped with a scalar branch.
   // Padding rows read the block's first row (always valid) instead; their
   // LDS columns only feed output columns that are never stored.
-  const int fallback_row = s_row[0];
+  // Addressing: every stream is (wave-uniform base in SGPRs) + (per-lane
+  // 32-bit byte offset fixed for the whole loop) + (uniform chunk offset), so
+  // the per-chunk address update is scalar and loads use the saddr form.
+  const int fallback_row = sm.row[0];
   const int xcol = (tid & 15) * 8;
-  const uint16_t* xsrc[PPT];
+  const gptr_t xbase = uniform_ptr(p.a);
+  uint32_t xoff[PPT];
 #pragma unroll
   for (int i = 0; i < PPT; ++i) {
-    const int row = (tid >> 4) + i * ROWS_PER_PASS;
-    const int r = s_row[row];
-    xsrc[i] = p.a + (int64_t)(r >= 0 ? r : fallback_row) * p.K + xcol;
+    const int r = sm.row[(tid >> 4) + i * ROWS_PER_PASS];
+    xoff[i] = (uint32_t)((r >= 0 ? r : fallback_row) * p.K + xcol) * 2u;
   }
   auto piece_tile = [&](int i) { return (wave * kWave) / 256 + i * (ROWS_PER_PASS / 16); };
 
   // this wave's weight tiles (clamped so loads stay in bounds; tiles past N
   // compute throw-away values that are never stored)
   const int rt_base = nt * (NW * NR) + wave * NR;
-  const int nr_valid = min(NR, p.NT - rt_base);
-  const uint4* wptr[NR];
-  const uint16_t* sptr[NR];
+  gptr_t wbase[NR];
+  gptr_t sbase[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const int rt = min(rt_base + r, p.NT - 1);
-    const int64_t tile = ((int64_t)expert * p.NT + rt) * p.KC;
-    wptr[r] = p.packed_w + tile * kWave + lane;
-    sptr[r] = p.packed_s + tile * kWave + lane;
+    const int64_t tile = (int64_t)expert * p.NT + rt;
+    wbase[r] = uniform_ptr(p.packed_w + tile * p.KC * kWave);
+    sbase[r] = uniform_ptr(p.packed_s + tile * ((p.KC + 1) / 2) * kWave);
   }
+  const uint32_t woff = (uint32_t)lane * 16u;   // one 16-byte fragment set per lane
+  const uint32_t soff = (uint32_t)lane * 4u;    // one pair of bf16 scales per lane
 
   const int K = p.K;
-  const int KC = p.KC;
-  auto issue_x = [&](int c, uint4 (&xr)[PPT]) {
-    // ragged K: a piece past K reads column 0 of its row instead (in bounds)
-    // and is replaced by zeros when stored; no select here, so the load's
-    // destination is never rewritten before it lands
-    const int64_t off = (c * kChunk + xcol < K) ? (int64_t)c * kChunk : 0;
+  // `tail`: chunk c may be the ragged last one; a piece past K then reads
+  // column 0 of its row (in bounds) and store_x replaces it by zeros.  No
+  // select on the loaded value, so its destination is never rewritten
+  // before it lands.
+  auto issue_x = [&](int c, uint4 (&xr)[PPT], bool tail) {
+    const gptr_t base = xbase + (int64_t)c * (kChunk * 2);
+    const bool kin = !tail || c * kChunk + xcol < K;
+    // unconditional, even for token tiles without valid rows (their pieces
+    // read the block's first row): the same number of loads on every path
+    // lets the compiler wait for exactly the loads it needs, not all of them
 #pragma unroll
-    for (int i = 0; i < PPT; ++i)
-      if ((tmask >> piece_tile(i)) & 1u) xr[i] = *reinterpret_cast<const uint4*>(xsrc[i] + off);
+    for (int i = 0; i < PPT; ++i) xr[i] = gload_u32x4(kin ? base + xoff[i] : xbase + xoff[i]);
   };
-  // `tail`: the chunk may be the ragged last one, pieces past K become zeros
   auto store_x = [&](int buf, int c, const uint4 (&xr)[PPT], bool tail) {
     const bool kin = !tail || c * kChunk + xcol < K;
 #pragma unroll
     for (int i = 0; i < PPT; ++i)
       if ((tmask >> piece_tile(i)) & 1u) {
         const uint4 v = kin ? xr[i] : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(&xs[buf][(tid >> 4) + i * ROWS_PER_PASS][xcol]) = v;
+        *reinterpret_cast<uint4*>(&sm.xs[buf][(tid >> 4) + i * ROWS_PER_PASS][xcol]) = v;
       }
   };
   auto issue_w = [&](int c, uint4 (&w)[NR], uint32_t (&sc)[NR]) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      w[r] = wptr[r][(int64_t)c * kWave];
-      sc[r] = sptr[r][(int64_t)c * kWave];
+      w[r] = gload_u32x4(wbase[r] + (int64_t)c * (kWave * 16) + woff);
+      sc[r] = gload_u32(sbase[r] + (int64_t)(c >> 1) * (kWave * 4) + soff);
     }
   };
 
-  f32x4_t acc[NR][MT];
-#pragma unroll
-  for (int r = 0; r < NR; ++r)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Two register sets: chunk c uses set c % 2.  At the top of chunk c the
-  // activation pieces of chunk c + 2 are requested into the set whose data
-  // (chunk c) already sits in LDS; weights and scales of chunk c + 2 are
-  // requested as soon as chunk c's have been dequantised; chunk c + 1's
-  // activations (requested one chunk earlier) are written to the other LDS
-  // buffer before the barrier.  So every global load has about two chunk
-  // times to land, and the barrier never waits on HBM.
+  // Weights and scales: a ring of D register sets (the config's prefetch
+  // stages); chunk c0 + m*D + P uses set P, and the set is refilled with
+  // chunk c + D as soon as chunk c has been dequantised, so weights have
+  // about D chunk times to arrive from HBM.  Activations come from L2
+  // (every N tile of a block reads the same rows): one register set,
+  // requested at the top of a chunk and written to the other LDS buffer at
+  // its end, before the barrier.
+  static_assert(D >= 2 && D <= 4, "two to four prefetch stages");
   const DequantMasks masks = make_dequant_masks();
-  uint4 xr[2][PPT];
-  uint4 wr[2][NR];
-  uint32_t sr[2][NR];
+  uint4 xr[PPT];
+  uint4 wr[D][NR];
+  uint32_t sr[D][NR];
 
-  issue_x(0, xr[0]);
-  issue_w(0, wr[0], sr[0]);
-  if (KC > 1) {
-    issue_x(1, xr[1]);
-    issue_w(1, wr[1], sr[1]);
-  }
-  store_x(0, 0, xr[0], true);
+  issue_x(c0, xr, true);
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+    if (c0 + i < c1) issue_w(c0 + i, wr[i], sr[i]);
+  store_x(0, c0, xr, true);
   __syncthreads();
 
-  // one chunk; STEADY: chunks c + 1 and c + 2 exist and c + 1 is not the
-  // ragged last chunk, so every prefetch and store is unconditional (no
-  // register phis, no selects)
+  // one chunk; STEADY: chunk c + D exists and c + 1 is not the ragged last
+  // chunk, so every prefetch and store is unconditional (no register phis,
+  // no selects)
   auto chunk = [&](auto P_, auto STEADY_, int c) {
     constexpr int P = decltype(P_)::value;
     constexpr bool STEADY = decltype(STEADY_)::value;
-    const bool pf = STEADY || c + 2 < KC;
-    if (pf) issue_x(c + 2, xr[P]);
-    bf16x8_t A[NR][4];
+    const int buf = (c - c0) & 1;                   // LDS buffer holding chunk c
+    const bool next = STEADY || c + 1 < c1;
+    if (next) issue_x(c + 1, xr, !STEADY);
+    float sv[NR], cv0[NR], sv16[NR], cv1[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      const float s = bf16_bits_to_float(sr[P][r] & 0xFFFFu);
-      const float c0 = -1032.0f * s, s16 = 0.0625f * s, c1 = -72.0f * s;
-      A[r][0] = dequant8(wr[P][r].x, s, c0, s16, c1, masks);
-      A[r][1] = dequant8(wr[P][r].y, s, c0, s16, c1, masks);
-      A[r][2] = dequant8(wr[P][r].z, s, c0, s16, c1, masks);
-      A[r][3] = dequant8(wr[P][r].w, s, c0, s16, c1, masks);
+      // the word holds the scales of chunks c & ~1 (low) and c | 1 (high)
+      sv[r] = __builtin_bit_cast(float, (c & 1) ? (sr[P][r] & 0xFFFF0000u) : (sr[P][r] << 16));
+      cv0[r] = -1032.0f * sv[r];
+      sv16[r] = 0.0625f * sv[r];
+      cv1[r] = -72.0f * sv[r];
     }
-    if (pf) issue_w(c + 2, wr[P], sr[P]);
+    // one 8-wide K fragment at a time: dequantise it, read the matching
+    // activation fragments, issue its MFMAs (keeps 2 * NR operand VGPRs live
+    // instead of 8 * NR)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      bf16x8_t A[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const uint32_t d = j == 0 ? wr[P][r].x : j == 1 ? wr[P][r].y : j == 2 ? wr[P][r].z : wr[P][r].w;
+        A[r] = dequant8(d, sv[r], cv0[r], sv16[r], cv1[r], masks);
+      }
+      if (j == 3 && (STEADY || c + D < c1)) issue_w(c + D, wr[P], sr[P]);   // set P consumed
       bf16x8_t B[MT];
 #pragma unroll
       for (int t = 0; t < MT; ++t)
         if ((tmask >> t) & 1u)
           B[t] = *reinterpret_cast<const bf16x8_t*>(
-              &xs[P][16 * t + (lane & 15)][32 * (lane >> 4) + 8 * j]);
+              &sm.xs[buf][16 * t + (lane & 15)][32 * (lane >> 4) + 8 * j]);
 #pragma unroll
       for (int t = 0; t < MT; ++t)
         if ((tmask >> t) & 1u)
 #pragma unroll
           for (int r = 0; r < NR; ++r)
-            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r][j], B[t], acc[r][t], 0, 0, 0);
+            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r], B[t], acc[r][t], 0, 0, 0);
     }
-    if (STEADY || c + 1 < KC) store_x(P ^ 1, c + 1, xr[P ^ 1], !STEADY);
+    if (next) store_x(buf ^ 1, c + 1, xr, !STEADY);
     __syncthreads();
   };
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
   using Steady = std::integral_constant<bool, true>;
   using Tail = std::integral_constant<bool, false>;
-  int c = 0;
-  for (; c + 3 < KC; c += 2) {
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1 % D>;
+  using I2 = std::integral_constant<int, 2 % D>;
+  using I3 = std::integral_constant<int, 3 % D>;
+  int c = c0;
+  for (; c + 2 * D - 1 < c1; c += D) {
     chunk(I0{}, Steady{}, c);
     chunk(I1{}, Steady{}, c + 1);
+    if constexpr (D > 2) chunk(I2{}, Steady{}, c + 2);
+    if constexpr (D > 3) chunk(I3{}, Steady{}, c + 3);
   }
-  // the last one to three chunks (c is even here)
-  if (c < KC) chunk(I0{}, Tail{}, c);
-  if (c + 1 < KC) chunk(I1{}, Tail{}, c + 1);
-  if (c + 2 < KC) chunk(I0{}, Tail{}, c + 2);
+  // the last up to 2D - 1 chunks (c - c0 is a multiple of D here)
+  for (int m = 0; m < 2; ++m, c += D) {
+    if (c < c1) chunk(I0{}, Tail{}, c);
+    if (c + 1 < c1) chunk(I1{}, Tail{}, c + 1);
+    if constexpr (D > 2) if (c + 2 < c1) chunk(I2{}, Tail{}, c + 2);
+    if constexpr (D > 3) if (c + 3 < c1) chunk(I3{}, Tail{}, c + 3);
+  }
+}
 
-  // ---------------------------------------------------------------- epilogue
-  // lane holds rows n = 16*tile + 4*(lane/16) + v (v = 0..3) of token
-  // column lane % 16 of each token tile.
+// Write the tile's outputs.  Lane holds rows n = 16*tile + 4*(lane/16) + v
+// (v = 0..3) of token column lane % 16 of each token tile.
+template <int MT, int NR, int NW, int EPI>
+__device__ __forceinline__ void epilogue(const GemmParams& p, const TileSmem<MT>& sm, int nt,
+                                         uint32_t tmask, const f32x4_t (&acc)[NR][MT]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int rt_base = nt * (NW * NR) + wave * NR;
+  const int nr_valid = min(NR, p.NT - rt_base);
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     if (r >= nr_valid) continue;
@@ -261,7 +317,7 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p
     for (int t = 0; t < MT; ++t) {
       if (!((tmask >> t) & 1u)) continue;
       const int i = 16 * t + (lane & 15);
-      const int orow = s_out[i];
+      const int orow = sm.out[i];
       if (orow < 0) continue;
       const f32x4_t v = acc[r][t];
       if constexpr (EPI == kEpiStore) {
@@ -270,12 +326,140 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p
         o.y = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + (int64_t)orow * p.N + n) = o;
       } else {
-        const float w = s_w[i];
+        const float w = sm.w[i];
         float4 o = make_float4(w * v[0], w * v[1], w * v[2], w * v[3]);
         *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (int64_t)orow * p.N + n) = o;
       }
     }
   }
+}
+
+// Stream-K partial slots: slot s holds NR * MT float4 per thread, laid out
+// [(r * MT + t)][thread] so each (r, t) is one coalesced 16 * NTHR-byte store.
+template <int MT, int NR, int NW>
+__device__ __forceinline__ float4* partial_slot(const GemmParams& p, int64_t slot) {
+  constexpr int NTHR = NW * kWave;
+  return reinterpret_cast<float4*>(p.sk_partial) + slot * (int64_t)(NR * MT * NTHR);
+}
+
+template <int MT, int NR, int NW, int D, int ROUTE, int EPI>
+__global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(16))) TileSmem<MT> sm;
+  const int mb = blockIdx.x / p.n_tiles;
+  const int nt = blockIdx.x - mb * p.n_tiles;
+  const int expert = setup_rows<MT, NW, ROUTE, EPI>(p, mb, sm);
+  if (expert < 0) return;
+  __syncthreads();
+  const uint32_t tmask = active_tiles<MT>(sm);
+  f32x4_t acc[NR][MT];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  mainloop<MT, NR, NW, D>(p, sm, expert, nt, tmask, 0, p.KC, acc);
+  epilogue<MT, NR, NW, EPI>(p, sm, nt, tmask, acc);
+}
+
+// Work partition shared by the stream-K kernel and its fix-up: `units`
+// (tile, chunk) units split into ranges of `per` units, one per workgroup.
+struct SkPartition {
+  int64_t units, per;
+};
+
+template <int MT, int ROUTE>
+__device__ __forceinline__ SkPartition sk_partition(const GemmParams& p, int64_t workgroups) {
+  const int64_t units = (int64_t)live_blocks<MT, ROUTE>(p) * p.n_tiles * p.KC;
+  return SkPartition{units, (units + workgroups - 1) / workgroups};
+}
+
+template <int MT, int NR, int NW, int D, int ROUTE, int EPI>
+__global__ __launch_bounds__(NW * kWave) void moe_gemm_streamk_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(16))) TileSmem<MT> sm;
+  constexpr int NTHR = NW * kWave;
+  const SkPartition part = sk_partition<MT, ROUTE>(p, gridDim.x);
+  const int64_t g = blockIdx.x;
+  const int64_t end = min(part.units, (g + 1) * part.per);
+  const int KC = p.KC;
+  bool first = true;
+  for (int64_t u = g * part.per; u < end;) {
+    const int64_t item = u / KC;
+    const int c0 = (int)(u - item * KC);
+    const int c1 = (int)min((int64_t)KC, c0 + (end - u));
+    const int mb = (int)(item / p.n_tiles);
+    const int nt = (int)(item - (int64_t)mb * p.n_tiles);
+    __syncthreads();                       // previous tile's LDS readers are done
+    const int expert = setup_rows<MT, NW, ROUTE, EPI>(p, mb, sm);
+    __syncthreads();
+    if (expert >= 0) {
+      const uint32_t tmask = active_tiles<MT>(sm);
+      f32x4_t acc[NR][MT];
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      mainloop<MT, NR, NW, D>(p, sm, expert, nt, tmask, c0, c1, acc);
+      if (c0 == 0 && c1 == KC) {
+        epilogue<MT, NR, NW, EPI>(p, sm, nt, tmask, acc);
+      } else {
+        // a range holds at most two cut tiles: its first and its last
+        float4* slot = partial_slot<MT, NR, NW>(p, 2 * g + (first ? 0 : 1));
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+            if ((tmask >> t) & 1u) {
+              const f32x4_t v = acc[r][t];
+              slot[(r * MT + t) * NTHR + threadIdx.x] = make_float4(v[0], v[1], v[2], v[3]);
+            }
+      }
+    }
+    first = false;
+    u += c1 - c0;
+  }
+}
+
+// One workgroup per range boundary: if the boundary cuts a tile and is the
+// first boundary inside it, sum that tile's partials in range order (the
+// order of the K chunks they cover) and write its outputs.
+template <int MT, int NR, int NW, int ROUTE, int EPI>
+__global__ __launch_bounds__(NW * kWave) void streamk_fixup_kernel(const GemmParams p, int sk_grid) {
+  __shared__ __attribute__((aligned(16))) TileSmem<MT> sm;
+  constexpr int NTHR = NW * kWave;
+  const SkPartition part = sk_partition<MT, ROUTE>(p, sk_grid);
+  const int KC = p.KC;
+  const int64_t g = (int64_t)blockIdx.x + 1;       // boundary between ranges g-1 and g
+  const int64_t b = g * part.per;
+  if (b >= part.units || b % KC == 0) return;      // boundary at a tile edge: nothing cut
+  const int64_t item = b / KC;
+  if ((g - 1) * part.per > item * KC) return;      // an earlier boundary inside this tile owns it
+  const int mb = (int)(item / p.n_tiles);
+  const int nt = (int)(item - (int64_t)mb * p.n_tiles);
+  const int expert = setup_rows<MT, NW, ROUTE, EPI>(p, mb, sm);
+  if (expert < 0) return;
+  __syncthreads();
+  const uint32_t tmask = active_tiles<MT>(sm);
+  f32x4_t acc[NR][MT];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int64_t h0 = item * KC / part.per, h1 = ((item + 1) * KC - 1) / part.per;
+  for (int64_t h = h0; h <= h1; ++h) {
+    const int64_t slot = (h * part.per) / KC == item ? 2 * h : 2 * h + 1;
+    const float4* src = partial_slot<MT, NR, NW>(p, slot);
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        if ((tmask >> t) & 1u) {
+          const float4 v = src[(r * MT + t) * NTHR + threadIdx.x];
+          acc[r][t][0] += v.x;
+          acc[r][t][1] += v.y;
+          acc[r][t][2] += v.z;
+          acc[r][t][3] += v.w;
+        }
+  }
+  epilogue<MT, NR, NW, EPI>(p, sm, nt, tmask, acc);
 }
 
 // Top-k combine: out[t, n] = bf16(sum over local j, in j order, of
@@ -319,39 +503,86 @@ hipError_t launch_combine(const float* partial, const int32_t* topk_ids, int32_t
 
 // ------------------------------------------------------------------ dispatch
 typedef void (*GemmKernel)(const GemmParams);
+typedef void (*FixupKernel)(const GemmParams, int);
 
-template <int MT, int NR, int NW>
-static GemmKernel pick_kernel(int route, int epi) {
+struct KernelSet {
+  GemmKernel classic = nullptr;
+  GemmKernel streamk = nullptr;
+  FixupKernel fixup = nullptr;
+};
+
+template <int MT, int NR, int NW, int D, int ROUTE, int EPI>
+static KernelSet make_set() {
+  KernelSet s;
+  s.classic = moe_gemm_kernel<MT, NR, NW, D, ROUTE, EPI>;
+  s.streamk = moe_gemm_streamk_kernel<MT, NR, NW, D, ROUTE, EPI>;
+  s.fixup = streamk_fixup_kernel<MT, NR, NW, ROUTE, EPI>;
+  return s;
+}
+
+template <int MT, int NR, int NW, int D>
+static KernelSet pick(int route, int epi) {
   if (route == kRouteIndexed)
-    return epi == kEpiWeighted ? moe_gemm_kernel<MT, NR, NW, kRouteIndexed, kEpiWeighted>
-                               : moe_gemm_kernel<MT, NR, NW, kRouteIndexed, kEpiStore>;
-  if (epi != kEpiStore) return nullptr;
-  if (route == kRouteContiguous) return moe_gemm_kernel<MT, NR, NW, kRouteContiguous, kEpiStore>;
-  if (route == kRouteMasked) return moe_gemm_kernel<MT, NR, NW, kRouteMasked, kEpiStore>;
-  return nullptr;
+    return epi == kEpiWeighted ? make_set<MT, NR, NW, D, kRouteIndexed, kEpiWeighted>()
+                               : make_set<MT, NR, NW, D, kRouteIndexed, kEpiStore>();
+  if (epi != kEpiStore) return KernelSet{};
+  if (route == kRouteContiguous) return make_set<MT, NR, NW, D, kRouteContiguous, kEpiStore>();
+  if (route == kRouteMasked) return make_set<MT, NR, NW, D, kRouteMasked, kEpiStore>();
+  return KernelSet{};
 }
 
-static GemmKernel find_kernel(int route, int epi, int m_tiles, int nr, int waves) {
-  if (waves != 4) return nullptr;
-#define W4A16_CASE(MT_, NR_) \
-  if (m_tiles == MT_ && nr == NR_) return pick_kernel<MT_, NR_, 4>(route, epi);
-  W4A16_CASE(1, 2) W4A16_CASE(2, 2) W4A16_CASE(4, 2) W4A16_CASE(8, 2)
-  W4A16_CASE(1, 4) W4A16_CASE(2, 4) W4A16_CASE(4, 4) W4A16_CASE(8, 4)
+// Built tile configurations: every (MT, NR) with two prefetch stages; three
+// and four stages for the decode tiles (MT <= 2, NR = 2).
+static KernelSet find_kernels(int route, int epi, int m_tiles, int nr, int waves, int stages) {
+  if (waves != 4) return KernelSet{};
+#define W4A16_CASE(MT_, NR_, D_) \
+  if (m_tiles == MT_ && nr == NR_ && stages == D_) return pick<MT_, NR_, 4, D_>(route, epi);
+  W4A16_CASE(1, 2, 2) W4A16_CASE(2, 2, 2) W4A16_CASE(4, 2, 2) W4A16_CASE(8, 2, 2)
+  W4A16_CASE(1, 4, 2) W4A16_CASE(2, 4, 2) W4A16_CASE(4, 4, 2) W4A16_CASE(8, 4, 2)
+  W4A16_CASE(1, 2, 3) W4A16_CASE(2, 2, 3) W4A16_CASE(1, 2, 4) W4A16_CASE(2, 2, 4)
 #undef W4A16_CASE
-  return nullptr;
+  return KernelSet{};
 }
 
-bool gemm_config_supported(int route, int epilogue, int m_tiles, int nr, int waves) {
-  return find_kernel(route, epilogue, m_tiles, nr, waves) != nullptr;
+bool gemm_config_supported(int route, int epilogue, int m_tiles, int nr, int waves, int stages) {
+  return find_kernels(route, epilogue, m_tiles, nr, waves, stages).classic != nullptr;
 }
 
-hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves,
-                       const GemmParams& p, int64_t grid_blocks, hipStream_t stream) {
-  GemmKernel k = find_kernel(route, epilogue, m_tiles, nr, waves);
-  if (k == nullptr) return hipErrorInvalidValue;
-  const int64_t grid = grid_blocks * p.n_tiles;
+hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves, int stages,
+                       const GemmParams& p, hipStream_t stream) {
+  const KernelSet k = find_kernels(route, epilogue, m_tiles, nr, waves, stages);
+  if (k.classic == nullptr) return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)p.grid_blocks * p.n_tiles;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(waves * kWave), 0, stream, p);
+  hipLaunchKernelGGL(k.classic, dim3((unsigned)grid), dim3(waves * kWave), 0, stream, p);
+  return hipGetLastError();
+}
+
+int streamk_workgroups(int route, int epilogue, int m_tiles, int nr, int waves, int stages) {
+  const KernelSet k = find_kernels(route, epilogue, m_tiles, nr, waves, stages);
+  if (k.streamk == nullptr) return 0;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k.streamk),
+                                                   waves * kWave, 0) != hipSuccess)
+    return 0;
+  return cus * std::max(per_cu, 1);
+}
+
+size_t streamk_partial_bytes(int m_tiles, int nr, int waves, int workgroups) {
+  return (size_t)2 * workgroups * (size_t)(nr * m_tiles * waves * kWave) * 16;
+}
+
+hipError_t launch_gemm_streamk(int route, int epilogue, int m_tiles, int nr, int waves, int stages,
+                               const GemmParams& p, int workgroups, hipStream_t stream) {
+  const KernelSet k = find_kernels(route, epilogue, m_tiles, nr, waves, stages);
+  if (k.streamk == nullptr || workgroups <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k.streamk, dim3((unsigned)workgroups), dim3(waves * kWave), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || workgroups < 2) return e;
+  hipLaunchKernelGGL(k.fixup, dim3((unsigned)(workgroups - 1)), dim3(waves * kWave), 0, stream, p,
+                     workgroups);
   return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@ hipError_t launch_align(const int32_t* topk_ids, int32_t total_slots, int32_t fi
 // ---- packer (pack.hip)
 hipError_t launch_pack(const uint8_t* codes, const uint16_t* scales, int32_t E, int32_t N,
                        int32_t K, int32_t KC, uint32_t* packed_w,
-                       uint16_t* packed_s, hipStream_t stream);
+                       uint32_t* packed_s, hipStream_t stream);
 
 // ---- GEMM (gemm.hip)
 enum RouteKind : int { kRouteIndexed = 0, kRouteContiguous = 1, kRouteMasked = 2 };
@@ -23,7 +23,7 @@ enum EpilogueKind : int { kEpiStore = 0, kEpiWeighted = 1 };
 
 struct GemmParams {
   const uint4* packed_w;        // [E][NT][KC][64][4 words]
-  const uint16_t* packed_s;     // [E][NT][KC][64]
+  const uint32_t* packed_s;     // [E][NT][KC2][64], bf16 scale pairs
   const uint16_t* a;            // bf16 activations, row stride K
   int32_t E, N, K, NT, KC;
   int32_t n_tiles;              // workgroup tiles along N
@@ -42,13 +42,32 @@ struct GemmParams {
   int32_t blocks_per_group;
   // output: bf16 [rows][N] (store) or fp32 [rows][N] (weighted)
   void* out;
+  // routed blocks (all kinds; for indexed the live count comes from
+  // num_tokens_padded on the device, this is the capacity bound)
+  int32_t grid_blocks;
+  // stream-K: fp32 partial tiles, two slots per persistent workgroup
+  float* sk_partial;
 };
 
 // m_tiles: 16-row token tiles per block (block_m / 16); nr: 16-row weight
-// tiles per wave; waves: waves per workgroup; grid_blocks: routed blocks.
-hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves,
-                       const GemmParams& p, int64_t grid_blocks, hipStream_t stream);
-bool gemm_config_supported(int route, int epilogue, int m_tiles, int nr, int waves);
+// tiles per wave; waves: waves per workgroup; stages: chunks of weights in
+// flight per wave (2 or 3).
+bool gemm_config_supported(int route, int epilogue, int m_tiles, int nr, int waves, int stages);
+
+// One workgroup per (routed block, N tile), full K each.
+hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves, int stages,
+                       const GemmParams& p, hipStream_t stream);
+
+// Stream-K: `workgroups` persistent workgroups each take an equal contiguous
+// range of (tile, 128-K chunk) units; tiles cut by a range boundary leave
+// fp32 partials in p.sk_partial that a fix-up kernel sums in range order.
+hipError_t launch_gemm_streamk(int route, int epilogue, int m_tiles, int nr, int waves, int stages,
+                               const GemmParams& p, int workgroups, hipStream_t stream);
+
+// Persistent workgroups for stream-K on the current device (resident
+// workgroups per CU x CUs), and the partial-tile bytes they need.
+int streamk_workgroups(int route, int epilogue, int m_tiles, int nr, int waves, int stages);
+size_t streamk_partial_bytes(int m_tiles, int nr, int waves, int workgroups);
 
 // ---- combine of weighted per-slot partials (gemm.hip)
 hipError_t launch_combine(const float* partial, const int32_t* topk_ids, int32_t T, int32_t topk,

@@ -41,28 +41,32 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const uint8_t* __restrict__
 __global__ __launch_bounds__(256) void pack_s_kernel(const uint16_t* __restrict__ scales,
                                                      int32_t N, int32_t K, int32_t NT,
                                                      int32_t KC, int64_t total,
-                                                     uint16_t* __restrict__ packed_s) {
-  // output index = ((e * NT + tile) * KC + c) * 64 + lane
+                                                     uint32_t* __restrict__ packed_s) {
+  // output word index = ((e * NT + tile) * KC2 + m) * 64 + lane; the word
+  // holds the lane's scale for chunk 2m (low half) and 2m + 1 (high half)
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
+  const int KC2 = (KC + 1) / 2;
   const int l = (int)(idx & 63);
   int64_t rest = idx >> 6;
-  const int c = (int)(rest % KC);
-  rest /= KC;
+  const int m = (int)(rest % KC2);
+  rest /= KC2;
   const int tile = (int)(rest % NT);
   const int64_t e = rest / NT;
   const int n = tile * kRowTile + (l & 15);
-  const int grp = 4 * c + (l >> 4);
   const int G = K / kGroup;
-  packed_s[idx] = grp < G ? scales[(e * N + n) * (int64_t)G + grp] : (uint16_t)0;
+  const uint16_t* row = scales + (e * N + n) * (int64_t)G;
+  const int g0 = 4 * (2 * m) + (l >> 4), g1 = g0 + 4;
+  const uint32_t lo = g0 < G ? row[g0] : 0u, hi = g1 < G ? row[g1] : 0u;
+  packed_s[idx] = lo | (hi << 16);
 }
 
 hipError_t launch_pack(const uint8_t* codes, const uint16_t* scales, int32_t E, int32_t N,
                        int32_t K, int32_t KC, uint32_t* packed_w,
-                       uint16_t* packed_s, hipStream_t stream) {
+                       uint32_t* packed_s, hipStream_t stream) {
   const int32_t NT = N / kRowTile;
   const int64_t words = (int64_t)E * NT * KC * 256;
-  const int64_t sents = (int64_t)E * NT * KC * 64;
+  const int64_t sents = (int64_t)E * NT * ((KC + 1) / 2) * 64;
   hipLaunchKernelGGL(pack_w_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
                      codes, N, K, NT, KC, words, packed_w);
   hipError_t err = hipGetLastError();
