@@ -69,6 +69,7 @@ def main() -> int:
     ap.add_argument("--workload", default="ep8_decode")
     ap.add_argument("--block-m", type=int, default=0, help="override the selector's block_m")
     ap.add_argument("--nr", type=int, default=0, help="override the selector's weight tiles per wave")
+    ap.add_argument("--waves", type=int, default=0, help="override the selector's waves per workgroup")
     ap.add_argument("--split-k", type=int, default=-1, help="override: 0 stream-K, 1 one workgroup per tile")
     ap.add_argument("--stages", type=int, default=0, help="override: K chunks of weights in flight per wave")
     ap.add_argument("--cpu-experts", type=int, default=4, help="experts in the CPU-baseline sample (0: skip)")
@@ -109,6 +110,8 @@ def main() -> int:
         cfg.block_m = args.block_m
     if args.nr:
         cfg.nr = args.nr
+    if args.waves:
+        cfg.waves = args.waves
     if args.split_k >= 0:
         cfg.split_k = args.split_k
     if args.stages:

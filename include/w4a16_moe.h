@@ -165,7 +165,7 @@ typedef struct {
                         tiles cut between two workgroups are finished from
                         fp32 partials in workspace, summed in K order (results
                         then depend on the device's CU count, not on timing) */
-  int32_t stages;    /* K chunks of weights each wave keeps in flight: 2, or 3
+  int32_t stages;    /* K chunks of weights each wave keeps in flight: 2, or 4
                         for block_m <= 32 with nr = 2 */
 } w4a16_config;
 

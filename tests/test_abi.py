@@ -78,8 +78,9 @@ def test_capacity_and_workspace(L):
     assert W.workspace_bytes(p, 10, 8, True, W.config(32, 3)) == 0          # unsupported config
     d = W.indexed_config(64)
     assert (d.block_m, d.nr, d.waves, d.split_k, d.stages) == (64, 2, 4, 1, 2)
-    assert W.workspace_bytes(p, 10, 8, True, W.config(32, 2, stages=3)) == 10 * 8 * 7168 * 4
-    assert W.workspace_bytes(p, 10, 8, True, W.config(64, 4, stages=3)) == 0   # not built
+    assert W.workspace_bytes(p, 10, 8, True, W.config(32, 2, stages=4)) == 10 * 8 * 7168 * 4
+    assert W.workspace_bytes(p, 10, 8, True, W.config(64, 4, stages=4)) == 0   # not built
+    assert W.workspace_bytes(p, 10, 8, True, W.config(32, 2, stages=3)) == 0   # odd depth: not built
 
 
 def test_align_argument_errors(L):

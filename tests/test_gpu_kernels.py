@@ -106,11 +106,11 @@ def test_pack_round_trip_bit_exact(E, N, K):
 
 # ------------------------------------------------------------ indexed GEMM
 
-def _run_indexed(P, bm, nr=None, first=None, stages=2):
+def _run_indexed(P, bm, nr=None, first=None, stages=2, waves=4):
     sh = P.sh
     first = sh.first if first is None else first
     r = M.moe_align(P.d_ids, sh.E_glob, first, sh.E_loc, bm)
-    cfg = M.config(bm, nr if nr else (4 if bm >= 64 else 2), stages=stages)
+    cfg = M.config(bm, nr if nr else (4 if bm >= 64 else 2), waves=waves, stages=stages)
     h = M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=cfg)
     y = M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=cfg) if P.with_down else None
     torch.cuda.synchronize()
@@ -133,17 +133,17 @@ def _check_indexed(P, h, y, what):
 
 
 def test_tiny_workload_all_tile_configs_match_oracle_and_each_other():
-    """Every built tile configuration, including the pipeline depth (2 or 3
+    """Every built tile configuration, including the pipeline depth (2 or 4
     chunks of weights in flight), gives the same output bits."""
     P = Problem(W.WORKLOADS["tiny"]).upload()
     outs = {}
-    combos = [(bm, nr, 2) for bm, nr in itertools.product((16, 32, 64, 128), (2, 4))]
-    combos += [(16, 2, 3), (32, 2, 3)]
-    for bm, nr, st in combos:
-        _, h, y = _run_indexed(P, bm, nr, stages=st)
-        _check_indexed(P, h, y, f"tiny bm={bm} nr={nr} stages={st}")
-        outs[(bm, nr, st)] = (bits(h), bits(y))
-    base = outs[(16, 2, 2)]
+    combos = [(bm, nr, 2, 4) for bm, nr in itertools.product((16, 32, 64, 128), (2, 4))]
+    combos += [(16, 2, 4, 4), (32, 2, 4, 4), (16, 2, 2, 8), (32, 2, 2, 8), (128, 2, 2, 8)]
+    for bm, nr, st, nw in combos:
+        _, h, y = _run_indexed(P, bm, nr, stages=st, waves=nw)
+        _check_indexed(P, h, y, f"tiny bm={bm} nr={nr} stages={st} waves={nw}")
+        outs[(bm, nr, st, nw)] = (bits(h), bits(y))
+    base = outs[(16, 2, 2, 4)]
     for key, (h, y) in outs.items():          # tile configuration does not change bits
         np.testing.assert_array_equal(h, base[0], err_msg=str(key))
         np.testing.assert_array_equal(y, base[1], err_msg=str(key))
@@ -157,8 +157,29 @@ def test_ragged_shapes():
     for bm in (16, 32, 128):
         _, h, y = _run_indexed(P, bm)
         _check_indexed(P, h, y, f"ragged bm={bm}")
-    _, h, y = _run_indexed(P, 32, stages=3)
-    _check_indexed(P, h, y, "ragged bm=32 stages=3")
+    _, h, y = _run_indexed(P, 32, stages=4)
+    _check_indexed(P, h, y, "ragged bm=32 stages=4")
+    for bm in (16, 32, 128):
+        _, h, y = _run_indexed(P, bm, 2, waves=8)
+        _check_indexed(P, h, y, f"ragged bm={bm} waves=8")
+
+
+def test_multi_chunk_k():
+    """K spanning many 128-wide chunks (steady-state loop plus its tail, both
+    prefetch depths), ragged and not, against the oracle; depths agree bit
+    for bit."""
+    for K1, K2 in ((1312, 1024), (2304, 1184)):
+        sh = W.MoEShape(name=f"k{K1}", E_glob=8, E_loc=6, first=1, topk=2, T=40, K1=K1, N1=96,
+                        K2=K2, N2=80, seed=91)
+        P = Problem(sh).upload()
+        outs = []
+        for bm, st, nw in ((16, 2, 4), (32, 4, 4), (64, 2, 4), (16, 2, 8), (32, 2, 8), (128, 2, 8)):
+            _, h, y = _run_indexed(P, bm, 2, stages=st, waves=nw)
+            _check_indexed(P, h, y, f"K1={K1} K2={K2} bm={bm} stages={st} waves={nw}")
+            outs.append((bits(h), bits(y)))
+        for h, y in outs[1:]:
+            np.testing.assert_array_equal(h, outs[0][0])
+            np.testing.assert_array_equal(y, outs[0][1])
 
 
 def test_one_hot_activations_return_dequantised_weights_bit_exact():
@@ -299,15 +320,15 @@ def test_grouped_contiguous_and_masked_small():
     P = Problem(sh, with_down=False).upload()
     A, mi, slots = W.contiguous_layout(P.topk_ids, P.x, sh.first, sh.E_loc, pad=128, pad_fill=0x7FC0)
     ref, valid = O.grouped_contiguous(A, P.c1, P.s1, mi)
-    for bm in (16, 64, 128):
-        out = bits(M.grouped_contiguous(to_dev_bf16(A), P.p1, to_dev(mi), cfg=M.config(bm, 4 if bm >= 64 else 2)))
-        assert_close(out[valid], ref[valid], f"contiguous bm={bm}")
+    for bm, nr, nw in ((16, 2, 4), (64, 4, 4), (128, 4, 4), (128, 2, 8), (32, 2, 8)):
+        out = bits(M.grouped_contiguous(to_dev_bf16(A), P.p1, to_dev(mi), cfg=M.config(bm, nr, waves=nw)))
+        assert_close(out[valid], ref[valid], f"contiguous bm={bm} nr={nr} waves={nw}")
     A3, mm, sl3, dropped = W.masked_layout(P.topk_ids, P.x, sh.first, sh.E_loc, sh.max_m, pad_fill=0x7FC0)
     log("masked dropped", dropped, "masked_m", mm.tolist())
     ref, valid = O.grouped_masked(A3, P.c1, P.s1, mm)
-    for bm in (16, 32, 64):
-        out = bits(M.grouped_masked(to_dev_bf16(A3), P.p1, to_dev(mm), 32, cfg=M.config(bm, 2)))
-        assert_close(out[valid], ref[valid], f"masked bm={bm}")
+    for bm, nw in ((16, 4), (32, 4), (64, 4), (16, 8), (32, 8)):
+        out = bits(M.grouped_masked(to_dev_bf16(A3), P.p1, to_dev(mm), 32, cfg=M.config(bm, 2, waves=nw)))
+        assert_close(out[valid], ref[valid], f"masked bm={bm} waves={nw}")
     out = bits(M.grouped_masked(to_dev_bf16(A3), P.p1, to_dev(mm), expected_m=max(1, int(mm.mean()))))
     assert_close(out[valid], ref[valid], "masked auto config")
     # grouped and indexed agree on the same rows

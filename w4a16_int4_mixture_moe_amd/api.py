@@ -145,7 +145,7 @@ def select(T: int, topk: int, E_glob: int, E_loc: int, N: int, K: int) -> Config
 
 def config(block_m: int, nr: int, waves: int = 4, split_k: int = 1, stages: int = 2) -> Config:
     """split_k = 1: one workgroup per tile; 0: stream-K over resident workgroups.
-    stages: K chunks of weights in flight per wave (2, or 3 for small tiles)."""
+    stages: K chunks of weights in flight per wave (2, or 4 for small tiles)."""
     return Config(block_m, nr, waves, split_k, stages)
 
 

@@ -29,6 +29,10 @@ SOURCES = ["api.cpp", "align.hip", "pack.hip", "gemm.hip"]
 COMMON = [
     f"--offload-arch={ARCH}", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: with accumulation registers the
+    # allocator rotates the GEMM accumulators between registers inside the
+    # main loop, and every such move waits for an MFMA
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -162,11 +162,12 @@ const char* env_str(const char* name) {
   return (v && *v) ? v : nullptr;
 }
 
-// W4A16_BLOCK_M / W4A16_NR / W4A16_SPLIT_K / W4A16_STAGES override the selector (read on every call; the
-// memoised result is the selector's, overrides are applied on top).
+// W4A16_BLOCK_M / W4A16_NR / W4A16_WAVES / W4A16_SPLIT_K / W4A16_STAGES override the selector (read on
+// every call; the memoised result is the selector's, overrides are applied on top).
 void apply_env_overrides(w4a16_config* c) {
   if (const char* v = env_str("W4A16_BLOCK_M")) c->block_m = std::atoi(v);
   if (const char* v = env_str("W4A16_NR")) c->nr = std::atoi(v);
+  if (const char* v = env_str("W4A16_WAVES")) c->waves = std::atoi(v);
   if (const char* v = env_str("W4A16_SPLIT_K")) c->split_k = std::atoi(v);
   if (const char* v = env_str("W4A16_STAGES")) c->stages = std::atoi(v);
 }

@@ -82,9 +82,8 @@ __device__ __forceinline__ gptr_t uniform_ptr(const T* p) {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint4 gload_u32x4(gptr_t p) {
-  const u32x4_t v = *reinterpret_cast<const u32x4_t __attribute__((address_space(1)))*>(p);
-  return make_uint4(v[0], v[1], v[2], v[3]);
+__device__ __forceinline__ u32x4_t gload_u32x4(gptr_t p) {
+  return *reinterpret_cast<const u32x4_t __attribute__((address_space(1)))*>(p);
 }
 
 __device__ __forceinline__ uint32_t gload_u32(gptr_t p) {

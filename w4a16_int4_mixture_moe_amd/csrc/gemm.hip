@@ -132,38 +132,50 @@ __device__ __forceinline__ uint32_t active_tiles(const TileSmem<MT>& sm) {
 }
 
 // acc += this wave's weight tiles x the block's rows over K chunks [c0, c1).
-// Starts and ends with the workgroup synchronised.
-template <int MT, int NR, int NW, int D>
+// Starts and ends with the workgroup synchronised.  The active token tiles
+// are always a prefix (valid rows come first in every layout).  NA > 0:
+// exactly tiles [0, NA) are active, fixed at compile time, so the loop loads,
+// reads and multiplies only those, without per-tile branches.  NA = 0: any
+// prefix, tested against tmask inside the loop.
+template <int MT, int NR, int NW, int D, int NA>
 __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, int expert, int nt,
                                          uint32_t tmask, int c0, int c1, f32x4_t (&acc)[NR][MT]) {
   constexpr int NTHR = NW * kWave;
-  constexpr int PIECES = 16 * MT * (kChunk / 8);   // 16-byte pieces per chunk
-  static_assert(PIECES % NTHR == 0, "block rows must cover the workgroup's threads");
-  constexpr int PPT = PIECES / NTHR;                // pieces per thread
   constexpr int ROWS_PER_PASS = NTHR / 16;          // staged rows covered by one piece index
+  static_assert(ROWS_PER_PASS == 16 || ROWS_PER_PASS == 32, "four or eight waves");
+  constexpr int PPT = (16 * MT + ROWS_PER_PASS - 1) / ROWS_PER_PASS;   // pieces per thread
+  static_assert(NA >= 0 && NA <= MT, "active tile count");
+  constexpr bool FIXED = NA > 0;
+  auto active = [&](int t) { return FIXED ? t < NA : ((tmask >> t) & 1u) != 0; };
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
   // Activation staging.  Piece i of this thread is row (tid / 16) +
-  // i * ROWS_PER_PASS, 16 bytes at column 8 * (tid % 16); the row's token
-  // tile is wave-uniform, so inactive tiles are skipped with a scalar branch.
-  // Padding rows read the block's first row (always valid) instead; their
-  // LDS columns only feed output columns that are never stored.
+  // i * ROWS_PER_PASS, 16 bytes at column 8 * (tid % 16); its token tile is
+  // wave-uniform (a wave covers 4 consecutive rows), so pieces of inactive
+  // tiles, or past the block (eight waves, one tile), are skipped with a
+  // scalar branch.  Padding rows read the block's first row (always valid)
+  // instead; their LDS columns only feed output columns never stored.
   // Addressing: every stream is (wave-uniform base in SGPRs) + (per-lane
   // 32-bit byte offset fixed for the whole loop) + (uniform chunk offset), so
   // the per-chunk address update is scalar and loads use the saddr form.
   const int fallback_row = sm.row[0];
   const int xcol = (tid & 15) * 8;
   const gptr_t xbase = uniform_ptr(p.a);
+  auto piece_row = [&](int i) { return (tid >> 4) + i * ROWS_PER_PASS; };
+  // wave-uniform: the tile of piece i, and whether the piece is loaded
+  auto piece_tile = [&](int i) { return ROWS_PER_PASS == 16 ? i : 2 * i + (wave >> 2); };
+  auto piece_on = [&](int i) {
+    return FIXED ? piece_tile(i) < NA : piece_tile(i) < MT;
+  };
   uint32_t xoff[PPT];
 #pragma unroll
   for (int i = 0; i < PPT; ++i) {
-    const int r = sm.row[(tid >> 4) + i * ROWS_PER_PASS];
+    const int r = sm.row[min(piece_row(i), 16 * MT - 1)];
     xoff[i] = (uint32_t)((r >= 0 ? r : fallback_row) * p.K + xcol) * 2u;
   }
-  auto piece_tile = [&](int i) { return (wave * kWave) / 256 + i * (ROWS_PER_PASS / 16); };
 
   // this wave's weight tiles (clamped so loads stay in bounds; tiles past N
   // compute throw-away values that are never stored)
@@ -185,25 +197,26 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
   // column 0 of its row (in bounds) and store_x replaces it by zeros.  No
   // select on the loaded value, so its destination is never rewritten
   // before it lands.
-  auto issue_x = [&](int c, uint4 (&xr)[PPT], bool tail) {
+  auto issue_x = [&](int c, u32x4_t (&xr)[PPT], bool tail) {
     const gptr_t base = xbase + (int64_t)c * (kChunk * 2);
     const bool kin = !tail || c * kChunk + xcol < K;
-    // unconditional, even for token tiles without valid rows (their pieces
+    // with NA = 0, unconditional even for inactive token tiles (their pieces
     // read the block's first row): the same number of loads on every path
     // lets the compiler wait for exactly the loads it needs, not all of them
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) xr[i] = gload_u32x4(kin ? base + xoff[i] : xbase + xoff[i]);
+    for (int i = 0; i < PPT; ++i)
+      if (piece_on(i)) xr[i] = gload_u32x4(kin ? base + xoff[i] : xbase + xoff[i]);
   };
-  auto store_x = [&](int buf, int c, const uint4 (&xr)[PPT], bool tail) {
+  auto store_x = [&](int buf, int c, const u32x4_t (&xr)[PPT], bool tail) {
     const bool kin = !tail || c * kChunk + xcol < K;
 #pragma unroll
     for (int i = 0; i < PPT; ++i)
-      if ((tmask >> piece_tile(i)) & 1u) {
-        const uint4 v = kin ? xr[i] : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(&sm.xs[buf][(tid >> 4) + i * ROWS_PER_PASS][xcol]) = v;
+      if (piece_on(i) && active(piece_tile(i))) {
+        const u32x4_t v = kin ? xr[i] : u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t*>(&sm.xs[buf][piece_row(i)][xcol]) = v;
       }
   };
-  auto issue_w = [&](int c, uint4 (&w)[NR], uint32_t (&sc)[NR]) {
+  auto issue_w = [&](int c, u32x4_t (&w)[NR], uint32_t (&sc)[NR]) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       w[r] = gload_u32x4(wbase[r] + (int64_t)c * (kWave * 16) + woff);
@@ -217,29 +230,38 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
   // about D chunk times to arrive from HBM.  Activations come from L2
   // (every N tile of a block reads the same rows): one register set,
   // requested at the top of a chunk and written to the other LDS buffer at
-  // its end, before the barrier.
-  static_assert(D >= 2 && D <= 4, "two to four prefetch stages");
+  // its end, before the barrier.  (A second set, for two chunks of
+  // distance, measured no faster and costs registers.)
+  static_assert(D == 2 || D == 4, "the loop body below unrolls two or four chunks");
   const DequantMasks masks = make_dequant_masks();
-  uint4 xr[PPT];
-  uint4 wr[D][NR];
+  // 128-bit vector registers (not the 4-field struct): each loop-carried
+  // value stays one register tuple that the allocator can keep in place
+  u32x4_t xr[PPT];
+  u32x4_t wr[D][NR];
   uint32_t sr[D][NR];
 
+  // c0 < c1 (both callers).  Unconditional, clamped (a set past the range
+  // re-reads the last chunk and is never used) and in ring order: the waits
+  // inside the loop are computed for the worst entry path, so a conditional
+  // or reordered load here would make every chunk wait for the newest loads.
   issue_x(c0, xr, true);
 #pragma unroll
-  for (int i = 0; i < D; ++i)
-    if (c0 + i < c1) issue_w(c0 + i, wr[i], sr[i]);
+  for (int i = 0; i < D; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(min(c0 + i, c1 - 1), wr[i], sr[i]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   store_x(0, c0, xr, true);
   __syncthreads();
 
-  // one chunk; STEADY: chunk c + D exists and c + 1 is not the ragged last
-  // chunk, so every prefetch and store is unconditional (no register phis,
-  // no selects)
+  // one chunk at ring position P (c - c0 = P mod D).  STEADY: chunks c + 1
+  // and c + D exist and c + 1 is not the ragged last chunk, so every
+  // prefetch and store is unconditional (no register phis, no selects)
   auto chunk = [&](auto P_, auto STEADY_, int c) {
     constexpr int P = decltype(P_)::value;
     constexpr bool STEADY = decltype(STEADY_)::value;
     const int buf = (c - c0) & 1;                   // LDS buffer holding chunk c
-    const bool next = STEADY || c + 1 < c1;
-    if (next) issue_x(c + 1, xr, !STEADY);
+    if (STEADY || c + 1 < c1) issue_x(c + 1, xr, !STEADY);
     float sv[NR], cv0[NR], sv16[NR], cv1[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -257,46 +279,98 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
       bf16x8_t A[NR];
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        const uint32_t d = j == 0 ? wr[P][r].x : j == 1 ? wr[P][r].y : j == 2 ? wr[P][r].z : wr[P][r].w;
+        const uint32_t d = wr[P][r][j];
         A[r] = dequant8(d, sv[r], cv0[r], sv16[r], cv1[r], masks);
       }
-      if (j == 3 && (STEADY || c + D < c1)) issue_w(c + D, wr[P], sr[P]);   // set P consumed
+      if (j == 3 && (STEADY || c + D < c1)) {
+        // set P is consumed: refill it in place.  The empty asm (it takes the
+        // dequantised operands) and the scheduling barrier keep the loads
+        // below the last dequant of the old values: moved past them, old and
+        // new values overlap, the new ones land in other registers and the
+        // loop back-edge copies them over, which waits for the loads just
+        // issued and serialises the prefetch
+#pragma unroll
+        for (int r = 0; r < NR; ++r) asm volatile("" ::"v"(A[r]));
+        __builtin_amdgcn_sched_barrier(0);
+        issue_w(c + D, wr[P], sr[P]);
+        // and keep them above the chunk's activation store: moved below it,
+        // the store's wait (for the newest activation load) would also wait
+        // for these
+        __builtin_amdgcn_sched_barrier(0);
+      }
       bf16x8_t B[MT];
 #pragma unroll
       for (int t = 0; t < MT; ++t)
-        if ((tmask >> t) & 1u)
+        if (active(t))
           B[t] = *reinterpret_cast<const bf16x8_t*>(
               &sm.xs[buf][16 * t + (lane & 15)][32 * (lane >> 4) + 8 * j]);
 #pragma unroll
       for (int t = 0; t < MT; ++t)
-        if ((tmask >> t) & 1u)
+        if (active(t))
 #pragma unroll
           for (int r = 0; r < NR; ++r)
             acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r], B[t], acc[r][t], 0, 0, 0);
     }
-    if (next) store_x(buf ^ 1, c + 1, xr, !STEADY);
+    if (STEADY || c + 1 < c1) store_x(buf ^ 1, c + 1, xr, !STEADY);
     __syncthreads();
   };
 
   using Steady = std::integral_constant<bool, true>;
   using Tail = std::integral_constant<bool, false>;
   using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1 % D>;
+  using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2 % D>;
   using I3 = std::integral_constant<int, 3 % D>;
   int c = c0;
   for (; c + 2 * D - 1 < c1; c += D) {
     chunk(I0{}, Steady{}, c);
     chunk(I1{}, Steady{}, c + 1);
-    if constexpr (D > 2) chunk(I2{}, Steady{}, c + 2);
-    if constexpr (D > 3) chunk(I3{}, Steady{}, c + 3);
+    if constexpr (D > 2) {
+      chunk(I2{}, Steady{}, c + 2);
+      chunk(I3{}, Steady{}, c + 3);
+    }
   }
   // the last up to 2D - 1 chunks (c - c0 is a multiple of D here)
   for (int m = 0; m < 2; ++m, c += D) {
     if (c < c1) chunk(I0{}, Tail{}, c);
     if (c + 1 < c1) chunk(I1{}, Tail{}, c + 1);
-    if constexpr (D > 2) if (c + 2 < c1) chunk(I2{}, Tail{}, c + 2);
-    if constexpr (D > 3) if (c + 3 < c1) chunk(I3{}, Tail{}, c + 3);
+    if constexpr (D > 2) {
+      if (c + 2 < c1) chunk(I2{}, Tail{}, c + 2);
+      if (c + 3 < c1) chunk(I3{}, Tail{}, c + 3);
+    }
+  }
+}
+
+// One tile's K range [c0, c1): zeroed accumulators, the main loop
+// specialised for the block's active token tiles (a workgroup-uniform
+// prefix), then finish(acc, mask).  One- and two-tile blocks run exactly
+// their active tiles; larger blocks run the checked loop (a second copy of
+// their loop would need a second set of accumulators).  Each path owns its
+// accumulators and finishes on its own: merging them into one array before
+// a shared epilogue makes the allocator rotate them between registers with
+// moves inside the loop, each of which waits for an MFMA.
+template <int MT, int NR, int NW, int D, typename Finish>
+__device__ __forceinline__ void run_tile(const GemmParams& p, TileSmem<MT>& sm, int expert, int nt,
+                                         uint32_t tmask, int c0, int c1, Finish&& finish) {
+  auto go = [&](auto na) {
+    constexpr int NA = decltype(na)::value;
+    f32x4_t acc[NR][MT];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    mainloop<MT, NR, NW, D, NA>(p, sm, expert, nt, tmask, c0, c1, acc);
+    finish(acc, NA > 0 ? (1u << NA) - 1u : tmask);
+  };
+  if constexpr (MT == 1) {
+    go(std::integral_constant<int, 1>{});
+  } else if constexpr (MT == 2) {
+    if (tmask == 1u)
+      go(std::integral_constant<int, 1>{});
+    else
+      go(std::integral_constant<int, 2>{});
+  } else {
+    go(std::integral_constant<int, 0>{});
   }
 }
 
@@ -351,13 +425,9 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p
   if (expert < 0) return;
   __syncthreads();
   const uint32_t tmask = active_tiles<MT>(sm);
-  f32x4_t acc[NR][MT];
-#pragma unroll
-  for (int r = 0; r < NR; ++r)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  mainloop<MT, NR, NW, D>(p, sm, expert, nt, tmask, 0, p.KC, acc);
-  epilogue<MT, NR, NW, EPI>(p, sm, nt, tmask, acc);
+  run_tile<MT, NR, NW, D>(p, sm, expert, nt, tmask, 0, p.KC, [&](const f32x4_t(&acc)[NR][MT], uint32_t tm) {
+    epilogue<MT, NR, NW, EPI>(p, sm, nt, tm, acc);
+  });
 }
 
 // Work partition shared by the stream-K kernel and its fix-up: `units`
@@ -392,26 +462,22 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_streamk_kernel(const Gemm
     __syncthreads();
     if (expert >= 0) {
       const uint32_t tmask = active_tiles<MT>(sm);
-      f32x4_t acc[NR][MT];
+      run_tile<MT, NR, NW, D>(p, sm, expert, nt, tmask, c0, c1, [&](const f32x4_t(&acc)[NR][MT], uint32_t tm) {
+        if (c0 == 0 && c1 == KC) {
+          epilogue<MT, NR, NW, EPI>(p, sm, nt, tm, acc);
+        } else {
+          // a range holds at most two cut tiles: its first and its last
+          float4* slot = partial_slot<MT, NR, NW>(p, 2 * g + (first ? 0 : 1));
 #pragma unroll
-      for (int r = 0; r < NR; ++r)
+          for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      mainloop<MT, NR, NW, D>(p, sm, expert, nt, tmask, c0, c1, acc);
-      if (c0 == 0 && c1 == KC) {
-        epilogue<MT, NR, NW, EPI>(p, sm, nt, tmask, acc);
-      } else {
-        // a range holds at most two cut tiles: its first and its last
-        float4* slot = partial_slot<MT, NR, NW>(p, 2 * g + (first ? 0 : 1));
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-#pragma unroll
-          for (int t = 0; t < MT; ++t)
-            if ((tmask >> t) & 1u) {
-              const f32x4_t v = acc[r][t];
-              slot[(r * MT + t) * NTHR + threadIdx.x] = make_float4(v[0], v[1], v[2], v[3]);
-            }
-      }
+            for (int t = 0; t < MT; ++t)
+              if ((tm >> t) & 1u) {
+                const f32x4_t v = acc[r][t];
+                slot[(r * MT + t) * NTHR + threadIdx.x] = make_float4(v[0], v[1], v[2], v[3]);
+              }
+        }
+      });
     }
     first = false;
     u += c1 - c0;
@@ -531,15 +597,17 @@ static KernelSet pick(int route, int epi) {
   return KernelSet{};
 }
 
-// Built tile configurations: every (MT, NR) with two prefetch stages; three
-// and four stages for the decode tiles (MT <= 2, NR = 2).
+// Built tile configurations (MT, NR, waves, stages): every (MT, NR) with four
+// waves and two prefetch stages; four stages for the decode tiles (MT <= 2,
+// NR = 2); eight waves (twice the weight rows per staged activation chunk)
+// for MT = 1, 2 and 8 with NR = 2.
 static KernelSet find_kernels(int route, int epi, int m_tiles, int nr, int waves, int stages) {
-  if (waves != 4) return KernelSet{};
-#define W4A16_CASE(MT_, NR_, D_) \
-  if (m_tiles == MT_ && nr == NR_ && stages == D_) return pick<MT_, NR_, 4, D_>(route, epi);
-  W4A16_CASE(1, 2, 2) W4A16_CASE(2, 2, 2) W4A16_CASE(4, 2, 2) W4A16_CASE(8, 2, 2)
-  W4A16_CASE(1, 4, 2) W4A16_CASE(2, 4, 2) W4A16_CASE(4, 4, 2) W4A16_CASE(8, 4, 2)
-  W4A16_CASE(1, 2, 3) W4A16_CASE(2, 2, 3) W4A16_CASE(1, 2, 4) W4A16_CASE(2, 2, 4)
+#define W4A16_CASE(MT_, NR_, NW_, D_) \
+  if (m_tiles == MT_ && nr == NR_ && waves == NW_ && stages == D_) return pick<MT_, NR_, NW_, D_>(route, epi);
+  W4A16_CASE(1, 2, 4, 2) W4A16_CASE(2, 2, 4, 2) W4A16_CASE(4, 2, 4, 2) W4A16_CASE(8, 2, 4, 2)
+  W4A16_CASE(1, 4, 4, 2) W4A16_CASE(2, 4, 4, 2) W4A16_CASE(4, 4, 4, 2) W4A16_CASE(8, 4, 4, 2)
+  W4A16_CASE(1, 2, 4, 4) W4A16_CASE(2, 2, 4, 4)
+  W4A16_CASE(1, 2, 8, 2) W4A16_CASE(2, 2, 8, 2) W4A16_CASE(8, 2, 8, 2)
 #undef W4A16_CASE
   return KernelSet{};
 }
