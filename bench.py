@@ -27,6 +27,12 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+# Measured HBM traffic of the gate/up GEMM (rocprofv3 FETCH_SIZE / WRITE_SIZE
+# per dispatch, scaled by a copy of known size); valid only for the kernel
+# sources it was taken on, identified by their hash.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "moe_gemm_ep8_decode_traffic.md")
+KERNEL_SOURCES = ["w4a16_int4_mixture_moe_amd/csrc/gemm.hip", "w4a16_int4_mixture_moe_amd/csrc/device_common.hpp",
+                  "w4a16_int4_mixture_moe_amd/csrc/launch.hpp", "w4a16_int4_mixture_moe_amd/build.py"]
 
 
 def log(*a):
@@ -36,6 +42,49 @@ def log(*a):
 def weight_bytes(n_touched: int, N: int, K: int) -> int:
     """Packed INT4 weights (K/2 bytes per row) + bf16 group-32 scales."""
     return n_touched * (N * K // 2 + N * (K // 32) * 2)
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, cfg_tag: str):
+    """HBM bytes per gate/up launch from the committed counter summary, or
+    None when there is none for this workload and config or the kernel
+    sources changed since the counters were taken."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    import re
+    m = re.search(r"<!-- traffic: (\{.*?\}) -->", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("workload") != workload or rec.get("config") != cfg_tag:
+        return None
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    return int(round(rec["fetch_kib"] * 1024 * rec["fetch_factor"] + rec["write_kib"] * 1024 * rec["write_factor"]))
+
+
+def copy_calibration() -> int:
+    """A plain device copy of 1 GiB, three times: the reference that scales
+    the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    x = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": x.numel() * 4, "copies": 3}), flush=True)
+    return 0
 
 
 def cpu_baseline(sh, ids, wts, x, a, c1, s1, c2, s2, n_experts: int) -> dict:
@@ -72,9 +121,13 @@ def main() -> int:
     ap.add_argument("--waves", type=int, default=0, help="override the selector's waves per workgroup")
     ap.add_argument("--split-k", type=int, default=-1, help="override: 0 stream-K, 1 one workgroup per tile")
     ap.add_argument("--stages", type=int, default=0, help="override: K chunks of weights in flight per wave")
-    ap.add_argument("--cpu-experts", type=int, default=4, help="experts in the CPU-baseline sample (0: skip)")
+    ap.add_argument("--cpu-experts", type=int, default=20, help="experts in the CPU-baseline sample (0: skip)")
     ap.add_argument("--eager", action="store_true", help="launch the step eagerly instead of replaying a HIP graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB three times (reference for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(collectives and sharding are out of scope); run with --gpus 1", file=sys.stderr)
@@ -211,6 +264,7 @@ def main() -> int:
     # the routing indices
     alg1 = wb1 + n_local * sh.K1 * 2 + n_local * sh.N1 * 2 + n_ntp * 4 + (n_ntp // cfg.block_m) * 4
     value = (wb1 + wb2) / (ms_step * 1e-3) / 1e9
+    cfg_tag = f"bm{cfg.block_m} nr{cfg.nr} waves{cfg.waves} split_k{cfg.split_k} stages{cfg.stages}"
     gu_gbs = alg1 / (us_gu * 1e-6) / 1e9
     flops1 = 2.0 * n_local * sh.N1 * sh.K1
     flops2 = 2.0 * n_local * sh.N2 * sh.K2
@@ -243,7 +297,8 @@ def main() -> int:
         },
         "roofline": {"kernel": "moe_gemm_kernel (gate/up)", "bound": "hbm",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(sh.name, cfg_tag),
                      "algorithmic_bytes": int(alg1)},
     }
     if args.cpu_experts > 0:

@@ -370,7 +370,10 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, TileSmem<MT>& sm, 
     else
       go(std::integral_constant<int, 2>{});
   } else {
-    go(std::integral_constant<int, 0>{});
+    if (tmask == (1u << MT) - 1u)
+      go(std::integral_constant<int, MT>{});
+    else
+      go(std::integral_constant<int, 0>{});
   }
 }
 
@@ -620,8 +623,14 @@ hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves, 
                        const GemmParams& p, hipStream_t stream) {
   const KernelSet k = find_kernels(route, epilogue, m_tiles, nr, waves, stages);
   if (k.classic == nullptr) return hipErrorInvalidValue;
+  // Consecutive workgroups (the N tiles of one block) go to different XCDs
+  // (round robin), so the L2 requests for a block's activation rows spread
+  // over all eight L2s.  (Keeping a block's N tiles on one XCD, which saves
+  // the repeated activation fetch, measured several times slower: all its
+  // workgroups then request the same lines from one L2 at once.)
   const int64_t grid = (int64_t)p.grid_blocks * p.n_tiles;
   if (grid <= 0) return hipSuccess;
+  if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(k.classic, dim3((unsigned)grid), dim3(waves * kWave), 0, stream, p);
   return hipGetLastError();
 }
