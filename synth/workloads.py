@@ -186,6 +186,18 @@ for _t in TP8_TOKENS:
     WORKLOADS[f"tp8_t{_t}"] = _cfg(3, name=f"tp8_t{_t}", E_glob=384, E_loc=384, first=0,
                                    topk=8, T=_t, K1=7168, N1=512, K2=256, N2=7168)
 
+# Second workloads on the same kernels: the EP16 and EP32 shares of the same
+# layer (24 and 12 local experts; the Chord post's grouped tables cover EP8,
+# EP16 and EP32), and a Kimi-K3-like routing shape (16 of 896 experts per
+# token, AMD's Kimi-K3 post) on the K2.x projection shapes, since that post
+# gives the routing but not the projection sizes.
+for _i, (_name, _eloc, _T, _zipf) in enumerate((("ep16_decode", 24, 576, None), ("ep32_decode", 12, 576, None),
+                                                ("ep16_prefill", 24, 8192, 1.0), ("ep32_prefill", 12, 8192, 1.0))):
+    WORKLOADS[_name] = _cfg(5 + _i, name=_name, E_glob=384, E_loc=_eloc, first=0, topk=8, T=_T,
+                            K1=7168, N1=4096, K2=2048, N2=7168, zipf_s=_zipf)
+WORKLOADS["k3_decode"] = _cfg(9, name="k3_decode", E_glob=896, E_loc=112, first=0, topk=16, T=576,
+                              K1=7168, N1=4096, K2=2048, N2=7168)
+
 
 def zero_expert_ids(shape: MoEShape) -> np.ndarray:
     """Seeded choice of local experts that receive no rows."""

@@ -53,8 +53,9 @@ def _indexed_full(P, name):
     log(name, dict(gate_up_max_err=e1, gate_up_exact=x1, down_max_err=e2, down_exact=x2))
 
 
-@pytest.mark.parametrize("name", ["ep8_decode", "ep8_prefill"])
-def test_ep8_full_size(name):
+@pytest.mark.parametrize("name", ["ep8_decode", "ep8_prefill", "ep16_decode", "ep32_decode", "ep16_prefill",
+                                  "ep32_prefill", "k3_decode"])
+def test_ep_full_size(name):
     log("generating", name)
     P = Problem(W.WORKLOADS[name]).upload()
     _indexed_full(P, name)

@@ -147,13 +147,15 @@ w4a16_config select_config(int32_t T, int32_t topk, int32_t E_glob, int32_t E_lo
       }
     c.nr = 2;
   }
-  // Stream-K only when the tile grid would leave resident workgroups idle
-  // (the post keeps stream-K where the plain grid under-fills the machine,
-  // section "H200 prefill and TP8"); otherwise one workgroup per tile keeps
-  // more waves resident, which the latency-bound decode tiles need more.
+  // Stream-K only when the tile grid would leave most resident workgroups
+  // idle (the post keeps stream-K where the plain grid under-fills the
+  // machine, section "H200 prefill and TP8").  Measured on MI355X: stream-K
+  // wins clearly below half a round of resident workgroups (TP8 at small T),
+  // ties around 0.4 (EP32 decode) and loses at 0.75 (EP16 decode, about 10 %,
+  // mostly its fix-up pass), so the gate is half a round.
   const int64_t tiles = sampled_blocks(counts, c.block_m) * ((N / 16 + 4 * c.nr - 1) / (4 * c.nr));
   const int resident = resident_workgroups(c, w4a16::kEpiStore);
-  if (resident > 0 && tiles < resident) c.split_k = 0;
+  if (resident > 0 && 2 * tiles < resident) c.split_k = 0;
   return c;
 }
 

@@ -131,6 +131,11 @@ __device__ __forceinline__ uint32_t active_tiles(const TileSmem<MT>& sm) {
   return tmask;
 }
 
+#ifndef W4A16_PIPELINED_DEQUANT
+#define W4A16_PIPELINED_DEQUANT 1
+#endif
+constexpr bool kPipelinedDequant = W4A16_PIPELINED_DEQUANT != 0;
+
 // acc += this wave's weight tiles x the block's rows over K chunks [c0, c1).
 // Starts and ends with the workgroup synchronised.  The active token tiles
 // are always a prefix (valid rows come first in every layout).  NA > 0:
@@ -257,64 +262,105 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
   // one chunk at ring position P (c - c0 = P mod D).  STEADY: chunks c + 1
   // and c + D exist and c + 1 is not the ragged last chunk, so every
   // prefetch and store is unconditional (no register phis, no selects)
+  // Scale constants of chunk c for a weight set: s, -1032 s, s / 16, -72 s
+  // (the word holds the scales of chunks c & ~1 (low half) and c | 1 (high))
+  auto scale_consts = [&](const uint32_t (&sc)[NR], int c, float (&k)[NR][4]) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float sv = __builtin_bit_cast(float, (c & 1) ? (sc[r] & 0xFFFF0000u) : (sc[r] << 16));
+      k[r][0] = sv;
+      k[r][1] = -1032.0f * sv;
+      k[r][2] = 0.0625f * sv;
+      k[r][3] = -72.0f * sv;
+    }
+  };
+  auto dequant_set = [&](const u32x4_t (&w)[NR], int j, const float (&k)[NR][4], bf16x8_t (&A)[NR]) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) A[r] = dequant8(w[r][j], k[r][0], k[r][1], k[r][2], k[r][3], masks);
+  };
+  auto mfmas = [&](int buf, int j, const bf16x8_t (&A)[NR]) {
+    bf16x8_t B[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      if (active(t))
+        B[t] = *reinterpret_cast<const bf16x8_t*>(&sm.xs[buf][16 * t + (lane & 15)][32 * (lane >> 4) + 8 * j]);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      if (active(t))
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r], B[t], acc[r][t], 0, 0, 0);
+  };
+  // refill weight set P with chunk c + D once its last word is dequantised
+  // (A holds that word's operands).  The empty asm and the scheduling
+  // barrier keep the loads below that dequant: moved above it, old and new
+  // values overlap, the new ones land in other registers and the loop
+  // back-edge copies them over, which waits for the loads just issued and
+  // serialises the prefetch.  The second barrier keeps them above the
+  // chunk's activation store, whose wait (for the newest activation load)
+  // would otherwise cover them too.
+  auto refill = [&](auto P_, int c, const bf16x8_t (&A)[NR]) {
+    constexpr int P = decltype(P_)::value;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) asm volatile("" ::"v"(A[r]));
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(c + D, wr[P], sr[P]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Pipelined form (fixed active tiles): fragment j + 1 is dequantised
+  // before fragment j's MFMAs are issued, so the VALU work of one overlaps
+  // the matrix work of the other inside a wave; the last fragment of a chunk
+  // dequantises the first one of the next chunk (its weights are already
+  // resident).  Acur / kcur carry that across chunks.
+  constexpr bool PIPE = FIXED && kPipelinedDequant;
+  bf16x8_t Acur[NR];
+  float kcur[NR][4];
+  if constexpr (PIPE) {
+    scale_consts(sr[0], c0, kcur);
+    dequant_set(wr[0], 0, kcur, Acur);
+  }
+
+  // one chunk at ring position P (c - c0 = P mod D).  STEADY: chunks c + 1
+  // and c + D exist and c + 1 is not the ragged last chunk, so every
+  // prefetch and store is unconditional (no register phis, no selects)
   auto chunk = [&](auto P_, auto STEADY_, int c) {
     constexpr int P = decltype(P_)::value;
     constexpr bool STEADY = decltype(STEADY_)::value;
     const int buf = (c - c0) & 1;                   // LDS buffer holding chunk c
     if (STEADY || c + 1 < c1) issue_x(c + 1, xr, !STEADY);
-    float sv[NR], cv0[NR], sv16[NR], cv1[NR];
+    if constexpr (PIPE) {
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      // the word holds the scales of chunks c & ~1 (low) and c | 1 (high)
-      sv[r] = __builtin_bit_cast(float, (c & 1) ? (sr[P][r] & 0xFFFF0000u) : (sr[P][r] << 16));
-      cv0[r] = -1032.0f * sv[r];
-      sv16[r] = 0.0625f * sv[r];
-      cv1[r] = -72.0f * sv[r];
-    }
-    // one 8-wide K fragment at a time: dequantise it, read the matching
-    // activation fragments, issue its MFMAs (keeps 2 * NR operand VGPRs live
-    // instead of 8 * NR)
+      for (int j = 0; j < 4; ++j) {
+        bf16x8_t Anext[NR];
+        if (j < 3) {
+          dequant_set(wr[P], j + 1, kcur, Anext);
+          if (j == 2 && (STEADY || c + D < c1)) refill(P_, c, Anext);
+        } else if (STEADY || c + 1 < c1) {
+          constexpr int PN = (P + 1) % D;
+          scale_consts(sr[PN], c + 1, kcur);
+          dequant_set(wr[PN], 0, kcur, Anext);
+        }
+        mfmas(buf, j, Acur);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8_t A[NR];
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const uint32_t d = wr[P][r][j];
-        A[r] = dequant8(d, sv[r], cv0[r], sv16[r], cv1[r], masks);
+        for (int r = 0; r < NR; ++r) Acur[r] = Anext[r];
       }
-      if (j == 3 && (STEADY || c + D < c1)) {
-        // set P is consumed: refill it in place.  The empty asm (it takes the
-        // dequantised operands) and the scheduling barrier keep the loads
-        // below the last dequant of the old values: moved past them, old and
-        // new values overlap, the new ones land in other registers and the
-        // loop back-edge copies them over, which waits for the loads just
-        // issued and serialises the prefetch
+    } else {
+      float k[NR][4];
+      scale_consts(sr[P], c, k);
+      // one 8-wide K fragment at a time: dequantise it, read the matching
+      // activation fragments, issue its MFMAs
 #pragma unroll
-        for (int r = 0; r < NR; ++r) asm volatile("" ::"v"(A[r]));
-        __builtin_amdgcn_sched_barrier(0);
-        issue_w(c + D, wr[P], sr[P]);
-        // and keep them above the chunk's activation store: moved below it,
-        // the store's wait (for the newest activation load) would also wait
-        // for these
-        __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < 4; ++j) {
+        bf16x8_t A[NR];
+        dequant_set(wr[P], j, k, A);
+        if (j == 3 && (STEADY || c + D < c1)) refill(P_, c, A);
+        mfmas(buf, j, A);
       }
-      bf16x8_t B[MT];
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-        if (active(t))
-          B[t] = *reinterpret_cast<const bf16x8_t*>(
-              &sm.xs[buf][16 * t + (lane & 15)][32 * (lane >> 4) + 8 * j]);
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-        if (active(t))
-#pragma unroll
-          for (int r = 0; r < NR; ++r)
-            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r], B[t], acc[r][t], 0, 0, 0);
     }
     if (STEADY || c + 1 < c1) store_x(buf ^ 1, c + 1, xr, !STEADY);
     __syncthreads();
   };
-
   using Steady = std::integral_constant<bool, true>;
   using Tail = std::integral_constant<bool, false>;
   using I0 = std::integral_constant<int, 0>;
