@@ -123,6 +123,9 @@ def main() -> int:
     ap.add_argument("--stages", type=int, default=0, help="override: K chunks of weights in flight per wave")
     ap.add_argument("--cpu-experts", type=int, default=20, help="experts in the CPU-baseline sample (0: skip)")
     ap.add_argument("--eager", action="store_true", help="launch the step eagerly instead of replaying a HIP graph")
+    ap.add_argument("--fused", action="store_true",
+                    help="chained layer: gate/up with the SiLU activation fused, written in sorted order, "
+                         "read as is by the down projection (instead of a synthetic per-slot down input)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB three times (reference for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -153,7 +156,7 @@ def main() -> int:
     def bf(b):
         return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    p1 = M.pack_w4(torch.from_numpy(c1).to(dev), bf(s1))
+    p1 = M.pack_w4(torch.from_numpy(c1).to(dev), bf(s1), gate_up=args.fused)
     p2 = M.pack_w4(torch.from_numpy(c2).to(dev), bf(s2))
     d_ids = torch.from_numpy(ids).to(dev)
     d_w = torch.from_numpy(wts).to(dev)
@@ -190,11 +193,23 @@ def main() -> int:
                                        cfg.block_m, sorted_ids.data_ptr(), expert_ids.data_ptr(),
                                        ntp.data_ptr(), cap, 0, s_ptr))
 
+    inter = torch.zeros(cap, sh.N1 // 2, dtype=torch.bfloat16, device=dev) if args.fused else None
+    if args.fused and (sh.K2 != sh.N1 // 2 or cfg.split_k != 1 or cfg.nr % 2):
+        log("--fused needs K2 = N1 / 2, split_k = 1 and an even nr")
+        return 2
+
     def gate_up():
-        M.moe_w4a16_gemm(d_x, p1, routing, cfg=cfg, out=h, workspace=ws1)
+        if args.fused:
+            M.moe_gate_up_silu(d_x, p1, routing, cfg=cfg, out=inter)
+        else:
+            M.moe_w4a16_gemm(d_x, p1, routing, cfg=cfg, out=h, workspace=ws1)
 
     def down():
-        M.moe_w4a16_gemm(d_a, p2, routing, topk_weights=d_w, cfg=cfg, out=y, workspace=ws2)
+        if args.fused:
+            M.moe_w4a16_gemm(inter, p2, routing, topk_weights=d_w, a_layout="sorted", cfg=cfg, out=y,
+                             workspace=ws2)
+        else:
+            M.moe_w4a16_gemm(d_a, p2, routing, topk_weights=d_w, cfg=cfg, out=y, workspace=ws2)
 
     def step():
         align()
@@ -262,7 +277,8 @@ def main() -> int:
     # algorithmic bytes per gate/up launch: weights+scales of touched experts,
     # one activation row read and one output row written per routed slot,
     # the routing indices
-    alg1 = wb1 + n_local * sh.K1 * 2 + n_local * sh.N1 * 2 + n_ntp * 4 + (n_ntp // cfg.block_m) * 4
+    out1 = n_local * (sh.N1 // 2 if args.fused else sh.N1) * 2   # fused: the activation, half the columns
+    alg1 = wb1 + n_local * sh.K1 * 2 + out1 + n_ntp * 4 + (n_ntp // cfg.block_m) * 4
     value = (wb1 + wb2) / (ms_step * 1e-3) / 1e9
     cfg_tag = f"bm{cfg.block_m} nr{cfg.nr} waves{cfg.waves} split_k{cfg.split_k} stages{cfg.stages}"
     gu_gbs = alg1 / (us_gu * 1e-6) / 1e9
@@ -283,7 +299,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": sh.name, "T": T, "topk": k, "E_glob": sh.E_glob, "E_loc": sh.E_loc,
+        "config": {"workload": sh.name, "fused_silu": bool(args.fused), "T": T, "topk": k, "E_glob": sh.E_glob, "E_loc": sh.E_loc,
                    "K1": sh.K1, "N1": sh.N1, "K2": sh.K2, "N2": sh.N2, "block_m": cfg.block_m,
                    "nr": cfg.nr, "waves": cfg.waves, "split_k": cfg.split_k, "stages": cfg.stages, "routed_rows": n_local,
                    "experts_touched": touched, "num_tokens_padded": n_ntp},

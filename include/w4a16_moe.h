@@ -58,7 +58,7 @@ typedef enum {
 const char* w4a16_last_error(void);
 
 /* ABI version of this header (W4A16_ABI_VERSION). */
-#define W4A16_ABI_VERSION 1
+#define W4A16_ABI_VERSION 2
 int32_t w4a16_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -87,9 +87,16 @@ int32_t w4a16_abi_version(void);
  *     c = 2m + 1 (high half), 0 past K / 32: the one scale each of its
  *     chunks needs, so a wave's scales for a chunk pair are one 256-byte run.
  *   packed_w is E * NT * KC * 1024 bytes, packed_s is E * NT * KC2 * 256.
+ *
+ * Gate/up interleaved (flag W4A16_DESC_GATE_UP): a gate/up projection whose
+ * rows [0, N/2) are the gate and [N/2, N) the up rows is packed with their
+ * 16-row tiles alternating: packed tile 2i holds gate tile i, packed tile
+ * 2i + 1 up tile i.  Every call on such a weight still produces output
+ * columns in the logical order; the fused SiLU gate/up call needs it.
  * ---------------------------------------------------------------------- */
 #define W4A16_DESC_MAGIC 0x16A4B0E5u /* arbitrary tag */
-#define W4A16_DESC_VERSION 1u
+#define W4A16_DESC_VERSION 2u
+#define W4A16_DESC_GATE_UP 1         /* flags: gate/up tiles interleaved */
 
 typedef struct {
   uint32_t magic;       /* W4A16_DESC_MAGIC */
@@ -98,6 +105,8 @@ typedef struct {
   int32_t K_pad;        /* KP above */
   int32_t chunks;       /* KC above */
   int32_t group;        /* 32 */
+  int32_t flags;        /* 0 or W4A16_DESC_GATE_UP */
+  int32_t reserved;     /* 0 */
   uint64_t w_bytes;     /* size of packed_w */
   uint64_t s_bytes;     /* size of packed_s */
   uint64_t check;       /* checksum of the fields above */
@@ -106,6 +115,11 @@ typedef struct {
 /* Fill *out for an [E, N, K] weight (host only, no device work).
  * Errors: ERR_ARG (out NULL, E/N/K <= 0), ERR_SHAPE (K % 32 or N % 16). */
 w4a16_status w4a16_weight_desc_init(int32_t E, int32_t N, int32_t K, w4a16_weight_desc* out);
+
+/* The same for a gate/up weight packed with interleaved tiles (flag
+ * W4A16_DESC_GATE_UP): rows [0, N/2) gate, [N/2, N) up.
+ * Errors: as above, and ERR_SHAPE when N % 32 != 0. */
+w4a16_status w4a16_weight_desc_init_gate_up(int32_t E, int32_t N, int32_t K, w4a16_weight_desc* out);
 
 /* Pack codes [E, N, K] (uint8) and scales [E, N, K/32] (bf16) into the
  * layout above.  `desc` must come from w4a16_weight_desc_init for the same
@@ -202,10 +216,16 @@ typedef struct {
 size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, int32_t T, int32_t topk,
                                       int32_t combine, const w4a16_config* cfg);
 
+/* Row layouts of the activations `a` (argument a_layout). */
+#define W4A16_A_TOKEN 0   /* one row per token, [T, K] (gate/up input) */
+#define W4A16_A_SLOT 1    /* one row per slot t * topk + j, [T * topk, K] */
+#define W4A16_A_SORTED 2  /* one row per sorted position p (row p serves the
+                             slot sorted_ids[p]), [capacity, K]: the output of
+                             w4a16_moe_gate_up_silu, read without a gather */
+
 /* out = routed W4A16 product.
- *  a          : bf16 activations, row stride K (desc->K).  a_per_slot = 0:
- *               one row per token ([T, K], gate/up); a_per_slot = 1: one row
- *               per slot ([T * topk, K], down).  a_rows = rows in `a`.
+ *  a          : bf16 activations, row stride K (desc->K), rows as a_layout
+ *               says; a_rows = rows in `a`.
  *  topk_weights == NULL: per-slot output out[T * topk, N]; only local slots
  *               are written, other rows keep their contents.
  *  topk_weights != NULL (float32 [T, topk]): top-k-weighted combine,
@@ -220,10 +240,34 @@ size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, int32_t T, 
  * Errors: ERR_ARG, ERR_LAYOUT, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP. */
 w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
                             const void* packed_s, const uint16_t* a, int64_t a_rows,
-                            int32_t a_per_slot, const w4a16_indexed_routing* routing,
+                            int32_t a_layout, const w4a16_indexed_routing* routing,
                             const float* topk_weights, uint16_t* out,
                             const w4a16_config* cfg, void* workspace, size_t workspace_bytes,
                             w4a16_stream_t stream);
+
+/* Gate/up projection with the activation between the two projections
+ * fused into its epilogue, written in sorted order for the down projection.
+ * (The post's layer numbers exclude the activation, section "Measurement";
+ * fusing it and keeping rows in sorted order removes a launch, a pass over
+ * the intermediate and the down projection's row gather.)
+ *  desc       : a W4A16_DESC_GATE_UP weight, N = 2 * I.
+ *  x          : bf16 token rows [x_rows, K], x_rows >= routing->T.
+ *  out        : bf16 [routing->capacity, I]; for each sorted position p that
+ *               holds a local slot s = sorted_ids[p] = t * topk + j:
+ *               out[p][n] = bf16(silu(g) * u), g = bf16(x[t] . W_gate[n]),
+ *               u = bf16(x[t] . W_up[n]) (the same bf16 values the unfused
+ *               per-slot call writes), silu(g) = g / (1 + exp(-g)) in fp32.
+ *               Padding positions are left unwritten (the down call never
+ *               uses them).
+ *  cfg        : NULL: w4a16_indexed_config(routing->block_m); one workgroup
+ *               per tile (split_k = 1), nr even.
+ * Pointers 16-byte aligned.
+ * Errors: ERR_ARG, ERR_LAYOUT (not a gate/up weight), ERR_SHAPE,
+ * ERR_UNSUPPORTED, ERR_HIP. */
+w4a16_status w4a16_moe_gate_up_silu(const w4a16_weight_desc* desc, const void* packed_w,
+                                    const void* packed_s, const uint16_t* x, int64_t x_rows,
+                                    const w4a16_indexed_routing* routing, uint16_t* out,
+                                    const w4a16_config* cfg, w4a16_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Grouped layouts (the post's grouped family, section "Grouped SM90

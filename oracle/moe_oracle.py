@@ -287,6 +287,21 @@ def silu_mul(h_bits: np.ndarray) -> np.ndarray:
     return f64_to_bf16(g / (1.0 + np.exp(-g)) * u)
 
 
+def gate_up_silu_sorted(h_bits: np.ndarray, sorted_ids: np.ndarray, sentinel: int):
+    """The activation between the projections, placed in sorted order: for
+    each sorted position p holding a slot s (sorted_ids[p] < sentinel),
+    out[p] = silu_mul(h[s]), h the per-slot gate/up output.  Padding
+    positions are not defined (mask False).  (The post excludes this step
+    from its layer numbers, section "Measurement"; gate = first half of the
+    gate/up columns.)
+    Returns (out uint16 [len(sorted_ids), N/2], valid bool [len(sorted_ids)])."""
+    sid = np.asarray(sorted_ids).astype(np.int64)
+    valid = sid < sentinel
+    out = np.zeros((len(sid), h_bits.shape[1] // 2), dtype=np.uint16)
+    out[valid] = silu_mul(h_bits[sid[valid]])
+    return out, valid
+
+
 # ---------------------------------------------------------------- fp32 baseline
 
 def indexed_gate_up_fp32(x_bits, codes, scale_bits, topk_ids, first, E_loc):

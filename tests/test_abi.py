@@ -36,13 +36,14 @@ def test_every_declared_function_is_exported_and_bound(L):
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(_lib.WeightDesc) == 56
+    assert ctypes.sizeof(_lib.WeightDesc) == 64
+    assert _lib.WeightDesc.flags.offset == 32 and _lib.WeightDesc.w_bytes.offset == 40
     assert ctypes.sizeof(_lib.Config) == 20
     assert _lib.IndexedRouting.capacity.offset == 24
 
 
 def test_version_and_desc(L):
-    assert L.w4a16_abi_version() == 1
+    assert L.w4a16_abi_version() == 2
     d = W.weight_desc(48, 4096, 7168)
     assert (d.K_pad, d.chunks, d.group) == (7168, 56, 32)
     assert d.w_bytes == 48 * 4096 * 7168 // 2
@@ -56,6 +57,15 @@ def test_desc_rejects_bad_shapes(L, E, N, K, code):
     d = _lib.WeightDesc()
     assert L.w4a16_weight_desc_init(E, N, K, ctypes.byref(d)) == code
     assert L.w4a16_last_error()
+
+
+def test_gate_up_descriptor(L):
+    d = W.weight_desc(4, 64, 256, gate_up=True)
+    assert d.flags == _lib.DESC_GATE_UP and d.w_bytes == W.weight_desc(4, 64, 256).w_bytes
+    e = _lib.WeightDesc()
+    assert L.w4a16_weight_desc_init_gate_up(4, 48, 256, ctypes.byref(e)) == -2       # N % 32
+    d.flags = 2                                                                      # unknown flag
+    assert L.w4a16_pack_w4(16, 16, ctypes.byref(d), 16, 16, None) == -3
 
 
 def test_corrupted_descriptor_is_rejected(L):
@@ -112,6 +122,23 @@ def test_gemm_argument_errors(L):
     assert L.w4a16_grouped_masked(ctypes.byref(d), P, P, P, 0, P, 4, P, None, None) == -1
     assert L.w4a16_grouped_masked(ctypes.byref(d), P, P, P, 32, P, 0, P, None, None) == -1
     assert L.w4a16_grouped_contiguous(ctypes.byref(d), P, P, P, 100, P, P, None, None) == -2
+    lay = lambda layout, rows: L.w4a16_moe_gemm(ctypes.byref(d), P, P, P, rows, layout, ctypes.byref(r), None, P,
+                                                ctypes.byref(cfg), None, 0, None)
+    assert lay(3, 4096) == -1                                            # unknown activation layout
+    assert lay(_lib.A_SLOT, 64) == -2                                    # slot rows: needs T * topk = 128
+    assert lay(_lib.A_SORTED, 128) == -2                                 # sorted rows: needs capacity = 1024
+
+
+def test_gate_up_silu_argument_errors(L):
+    P = 16
+    plain = W.weight_desc(8, 64, 256)
+    gated = W.weight_desc(8, 64, 256, gate_up=True)
+    r = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 8)
+    call = lambda d, cfg: L.w4a16_moe_gate_up_silu(ctypes.byref(d), P, P, P, 64, ctypes.byref(r), P,
+                                                   ctypes.byref(cfg), None)
+    assert call(plain, W.config(32, 2)) == -3                            # weight not gate/up packed
+    assert call(gated, W.config(32, 2, split_k=0)) == -4                 # one workgroup per tile only
+    assert call(gated, W.config(16, 2)) == -3                            # block_m disagrees with routing
 
 
 def test_selector_follows_tokens_per_expert(L):

@@ -398,6 +398,37 @@ def test_silu_mul_closed_forms():
     assert out[0, 1] == -90.0                     # silu(30) rounds to 30 in bf16 range; 30 * -3
 
 
+def test_silu_mul_matches_library_logistic():
+    """silu(g) * u against SciPy's logistic function (a separate library
+    routine): bf16(g * expit(g) * u) for bf16 inputs."""
+    from scipy.special import expit
+    rng = np.random.default_rng(7)
+    g = W.to_bf16_bits(rng.normal(0, 4, 20000).astype(np.float32))
+    u = W.to_bf16_bits(rng.normal(0, 1, 20000).astype(np.float32))
+    h = np.stack([g, u], axis=1)
+    got = O.silu_mul(h)[:, 0]
+    gf, uf = O.bf16_to_f64(g), O.bf16_to_f64(u)
+    ref = O.f64_to_bf16(gf * expit(gf) * uf)
+    assert np.array_equal(got, ref)
+    # odd-part identity: silu(x) - silu(-x) = x (checked in fp64 before rounding)
+    x = np.linspace(-30, 30, 601)
+    np.testing.assert_allclose(x * expit(x) - (-x) * expit(-x), x, rtol=0, atol=1e-12)
+
+
+def test_gate_up_silu_sorted_places_rows():
+    """Each valid sorted position gets the activation of its slot's row;
+    padding positions are masked out; the ordering is that of moe_align."""
+    T, k, E = 6, 2, 3
+    ids = np.array([[0, 2], [1, 0], [2, 2], [0, 1], [1, 1], [2, 0]], np.int32)
+    sid, eid, ntp = O.moe_align(ids, E, 0, E, 16)
+    h = W.to_bf16_bits(np.arange(T * k * 4, dtype=np.float32).reshape(T * k, 4) / 7.0 - 3.0)
+    out, valid = O.gate_up_silu_sorted(h, sid, T * k)
+    assert valid.sum() == T * k and not valid[ntp:].any()
+    act = O.silu_mul(h)
+    for p in np.nonzero(valid)[0]:
+        assert np.array_equal(out[p], act[sid[p]])
+
+
 def test_fp32_baseline_within_tolerance_of_fp64():
     sh = W.scaled(W.WORKLOADS["tiny"])
     ids, w = W.routing_for(sh)

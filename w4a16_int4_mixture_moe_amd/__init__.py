@@ -6,6 +6,6 @@ contiguous / masked layouts.  The computation lives in the HIP library built
 from csrc/ (C ABI: include/w4a16_moe.h); this package is its binding.
 """
 from .api import (Config, PackedW4, Routing, W4A16Error, align_capacity, config,  # noqa: F401
-                  grouped_contiguous, grouped_masked, indexed_config, moe_align, moe_w4a16_gemm,
-                  pack_w4, select, weight_desc, workspace_bytes)
+                  grouped_contiguous, grouped_masked, indexed_config, moe_align, moe_gate_up_silu,
+                  moe_w4a16_gemm, pack_w4, select, weight_desc, workspace_bytes)
 from ._lib import lib_path, load  # noqa: F401

@@ -28,8 +28,13 @@ class WeightDesc(ctypes.Structure):
         ("magic", ctypes.c_uint32), ("version", ctypes.c_uint32),
         ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
         ("K_pad", ctypes.c_int32), ("chunks", ctypes.c_int32), ("group", ctypes.c_int32),
+        ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("w_bytes", ctypes.c_uint64), ("s_bytes", ctypes.c_uint64), ("check", ctypes.c_uint64),
     ]
+
+
+DESC_GATE_UP = 1            # W4A16_DESC_GATE_UP
+A_TOKEN, A_SLOT, A_SORTED = 0, 1, 2   # W4A16_A_TOKEN / _SLOT / _SORTED
 
 
 class Config(ctypes.Structure):
@@ -60,6 +65,7 @@ SIGNATURES = {
     "w4a16_last_error": (ctypes.c_char_p, []),
     "w4a16_abi_version": (_I32, []),
     "w4a16_weight_desc_init": (_I32, [_I32, _I32, _I32, ctypes.POINTER(WeightDesc)]),
+    "w4a16_weight_desc_init_gate_up": (_I32, [_I32, _I32, _I32, ctypes.POINTER(WeightDesc)]),
     "w4a16_pack_w4": (_I32, [_P, _P, ctypes.POINTER(WeightDesc), _P, _P, _P]),
     "w4a16_align_capacity": (_I64, [_I32, _I32, _I32, _I32]),
     "w4a16_moe_align": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P]),
@@ -70,6 +76,8 @@ SIGNATURES = {
     "w4a16_moe_gemm": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I64, _I32,
                               ctypes.POINTER(IndexedRouting), _P, _P, ctypes.POINTER(Config),
                               _P, _SZ, _P]),
+    "w4a16_moe_gate_up_silu": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I64,
+                                      ctypes.POINTER(IndexedRouting), _P, ctypes.POINTER(Config), _P]),
     "w4a16_grouped_contiguous": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I64, _P, _P,
                                         ctypes.POINTER(Config), _P]),
     "w4a16_grouped_masked": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I32, _P, _I32, _P,

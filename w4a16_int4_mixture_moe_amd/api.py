@@ -6,6 +6,10 @@ the computation runs in the HIP library's kernels.
     routing = moe_align(topk_ids[T, k], E_glob, first_expert, E_loc, block_m)
     h = moe_w4a16_gemm(x[T, K], packed, routing)                     # per slot
     y = moe_w4a16_gemm(a[T*k, K2], packed2, routing, topk_weights)   # combined
+    # chained layer: fused SiLU gate/up in sorted order, down reads it as is
+    p1 = pack_w4(codes1, scales1, gate_up=True)
+    inter = moe_gate_up_silu(x, p1, routing)                         # [capacity, N/2]
+    y = moe_w4a16_gemm(inter, packed2, routing, topk_weights, a_layout="sorted")
     out = grouped_contiguous(a2[m, K], packed, m_indices)
     out = grouped_masked(a3[E, max_m, K], packed, masked_m, expected_m)
 """
@@ -17,7 +21,8 @@ from typing import Optional
 
 import torch
 
-from ._lib import Config, IndexedRouting, W4A16Error, WeightDesc, check, load
+from ._lib import (A_SLOT, A_SORTED, A_TOKEN, DESC_GATE_UP, Config, IndexedRouting, W4A16Error,
+                   WeightDesc, check, load)
 
 
 def _stream(dev: torch.device) -> ctypes.c_void_p:
@@ -62,21 +67,29 @@ class PackedW4:
     def K(self):
         return self.desc.K
 
+    @property
+    def gate_up(self):
+        return self.desc.flags == DESC_GATE_UP
 
-def weight_desc(E: int, N: int, K: int) -> WeightDesc:
+
+def weight_desc(E: int, N: int, K: int, gate_up: bool = False) -> WeightDesc:
     d = WeightDesc()
-    check(load().w4a16_weight_desc_init(E, N, K, ctypes.byref(d)))
+    init = load().w4a16_weight_desc_init_gate_up if gate_up else load().w4a16_weight_desc_init
+    check(init(E, N, K, ctypes.byref(d)))
     return d
 
 
-def pack_w4(codes: torch.Tensor, scales: torch.Tensor) -> PackedW4:
-    """codes uint8 [E, N, K] (0..15), scales bf16 [E, N, K/32] -> packed weight."""
+def pack_w4(codes: torch.Tensor, scales: torch.Tensor, gate_up: bool = False) -> PackedW4:
+    """codes uint8 [E, N, K] (0..15), scales bf16 [E, N, K/32] -> packed weight.
+    gate_up: rows [0, N/2) are the gate and [N/2, N) the up projection; their
+    tiles are interleaved (needed by moe_gate_up_silu; every call still sees
+    the logical column order)."""
     _need(codes, "codes", (torch.uint8,), 3)
     _need(scales, "scales", _BF16, 3)
     E, N, K = codes.shape
     if tuple(scales.shape) != (E, N, K // 32) or K % 32:
         raise ValueError(f"scales shape {tuple(scales.shape)} does not match codes {tuple(codes.shape)}")
-    d = weight_desc(E, N, K)
+    d = weight_desc(E, N, K, gate_up)
     w = torch.empty(d.w_bytes, dtype=torch.uint8, device=codes.device)
     s = torch.empty(d.s_bytes, dtype=torch.uint8, device=codes.device)
     check(load().w4a16_pack_w4(codes.data_ptr(), scales.data_ptr(), ctypes.byref(d), w.data_ptr(),
@@ -163,17 +176,24 @@ def workspace_bytes(packed: PackedW4, T: int, topk: int, combine: bool,
         None if cfg is None else ctypes.byref(cfg)))
 
 
+_A_LAYOUTS = {"token": A_TOKEN, "slot": A_SLOT, "sorted": A_SORTED}
+
+
 def moe_w4a16_gemm(a: torch.Tensor, packed: PackedW4, routing: Routing,
-                   topk_weights: Optional[torch.Tensor] = None, a_per_slot: Optional[bool] = None,
+                   topk_weights: Optional[torch.Tensor] = None, a_layout: Optional[str] = None,
                    cfg: Optional[Config] = None, out: Optional[torch.Tensor] = None,
                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Indexed MoE GEMM.  Without topk_weights: out[T*k, N] per routed slot
     (only local slots written).  With topk_weights float32 [T, k]: out[T, N]
-    top-k-weighted combine.  a_per_slot defaults to (topk_weights given)."""
+    top-k-weighted combine.  a_layout: "token" (a[T, K]), "slot" (a[T*k, K])
+    or "sorted" (a[capacity, K], row p for sorted position p, as written by
+    moe_gate_up_silu); default "slot" with topk_weights, else "token"."""
     _need(a, "a", _BF16, 2)
     T, k = routing.T, routing.topk
-    if a_per_slot is None:
-        a_per_slot = topk_weights is not None
+    if a_layout is None:
+        a_layout = "slot" if topk_weights is not None else "token"
+    if a_layout not in _A_LAYOUTS:
+        raise ValueError(f"a_layout must be one of {sorted(_A_LAYOUTS)}")
     if a.shape[1] != packed.K:
         raise ValueError(f"a has K={a.shape[1]}, weight has K={packed.K}")
     dev = a.device
@@ -197,11 +217,36 @@ def moe_w4a16_gemm(a: torch.Tensor, packed: PackedW4, routing: Routing,
             workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
     r = routing.as_c()
     check(load().w4a16_moe_gemm(ctypes.byref(packed.desc), packed.w.data_ptr(), packed.s.data_ptr(),
-                                a.data_ptr(), a.shape[0], int(bool(a_per_slot)), ctypes.byref(r),
+                                a.data_ptr(), a.shape[0], _A_LAYOUTS[a_layout], ctypes.byref(r),
                                 _ptr(topk_weights), out.data_ptr(),
                                 None if cfg is None else ctypes.byref(cfg),
                                 _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                 _stream(dev)))
+    return out
+
+
+def moe_gate_up_silu(x: torch.Tensor, packed: PackedW4, routing: Routing,
+                     cfg: Optional[Config] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fused gate/up + SiLU(gate) * up for a gate_up-packed weight [E, 2I, K]:
+    out bf16 [capacity, I], row p = sorted position p (rows of local slots
+    written, padding rows left as they are)."""
+    _need(x, "x", _BF16, 2)
+    if not packed.gate_up:
+        raise ValueError("moe_gate_up_silu needs a weight packed with gate_up=True")
+    if x.shape[1] != packed.K:
+        raise ValueError(f"x has K={x.shape[1]}, weight has K={packed.K}")
+    if out is None:
+        out = torch.empty(routing.capacity, packed.N // 2, dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(out, "out", _BF16, 2)
+        if out.shape[0] < routing.capacity or out.shape[1] != packed.N // 2:
+            raise ValueError(f"out must be [{routing.capacity}, {packed.N // 2}]")
+    if cfg is None:
+        cfg = indexed_config(routing.block_m)
+    r = routing.as_c()
+    check(load().w4a16_moe_gate_up_silu(ctypes.byref(packed.desc), packed.w.data_ptr(), packed.s.data_ptr(),
+                                        x.data_ptr(), x.shape[0], ctypes.byref(r), out.data_ptr(),
+                                        ctypes.byref(cfg), _stream(x.device)))
     return out
 
 
@@ -242,6 +287,7 @@ def grouped_masked(a: torch.Tensor, packed: PackedW4, masked_m: torch.Tensor, ex
 
 __all__ = [
     "W4A16Error", "PackedW4", "Routing", "Config", "weight_desc", "pack_w4", "align_capacity",
-    "moe_align", "select", "config", "indexed_config", "workspace_bytes", "moe_w4a16_gemm", "grouped_contiguous",
+    "moe_align", "select", "config", "indexed_config", "workspace_bytes", "moe_w4a16_gemm", "moe_gate_up_silu",
+    "grouped_contiguous",
     "grouped_masked",
 ]

@@ -52,7 +52,7 @@ uint64_t desc_checksum(const w4a16_weight_desc& d) {
   return h;
 }
 
-w4a16_weight_desc make_desc(int32_t E, int32_t N, int32_t K) {
+w4a16_weight_desc make_desc(int32_t E, int32_t N, int32_t K, int32_t flags) {
   w4a16_weight_desc d;
   std::memset(&d, 0, sizeof d);
   d.magic = W4A16_DESC_MAGIC;
@@ -60,6 +60,7 @@ w4a16_weight_desc make_desc(int32_t E, int32_t N, int32_t K) {
   d.E = E;
   d.N = N;
   d.K = K;
+  d.flags = flags;
   d.K_pad = (int32_t)round_up(K, 128);
   const int64_t KC = d.K_pad / 128;
   d.chunks = (int32_t)KC;
@@ -86,7 +87,9 @@ w4a16_status check_desc(const w4a16_weight_desc* d) {
   if (d->check != desc_checksum(*d)) return fail(W4A16_ERR_LAYOUT, "weight descriptor checksum mismatch (corrupted)");
   w4a16_status st = check_shape(d->E, d->N, d->K);
   if (st != W4A16_OK) return fail(W4A16_ERR_LAYOUT, "weight descriptor shape invalid: %s", g_last_error.c_str());
-  const w4a16_weight_desc ref = make_desc(d->E, d->N, d->K);
+  if (d->flags != 0 && (d->flags != W4A16_DESC_GATE_UP || d->N % 32))
+    return fail(W4A16_ERR_LAYOUT, "weight descriptor flags invalid");
+  const w4a16_weight_desc ref = make_desc(d->E, d->N, d->K, d->flags);
   if (std::memcmp(&ref, d, sizeof ref) != 0) return fail(W4A16_ERR_LAYOUT, "weight descriptor fields inconsistent");
   return W4A16_OK;
 }
@@ -198,6 +201,7 @@ w4a16::GemmParams base_params(const w4a16_weight_desc* d, const void* pw, const 
   p.KC = d->K_pad / 128;
   const int tiles_per_wg = nr * waves;
   p.n_tiles = (p.NT + tiles_per_wg - 1) / tiles_per_wg;
+  p.gated = d->flags == W4A16_DESC_GATE_UP;
   p.out = out;
   return p;
 }
@@ -243,7 +247,16 @@ w4a16_status w4a16_weight_desc_init(int32_t E, int32_t N, int32_t K, w4a16_weigh
   if (out == nullptr) return fail(W4A16_ERR_ARG, "out is NULL");
   w4a16_status st = check_shape(E, N, K);
   if (st != W4A16_OK) return st;
-  *out = make_desc(E, N, K);
+  *out = make_desc(E, N, K, 0);
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_weight_desc_init_gate_up(int32_t E, int32_t N, int32_t K, w4a16_weight_desc* out) {
+  if (out == nullptr) return fail(W4A16_ERR_ARG, "out is NULL");
+  w4a16_status st = check_shape(E, N, K);
+  if (st != W4A16_OK) return st;
+  if (N % 32) return fail(W4A16_ERR_SHAPE, "a gate/up weight needs N %% 32 == 0 (got %d)", N);
+  *out = make_desc(E, N, K, W4A16_DESC_GATE_UP);
   return W4A16_OK;
 }
 
@@ -256,7 +269,7 @@ w4a16_status w4a16_pack_w4(const uint8_t* codes, const uint16_t* scales,
   if (!aligned16(packed_w) || !aligned16(packed_s)) return fail(W4A16_ERR_ARG, "packed buffers must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(scales) & 1u) return fail(W4A16_ERR_ARG, "scales must be 2-byte aligned");
   hipError_t e = w4a16::launch_pack(codes, scales, desc->E, desc->N, desc->K, desc->chunks,
-                                    static_cast<uint32_t*>(packed_w),
+                                    desc->flags == W4A16_DESC_GATE_UP, static_cast<uint32_t*>(packed_w),
                                     static_cast<uint32_t*>(packed_s), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pack_w4 launch");
   return W4A16_OK;
@@ -344,7 +357,7 @@ size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, int32_t T, 
 
 w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
                             const void* packed_s, const uint16_t* a, int64_t a_rows,
-                            int32_t a_per_slot, const w4a16_indexed_routing* routing,
+                            int32_t a_layout, const w4a16_indexed_routing* routing,
                             const float* topk_weights, uint16_t* out,
                             const w4a16_config* cfg, void* workspace, size_t workspace_bytes,
                             w4a16_stream_t stream) {
@@ -361,7 +374,11 @@ w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
     return fail(W4A16_ERR_ARG, "packed weights, activations and output must be 16-byte aligned");
   if (r.E_loc != desc->E)
     return fail(W4A16_ERR_LAYOUT, "routing has E_loc=%d but the packed weight holds %d experts", r.E_loc, desc->E);
-  const int64_t need_rows = a_per_slot ? (int64_t)r.T * r.topk : r.T;
+  if (a_layout != W4A16_A_TOKEN && a_layout != W4A16_A_SLOT && a_layout != W4A16_A_SORTED)
+    return fail(W4A16_ERR_ARG, "a_layout %d is not W4A16_A_TOKEN, W4A16_A_SLOT or W4A16_A_SORTED", a_layout);
+  const int64_t need_rows = a_layout == W4A16_A_TOKEN  ? (int64_t)r.T
+                            : a_layout == W4A16_A_SLOT ? (int64_t)r.T * r.topk
+                                                       : r.capacity;
   if (a_rows < need_rows)
     return fail(W4A16_ERR_SHAPE, "activations have %lld rows, need %lld", (long long)a_rows, (long long)need_rows);
   if ((int64_t)r.T * r.topk >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "T*topk too large");
@@ -394,7 +411,7 @@ w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
   p.expert_ids = r.expert_ids;
   p.num_tokens_padded = r.num_tokens_padded;
   p.sentinel = r.T * r.topk;
-  p.a_row_div = a_per_slot ? 1 : r.topk;
+  p.a_row_div = a_layout == W4A16_A_TOKEN ? r.topk : a_layout == W4A16_A_SLOT ? 1 : 0;
   p.slot_weight = topk_weights;
   p.grid_blocks = (int32_t)(r.capacity / r.block_m);
   hipError_t e;
@@ -412,6 +429,48 @@ w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
                               r.first_expert, r.E_loc, desc->N, out, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
   }
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_moe_gate_up_silu(const w4a16_weight_desc* desc, const void* packed_w,
+                                    const void* packed_s, const uint16_t* x, int64_t x_rows,
+                                    const w4a16_indexed_routing* routing, uint16_t* out,
+                                    const w4a16_config* cfg, w4a16_stream_t stream) {
+  w4a16_status st = check_desc(desc);
+  if (st != W4A16_OK) return st;
+  if (desc->flags != W4A16_DESC_GATE_UP)
+    return fail(W4A16_ERR_LAYOUT, "the fused SiLU gate/up call needs a weight packed with w4a16_weight_desc_init_gate_up");
+  if (!routing) return fail(W4A16_ERR_ARG, "routing is NULL");
+  const w4a16_indexed_routing& r = *routing;
+  if (!packed_w || !packed_s || !r.sorted_ids || !r.expert_ids || !r.num_tokens_padded)
+    return fail(W4A16_ERR_ARG, "NULL pointer argument");
+  if (r.T < 0 || r.topk <= 0 || r.capacity < 0) return fail(W4A16_ERR_ARG, "bad routing sizes");
+  if (r.T > 0 && (!x || !out)) return fail(W4A16_ERR_ARG, "activations or output are NULL");
+  if (!aligned16(packed_w) || !aligned16(packed_s) || !aligned16(x) || !aligned16(out))
+    return fail(W4A16_ERR_ARG, "packed weights, activations and output must be 16-byte aligned");
+  if (r.E_loc != desc->E)
+    return fail(W4A16_ERR_LAYOUT, "routing has E_loc=%d but the packed weight holds %d experts", r.E_loc, desc->E);
+  if (x_rows < r.T) return fail(W4A16_ERR_SHAPE, "activations have %lld rows, need %d", (long long)x_rows, r.T);
+  if ((int64_t)r.T * r.topk >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "T*topk too large");
+  w4a16_config c = cfg ? *cfg : default_indexed_config(r.block_m);
+  if (c.split_k != 1) return fail(W4A16_ERR_UNSUPPORTED, "the fused SiLU gate/up call runs one workgroup per tile (split_k = 1)");
+  if (c.nr % 2) return fail(W4A16_ERR_UNSUPPORTED, "the fused SiLU gate/up call needs an even nr (gate and up tiles in pairs)");
+  st = check_config(c, w4a16::kRouteIndexed, w4a16::kEpiSilu);
+  if (st != W4A16_OK) return st;
+  if (c.block_m != r.block_m)
+    return fail(W4A16_ERR_LAYOUT, "config block_m=%d differs from the routing's block_m=%d", c.block_m, r.block_m);
+  if (r.capacity % r.block_m) return fail(W4A16_ERR_CAPACITY, "capacity not a multiple of block_m");
+  if (r.T == 0) return W4A16_OK;
+  w4a16::GemmParams p = base_params(desc, packed_w, packed_s, x, out, c.nr, c.waves);
+  p.sorted_ids = r.sorted_ids;
+  p.expert_ids = r.expert_ids;
+  p.num_tokens_padded = r.num_tokens_padded;
+  p.sentinel = r.T * r.topk;
+  p.a_row_div = r.topk;
+  p.grid_blocks = (int32_t)(r.capacity / r.block_m);
+  hipError_t e = w4a16::launch_gemm(w4a16::kRouteIndexed, w4a16::kEpiSilu, c.block_m / 16, c.nr, c.waves,
+                                    c.stages, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gate_up_silu launch");
   return W4A16_OK;
 }
 

@@ -89,10 +89,13 @@ __device__ __forceinline__ int setup_rows(const GemmParams& p, int mb, TileSmem<
     expert = p.expert_ids[mb];
     if ((unsigned)expert >= (unsigned)p.E) return -1;   // -1 (unused block) or foreign id
     for (int i = tid; i < BM; i += NTHR) {
-      const int s = p.sorted_ids[(int64_t)mb * BM + i];
+      const int pos = mb * BM + i;                         // sorted position
+      const int s = p.sorted_ids[pos];
       const bool v = (unsigned)s < (unsigned)p.sentinel;
-      sm.row[i] = v ? s / p.a_row_div : -1;
-      sm.out[i] = v ? s : -1;
+      // activation row: the slot's token (a_row_div = topk), the slot (1),
+      // or the sorted position itself (0: rows already in sorted order)
+      sm.row[i] = v ? (p.a_row_div > 0 ? s / p.a_row_div : pos) : -1;
+      sm.out[i] = v ? (EPI == kEpiSilu ? pos : s) : -1;
       if constexpr (EPI == kEpiWeighted) sm.w[i] = v ? p.slot_weight[s] : 0.f;
     }
   } else if constexpr (ROUTE == kRouteContiguous) {
@@ -423,6 +426,18 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, TileSmem<MT>& sm, 
   }
 }
 
+// Output feature tile of packed tile `rt` (gate/up interleaved weights store
+// gate tile t at 2t and up tile t at 2t + 1).
+__device__ __forceinline__ int logical_tile(const GemmParams& p, int rt) {
+  return p.gated ? (rt & 1 ? p.NT / 2 + (rt >> 1) : rt >> 1) : rt;
+}
+
+// silu(g) * u in fp32 for bf16-rounded g and u (the values the per-slot
+// gate/up output holds), rounded once to bf16 by the caller
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
 // Write the tile's outputs.  Lane holds rows n = 16*tile + 4*(lane/16) + v
 // (v = 0..3) of token column lane % 16 of each token tile.
 template <int MT, int NR, int NW, int EPI>
@@ -432,10 +447,40 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TileSmem<MT>
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int rt_base = nt * (NW * NR) + wave * NR;
   const int nr_valid = min(NR, p.NT - rt_base);
+  if constexpr (EPI == kEpiSilu) {
+    // tiles come in (gate, up) pairs: packed tiles rt_base + r and + r + 1
+    // (rt_base and NT are even) hold gate and up tile (rt_base + r) / 2
+    static_assert(NR % 2 == 0, "gate and up tiles in pairs");
+    const int NI = p.N / 2;
+#pragma unroll
+    for (int r = 0; r < NR; r += 2) {
+      if (r >= nr_valid) continue;
+      const int n = ((rt_base + r) >> 1) * kRowTile + 4 * (lane >> 4);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        if (!((tmask >> t) & 1u)) continue;
+        const int i = 16 * t + (lane & 15);
+        const int orow = sm.out[i];
+        if (orow < 0) continue;
+        const f32x4_t g = acc[r][t], u = acc[r + 1][t];
+        float y[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t gu = pack_bf16x2(g[v], u[v]);       // the per-slot bf16 outputs
+          y[v] = silu_mul(bf16_bits_to_float(gu & 0xFFFFu), bf16_bits_to_float(gu >> 16));
+        }
+        uint2 o;
+        o.x = pack_bf16x2(y[0], y[1]);
+        o.y = pack_bf16x2(y[2], y[3]);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + (int64_t)orow * NI + n) = o;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     if (r >= nr_valid) continue;
-    const int n = (rt_base + r) * kRowTile + 4 * (lane >> 4);
+    const int n = logical_tile(p, rt_base + r) * kRowTile + 4 * (lane >> 4);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       if (!((tmask >> t) & 1u)) continue;
@@ -635,11 +680,24 @@ static KernelSet make_set() {
   return s;
 }
 
+// one workgroup per tile only (no stream-K form)
+template <int MT, int NR, int NW, int D, int ROUTE, int EPI>
+static KernelSet make_classic() {
+  KernelSet s;
+  s.classic = moe_gemm_kernel<MT, NR, NW, D, ROUTE, EPI>;
+  return s;
+}
+
 template <int MT, int NR, int NW, int D>
 static KernelSet pick(int route, int epi) {
-  if (route == kRouteIndexed)
+  if (route == kRouteIndexed) {
+    if (epi == kEpiSilu) {
+      if constexpr (NR % 2 == 0) return make_classic<MT, NR, NW, D, kRouteIndexed, kEpiSilu>();
+      return KernelSet{};
+    }
     return epi == kEpiWeighted ? make_set<MT, NR, NW, D, kRouteIndexed, kEpiWeighted>()
                                : make_set<MT, NR, NW, D, kRouteIndexed, kEpiStore>();
+  }
   if (epi != kEpiStore) return KernelSet{};
   if (route == kRouteContiguous) return make_set<MT, NR, NW, D, kRouteContiguous, kEpiStore>();
   if (route == kRouteMasked) return make_set<MT, NR, NW, D, kRouteMasked, kEpiStore>();

@@ -14,12 +14,13 @@ hipError_t launch_align(const int32_t* topk_ids, int32_t total_slots, int32_t fi
 
 // ---- packer (pack.hip)
 hipError_t launch_pack(const uint8_t* codes, const uint16_t* scales, int32_t E, int32_t N,
-                       int32_t K, int32_t KC, uint32_t* packed_w,
+                       int32_t K, int32_t KC, int32_t gate_up, uint32_t* packed_w,
                        uint32_t* packed_s, hipStream_t stream);
 
 // ---- GEMM (gemm.hip)
 enum RouteKind : int { kRouteIndexed = 0, kRouteContiguous = 1, kRouteMasked = 2 };
-enum EpilogueKind : int { kEpiStore = 0, kEpiWeighted = 1 };
+// kEpiSilu: gate/up pairs of tiles -> bf16(silu(g) * u) at sorted positions
+enum EpilogueKind : int { kEpiStore = 0, kEpiWeighted = 1, kEpiSilu = 2 };
 
 struct GemmParams {
   const uint4* packed_w;        // [E][NT][KC][64][4 words]
@@ -32,7 +33,8 @@ struct GemmParams {
   const int32_t* expert_ids;
   const int32_t* num_tokens_padded;
   int32_t sentinel;             // T * topk
-  int32_t a_row_div;            // topk (rows per token) or 1 (rows per slot)
+  int32_t a_row_div;            // topk (rows per token), 1 (rows per slot), 0 (rows per sorted position)
+  int32_t gated;                // packed tiles alternate gate / up (output columns remapped)
   const float* slot_weight;     // weighted epilogue: topk weights, one per slot
   // contiguous
   const int32_t* m_indices;

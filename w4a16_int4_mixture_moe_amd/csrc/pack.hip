@@ -12,9 +12,16 @@
 
 namespace w4a16 {
 
+// Source row of row i of packed tile `tile`: with gate_up, packed tile 2t is
+// gate tile t (rows 16t..) and packed tile 2t + 1 up tile t (rows N/2 + 16t..)
+__device__ __forceinline__ int source_row(int tile, int i, int N, int gate_up) {
+  const int t = gate_up ? (tile & 1 ? N / 32 + (tile >> 1) : tile >> 1) : tile;
+  return t * kRowTile + i;
+}
+
 __global__ __launch_bounds__(256) void pack_w_kernel(const uint8_t* __restrict__ codes, int32_t N,
                                                      int32_t K, int32_t NT, int32_t KC,
-                                                     int64_t total_words,
+                                                     int32_t gate_up, int64_t total_words,
                                                      uint32_t* __restrict__ packed_w) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total_words) return;
@@ -25,7 +32,7 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const uint8_t* __restrict__
   rest /= KC;
   const int tile = (int)(rest % NT);
   const int64_t e = rest / NT;
-  const int n = tile * kRowTile + (l & 15);
+  const int n = source_row(tile, l & 15, N, gate_up);
   const int k0 = c * kChunk + (l >> 4) * kGroup + j * 8;
   const uint8_t* src = codes + (e * N + n) * (int64_t)K;
   uint32_t word = 0;
@@ -40,7 +47,7 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const uint8_t* __restrict__
 
 __global__ __launch_bounds__(256) void pack_s_kernel(const uint16_t* __restrict__ scales,
                                                      int32_t N, int32_t K, int32_t NT,
-                                                     int32_t KC, int64_t total,
+                                                     int32_t KC, int32_t gate_up, int64_t total,
                                                      uint32_t* __restrict__ packed_s) {
   // output word index = ((e * NT + tile) * KC2 + m) * 64 + lane; the word
   // holds the lane's scale for chunk 2m (low half) and 2m + 1 (high half)
@@ -53,7 +60,7 @@ __global__ __launch_bounds__(256) void pack_s_kernel(const uint16_t* __restrict_
   rest /= KC2;
   const int tile = (int)(rest % NT);
   const int64_t e = rest / NT;
-  const int n = tile * kRowTile + (l & 15);
+  const int n = source_row(tile, l & 15, N, gate_up);
   const int G = K / kGroup;
   const uint16_t* row = scales + (e * N + n) * (int64_t)G;
   const int g0 = 4 * (2 * m) + (l >> 4), g1 = g0 + 4;
@@ -62,17 +69,17 @@ __global__ __launch_bounds__(256) void pack_s_kernel(const uint16_t* __restrict_
 }
 
 hipError_t launch_pack(const uint8_t* codes, const uint16_t* scales, int32_t E, int32_t N,
-                       int32_t K, int32_t KC, uint32_t* packed_w,
+                       int32_t K, int32_t KC, int32_t gate_up, uint32_t* packed_w,
                        uint32_t* packed_s, hipStream_t stream) {
   const int32_t NT = N / kRowTile;
   const int64_t words = (int64_t)E * NT * KC * 256;
   const int64_t sents = (int64_t)E * NT * ((KC + 1) / 2) * 64;
   hipLaunchKernelGGL(pack_w_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
-                     codes, N, K, NT, KC, words, packed_w);
+                     codes, N, K, NT, KC, gate_up, words, packed_w);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(pack_s_kernel, dim3((unsigned)((sents + 255) / 256)), dim3(256), 0, stream,
-                     scales, N, K, NT, KC, sents, packed_s);
+                     scales, N, K, NT, KC, gate_up, sents, packed_s);
   return hipGetLastError();
 }
 
