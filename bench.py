@@ -113,8 +113,11 @@ def cpu_baseline(sh, ids, wts, x, a, c1, s1, c2, s2, n_experts: int) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 200 warmup steps (about 60 ms of GPU work at the decode size): with only a
+    # few, the timed region starts before the GPU's clocks have ramped to
+    # their steady level and every figure reads 10-20 % slow
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="ep8_decode")
     ap.add_argument("--block-m", type=int, default=0, help="override the selector's block_m")
     ap.add_argument("--nr", type=int, default=0, help="override the selector's weight tiles per wave")
