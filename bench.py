@@ -230,18 +230,20 @@ def main() -> int:
         return g
 
     def timed(g, reps, per):
-        """Average duration of one call: replay g `reps` times between two
-        events on the stream the kernels run on."""
+        """Per-call duration: replay g (per calls back to back) `reps` times,
+        each replay between two events on the stream the kernels run on.
+        Returns (mean, median, min, p90) of the per-call averages, in us."""
         s_ = torch.cuda.current_stream(dev)
-        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         g.replay()
         torch.cuda.synchronize()
-        a_.record(s_)
-        for _ in range(reps):
+        for a_, b_ in ev:
+            a_.record(s_)
             g.replay()
-        b_.record(s_)
+            b_.record(s_)
         torch.cuda.synchronize()
-        return a_.elapsed_time(b_) * 1e3 / (reps * per)
+        t = np.array([a_.elapsed_time(b_) * 1e3 / per for a_, b_ in ev])
+        return float(t.mean()), float(np.median(t)), float(t.min()), float(np.percentile(t, 90))
 
     for _ in range(args.warmup):
         step()
@@ -265,9 +267,26 @@ def main() -> int:
     ms_step = t0.elapsed_time(t1) / args.steps
     # per-kernel averages: each call replayed back to back inside one graph
     inner = 8
-    us_align = timed(graph_of(align, inner), max(2, args.steps // 4), inner)
-    us_gu = timed(graph_of(gate_up, inner), max(2, args.steps // 4), inner)
-    us_dn = timed(graph_of(down, inner), max(2, args.steps // 4), inner)
+    st_align = timed(graph_of(align, inner), max(4, args.steps // 2), inner)
+    st_gu = timed(graph_of(gate_up, inner), max(4, args.steps // 2), inner)
+    st_dn = timed(graph_of(down, inner), max(4, args.steps // 2), inner)
+    us_align, us_gu, us_dn = st_align[0], st_gu[0], st_dn[0]
+
+    # host cost of choosing a config (first call runs the sampled search,
+    # later calls hit the memoised result) and of one launch (binding +
+    # argument checks + kernel enqueue), no device time
+    def host_us(fn, reps):
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        return (time.perf_counter() - t0) / reps * 1e6
+    probe_T = T + 1                                        # a shape the run has not selected for yet
+    t0 = time.perf_counter()
+    M.select(probe_T, k, sh.E_glob, sh.E_loc, sh.N1, sh.K1)
+    host_select_first = (time.perf_counter() - t0) * 1e6
+    host_select_memo = host_us(lambda: M.select(probe_T, k, sh.E_glob, sh.E_loc, sh.N1, sh.K1), 200)
+    host_launch = host_us(gate_up, 50)
+    torch.cuda.synchronize()
 
     flat = ids.reshape(-1)
     local = (flat >= sh.first) & (flat < sh.first + sh.E_loc)
@@ -306,6 +325,10 @@ def main() -> int:
                    "K1": sh.K1, "N1": sh.N1, "K2": sh.K2, "N2": sh.N2, "block_m": cfg.block_m,
                    "nr": cfg.nr, "waves": cfg.waves, "split_k": cfg.split_k, "stages": cfg.stages, "routed_rows": n_local,
                    "experts_touched": touched, "num_tokens_padded": n_ntp},
+        "per_call_stats_us": {name: {"median": round(v[1], 2), "min": round(v[2], 2), "p90": round(v[3], 2)}
+                              for name, v in (("align", st_align), ("gate_up", st_gu), ("down_combine", st_dn))},
+        "host_us": {"select_first_call": round(host_select_first, 1), "select_memoised": round(host_select_memo, 2),
+                    "gate_up_launch": round(host_launch, 1)},
         "per_call_us": {"align": round(us_align, 2), "gate_up": round(us_gu, 2),
                         "down_combine": round(us_dn, 2)},
         "gemm_rates": {

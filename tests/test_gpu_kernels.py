@@ -56,6 +56,11 @@ def test_align_edge_cases():
     _align_case(np.full((50, 2), 7, np.int32), 8, 0, 4, 32)                   # no local slot
     _align_case(np.full((300, 2), 3, np.int32), 8, 0, 8, 16)                  # all to one expert
     _align_case(np.random.default_rng(1).integers(0, 1024, (256, 8)).astype(np.int32), 1024, 0, 1024, 16)
+    # both sides of the 16-wave / 8-wave switch at 512 local experts, with a
+    # slot count that ends mid-batch in the last wave's range
+    g = np.random.default_rng(2)
+    for E_loc in (512, 513, 777):
+        _align_case(g.integers(0, 1000, (4099, 5)).astype(np.int32), 1000, 1000 - E_loc, E_loc, 32)
 
 
 @pytest.mark.parametrize("name", ["ep8_decode", "ep8_prefill", "tp8_t1", "tp8_t4096", "grouped_skewed"])

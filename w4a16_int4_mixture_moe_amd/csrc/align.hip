@@ -8,9 +8,11 @@
 // to the host and the call stays graph-capturable; section "Grouped SM90
 // kernels", Figure 3: indexed routing puts its padding in sentinel indices.
 //
-// One workgroup of 8 waves.  Wave w owns a contiguous range of slots, so the
+// One workgroup of 16 waves.  Wave w owns a contiguous range of slots, so the
 // order of slots inside an expert segment is ascending by construction:
-//   pass 1  each wave counts its slots per expert (LDS atomics);
+//   pass 1  each wave counts its slots per expert (LDS atomics), 16 loads in
+//           flight per lane (one workgroup has to keep many requests out to
+//           read the ids at more than a trickle);
 //   scan    per expert, exclusive prefix over waves, then an exclusive scan of
 //           the padded expert totals gives segment starts;
 //   fill    sentinels inside segment tails and after the padded total,
@@ -24,13 +26,16 @@
 
 namespace w4a16 {
 
-constexpr int kAlignWaves = 8;
-constexpr int kAlignThreads = kAlignWaves * kWave;
+constexpr int kAlignBatch = 16;                // slot ids in flight per lane
 
-__global__ __launch_bounds__(kAlignThreads) void align_kernel(
+// kAlignWaves waves: 16, or 8 when the per-wave counters of many experts
+// would not fit the default LDS allocation
+template <int kAlignWaves>
+__global__ __launch_bounds__(kAlignWaves * kWave) void align_kernel(
     const int32_t* __restrict__ topk_ids, int32_t total, int32_t first, int32_t E_loc,
     int32_t bm, int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
     int32_t* __restrict__ ntp_out, int64_t capacity) {
+  constexpr int kAlignThreads = kAlignWaves * kWave;
   extern __shared__ int smem[];
   int* cnt = smem;                            // [kAlignWaves][E_loc]: counts, then cursors
   int* seg = smem + kAlignWaves * E_loc;      // [E_loc + 1]: padded segment starts
@@ -47,16 +52,16 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   const int beg = min(w * per, total);
   const int end = min(beg + per, total);
 
-  // pass 1: per-wave expert histogram; 8 loads in flight per lane
-  for (int s0 = beg; s0 < end; s0 += 8 * kWave) {
-    int id[8];
+  // pass 1: per-wave expert histogram
+  for (int s0 = beg; s0 < end; s0 += kAlignBatch * kWave) {
+    int id[kAlignBatch];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kAlignBatch; ++u) {
       const int s = s0 + u * kWave + lane;
       id[u] = s < end ? topk_ids[s] : -1;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kAlignBatch; ++u) {
       const int e = id[u] - first;
       if (id[u] >= 0 && (unsigned)e < (unsigned)E_loc) atomicAdd(&cnt[w * E_loc + e], 1);
     }
@@ -112,16 +117,17 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   // pass 2: stable scatter
   const int nbits = 32 - __clz(max(E_loc - 1, 1));
   const uint64_t lanes_below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
-  // ids of the next 8 sub-tiles are requested together, then consumed in order
-  for (int s0 = beg; s0 < end; s0 += 8 * kWave) {
-    int id8[8];
+  // ids of the next kAlignBatch sub-tiles are requested together, then
+  // consumed in order
+  for (int s0 = beg; s0 < end; s0 += kAlignBatch * kWave) {
+    int id8[kAlignBatch];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kAlignBatch; ++u) {
       const int s = s0 + u * kWave + lane;
       id8[u] = s < end ? topk_ids[s] : -1;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kAlignBatch; ++u) {
       const int base = s0 + u * kWave;
       if (base >= end) break;
       const int s = base + lane;
@@ -149,10 +155,14 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
 hipError_t launch_align(const int32_t* topk_ids, int32_t total_slots, int32_t first, int32_t E_loc,
                         int32_t block_m, int32_t* sorted_ids, int32_t* expert_ids,
                         int32_t* num_tokens_padded, int64_t capacity, hipStream_t stream) {
-  const size_t lds = sizeof(int) * ((size_t)kAlignWaves * E_loc + 2 * (size_t)E_loc + 1);
-  hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), lds, stream, topk_ids,
-                     total_slots, first, E_loc, block_m, sorted_ids, expert_ids,
-                     num_tokens_padded, capacity);
+  const int waves = E_loc <= 512 ? 16 : 8;                  // LDS <= 37 KB (16) / 41 KB (8)
+  const size_t lds = sizeof(int) * ((size_t)waves * E_loc + 2 * (size_t)E_loc + 1);
+  if (waves == 16)
+    hipLaunchKernelGGL(align_kernel<16>, dim3(1), dim3(16 * kWave), lds, stream, topk_ids, total_slots, first,
+                       E_loc, block_m, sorted_ids, expert_ids, num_tokens_padded, capacity);
+  else
+    hipLaunchKernelGGL(align_kernel<8>, dim3(1), dim3(8 * kWave), lds, stream, topk_ids, total_slots, first,
+                       E_loc, block_m, sorted_ids, expert_ids, num_tokens_padded, capacity);
   return hipGetLastError();
 }
 
