@@ -393,8 +393,11 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
 // One tile's K range [c0, c1): zeroed accumulators, the main loop
 // specialised for the block's active token tiles (a workgroup-uniform
 // prefix), then finish(acc, mask).  One- and two-tile blocks run exactly
-// their active tiles; larger blocks run the checked loop (a second copy of
-// their loop would need a second set of accumulators).  Each path owns its
+// their active tiles; four- and eight-tile blocks round the count up to an
+// even one, so the extra tile (rows that are all padding: they read the
+// block's first row and are never stored) costs at most one tile of MFMAs,
+// while the checked loop (NA = 0) would wait for every outstanding load
+// wherever a tile is tested.  Each path owns its
 // accumulators and finishes on its own: merging them into one array before
 // a shared epilogue makes the allocator rotate them between registers with
 // moves inside the loop, each of which waits for an MFMA.
@@ -418,11 +421,22 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, TileSmem<MT>& sm, 
       go(std::integral_constant<int, 1>{});
     else
       go(std::integral_constant<int, 2>{});
-  } else {
-    if (tmask == (1u << MT) - 1u)
-      go(std::integral_constant<int, MT>{});
+  } else if constexpr (MT == 4) {
+    if (tmask < 4u)
+      go(std::integral_constant<int, 2>{});
     else
-      go(std::integral_constant<int, 0>{});
+      go(std::integral_constant<int, 4>{});
+  } else {
+    static_assert(MT == 8, "token tiles per block: 1, 2, 4 or 8");
+    const int na = 32 - __clz(tmask);               // tmask is a prefix
+    if (na <= 2)
+      go(std::integral_constant<int, 2>{});
+    else if (na <= 4)
+      go(std::integral_constant<int, 4>{});
+    else if (na <= 6)
+      go(std::integral_constant<int, 6>{});
+    else
+      go(std::integral_constant<int, 8>{});
   }
 }
 
