@@ -58,7 +58,7 @@ typedef enum {
 const char* w4a16_last_error(void);
 
 /* ABI version of this header (W4A16_ABI_VERSION). */
-#define W4A16_ABI_VERSION 2
+#define W4A16_ABI_VERSION 3
 int32_t w4a16_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -97,6 +97,7 @@ int32_t w4a16_abi_version(void);
 #define W4A16_DESC_MAGIC 0x16A4B0E5u /* arbitrary tag */
 #define W4A16_DESC_VERSION 2u
 #define W4A16_DESC_GATE_UP 1         /* flags: gate/up tiles interleaved */
+#define W4A16_DESC_MXFP4 2           /* flags: MXFP4 weight (A4W4 calls only) */
 
 typedef struct {
   uint32_t magic;       /* W4A16_DESC_MAGIC */
@@ -105,7 +106,7 @@ typedef struct {
   int32_t K_pad;        /* KP above */
   int32_t chunks;       /* KC above */
   int32_t group;        /* 32 */
-  int32_t flags;        /* 0 or W4A16_DESC_GATE_UP */
+  int32_t flags;        /* 0, W4A16_DESC_GATE_UP or W4A16_DESC_MXFP4 */
   int32_t reserved;     /* 0 */
   uint64_t w_bytes;     /* size of packed_w */
   uint64_t s_bytes;     /* size of packed_s */
@@ -294,6 +295,70 @@ w4a16_status w4a16_grouped_masked(const w4a16_weight_desc* desc, const void* pac
                                   const void* packed_s, const uint16_t* a, int32_t max_m,
                                   const int32_t* masked_m, int32_t expected_m, uint16_t* out,
                                   const w4a16_config* cfg, w4a16_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * A4W4: MXFP4 activations x MXFP4 weights.
+ *
+ * The AMD Kimi K3 post ("Blick hinter die Kulissen der Kimi-K3-Optimierung",
+ * technical note "Experten-Routing und Praezision") describes A4W4 as the
+ * MoE activations going from eight to four bits while the weights stay
+ * 4-bit, and serves MXFP4 model weights on MI355X.  MXFP4 as in the OCP
+ * Microscaling specification: FP4 E2M1 elements (values 0, 0.5, 1, 1.5, 2,
+ * 3, 4, 6 and their negatives; code bit 3 is the sign), two per byte with
+ * element 2i in the low nibble, and one E8M0 scale byte 2^(c - 127) per 32
+ * consecutive elements along K.  Routing is the indexed routing above.
+ * ---------------------------------------------------------------------- */
+
+/* Fill *out for an MXFP4 [E, N, K] weight (flag W4A16_DESC_MXFP4; host only).
+ * Packed layout, NT = N / 16, KC = K / 128:
+ *   packed_w : [E][NT][KC][64 lanes][16 bytes]; lane l = 16 g + i of (tile,
+ *     chunk c) holds row n = 16 tile + i, code bytes [64 c + 16 g, + 16) of
+ *     that row (the 32 elements of block 4 c + g: one scaled-FP4 MFMA operand
+ *     fragment);
+ *   packed_s : [E][NT][KC][64 lanes] bytes, the E8M0 scale of that block.
+ *   packed_w is E * N * K / 2 bytes, packed_s is E * N * K / 32.
+ * Errors: ERR_ARG (out NULL, E/N/K <= 0), ERR_SHAPE (K % 128 or N % 16). */
+w4a16_status w4a16_mxfp4_weight_desc_init(int32_t E, int32_t N, int32_t K, w4a16_weight_desc* out);
+
+/* Pack MXFP4 weights: codes [E, N, K/2] bytes (two per byte) and E8M0
+ * scales [E, N, K/32] bytes into the layout above.  codes 16-byte aligned;
+ * packed_w / packed_s 16-byte aligned and desc->w_bytes / desc->s_bytes long.
+ * Errors: ERR_ARG, ERR_LAYOUT (desc not from w4a16_mxfp4_weight_desc_init), ERR_HIP. */
+w4a16_status w4a16_mxfp4_pack(const uint8_t* codes, const uint8_t* scales, const w4a16_weight_desc* desc,
+                              void* packed_w, void* packed_s, w4a16_stream_t stream);
+
+/* Quantise bf16 rows x [rows, K] (K % 32 == 0) to MXFP4: codes [rows, K/2]
+ * bytes and scales [rows, K/32] bytes.  Per row and per block of 32: shared
+ * exponent floor(log2 max|v|) - 2 clamped to [-127, 127] (scale code 0 for a
+ * block of zeros), elements rounded to the nearest E2M1 value with ties to
+ * the even code, magnitudes past 6 clamped to 6, sign bit copied from the
+ * input (the OCP conversion).  Inf / NaN inputs give unspecified codes.
+ * x and codes 16-byte aligned.
+ * Errors: ERR_ARG, ERR_SHAPE, ERR_HIP. */
+w4a16_status w4a16_mxfp4_quant(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                               w4a16_stream_t stream);
+
+/* Bytes of workspace w4a16_mxfp4_moe_gemm needs (the top-k combine's fp32
+ * partials; 0 without combine). */
+size_t w4a16_mxfp4_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, int32_t T, int32_t topk,
+                                            int32_t combine);
+
+/* out = routed A4W4 product on MXFP4 activations (a_codes [a_rows, K/2],
+ * a_scales [a_rows, K/32], rows as a_layout says: W4A16_A_TOKEN or
+ * W4A16_A_SLOT) and an MXFP4 weight.  Outputs exactly as w4a16_moe_gemm:
+ * per-slot bf16 rows (topk_weights NULL) or the top-k-weighted combine into
+ * out[T, N] with fp32 partials summed in j order and rounded once.
+ * Accumulation is fp32 (the MFMA's); each output is rounded once to bf16.
+ *  cfg : NULL: block_m from the routing, nr 4, four waves, stages 4 for
+ *        block_m <= 32 else 2; split_k must be 1.
+ * Pointers: packed_w, packed_s, a_codes, out, workspace 16-byte aligned.
+ * Errors: ERR_ARG, ERR_LAYOUT (not an MXFP4 weight, E_loc or block_m
+ * mismatch), ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP. */
+w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w, const void* packed_s,
+                                  const uint8_t* a_codes, const uint8_t* a_scales, int64_t a_rows,
+                                  int32_t a_layout, const w4a16_indexed_routing* routing,
+                                  const float* topk_weights, uint16_t* out, const w4a16_config* cfg,
+                                  void* workspace, size_t workspace_bytes, w4a16_stream_t stream);
 
 #ifdef __cplusplus
 }

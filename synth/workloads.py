@@ -31,6 +31,7 @@ GROUP = 32  # scale group along K (the post's "group-32")
 _TAGS = {
     "logits": 0, "zipf_rank": 1, "zero_experts": 2, "x": 3, "a": 4,
     "w1_codes": 5, "w1_scales": 6, "w2_codes": 7, "w2_scales": 8,
+    "w1_mx_codes": 9, "w1_mx_scales": 10, "w2_mx_codes": 11, "w2_mx_scales": 12,
 }
 
 
@@ -65,6 +66,22 @@ def weight_scales(root_seed: int, tag: str, E: int, N: int, K: int,
     assert K % GROUP == 0
     rng = child_rng(root_seed, tag)
     return to_bf16_bits(rng.uniform(lo, hi, size=(E, N, K // GROUP)).astype(np.float32))
+
+
+def mx_weight_codes(root_seed: int, tag: str, E: int, N: int, K: int) -> np.ndarray:
+    """MXFP4 weight codes, every 4-bit E2M1 code uniform on 0..15, stored two
+    per byte: uniform bytes [E, N, K/2]."""
+    rng = child_rng(root_seed, tag)
+    return rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+
+
+def mx_weight_scales(root_seed: int, tag: str, E: int, N: int, K: int,
+                     lo: int = 120, hi: int = 123) -> np.ndarray:
+    """E8M0 scale codes uniform on [lo, hi) (2^-7 .. 2^-5 by default: weights
+    of magnitude up to about 0.19, like the INT4 weights' range), [E, N, K/32]."""
+    assert K % GROUP == 0
+    rng = child_rng(root_seed, tag)
+    return rng.integers(lo, hi, size=(E, N, K // GROUP), dtype=np.uint8)
 
 
 def route(root_seed: int, T: int, E_glob: int, topk: int,

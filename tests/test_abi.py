@@ -43,7 +43,7 @@ def test_struct_layouts_match_header():
 
 
 def test_version_and_desc(L):
-    assert L.w4a16_abi_version() == 2
+    assert L.w4a16_abi_version() == 3
     d = W.weight_desc(48, 4096, 7168)
     assert (d.K_pad, d.chunks, d.group) == (7168, 56, 32)
     assert d.w_bytes == 48 * 4096 * 7168 // 2
@@ -158,3 +158,33 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib._build, "lib_path", lambda: str(tmp_path / "nope.so"))
     with pytest.raises(_lib.W4A16Error):
         _lib.load()
+
+
+def test_mxfp4_descriptor_and_errors(L):
+    d = W.mxfp4_weight_desc(48, 4096, 7168)
+    assert d.flags == _lib.DESC_MXFP4 and d.chunks == 56
+    assert d.w_bytes == 48 * 4096 * 7168 // 2 and d.s_bytes == 48 * 4096 * 7168 // 32
+    e = _lib.WeightDesc()
+    assert L.w4a16_mxfp4_weight_desc_init(2, 32, 96, ctypes.byref(e)) == -2           # K % 128
+    P = 16
+    plain = W.weight_desc(8, 64, 256)
+    mx = W.mxfp4_weight_desc(8, 64, 256)
+    # each family's calls reject the other family's weights
+    assert L.w4a16_mxfp4_pack(P, P, ctypes.byref(plain), P, P, None) == -3
+    assert L.w4a16_pack_w4(P, P, ctypes.byref(mx), P, P, None) == -3
+    r = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 8)
+    cfg = W.mxfp4_config(32, 4)
+    call = lambda d=mx, layout=_lib.A_TOKEN, rows=64, c=cfg, w=None, ws=None, wsb=0: L.w4a16_mxfp4_moe_gemm(
+        ctypes.byref(d), P, P, P, P, rows, layout, ctypes.byref(r), w, P, ctypes.byref(c), ws, wsb, None)
+    assert call(d=plain) == -3                                           # not an MXFP4 weight
+    assert L.w4a16_moe_gemm(ctypes.byref(mx), P, P, P, 64, 0, ctypes.byref(r), None, P,
+                            ctypes.byref(W.config(32, 2)), None, 0, None) == -3
+    assert call(layout=_lib.A_SORTED) == -1                              # token or slot rows only
+    assert call(rows=10) == -2                                           # too few rows
+    assert call(c=W.mxfp4_config(32, 3)) == -4                           # not built
+    assert call(c=W.config(32, 4, split_k=0, stages=4)) == -4            # one workgroup per tile
+    assert call(c=W.mxfp4_config(64, 4)) == -3                           # block_m disagrees with routing
+    assert call(w=P) == -8                                               # combine without workspace
+    assert L.w4a16_mxfp4_moe_gemm_workspace_bytes(ctypes.byref(mx), 10, 8, 1) == 10 * 8 * 64 * 4
+    assert L.w4a16_mxfp4_quant(P, 4, 48, P, P, None) == -2               # K % 32
+    assert L.w4a16_mxfp4_quant(P + 4, 4, 64, P, P, None) == -1           # misaligned rows

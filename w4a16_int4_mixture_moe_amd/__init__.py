@@ -2,10 +2,12 @@
 
 BF16 activations x INT4 weights with BF16 group-32 scales, routed through
 sorted_ids / expert_ids / num_tokens_padded (indexed) or the grouped
-contiguous / masked layouts.  The computation lives in the HIP library built
+contiguous / masked layouts; and the A4W4 variant (MXFP4 activations x
+MXFP4 weights) on the same indexed routing.  The computation lives in the HIP library built
 from csrc/ (C ABI: include/w4a16_moe.h); this package is its binding.
 """
-from .api import (Config, PackedW4, Routing, W4A16Error, align_capacity, config,  # noqa: F401
+from .api import (Config, MXRows, PackedW4, Routing, W4A16Error, align_capacity, config,  # noqa: F401
                   grouped_contiguous, grouped_masked, indexed_config, moe_align, moe_gate_up_silu,
-                  moe_w4a16_gemm, pack_w4, select, weight_desc, workspace_bytes)
+                  moe_mxfp4_gemm, moe_w4a16_gemm, mxfp4_config, mxfp4_quant, mxfp4_weight_desc,
+                  pack_mxfp4, pack_w4, select, weight_desc, workspace_bytes)
 from ._lib import lib_path, load  # noqa: F401

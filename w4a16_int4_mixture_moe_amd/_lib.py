@@ -34,6 +34,7 @@ class WeightDesc(ctypes.Structure):
 
 
 DESC_GATE_UP = 1            # W4A16_DESC_GATE_UP
+DESC_MXFP4 = 2              # W4A16_DESC_MXFP4
 A_TOKEN, A_SLOT, A_SORTED = 0, 1, 2   # W4A16_A_TOKEN / _SLOT / _SORTED
 
 
@@ -82,6 +83,13 @@ SIGNATURES = {
                                         ctypes.POINTER(Config), _P]),
     "w4a16_grouped_masked": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I32, _P, _I32, _P,
                                     ctypes.POINTER(Config), _P]),
+    "w4a16_mxfp4_weight_desc_init": (_I32, [_I32, _I32, _I32, ctypes.POINTER(WeightDesc)]),
+    "w4a16_mxfp4_pack": (_I32, [_P, _P, ctypes.POINTER(WeightDesc), _P, _P, _P]),
+    "w4a16_mxfp4_quant": (_I32, [_P, _I64, _I32, _P, _P, _P]),
+    "w4a16_mxfp4_moe_gemm_workspace_bytes": (_SZ, [ctypes.POINTER(WeightDesc), _I32, _I32, _I32]),
+    "w4a16_mxfp4_moe_gemm": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _P, _I64, _I32,
+                                    ctypes.POINTER(IndexedRouting), _P, _P, ctypes.POINTER(Config),
+                                    _P, _SZ, _P]),
 }
 
 _lib = None

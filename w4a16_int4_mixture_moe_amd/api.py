@@ -12,6 +12,10 @@ the computation runs in the HIP library's kernels.
     y = moe_w4a16_gemm(inter, packed2, routing, topk_weights, a_layout="sorted")
     out = grouped_contiguous(a2[m, K], packed, m_indices)
     out = grouped_masked(a3[E, max_m, K], packed, masked_m, expected_m)
+    # A4W4: MXFP4 weights, activations quantised to MXFP4 on the device
+    pm = pack_mxfp4(codes_u8[E, N, K/2], scales_e8m0[E, N, K/32])
+    q = mxfp4_quant(x[T, K])                                         # MXFP4 rows
+    h = moe_mxfp4_gemm(q, pm, routing)                               # per slot
 """
 from __future__ import annotations
 
@@ -21,8 +25,8 @@ from typing import Optional
 
 import torch
 
-from ._lib import (A_SLOT, A_SORTED, A_TOKEN, DESC_GATE_UP, Config, IndexedRouting, W4A16Error,
-                   WeightDesc, check, load)
+from ._lib import (A_SLOT, A_SORTED, A_TOKEN, DESC_GATE_UP, DESC_MXFP4, Config, IndexedRouting,
+                   W4A16Error, WeightDesc, check, load)
 
 
 def _stream(dev: torch.device) -> ctypes.c_void_p:
@@ -291,3 +295,106 @@ __all__ = [
     "grouped_contiguous",
     "grouped_masked",
 ]
+
+
+# ------------------------------------------------------------ A4W4 (MXFP4)
+
+@dataclasses.dataclass
+class MXRows:
+    """MXFP4 rows: codes uint8 [rows, K/2] (two E2M1 codes per byte, element
+    2i in the low nibble) and E8M0 scales uint8 [rows, K/32]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+
+    @property
+    def rows(self):
+        return self.codes.shape[0]
+
+    @property
+    def K(self):
+        return 2 * self.codes.shape[1]
+
+
+def mxfp4_weight_desc(E: int, N: int, K: int) -> WeightDesc:
+    d = WeightDesc()
+    check(load().w4a16_mxfp4_weight_desc_init(E, N, K, ctypes.byref(d)))
+    return d
+
+
+def pack_mxfp4(codes: torch.Tensor, scales: torch.Tensor) -> PackedW4:
+    """MXFP4 weight: codes uint8 [E, N, K/2] (two per byte), E8M0 scales
+    uint8 [E, N, K/32] -> packed weight (K % 128 == 0)."""
+    _need(codes, "codes", (torch.uint8,), 3)
+    _need(scales, "scales", (torch.uint8,), 3)
+    E, N, K2 = codes.shape
+    K = 2 * K2
+    if tuple(scales.shape) != (E, N, K // 32):
+        raise ValueError(f"scales shape {tuple(scales.shape)} does not match codes {tuple(codes.shape)}")
+    d = mxfp4_weight_desc(E, N, K)
+    w = torch.empty(d.w_bytes, dtype=torch.uint8, device=codes.device)
+    s = torch.empty(d.s_bytes, dtype=torch.uint8, device=codes.device)
+    check(load().w4a16_mxfp4_pack(codes.data_ptr(), scales.data_ptr(), ctypes.byref(d), w.data_ptr(),
+                                  s.data_ptr(), _stream(codes.device)))
+    return PackedW4(d, w, s)
+
+
+def mxfp4_quant(x: torch.Tensor, out: Optional[MXRows] = None) -> MXRows:
+    """bf16 [rows, K] -> MXFP4 rows (per row and block of 32: shared exponent
+    floor(log2 max|v|) - 2, nearest-even E2M1 elements clamped at 6)."""
+    _need(x, "x", _BF16, 2)
+    R, K = x.shape
+    if out is None:
+        out = MXRows(torch.empty(R, K // 2, dtype=torch.uint8, device=x.device),
+                     torch.empty(R, K // 32, dtype=torch.uint8, device=x.device))
+    elif out.rows < R or out.K != K:
+        raise ValueError(f"out must hold [{R}, {K}] MXFP4 rows")
+    check(load().w4a16_mxfp4_quant(x.data_ptr(), R, K, out.codes.data_ptr(), out.scales.data_ptr(),
+                                   _stream(x.device)))
+    return out
+
+
+def mxfp4_config(block_m: int, nr: int = 4, stages: Optional[int] = None) -> Config:
+    return config(block_m, nr, waves=4, split_k=1, stages=(4 if block_m <= 32 else 2) if stages is None else stages)
+
+
+def moe_mxfp4_gemm(a: MXRows, packed: PackedW4, routing: Routing,
+                   topk_weights: Optional[torch.Tensor] = None, a_layout: Optional[str] = None,
+                   cfg: Optional[Config] = None, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Indexed A4W4 MoE GEMM on MXFP4 rows and an MXFP4 weight; outputs as
+    moe_w4a16_gemm (per slot, or the top-k combine with topk_weights).
+    a_layout: "token" or "slot" (default "slot" with topk_weights)."""
+    if packed.desc.flags != DESC_MXFP4:
+        raise ValueError("moe_mxfp4_gemm needs a weight from pack_mxfp4")
+    _need(a.codes, "a.codes", (torch.uint8,), 2)
+    _need(a.scales, "a.scales", (torch.uint8,), 2)
+    T, k = routing.T, routing.topk
+    if a_layout is None:
+        a_layout = "slot" if topk_weights is not None else "token"
+    if a_layout not in ("token", "slot"):
+        raise ValueError('a_layout must be "token" or "slot"')
+    if a.K != packed.K or a.scales.shape[1] != packed.K // 32:
+        raise ValueError(f"activations have K={a.K}, weight has K={packed.K}")
+    dev = a.codes.device
+    combine = topk_weights is not None
+    if combine:
+        _need(topk_weights, "topk_weights", (torch.float32,), 2)
+    rows = T if combine else T * k
+    if out is None:
+        out = (torch.zeros if not combine else torch.empty)(rows, packed.N, dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", _BF16, 2)
+        if out.shape[0] < rows or out.shape[1] != packed.N:
+            raise ValueError(f"out must be [{rows}, {packed.N}]")
+    if workspace is None:
+        nws = int(load().w4a16_mxfp4_moe_gemm_workspace_bytes(ctypes.byref(packed.desc), T, k, int(combine)))
+        if nws:
+            workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    r = routing.as_c()
+    check(load().w4a16_mxfp4_moe_gemm(ctypes.byref(packed.desc), packed.w.data_ptr(), packed.s.data_ptr(),
+                                      a.codes.data_ptr(), a.scales.data_ptr(), a.rows, _A_LAYOUTS[a_layout],
+                                      ctypes.byref(r), _ptr(topk_weights), out.data_ptr(),
+                                      None if cfg is None else ctypes.byref(cfg),
+                                      _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                      _stream(dev)))
+    return out

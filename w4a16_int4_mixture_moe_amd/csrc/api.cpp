@@ -67,7 +67,8 @@ w4a16_weight_desc make_desc(int32_t E, int32_t N, int32_t K, int32_t flags) {
   d.group = 32;
   const int64_t NT = N / 16;
   d.w_bytes = (uint64_t)E * NT * KC * 1024;
-  d.s_bytes = (uint64_t)E * NT * ((KC + 1) / 2) * 64 * 4;
+  d.s_bytes = flags == W4A16_DESC_MXFP4 ? (uint64_t)E * NT * KC * 64            // one E8M0 byte per lane
+                                        : (uint64_t)E * NT * ((KC + 1) / 2) * 64 * 4;
   d.check = desc_checksum(d);
   return d;
 }
@@ -87,10 +88,28 @@ w4a16_status check_desc(const w4a16_weight_desc* d) {
   if (d->check != desc_checksum(*d)) return fail(W4A16_ERR_LAYOUT, "weight descriptor checksum mismatch (corrupted)");
   w4a16_status st = check_shape(d->E, d->N, d->K);
   if (st != W4A16_OK) return fail(W4A16_ERR_LAYOUT, "weight descriptor shape invalid: %s", g_last_error.c_str());
-  if (d->flags != 0 && (d->flags != W4A16_DESC_GATE_UP || d->N % 32))
-    return fail(W4A16_ERR_LAYOUT, "weight descriptor flags invalid");
+  const bool flags_ok = d->flags == 0 || (d->flags == W4A16_DESC_GATE_UP && d->N % 32 == 0) ||
+                        (d->flags == W4A16_DESC_MXFP4 && d->K % 128 == 0);
+  if (!flags_ok) return fail(W4A16_ERR_LAYOUT, "weight descriptor flags invalid");
   const w4a16_weight_desc ref = make_desc(d->E, d->N, d->K, d->flags);
   if (std::memcmp(&ref, d, sizeof ref) != 0) return fail(W4A16_ERR_LAYOUT, "weight descriptor fields inconsistent");
+  return W4A16_OK;
+}
+
+// An INT4 (W4A16) weight descriptor: valid, and not an MXFP4 one.
+w4a16_status check_int4_desc(const w4a16_weight_desc* d) {
+  w4a16_status st = check_desc(d);
+  if (st != W4A16_OK) return st;
+  if (d->flags == W4A16_DESC_MXFP4)
+    return fail(W4A16_ERR_LAYOUT, "an MXFP4 weight descriptor is used by the w4a16_mxfp4_* calls only");
+  return W4A16_OK;
+}
+
+w4a16_status check_mx_desc(const w4a16_weight_desc* d) {
+  w4a16_status st = check_desc(d);
+  if (st != W4A16_OK) return st;
+  if (d->flags != W4A16_DESC_MXFP4)
+    return fail(W4A16_ERR_LAYOUT, "not an MXFP4 weight descriptor (use w4a16_mxfp4_weight_desc_init)");
   return W4A16_OK;
 }
 
@@ -263,7 +282,7 @@ w4a16_status w4a16_weight_desc_init_gate_up(int32_t E, int32_t N, int32_t K, w4a
 w4a16_status w4a16_pack_w4(const uint8_t* codes, const uint16_t* scales,
                            const w4a16_weight_desc* desc, void* packed_w, void* packed_s,
                            w4a16_stream_t stream) {
-  w4a16_status st = check_desc(desc);
+  w4a16_status st = check_int4_desc(desc);
   if (st != W4A16_OK) return st;
   if (!codes || !scales || !packed_w || !packed_s) return fail(W4A16_ERR_ARG, "NULL pointer argument");
   if (!aligned16(packed_w) || !aligned16(packed_s)) return fail(W4A16_ERR_ARG, "packed buffers must be 16-byte aligned");
@@ -348,7 +367,7 @@ w4a16_status w4a16_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc
 
 size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, int32_t T, int32_t topk,
                                       int32_t combine, const w4a16_config* cfg) {
-  if (check_desc(desc) != W4A16_OK || T < 0 || topk <= 0) return 0;
+  if (check_int4_desc(desc) != W4A16_OK || T < 0 || topk <= 0) return 0;
   const w4a16_config c = cfg ? *cfg : default_indexed_config(16);
   const int epi = combine ? w4a16::kEpiWeighted : w4a16::kEpiStore;
   if (check_config(c, w4a16::kRouteIndexed, epi) != W4A16_OK) return 0;
@@ -361,7 +380,7 @@ w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
                             const float* topk_weights, uint16_t* out,
                             const w4a16_config* cfg, void* workspace, size_t workspace_bytes,
                             w4a16_stream_t stream) {
-  w4a16_status st = check_desc(desc);
+  w4a16_status st = check_int4_desc(desc);
   if (st != W4A16_OK) return st;
   if (!routing) return fail(W4A16_ERR_ARG, "routing is NULL");
   const w4a16_indexed_routing& r = *routing;
@@ -436,7 +455,7 @@ w4a16_status w4a16_moe_gate_up_silu(const w4a16_weight_desc* desc, const void* p
                                     const void* packed_s, const uint16_t* x, int64_t x_rows,
                                     const w4a16_indexed_routing* routing, uint16_t* out,
                                     const w4a16_config* cfg, w4a16_stream_t stream) {
-  w4a16_status st = check_desc(desc);
+  w4a16_status st = check_int4_desc(desc);
   if (st != W4A16_OK) return st;
   if (desc->flags != W4A16_DESC_GATE_UP)
     return fail(W4A16_ERR_LAYOUT, "the fused SiLU gate/up call needs a weight packed with w4a16_weight_desc_init_gate_up");
@@ -478,7 +497,7 @@ w4a16_status w4a16_grouped_contiguous(const w4a16_weight_desc* desc, const void*
                                       const void* packed_s, const uint16_t* a, int64_t m_rows,
                                       const int32_t* m_indices, uint16_t* out,
                                       const w4a16_config* cfg, w4a16_stream_t stream) {
-  w4a16_status st = check_desc(desc);
+  w4a16_status st = check_int4_desc(desc);
   if (st != W4A16_OK) return st;
   if (m_rows < 0) return fail(W4A16_ERR_ARG, "m_rows < 0");
   if (m_rows > 0 && (!a || !m_indices || !out)) return fail(W4A16_ERR_ARG, "NULL pointer argument");
@@ -512,7 +531,7 @@ w4a16_status w4a16_grouped_masked(const w4a16_weight_desc* desc, const void* pac
                                   const void* packed_s, const uint16_t* a, int32_t max_m,
                                   const int32_t* masked_m, int32_t expected_m, uint16_t* out,
                                   const w4a16_config* cfg, w4a16_stream_t stream) {
-  w4a16_status st = check_desc(desc);
+  w4a16_status st = check_int4_desc(desc);
   if (st != W4A16_OK) return st;
   if (max_m <= 0) return fail(W4A16_ERR_ARG, "max_m must be positive");
   if (!a || !masked_m || !out || !packed_w || !packed_s) return fail(W4A16_ERR_ARG, "NULL pointer argument");
@@ -545,6 +564,121 @@ w4a16_status w4a16_grouped_masked(const w4a16_weight_desc* desc, const void* pac
   hipError_t e = w4a16::launch_gemm(w4a16::kRouteMasked, w4a16::kEpiStore, c.block_m / 16, c.nr,
                                     c.waves, c.stages, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "grouped_masked launch");
+  return W4A16_OK;
+}
+
+// ------------------------------------------------------------ A4W4 (MXFP4)
+
+w4a16_status w4a16_mxfp4_weight_desc_init(int32_t E, int32_t N, int32_t K, w4a16_weight_desc* out) {
+  if (out == nullptr) return fail(W4A16_ERR_ARG, "out is NULL");
+  w4a16_status st = check_shape(E, N, K);
+  if (st != W4A16_OK) return st;
+  if (K % 128) return fail(W4A16_ERR_SHAPE, "an MXFP4 weight needs K %% 128 == 0 (got %d)", K);
+  *out = make_desc(E, N, K, W4A16_DESC_MXFP4);
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_mxfp4_pack(const uint8_t* codes, const uint8_t* scales, const w4a16_weight_desc* desc,
+                              void* packed_w, void* packed_s, w4a16_stream_t stream) {
+  w4a16_status st = check_mx_desc(desc);
+  if (st != W4A16_OK) return st;
+  if (!codes || !scales || !packed_w || !packed_s) return fail(W4A16_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(codes) || !aligned16(packed_w) || !aligned16(packed_s))
+    return fail(W4A16_ERR_ARG, "codes and packed buffers must be 16-byte aligned");
+  hipError_t e = w4a16::launch_mx_pack(codes, scales, desc->E, desc->N, desc->K, static_cast<uint4*>(packed_w),
+                                       static_cast<uint8_t*>(packed_s), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mxfp4_pack launch");
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_mxfp4_quant(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                               w4a16_stream_t stream) {
+  if (rows < 0 || K <= 0) return fail(W4A16_ERR_ARG, "bad sizes rows=%lld K=%d", (long long)rows, K);
+  if (K % 32) return fail(W4A16_ERR_SHAPE, "K = %d is not a multiple of the MX block 32", K);
+  if (rows == 0) return W4A16_OK;
+  if (!x || !codes || !scales) return fail(W4A16_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(x) || !aligned16(codes)) return fail(W4A16_ERR_ARG, "x and codes must be 16-byte aligned");
+  hipError_t e = w4a16::launch_mx_quant(x, rows, K, codes, scales, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mxfp4_quant launch");
+  return W4A16_OK;
+}
+
+size_t w4a16_mxfp4_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, int32_t T, int32_t topk,
+                                            int32_t combine) {
+  if (check_mx_desc(desc) != W4A16_OK || T < 0 || topk <= 0) return 0;
+  return combine_region(T, topk, desc->N, combine != 0);
+}
+
+w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w, const void* packed_s,
+                                  const uint8_t* a_codes, const uint8_t* a_scales, int64_t a_rows,
+                                  int32_t a_layout, const w4a16_indexed_routing* routing,
+                                  const float* topk_weights, uint16_t* out, const w4a16_config* cfg,
+                                  void* workspace, size_t workspace_bytes, w4a16_stream_t stream) {
+  w4a16_status st = check_mx_desc(desc);
+  if (st != W4A16_OK) return st;
+  if (!routing) return fail(W4A16_ERR_ARG, "routing is NULL");
+  const w4a16_indexed_routing& r = *routing;
+  const bool combine = topk_weights != nullptr;
+  if (!packed_w || !packed_s || !r.sorted_ids || !r.expert_ids || !r.num_tokens_padded)
+    return fail(W4A16_ERR_ARG, "NULL pointer argument");
+  if (r.T < 0 || r.topk <= 0 || r.capacity < 0) return fail(W4A16_ERR_ARG, "bad routing sizes");
+  if (r.T > 0 && (!a_codes || !a_scales || !out)) return fail(W4A16_ERR_ARG, "activations or output are NULL");
+  if (!aligned16(packed_w) || !aligned16(packed_s) || !aligned16(a_codes) || !aligned16(out))
+    return fail(W4A16_ERR_ARG, "packed weights, activation codes and output must be 16-byte aligned");
+  if (r.E_loc != desc->E)
+    return fail(W4A16_ERR_LAYOUT, "routing has E_loc=%d but the packed weight holds %d experts", r.E_loc, desc->E);
+  if (a_layout != W4A16_A_TOKEN && a_layout != W4A16_A_SLOT)
+    return fail(W4A16_ERR_ARG, "a_layout %d is not W4A16_A_TOKEN or W4A16_A_SLOT", a_layout);
+  const int64_t need_rows = a_layout == W4A16_A_TOKEN ? (int64_t)r.T : (int64_t)r.T * r.topk;
+  if (a_rows < need_rows)
+    return fail(W4A16_ERR_SHAPE, "activations have %lld rows, need %lld", (long long)a_rows, (long long)need_rows);
+  if ((int64_t)r.T * r.topk >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "T*topk too large");
+  if (a_rows * (int64_t)(desc->K / 2) >= ((int64_t)1 << 32))
+    return fail(W4A16_ERR_SHAPE, "activation codes exceed 4 GiB (32-bit row offsets)");
+  const int epi = combine ? w4a16::kEpiWeighted : w4a16::kEpiStore;
+  w4a16_config c;
+  if (cfg) {
+    c = *cfg;
+  } else {
+    c.block_m = r.block_m;            // the routing buffers fix block_m
+    c.nr = 4;
+    c.waves = 4;
+    c.split_k = 1;
+    c.stages = r.block_m <= 32 ? 4 : 2;
+    apply_env_overrides(&c);
+  }
+  if (!valid_block_m(c.block_m)) return fail(W4A16_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128}", c.block_m);
+  if (c.split_k != 1) return fail(W4A16_ERR_UNSUPPORTED, "the MXFP4 GEMM runs one workgroup per tile (split_k = 1)");
+  if (!w4a16::mx_gemm_config_supported(epi, c.block_m / 16, c.nr, c.waves, c.stages))
+    return fail(W4A16_ERR_UNSUPPORTED, "MXFP4 tile config block_m=%d nr=%d waves=%d stages=%d not built", c.block_m,
+                c.nr, c.waves, c.stages);
+  if (c.block_m != r.block_m)
+    return fail(W4A16_ERR_LAYOUT, "config block_m=%d differs from the routing's block_m=%d", c.block_m, r.block_m);
+  if (r.capacity % r.block_m) return fail(W4A16_ERR_CAPACITY, "capacity not a multiple of block_m");
+  if (combine && !r.topk_ids) return fail(W4A16_ERR_ARG, "combine needs routing.topk_ids");
+  const size_t need = combine_region(r.T, r.topk, desc->N, combine);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(W4A16_ERR_WORKSPACE, "this call needs %zu bytes of 16-byte aligned workspace, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (r.T == 0) return W4A16_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  w4a16::GemmParams p = base_params(desc, packed_w, packed_s, reinterpret_cast<const uint16_t*>(a_codes),
+                                    combine ? workspace : (void*)out, c.nr, c.waves);
+  p.a_scale = a_scales;
+  p.sorted_ids = r.sorted_ids;
+  p.expert_ids = r.expert_ids;
+  p.num_tokens_padded = r.num_tokens_padded;
+  p.sentinel = r.T * r.topk;
+  p.a_row_div = a_layout == W4A16_A_TOKEN ? r.topk : 1;
+  p.slot_weight = topk_weights;
+  p.grid_blocks = (int32_t)(r.capacity / r.block_m);
+  hipError_t e = w4a16::launch_mx_gemm(epi, c.block_m / 16, c.nr, c.waves, c.stages, p, s);
+  if (e != hipSuccess) return hip_fail(e, "mxfp4_moe_gemm launch");
+  if (combine) {
+    e = w4a16::launch_combine(static_cast<const float*>(workspace), r.topk_ids, r.T, r.topk, r.first_expert,
+                              r.E_loc, desc->N, out, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
   return W4A16_OK;
 }
 

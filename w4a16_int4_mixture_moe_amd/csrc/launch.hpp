@@ -24,8 +24,9 @@ enum EpilogueKind : int { kEpiStore = 0, kEpiWeighted = 1, kEpiSilu = 2 };
 
 struct GemmParams {
   const uint4* packed_w;        // [E][NT][KC][64][4 words]
-  const uint32_t* packed_s;     // [E][NT][KC2][64], bf16 scale pairs
-  const uint16_t* a;            // bf16 activations, row stride K
+  const uint32_t* packed_s;     // [E][NT][KC2][64], bf16 scale pairs (MXFP4: [E][NT][KC][64] E8M0 bytes)
+  const uint16_t* a;            // bf16 activations, row stride K (MXFP4: E2M1 codes, two per byte, row stride K/2 bytes)
+  const uint8_t* a_scale;       // MXFP4 activations: E8M0 scales, row stride K/32 bytes
   int32_t E, N, K, NT, KC;
   int32_t n_tiles;              // workgroup tiles along N
   // indexed
@@ -74,6 +75,20 @@ size_t streamk_partial_bytes(int m_tiles, int nr, int waves, int workgroups);
 // ---- combine of weighted per-slot partials (gemm.hip)
 hipError_t launch_combine(const float* partial, const int32_t* topk_ids, int32_t T, int32_t topk,
                           int32_t first, int32_t E_loc, int32_t N, uint16_t* out,
+                          hipStream_t stream);
+
+// ---- A4W4: MXFP4 activations x MXFP4 weights (mx.hip)
+// bf16 [rows][K] -> E2M1 codes [rows][K/2] (two per byte, low nibble first)
+// and E8M0 scales [rows][K/32]; K % 32 == 0.
+hipError_t launch_mx_quant(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                           hipStream_t stream);
+// codes [E][N][K/2] + scales [E][N][K/32] -> packed [E][N/16][K/128][64]
+// 16-byte fragments + [E][N/16][K/128][64] scale bytes; K % 128 == 0.
+hipError_t launch_mx_pack(const uint8_t* w, const uint8_t* s, int32_t E, int32_t N, int32_t K, uint4* pw,
+                          uint8_t* ps, hipStream_t stream);
+// Indexed routing only; epilogue kEpiStore or kEpiWeighted.
+bool mx_gemm_config_supported(int epilogue, int m_tiles, int nr, int waves, int stages);
+hipError_t launch_mx_gemm(int epilogue, int m_tiles, int nr, int waves, int stages, const GemmParams& p,
                           hipStream_t stream);
 
 }  // namespace w4a16

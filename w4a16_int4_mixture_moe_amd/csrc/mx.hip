@@ -1,0 +1,319 @@
+// A4W4 path for gfx950: MXFP4 activations x MXFP4 weights (FP4 E2M1 codes,
+// one E8M0 scale per 32 consecutive K) in v_mfma_scale_f32_16x16x128_f8f6f4,
+// routed like the W4A16 GEMM (indexed sorted_ids / expert_ids).
+//
+// The AMD Kimi K3 post ("Blick hinter die Kulissen der Kimi-K3-Optimierung",
+// technical note "Experten-Routing und Praezision") describes A4W4 as the
+// MoE activations going from eight to four bits while the weights stay
+// 4-bit, with MXFP4 model weights on MI355X; the formats are those of the OCP
+// Microscaling specification (E2M1 elements, E8M0 block scales).
+//
+// Operand layout of the scaled FP4 MFMA (16 x 16 x 128; checked on the
+// device): lane l holds row l % 16 of its operand and the 32 consecutive K of
+// block l / 16 of the 128, element i in nibble i of the lane's 128-bit value
+// (low nibble first), and that block's E8M0 scale in byte 0 of its scale
+// register.  A row of MXFP4 codes stored two per byte (element 2i in the low
+// nibble) therefore already holds, for every lane, exactly the 16 bytes it
+// needs: bytes 64 c + 16 (l / 16) of the row for K chunk c.  So
+//   - activations need no staging: each lane loads its 16 bytes and its one
+//     scale byte straight from the quantised rows (L2), no LDS, no barrier;
+//   - weights are re-tiled once (mx_pack_kernel) to [E][N/16][K/128][64]
+//     16-byte lane fragments plus [E][N/16][K/128][64] scale bytes, so a
+//     wave's tile stream is contiguous;
+//   - there is nothing to dequantise: one MFMA per (weight tile, token tile,
+//     chunk).
+// Activation quantisation (mx_quant_kernel) is the OCP conversion: shared
+// exponent floor(log2 max|v|) - 2 clamped to E8M0's range (a zero block takes
+// code 0), elements rounded to the nearest E2M1 value, ties to even, clamped
+// at 6, sign from the input's sign bit.
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+#include "tile_common.hpp"
+
+namespace w4a16 {
+
+// ------------------------------------------------------------ quantisation
+
+// |y| -> E2M1 magnitude code: the number of rounding thresholds |y| has
+// passed.  Between two neighbours the tie goes to the even code (mantissa 0):
+// the threshold is strict (>) where the upper neighbour is odd and inclusive
+// (>=) where it is even; past 5 everything rounds to 6 (code 7).
+__device__ __forceinline__ uint32_t e2m1_mag(float a) {
+  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+         (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+}
+
+// One thread per 32-element block: 64 bytes of bf16 in, 16 bytes of codes
+// and one scale byte out.
+__global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restrict__ x, int64_t blocks,
+                                                        int32_t kb, uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= blocks) return;
+  const int64_t row = i / kb;
+  const int b = (int)(i - row * kb);
+  const uint4* src = reinterpret_cast<const uint4*>(x + row * (int64_t)kb * 32 + b * 32);
+  uint32_t v[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 u = src[q];
+    v[4 * q] = u.x;
+    v[4 * q + 1] = u.y;
+    v[4 * q + 2] = u.z;
+    v[4 * q + 3] = u.w;
+  }
+  // max |v| as a bit pattern: for finite bf16 the magnitude bits order like
+  // the values, and only the exponent field is needed
+  uint32_t amax = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) amax = max(amax, max(v[q] & 0x7FFFu, (v[q] >> 16) & 0x7FFFu));
+  // floor(log2 amax) = exponent field - 127 for a normal amax; subnormal and
+  // zero blocks clamp to code 0 either way, so code = max(field - 2, 0)
+  const int field = (int)(amax >> 7);
+  const uint32_t code = (uint32_t)max(field - 2, 0);
+  const float inv = __builtin_bit_cast(float, (254u - code) << 23);    // 2^(127 - code), exact
+  uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const uint32_t h = (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xFFFFu);
+    const float y = __builtin_bit_cast(float, h << 16) * inv;          // exact (denormals kept)
+    const uint32_t c = e2m1_mag(__builtin_fabsf(y)) | ((h >> 12) & 8u);
+    out[e >> 3] |= c << (4 * (e & 7));
+  }
+  *reinterpret_cast<uint4*>(codes + i * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+  scales[i] = (uint8_t)code;
+}
+
+hipError_t launch_mx_quant(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                           hipStream_t stream) {
+  const int64_t blocks = rows * (K / 32);
+  if (blocks == 0) return hipSuccess;
+  const int64_t grid = (blocks + 255) / 256;
+  if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, blocks, K / 32, codes,
+                     scales);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ weight packing
+
+// One thread per (expert, tile, chunk, lane): row n = 16 tile + lane % 16,
+// block 4 chunk + lane / 16 -> the row's 16 code bytes of that block and its
+// scale byte.
+__global__ __launch_bounds__(256) void mx_pack_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ s,
+                                                       int32_t E, int32_t N, int32_t K, uint4* __restrict__ pw,
+                                                       uint8_t* __restrict__ ps) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int KC = K / 128, NT = N / 16;
+  const int64_t total = (int64_t)E * NT * KC * kWave;
+  if (i >= total) return;
+  const int lane = (int)(i % kWave);
+  const int64_t q = i / kWave;
+  const int c = (int)(q % KC);
+  const int64_t et = q / KC;                    // expert * NT + tile
+  const int t = (int)(et % NT);
+  const int64_t e = et / NT;
+  const int64_t n = e * N + 16 * t + (lane & 15);
+  const int b = 4 * c + (lane >> 4);
+  pw[i] = *reinterpret_cast<const uint4*>(w + n * (K / 2) + 16 * b);
+  ps[i] = s[n * (K / 32) + b];
+}
+
+hipError_t launch_mx_pack(const uint8_t* w, const uint8_t* s, int32_t E, int32_t N, int32_t K, uint4* pw,
+                          uint8_t* ps, hipStream_t stream) {
+  const int64_t total = (int64_t)E * (N / 16) * (K / 128) * kWave;
+  if (total == 0) return hipSuccess;
+  const int64_t grid = (total + 255) / 256;
+  if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(mx_pack_kernel, dim3((unsigned)grid), dim3(256), 0, stream, w, s, E, N, K, pw, ps);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ GEMM
+
+template <int MT>
+struct MxSmem {
+  int row[16 * MT];
+  int out[16 * MT];
+  float w[16 * MT];
+};
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// 128 K of one weight tile (A) against 128 K of one token tile (B); only the
+// low four dwords of each operand carry FP4 data
+__device__ __forceinline__ f32x4_t mx_mfma(const u32x4_t& w, uint32_t ws, const u32x4_t& x, uint32_t xs,
+                                           const f32x4_t& acc) {
+  const i32x8_t A = {(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+  const i32x8_t B = {(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 4, 4, 0, (int)ws, 0, (int)xs);
+}
+
+__device__ __forceinline__ uint32_t gload_u8(gptr_t p) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) uint8_t*>(p);
+}
+
+// acc += this wave's NR weight tiles x the block's first NA token tiles over
+// all K chunks.  A ring of D stages, each holding one chunk's weight and
+// activation fragments and scales: chunk c lives in stage c mod D and the
+// stage is refilled with chunk c + D right after its MFMAs are issued, so
+// every load has D - 1 chunks of MFMAs and loads ahead of its use.  Loads
+// past the last chunk re-read the last chunk (never used), so every stage is
+// filled unconditionally and in the same order on every path.
+template <int MT, int NR, int NW, int D, int NA>
+__device__ __forceinline__ void mx_mainloop(const GemmParams& p, const MxSmem<MT>& sm, int expert, int nt,
+                                            f32x4_t (&acc)[NR][MT]) {
+  static_assert(NA >= 1 && NA <= MT, "active token tiles");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int KC = p.KC;
+
+  // activation rows: 16-byte fragment and scale byte of (row, block l/16)
+  const gptr_t abase = uniform_ptr(p.a);
+  const gptr_t asbase = uniform_ptr(p.a_scale);
+  const uint32_t kb = (uint32_t)p.K / 2, ks = (uint32_t)p.K / 32;
+  const int fallback_row = sm.row[0];
+  uint32_t aoff[NA], asoff[NA];
+#pragma unroll
+  for (int t = 0; t < NA; ++t) {
+    const int r = sm.row[16 * t + (lane & 15)];
+    const uint32_t row = (uint32_t)(r >= 0 ? r : fallback_row);     // padding reads a valid row
+    aoff[t] = row * kb + 16u * (uint32_t)(lane >> 4);
+    asoff[t] = row * ks + (uint32_t)(lane >> 4);
+  }
+  // weight tiles (clamped: tiles past N compute values never stored)
+  const int rt_base = nt * (NW * NR) + wave * NR;
+  gptr_t wbase[NR], sbase[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int rt = min(rt_base + r, p.NT - 1);
+    const int64_t tile = (int64_t)expert * p.NT + rt;
+    wbase[r] = uniform_ptr(p.packed_w + tile * KC * kWave);
+    sbase[r] = uniform_ptr(reinterpret_cast<const uint8_t*>(p.packed_s) + tile * KC * kWave);
+  }
+  const uint32_t woff = (uint32_t)lane * 16u;
+
+  u32x4_t wr[D][NR], xr[D][NA];
+  uint32_t wsr[D][NR], xsr[D][NA];
+  auto issue = [&](int st, int c) {
+    c = min(c, KC - 1);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      wr[st][r] = gload_u32x4((wbase[r] + (int64_t)c * (kWave * 16)) + woff);
+      wsr[st][r] = gload_u8((sbase[r] + (int64_t)c * kWave) + (uint32_t)lane);
+    }
+    const gptr_t ac = abase + (int64_t)c * 64, asc = asbase + (int64_t)c * 4;
+#pragma unroll
+    for (int t = 0; t < NA; ++t) {
+      xr[st][t] = gload_u32x4(ac + aoff[t]);
+      xsr[st][t] = gload_u8(asc + asoff[t]);
+    }
+  };
+  auto compute = [&](int st) {
+#pragma unroll
+    for (int t = 0; t < NA; ++t)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r][t] = mx_mfma(wr[st][r], wsr[st][r], xr[st][t], xsr[st][t], acc[r][t]);
+  };
+
+#pragma unroll
+  for (int st = 0; st < D; ++st) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue(st, st);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  int c = 0;
+  for (; c + D <= KC; c += D) {
+#pragma unroll
+    for (int st = 0; st < D; ++st) {
+      compute(st);
+      // the refill stays after this stage's MFMAs, which read its registers
+      __builtin_amdgcn_sched_barrier(0);
+      issue(st, c + st + D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int st = 0; st < D; ++st)
+    if (c + st < KC) compute(st);
+}
+
+template <int MT, int NR, int NW, int D, int EPI>
+__global__ __launch_bounds__(NW * kWave) void mx_gemm_kernel(const GemmParams p) {
+  __shared__ MxSmem<MT> sm;
+  const int mb = blockIdx.x / p.n_tiles;
+  const int nt = blockIdx.x - mb * p.n_tiles;
+  const int expert = setup_rows<MT, NW, kRouteIndexed, EPI>(p, mb, sm);
+  if (expert < 0) return;
+  __syncthreads();
+  const uint32_t tmask = active_tiles<MT>(sm);
+  // token tiles run: the active prefix, rounded up to an even count for
+  // four- and eight-tile blocks (an extra tile of padding rows reads a valid
+  // row and is never stored)
+  auto go = [&](auto na) {
+    constexpr int NA = decltype(na)::value;
+    f32x4_t acc[NR][MT];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    mx_mainloop<MT, NR, NW, D, NA>(p, sm, expert, nt, acc);
+    epilogue<MT, NR, NW, EPI>(p, sm, nt, (1u << NA) - 1u, acc);
+  };
+  const int na = 32 - __clz(tmask);
+  if constexpr (MT == 1) {
+    go(std::integral_constant<int, 1>{});
+  } else if constexpr (MT == 2) {
+    if (na <= 1) go(std::integral_constant<int, 1>{});
+    else go(std::integral_constant<int, 2>{});
+  } else if constexpr (MT == 4) {
+    if (na <= 2) go(std::integral_constant<int, 2>{});
+    else go(std::integral_constant<int, 4>{});
+  } else {
+    static_assert(MT == 8, "token tiles per block: 1, 2, 4 or 8");
+    if (na <= 2) go(std::integral_constant<int, 2>{});
+    else if (na <= 4) go(std::integral_constant<int, 4>{});
+    else if (na <= 6) go(std::integral_constant<int, 6>{});
+    else go(std::integral_constant<int, 8>{});
+  }
+}
+
+typedef void (*MxKernel)(const GemmParams);
+
+template <int MT, int NR, int NW, int D>
+static MxKernel mx_pick(int epi) {
+  if (epi == kEpiStore) return mx_gemm_kernel<MT, NR, NW, D, kEpiStore>;
+  if (epi == kEpiWeighted) return mx_gemm_kernel<MT, NR, NW, D, kEpiWeighted>;
+  return nullptr;
+}
+
+// Built tile configurations (MT, NR, waves, stages): four waves; NR = 2 or 4
+// weight tiles per wave; four stages for the decode tiles (MT <= 2), two for
+// the larger blocks.
+static MxKernel find_mx_kernel(int epi, int m_tiles, int nr, int waves, int stages) {
+#define W4A16_MX_CASE(MT_, NR_, NW_, D_) \
+  if (m_tiles == MT_ && nr == NR_ && waves == NW_ && stages == D_) return mx_pick<MT_, NR_, NW_, D_>(epi);
+  W4A16_MX_CASE(1, 2, 4, 4) W4A16_MX_CASE(2, 2, 4, 4) W4A16_MX_CASE(4, 2, 4, 2) W4A16_MX_CASE(8, 2, 4, 2)
+  W4A16_MX_CASE(1, 4, 4, 4) W4A16_MX_CASE(2, 4, 4, 4) W4A16_MX_CASE(4, 4, 4, 2) W4A16_MX_CASE(8, 4, 4, 2)
+#undef W4A16_MX_CASE
+  return nullptr;
+}
+
+bool mx_gemm_config_supported(int epilogue, int m_tiles, int nr, int waves, int stages) {
+  return find_mx_kernel(epilogue, m_tiles, nr, waves, stages) != nullptr;
+}
+
+hipError_t launch_mx_gemm(int epilogue, int m_tiles, int nr, int waves, int stages, const GemmParams& p,
+                          hipStream_t stream) {
+  const MxKernel k = find_mx_kernel(epilogue, m_tiles, nr, waves, stages);
+  if (k == nullptr) return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)p.grid_blocks * p.n_tiles;
+  if (grid <= 0) return hipSuccess;
+  if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(waves * kWave), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace w4a16
