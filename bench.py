@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
 # Measured HBM traffic of the gate/up GEMM (rocprofv3 FETCH_SIZE / WRITE_SIZE
 # per dispatch, scaled by a copy of known size); valid only for the kernel
 # sources it was taken on, identified by their hash.
@@ -110,6 +111,44 @@ def cpu_baseline(sh, ids, wts, x, a, c1, s1, c2, s2, n_experts: int) -> dict:
                       f"({rows} routed rows), same inputs as the GPU step; GB/s of weight+scale bytes"}
 
 
+def mx_weight_bytes(n_touched: int, N: int, K: int) -> int:
+    """MXFP4 weights (K/2 bytes per row) + one E8M0 byte per 32 K."""
+    return n_touched * (N * K // 2 + N * (K // 32))
+
+
+def mx_workspace_bytes(M, packed, T: int, k: int) -> int:
+    """Workspace of the A4W4 down projection's top-k combine."""
+    import ctypes
+    return M.load().w4a16_mxfp4_moe_gemm_workspace_bytes(ctypes.byref(packed.desc), T, k, 1)
+
+
+def cpu_baseline_mx(sh, ids, wts, x, a, w1, s1, w2, s2, n_experts: int) -> dict:
+    """The MXFP4 oracle as it stands (quantise the step's activation rows,
+    dequantise, float64 matmul, combine) on the first `n_experts` local
+    experts and all rows routed to them."""
+    from oracle import mx_oracle as X
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    S = n_experts
+    t0 = time.perf_counter()
+    xq = X.mx_quantize(x)
+    aq = X.mx_quantize(a)
+    X.mx_indexed_gate_up(*xq, X.unpack_nibbles(w1[:S]), s1[:S], ids, sh.first, S)
+    X.mx_indexed_down_combine(*aq, X.unpack_nibbles(w2[:S]), s2[:S], ids, wts, sh.first, S)
+    dt = time.perf_counter() - t0
+    flat = ids.reshape(-1)
+    rows = int(((flat >= sh.first) & (flat < sh.first + S)).sum())
+    b = mx_weight_bytes(S, sh.N1, sh.K1) + mx_weight_bytes(S, sh.N2, sh.K2)
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"A4W4: quantise all activation rows, gate/up + down+combine for local experts "
+                      f"0..{S - 1} of {sh.E_loc} ({rows} routed rows), same inputs as the GPU step; "
+                      f"GB/s of MXFP4 weight+scale bytes"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +168,9 @@ def main() -> int:
     ap.add_argument("--fused", action="store_true",
                     help="chained layer: gate/up with the SiLU activation fused, written in sorted order, "
                          "read as is by the down projection (instead of a synthetic per-slot down input)")
+    ap.add_argument("--mx", action="store_true",
+                    help="A4W4 variant: MXFP4 weights, activations quantised to MXFP4 on the device "
+                         "inside the step (quantise x, gate/up, quantise the down input, down+combine)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB three times (reference for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -150,17 +192,30 @@ def main() -> int:
     ids, wts = W.routing_for(sh)
     x = W.activations(sh.seed, "x", sh.T, sh.K1)
     a = W.activations(sh.seed, "a", sh.T * sh.topk, sh.K2)
-    c1 = W.weight_codes(sh.seed, "w1_codes", sh.E_loc, sh.N1, sh.K1)
-    s1 = W.weight_scales(sh.seed, "w1_scales", sh.E_loc, sh.N1, sh.K1)
-    c2 = W.weight_codes(sh.seed, "w2_codes", sh.E_loc, sh.N2, sh.K2)
-    s2 = W.weight_scales(sh.seed, "w2_scales", sh.E_loc, sh.N2, sh.K2)
+    if args.mx and args.fused:
+        log("--mx and --fused are separate variants")
+        return 2
+    if args.mx:
+        c1 = W.mx_weight_codes(sh.seed, "w1_mx_codes", sh.E_loc, sh.N1, sh.K1)
+        s1 = W.mx_weight_scales(sh.seed, "w1_mx_scales", sh.E_loc, sh.N1, sh.K1)
+        c2 = W.mx_weight_codes(sh.seed, "w2_mx_codes", sh.E_loc, sh.N2, sh.K2)
+        s2 = W.mx_weight_scales(sh.seed, "w2_mx_scales", sh.E_loc, sh.N2, sh.K2)
+    else:
+        c1 = W.weight_codes(sh.seed, "w1_codes", sh.E_loc, sh.N1, sh.K1)
+        s1 = W.weight_scales(sh.seed, "w1_scales", sh.E_loc, sh.N1, sh.K1)
+        c2 = W.weight_codes(sh.seed, "w2_codes", sh.E_loc, sh.N2, sh.K2)
+        s2 = W.weight_scales(sh.seed, "w2_scales", sh.E_loc, sh.N2, sh.K2)
     log(f"inputs generated in {time.perf_counter() - t_gen:.1f}s")
 
     def bf(b):
         return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    p1 = M.pack_w4(torch.from_numpy(c1).to(dev), bf(s1), gate_up=args.fused)
-    p2 = M.pack_w4(torch.from_numpy(c2).to(dev), bf(s2))
+    if args.mx:
+        p1 = M.pack_mxfp4(torch.from_numpy(c1).to(dev), torch.from_numpy(s1).to(dev))
+        p2 = M.pack_mxfp4(torch.from_numpy(c2).to(dev), torch.from_numpy(s2).to(dev))
+    else:
+        p1 = M.pack_w4(torch.from_numpy(c1).to(dev), bf(s1), gate_up=args.fused)
+        p2 = M.pack_w4(torch.from_numpy(c2).to(dev), bf(s2))
     d_ids = torch.from_numpy(ids).to(dev)
     d_w = torch.from_numpy(wts).to(dev)
     d_x, d_a = bf(x), bf(a)
@@ -183,8 +238,19 @@ def main() -> int:
     routing = M.Routing(sorted_ids, expert_ids, ntp, cfg.block_m, d_ids, sh.E_glob, sh.first, sh.E_loc)
     h = torch.empty(T * k, sh.N1, dtype=torch.bfloat16, device=dev)
     y = torch.empty(T, sh.N2, dtype=torch.bfloat16, device=dev)
-    ws1 = torch.empty(max(16, M.workspace_bytes(p1, T, k, False, cfg)), dtype=torch.uint8, device=dev)
-    ws2 = torch.empty(max(16, M.workspace_bytes(p2, T, k, True, cfg)), dtype=torch.uint8, device=dev)
+    if args.mx:
+        # the A4W4 kernels: four weight tiles per wave, four stages for the
+        # decode blocks (overrides apply as for the W4A16 kernels)
+        cfg = M.mxfp4_config(cfg.block_m, args.nr or 4, args.stages or None)
+        ws1 = torch.empty(16, dtype=torch.uint8, device=dev)
+        ws2 = torch.empty(max(16, int(mx_workspace_bytes(M, p2, T, k))), dtype=torch.uint8, device=dev)
+        qx = M.MXRows(torch.empty(T, sh.K1 // 2, dtype=torch.uint8, device=dev),
+                      torch.empty(T, sh.K1 // 32, dtype=torch.uint8, device=dev))
+        qa = M.MXRows(torch.empty(T * k, sh.K2 // 2, dtype=torch.uint8, device=dev),
+                      torch.empty(T * k, sh.K2 // 32, dtype=torch.uint8, device=dev))
+    else:
+        ws1 = torch.empty(max(16, M.workspace_bytes(p1, T, k, False, cfg)), dtype=torch.uint8, device=dev)
+        ws2 = torch.empty(max(16, M.workspace_bytes(p2, T, k, True, cfg)), dtype=torch.uint8, device=dev)
     L = M.load()
     stream = torch.cuda.current_stream(dev)
     import ctypes
@@ -202,21 +268,35 @@ def main() -> int:
         return 2
 
     def gate_up():
-        if args.fused:
+        if args.mx:
+            M.moe_mxfp4_gemm(qx, p1, routing, cfg=cfg, out=h)
+        elif args.fused:
             M.moe_gate_up_silu(d_x, p1, routing, cfg=cfg, out=inter)
         else:
             M.moe_w4a16_gemm(d_x, p1, routing, cfg=cfg, out=h, workspace=ws1)
 
     def down():
-        if args.fused:
+        if args.mx:
+            M.moe_mxfp4_gemm(qa, p2, routing, topk_weights=d_w, cfg=cfg, out=y, workspace=ws2)
+        elif args.fused:
             M.moe_w4a16_gemm(inter, p2, routing, topk_weights=d_w, a_layout="sorted", cfg=cfg, out=y,
                              workspace=ws2)
         else:
             M.moe_w4a16_gemm(d_a, p2, routing, topk_weights=d_w, cfg=cfg, out=y, workspace=ws2)
 
+    def quant():
+        # A4W4: both projections' activation rows to MXFP4 (the down input
+        # is the step's synthetic per-slot rows, quantised like x)
+        M.mxfp4_quant(d_x, out=qx)
+        M.mxfp4_quant(d_a, out=qa)
+
     def step():
         align()
+        if args.mx:
+            M.mxfp4_quant(d_x, out=qx)
         gate_up()
+        if args.mx:
+            M.mxfp4_quant(d_a, out=qa)
         down()
 
     def graph_of(fn, n):
@@ -270,6 +350,7 @@ def main() -> int:
     st_align = timed(graph_of(align, inner), max(4, args.steps // 2), inner)
     st_gu = timed(graph_of(gate_up, inner), max(4, args.steps // 2), inner)
     st_dn = timed(graph_of(down, inner), max(4, args.steps // 2), inner)
+    st_q = timed(graph_of(quant, inner), max(4, args.steps // 2), inner) if args.mx else None
     us_align, us_gu, us_dn = st_align[0], st_gu[0], st_dn[0]
 
     # host cost of choosing a config (first call runs the sampled search,
@@ -293,21 +374,26 @@ def main() -> int:
     n_local = int(local.sum())
     touched = int(len(np.unique(flat[local])))
     tokens_with_local = int(local.reshape(T, k).any(1).sum())
-    wb1 = weight_bytes(touched, sh.N1, sh.K1)
-    wb2 = weight_bytes(touched, sh.N2, sh.K2)
+    wbytes = mx_weight_bytes if args.mx else weight_bytes
+    wb1 = wbytes(touched, sh.N1, sh.K1)
+    wb2 = wbytes(touched, sh.N2, sh.K2)
     n_ntp = int(ntp.item())
     # algorithmic bytes per gate/up launch: weights+scales of touched experts,
     # one activation row read and one output row written per routed slot,
     # the routing indices
     out1 = n_local * (sh.N1 // 2 if args.fused else sh.N1) * 2   # fused: the activation, half the columns
-    alg1 = wb1 + n_local * sh.K1 * 2 + out1 + n_ntp * 4 + (n_ntp // cfg.block_m) * 4
+    row1 = sh.K1 // 2 + sh.K1 // 32 if args.mx else sh.K1 * 2     # MXFP4 row: codes + scales
+    alg1 = wb1 + n_local * row1 + out1 + n_ntp * 4 + (n_ntp // cfg.block_m) * 4
     value = (wb1 + wb2) / (ms_step * 1e-3) / 1e9
     cfg_tag = f"bm{cfg.block_m} nr{cfg.nr} waves{cfg.waves} split_k{cfg.split_k} stages{cfg.stages}"
     gu_gbs = alg1 / (us_gu * 1e-6) / 1e9
     flops1 = 2.0 * n_local * sh.N1 * sh.K1
     flops2 = 2.0 * n_local * sh.N2 * sh.K2
+    kname = "mx_gemm_kernel (A4W4 gate/up)" if args.mx else "moe_gemm_kernel (gate/up)"
     out = {
-        "metric": "weight-HBM GB/s of one MoE layer step (align + gate/up + down+combine), "
+        "metric": ("weight-HBM GB/s of one A4W4 MoE layer step (align + MXFP4 quantisation + gate/up + "
+                   "down+combine), with us/call per MXFP4 GEMM") if args.mx else
+                  "weight-HBM GB/s of one MoE layer step (align + gate/up + down+combine), "
                   "with us/call per W4A16 GEMM",
         "value": round(value, 2),
         "unit": "GB/s",
@@ -319,9 +405,10 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp4" if args.mx else "bf16",
         "data": "synthetic",
-        "config": {"workload": sh.name, "fused_silu": bool(args.fused), "T": T, "topk": k, "E_glob": sh.E_glob, "E_loc": sh.E_loc,
+        "config": {"workload": sh.name, "variant": "a4w4-mxfp4" if args.mx else "w4a16",
+                   "fused_silu": bool(args.fused), "T": T, "topk": k, "E_glob": sh.E_glob, "E_loc": sh.E_loc,
                    "K1": sh.K1, "N1": sh.N1, "K2": sh.K2, "N2": sh.N2, "block_m": cfg.block_m,
                    "nr": cfg.nr, "waves": cfg.waves, "split_k": cfg.split_k, "stages": cfg.stages, "routed_rows": n_local,
                    "experts_touched": touched, "num_tokens_padded": n_ntp},
@@ -337,15 +424,21 @@ def main() -> int:
             "gate_up_TFLOPs": round(flops1 / (us_gu * 1e-6) / 1e12, 2),
             "down_TFLOPs": round(flops2 / (us_dn * 1e-6) / 1e12, 2),
         },
-        "roofline": {"kernel": "moe_gemm_kernel (gate/up)", "bound": "hbm",
+        "roofline": {"kernel": kname, "bound": "hbm",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(sh.name, cfg_tag),
+                     "traffic": None if args.mx else measured_traffic(sh.name, cfg_tag),
                      "algorithmic_bytes": int(alg1)},
     }
+    if st_q is not None:
+        out["per_call_stats_us"]["mxfp4_quant_x_and_a"] = {"median": round(st_q[1], 2), "min": round(st_q[2], 2),
+                                                          "p90": round(st_q[3], 2)}
+        out["per_call_us"]["mxfp4_quant_x_and_a"] = round(st_q[0], 2)
+        out["gemm_rates"]["gate_up_fp4_frac"] = round(flops1 / (us_gu * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4)
     if args.cpu_experts > 0:
         log("timing the CPU oracle baseline ...")
-        out["cpu_baseline"] = cpu_baseline(sh, ids, wts, x, a, c1, s1, c2, s2, args.cpu_experts)
+        base = cpu_baseline_mx if args.mx else cpu_baseline
+        out["cpu_baseline"] = base(sh, ids, wts, x, a, c1, s1, c2, s2, args.cpu_experts)
     print(json.dumps(out), flush=True)
     return 0
 
