@@ -32,7 +32,8 @@ FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
 # per dispatch, scaled by a copy of known size); valid only for the kernel
 # sources it was taken on, identified by their hash.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "moe_gemm_ep8_decode_traffic.md")
-KERNEL_SOURCES = ["w4a16_int4_mixture_moe_amd/csrc/gemm.hip", "w4a16_int4_mixture_moe_amd/csrc/device_common.hpp",
+KERNEL_SOURCES = ["w4a16_int4_mixture_moe_amd/csrc/gemm.hip", "w4a16_int4_mixture_moe_amd/csrc/tile_common.hpp",
+                  "w4a16_int4_mixture_moe_amd/csrc/device_common.hpp",
                   "w4a16_int4_mixture_moe_amd/csrc/launch.hpp", "w4a16_int4_mixture_moe_amd/build.py"]
 
 
