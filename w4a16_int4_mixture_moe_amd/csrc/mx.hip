@@ -140,6 +140,16 @@ struct MxSmem {
   float w[16 * MT];
 };
 
+// Blocks of four or eight token tiles stage each chunk's activation
+// fragments once per workgroup in LDS (double buffered), laid out as the
+// lanes read them: frag[buf][t][lane] is lane `lane`'s 16-byte operand of
+// token tile t and sc[buf][t][lane] its scale byte.
+template <int MT>
+struct MxStagedSmem : MxSmem<MT> {
+  u32x4_t frag[2][MT][kWave];
+  uint32_t sc[2][MT][kWave];
+};
+
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 // 128 K of one weight tile (A) against 128 K of one token tile (B); only the
@@ -240,9 +250,129 @@ __device__ __forceinline__ void mx_mainloop(const GemmParams& p, const MxSmem<MT
     if (c + st < KC) compute(st);
 }
 
+// The same product for blocks of four or eight token tiles: every wave of
+// the workgroup multiplies the same activation fragments, so loading them
+// per wave (as above) reads each one NW times through the L1; here the
+// workgroup loads each fragment once per chunk into LDS (thread i takes
+// fragments i, i + NW * 64, ...), and the waves read it from there.  Chunk c:
+// request the fragments of chunk c + 1, multiply chunk c from LDS buffer
+// c & 1 with weight stage c mod D, refill that stage with chunk c + D, store
+// chunk c + 1 into the other buffer, barrier.
+template <int MT, int NR, int NW, int D, int NA>
+__device__ __forceinline__ void mx_mainloop_staged(const GemmParams& p, MxStagedSmem<MT>& sm, int expert, int nt,
+                                                   f32x4_t (&acc)[NR][MT]) {
+  static_assert(NA >= 1 && NA <= MT, "active token tiles");
+  constexpr int NTHR = NW * kWave;
+  constexpr int FPT = (NA * kWave + NTHR - 1) / NTHR;     // fragments per thread
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int KC = p.KC;
+
+  const gptr_t abase = uniform_ptr(p.a);
+  const gptr_t asbase = uniform_ptr(p.a_scale);
+  const uint32_t kb = (uint32_t)p.K / 2, ks = (uint32_t)p.K / 32;
+  const int fallback_row = sm.row[0];
+  // fragment f = tid + i * NTHR: token tile f / 64, lane f % 64 of that tile;
+  // wave-uniform whether it exists (NTHR is a multiple of 64)
+  uint32_t goff[FPT], gsoff[FPT];
+#pragma unroll
+  for (int i = 0; i < FPT; ++i) {
+    const int f = min(tid + i * NTHR, NA * kWave - 1);
+    const int t = f / kWave, l = f % kWave;
+    const int r = sm.row[16 * t + (l & 15)];
+    const uint32_t row = (uint32_t)(r >= 0 ? r : fallback_row);
+    goff[i] = row * kb + 16u * (uint32_t)(l >> 4);
+    gsoff[i] = row * ks + (uint32_t)(l >> 4);
+  }
+  auto frag_on = [&](int i) { return i * NTHR + wave * kWave < NA * kWave; };
+
+  const int rt_base = nt * (NW * NR) + wave * NR;
+  gptr_t wbase[NR], sbase[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int rt = min(rt_base + r, p.NT - 1);
+    const int64_t tile = (int64_t)expert * p.NT + rt;
+    wbase[r] = uniform_ptr(p.packed_w + tile * KC * kWave);
+    sbase[r] = uniform_ptr(reinterpret_cast<const uint8_t*>(p.packed_s) + tile * KC * kWave);
+  }
+  const uint32_t woff = (uint32_t)lane * 16u;
+
+  u32x4_t wr[D][NR];
+  uint32_t wsr[D][NR];
+  u32x4_t xr[FPT];
+  uint32_t xsr[FPT];
+  auto issue_w = [&](int st, int c) {
+    c = min(c, KC - 1);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      wr[st][r] = gload_u32x4((wbase[r] + (int64_t)c * (kWave * 16)) + woff);
+      wsr[st][r] = gload_u8((sbase[r] + (int64_t)c * kWave) + (uint32_t)lane);
+    }
+  };
+  auto issue_x = [&](int c) {
+    c = min(c, KC - 1);
+    const gptr_t ac = abase + (int64_t)c * 64, asc = asbase + (int64_t)c * 4;
+#pragma unroll
+    for (int i = 0; i < FPT; ++i)
+      if (frag_on(i)) {
+        xr[i] = gload_u32x4(ac + goff[i]);
+        xsr[i] = gload_u8(asc + gsoff[i]);
+      }
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < FPT; ++i)
+      if (frag_on(i)) {
+        const int f = tid + i * NTHR;
+        sm.frag[buf][f / kWave][f % kWave] = xr[i];
+        sm.sc[buf][f / kWave][f % kWave] = xsr[i];
+      }
+  };
+  auto compute = [&](int buf, int st) {
+#pragma unroll
+    for (int t = 0; t < NA; ++t) {
+      const u32x4_t B = sm.frag[buf][t][lane];
+      const uint32_t bs = sm.sc[buf][t][lane];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r][t] = mx_mfma(wr[st][r], wsr[st][r], B, bs, acc[r][t]);
+    }
+  };
+
+  issue_x(0);
+#pragma unroll
+  for (int st = 0; st < D; ++st) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(st, st);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  store_x(0);
+  __syncthreads();
+  auto chunk = [&](int c, int st) {
+    const int buf = c & 1;
+    issue_x(c + 1);                          // clamped: the last chunk re-reads itself, never stored
+    __builtin_amdgcn_sched_barrier(0);
+    compute(buf, st);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(st, c + D);
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 < KC) store_x(buf ^ 1);
+    __syncthreads();
+  };
+  int c = 0;
+  for (; c + D <= KC; c += D) {
+#pragma unroll
+    for (int st = 0; st < D; ++st) chunk(c + st, st);
+  }
+#pragma unroll
+  for (int st = 0; st < D; ++st)
+    if (c + st < KC) chunk(c + st, st);
+}
+
 template <int MT, int NR, int NW, int D, int EPI>
 __global__ __launch_bounds__(NW * kWave) void mx_gemm_kernel(const GemmParams p) {
-  __shared__ MxSmem<MT> sm;
+  constexpr bool STAGED = MT >= 4;
+  __shared__ std::conditional_t<STAGED, MxStagedSmem<MT>, MxSmem<MT>> sm;
   const int mb = blockIdx.x / p.n_tiles;
   const int nt = blockIdx.x - mb * p.n_tiles;
   const int expert = setup_rows<MT, NW, kRouteIndexed, EPI>(p, mb, sm);
@@ -259,7 +389,10 @@ __global__ __launch_bounds__(NW * kWave) void mx_gemm_kernel(const GemmParams p)
     for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    mx_mainloop<MT, NR, NW, D, NA>(p, sm, expert, nt, acc);
+    if constexpr (STAGED)
+      mx_mainloop_staged<MT, NR, NW, D, NA>(p, sm, expert, nt, acc);
+    else
+      mx_mainloop<MT, NR, NW, D, NA>(p, sm, expert, nt, acc);
     epilogue<MT, NR, NW, EPI>(p, sm, nt, (1u << NA) - 1u, acc);
   };
   const int na = 32 - __clz(tmask);
