@@ -25,7 +25,8 @@
 // Activation quantisation (mx_quant_kernel) is the OCP conversion: shared
 // exponent floor(log2 max|v|) - 2 clamped to E8M0's range (a zero block takes
 // code 0), elements rounded to the nearest E2M1 value, ties to even, clamped
-// at 6, sign from the input's sign bit.
+// at 6, sign from the input's sign bit (gfx950's FP4 conversion instruction
+// does the rounding).
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -35,15 +36,6 @@
 namespace w4a16 {
 
 // ------------------------------------------------------------ quantisation
-
-// |y| -> E2M1 magnitude code: the number of rounding thresholds |y| has
-// passed.  Between two neighbours the tie goes to the even code (mantissa 0):
-// the threshold is strict (>) where the upper neighbour is odd and inclusive
-// (>=) where it is even; past 5 everything rounds to 6 (code 7).
-__device__ __forceinline__ uint32_t e2m1_mag(float a) {
-  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
-         (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
-}
 
 // One thread per 32-element block: 64 bytes of bf16 in, 16 bytes of codes
 // and one scale byte out.
@@ -74,13 +66,27 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
   const int field = (int)(amax >> 7);
   const uint32_t code = (uint32_t)max(field - 2, 0);
   const float inv = __builtin_bit_cast(float, (254u - code) << 23);    // 2^(127 - code), exact
-  uint32_t out[4] = {0u, 0u, 0u, 0u};
+  // y = v * 2^(127 - code) is exact (denormals are kept), and gfx950's
+  // v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds a pair of floats to E2M1
+  // exactly as the conversion asks: nearest, ties to the even code, clamped
+  // at 6, sign kept for results that round to zero (checked on the device
+  // against a CPU reference at every tie, past the clamp and at -0); the
+  // byte selector packs four pairs into one word, element 2i in the low
+  // nibble of byte i.
+  uint32_t out[4];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    const uint32_t h = (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xFFFFu);
-    const float y = __builtin_bit_cast(float, h << 16) * inv;          // exact (denormals kept)
-    const uint32_t c = e2m1_mag(__builtin_fabsf(y)) | ((h >> 12) & 8u);
-    out[e >> 3] |= c << (4 * (e & 7));
+  for (int w = 0; w < 4; ++w) {
+    uint32_t word = 0u;
+#define W4A16_PAIR(b)                                                                              \
+    {                                                                                              \
+      const uint32_t pv = v[4 * w + (b)];                                                          \
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, __builtin_bit_cast(float, pv << 16) * inv, \
+                                                      __builtin_bit_cast(float, pv & 0xFFFF0000u) * inv, \
+                                                      1.0f, (b));                                  \
+    }
+    W4A16_PAIR(0) W4A16_PAIR(1) W4A16_PAIR(2) W4A16_PAIR(3)
+#undef W4A16_PAIR
+    out[w] = word;
   }
   *reinterpret_cast<uint4*>(codes + i * 16) = make_uint4(out[0], out[1], out[2], out[3]);
   scales[i] = (uint8_t)code;
