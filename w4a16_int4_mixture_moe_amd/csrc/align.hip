@@ -8,7 +8,7 @@
 // to the host and the call stays graph-capturable; section "Grouped SM90
 // kernels", Figure 3: indexed routing puts its padding in sentinel indices.
 //
-// One workgroup of 16 waves.  Wave w owns a contiguous range of slots, so the
+// One workgroup of 16 or 8 waves.  Wave w owns a contiguous range of slots, so the
 // order of slots inside an expert segment is ascending by construction:
 //   pass 1  each wave counts its slots per expert (LDS atomics), 16 loads in
 //           flight per lane (one workgroup has to keep many requests out to
@@ -18,9 +18,10 @@
 //   fill    sentinels inside segment tails and after the padded total,
 //           expert_ids per block, the padded total itself;
 //   pass 2  each wave walks its range 64 slots at a time; lanes routed to the
-//           same expert find each other with one ballot per expert-id bit,
-//           take consecutive positions in lane order, and the group's lowest
-//           lane advances the wave's cursor for that expert.
+//           same expert find each other (a per-wave table of lane masks in
+//           LDS, or one ballot per expert-id bit), take consecutive
+//           positions in lane order, and the group's lowest lane advances
+//           the wave's cursor for that expert.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -28,24 +29,33 @@ namespace w4a16 {
 
 constexpr int kAlignBatch = 16;                // slot ids in flight per lane
 
-// kAlignWaves waves: 16, or 8 when the per-wave counters of many experts
-// would not fit the default LDS allocation
-template <int kAlignWaves>
+// kAlignWaves waves: 16, or 8 when the per-wave tables of many experts would
+// not fit the default LDS allocation.  kMaskMatch: pass 2 finds the lanes of
+// a sub-tile routed to the same expert through a per-wave table of 64-bit
+// lane masks in LDS (one atomic OR per lane, one read back); otherwise with
+// one ballot per expert-id bit (no table; for more than 512 local experts).
+template <int kAlignWaves, bool kMaskMatch>
 __global__ __launch_bounds__(kAlignWaves * kWave) void align_kernel(
     const int32_t* __restrict__ topk_ids, int32_t total, int32_t first, int32_t E_loc,
     int32_t bm, int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
     int32_t* __restrict__ ntp_out, int64_t capacity) {
   constexpr int kAlignThreads = kAlignWaves * kWave;
-  extern __shared__ int smem[];
-  int* cnt = smem;                            // [kAlignWaves][E_loc]: counts, then cursors
-  int* seg = smem + kAlignWaves * E_loc;      // [E_loc + 1]: padded segment starts
+  extern __shared__ unsigned long long smem64[];
+  // [kAlignWaves][E_loc] lane masks (kMaskMatch only), 8-byte aligned first
+  unsigned long long* lanes_of = smem64;
+  int* cnt = reinterpret_cast<int*>(smem64 + (kMaskMatch ? kAlignWaves * E_loc : 0));
+                                              // [kAlignWaves][E_loc]: counts, then cursors
+  int* seg = cnt + kAlignWaves * E_loc;       // [E_loc + 1]: padded segment starts
   int* num = seg + E_loc + 1;                 // [E_loc]: slots per expert
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = tid / kWave;
 
-  for (int i = tid; i < kAlignWaves * E_loc; i += kAlignThreads) cnt[i] = 0;
+  for (int i = tid; i < kAlignWaves * E_loc; i += kAlignThreads) {
+    cnt[i] = 0;
+    if constexpr (kMaskMatch) lanes_of[i] = 0ull;
+  }
   __syncthreads();
 
   const int per = ((total + kAlignWaves - 1) / kAlignWaves + kWave - 1) & ~(kWave - 1);
@@ -133,20 +143,33 @@ __global__ __launch_bounds__(kAlignWaves * kWave) void align_kernel(
       const int s = base + lane;
       const int e = id8[u] - first;
       const bool loc = (s < end) && id8[u] >= 0 && ((unsigned)e < (unsigned)E_loc);
-      uint64_t peers = __ballot(loc);
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = loc && ((e >> b) & 1);
-        const uint64_t m = __ballot(bit);
-        peers &= bit ? m : ~m;
+      uint64_t peers;
+      if constexpr (kMaskMatch) {
+        // every lane ORs its bit into its expert's mask; the wave's LDS
+        // operations complete in order, so the read-back sees all of them
+        if (loc) atomicOr(&lanes_of[w * E_loc + e], 1ull << lane);
+        __builtin_amdgcn_wave_barrier();
+        peers = loc ? lanes_of[w * E_loc + e] : 0ull;
+      } else {
+        peers = __ballot(loc);
+        for (int b = 0; b < nbits; ++b) {
+          const bool bit = loc && ((e >> b) & 1);
+          const uint64_t m = __ballot(bit);
+          peers &= bit ? m : ~m;
+        }
       }
       int cur = 0;
       if (loc) {
         cur = cnt[w * E_loc + e];
         sorted_ids[cur + __popcll(peers & lanes_below)] = s;
       }
-      // every lane has read its cursor before any lane of this wave updates it
+      // every lane has read its cursor (and mask) before any lane of this
+      // wave updates them
       __builtin_amdgcn_wave_barrier();
-      if (loc && (peers & lanes_below) == 0) cnt[w * E_loc + e] = cur + __popcll(peers);
+      if (loc && (peers & lanes_below) == 0) {
+        cnt[w * E_loc + e] = cur + __popcll(peers);
+        if constexpr (kMaskMatch) lanes_of[w * E_loc + e] = 0ull;
+      }
       __builtin_amdgcn_wave_barrier();
     }
   }
@@ -155,14 +178,21 @@ __global__ __launch_bounds__(kAlignWaves * kWave) void align_kernel(
 hipError_t launch_align(const int32_t* topk_ids, int32_t total_slots, int32_t first, int32_t E_loc,
                         int32_t block_m, int32_t* sorted_ids, int32_t* expert_ids,
                         int32_t* num_tokens_padded, int64_t capacity, hipStream_t stream) {
-  const int waves = E_loc <= 512 ? 16 : 8;                  // LDS <= 37 KB (16) / 41 KB (8)
-  const size_t lds = sizeof(int) * ((size_t)waves * E_loc + 2 * (size_t)E_loc + 1);
-  if (waves == 16)
-    hipLaunchKernelGGL(align_kernel<16>, dim3(1), dim3(16 * kWave), lds, stream, topk_ids, total_slots, first,
-                       E_loc, block_m, sorted_ids, expert_ids, num_tokens_padded, capacity);
+  // LDS: lane masks 8 B and counters 4 B per (wave, expert), plus 8 B per
+  // expert: <= 27 KB (16 waves, <= 128 experts), <= 53 KB (8 waves, <= 512),
+  // <= 41 KB (8 waves, ballot matching, <= 1024)
+  auto lds = [&](int waves, bool masks) {
+    return (masks ? 8 * (size_t)waves * E_loc : 0) + sizeof(int) * ((size_t)waves * E_loc + 2 * (size_t)E_loc + 1);
+  };
+  if (E_loc <= 128)
+    hipLaunchKernelGGL((align_kernel<16, true>), dim3(1), dim3(16 * kWave), lds(16, true), stream, topk_ids,
+                       total_slots, first, E_loc, block_m, sorted_ids, expert_ids, num_tokens_padded, capacity);
+  else if (E_loc <= 512)
+    hipLaunchKernelGGL((align_kernel<8, true>), dim3(1), dim3(8 * kWave), lds(8, true), stream, topk_ids,
+                       total_slots, first, E_loc, block_m, sorted_ids, expert_ids, num_tokens_padded, capacity);
   else
-    hipLaunchKernelGGL(align_kernel<8>, dim3(1), dim3(8 * kWave), lds, stream, topk_ids, total_slots, first,
-                       E_loc, block_m, sorted_ids, expert_ids, num_tokens_padded, capacity);
+    hipLaunchKernelGGL((align_kernel<8, false>), dim3(1), dim3(8 * kWave), lds(8, false), stream, topk_ids,
+                       total_slots, first, E_loc, block_m, sorted_ids, expert_ids, num_tokens_padded, capacity);
   return hipGetLastError();
 }
 
