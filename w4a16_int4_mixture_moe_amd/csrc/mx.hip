@@ -291,7 +291,10 @@ __device__ __forceinline__ void mx_mainloop_staged(const GemmParams& p, MxStaged
     goff[i] = row * kb + 16u * (uint32_t)(l >> 4);
     gsoff[i] = row * ks + (uint32_t)(l >> 4);
   }
-  auto frag_on = [&](int i) { return i * NTHR + wave * kWave < NA * kWave; };
+  // every thread has all its fragments when NA * 64 is a multiple of the
+  // workgroup size (known at compile time: no branch around the loads)
+  constexpr bool ALL_ON = (NA * kWave) % NTHR == 0;
+  auto frag_on = [&](int i) { return ALL_ON || i * NTHR + wave * kWave < NA * kWave; };
 
   const int rt_base = nt * (NW * NR) + wave * NR;
   gptr_t wbase[NR], sbase[NR];
@@ -354,25 +357,31 @@ __device__ __forceinline__ void mx_mainloop_staged(const GemmParams& p, MxStaged
   __builtin_amdgcn_sched_barrier(0);
   store_x(0);
   __syncthreads();
-  auto chunk = [&](int c, int st) {
+  // STEADY: chunk c + 1 exists, so the store is unconditional and the loop
+  // body is one basic block (a branch there lets the compiler sink the
+  // MFMAs past the stores and the barrier into the next block)
+  auto chunk = [&](auto steady_, int c, int st) {
+    constexpr bool STEADY = decltype(steady_)::value;
     const int buf = c & 1;
-    issue_x(c + 1);                          // clamped: the last chunk re-reads itself, never stored
+    issue_x(c + 1);                          // clamped: past the end it re-reads the last chunk, never stored
     __builtin_amdgcn_sched_barrier(0);
     compute(buf, st);
     __builtin_amdgcn_sched_barrier(0);
     issue_w(st, c + D);
     __builtin_amdgcn_sched_barrier(0);
-    if (c + 1 < KC) store_x(buf ^ 1);
+    if (STEADY || c + 1 < KC) store_x(buf ^ 1);
     __syncthreads();
   };
+  using Steady = std::integral_constant<bool, true>;
+  using Tail = std::integral_constant<bool, false>;
   int c = 0;
-  for (; c + D <= KC; c += D) {
+  for (; c + D < KC; c += D) {
 #pragma unroll
-    for (int st = 0; st < D; ++st) chunk(c + st, st);
+    for (int st = 0; st < D; ++st) chunk(Steady{}, c + st, st);
   }
 #pragma unroll
   for (int st = 0; st < D; ++st)
-    if (c + st < KC) chunk(c + st, st);
+    if (c + st < KC) chunk(Tail{}, c + st, st);
 }
 
 template <int MT, int NR, int NW, int D, int EPI>
