@@ -74,20 +74,18 @@ constexpr bool kPipelinedDequant = W4A16_PIPELINED_DEQUANT != 0;
 
 // acc += this wave's weight tiles x the block's rows over K chunks [c0, c1).
 // Starts and ends with the workgroup synchronised.  The active token tiles
-// are always a prefix (valid rows come first in every layout).  NA > 0:
-// exactly tiles [0, NA) are active, fixed at compile time, so the loop loads,
-// reads and multiplies only those, without per-tile branches.  NA = 0: any
-// prefix, tested against tmask inside the loop.
+// are always a prefix (valid rows come first in every layout); the loop
+// processes exactly tiles [0, NA), NA fixed at compile time, so it loads,
+// reads and multiplies only those, without per-tile branches.
 template <int MT, int NR, int NW, int D, int NA>
 __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, int expert, int nt,
-                                         uint32_t tmask, int c0, int c1, f32x4_t (&acc)[NR][MT]) {
+                                         int c0, int c1, f32x4_t (&acc)[NR][MT]) {
   constexpr int NTHR = NW * kWave;
   constexpr int ROWS_PER_PASS = NTHR / 16;          // staged rows covered by one piece index
   static_assert(ROWS_PER_PASS == 16 || ROWS_PER_PASS == 32, "four or eight waves");
   constexpr int PPT = (16 * MT + ROWS_PER_PASS - 1) / ROWS_PER_PASS;   // pieces per thread
-  static_assert(NA >= 0 && NA <= MT, "active tile count");
-  constexpr bool FIXED = NA > 0;
-  auto active = [&](int t) { return FIXED ? t < NA : ((tmask >> t) & 1u) != 0; };
+  static_assert(NA >= 1 && NA <= MT, "active tile count");
+  auto active = [&](int t) { return t < NA; };
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -108,9 +106,7 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
   auto piece_row = [&](int i) { return (tid >> 4) + i * ROWS_PER_PASS; };
   // wave-uniform: the tile of piece i, and whether the piece is loaded
   auto piece_tile = [&](int i) { return ROWS_PER_PASS == 16 ? i : 2 * i + (wave >> 2); };
-  auto piece_on = [&](int i) {
-    return FIXED ? piece_tile(i) < NA : piece_tile(i) < MT;
-  };
+  auto piece_on = [&](int i) { return piece_tile(i) < NA; };
   uint32_t xoff[PPT];
 #pragma unroll
   for (int i = 0; i < PPT; ++i) {
@@ -141,9 +137,6 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
   auto issue_x = [&](int c, u32x4_t (&xr)[PPT], bool tail) {
     const gptr_t base = xbase + (int64_t)c * (kChunk * 2);
     const bool kin = !tail || c * kChunk + xcol < K;
-    // with NA = 0, unconditional even for inactive token tiles (their pieces
-    // read the block's first row): the same number of loads on every path
-    // lets the compiler wait for exactly the loads it needs, not all of them
 #pragma unroll
     for (int i = 0; i < PPT; ++i)
       if (piece_on(i)) xr[i] = gload_u32x4(kin ? base + xoff[i] : xbase + xoff[i]);
@@ -152,7 +145,7 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
     const bool kin = !tail || c * kChunk + xcol < K;
 #pragma unroll
     for (int i = 0; i < PPT; ++i)
-      if (piece_on(i) && active(piece_tile(i))) {
+      if (piece_on(i)) {
         const u32x4_t v = kin ? xr[i] : u32x4_t{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4_t*>(&sm.xs[buf][piece_row(i)][xcol]) = v;
       }
@@ -244,12 +237,12 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Pipelined form (fixed active tiles): fragment j + 1 is dequantised
+  // Pipelined form: fragment j + 1 is dequantised
   // before fragment j's MFMAs are issued, so the VALU work of one overlaps
   // the matrix work of the other inside a wave; the last fragment of a chunk
   // dequantises the first one of the next chunk (its weights are already
   // resident).  Acur / kcur carry that across chunks.
-  constexpr bool PIPE = FIXED && kPipelinedDequant;
+  constexpr bool PIPE = kPipelinedDequant;
   bf16x8_t Acur[NR];
   float kcur[NR][4];
   if constexpr (PIPE) {
@@ -329,8 +322,8 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
 // their active tiles; four- and eight-tile blocks round the count up to an
 // even one, so the extra tile (rows that are all padding: they read the
 // block's first row and are never stored) costs at most one tile of MFMAs,
-// while the checked loop (NA = 0) would wait for every outstanding load
-// wherever a tile is tested.  Each path owns its
+// where testing tiles inside the loop made it wait for every outstanding
+// load at each test.  Each path owns its
 // accumulators and finishes on its own: merging them into one array before
 // a shared epilogue makes the allocator rotate them between registers with
 // moves inside the loop, each of which waits for an MFMA.
@@ -344,8 +337,8 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, TileSmem<MT>& sm, 
     for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    mainloop<MT, NR, NW, D, NA>(p, sm, expert, nt, tmask, c0, c1, acc);
-    finish(acc, NA > 0 ? (1u << NA) - 1u : tmask);
+    mainloop<MT, NR, NW, D, NA>(p, sm, expert, nt, c0, c1, acc);
+    finish(acc, (1u << NA) - 1u);
   };
   if constexpr (MT == 1) {
     go(std::integral_constant<int, 1>{});
