@@ -83,12 +83,21 @@ def f64_to_e2m1(y: np.ndarray, negative: np.ndarray | None = None) -> np.ndarray
 
 # ------------------------------------------------------------ quantisation
 
-def mx_quantize(x_bits: np.ndarray):
+def mx_quantize(x_bits: np.ndarray, rows_per_slice: int = 2048):
     """BF16 rows [R, K] (K % 32 == 0) -> (codes uint8 [R, K], scales uint8
-    [R, K/32]) by the per-block conversion in the module docstring."""
+    [R, K/32]) by the per-block conversion in the module docstring.  Rows are
+    independent; they are converted a slice at a time to bound memory."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     R, K = x_bits.shape
     assert K % BLOCK == 0
+    if R > rows_per_slice:
+        parts = [_mx_quantize_rows(x_bits[i:i + rows_per_slice]) for i in range(0, R, rows_per_slice)]
+        return np.concatenate([c for c, _ in parts]), np.concatenate([s for _, s in parts])
+    return _mx_quantize_rows(x_bits)
+
+
+def _mx_quantize_rows(x_bits: np.ndarray):
+    R, K = x_bits.shape
     v = bf16_to_f64(x_bits).reshape(R, K // BLOCK, BLOCK)
     negative = ((x_bits >> 15) & 1).astype(bool).reshape(R, K // BLOCK, BLOCK)
     amax = np.abs(v).max(axis=-1)

@@ -195,11 +195,13 @@ def test_mx_no_local_slots_and_empty():
     assert out.shape == (0, sh.N1)
 
 
-def test_mx_full_size_ep8_decode():
-    """The EP8 decode share at full size (48 experts, N 4096, K 7168 and the
-    down projection), with the selector's block_m: all slots, 64 sampled
-    output columns, against the oracle."""
-    sh = W.WORKLOADS["ep8_decode"]
+@pytest.mark.parametrize("name", ["ep8_decode", "k3_decode", "ep8_prefill"])
+def test_mx_full_size(name):
+    """Full-size shares (EP8 decode and prefill: 48 experts, N 4096, K 7168
+    and the down projection; the K3-like routing), with the selector's
+    block_m: all slots, 64 sampled output columns, against the oracle."""
+    log("generating", name)
+    sh = W.WORKLOADS[name]
     P = MxProblem(sh).upload()
     T, k = P.T, sh.topk
     cfg0 = M.select(T, k, sh.E_glob, sh.E_loc, sh.N1, sh.K1)
@@ -213,6 +215,6 @@ def test_mx_full_size_ep8_decode():
                                      sh.first, sh.E_loc)
     y_ref = X.mx_indexed_down_combine(*P.aq, X.unpack_nibbles(P.w2[:, c2]), P.s2[:, c2], P.topk_ids,
                                       P.topk_w, sh.first, sh.E_loc)
-    e1, x1 = assert_close(h[ok][:, c1], h_ref[ok], "ep8 mx gate/up")
-    e2, x2 = assert_close(y[:, c2], y_ref, "ep8 mx down+combine")
-    log("ep8 mx full size", dict(block_m=cfg0.block_m, gu_err=e1, gu_exact=x1, dn_err=e2, dn_exact=x2))
+    e1, x1 = assert_close(h[ok][:, c1], h_ref[ok], f"{name} mx gate/up")
+    e2, x2 = assert_close(y[:, c2], y_ref, f"{name} mx down+combine")
+    log(name, "mx full size", dict(block_m=cfg0.block_m, gu_err=e1, gu_exact=x1, dn_err=e2, dn_exact=x2))
