@@ -193,9 +193,6 @@ def main() -> int:
     ids, wts = W.routing_for(sh)
     x = W.activations(sh.seed, "x", sh.T, sh.K1)
     a = W.activations(sh.seed, "a", sh.T * sh.topk, sh.K2)
-    if args.mx and args.fused:
-        log("--mx and --fused are separate variants")
-        return 2
     if args.mx:
         c1 = W.mx_weight_codes(sh.seed, "w1_mx_codes", sh.E_loc, sh.N1, sh.K1)
         s1 = W.mx_weight_scales(sh.seed, "w1_mx_scales", sh.E_loc, sh.N1, sh.K1)
@@ -212,7 +209,7 @@ def main() -> int:
         return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(torch.bfloat16)
 
     if args.mx:
-        p1 = M.pack_mxfp4(torch.from_numpy(c1).to(dev), torch.from_numpy(s1).to(dev))
+        p1 = M.pack_mxfp4(torch.from_numpy(c1).to(dev), torch.from_numpy(s1).to(dev), gate_up=args.fused)
         p2 = M.pack_mxfp4(torch.from_numpy(c2).to(dev), torch.from_numpy(s2).to(dev))
     else:
         p1 = M.pack_w4(torch.from_numpy(c1).to(dev), bf(s1), gate_up=args.fused)
@@ -263,13 +260,18 @@ def main() -> int:
                                        cfg.block_m, sorted_ids.data_ptr(), expert_ids.data_ptr(),
                                        ntp.data_ptr(), cap, 0, s_ptr))
 
-    inter = torch.zeros(cap, sh.N1 // 2, dtype=torch.bfloat16, device=dev) if args.fused else None
-    if args.fused and (sh.K2 != sh.N1 // 2 or cfg.split_k != 1 or cfg.nr % 2):
-        log("--fused needs K2 = N1 / 2, split_k = 1 and an even nr")
+    inter = torch.zeros(cap, sh.N1 // 2, dtype=torch.bfloat16, device=dev) if args.fused and not args.mx else None
+    inter_mx = (M.MXRows(torch.zeros(cap, sh.N1 // 4, dtype=torch.uint8, device=dev),
+                         torch.zeros(cap, sh.N1 // 64, dtype=torch.uint8, device=dev))
+                if args.fused and args.mx else None)
+    if args.fused and (sh.K2 != sh.N1 // 2 or cfg.split_k != 1 or cfg.nr % 2 or (args.mx and cfg.nr != 4)):
+        log("--fused needs K2 = N1 / 2, split_k = 1 and an even nr (4 with --mx)")
         return 2
 
     def gate_up():
-        if args.mx:
+        if args.mx and args.fused:
+            M.moe_mxfp4_gate_up_silu(qx, p1, routing, cfg=cfg, out=inter_mx)
+        elif args.mx:
             M.moe_mxfp4_gemm(qx, p1, routing, cfg=cfg, out=h)
         elif args.fused:
             M.moe_gate_up_silu(d_x, p1, routing, cfg=cfg, out=inter)
@@ -277,7 +279,10 @@ def main() -> int:
             M.moe_w4a16_gemm(d_x, p1, routing, cfg=cfg, out=h, workspace=ws1)
 
     def down():
-        if args.mx:
+        if args.mx and args.fused:
+            M.moe_mxfp4_gemm(inter_mx, p2, routing, topk_weights=d_w, a_layout="sorted", cfg=cfg, out=y,
+                             workspace=ws2)
+        elif args.mx:
             M.moe_mxfp4_gemm(qa, p2, routing, topk_weights=d_w, cfg=cfg, out=y, workspace=ws2)
         elif args.fused:
             M.moe_w4a16_gemm(inter, p2, routing, topk_weights=d_w, a_layout="sorted", cfg=cfg, out=y,
@@ -286,17 +291,19 @@ def main() -> int:
             M.moe_w4a16_gemm(d_a, p2, routing, topk_weights=d_w, cfg=cfg, out=y, workspace=ws2)
 
     def quant():
-        # A4W4: both projections' activation rows to MXFP4 (the down input
-        # is the step's synthetic per-slot rows, quantised like x)
+        # A4W4: the activation rows to MXFP4 (unfused: also the step's
+        # synthetic per-slot down input; fused: the gate/up epilogue
+        # quantises the down input itself)
         M.mxfp4_quant(d_x, out=qx)
-        M.mxfp4_quant(d_a, out=qa)
+        if not args.fused:
+            M.mxfp4_quant(d_a, out=qa)
 
     def step():
         align()
         if args.mx:
             M.mxfp4_quant(d_x, out=qx)
         gate_up()
-        if args.mx:
+        if args.mx and not args.fused:
             M.mxfp4_quant(d_a, out=qa)
         down()
 
@@ -382,7 +389,11 @@ def main() -> int:
     # algorithmic bytes per gate/up launch: weights+scales of touched experts,
     # one activation row read and one output row written per routed slot,
     # the routing indices
-    out1 = n_local * (sh.N1 // 2 if args.fused else sh.N1) * 2   # fused: the activation, half the columns
+    # fused: the activation, half the columns (MXFP4 with --mx: codes + scales)
+    if args.fused and args.mx:
+        out1 = n_local * (sh.N1 // 4 + sh.N1 // 64)
+    else:
+        out1 = n_local * (sh.N1 // 2 if args.fused else sh.N1) * 2
     row1 = sh.K1 // 2 + sh.K1 // 32 if args.mx else sh.K1 * 2     # MXFP4 row: codes + scales
     alg1 = wb1 + n_local * row1 + out1 + n_ntp * 4 + (n_ntp // cfg.block_m) * 4
     value = (wb1 + wb2) / (ms_step * 1e-3) / 1e9
@@ -432,9 +443,10 @@ def main() -> int:
                      "algorithmic_bytes": int(alg1)},
     }
     if st_q is not None:
-        out["per_call_stats_us"]["mxfp4_quant_x_and_a"] = {"median": round(st_q[1], 2), "min": round(st_q[2], 2),
+        qname = "mxfp4_quant_x" if args.fused else "mxfp4_quant_x_and_a"
+        out["per_call_stats_us"][qname] = {"median": round(st_q[1], 2), "min": round(st_q[2], 2),
                                                           "p90": round(st_q[3], 2)}
-        out["per_call_us"]["mxfp4_quant_x_and_a"] = round(st_q[0], 2)
+        out["per_call_us"][qname] = round(st_q[0], 2)
         out["gemm_rates"]["gate_up_fp4_frac"] = round(flops1 / (us_gu * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4)
     if args.cpu_experts > 0:
         log("timing the CPU oracle baseline ...")

@@ -97,7 +97,8 @@ int32_t w4a16_abi_version(void);
 #define W4A16_DESC_MAGIC 0x16A4B0E5u /* arbitrary tag */
 #define W4A16_DESC_VERSION 2u
 #define W4A16_DESC_GATE_UP 1         /* flags: gate/up tiles interleaved */
-#define W4A16_DESC_MXFP4 2           /* flags: MXFP4 weight (A4W4 calls only) */
+#define W4A16_DESC_MXFP4 2           /* flags: MXFP4 weight (A4W4 calls only); may be
+                                        combined with W4A16_DESC_GATE_UP */
 
 typedef struct {
   uint32_t magic;       /* W4A16_DESC_MAGIC */
@@ -106,7 +107,7 @@ typedef struct {
   int32_t K_pad;        /* KP above */
   int32_t chunks;       /* KC above */
   int32_t group;        /* 32 */
-  int32_t flags;        /* 0, W4A16_DESC_GATE_UP or W4A16_DESC_MXFP4 */
+  int32_t flags;        /* 0, W4A16_DESC_GATE_UP, W4A16_DESC_MXFP4 or both MXFP4 bits */
   int32_t reserved;     /* 0 */
   uint64_t w_bytes;     /* size of packed_w */
   uint64_t s_bytes;     /* size of packed_s */
@@ -320,6 +321,13 @@ w4a16_status w4a16_grouped_masked(const w4a16_weight_desc* desc, const void* pac
  * Errors: ERR_ARG (out NULL, E/N/K <= 0), ERR_SHAPE (K % 128 or N % 16). */
 w4a16_status w4a16_mxfp4_weight_desc_init(int32_t E, int32_t N, int32_t K, w4a16_weight_desc* out);
 
+/* The same for an MXFP4 gate/up weight (rows [0, N/2) gate, [N/2, N) up)
+ * packed with its gate and up tiles alternating (flags W4A16_DESC_MXFP4 |
+ * W4A16_DESC_GATE_UP), as the fused A4W4 gate/up call needs; every other
+ * call on it still sees the logical column order.
+ * Errors: as above, and ERR_SHAPE when N % 64 != 0. */
+w4a16_status w4a16_mxfp4_weight_desc_init_gate_up(int32_t E, int32_t N, int32_t K, w4a16_weight_desc* out);
+
 /* Pack MXFP4 weights: codes [E, N, K/2] bytes (two per byte) and E8M0
  * scales [E, N, K/32] bytes into the layout above.  codes 16-byte aligned;
  * packed_w / packed_s 16-byte aligned and desc->w_bytes / desc->s_bytes long.
@@ -344,8 +352,9 @@ size_t w4a16_mxfp4_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, int32
                                             int32_t combine);
 
 /* out = routed A4W4 product on MXFP4 activations (a_codes [a_rows, K/2],
- * a_scales [a_rows, K/32], rows as a_layout says: W4A16_A_TOKEN or
- * W4A16_A_SLOT) and an MXFP4 weight.  Outputs exactly as w4a16_moe_gemm:
+ * a_scales [a_rows, K/32], rows as a_layout says: W4A16_A_TOKEN,
+ * W4A16_A_SLOT, or W4A16_A_SORTED for the rows w4a16_mxfp4_gate_up_silu
+ * writes) and an MXFP4 weight.  Outputs exactly as w4a16_moe_gemm:
  * per-slot bf16 rows (topk_weights NULL) or the top-k-weighted combine into
  * out[T, N] with fp32 partials summed in j order and rounded once.
  * Accumulation is fp32 (the MFMA's); each output is rounded once to bf16.
@@ -359,6 +368,25 @@ w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* pac
                                   int32_t a_layout, const w4a16_indexed_routing* routing,
                                   const float* topk_weights, uint16_t* out, const w4a16_config* cfg,
                                   void* workspace, size_t workspace_bytes, w4a16_stream_t stream);
+
+/* Fused A4W4 gate/up: the gate/up product on MXFP4 token rows (x_codes
+ * [x_rows, K/2], x_scales [x_rows, K/32], x_rows >= routing->T) with a
+ * W4A16_DESC_MXFP4 | W4A16_DESC_GATE_UP weight (N = 2 I), the activation
+ * bf16(silu(g) * u) of its bf16-rounded per-slot values (as
+ * w4a16_moe_gate_up_silu), quantised to MXFP4 by the conversion of
+ * w4a16_mxfp4_quant, written for each sorted position p that holds a local
+ * slot: out_codes[p] ([capacity, I/2] bytes), out_scales[p] ([capacity,
+ * I/32]).  Padding positions are left unwritten; the down projection reads
+ * the rows with a_layout = W4A16_A_SORTED.
+ *  cfg : NULL: block_m from the routing, nr 4, four waves; nr must be 4 and
+ *        split_k 1.
+ * Pointers: packed_w, packed_s, x_codes, out_codes 16-byte aligned.
+ * Errors: ERR_ARG, ERR_LAYOUT (not an MXFP4 gate/up weight), ERR_SHAPE,
+ * ERR_UNSUPPORTED, ERR_HIP. */
+w4a16_status w4a16_mxfp4_gate_up_silu(const w4a16_weight_desc* desc, const void* packed_w, const void* packed_s,
+                                      const uint8_t* x_codes, const uint8_t* x_scales, int64_t x_rows,
+                                      const w4a16_indexed_routing* routing, uint8_t* out_codes,
+                                      uint8_t* out_scales, const w4a16_config* cfg, w4a16_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -179,7 +179,8 @@ def test_mxfp4_descriptor_and_errors(L):
     assert call(d=plain) == -3                                           # not an MXFP4 weight
     assert L.w4a16_moe_gemm(ctypes.byref(mx), P, P, P, 64, 0, ctypes.byref(r), None, P,
                             ctypes.byref(W.config(32, 2)), None, 0, None) == -3
-    assert call(layout=_lib.A_SORTED) == -1                              # token or slot rows only
+    assert call(layout=3) == -1                                          # unknown activation layout
+    assert call(layout=_lib.A_SORTED) == -2                              # sorted rows: needs capacity = 1024
     assert call(rows=10) == -2                                           # too few rows
     assert call(c=W.mxfp4_config(32, 3)) == -4                           # not built
     assert call(c=W.config(32, 4, split_k=0, stages=4)) == -4            # one workgroup per tile
@@ -188,3 +189,21 @@ def test_mxfp4_descriptor_and_errors(L):
     assert L.w4a16_mxfp4_moe_gemm_workspace_bytes(ctypes.byref(mx), 10, 8, 1) == 10 * 8 * 64 * 4
     assert L.w4a16_mxfp4_quant(P, 4, 48, P, P, None) == -2               # K % 32
     assert L.w4a16_mxfp4_quant(P + 4, 4, 64, P, P, None) == -1           # misaligned rows
+
+
+def test_mxfp4_gate_up_silu_errors(L):
+    P = 16
+    plain = W.mxfp4_weight_desc(8, 128, 256)
+    gated = W.mxfp4_weight_desc(8, 128, 256, gate_up=True)
+    assert gated.flags == _lib.DESC_MXFP4 | _lib.DESC_GATE_UP
+    e = _lib.WeightDesc()
+    assert L.w4a16_mxfp4_weight_desc_init_gate_up(8, 96, 256, ctypes.byref(e)) == -2   # N % 64
+    r = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 8)
+    call = lambda d, cfg: L.w4a16_mxfp4_gate_up_silu(ctypes.byref(d), P, P, P, P, 64, ctypes.byref(r), P, P,
+                                                     ctypes.byref(cfg), None)
+    assert call(plain, W.mxfp4_config(32, 4)) == -3                      # not a gate/up MXFP4 weight
+    assert call(W.weight_desc(8, 128, 256, gate_up=True), W.mxfp4_config(32, 4)) == -3   # INT4 weight
+    assert call(gated, W.mxfp4_config(32, 2)) == -4                      # nr must be 4
+    assert call(gated, W.mxfp4_config(64, 4)) == -3                      # block_m disagrees with routing
+    # the INT4 calls reject the combined flags too
+    assert L.w4a16_pack_w4(P, P, ctypes.byref(gated), P, P, None) == -3

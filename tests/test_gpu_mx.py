@@ -218,3 +218,74 @@ def test_mx_full_size(name):
     e1, x1 = assert_close(h[ok][:, c1], h_ref[ok], f"{name} mx gate/up")
     e2, x2 = assert_close(y[:, c2], y_ref, f"{name} mx down+combine")
     log(name, "mx full size", dict(block_m=cfg0.block_m, gu_err=e1, gu_exact=x1, dn_err=e2, dn_exact=x2))
+
+
+# ------------------------------------------------------------ fused A4W4 chain
+
+def _fused_shapes():
+    tiny = W.WORKLOADS["tiny"]                                         # K2 = N1 / 2
+    ragged = W.MoEShape(name="ragged_mxf", E_glob=9, E_loc=5, first=2, topk=3, T=37, K1=384, N1=256,
+                        K2=128, N2=48, seed=83)
+    deep = W.MoEShape(name="deep_mxf", E_glob=8, E_loc=6, first=1, topk=2, T=70, K1=1408, N1=512,
+                      K2=256, N2=64, seed=95)
+    return [tiny, ragged, deep]
+
+
+@pytest.mark.parametrize("shape", _fused_shapes(), ids=lambda s: s.name)
+def test_mx_fused_silu_quant_and_sorted_down(shape):
+    """Fused A4W4 gate/up (activation + MXFP4 quantisation in sorted order)
+    against the oracle's activation and quantiser applied to the GPU's own
+    per-slot gate/up output; the down projection on the sorted rows
+    bit-identical to the same rows gathered per slot; the chain against the
+    oracle's chain."""
+    sh = shape
+    assert sh.K2 == sh.N1 // 2
+    P = MxProblem(sh).upload()
+    T, k = P.T, sh.topk
+    p1g = M.pack_mxfp4(to_dev(P.w1), to_dev(P.s1), gate_up=True)
+    # oracle chain: per-slot gate/up, activation, MXFP4, down + combine
+    h_ref, ok = X.mx_indexed_gate_up(*P.xq, X.unpack_nibbles(P.w1), P.s1, P.topk_ids, sh.first, sh.E_loc)
+    a_ref = np.zeros((T * k, sh.K2), np.uint16)
+    a_ref[ok] = O.silu_mul(h_ref[ok])
+    y_ref = X.mx_indexed_down_combine(*X.mx_quantize(a_ref), X.unpack_nibbles(P.w2), P.s2, P.topk_ids, P.topk_w,
+                                      sh.first, sh.E_loc)
+    for bm in (16, 32, 64, 128):
+        r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, bm)
+        cfg = M.mxfp4_config(bm, 4)
+        h = M.moe_mxfp4_gemm(P.d_x, P.p1, r, cfg=cfg)
+        hg = M.moe_mxfp4_gemm(P.d_x, p1g, r, cfg=cfg)
+        inter = M.moe_mxfp4_gate_up_silu(P.d_x, p1g, r, cfg=cfg)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(hg), bits(h), err_msg=f"interleaved packing changed bits, bm={bm}")
+        sid = r.sorted_ids.cpu().numpy()
+        valid = sid < T * k
+        # the oracle's activation and quantiser on the GPU's per-slot values
+        hb = bits(h)
+        act = O.silu_mul(hb[sid[valid]])
+        rc, rs = X.mx_quantize(act)
+        gc = X.unpack_nibbles(inter.codes.cpu().numpy())[valid]
+        gs = inter.scales.cpu().numpy()[valid]
+        same_s = gs == rs
+        same_c = gc == rc
+        got_v = X.mx_dequant(gc, gs)
+        ref_v = X.mx_dequant(rc, rs)
+        # a one-ulp difference in the bf16 activation (fp32 exp on the GPU,
+        # fp64 in the oracle) can move a code by one step or the block scale
+        # by one binade: at most one step of the coarser E2M1 spacing (2 X)
+        bound = 2.0 * np.repeat(np.maximum(X.e8m0_to_f64(gs), X.e8m0_to_f64(rs)), 32, axis=1)
+        assert np.all(np.abs(got_v - ref_v) <= bound), f"bm={bm}"
+        assert same_s.mean() > 0.99 and same_c.mean() > 0.99, (same_s.mean(), same_c.mean())
+        # down on sorted rows == down on the same rows gathered per slot
+        slot_rows = M.MXRows(torch.zeros(T * k, sh.K2 // 2, dtype=torch.uint8, device="cuda"),
+                             torch.zeros(T * k, sh.K2 // 32, dtype=torch.uint8, device="cuda"))
+        vpos = torch.from_numpy(np.nonzero(valid)[0]).cuda()
+        vslot = torch.from_numpy(sid[valid].astype(np.int64)).cuda()
+        slot_rows.codes[vslot] = inter.codes[vpos]
+        slot_rows.scales[vslot] = inter.scales[vpos]
+        y_sorted = M.moe_mxfp4_gemm(inter, P.p2, r, topk_weights=P.d_w, a_layout="sorted", cfg=cfg)
+        y_slot = M.moe_mxfp4_gemm(slot_rows, P.p2, r, topk_weights=P.d_w, a_layout="slot", cfg=cfg)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(y_sorted), bits(y_slot), err_msg=f"bm={bm}")
+        e, x_ = assert_close(bits(y_sorted), y_ref, f"{sh.name} A4W4 chain bm={bm}")
+        log(sh.name, f"bm={bm}", dict(chain_err=e, chain_exact=x_, codes_exact=float(same_c.mean()),
+                                      scales_exact=float(same_s.mean())))

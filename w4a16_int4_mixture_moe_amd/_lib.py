@@ -84,6 +84,9 @@ SIGNATURES = {
     "w4a16_grouped_masked": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I32, _P, _I32, _P,
                                     ctypes.POINTER(Config), _P]),
     "w4a16_mxfp4_weight_desc_init": (_I32, [_I32, _I32, _I32, ctypes.POINTER(WeightDesc)]),
+    "w4a16_mxfp4_weight_desc_init_gate_up": (_I32, [_I32, _I32, _I32, ctypes.POINTER(WeightDesc)]),
+    "w4a16_mxfp4_gate_up_silu": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _P, _I64,
+                                        ctypes.POINTER(IndexedRouting), _P, _P, ctypes.POINTER(Config), _P]),
     "w4a16_mxfp4_pack": (_I32, [_P, _P, ctypes.POINTER(WeightDesc), _P, _P, _P]),
     "w4a16_mxfp4_quant": (_I32, [_P, _I64, _I32, _P, _P, _P]),
     "w4a16_mxfp4_moe_gemm_workspace_bytes": (_SZ, [ctypes.POINTER(WeightDesc), _I32, _I32, _I32]),

@@ -315,22 +315,24 @@ class MXRows:
         return 2 * self.codes.shape[1]
 
 
-def mxfp4_weight_desc(E: int, N: int, K: int) -> WeightDesc:
+def mxfp4_weight_desc(E: int, N: int, K: int, gate_up: bool = False) -> WeightDesc:
     d = WeightDesc()
-    check(load().w4a16_mxfp4_weight_desc_init(E, N, K, ctypes.byref(d)))
+    init = load().w4a16_mxfp4_weight_desc_init_gate_up if gate_up else load().w4a16_mxfp4_weight_desc_init
+    check(init(E, N, K, ctypes.byref(d)))
     return d
 
 
-def pack_mxfp4(codes: torch.Tensor, scales: torch.Tensor) -> PackedW4:
+def pack_mxfp4(codes: torch.Tensor, scales: torch.Tensor, gate_up: bool = False) -> PackedW4:
     """MXFP4 weight: codes uint8 [E, N, K/2] (two per byte), E8M0 scales
-    uint8 [E, N, K/32] -> packed weight (K % 128 == 0)."""
+    uint8 [E, N, K/32] -> packed weight (K % 128 == 0).  gate_up: rows
+    [0, N/2) gate, [N/2, N) up, tiles interleaved (moe_mxfp4_gate_up_silu)."""
     _need(codes, "codes", (torch.uint8,), 3)
     _need(scales, "scales", (torch.uint8,), 3)
     E, N, K2 = codes.shape
     K = 2 * K2
     if tuple(scales.shape) != (E, N, K // 32):
         raise ValueError(f"scales shape {tuple(scales.shape)} does not match codes {tuple(codes.shape)}")
-    d = mxfp4_weight_desc(E, N, K)
+    d = mxfp4_weight_desc(E, N, K, gate_up)
     w = torch.empty(d.w_bytes, dtype=torch.uint8, device=codes.device)
     s = torch.empty(d.s_bytes, dtype=torch.uint8, device=codes.device)
     check(load().w4a16_mxfp4_pack(codes.data_ptr(), scales.data_ptr(), ctypes.byref(d), w.data_ptr(),
@@ -363,16 +365,17 @@ def moe_mxfp4_gemm(a: MXRows, packed: PackedW4, routing: Routing,
                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Indexed A4W4 MoE GEMM on MXFP4 rows and an MXFP4 weight; outputs as
     moe_w4a16_gemm (per slot, or the top-k combine with topk_weights).
-    a_layout: "token" or "slot" (default "slot" with topk_weights)."""
-    if packed.desc.flags != DESC_MXFP4:
+    a_layout: "token", "slot" (default with topk_weights) or "sorted" (the
+    rows moe_mxfp4_gate_up_silu writes)."""
+    if not packed.desc.flags & DESC_MXFP4:
         raise ValueError("moe_mxfp4_gemm needs a weight from pack_mxfp4")
     _need(a.codes, "a.codes", (torch.uint8,), 2)
     _need(a.scales, "a.scales", (torch.uint8,), 2)
     T, k = routing.T, routing.topk
     if a_layout is None:
         a_layout = "slot" if topk_weights is not None else "token"
-    if a_layout not in ("token", "slot"):
-        raise ValueError('a_layout must be "token" or "slot"')
+    if a_layout not in _A_LAYOUTS:
+        raise ValueError(f"a_layout must be one of {sorted(_A_LAYOUTS)}")
     if a.K != packed.K or a.scales.shape[1] != packed.K // 32:
         raise ValueError(f"activations have K={a.K}, weight has K={packed.K}")
     dev = a.codes.device
@@ -397,4 +400,32 @@ def moe_mxfp4_gemm(a: MXRows, packed: PackedW4, routing: Routing,
                                       None if cfg is None else ctypes.byref(cfg),
                                       _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                       _stream(dev)))
+    return out
+
+
+def moe_mxfp4_gate_up_silu(x: MXRows, packed: PackedW4, routing: Routing, cfg: Optional[Config] = None,
+                           out: Optional[MXRows] = None) -> MXRows:
+    """Fused A4W4 gate/up for a gate/up-interleaved MXFP4 weight [E, 2I, K]:
+    MXFP4 rows of bf16(silu(g) * u) at sorted positions, [capacity, I]
+    (padding positions unwritten); the down projection reads them with
+    a_layout="sorted"."""
+    if packed.desc.flags != (DESC_MXFP4 | DESC_GATE_UP):
+        raise ValueError("moe_mxfp4_gate_up_silu needs a weight from pack_mxfp4(..., gate_up=True)")
+    _need(x.codes, "x.codes", (torch.uint8,), 2)
+    _need(x.scales, "x.scales", (torch.uint8,), 2)
+    if x.K != packed.K:
+        raise ValueError(f"activations have K={x.K}, weight has K={packed.K}")
+    I = packed.N // 2
+    cap = routing.capacity
+    dev = x.codes.device
+    if out is None:
+        out = MXRows(torch.zeros(cap, I // 2, dtype=torch.uint8, device=dev),
+                     torch.zeros(cap, I // 32, dtype=torch.uint8, device=dev))
+    elif out.rows < cap or out.K != I:
+        raise ValueError(f"out must hold [{cap}, {I}] MXFP4 rows")
+    r = routing.as_c()
+    check(load().w4a16_mxfp4_gate_up_silu(ctypes.byref(packed.desc), packed.w.data_ptr(), packed.s.data_ptr(),
+                                          x.codes.data_ptr(), x.scales.data_ptr(), x.rows, ctypes.byref(r),
+                                          out.codes.data_ptr(), out.scales.data_ptr(),
+                                          None if cfg is None else ctypes.byref(cfg), _stream(dev)))
     return out

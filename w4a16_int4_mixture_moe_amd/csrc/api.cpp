@@ -67,8 +67,8 @@ w4a16_weight_desc make_desc(int32_t E, int32_t N, int32_t K, int32_t flags) {
   d.group = 32;
   const int64_t NT = N / 16;
   d.w_bytes = (uint64_t)E * NT * KC * 1024;
-  d.s_bytes = flags == W4A16_DESC_MXFP4 ? (uint64_t)E * NT * KC * 64            // one E8M0 byte per lane
-                                        : (uint64_t)E * NT * ((KC + 1) / 2) * 64 * 4;
+  d.s_bytes = (flags & W4A16_DESC_MXFP4) ? (uint64_t)E * NT * KC * 64          // one E8M0 byte per lane
+                                         : (uint64_t)E * NT * ((KC + 1) / 2) * 64 * 4;
   d.check = desc_checksum(d);
   return d;
 }
@@ -89,7 +89,8 @@ w4a16_status check_desc(const w4a16_weight_desc* d) {
   w4a16_status st = check_shape(d->E, d->N, d->K);
   if (st != W4A16_OK) return fail(W4A16_ERR_LAYOUT, "weight descriptor shape invalid: %s", g_last_error.c_str());
   const bool flags_ok = d->flags == 0 || (d->flags == W4A16_DESC_GATE_UP && d->N % 32 == 0) ||
-                        (d->flags == W4A16_DESC_MXFP4 && d->K % 128 == 0);
+                        (d->flags == W4A16_DESC_MXFP4 && d->K % 128 == 0) ||
+                        (d->flags == (W4A16_DESC_MXFP4 | W4A16_DESC_GATE_UP) && d->K % 128 == 0 && d->N % 64 == 0);
   if (!flags_ok) return fail(W4A16_ERR_LAYOUT, "weight descriptor flags invalid");
   const w4a16_weight_desc ref = make_desc(d->E, d->N, d->K, d->flags);
   if (std::memcmp(&ref, d, sizeof ref) != 0) return fail(W4A16_ERR_LAYOUT, "weight descriptor fields inconsistent");
@@ -100,7 +101,7 @@ w4a16_status check_desc(const w4a16_weight_desc* d) {
 w4a16_status check_int4_desc(const w4a16_weight_desc* d) {
   w4a16_status st = check_desc(d);
   if (st != W4A16_OK) return st;
-  if (d->flags == W4A16_DESC_MXFP4)
+  if (d->flags & W4A16_DESC_MXFP4)
     return fail(W4A16_ERR_LAYOUT, "an MXFP4 weight descriptor is used by the w4a16_mxfp4_* calls only");
   return W4A16_OK;
 }
@@ -108,7 +109,7 @@ w4a16_status check_int4_desc(const w4a16_weight_desc* d) {
 w4a16_status check_mx_desc(const w4a16_weight_desc* d) {
   w4a16_status st = check_desc(d);
   if (st != W4A16_OK) return st;
-  if (d->flags != W4A16_DESC_MXFP4)
+  if (!(d->flags & W4A16_DESC_MXFP4))
     return fail(W4A16_ERR_LAYOUT, "not an MXFP4 weight descriptor (use w4a16_mxfp4_weight_desc_init)");
   return W4A16_OK;
 }
@@ -220,7 +221,7 @@ w4a16::GemmParams base_params(const w4a16_weight_desc* d, const void* pw, const 
   p.KC = d->K_pad / 128;
   const int tiles_per_wg = nr * waves;
   p.n_tiles = (p.NT + tiles_per_wg - 1) / tiles_per_wg;
-  p.gated = d->flags == W4A16_DESC_GATE_UP;
+  p.gated = (d->flags & W4A16_DESC_GATE_UP) != 0;
   p.out = out;
   return p;
 }
@@ -578,6 +579,16 @@ w4a16_status w4a16_mxfp4_weight_desc_init(int32_t E, int32_t N, int32_t K, w4a16
   return W4A16_OK;
 }
 
+w4a16_status w4a16_mxfp4_weight_desc_init_gate_up(int32_t E, int32_t N, int32_t K, w4a16_weight_desc* out) {
+  if (out == nullptr) return fail(W4A16_ERR_ARG, "out is NULL");
+  w4a16_status st = check_shape(E, N, K);
+  if (st != W4A16_OK) return st;
+  if (K % 128) return fail(W4A16_ERR_SHAPE, "an MXFP4 weight needs K %% 128 == 0 (got %d)", K);
+  if (N % 64) return fail(W4A16_ERR_SHAPE, "an MXFP4 gate/up weight needs N %% 64 == 0 (got %d)", N);
+  *out = make_desc(E, N, K, W4A16_DESC_MXFP4 | W4A16_DESC_GATE_UP);
+  return W4A16_OK;
+}
+
 w4a16_status w4a16_mxfp4_pack(const uint8_t* codes, const uint8_t* scales, const w4a16_weight_desc* desc,
                               void* packed_w, void* packed_s, w4a16_stream_t stream) {
   w4a16_status st = check_mx_desc(desc);
@@ -585,7 +596,8 @@ w4a16_status w4a16_mxfp4_pack(const uint8_t* codes, const uint8_t* scales, const
   if (!codes || !scales || !packed_w || !packed_s) return fail(W4A16_ERR_ARG, "NULL pointer argument");
   if (!aligned16(codes) || !aligned16(packed_w) || !aligned16(packed_s))
     return fail(W4A16_ERR_ARG, "codes and packed buffers must be 16-byte aligned");
-  hipError_t e = w4a16::launch_mx_pack(codes, scales, desc->E, desc->N, desc->K, static_cast<uint4*>(packed_w),
+  hipError_t e = w4a16::launch_mx_pack(codes, scales, desc->E, desc->N, desc->K,
+                                       (desc->flags & W4A16_DESC_GATE_UP) != 0, static_cast<uint4*>(packed_w),
                                        static_cast<uint8_t*>(packed_s), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mxfp4_pack launch");
   return W4A16_OK;
@@ -627,9 +639,11 @@ w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* pac
     return fail(W4A16_ERR_ARG, "packed weights, activation codes and output must be 16-byte aligned");
   if (r.E_loc != desc->E)
     return fail(W4A16_ERR_LAYOUT, "routing has E_loc=%d but the packed weight holds %d experts", r.E_loc, desc->E);
-  if (a_layout != W4A16_A_TOKEN && a_layout != W4A16_A_SLOT)
-    return fail(W4A16_ERR_ARG, "a_layout %d is not W4A16_A_TOKEN or W4A16_A_SLOT", a_layout);
-  const int64_t need_rows = a_layout == W4A16_A_TOKEN ? (int64_t)r.T : (int64_t)r.T * r.topk;
+  if (a_layout != W4A16_A_TOKEN && a_layout != W4A16_A_SLOT && a_layout != W4A16_A_SORTED)
+    return fail(W4A16_ERR_ARG, "a_layout %d is not W4A16_A_TOKEN, W4A16_A_SLOT or W4A16_A_SORTED", a_layout);
+  const int64_t need_rows = a_layout == W4A16_A_TOKEN  ? (int64_t)r.T
+                            : a_layout == W4A16_A_SLOT ? (int64_t)r.T * r.topk
+                                                       : r.capacity;
   if (a_rows < need_rows)
     return fail(W4A16_ERR_SHAPE, "activations have %lld rows, need %lld", (long long)a_rows, (long long)need_rows);
   if ((int64_t)r.T * r.topk >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "T*topk too large");
@@ -669,7 +683,7 @@ w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* pac
   p.expert_ids = r.expert_ids;
   p.num_tokens_padded = r.num_tokens_padded;
   p.sentinel = r.T * r.topk;
-  p.a_row_div = a_layout == W4A16_A_TOKEN ? r.topk : 1;
+  p.a_row_div = a_layout == W4A16_A_TOKEN ? r.topk : a_layout == W4A16_A_SLOT ? 1 : 0;
   p.slot_weight = topk_weights;
   p.grid_blocks = (int32_t)(r.capacity / r.block_m);
   hipError_t e = w4a16::launch_mx_gemm(epi, c.block_m / 16, c.nr, c.waves, c.stages, p, s);
@@ -679,6 +693,66 @@ w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* pac
                               r.E_loc, desc->N, out, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
   }
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_mxfp4_gate_up_silu(const w4a16_weight_desc* desc, const void* packed_w, const void* packed_s,
+                                      const uint8_t* x_codes, const uint8_t* x_scales, int64_t x_rows,
+                                      const w4a16_indexed_routing* routing, uint8_t* out_codes,
+                                      uint8_t* out_scales, const w4a16_config* cfg, w4a16_stream_t stream) {
+  w4a16_status st = check_mx_desc(desc);
+  if (st != W4A16_OK) return st;
+  if (!(desc->flags & W4A16_DESC_GATE_UP))
+    return fail(W4A16_ERR_LAYOUT, "the fused A4W4 gate/up call needs a weight from w4a16_mxfp4_weight_desc_init_gate_up");
+  if (!routing) return fail(W4A16_ERR_ARG, "routing is NULL");
+  const w4a16_indexed_routing& r = *routing;
+  if (!packed_w || !packed_s || !r.sorted_ids || !r.expert_ids || !r.num_tokens_padded)
+    return fail(W4A16_ERR_ARG, "NULL pointer argument");
+  if (r.T < 0 || r.topk <= 0 || r.capacity < 0) return fail(W4A16_ERR_ARG, "bad routing sizes");
+  if (r.T > 0 && (!x_codes || !x_scales || !out_codes || !out_scales))
+    return fail(W4A16_ERR_ARG, "activations or outputs are NULL");
+  if (!aligned16(packed_w) || !aligned16(packed_s) || !aligned16(x_codes) || !aligned16(out_codes))
+    return fail(W4A16_ERR_ARG, "packed weights and code buffers must be 16-byte aligned");
+  if (r.E_loc != desc->E)
+    return fail(W4A16_ERR_LAYOUT, "routing has E_loc=%d but the packed weight holds %d experts", r.E_loc, desc->E);
+  if (x_rows < r.T) return fail(W4A16_ERR_SHAPE, "activations have %lld rows, need %d", (long long)x_rows, r.T);
+  if ((int64_t)r.T * r.topk >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "T*topk too large");
+  if (x_rows * (int64_t)(desc->K / 2) >= ((int64_t)1 << 32))
+    return fail(W4A16_ERR_SHAPE, "activation codes exceed 4 GiB (32-bit row offsets)");
+  w4a16_config c;
+  if (cfg) {
+    c = *cfg;
+  } else {
+    c.block_m = r.block_m;
+    c.nr = 4;
+    c.waves = 4;
+    c.split_k = 1;
+    c.stages = r.block_m <= 32 ? 4 : 2;
+    apply_env_overrides(&c);
+  }
+  if (!valid_block_m(c.block_m)) return fail(W4A16_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128}", c.block_m);
+  if (c.split_k != 1 || c.nr != 4)
+    return fail(W4A16_ERR_UNSUPPORTED, "the fused A4W4 gate/up call runs one workgroup per tile with nr = 4");
+  if (!w4a16::mx_gemm_config_supported(w4a16::kEpiSiluMx, c.block_m / 16, c.nr, c.waves, c.stages))
+    return fail(W4A16_ERR_UNSUPPORTED, "MXFP4 tile config block_m=%d nr=%d waves=%d stages=%d not built", c.block_m,
+                c.nr, c.waves, c.stages);
+  if (c.block_m != r.block_m)
+    return fail(W4A16_ERR_LAYOUT, "config block_m=%d differs from the routing's block_m=%d", c.block_m, r.block_m);
+  if (r.capacity % r.block_m) return fail(W4A16_ERR_CAPACITY, "capacity not a multiple of block_m");
+  if (r.T == 0) return W4A16_OK;
+  w4a16::GemmParams p = base_params(desc, packed_w, packed_s, reinterpret_cast<const uint16_t*>(x_codes),
+                                    out_codes, c.nr, c.waves);
+  p.a_scale = x_scales;
+  p.out_scale = out_scales;
+  p.sorted_ids = r.sorted_ids;
+  p.expert_ids = r.expert_ids;
+  p.num_tokens_padded = r.num_tokens_padded;
+  p.sentinel = r.T * r.topk;
+  p.a_row_div = r.topk;
+  p.grid_blocks = (int32_t)(r.capacity / r.block_m);
+  hipError_t e = w4a16::launch_mx_gemm(w4a16::kEpiSiluMx, c.block_m / 16, c.nr, c.waves, c.stages, p,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mxfp4_gate_up_silu launch");
   return W4A16_OK;
 }
 

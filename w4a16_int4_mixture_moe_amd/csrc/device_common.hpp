@@ -66,6 +66,14 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t d, float s, float c0, floa
   return r;
 }
 
+// Source row of row i of packed tile `tile`: with gate_up, packed tile 2t is
+// gate tile t (rows 16t..) and packed tile 2t + 1 up tile t (rows N/2 + 16t..)
+// (both weight packers)
+__device__ __forceinline__ int source_row(int tile, int i, int N, int gate_up) {
+  const int t = gate_up ? (tile & 1 ? N / 32 + (tile >> 1) : tile >> 1) : tile;
+  return t * kRowTile + i;
+}
+
 // Global-memory byte pointer (address space 1: loads through it are
 // global_load, never flat_load).
 typedef const char __attribute__((address_space(1)))* gptr_t;

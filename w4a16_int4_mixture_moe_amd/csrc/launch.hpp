@@ -19,8 +19,9 @@ hipError_t launch_pack(const uint8_t* codes, const uint16_t* scales, int32_t E, 
 
 // ---- GEMM (gemm.hip)
 enum RouteKind : int { kRouteIndexed = 0, kRouteContiguous = 1, kRouteMasked = 2 };
-// kEpiSilu: gate/up pairs of tiles -> bf16(silu(g) * u) at sorted positions
-enum EpilogueKind : int { kEpiStore = 0, kEpiWeighted = 1, kEpiSilu = 2 };
+// kEpiSilu: gate/up pairs of tiles -> bf16(silu(g) * u) at sorted positions;
+// kEpiSiluMx (MXFP4 kernels): the same activation quantised to MXFP4 rows
+enum EpilogueKind : int { kEpiStore = 0, kEpiWeighted = 1, kEpiSilu = 2, kEpiSiluMx = 3 };
 
 struct GemmParams {
   const uint4* packed_w;        // [E][NT][KC][64][4 words]
@@ -43,8 +44,10 @@ struct GemmParams {
   const int32_t* masked_m;
   int32_t max_m;
   int32_t blocks_per_group;
-  // output: bf16 [rows][N] (store) or fp32 [rows][N] (weighted)
+  // output: bf16 [rows][N] (store) or fp32 [rows][N] (weighted); kEpiSiluMx:
+  // E2M1 codes [rows][N/4] bytes (N/2 activation columns, two per byte)
   void* out;
+  uint8_t* out_scale;           // kEpiSiluMx: E8M0 scales [rows][N/64]
   // routed blocks (all kinds; for indexed the live count comes from
   // num_tokens_padded on the device, this is the capacity bound)
   int32_t grid_blocks;
@@ -84,9 +87,10 @@ hipError_t launch_mx_quant(const uint16_t* x, int64_t rows, int32_t K, uint8_t* 
                            hipStream_t stream);
 // codes [E][N][K/2] + scales [E][N][K/32] -> packed [E][N/16][K/128][64]
 // 16-byte fragments + [E][N/16][K/128][64] scale bytes; K % 128 == 0.
-hipError_t launch_mx_pack(const uint8_t* w, const uint8_t* s, int32_t E, int32_t N, int32_t K, uint4* pw,
-                          uint8_t* ps, hipStream_t stream);
-// Indexed routing only; epilogue kEpiStore or kEpiWeighted.
+// gate_up: tiles of the gate rows [0, N/2) and up rows [N/2, N) alternate.
+hipError_t launch_mx_pack(const uint8_t* w, const uint8_t* s, int32_t E, int32_t N, int32_t K, int32_t gate_up,
+                          uint4* pw, uint8_t* ps, hipStream_t stream);
+// Indexed routing only; epilogue kEpiStore, kEpiWeighted or kEpiSiluMx.
 bool mx_gemm_config_supported(int epilogue, int m_tiles, int nr, int waves, int stages);
 hipError_t launch_mx_gemm(int epilogue, int m_tiles, int nr, int waves, int stages, const GemmParams& p,
                           hipStream_t stream);

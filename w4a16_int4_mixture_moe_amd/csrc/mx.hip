@@ -109,8 +109,8 @@ hipError_t launch_mx_quant(const uint16_t* x, int64_t rows, int32_t K, uint8_t* 
 // block 4 chunk + lane / 16 -> the row's 16 code bytes of that block and its
 // scale byte.
 __global__ __launch_bounds__(256) void mx_pack_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ s,
-                                                       int32_t E, int32_t N, int32_t K, uint4* __restrict__ pw,
-                                                       uint8_t* __restrict__ ps) {
+                                                       int32_t E, int32_t N, int32_t K, int32_t gate_up,
+                                                       uint4* __restrict__ pw, uint8_t* __restrict__ ps) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int KC = K / 128, NT = N / 16;
   const int64_t total = (int64_t)E * NT * KC * kWave;
@@ -121,19 +121,19 @@ __global__ __launch_bounds__(256) void mx_pack_kernel(const uint8_t* __restrict_
   const int64_t et = q / KC;                    // expert * NT + tile
   const int t = (int)(et % NT);
   const int64_t e = et / NT;
-  const int64_t n = e * N + 16 * t + (lane & 15);
+  const int64_t n = e * N + source_row(t, lane & 15, N, gate_up);
   const int b = 4 * c + (lane >> 4);
   pw[i] = *reinterpret_cast<const uint4*>(w + n * (K / 2) + 16 * b);
   ps[i] = s[n * (K / 32) + b];
 }
 
-hipError_t launch_mx_pack(const uint8_t* w, const uint8_t* s, int32_t E, int32_t N, int32_t K, uint4* pw,
-                          uint8_t* ps, hipStream_t stream) {
+hipError_t launch_mx_pack(const uint8_t* w, const uint8_t* s, int32_t E, int32_t N, int32_t K, int32_t gate_up,
+                          uint4* pw, uint8_t* ps, hipStream_t stream) {
   const int64_t total = (int64_t)E * (N / 16) * (K / 128) * kWave;
   if (total == 0) return hipSuccess;
   const int64_t grid = (total + 255) / 256;
   if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(mx_pack_kernel, dim3((unsigned)grid), dim3(256), 0, stream, w, s, E, N, K, pw, ps);
+  hipLaunchKernelGGL(mx_pack_kernel, dim3((unsigned)grid), dim3(256), 0, stream, w, s, E, N, K, gate_up, pw, ps);
   return hipGetLastError();
 }
 
@@ -384,6 +384,60 @@ __device__ __forceinline__ void mx_mainloop_staged(const GemmParams& p, MxStaged
     if (c + st < KC) chunk(Tail{}, c + st, st);
 }
 
+// Fused activation for the A4W4 chain: a wave's four packed tiles of a
+// gate/up-interleaved weight (gate t, up t, gate t + 1, up t + 1, t even)
+// hold output columns [16 t, 16 t + 32) of the activation, one whole MXFP4
+// block per token.  Each lane forms bf16(silu(g) * u) from the bf16-rounded
+// per-slot values (as the bf16 path's fused epilogue does) for its 8 of the
+// token's 32 values; the four lanes of a token (lane % 16 equal) combine
+// their maxima with two cross-lane shuffles; each lane rounds its 8 values
+// with the FP4 conversion (the quantiser's steps) and stores its 4 code
+// bytes, the first lane the block's scale.  Rows go to sorted positions.
+template <int MT, int NR, int NW, typename Smem>
+__device__ __forceinline__ void mx_silu_epilogue(const GemmParams& p, const Smem& sm, int nt, uint32_t tmask,
+                                                 const f32x4_t (&acc)[NR][MT]) {
+  static_assert(NR == 4, "four packed tiles per wave: one 32-column block");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int rt_base = nt * (NW * NR) + wave * NR;
+  if (rt_base >= p.NT) return;                    // NT % 4 == 0: all four tiles exist
+  const int blk = rt_base / 4;                    // activation block of 32 columns
+  const int g = lane >> 4;
+  const int64_t row_bytes = p.N / 4;              // N / 2 activation columns, two per byte
+  const int64_t row_scales = p.N / 64;
+  uint8_t* codes = static_cast<uint8_t*>(p.out);
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    if (!((tmask >> t) & 1u)) continue;           // wave-uniform
+    float y[2][4];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t gu = pack_bf16x2(acc[2 * h][t][v], acc[2 * h + 1][t][v]);
+        const uint32_t a = pack_bf16x2(silu_mul(bf16_bits_to_float(gu & 0xFFFFu), bf16_bits_to_float(gu >> 16)), 0.f);
+        y[h][v] = bf16_bits_to_float(a & 0xFFFFu);
+        amax = max(amax, a & 0x7FFFu);
+      }
+    // every lane takes part in the shuffles; padding rows are dropped below
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16));
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+    const uint32_t code = (uint32_t)max((int)(amax >> 7) - 2, 0);
+    const float inv = __builtin_bit_cast(float, (254u - code) << 23);
+    const int orow = sm.out[16 * t + (lane & 15)];
+    if (orow < 0) continue;
+    uint8_t* dst = codes + (int64_t)orow * row_bytes + 16 * blk + 2 * g;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[h][0] * inv, y[h][1] * inv, 1.0f, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[h][2] * inv, y[h][3] * inv, 1.0f, 1);
+      *reinterpret_cast<uint16_t*>(dst + 8 * h) = (uint16_t)w;
+    }
+    if (g == 0) p.out_scale[(int64_t)orow * row_scales + blk] = (uint8_t)code;
+  }
+}
+
 template <int MT, int NR, int NW, int D, int EPI>
 __global__ __launch_bounds__(NW * kWave) void mx_gemm_kernel(const GemmParams p) {
   constexpr bool STAGED = MT >= 4;
@@ -408,7 +462,10 @@ __global__ __launch_bounds__(NW * kWave) void mx_gemm_kernel(const GemmParams p)
       mx_mainloop_staged<MT, NR, NW, D, NA>(p, sm, expert, nt, acc);
     else
       mx_mainloop<MT, NR, NW, D, NA>(p, sm, expert, nt, acc);
-    epilogue<MT, NR, NW, EPI>(p, sm, nt, (1u << NA) - 1u, acc);
+    if constexpr (EPI == kEpiSiluMx)
+      mx_silu_epilogue<MT, NR, NW>(p, sm, nt, (1u << NA) - 1u, acc);
+    else
+      epilogue<MT, NR, NW, EPI>(p, sm, nt, (1u << NA) - 1u, acc);
   };
   const int na = 32 - __clz(tmask);
   if constexpr (MT == 1) {
@@ -434,6 +491,8 @@ template <int MT, int NR, int NW, int D>
 static MxKernel mx_pick(int epi) {
   if (epi == kEpiStore) return mx_gemm_kernel<MT, NR, NW, D, kEpiStore>;
   if (epi == kEpiWeighted) return mx_gemm_kernel<MT, NR, NW, D, kEpiWeighted>;
+  if constexpr (NR == 4)
+    if (epi == kEpiSiluMx) return mx_gemm_kernel<MT, NR, NW, D, kEpiSiluMx>;
   return nullptr;
 }
 

@@ -12,13 +12,6 @@
 
 namespace w4a16 {
 
-// Source row of row i of packed tile `tile`: with gate_up, packed tile 2t is
-// gate tile t (rows 16t..) and packed tile 2t + 1 up tile t (rows N/2 + 16t..)
-__device__ __forceinline__ int source_row(int tile, int i, int N, int gate_up) {
-  const int t = gate_up ? (tile & 1 ? N / 32 + (tile >> 1) : tile >> 1) : tile;
-  return t * kRowTile + i;
-}
-
 __global__ __launch_bounds__(256) void pack_w_kernel(const uint8_t* __restrict__ codes, int32_t N,
                                                      int32_t K, int32_t NT, int32_t KC,
                                                      int32_t gate_up, int64_t total_words,

@@ -41,7 +41,7 @@ __device__ __forceinline__ int setup_rows(const GemmParams& p, int mb, Smem& sm)
       // activation row: the slot's token (a_row_div = topk), the slot (1),
       // or the sorted position itself (0: rows already in sorted order)
       sm.row[i] = v ? (p.a_row_div > 0 ? s / p.a_row_div : pos) : -1;
-      sm.out[i] = v ? (EPI == kEpiSilu ? pos : s) : -1;
+      sm.out[i] = v ? (EPI == kEpiSilu || EPI == kEpiSiluMx ? pos : s) : -1;
       if constexpr (EPI == kEpiWeighted) sm.w[i] = v ? p.slot_weight[s] : 0.f;
     }
   } else if constexpr (ROUTE == kRouteContiguous) {
