@@ -289,3 +289,55 @@ def test_mx_fused_silu_quant_and_sorted_down(shape):
         e, x_ = assert_close(bits(y_sorted), y_ref, f"{sh.name} A4W4 chain bm={bm}")
         log(sh.name, f"bm={bm}", dict(chain_err=e, chain_exact=x_, codes_exact=float(same_c.mean()),
                                       scales_exact=float(same_s.mean())))
+
+
+def test_mx_graph_capture_replays_match_eager():
+    """The fused A4W4 step (align, quantise x, fused gate/up, sorted-row down
+    + combine) captured in one HIP graph: replays reproduce the eager outputs
+    bit for bit, with other eager work and poisoned buffers between them."""
+    sh = W.WORKLOADS["tiny"]
+    P = MxProblem(sh).upload()
+    T, k = P.T, sh.topk
+    p1g = M.pack_mxfp4(to_dev(P.w1), to_dev(P.s1), gate_up=True)
+    bm = 32
+    x = to_dev_bf16(P.x_bits)
+    cap = M.align_capacity(T, k, sh.E_loc, bm)
+    r = M.Routing(torch.empty(cap, dtype=torch.int32, device="cuda"),
+                  torch.empty(cap // bm, dtype=torch.int32, device="cuda"),
+                  torch.empty(1, dtype=torch.int32, device="cuda"), bm, P.d_ids, sh.E_glob, sh.first, sh.E_loc)
+    q = M.MXRows(torch.empty(T, sh.K1 // 2, dtype=torch.uint8, device="cuda"),
+                 torch.empty(T, sh.K1 // 32, dtype=torch.uint8, device="cuda"))
+    inter = M.MXRows(torch.zeros(cap, sh.K2 // 2, dtype=torch.uint8, device="cuda"),
+                     torch.zeros(cap, sh.K2 // 32, dtype=torch.uint8, device="cuda"))
+    y = torch.empty(T, sh.N2, dtype=torch.bfloat16, device="cuda")
+    import ctypes
+    ws = torch.empty(int(M.load().w4a16_mxfp4_moe_gemm_workspace_bytes(ctypes.byref(P.p2.desc), T, k, 1)),
+                     dtype=torch.uint8, device="cuda")
+    cfg = M.mxfp4_config(bm, 4)
+    L = M.load()
+
+    def step():
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        M._lib.check(L.w4a16_moe_align(P.d_ids.data_ptr(), T, k, sh.E_glob, sh.first, sh.E_loc, bm,
+                                       r.sorted_ids.data_ptr(), r.expert_ids.data_ptr(),
+                                       r.num_tokens_padded.data_ptr(), cap, 0, s))
+        M.mxfp4_quant(x, out=q)
+        M.moe_mxfp4_gate_up_silu(q, p1g, r, cfg=cfg, out=inter)
+        M.moe_mxfp4_gemm(inter, P.p2, r, topk_weights=P.d_w, a_layout="sorted", cfg=cfg, out=y, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_y = bits(y).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        r.sorted_ids.fill_(-5)
+        q.codes.fill_(0xFF)
+        y.fill_(1.0)
+        ws.fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(y), ref_y, err_msg=f"replay {rep}")
+        _ = (x.float() @ x.float().t()).sum().item()                  # unrelated eager work
