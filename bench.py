@@ -117,12 +117,6 @@ def mx_weight_bytes(n_touched: int, N: int, K: int) -> int:
     return n_touched * (N * K // 2 + N * (K // 32))
 
 
-def mx_workspace_bytes(M, packed, T: int, k: int) -> int:
-    """Workspace of the A4W4 down projection's top-k combine."""
-    import ctypes
-    return M.load().w4a16_mxfp4_moe_gemm_workspace_bytes(ctypes.byref(packed.desc), T, k, 1)
-
-
 def cpu_baseline_mx(sh, ids, wts, x, a, w1, s1, w2, s2, n_experts: int) -> dict:
     """The MXFP4 oracle as it stands (quantise the step's activation rows,
     dequantise, float64 matmul, combine) on the first `n_experts` local
@@ -241,7 +235,7 @@ def main() -> int:
         # decode blocks (overrides apply as for the W4A16 kernels)
         cfg = M.mxfp4_config(cfg.block_m, args.nr or 4, args.stages or None)
         ws1 = torch.empty(16, dtype=torch.uint8, device=dev)
-        ws2 = torch.empty(max(16, int(mx_workspace_bytes(M, p2, T, k))), dtype=torch.uint8, device=dev)
+        ws2 = torch.empty(max(16, M.mxfp4_workspace_bytes(p2, T, k, True)), dtype=torch.uint8, device=dev)
         qx = M.MXRows(torch.empty(T, sh.K1 // 2, dtype=torch.uint8, device=dev),
                       torch.empty(T, sh.K1 // 32, dtype=torch.uint8, device=dev))
         qa = M.MXRows(torch.empty(T * k, sh.K2 // 2, dtype=torch.uint8, device=dev),

@@ -310,11 +310,10 @@ def test_mx_graph_capture_replays_match_eager():
     inter = M.MXRows(torch.zeros(cap, sh.K2 // 2, dtype=torch.uint8, device="cuda"),
                      torch.zeros(cap, sh.K2 // 32, dtype=torch.uint8, device="cuda"))
     y = torch.empty(T, sh.N2, dtype=torch.bfloat16, device="cuda")
-    import ctypes
-    ws = torch.empty(int(M.load().w4a16_mxfp4_moe_gemm_workspace_bytes(ctypes.byref(P.p2.desc), T, k, 1)),
-                     dtype=torch.uint8, device="cuda")
+    ws = torch.empty(M.mxfp4_workspace_bytes(P.p2, T, k, True), dtype=torch.uint8, device="cuda")
     cfg = M.mxfp4_config(bm, 4)
     L = M.load()
+    import ctypes
 
     def step():
         s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)

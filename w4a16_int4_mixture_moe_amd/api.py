@@ -355,6 +355,11 @@ def mxfp4_quant(x: torch.Tensor, out: Optional[MXRows] = None) -> MXRows:
     return out
 
 
+def mxfp4_workspace_bytes(packed: PackedW4, T: int, topk: int, combine: bool) -> int:
+    """Workspace moe_mxfp4_gemm needs (the top-k combine's fp32 partials)."""
+    return int(load().w4a16_mxfp4_moe_gemm_workspace_bytes(ctypes.byref(packed.desc), T, topk, int(bool(combine))))
+
+
 def mxfp4_config(block_m: int, nr: int = 4, stages: Optional[int] = None) -> Config:
     return config(block_m, nr, waves=4, split_k=1, stages=(4 if block_m <= 32 else 2) if stages is None else stages)
 
@@ -390,7 +395,7 @@ def moe_mxfp4_gemm(a: MXRows, packed: PackedW4, routing: Routing,
         if out.shape[0] < rows or out.shape[1] != packed.N:
             raise ValueError(f"out must be [{rows}, {packed.N}]")
     if workspace is None:
-        nws = int(load().w4a16_mxfp4_moe_gemm_workspace_bytes(ctypes.byref(packed.desc), T, k, int(combine)))
+        nws = mxfp4_workspace_bytes(packed, T, k, combine)
         if nws:
             workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
     r = routing.as_c()

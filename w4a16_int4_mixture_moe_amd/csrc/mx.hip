@@ -73,20 +73,19 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
   // against a CPU reference at every tie, past the clamp and at -0); the
   // byte selector packs four pairs into one word, element 2i in the low
   // nibble of byte i.
+  // one pair of bf16 values (a packed word) into byte B of `word`
+  auto pair = [&](auto b_, uint32_t word, uint32_t pv) {
+    constexpr int B = decltype(b_)::value;
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, __builtin_bit_cast(float, pv << 16) * inv,
+                                                    __builtin_bit_cast(float, pv & 0xFFFF0000u) * inv, 1.0f, B);
+  };
   uint32_t out[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t word = 0u;
-#define W4A16_PAIR(b)                                                                              \
-    {                                                                                              \
-      const uint32_t pv = v[4 * w + (b)];                                                          \
-      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, __builtin_bit_cast(float, pv << 16) * inv, \
-                                                      __builtin_bit_cast(float, pv & 0xFFFF0000u) * inv, \
-                                                      1.0f, (b));                                  \
-    }
-    W4A16_PAIR(0) W4A16_PAIR(1) W4A16_PAIR(2) W4A16_PAIR(3)
-#undef W4A16_PAIR
-    out[w] = word;
+    uint32_t word = pair(std::integral_constant<int, 0>{}, 0u, v[4 * w]);
+    word = pair(std::integral_constant<int, 1>{}, word, v[4 * w + 1]);
+    word = pair(std::integral_constant<int, 2>{}, word, v[4 * w + 2]);
+    out[w] = pair(std::integral_constant<int, 3>{}, word, v[4 * w + 3]);
   }
   *reinterpret_cast<uint4*>(codes + i * 16) = make_uint4(out[0], out[1], out[2], out[3]);
   scales[i] = (uint8_t)code;
