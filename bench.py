@@ -101,13 +101,15 @@ def cpu_baseline(sh, ids, wts, x, a, c1, s1, c2, s2, n_experts: int) -> dict:
     S = n_experts
     t0 = time.perf_counter()
     O.indexed_gate_up_fp32(x, c1[:S], s1[:S], ids, sh.first, S)
+    t1 = time.perf_counter()
     O.indexed_down_combine_fp32(a, c2[:S], s2[:S], ids, wts, sh.first, S)
-    dt = time.perf_counter() - t0
+    t2 = time.perf_counter()
+    dt = t2 - t0
     flat = ids.reshape(-1)
     rows = int(((flat >= sh.first) & (flat < sh.first + S)).sum())
     b = weight_bytes(S, sh.N1, sh.K1) + weight_bytes(S, sh.N2, sh.K2)
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 3),
+            "seconds": round(dt, 3), "gate_up_seconds": round(t1 - t0, 3), "down_combine_seconds": round(t2 - t1, 3),
             "sample": f"gate/up + down+combine for local experts 0..{S - 1} of {sh.E_loc} "
                       f"({rows} routed rows), same inputs as the GPU step; GB/s of weight+scale bytes"}
 
@@ -131,14 +133,19 @@ def cpu_baseline_mx(sh, ids, wts, x, a, w1, s1, w2, s2, n_experts: int) -> dict:
     t0 = time.perf_counter()
     xq = X.mx_quantize(x)
     aq = X.mx_quantize(a)
+    t1 = time.perf_counter()
     X.mx_indexed_gate_up(*xq, X.unpack_nibbles(w1[:S]), s1[:S], ids, sh.first, S)
+    t2 = time.perf_counter()
     X.mx_indexed_down_combine(*aq, X.unpack_nibbles(w2[:S]), s2[:S], ids, wts, sh.first, S)
-    dt = time.perf_counter() - t0
+    t3 = time.perf_counter()
+    dt = t3 - t0
     flat = ids.reshape(-1)
     rows = int(((flat >= sh.first) & (flat < sh.first + S)).sum())
     b = mx_weight_bytes(S, sh.N1, sh.K1) + mx_weight_bytes(S, sh.N2, sh.K2)
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "seconds": round(dt, 3),
+            "quantise_seconds": round(t1 - t0, 3), "gate_up_seconds": round(t2 - t1, 3),
+            "down_combine_seconds": round(t3 - t2, 3),
             "sample": f"A4W4: quantise all activation rows, gate/up + down+combine for local experts "
                       f"0..{S - 1} of {sh.E_loc} ({rows} routed rows), same inputs as the GPU step; "
                       f"GB/s of MXFP4 weight+scale bytes"}
