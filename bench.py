@@ -334,6 +334,24 @@ def main() -> int:
         t = np.array([a_.elapsed_time(b_) * 1e3 / per for a_, b_ in ev])
         return float(t.mean()), float(np.median(t)), float(t.min()), float(np.percentile(t, 90))
 
+    def cold(fn, reps):
+        """Per-call duration with every cache cold: before each call a
+        1 GiB read (far beyond the 256 MB last-level cache) evicts whatever
+        the previous call left, leaving only clean lines (a writing flush
+        would leave the call to compete with their write-back); events
+        bracket the call alone on its stream.  Returns (median, min, p90)
+        in us."""
+        s_ = torch.cuda.current_stream(dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a_, b_ in ev:
+            torch.amax(flush_buf, dim=0, out=flush_sink)
+            a_.record(s_)
+            fn()
+            b_.record(s_)
+        torch.cuda.synchronize()
+        t = np.array([a_.elapsed_time(b_) * 1e3 for a_, b_ in ev])
+        return float(np.median(t)), float(t.min()), float(np.percentile(t, 90))
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -361,6 +379,12 @@ def main() -> int:
     st_dn = timed(graph_of(down, inner), max(4, args.steps // 2), inner)
     st_q = timed(graph_of(quant, inner), max(4, args.steps // 2), inner) if args.mx else None
     us_align, us_gu, us_dn = st_align[0], st_gu[0], st_dn[0]
+    flush_buf = torch.zeros(1 << 28, dtype=torch.int32, device=dev)
+    flush_sink = torch.zeros((), dtype=torch.int32, device=dev)
+    cold_reps = 20
+    st_cold = {"align": cold(align, cold_reps), "gate_up": cold(gate_up, cold_reps),
+               "down_combine": cold(down, cold_reps)}
+    del flush_buf, flush_sink
 
     # host cost of choosing a config (first call runs the sampled search,
     # later calls hit the memoised result) and of one launch (binding +
@@ -445,6 +469,8 @@ def main() -> int:
                    "experts_touched": touched, "num_tokens_padded": n_ntp},
         "per_call_stats_us": {name: {"median": round(v[1], 2), "min": round(v[2], 2), "p90": round(v[3], 2)}
                               for name, v in (("align", st_align), ("gate_up", st_gu), ("down_combine", st_dn))},
+        "per_call_cold_us": {name: {"median": round(v[0], 2), "min": round(v[1], 2), "p90": round(v[2], 2)}
+                             for name, v in st_cold.items()},
         "host_us": {"select_first_call": round(host_select_first, 1), "select_memoised": round(host_select_memo, 2),
                     "gate_up_launch": round(host_launch, 1)},
         "per_call_us": {"align": round(us_align, 2), "gate_up": round(us_gu, 2),
