@@ -218,7 +218,9 @@ def main() -> int:
     d_ids = torch.from_numpy(ids).to(dev)
     d_w = torch.from_numpy(wts).to(dev)
     d_x, d_a = bf(x), bf(a)
-    cfg = M.select(sh.T, sh.topk, sh.E_glob, sh.E_loc, sh.N1, sh.K1)
+    # the selector decides block_m, which fixes the routing alignment
+    select = M.mxfp4_select if args.mx else M.select
+    cfg = select(sh.T, sh.topk, sh.E_glob, sh.E_loc, sh.N1, sh.K1)
     if args.block_m:
         cfg.block_m = args.block_m
     if args.nr:

@@ -58,7 +58,7 @@ typedef enum {
 const char* w4a16_last_error(void);
 
 /* ABI version of this header (W4A16_ABI_VERSION). */
-#define W4A16_ABI_VERSION 3
+#define W4A16_ABI_VERSION 4
 int32_t w4a16_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -345,6 +345,15 @@ w4a16_status w4a16_mxfp4_pack(const uint8_t* codes, const uint8_t* scales, const
  * Errors: ERR_ARG, ERR_SHAPE, ERR_HIP. */
 w4a16_status w4a16_mxfp4_quant(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
                                w4a16_stream_t stream);
+
+/* Choose a config for the A4W4 GEMM (host only; arguments, memoisation and
+ * environment overrides as w4a16_select): block_m as w4a16_select, except
+ * that where it gives 128 and tokens per expert T * topk / E_glob are at
+ * least 128, 64 (the MXFP4 kernel keeps more waves resident on 64-row
+ * blocks and measured faster there); nr 4, waves 4, one workgroup per
+ * tile, stages 4 for block_m <= 32, else 2.  Errors: ERR_ARG. */
+w4a16_status w4a16_mxfp4_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc,
+                                int32_t N, int32_t K, w4a16_config* out);
 
 /* Bytes of workspace w4a16_mxfp4_moe_gemm needs (the top-k combine's fp32
  * partials; 0 without combine). */

@@ -43,7 +43,7 @@ def test_struct_layouts_match_header():
 
 
 def test_version_and_desc(L):
-    assert L.w4a16_abi_version() == 3
+    assert L.w4a16_abi_version() == 4
     d = W.weight_desc(48, 4096, 7168)
     assert (d.K_pad, d.chunks, d.group) == (7168, 56, 32)
     assert d.w_bytes == 48 * 4096 * 7168 // 2
@@ -139,6 +139,23 @@ def test_gate_up_silu_argument_errors(L):
     assert call(plain, W.config(32, 2)) == -3                            # weight not gate/up packed
     assert call(gated, W.config(32, 2, split_k=0)) == -4                 # one workgroup per tile only
     assert call(gated, W.config(16, 2)) == -3                            # block_m disagrees with routing
+
+
+def test_mxfp4_selector_halves_large_prefill_blocks(L):
+    """A4W4 takes 64-row blocks where the W4A16 rule gives 128 at >= 128 rows
+    per expert, keeps 128 below that, follows the W4A16 block_m elsewhere,
+    and always uses one workgroup per tile with four weight tiles per wave."""
+    pre = W.mxfp4_select(8192, 8, 384, 48, 4096, 7168)          # ~171 rows/expert
+    assert W.select(8192, 8, 384, 48, 4096, 7168).block_m == 128
+    assert (pre.block_m, pre.nr, pre.waves, pre.split_k, pre.stages) == (64, 4, 4, 1, 2)
+    tp = W.mxfp4_select(4096, 8, 384, 384, 512, 7168)           # ~85 rows/expert
+    assert W.select(4096, 8, 384, 384, 512, 7168).block_m == 128 and tp.block_m == 128
+    for args in ((576, 8, 384, 48, 4096, 7168), (16, 8, 384, 384, 512, 7168), (1024, 8, 384, 384, 512, 7168)):
+        c, w = W.mxfp4_select(*args), W.select(*args)
+        assert c.block_m == w.block_m and c.split_k == 1 and c.nr == 4
+        assert c.stages == (4 if c.block_m <= 32 else 2)
+    with pytest.raises(W.W4A16Error):
+        W.mxfp4_select(16, 0, 384, 48, 4096, 7168)
 
 
 def test_selector_follows_tokens_per_expert(L):

@@ -360,6 +360,13 @@ def mxfp4_workspace_bytes(packed: PackedW4, T: int, topk: int, combine: bool) ->
     return int(load().w4a16_mxfp4_moe_gemm_workspace_bytes(ctypes.byref(packed.desc), T, topk, int(bool(combine))))
 
 
+def mxfp4_select(T: int, topk: int, E_glob: int, E_loc: int, N: int, K: int) -> Config:
+    """The library's A4W4 tile choice (block_m decides the routing alignment)."""
+    c = Config()
+    check(load().w4a16_mxfp4_select(T, topk, E_glob, E_loc, N, K, ctypes.byref(c)))
+    return c
+
+
 def mxfp4_config(block_m: int, nr: int = 4, stages: Optional[int] = None) -> Config:
     return config(block_m, nr, waves=4, split_k=1, stages=(4 if block_m <= 32 else 2) if stages is None else stages)
 

@@ -128,9 +128,15 @@ bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm =
 //   - decode side (tok_e < kPrefillTokE): sample per-expert counts, pick the
 //     smallest block_m whose total block count is within 2 % of the minimum
 //     (smaller blocks keep fewer accumulators live and more waves resident);
-//   - prefill side: block_m 128 (largest tile the accumulators allow), 4
-//     weight tiles per wave so each staged activation fragment feeds 4 MFMAs.
+//   - prefill side: block_m 128 (largest tile the accumulators allow), two
+//     weight tiles per wave (measured faster than four at 128 rows).
 constexpr double kPrefillTokE = 48.0;
+// A4W4: above this many rows per expert the MXFP4 GEMM takes 64-row blocks
+// where the W4A16 rule gives 128 (measured on MI355X, step time: EP8 / EP16
+// prefill shares 5 % / 9 % faster at 64; at 85 rows per expert, TP8 T = 4096,
+// 128 stays 6 % faster, since 64 would split most experts into two blocks
+// that each stream the expert's weights).
+constexpr double kMxHalfTileTokE = 128.0;
 
 std::mutex g_cache_mu;
 std::map<std::tuple<int, int, int, int, int, int>, w4a16_config> g_cache;
@@ -341,26 +347,42 @@ w4a16_status w4a16_indexed_config(int32_t block_m, w4a16_config* out) {
   return W4A16_OK;
 }
 
+// select_config, memoised per argument set (no environment overrides)
+w4a16_config cached_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N, int32_t K) {
+  const auto key = std::make_tuple(T, topk, E_glob, E_loc, N, K);
+  {
+    std::lock_guard<std::mutex> g(g_cache_mu);
+    auto it = g_cache.find(key);
+    if (it != g_cache.end()) return it->second;
+  }
+  const w4a16_config c = select_config(T, topk, E_glob, E_loc, N);
+  std::lock_guard<std::mutex> g(g_cache_mu);
+  g_cache[key] = c;
+  return c;
+}
+
 w4a16_status w4a16_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N,
                           int32_t K, w4a16_config* out) {
   if (!out) return fail(W4A16_ERR_ARG, "out is NULL");
   if (T < 0 || topk <= 0 || E_glob <= 0 || E_loc <= 0 || N <= 0 || K <= 0)
     return fail(W4A16_ERR_ARG, "bad sizes for select");
-  const auto key = std::make_tuple(T, topk, E_glob, E_loc, N, K);
-  {
-    std::lock_guard<std::mutex> g(g_cache_mu);
-    auto it = g_cache.find(key);
-    if (it != g_cache.end()) {
-      *out = it->second;
-      apply_env_overrides(out);
-      return W4A16_OK;
-    }
-  }
-  w4a16_config c = select_config(T, topk, E_glob, E_loc, N);
-  {
-    std::lock_guard<std::mutex> g(g_cache_mu);
-    g_cache[key] = c;
-  }
+  *out = cached_select(T, topk, E_glob, E_loc, N, K);
+  apply_env_overrides(out);
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_mxfp4_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N,
+                                int32_t K, w4a16_config* out) {
+  if (!out) return fail(W4A16_ERR_ARG, "out is NULL");
+  if (T < 0 || topk <= 0 || E_glob <= 0 || E_loc <= 0 || N <= 0 || K <= 0)
+    return fail(W4A16_ERR_ARG, "bad sizes for select");
+  w4a16_config c = cached_select(T, topk, E_glob, E_loc, N, K);
+  const double tok_e = (double)T * topk / E_glob;
+  if (c.block_m == 128 && tok_e >= kMxHalfTileTokE) c.block_m = 64;
+  c.nr = 4;
+  c.waves = 4;
+  c.split_k = 1;
+  c.stages = c.block_m <= 32 ? 4 : 2;
   *out = c;
   apply_env_overrides(out);
   return W4A16_OK;
