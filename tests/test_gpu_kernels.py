@@ -63,6 +63,26 @@ def test_align_edge_cases():
         _align_case(g.integers(0, 1000, (4099, 5)).astype(np.int32), 1000, 1000 - E_loc, E_loc, 32)
 
 
+def test_align_several_workgroups_bit_exact():
+    """From 16,384 slots the align splits its scatter over several
+    workgroups (each counts every slot): slot counts on both sides of that
+    switch and ending mid-tile, one to 777 local experts (ballot matching
+    above 512), out-of-range ids, skewed routing, every block_m."""
+    g = np.random.default_rng(3)
+    cases = [(2048, 8, 64, 0, 64, 16), (2048, 8, 64, 0, 64, 128),       # 16,384: one workgroup
+             (2049, 8, 64, 8, 40, 32),                                  # 16,392: three
+             (4099, 5, 1000, 223, 777, 64),                             # 20,495 slots, 777 experts
+             (8191, 8, 384, 0, 48, 128), (12000, 8, 96, 5, 1, 16)]      # up to 96,000 slots, one expert
+    for T, k, E_glob, first, E_loc, bm in cases:
+        ids = g.integers(-1, E_glob + 1, (T, k)).astype(np.int32)       # -1 and E_glob are not local
+        _align_case(ids, E_glob, first, E_loc, bm)
+    # skewed: most slots on a few experts
+    p = 1.0 / np.arange(1, 65) ** 1.5
+    ids = g.choice(64, size=(9000, 4), p=p / p.sum()).astype(np.int32)
+    for bm in (16, 64, 128):
+        _align_case(ids, 64, 0, 64, bm)
+
+
 @pytest.mark.parametrize("name", ["ep8_decode", "ep8_prefill", "tp8_t1", "tp8_t4096", "grouped_skewed"])
 def test_align_bit_exact_workloads(name):
     sh = W.WORKLOADS[name]

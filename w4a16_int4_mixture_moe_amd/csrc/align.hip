@@ -8,33 +8,49 @@
 // to the host and the call stays graph-capturable; section "Grouped SM90
 // kernels", Figure 3: indexed routing puts its padding in sentinel indices.
 //
-// One workgroup of 16 or 8 waves.  Wave w owns a contiguous range of slots, so the
-// order of slots inside an expert segment is ascending by construction:
-//   pass 1  each wave counts its slots per expert (LDS atomics), 16 loads in
-//           flight per lane (one workgroup has to keep many requests out to
-//           read the ids at more than a trickle);
-//   scan    per expert, exclusive prefix over waves, then an exclusive scan of
-//           the padded expert totals gives segment starts;
+// G workgroups of 16 or 8 waves (G = 1 below kAlignMultiMin slots).
+// Workgroup g owns a contiguous chunk of the slots and wave w a contiguous
+// range of that chunk, so the order of slots inside an expert segment is
+// ascending by construction:
+//   pass 1  every workgroup counts all slots per expert (LDS atomics, 16
+//           loads in flight per lane; past the first workgroup the ids come
+//           from L2): its own waves' slots per wave, the slots of earlier and
+//           later chunks in two totals, so each workgroup knows every
+//           segment and where its own slots start in each, with no
+//           communication between workgroups;
+//   scan    per expert, exclusive prefix over earlier chunks and waves, then
+//           an exclusive scan of the padded expert totals gives segment
+//           starts;
 //   fill    sentinels inside segment tails and after the padded total,
-//           expert_ids per block, the padded total itself;
+//           expert_ids per block, the padded total itself (experts and tail
+//           positions dealt round robin over the workgroups);
 //   pass 2  each wave walks its range 64 slots at a time; lanes routed to the
 //           same expert find each other (a per-wave table of lane masks in
 //           LDS, or one ballot per expert-id bit), take consecutive
 //           positions in lane order, and the group's lowest lane advances
 //           the wave's cursor for that expert.
+// With G workgroups the scatter and fill are split G ways; the count is not
+// (every workgroup reads all ids), which is what bounds a large align.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace w4a16 {
 
 constexpr int kAlignBatch = 16;                // slot ids in flight per lane
+constexpr int kAlignMultiMin = 16384;          // slots from which several workgroups share the work
+constexpr int kAlignSlotsPerGroup = 2048;
+constexpr int kAlignMaxGroups = 64;
 
 // kAlignWaves waves: 16, or 8 when the per-wave tables of many experts would
 // not fit the default LDS allocation.  kMaskMatch: pass 2 finds the lanes of
 // a sub-tile routed to the same expert through a per-wave table of 64-bit
 // lane masks in LDS (one atomic OR per lane, one read back); otherwise with
 // one ballot per expert-id bit (no table; for more than 512 local experts).
-template <int kAlignWaves, bool kMaskMatch>
+// kMulti: launched as several workgroups (otherwise exactly one, and the
+// chunk bookkeeping compiles away).
+template <int kAlignWaves, bool kMaskMatch, bool kMulti>
 __global__ __launch_bounds__(kAlignWaves * kWave) void align_kernel(
     const int32_t* __restrict__ topk_ids, int32_t total, int32_t first, int32_t E_loc,
     int32_t bm, int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
@@ -47,46 +63,83 @@ __global__ __launch_bounds__(kAlignWaves * kWave) void align_kernel(
                                               // [kAlignWaves][E_loc]: counts, then cursors
   int* seg = cnt + kAlignWaves * E_loc;       // [E_loc + 1]: padded segment starts
   int* num = seg + E_loc + 1;                 // [E_loc]: slots per expert
+  int* pre = num + E_loc;                     // [E_loc]: slots of earlier chunks
+  int* post = pre + E_loc;                    // [E_loc]: slots of later chunks
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = tid / kWave;
+  const int G = kMulti ? (int)gridDim.x : 1;
+  const int g = kMulti ? (int)blockIdx.x : 0;
 
   for (int i = tid; i < kAlignWaves * E_loc; i += kAlignThreads) {
     cnt[i] = 0;
     if constexpr (kMaskMatch) lanes_of[i] = 0ull;
   }
+  if constexpr (kMulti)
+    for (int e = tid; e < E_loc; e += kAlignThreads) {
+      pre[e] = 0;
+      post[e] = 0;
+    }
   __syncthreads();
 
-  const int per = ((total + kAlignWaves - 1) / kAlignWaves + kWave - 1) & ~(kWave - 1);
-  const int beg = min(w * per, total);
-  const int end = min(beg + per, total);
+  // this workgroup's chunk and this wave's range of it (multiples of 64
+  // slots, so a 64-slot tile never straddles two owners)
+  const int chunk = ((total + G - 1) / G + kWave - 1) & ~(kWave - 1);
+  const int cbeg = min(g * chunk, total);
+  const int cend = min(cbeg + chunk, total);
+  const int per = ((cend - cbeg + kAlignWaves - 1) / kAlignWaves + kWave - 1) & ~(kWave - 1);
+  const int beg = min(cbeg + w * per, cend);
+  const int end = min(beg + per, cend);
 
-  // pass 1: per-wave expert histogram
-  for (int s0 = beg; s0 < end; s0 += kAlignBatch * kWave) {
-    int id[kAlignBatch];
+  // pass 1: expert histogram
+  if constexpr (!kMulti) {
+    // one workgroup: each wave counts its own range
+    for (int s0 = beg; s0 < end; s0 += kAlignBatch * kWave) {
+      int id[kAlignBatch];
 #pragma unroll
-    for (int u = 0; u < kAlignBatch; ++u) {
-      const int s = s0 + u * kWave + lane;
-      id[u] = s < end ? topk_ids[s] : -1;
+      for (int u = 0; u < kAlignBatch; ++u) {
+        const int s = s0 + u * kWave + lane;
+        id[u] = s < end ? topk_ids[s] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kAlignBatch; ++u) {
+        const int e = id[u] - first;
+        if (id[u] >= 0 && (unsigned)e < (unsigned)E_loc) atomicAdd(&cnt[w * E_loc + e], 1);
+      }
     }
+  } else {
+    // all slots, tile by tile (64 slots each), counted for the owning wave
+    // of this workgroup or as earlier / later chunks
+    const int ntiles = (total + kWave - 1) / kWave;
+    for (int t0 = w * kAlignBatch; t0 < ntiles; t0 += kAlignWaves * kAlignBatch) {
+      int id[kAlignBatch];
 #pragma unroll
-    for (int u = 0; u < kAlignBatch; ++u) {
-      const int e = id[u] - first;
-      if (id[u] >= 0 && (unsigned)e < (unsigned)E_loc) atomicAdd(&cnt[w * E_loc + e], 1);
+      for (int u = 0; u < kAlignBatch; ++u) {
+        const int s = (t0 + u) * kWave + lane;
+        id[u] = s < total ? topk_ids[s] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kAlignBatch; ++u) {
+        const int tb = (t0 + u) * kWave;                      // wave-uniform
+        int* dst = tb < cbeg ? pre : tb >= cend ? post : cnt + ((tb - cbeg) / max(per, kWave)) * E_loc;
+        const int e = id[u] - first;
+        if (id[u] >= 0 && (unsigned)e < (unsigned)E_loc) atomicAdd(&dst[e], 1);
+      }
     }
   }
   __syncthreads();
 
-  // per expert: exclusive prefix over waves, total count
+  // per expert: exclusive prefix over earlier chunks and this chunk's
+  // waves, total count
   for (int e = tid; e < E_loc; e += kAlignThreads) {
-    int run = 0;
+    int run = kMulti ? pre[e] : 0;
     for (int v = 0; v < kAlignWaves; ++v) {
       const int c = cnt[v * E_loc + e];
       cnt[v * E_loc + e] = run;
       run += c;
     }
-    num[e] = run;
+    num[e] = kMulti ? run + post[e] : run;
   }
   __syncthreads();
 
@@ -114,14 +167,16 @@ __global__ __launch_bounds__(kAlignWaves * kWave) void align_kernel(
   const int ntp = seg[E_loc];
   const int sentinel = total;
   for (int i = tid; i < kAlignWaves * E_loc; i += kAlignThreads) cnt[i] += seg[i % E_loc];
-  for (int e = tid; e < E_loc; e += kAlignThreads) {
+  for (int e = g + G * tid; e < E_loc; e += G * kAlignThreads) {
     const int o = seg[e], n = num[e], o_end = seg[e + 1];
     for (int q = o + n; q < o_end; ++q) sorted_ids[q] = sentinel;
     for (int b = o / bm; b < o_end / bm; ++b) expert_ids[b] = e;
   }
-  for (int64_t q = ntp + tid; q < capacity; q += kAlignThreads) sorted_ids[q] = sentinel;
-  for (int64_t b = ntp / bm + tid; b < capacity / bm; b += kAlignThreads) expert_ids[b] = -1;
-  if (tid == 0) *ntp_out = ntp;
+  const int64_t stride = (int64_t)G * kAlignThreads;
+  const int64_t first_q = (int64_t)g * kAlignThreads + tid;
+  for (int64_t q = ntp + first_q; q < capacity; q += stride) sorted_ids[q] = sentinel;
+  for (int64_t b = ntp / bm + first_q; b < capacity / bm; b += stride) expert_ids[b] = -1;
+  if (g == 0 && tid == 0) *ntp_out = ntp;
   __syncthreads();
 
   // pass 2: stable scatter
@@ -178,21 +233,29 @@ __global__ __launch_bounds__(kAlignWaves * kWave) void align_kernel(
 hipError_t launch_align(const int32_t* topk_ids, int32_t total_slots, int32_t first, int32_t E_loc,
                         int32_t block_m, int32_t* sorted_ids, int32_t* expert_ids,
                         int32_t* num_tokens_padded, int64_t capacity, hipStream_t stream) {
-  // LDS: lane masks 8 B and counters 4 B per (wave, expert), plus 8 B per
-  // expert: <= 27 KB (16 waves, <= 128 experts), <= 53 KB (8 waves, <= 512),
-  // <= 41 KB (8 waves, ballot matching, <= 1024)
+  // LDS: lane masks 8 B and counters 4 B per (wave, expert), plus 16 B per
+  // expert: <= 27 KB (16 waves, <= 128 experts), <= 54 KB (8 waves, <= 512),
+  // <= 45 KB (8 waves, ballot matching, <= 1024)
   auto lds = [&](int waves, bool masks) {
-    return (masks ? 8 * (size_t)waves * E_loc : 0) + sizeof(int) * ((size_t)waves * E_loc + 2 * (size_t)E_loc + 1);
+    return (masks ? 8 * (size_t)waves * E_loc : 0) + sizeof(int) * ((size_t)waves * E_loc + 4 * (size_t)E_loc + 1);
   };
+  // one workgroup up to kAlignMultiMin slots (its count and scatter are
+  // latency-bound, and more workgroups would each count everything again),
+  // then one per kAlignSlotsPerGroup slots
+  const int groups = total_slots < kAlignMultiMin
+                         ? 1
+                         : std::min(kAlignMaxGroups, (total_slots + kAlignSlotsPerGroup - 1) / kAlignSlotsPerGroup);
+  auto go = [&](auto kernel, int waves, bool masks) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)groups), dim3(waves * kWave), lds(waves, masks), stream, topk_ids,
+                       total_slots, first, E_loc, block_m, sorted_ids, expert_ids, num_tokens_padded, capacity);
+  };
+  const bool multi = groups > 1;
   if (E_loc <= 128)
-    hipLaunchKernelGGL((align_kernel<16, true>), dim3(1), dim3(16 * kWave), lds(16, true), stream, topk_ids,
-                       total_slots, first, E_loc, block_m, sorted_ids, expert_ids, num_tokens_padded, capacity);
+    multi ? go(align_kernel<16, true, true>, 16, true) : go(align_kernel<16, true, false>, 16, true);
   else if (E_loc <= 512)
-    hipLaunchKernelGGL((align_kernel<8, true>), dim3(1), dim3(8 * kWave), lds(8, true), stream, topk_ids,
-                       total_slots, first, E_loc, block_m, sorted_ids, expert_ids, num_tokens_padded, capacity);
+    multi ? go(align_kernel<8, true, true>, 8, true) : go(align_kernel<8, true, false>, 8, true);
   else
-    hipLaunchKernelGGL((align_kernel<8, false>), dim3(1), dim3(8 * kWave), lds(8, false), stream, topk_ids,
-                       total_slots, first, E_loc, block_m, sorted_ids, expert_ids, num_tokens_padded, capacity);
+    multi ? go(align_kernel<8, false, true>, 8, false) : go(align_kernel<8, false, false>, 8, false);
   return hipGetLastError();
 }
 
