@@ -163,6 +163,7 @@ def test_selector_follows_tokens_per_expert(L):
     assert dec.block_m == 32 and dec.nr == 2
     one = W.select(16, 8, 384, 384, 512, 7168)             # ~0.3 rows/expert
     assert one.block_m == 16
+    assert dec.split_k == 1 and one.split_k == 1            # stream-K only when asked for
     pre = W.select(8192, 8, 384, 48, 4096, 7168)           # ~171 rows/expert
     assert pre.block_m == 128 and pre.nr == 2
     # tok_e, not total tokens: same T, 8x more experts -> decode side

@@ -176,15 +176,14 @@ w4a16_config select_config(int32_t T, int32_t topk, int32_t E_glob, int32_t E_lo
       }
     c.nr = 2;
   }
-  // Stream-K only when the tile grid would leave most resident workgroups
-  // idle (the post keeps stream-K where the plain grid under-fills the
-  // machine, section "H200 prefill and TP8").  Measured on MI355X: stream-K
-  // wins clearly below half a round of resident workgroups (TP8 at small T),
-  // ties around 0.4 (EP32 decode) and loses at 0.75 (EP16 decode, about 10 %,
-  // mostly its fix-up pass), so the gate is half a round.
-  const int64_t tiles = sampled_blocks(counts, c.block_m) * ((N / 16 + 4 * c.nr - 1) / (4 * c.nr));
-  const int resident = resident_workgroups(c, w4a16::kEpiStore);
-  if (resident > 0 && 2 * tiles < resident) c.split_k = 0;
+  // One workgroup per tile throughout.  Stream-K (split_k = 0) stays
+  // available as an explicit config; the post gates it by shape (section
+  // "H200 prefill and TP8"), but measured on MI355X against the current
+  // one-workgroup kernel it no longer wins anywhere on the step: TP8 T = 1
+  // 0.051 vs 0.059 ms, TP8 T = 16 0.095 vs 0.118, EP32 decode 0.089 vs
+  // 0.104 (one workgroup per tile first), the down projection losing most
+  // (its fix-up pass and per-segment pipeline restarts against K = 256 or
+  // 2048).
   return c;
 }
 
