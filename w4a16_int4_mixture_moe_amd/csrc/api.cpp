@@ -149,7 +149,7 @@ int64_t sampled_blocks(const std::vector<int>& counts, int bm) {
 
 int resident_workgroups(const w4a16_config& c, int epi);
 
-w4a16_config select_config(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N) {
+w4a16_config select_config(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc) {
   w4a16_config c;
   c.waves = 4;
   c.split_k = 1;
@@ -346,7 +346,8 @@ w4a16_status w4a16_indexed_config(int32_t block_m, w4a16_config* out) {
   return W4A16_OK;
 }
 
-// select_config, memoised per argument set (no environment overrides)
+// select_config, memoised per argument set of the public call (no
+// environment overrides)
 w4a16_config cached_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N, int32_t K) {
   const auto key = std::make_tuple(T, topk, E_glob, E_loc, N, K);
   {
@@ -354,7 +355,7 @@ w4a16_config cached_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_lo
     auto it = g_cache.find(key);
     if (it != g_cache.end()) return it->second;
   }
-  const w4a16_config c = select_config(T, topk, E_glob, E_loc, N);
+  const w4a16_config c = select_config(T, topk, E_glob, E_loc);
   std::lock_guard<std::mutex> g(g_cache_mu);
   g_cache[key] = c;
   return c;
