@@ -294,12 +294,13 @@ def main() -> int:
             M.moe_w4a16_gemm(d_a, p2, routing, topk_weights=d_w, cfg=cfg, out=y, workspace=ws2)
 
     def quant():
-        # A4W4: the activation rows to MXFP4 (unfused: also the step's
-        # synthetic per-slot down input; fused: the gate/up epilogue
-        # quantises the down input itself)
+        # A4W4: the activation rows to MXFP4 (unfused: also the rows of the
+        # step's synthetic per-slot down input that the down GEMM reads, those
+        # of local slots; fused: the gate/up epilogue quantises the down input
+        # itself)
         M.mxfp4_quant(d_x, out=qx)
         if not args.fused:
-            M.mxfp4_quant(d_a, out=qa)
+            M.mxfp4_quant_local_slots(d_a, routing, out=qa)
 
     def step():
         align()
@@ -307,7 +308,7 @@ def main() -> int:
             M.mxfp4_quant(d_x, out=qx)
         gate_up()
         if args.mx and not args.fused:
-            M.mxfp4_quant(d_a, out=qa)
+            M.mxfp4_quant_local_slots(d_a, routing, out=qa)
         down()
 
     def graph_of(fn, n):

@@ -346,6 +346,17 @@ w4a16_status w4a16_mxfp4_pack(const uint8_t* codes, const uint8_t* scales, const
 w4a16_status w4a16_mxfp4_quant(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
                                w4a16_stream_t stream);
 
+/* w4a16_mxfp4_quant on the per-slot rows x [T * topk][K] (the down
+ * projection's input, row s = slot s = t * topk + j), converting only the
+ * rows of slots routed to a local expert (first_expert <= topk_ids[s] <
+ * first_expert + E_loc); the codes and scales of other rows are left as they
+ * are.  These are the rows w4a16_mxfp4_moe_gemm with W4A16_A_SLOT reads.
+ * topk_ids: device int32 [T][topk].  Errors as w4a16_mxfp4_quant, and
+ * ERR_ARG for topk <= 0, E_loc <= 0 or a NULL topk_ids. */
+w4a16_status w4a16_mxfp4_quant_local_slots(const uint16_t* x, const int32_t* topk_ids, int32_t T, int32_t topk,
+                                           int32_t first_expert, int32_t E_loc, int32_t K, uint8_t* codes,
+                                           uint8_t* scales, w4a16_stream_t stream);
+
 /* Choose a config for the A4W4 GEMM (host only; arguments, memoisation and
  * environment overrides as w4a16_select): block_m as w4a16_select, except
  * that where it gives 128 and tokens per expert T * topk / E_glob are at

@@ -207,6 +207,12 @@ def test_mxfp4_descriptor_and_errors(L):
     assert L.w4a16_mxfp4_moe_gemm_workspace_bytes(ctypes.byref(mx), 10, 8, 1) == 10 * 8 * 64 * 4
     assert L.w4a16_mxfp4_quant(P, 4, 48, P, P, None) == -2               # K % 32
     assert L.w4a16_mxfp4_quant(P + 4, 4, 64, P, P, None) == -1           # misaligned rows
+    q = L.w4a16_mxfp4_quant_local_slots
+    assert q(P, None, 4, 8, 0, 48, 64, P, P, None) == -1                 # topk_ids NULL
+    assert q(P, P, 4, 8, 0, 48, 48, P, P, None) == -2                    # K % 32
+    assert q(P, P, 4, 0, 0, 48, 64, P, P, None) == -1                    # topk 0
+    assert q(P, P, 4, 8, 0, 0, 64, P, P, None) == -1                     # no local experts
+    assert q(None, None, 0, 8, 0, 48, 64, None, None, None) == 0         # no tokens: nothing to do
 
 
 def test_mxfp4_gate_up_silu_errors(L):

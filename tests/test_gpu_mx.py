@@ -19,7 +19,7 @@ import torch
 from oracle import moe_oracle as O
 from oracle import mx_oracle as X
 from synth import workloads as W
-from tests.gpu_util import assert_close, bits, log, to_dev, to_dev_bf16
+from tests.gpu_util import assert_close, bits, dev, log, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +76,27 @@ def test_mx_quant_bit_exact(K):
     np.testing.assert_array_equal(gs, os_)
     np.testing.assert_array_equal(gc, oc)
     log(f"mx quant K={K}: {R} rows bit-exact")
+
+
+def test_mx_quant_local_slots_converts_exactly_the_local_rows():
+    """Per-slot rows: local slots' rows equal the oracle's conversion bit for
+    bit; the rows of other slots (non-local ids, -1) keep their old bytes."""
+    rng = np.random.default_rng(11)
+    T, k, K, E_glob, first, E_loc = 37, 4, 256, 16, 5, 6
+    ids = rng.integers(-1, E_glob, (T, k)).astype(np.int32)
+    x = W.to_bf16_bits(rng.standard_normal((T * k, K)).astype(np.float32))
+    r = M.moe_align(to_dev(ids), E_glob, first, E_loc, 16)
+    out = M.MXRows(torch.full((T * k, K // 2), 0xA5, dtype=torch.uint8, device=dev()),
+                   torch.full((T * k, K // 32), 0x5A, dtype=torch.uint8, device=dev()))
+    M.mxfp4_quant_local_slots(to_dev_bf16(x), r, out=out)
+    torch.cuda.synchronize()
+    gc, gs = X.unpack_nibbles(out.codes.cpu().numpy()), out.scales.cpu().numpy()
+    local = ((ids >= first) & (ids < first + E_loc)).reshape(-1)
+    oc, os_ = X.mx_quantize(x[local])
+    np.testing.assert_array_equal(gc[local], oc)
+    np.testing.assert_array_equal(gs[local], os_)
+    assert (out.codes.cpu().numpy()[~local] == 0xA5).all() and (gs[~local] == 0x5A).all()
+    log(f"mx local-slot quant: {int(local.sum())} of {T * k} rows converted, others untouched")
 
 
 # ------------------------------------------------------------ GEMM

@@ -90,6 +90,7 @@ SIGNATURES = {
                                         ctypes.POINTER(IndexedRouting), _P, _P, ctypes.POINTER(Config), _P]),
     "w4a16_mxfp4_pack": (_I32, [_P, _P, ctypes.POINTER(WeightDesc), _P, _P, _P]),
     "w4a16_mxfp4_quant": (_I32, [_P, _I64, _I32, _P, _P, _P]),
+    "w4a16_mxfp4_quant_local_slots": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "w4a16_mxfp4_moe_gemm_workspace_bytes": (_SZ, [ctypes.POINTER(WeightDesc), _I32, _I32, _I32]),
     "w4a16_mxfp4_moe_gemm": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _P, _I64, _I32,
                                     ctypes.POINTER(IndexedRouting), _P, _P, ctypes.POINTER(Config),

@@ -355,6 +355,26 @@ def mxfp4_quant(x: torch.Tensor, out: Optional[MXRows] = None) -> MXRows:
     return out
 
 
+def mxfp4_quant_local_slots(x: torch.Tensor, routing: Routing, out: Optional[MXRows] = None) -> MXRows:
+    """mxfp4_quant on per-slot rows x [T * topk, K], converting only the rows
+    of slots routed to the routing's local experts (the rows the down GEMM
+    reads); other rows of `out` are left as they are."""
+    _need(x, "x", _BF16, 2)
+    R, K = x.shape
+    T, k = routing.T, routing.topk
+    if R != T * k:
+        raise ValueError(f"x must hold T * topk = {T * k} rows")
+    if out is None:
+        out = MXRows(torch.empty(R, K // 2, dtype=torch.uint8, device=x.device),
+                     torch.empty(R, K // 32, dtype=torch.uint8, device=x.device))
+    elif out.rows < R or out.K != K:
+        raise ValueError(f"out must hold [{R}, {K}] MXFP4 rows")
+    check(load().w4a16_mxfp4_quant_local_slots(x.data_ptr(), routing.topk_ids.data_ptr(), T, k,
+                                               routing.first_expert, routing.E_loc, K, out.codes.data_ptr(),
+                                               out.scales.data_ptr(), _stream(x.device)))
+    return out
+
+
 def mxfp4_workspace_bytes(packed: PackedW4, T: int, topk: int, combine: bool) -> int:
     """Workspace moe_mxfp4_gemm needs (the top-k combine's fp32 partials)."""
     return int(load().w4a16_mxfp4_moe_gemm_workspace_bytes(ctypes.byref(packed.desc), T, topk, int(bool(combine))))

@@ -632,8 +632,23 @@ w4a16_status w4a16_mxfp4_quant(const uint16_t* x, int64_t rows, int32_t K, uint8
   if (rows == 0) return W4A16_OK;
   if (!x || !codes || !scales) return fail(W4A16_ERR_ARG, "NULL pointer argument");
   if (!aligned16(x) || !aligned16(codes)) return fail(W4A16_ERR_ARG, "x and codes must be 16-byte aligned");
-  hipError_t e = w4a16::launch_mx_quant(x, rows, K, codes, scales, static_cast<hipStream_t>(stream));
+  hipError_t e = w4a16::launch_mx_quant(x, rows, K, codes, scales, nullptr, 0, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mxfp4_quant launch");
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_mxfp4_quant_local_slots(const uint16_t* x, const int32_t* topk_ids, int32_t T, int32_t topk,
+                                           int32_t first_expert, int32_t E_loc, int32_t K, uint8_t* codes,
+                                           uint8_t* scales, w4a16_stream_t stream) {
+  if (T < 0 || topk <= 0 || E_loc <= 0 || K <= 0)
+    return fail(W4A16_ERR_ARG, "bad sizes T=%d topk=%d E_loc=%d K=%d", T, topk, E_loc, K);
+  if (K % 32) return fail(W4A16_ERR_SHAPE, "K = %d is not a multiple of the MX block 32", K);
+  if (T == 0) return W4A16_OK;
+  if (!x || !topk_ids || !codes || !scales) return fail(W4A16_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(x) || !aligned16(codes)) return fail(W4A16_ERR_ARG, "x and codes must be 16-byte aligned");
+  hipError_t e = w4a16::launch_mx_quant(x, (int64_t)T * topk, K, codes, scales, topk_ids, first_expert, E_loc,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mxfp4_quant_local_slots launch");
   return W4A16_OK;
 }
 

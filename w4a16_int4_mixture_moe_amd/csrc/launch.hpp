@@ -82,9 +82,10 @@ hipError_t launch_combine(const float* partial, const int32_t* topk_ids, int32_t
 
 // ---- A4W4: MXFP4 activations x MXFP4 weights (mx.hip)
 // bf16 [rows][K] -> E2M1 codes [rows][K/2] (two per byte, low nibble first)
-// and E8M0 scales [rows][K/32]; K % 32 == 0.
+// and E8M0 scales [rows][K/32]; K % 32 == 0.  slot_ids != NULL: only rows r
+// with first <= slot_ids[r] < first + E_loc are converted.
 hipError_t launch_mx_quant(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
-                           hipStream_t stream);
+                           const int32_t* slot_ids, int32_t first, int32_t E_loc, hipStream_t stream);
 // codes [E][N][K/2] + scales [E][N][K/32] -> packed [E][N/16][K/128][64]
 // 16-byte fragments + [E][N/16][K/128][64] scale bytes; K % 128 == 0.
 // gate_up: tiles of the gate rows [0, N/2) and up rows [N/2, N) alternate.

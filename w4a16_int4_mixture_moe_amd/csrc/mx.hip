@@ -38,13 +38,18 @@ namespace w4a16 {
 // ------------------------------------------------------------ quantisation
 
 // One thread per 32-element block: 64 bytes of bf16 in, 16 bytes of codes
-// and one scale byte out.
+// and one scale byte out.  slot_ids != NULL: row r is routed slot r and is
+// converted only when slot_ids[r] names a local expert (first <= id <
+// first + E_loc); other rows are left as they are.
 __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restrict__ x, int64_t blocks,
                                                         int32_t kb, uint8_t* __restrict__ codes,
-                                                        uint8_t* __restrict__ scales) {
+                                                        uint8_t* __restrict__ scales,
+                                                        const int32_t* __restrict__ slot_ids, int32_t first,
+                                                        int32_t E_loc) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= blocks) return;
   const int64_t row = i / kb;
+  if (slot_ids != nullptr && (unsigned)(slot_ids[row] - first) >= (unsigned)E_loc) return;
   const int b = (int)(i - row * kb);
   const uint4* src = reinterpret_cast<const uint4*>(x + row * (int64_t)kb * 32 + b * 32);
   uint32_t v[16];
@@ -92,13 +97,13 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
 }
 
 hipError_t launch_mx_quant(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
-                           hipStream_t stream) {
+                           const int32_t* slot_ids, int32_t first, int32_t E_loc, hipStream_t stream) {
   const int64_t blocks = rows * (K / 32);
   if (blocks == 0) return hipSuccess;
   const int64_t grid = (blocks + 255) / 256;
   if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, blocks, K / 32, codes,
-                     scales);
+                     scales, slot_ids, first, E_loc);
   return hipGetLastError();
 }
 
