@@ -42,6 +42,46 @@ def test_struct_layouts_match_header():
     assert _lib.IndexedRouting.capacity.offset == 24
 
 
+def test_header_compiles_as_c_and_matches_the_binding(tmp_path):
+    """The header is plain C (gcc -std=c99 -Wall -Werror), and the struct
+    sizes and field offsets the C compiler gives agree with the ctypes
+    mirrors the binding passes to the library, as do the constants."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"w4a16_weight_desc": _lib.WeightDesc, "w4a16_config": _lib.Config,
+               "w4a16_indexed_routing": _lib.IndexedRouting}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "w4a16_moe.h"', "int main(void) {"]
+    for cname, ct in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in ct._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    for const in ("W4A16_ABI_VERSION", "W4A16_DESC_GATE_UP", "W4A16_DESC_MXFP4", "W4A16_A_TOKEN", "W4A16_A_SLOT",
+                  "W4A16_A_SORTED"):
+        lines.append(f'  printf("const {const} %d\\n", (int)({const}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True, capture_output=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        *key, val = line.split()
+        got[tuple(key)] = int(val)
+    for cname, ct in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(ct), cname
+        for f, _ in ct._fields_:
+            assert got[(cname, f)] == getattr(ct, f).offset, (cname, f)
+    assert got[("const", "W4A16_DESC_GATE_UP")] == _lib.DESC_GATE_UP
+    assert got[("const", "W4A16_DESC_MXFP4")] == _lib.DESC_MXFP4
+    assert (got[("const", "W4A16_A_TOKEN")], got[("const", "W4A16_A_SLOT")],
+            got[("const", "W4A16_A_SORTED")]) == (_lib.A_TOKEN, _lib.A_SLOT, _lib.A_SORTED)
+    assert got[("const", "W4A16_ABI_VERSION")] == 4
+
+
 def test_version_and_desc(L):
     assert L.w4a16_abi_version() == 4
     d = W.weight_desc(48, 4096, 7168)
