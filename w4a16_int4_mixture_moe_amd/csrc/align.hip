@@ -234,8 +234,8 @@ hipError_t launch_align(const int32_t* topk_ids, int32_t total_slots, int32_t fi
                         int32_t block_m, int32_t* sorted_ids, int32_t* expert_ids,
                         int32_t* num_tokens_padded, int64_t capacity, hipStream_t stream) {
   // LDS: lane masks 8 B and counters 4 B per (wave, expert), plus 16 B per
-  // expert: <= 26 KiB (16 waves, <= 128 experts), <= 56 KiB (8 waves, <= 512),
-  // <= 48 KiB (8 waves, ballot matching, <= 1024)
+  // expert: 26 KiB + 4 B at most (16 waves, <= 128 experts), 56 KiB + 4 B (8 waves,
+  // <= 512), 48 KiB + 4 B (8 waves, ballot matching, <= 1024)
   auto lds = [&](int waves, bool masks) {
     return (masks ? 8 * (size_t)waves * E_loc : 0) + sizeof(int) * ((size_t)waves * E_loc + 4 * (size_t)E_loc + 1);
   };
