@@ -48,8 +48,9 @@
 //   masked      block b -> (group g, rows r0..r0+BM) of A[g]; rows at or past
 //               masked_m[g] skipped; output row g*max_m + r.
 // Epilogues: bf16 store (round to nearest even) or, for the top-k combine,
-// fp32 partial = topk_weight(slot) * acc stored per slot; launch_combine then
-// sums a token's local slots in j order and rounds once.
+// fp32 partial = topk_weight(slot) * acc stored per slot (staged through LDS
+// so whole rows are written at once, when the tile is at most 128 columns);
+// launch_combine then sums a token's local slots in j order and rounds once.
 #include <algorithm>
 #include <type_traits>
 
@@ -374,6 +375,45 @@ __device__ __forceinline__ float4* partial_slot(const GemmParams& p, int64_t slo
   return reinterpret_cast<float4*>(p.sk_partial) + slot * (int64_t)(NR * MT * NTHR);
 }
 
+// Weighted epilogue through LDS: the tile's fp32 partials (times the slot's
+// top-k weight) are first placed in the idle activation buffers, rows padded
+// by 16 bytes, then written row by row, each wave storing two 512-byte row
+// runs per instruction instead of sixteen 64-byte pieces.
+template <int MT, int NR, int NW>
+__device__ __forceinline__ void epilogue_weighted_staged(const GemmParams& p, TileSmem<MT>& sm, int nt,
+                                                         uint32_t tmask, const f32x4_t (&acc)[NR][MT]) {
+  constexpr int BN = 16 * NR * NW;
+  constexpr int LD = BN + 4;
+  static_assert(16 * MT * LD * 4 <= (int)sizeof(sm.xs), "staged tile fits the activation buffers");
+  constexpr int NTHR = NW * kWave;
+  float* tile = reinterpret_cast<float*>(&sm.xs[0][0][0]);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  __syncthreads();                                   // every wave is done reading the buffers
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      if (!((tmask >> t) & 1u)) continue;
+      const int i = 16 * t + (lane & 15);
+      const float w = sm.w[i];
+      const f32x4_t v = acc[r][t];
+      *reinterpret_cast<float4*>(tile + i * LD + (wave * NR + r) * 16 + 4 * (lane >> 4)) =
+          make_float4(w * v[0], w * v[1], w * v[2], w * v[3]);
+    }
+  __syncthreads();
+  const int n0 = nt * BN;
+  const int rows = 16 * (32 - __clz(tmask));
+  for (int idx = threadIdx.x; idx < rows * (BN / 4); idx += NTHR) {
+    const int i = idx / (BN / 4);
+    const int c = 4 * (idx - i * (BN / 4));
+    const int orow = sm.out[i];
+    if (orow < 0 || n0 + c >= p.N) continue;
+    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (int64_t)orow * p.N + n0 + c) =
+        *reinterpret_cast<const float4*>(tile + i * LD + c);
+  }
+}
+
 template <int MT, int NR, int NW, int D, int ROUTE, int EPI>
 __global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) TileSmem<MT> sm;
@@ -384,7 +424,10 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p
   __syncthreads();
   const uint32_t tmask = active_tiles<MT>(sm);
   run_tile<MT, NR, NW, D>(p, sm, expert, nt, tmask, 0, p.KC, [&](const f32x4_t(&acc)[NR][MT], uint32_t tm) {
-    epilogue<MT, NR, NW, EPI>(p, sm, nt, tm, acc);
+    if constexpr (EPI == kEpiWeighted && 16 * NR * NW <= 128)
+      epilogue_weighted_staged<MT, NR, NW>(p, sm, nt, tm, acc);
+    else
+      epilogue<MT, NR, NW, EPI>(p, sm, nt, tm, acc);
   });
 }
 
