@@ -192,8 +192,9 @@ typedef struct {
 w4a16_status w4a16_indexed_config(int32_t block_m, w4a16_config* out);
 
 /* Choose a config for T tokens, top-k, E_glob model experts of which E_loc
- * are held here, projection [N, K] (host only).  Memoised per argument set.
- * Errors: ERR_ARG. */
+ * are held here, projection [N, K] (host only).  Memoised per argument set;
+ * always one workgroup per tile (stream-K, split_k = 0, only when a caller
+ * asks for it).  Errors: ERR_ARG. */
 w4a16_status w4a16_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc,
                           int32_t N, int32_t K, w4a16_config* out);
 
