@@ -58,7 +58,7 @@ typedef enum {
 const char* w4a16_last_error(void);
 
 /* ABI version of this header (W4A16_ABI_VERSION). */
-#define W4A16_ABI_VERSION 4
+#define W4A16_ABI_VERSION 5
 int32_t w4a16_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -168,35 +168,72 @@ w4a16_status w4a16_moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, i
  * The post picks block_m from tokens per expert, tok_e = routed rows /
  * experts, not from total tokens (section "H200 prefill and TP8": below about
  * 80 rows per expert a search over block counts on sampled routing, above it
- * a fit of padded expert rows).  w4a16_select applies the same idea with
- * gfx950 constants; a config may also be given explicitly.
+ * a fit of padded expert rows), and gates splitting of K by shape (same
+ * section: split only where the plain grid leaves the machine underfilled).
+ * The grouped calls choose their own tiles and accept no indexed config or
+ * tuning override (section "Grouped SM90 kernels").  w4a16_select applies
+ * these rules with gfx950 constants; a config may also be given explicitly.
  * ---------------------------------------------------------------------- */
+#define W4A16_ROUTE_INDEXED 0     /* sorted_ids / expert_ids / num_tokens_padded */
+#define W4A16_ROUTE_CONTIGUOUS 1  /* grouped, m_indices */
+#define W4A16_ROUTE_MASKED 2      /* grouped, masked_m */
+
 typedef struct {
   int32_t block_m;   /* rows per routed block: 16, 32, 64 or 128 */
   int32_t nr;        /* 16-row weight tiles per wave: 2 or 4 */
-  int32_t waves;     /* waves per workgroup: 4 */
+  int32_t waves;     /* waves per workgroup: 4 (8 for some tiles) */
   int32_t split_k;   /* 1: one workgroup per (block, N tile), whole K;
+                        2, 4, 8, 16: that many workgroups per tile, each over
+                        an equal share of the 128-K chunks (at least one
+                        chunk each); each leaves fp32 partials in workspace
+                        and the last to finish sums them in slice order
+                        (results independent of timing, but not bit-identical
+                        to split_k = 1);
                         0: stream-K -- the workgroups the device keeps resident
                         each take an equal share of (tile, 128-K chunk) units;
                         tiles cut between two workgroups are finished from
                         fp32 partials in workspace, summed in K order (results
-                        then depend on the device's CU count, not on timing) */
+                        then depend on the device's CU count, not on timing);
+                        indexed routing only */
   int32_t stages;    /* K chunks of weights each wave keeps in flight: 2, or 4
                         for block_m <= 32 with nr = 2 */
+  int32_t kind;      /* W4A16_ROUTE_*: the routing the config is for.  A call
+                        given a config of another kind returns ERR_ARG */
 } w4a16_config;
 
-/* The config w4a16_moe_gemm uses when its cfg is NULL, for routing buffers
- * aligned to block_m: one workgroup per tile (host only; environment
- * overrides W4A16_BLOCK_M, W4A16_NR, W4A16_SPLIT_K, W4A16_STAGES applied).
+/* The config w4a16_select gives for indexed routing aligned to block_m (the
+ * routing buffers fix block_m; the rest is chosen as w4a16_select does):
+ * what w4a16_moe_gemm uses when its cfg is NULL.  Host only; environment
+ * overrides W4A16_NR, W4A16_WAVES, W4A16_SPLIT_K, W4A16_STAGES applied.
  * Errors: ERR_ARG. */
-w4a16_status w4a16_indexed_config(int32_t block_m, w4a16_config* out);
+w4a16_status w4a16_indexed_config(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N,
+                                  int32_t K, int32_t block_m, w4a16_config* out);
 
-/* Choose a config for T tokens, top-k, E_glob model experts of which E_loc
- * are held here, projection [N, K] (host only).  Memoised per argument set;
- * always one workgroup per tile (stream-K, split_k = 0, only when a caller
- * asks for it).  Errors: ERR_ARG. */
-w4a16_status w4a16_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc,
-                          int32_t N, int32_t K, w4a16_config* out);
+/* Choose a config (host only; memoised per argument set, so repeated calls
+ * cost about a microsecond).
+ *  kind W4A16_ROUTE_INDEXED: T tokens, top-k, E_glob model experts of which
+ *    E_loc are held here, projection [N, K]; expected_m ignored.
+ *    tok_e = T * topk / E_glob.  Below 48 rows per expert block_m minimises
+ *    the total block count over {16, 32, 64} on a seeded multinomial sample
+ *    of the routing (ties to the smaller block); from 48 on, 128.  split_k
+ *    doubles from 1 while the sampled grid (routed blocks x N tiles x
+ *    split_k) stays below one round of resident workgroups on 256 CUs and
+ *    each slice keeps at least four 128-K chunks.
+ *  kind W4A16_ROUTE_CONTIGUOUS: T = rows of the contiguous layout, E_loc =
+ *    experts, [N, K]; topk, E_glob and expected_m ignored.  block_m 128 when
+ *    the grid of 128-row blocks fills the machine, else 64.
+ *  kind W4A16_ROUTE_MASKED: T = max_m, E_loc = groups, [N, K], expected_m > 0
+ *    the expected rows per group; topk and E_glob ignored.  block_m covers
+ *    1.3 * expected_m rows for K >= 4096 (a second M tile re-reads all of
+ *    K) and ceil(1.25 * expected_m, 8) for shorter K, rounded up to a built
+ *    block (at most 128); stages 4 (512 K elements in flight) for block_m
+ *    <= 32, else 2.
+ * Environment overrides W4A16_BLOCK_M, W4A16_NR, W4A16_WAVES,
+ * W4A16_SPLIT_K, W4A16_STAGES apply to indexed configs only; a grouped
+ * selection with any of them set returns ERR_ARG.
+ * Errors: ERR_ARG. */
+w4a16_status w4a16_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N,
+                          int32_t K, int32_t kind, int32_t expected_m, w4a16_config* out);
 
 /* ------------------------------------------------------------------------
  * Indexed MoE GEMM (the post's indexed family).
@@ -210,13 +247,22 @@ typedef struct {
   int32_t T, topk;                   /* sentinel is T * topk */
   const int32_t* topk_ids;           /* [T, topk]; read only by the combine */
   int32_t first_expert, E_loc;       /* local expert range; read only by the combine */
+  int32_t E_glob;                    /* model experts (tok_e = T * topk / E_glob for
+                                        the config chosen when cfg is NULL) */
 } w4a16_indexed_routing;
 
-/* Bytes of workspace w4a16_moe_gemm needs for this weight, T, topk, combine
- * flag and config (NULL: w4a16_indexed_config(16)): the combine's fp32 per-slot partials (T * topk * N * 4)
- * when combine != 0, plus, for split_k = 0, two partial tiles per resident
- * workgroup of the current device.  Returns 0 on bad arguments. */
-size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, int32_t T, int32_t topk,
+/* Bytes of workspace w4a16_moe_gemm needs for this weight, routing shape,
+ * combine flag and config (NULL: the config the call would choose):
+ *   - split_k > 1: 4 bytes of arrival counter per tile that may be split,
+ *     then that many tiles' fp32 slices;
+ *   - combine != 0: the fp32 per-slot partials, T * topk * N * 4 bytes;
+ *   - split_k = 0: two partial tiles per resident workgroup of the current
+ *     device.
+ * The workspace must be zero-filled once before its first use (the arrival
+ * counters start at zero); every call leaves the counters at zero again, so
+ * the same workspace serves any number of later calls on one stream.  The
+ * other bytes are scratch of the call.  Returns 0 on bad arguments. */
+size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, const w4a16_indexed_routing* routing,
                                       int32_t combine, const w4a16_config* cfg);
 
 /* Row layouts of the activations `a` (argument a_layout). */
@@ -236,9 +282,16 @@ size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, int32_t T, 
  *               with fp32 products, summed in j order, one rounding; tokens
  *               without local slots get 0; every row of out[T, N] written.
  *               Needs workspace (fp32 partials per slot).
- *  workspace  : w4a16_moe_gemm_workspace_bytes() bytes; contents need no
- *               initialisation and are scratch for this call only.
- *  cfg        : NULL: w4a16_indexed_config(routing->block_m).
+ *               A weight packed with interleaved gate/up tiles
+ *               (W4A16_DESC_GATE_UP) is rejected here (ERR_LAYOUT): the
+ *               combine belongs to the down projection.
+ *  workspace  : w4a16_moe_gemm_workspace_bytes() bytes, zero-filled before
+ *               its first use (see there).
+ *  cfg        : NULL: w4a16_indexed_config for the routing's shape and
+ *               block_m.  A config of another routing kind: ERR_ARG.
+ * Sizes: activation rows are addressed with 32-bit byte offsets, so the rows
+ * the call may read (T, T * topk or capacity by a_layout) times K * 2 bytes
+ * must not exceed 4 GiB (ERR_SHAPE otherwise).
  * Pointers: packed_w, packed_s, a, out, workspace 16-byte aligned.
  * Errors: ERR_ARG, ERR_LAYOUT, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP. */
 w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
@@ -262,8 +315,11 @@ w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
  *               per-slot call writes), silu(g) = g / (1 + exp(-g)) in fp32.
  *               Padding positions are left unwritten (the down call never
  *               uses them).
- *  cfg        : NULL: w4a16_indexed_config(routing->block_m); one workgroup
- *               per tile (split_k = 1), nr even.
+ *  cfg        : NULL: w4a16_indexed_config for the routing's shape and
+ *               block_m, without splitting; one workgroup per tile
+ *               (split_k = 1), nr even.  A config of another routing kind:
+ *               ERR_ARG.
+ * Sizes: x_rows * K * 2 bytes at most 4 GiB (ERR_SHAPE).
  * Pointers 16-byte aligned.
  * Errors: ERR_ARG, ERR_LAYOUT (not a gate/up weight), ERR_SHAPE,
  * ERR_UNSUPPORTED, ERR_HIP. */
@@ -275,28 +331,49 @@ w4a16_status w4a16_moe_gate_up_silu(const w4a16_weight_desc* desc, const void* p
 /* ------------------------------------------------------------------------
  * Grouped layouts (the post's grouped family, section "Grouped SM90
  * kernels": contiguous prefill and masked decode; same packed weights here).
+ * The grouped calls own their tile choice: cfg is NULL (the call selects
+ * with w4a16_select for its kind) or a config w4a16_select returned for that
+ * kind; an indexed config, or any W4A16_* tuning override in the
+ * environment, returns ERR_ARG (section "Grouped SM90 kernels": grouped
+ * dispatch accepts no indexed block_m or tuning override).
  * ---------------------------------------------------------------------- */
 
 /* Contiguous: a [m_rows, K] holds each expert's rows back to back, each
  * expert's segment starting at a multiple of 128 rows; m_indices[r] is the
  * expert of row r or -1 on padding.  out[m_rows, N]: rows with
  * m_indices[r] >= 0 written as bf16(a[r] . W[m_indices[r]]^T); -1 rows are
- * left unwritten.  cfg->block_m must divide 128 (NULL: 128).
- * Errors: ERR_ARG, ERR_LAYOUT, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP. */
+ * left unwritten.  cfg: see above (its block_m divides 128).
+ * workspace: w4a16_grouped_workspace_bytes(desc, W4A16_ROUTE_CONTIGUOUS,
+ * m_rows, 0, cfg) bytes, zero-filled before first use, or NULL when that is
+ * 0.  Sizes: m_rows * K * 2 bytes at most 4 GiB (ERR_SHAPE).
+ * Errors: ERR_ARG, ERR_LAYOUT, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP. */
 w4a16_status w4a16_grouped_contiguous(const w4a16_weight_desc* desc, const void* packed_w,
                                       const void* packed_s, const uint16_t* a, int64_t m_rows,
                                       const int32_t* m_indices, uint16_t* out,
-                                      const w4a16_config* cfg, w4a16_stream_t stream);
+                                      const w4a16_config* cfg, void* workspace, size_t workspace_bytes,
+                                      w4a16_stream_t stream);
 
 /* Masked: a [E, max_m, K]; masked_m[g] (device int32, E entries) valid rows
  * of group g; out flat [E * max_m, N], row g * max_m + r written for
  * r < min(masked_m[g], max_m), other rows unwritten.  expected_m (host, > 0)
- * only steers the tile choice when cfg is NULL.
- * Errors: ERR_ARG, ERR_LAYOUT, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP. */
+ * only steers the tile choice.  cfg: see above.  workspace:
+ * w4a16_grouped_workspace_bytes(desc, W4A16_ROUTE_MASKED, max_m,
+ * expected_m, cfg) bytes, zero-filled before first use, or NULL when that is
+ * 0.  Sizes: E * max_m * K * 2 bytes at most 4 GiB (ERR_SHAPE).
+ * Errors: ERR_ARG, ERR_LAYOUT, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP. */
 w4a16_status w4a16_grouped_masked(const w4a16_weight_desc* desc, const void* packed_w,
                                   const void* packed_s, const uint16_t* a, int32_t max_m,
                                   const int32_t* masked_m, int32_t expected_m, uint16_t* out,
-                                  const w4a16_config* cfg, w4a16_stream_t stream);
+                                  const w4a16_config* cfg, void* workspace, size_t workspace_bytes,
+                                  w4a16_stream_t stream);
+
+/* Workspace bytes of a grouped call (kind W4A16_ROUTE_CONTIGUOUS with
+ * rows = m_rows, or W4A16_ROUTE_MASKED with rows = max_m and its
+ * expected_m) with cfg (NULL: the call's own selection): split-K arrival
+ * counters and slices when the config splits K, else 0.  Returns 0 on bad
+ * arguments. */
+size_t w4a16_grouped_workspace_bytes(const w4a16_weight_desc* desc, int32_t kind, int64_t rows,
+                                     int32_t expected_m, const w4a16_config* cfg);
 
 /* ------------------------------------------------------------------------
  * A4W4: MXFP4 activations x MXFP4 weights.

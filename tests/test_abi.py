@@ -38,7 +38,8 @@ def test_every_declared_function_is_exported_and_bound(L):
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(_lib.WeightDesc) == 64
     assert _lib.WeightDesc.flags.offset == 32 and _lib.WeightDesc.w_bytes.offset == 40
-    assert ctypes.sizeof(_lib.Config) == 20
+    assert ctypes.sizeof(_lib.Config) == 24 and _lib.Config.kind.offset == 20
+    assert ctypes.sizeof(_lib.IndexedRouting) == 72 and _lib.IndexedRouting.E_glob.offset == 64
     assert _lib.IndexedRouting.capacity.offset == 24
 
 
@@ -59,7 +60,7 @@ def test_header_compiles_as_c_and_matches_the_binding(tmp_path):
         for f, _ in ct._fields_:
             lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
     for const in ("W4A16_ABI_VERSION", "W4A16_DESC_GATE_UP", "W4A16_DESC_MXFP4", "W4A16_A_TOKEN", "W4A16_A_SLOT",
-                  "W4A16_A_SORTED"):
+                  "W4A16_A_SORTED", "W4A16_ROUTE_INDEXED", "W4A16_ROUTE_CONTIGUOUS", "W4A16_ROUTE_MASKED"):
         lines.append(f'  printf("const {const} %d\\n", (int)({const}));')
     lines += ["  return 0;", "}"]
     src = tmp_path / "layout.c"
@@ -79,11 +80,13 @@ def test_header_compiles_as_c_and_matches_the_binding(tmp_path):
     assert got[("const", "W4A16_DESC_MXFP4")] == _lib.DESC_MXFP4
     assert (got[("const", "W4A16_A_TOKEN")], got[("const", "W4A16_A_SLOT")],
             got[("const", "W4A16_A_SORTED")]) == (_lib.A_TOKEN, _lib.A_SLOT, _lib.A_SORTED)
-    assert got[("const", "W4A16_ABI_VERSION")] == 4
+    assert (got[("const", "W4A16_ROUTE_INDEXED")], got[("const", "W4A16_ROUTE_CONTIGUOUS")],
+            got[("const", "W4A16_ROUTE_MASKED")]) == (_lib.ROUTE_INDEXED, _lib.ROUTE_CONTIGUOUS, _lib.ROUTE_MASKED)
+    assert got[("const", "W4A16_ABI_VERSION")] == 5
 
 
 def test_version_and_desc(L):
-    assert L.w4a16_abi_version() == 4
+    assert L.w4a16_abi_version() == 5
     d = W.weight_desc(48, 4096, 7168)
     assert (d.K_pad, d.chunks, d.group) == (7168, 56, 32)
     assert d.w_bytes == 48 * 4096 * 7168 // 2
@@ -111,26 +114,54 @@ def test_gate_up_descriptor(L):
 def test_corrupted_descriptor_is_rejected(L):
     d = W.weight_desc(4, 64, 256)
     d.N = 128                                           # shape changed after packing
-    st = L.w4a16_grouped_contiguous(ctypes.byref(d), 16, 16, 16, 128, 16, 16, None, None)
+    st = L.w4a16_grouped_contiguous(ctypes.byref(d), 16, 16, 16, 128, 16, 16, None, None, 0, None)
     assert st == -3 and b"checksum" in L.w4a16_last_error()
     d = W.weight_desc(4, 64, 256)
     d.magic = 0
     assert L.w4a16_pack_w4(16, 16, ctypes.byref(d), 16, 16, None) == -3
 
 
+def _routing(T, topk, E_loc, block_m, E_glob=384, P=16, capacity=None):
+    cap = W.align_capacity(T, topk, E_loc, block_m) if capacity is None else capacity
+    return _lib.IndexedRouting(P, P, P, cap, block_m, T, topk, P, 0, E_loc, E_glob)
+
+
+def _ws(desc, r, combine, cfg=None):
+    return L_().w4a16_moe_gemm_workspace_bytes(ctypes.byref(desc), ctypes.byref(r), int(combine),
+                                               None if cfg is None else ctypes.byref(cfg))
+
+
+def L_():
+    return W.load()
+
+
 def test_capacity_and_workspace(L):
     assert W.align_capacity(576, 8, 48, 32) == ((4608 + 48 * 31 + 31) // 32) * 32
     assert L.w4a16_align_capacity(4, 2, 3, 24) == -1
-    p = W.PackedW4(W.weight_desc(4, 7168, 2048), None, None)
+    d = W.weight_desc(4, 7168, 2048)
+    r = _routing(10, 8, 4, 32)
     one_wg_per_tile = W.config(32, 2, split_k=1)
-    assert W.workspace_bytes(p, 10, 8, True, one_wg_per_tile) == 10 * 8 * 7168 * 4
-    assert W.workspace_bytes(p, 10, 8, False, one_wg_per_tile) == 0
-    assert W.workspace_bytes(p, 10, 8, True, W.config(32, 3)) == 0          # unsupported config
-    d = W.indexed_config(64)
-    assert (d.block_m, d.nr, d.waves, d.split_k, d.stages) == (64, 2, 4, 1, 2)
-    assert W.workspace_bytes(p, 10, 8, True, W.config(32, 2, stages=4)) == 10 * 8 * 7168 * 4
-    assert W.workspace_bytes(p, 10, 8, True, W.config(64, 4, stages=4)) == 0   # not built
-    assert W.workspace_bytes(p, 10, 8, True, W.config(32, 2, stages=3)) == 0   # odd depth: not built
+    assert _ws(d, r, True, one_wg_per_tile) == 10 * 8 * 7168 * 4
+    assert _ws(d, r, False, one_wg_per_tile) == 0
+    assert _ws(d, r, True, W.config(32, 3)) == 0                     # unsupported config
+    assert _ws(d, r, True, W.config(32, 2, stages=4)) == 10 * 8 * 7168 * 4
+    assert _ws(d, r, True, W.config(64, 4, stages=4)) == 0           # not built
+    assert _ws(d, r, True, W.config(32, 2, stages=3)) == 0           # odd depth: not built
+    assert _ws(d, r, True, W.config(32, 2, kind="masked")) == 0      # config of another routing kind
+    # split K: arrival counters + slices for every tile that can exist (routed
+    # blocks bounded by min(capacity / block_m, T*topk / block_m + E_loc)),
+    # then the combine's partials
+    blocks = min(r.capacity // 32, -(-80 // 32) + 4)
+    tiles = blocks * (7168 // 16 // 8)
+    al = lambda v: -(-v // 256) * 256
+    slices = tiles * 4 * (2 * 2 * 256 * 16)
+    assert _ws(d, r, True, W.config(32, 2, split_k=4)) == al(tiles * 4) + al(slices) + 10 * 8 * 7168 * 4
+    assert _ws(d, r, True, W.config(32, 2, split_k=32)) == 0         # not a split count
+    # cfg NULL: the selector's config for the routing's block_m
+    c = _lib.Config()
+    assert L.w4a16_indexed_config(10, 8, 384, 4, 7168, 2048, 32, ctypes.byref(c)) == 0
+    assert (c.block_m, c.nr, c.waves, c.stages, c.kind) == (32, 2, 4, 2, 0)
+    assert _ws(d, r, True) == _ws(d, r, True, c)
 
 
 def test_align_argument_errors(L):
@@ -142,13 +173,13 @@ def test_align_argument_errors(L):
     assert L.w4a16_moe_align(P, 4, 2, 2000, 0, 1500, 16, P, P, P, 1 << 20, 0, None) == -2
 
 
-def test_gemm_argument_errors(L):
+def test_gemm_argument_errors(L, monkeypatch):
     P = 16
     d = W.weight_desc(8, 64, 256)
-    r = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 8)
+    r = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 8, 64)
     cfg = W.config(32, 2)
-    call = lambda **kw: L.w4a16_moe_gemm(ctypes.byref(d), P, P, kw.get("a", P), kw.get("rows", 64), 0,
-                                         ctypes.byref(kw.get("r", r)), kw.get("w"), P,
+    call = lambda **kw: L.w4a16_moe_gemm(ctypes.byref(kw.get("d", d)), P, P, kw.get("a", P), kw.get("rows", 64),
+                                         kw.get("layout", 0), ctypes.byref(kw.get("r", r)), kw.get("w"), P,
                                          kw.get("cfg", ctypes.byref(cfg)), kw.get("ws"),
                                          kw.get("wsb", 0), None)
     assert call(a=P + 2) == -1                                           # misaligned activations
@@ -156,12 +187,38 @@ def test_gemm_argument_errors(L):
     assert call(cfg=ctypes.byref(W.config(64, 2))) == -3                 # block_m disagrees with routing
     assert call(cfg=ctypes.byref(W.config(32, 3))) == -4                 # tile config not built
     assert call(w=P) == -8                                               # combine without workspace
-    assert call(cfg=ctypes.byref(W.config(32, 2, split_k=2))) == -4      # split_k must be 0 or 1
-    bad = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 4)
+    assert call(cfg=ctypes.byref(W.config(32, 2, split_k=3))) == -4     # not a split count
+    assert call(cfg=ctypes.byref(W.config(32, 2, split_k=4))) == -4     # more slices than the 2 K chunks
+    assert call(cfg=ctypes.byref(W.config(32, 2, split_k=2))) == -8     # split needs workspace
+    assert call(cfg=ctypes.byref(W.config(32, 2, kind="contiguous"))) == -1   # config of another kind
+    bad = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 4, 64)
     assert call(r=bad) == -3                                             # E_loc != weight experts
-    assert L.w4a16_grouped_masked(ctypes.byref(d), P, P, P, 0, P, 4, P, None, None) == -1
-    assert L.w4a16_grouped_masked(ctypes.byref(d), P, P, P, 32, P, 0, P, None, None) == -1
-    assert L.w4a16_grouped_contiguous(ctypes.byref(d), P, P, P, 100, P, P, None, None) == -2
+    no_eg = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 8, 0)
+    assert call(r=no_eg, cfg=None) == -1                                 # NULL cfg needs E_glob to select
+    gated = W.weight_desc(8, 64, 256, gate_up=True)
+    assert call(d=gated, w=P) == -3                                      # combine on a gate/up weight
+    # activations are addressed with 32-bit byte offsets: no call may read past 4 GiB
+    big = W.weight_desc(8, 64, 7168)
+    rb = _lib.IndexedRouting(P, P, P, 320128, 32, 40000, 8, P, 0, 8, 64)
+    assert call(d=big, r=rb, rows=320000, layout=_lib.A_SLOT) == -2      # 320000 x 7168 x 2 B > 4 GiB
+    gm = lambda max_m, em, cfg=None, d_=d: L.w4a16_grouped_masked(ctypes.byref(d_), P, P, P, max_m, P, em, P,
+                                                                 cfg, None, 0, None)
+    assert gm(0, 4) == -1
+    assert gm(32, 0) == -1
+    assert gm(32, 4, ctypes.byref(W.config(32, 2))) == -1                # indexed config on a grouped call
+    assert gm(37500, 4, None, W.weight_desc(8, 64, 7168)) == -2          # 8 x 37500 rows x 14 KB > 4 GiB
+    gc = lambda rows, cfg=None, d_=d: L.w4a16_grouped_contiguous(ctypes.byref(d_), P, P, P, rows, P, P, cfg,
+                                                                None, 0, None)
+    assert gc(100) == -2
+    assert gc(128, ctypes.byref(W.config(64, 2))) == -1                  # indexed config on a grouped call
+    assert gc(300032, None, W.weight_desc(8, 64, 7168)) == -2            # 300032 x 7168 x 2 B > 4 GiB
+    # tuning overrides belong to indexed routing: grouped calls and grouped selection refuse them
+    monkeypatch.setenv("W4A16_BLOCK_M", "64")
+    assert gc(128) == -1 and b"W4A16_BLOCK_M" in L.w4a16_last_error()
+    with pytest.raises(W.W4A16Error):
+        W.select(512, 1, 1, 8, 64, 256, kind="masked", expected_m=30)
+    assert W.select(576, 8, 384, 48, 4096, 7168).block_m == 64          # indexed selection takes the override
+    monkeypatch.delenv("W4A16_BLOCK_M")
     lay = lambda layout, rows: L.w4a16_moe_gemm(ctypes.byref(d), P, P, P, rows, layout, ctypes.byref(r), None, P,
                                                 ctypes.byref(cfg), None, 0, None)
     assert lay(3, 4096) == -1                                            # unknown activation layout
@@ -173,12 +230,14 @@ def test_gate_up_silu_argument_errors(L):
     P = 16
     plain = W.weight_desc(8, 64, 256)
     gated = W.weight_desc(8, 64, 256, gate_up=True)
-    r = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 8)
+    r = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 8, 64)
     call = lambda d, cfg: L.w4a16_moe_gate_up_silu(ctypes.byref(d), P, P, P, 64, ctypes.byref(r), P,
                                                    ctypes.byref(cfg), None)
     assert call(plain, W.config(32, 2)) == -3                            # weight not gate/up packed
     assert call(gated, W.config(32, 2, split_k=0)) == -4                 # one workgroup per tile only
+    assert call(gated, W.config(32, 2, split_k=2)) == -4
     assert call(gated, W.config(16, 2)) == -3                            # block_m disagrees with routing
+    assert call(gated, W.config(32, 2, kind="masked")) == -1             # config of another kind
 
 
 def test_mxfp4_selector_halves_large_prefill_blocks(L):
@@ -200,15 +259,47 @@ def test_mxfp4_selector_halves_large_prefill_blocks(L):
 
 def test_selector_follows_tokens_per_expert(L):
     dec = W.select(576, 8, 384, 48, 4096, 7168)            # ~12 rows/expert
-    assert dec.block_m == 32 and dec.nr == 2
+    assert dec.block_m == 32 and dec.nr == 2 and dec.kind == 0
     one = W.select(16, 8, 384, 384, 512, 7168)             # ~0.3 rows/expert
     assert one.block_m == 16
-    assert dec.split_k == 1 and one.split_k == 1            # stream-K only when asked for
     pre = W.select(8192, 8, 384, 48, 4096, 7168)           # ~171 rows/expert
     assert pre.block_m == 128 and pre.nr == 2
     # tok_e, not total tokens: same T, 8x more experts -> decode side
     assert W.select(8192, 8, 3072, 48, 4096, 7168).block_m < 128
     assert W.select(576, 8, 384, 48, 4096, 7168).block_m == dec.block_m   # memoised, stable
+
+
+def test_selector_splits_k_only_for_underfilled_grids(L):
+    """split_k doubles while the doubled grid (sampled routed blocks x N tiles x
+    split_k x 2) stays within 4/5 of one round of resident workgroups (256 CUs
+    x 4 for 16/32-row blocks) and each slice keeps >= 4 chunks of 128 K."""
+    assert W.select(576, 8, 384, 48, 4096, 7168).split_k == 1     # EP8 decode: 48 x 32 tiles fill the machine
+    assert W.select(576, 8, 384, 24, 4096, 7168).split_k == 1     # EP16 decode: 768 tiles
+    assert W.select(576, 8, 384, 12, 4096, 7168).split_k == 2     # EP32 decode: 384 tiles
+    assert W.select(16, 8, 384, 384, 512, 7168).split_k == 2      # TP8 T=16: ~400 sampled tiles
+    t1 = W.select(1, 8, 384, 384, 512, 7168)                      # TP8 T=1: 8 blocks x 4 tiles
+    assert t1.split_k == 8                                        # 56 chunks: 7 per slice
+    assert W.select(1, 8, 384, 384, 7168, 256).split_k == 1       # its down projection: K = 256, 2 chunks
+    assert W.select(4096, 8, 384, 384, 512, 7168).split_k == 1    # prefill-side grids fill the machine
+    assert W.select(8192, 8, 384, 48, 4096, 7168).split_k == 1
+
+
+def test_grouped_selection_follows_the_grouped_rules(L):
+    """Masked: deep K covers ~1.3 x expected_m rows, short K ceil(1.25 x
+    expected_m, 8), rounded up to a built block; contiguous: 128-row blocks
+    when their grid fills the machine, 64 for small problems."""
+    m = lambda em, K, N=4096: W.select(512, 1, 1, 48, N, K, kind="masked", expected_m=em)
+    assert m(12, 7168).block_m == 16 and m(13, 7168).block_m == 32      # 1.3 x 12 = 15.6; 1.3 x 13 = 16.9
+    assert m(24, 7168).block_m == 32 and m(25, 7168).block_m == 64      # 31.2 -> 32; 32.5 -> 64
+    assert m(25, 2048).block_m == 32                                     # ceil(31.25, 8) = 32
+    assert m(315, 7168).block_m == 128
+    assert m(12, 7168).stages == 4 and m(315, 7168).stages == 2          # ~512 buffered K for decode tiles
+    assert m(12, 7168).kind == 2
+    c = lambda rows, E=48: W.select(rows, 1, 1, E, 4096, 7168, kind="contiguous")
+    assert c(17024).block_m == 128 and c(17024).kind == 1                # 133 blocks x 32 N tiles
+    assert c(1024, 8).block_m == 64                                      # 8 x 32 tiles < one round: BM64
+    with pytest.raises(W.W4A16Error):
+        W.select(512, 1, 1, 48, 4096, 7168, kind="masked", expected_m=0)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

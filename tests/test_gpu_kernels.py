@@ -346,16 +346,23 @@ def test_grouped_contiguous_and_masked_small():
     A, mi, slots = W.contiguous_layout(P.topk_ids, P.x, sh.first, sh.E_loc, pad=128, pad_fill=0x7FC0)
     ref, valid = O.grouped_contiguous(A, P.c1, P.s1, mi)
     for bm, nr, nw in ((16, 2, 4), (64, 4, 4), (128, 4, 4), (128, 2, 8), (32, 2, 8)):
-        out = bits(M.grouped_contiguous(to_dev_bf16(A), P.p1, to_dev(mi), cfg=M.config(bm, nr, waves=nw)))
+        out = bits(M.grouped_contiguous(to_dev_bf16(A), P.p1, to_dev(mi),
+                                        cfg=M.config(bm, nr, waves=nw, kind="contiguous")))
         assert_close(out[valid], ref[valid], f"contiguous bm={bm} nr={nr} waves={nw}")
     A3, mm, sl3, dropped = W.masked_layout(P.topk_ids, P.x, sh.first, sh.E_loc, sh.max_m, pad_fill=0x7FC0)
     log("masked dropped", dropped, "masked_m", mm.tolist())
     ref, valid = O.grouped_masked(A3, P.c1, P.s1, mm)
     for bm, nw in ((16, 4), (32, 4), (64, 4), (16, 8), (32, 8)):
-        out = bits(M.grouped_masked(to_dev_bf16(A3), P.p1, to_dev(mm), 32, cfg=M.config(bm, 2, waves=nw)))
+        out = bits(M.grouped_masked(to_dev_bf16(A3), P.p1, to_dev(mm), 32, cfg=M.config(bm, 2, waves=nw, kind="masked")))
         assert_close(out[valid], ref[valid], f"masked bm={bm} waves={nw}")
     out = bits(M.grouped_masked(to_dev_bf16(A3), P.p1, to_dev(mm), expected_m=max(1, int(mm.mean()))))
     assert_close(out[valid], ref[valid], "masked auto config")
+    # split K on the grouped layouts (K = 256: two slices of one chunk)
+    out = bits(M.grouped_contiguous(to_dev_bf16(A), P.p1, to_dev(mi), cfg=M.config(32, 2, split_k=2, kind="contiguous")))
+    ref_c, valid_c = O.grouped_contiguous(A, P.c1, P.s1, mi)
+    assert_close(out[valid_c], ref_c[valid_c], "contiguous split_k=2")
+    out = bits(M.grouped_masked(to_dev_bf16(A3), P.p1, to_dev(mm), 32, cfg=M.config(16, 2, split_k=2, kind="masked")))
+    assert_close(out[valid], ref[valid], "masked split_k=2")
     # grouped and indexed agree on the same rows
     h, ok = O.indexed_gate_up(P.x, P.c1, P.s1, P.topk_ids, sh.first, sh.E_loc)
     s = sl3.reshape(-1)
@@ -377,9 +384,8 @@ def test_hip_graph_capture_replays_match_eager():
     h = torch.zeros(sh.T * sh.topk, sh.N1, dtype=torch.bfloat16, device=dev())
     y = torch.empty(sh.T, sh.N2, dtype=torch.bfloat16, device=dev())
     cfg = M.config(bm, 2, split_k=0)
-    ws = torch.empty(M.workspace_bytes(P.p2, sh.T, sh.topk, True, cfg), dtype=torch.uint8, device=dev())
-    ws1 = torch.empty(max(16, M.workspace_bytes(P.p1, sh.T, sh.topk, False, cfg)), dtype=torch.uint8,
-                      device=dev())
+    ws = torch.empty(M.workspace_bytes(P.p2, r, True, cfg), dtype=torch.uint8, device=dev())
+    ws1 = torch.empty(max(16, M.workspace_bytes(P.p1, r, False, cfg)), dtype=torch.uint8, device=dev())
 
     def step():
         rr = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, bm, capacity=cap)
@@ -444,3 +450,98 @@ def test_streamk_matches_oracle_and_is_deterministic(name, T):
         _check_indexed(P, torch.from_numpy(outs[0][0].view(np.int16)).view(torch.bfloat16),
                        torch.from_numpy(outs[0][1].view(np.int16)).view(torch.bfloat16),
                        f"stream-K {name} T={T} bm={bm}")
+
+
+# ------------------------------------------------------------ split K
+
+def _split_shapes():
+    return [W.WORKLOADS["tiny"],
+            W.MoEShape(name="ragged", E_glob=9, E_loc=5, first=2, topk=3, T=37, K1=96, N1=48,
+                       K2=160, N2=80, seed=77),
+            W.MoEShape(name="k1312", E_glob=8, E_loc=6, first=1, topk=2, T=40, K1=1312, N1=96,
+                       K2=1024, N2=80, seed=91)]
+
+
+@pytest.mark.parametrize("shape", _split_shapes(), ids=lambda s: s.name)
+def test_split_k_matches_oracle_is_deterministic_and_leaves_counters_zero(shape):
+    """split_k = S: S workgroups per tile over equal shares of the K chunks,
+    the last to finish summing the fp32 slices in slice order.  Within
+    tolerance of the oracle for every S the shape allows, bit-identical across
+    repeated calls on one workspace (whichever workgroup finishes last), and
+    the arrival counters are back at zero after every call."""
+    P = Problem(shape).upload()
+    sh = P.sh
+    for bm in (16, 32, 128):
+        r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, bm)
+        for S in (2, 4, 8):
+            if S > -(-sh.K1 // 128) and S > -(-sh.K2 // 128):
+                continue
+            outs = []
+            c1 = M.config(bm, 2, split_k=S if S <= -(-sh.K1 // 128) else 1)
+            c2 = M.config(bm, 2, split_k=S if S <= -(-sh.K2 // 128) else 1)
+            ws1 = torch.zeros(max(16, M.workspace_bytes(P.p1, r, False, c1)), dtype=torch.uint8, device=dev())
+            ws2 = torch.zeros(max(16, M.workspace_bytes(P.p2, r, True, c2)), dtype=torch.uint8, device=dev())
+            for rep in range(3):
+                h = M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=c1, workspace=ws1)
+                y = M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=c2, workspace=ws2)
+                torch.cuda.synchronize()
+                outs.append((bits(h), bits(y)))
+            for k_ in (1, 2):
+                np.testing.assert_array_equal(outs[0][0], outs[k_][0])
+                np.testing.assert_array_equal(outs[0][1], outs[k_][1])
+            for ws, c in ((ws1, c1), (ws2, c2)):
+                if c.split_k > 1:   # counters: the first region, 4 bytes per splittable tile
+                    assert not bool(ws[:256].any()), "split-K arrival counters not reset"
+            _check_indexed(P, torch.from_numpy(outs[0][0].view(np.int16)).view(torch.bfloat16),
+                           torch.from_numpy(outs[0][1].view(np.int16)).view(torch.bfloat16),
+                           f"split {sh.name} bm={bm} S={S} (gate/up {c1.split_k}, down {c2.split_k})")
+
+
+def test_split_k_past_the_tile_cap_runs_whole_tiles():
+    """More tiles than the split slices are kept for (2048): tiles past the
+    cap run whole in their first workgroup, the rest split; all within
+    tolerance of the oracle."""
+    sh = W.MoEShape(name="many_tiles", E_glob=96, E_loc=96, first=0, topk=4, T=900, K1=512, N1=2048,
+                    K2=256, N2=64, seed=5)
+    P = Problem(sh).upload()
+    r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, 16)
+    n_tiles = 2048 // 16 // 8
+    ntp = int(r.num_tokens_padded.item())
+    assert ntp // 16 * n_tiles > 2048, "shape must exceed the split tile cap"
+    c = M.config(16, 2, split_k=2)
+    h = M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=c)
+    torch.cuda.synchronize()
+    ref_h, ok = O.indexed_gate_up(P.x, P.c1, P.s1, P.topk_ids, sh.first, sh.E_loc)
+    assert_close(bits(h)[ok], ref_h[ok], "split past the tile cap")
+
+
+def test_split_k_graph_replays_match_eager():
+    """A split-K call captured in a HIP graph: every replay reproduces the
+    eager bits (the counters it leaves at zero let the next replay split
+    again), with eager work and poisoned outputs between replays."""
+    P = Problem(W.scaled(W.WORKLOADS["tiny"], K1=1024, K2=512)).upload()
+    sh = P.sh
+    r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, 16)
+    c1, c2 = M.config(16, 2, split_k=8), M.config(16, 2, split_k=4)
+    ws1 = torch.zeros(M.workspace_bytes(P.p1, r, False, c1), dtype=torch.uint8, device=dev())
+    ws2 = torch.zeros(M.workspace_bytes(P.p2, r, True, c2), dtype=torch.uint8, device=dev())
+    h = torch.zeros(sh.T * sh.topk, sh.N1, dtype=torch.bfloat16, device=dev())
+    y = torch.empty(sh.T, sh.N2, dtype=torch.bfloat16, device=dev())
+    M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=c1, out=h, workspace=ws1)
+    M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=c2, out=y, workspace=ws2)
+    torch.cuda.synchronize()
+    ref_h, ref_y = bits(h).copy(), bits(y).copy()
+    _check_indexed(P, h, y, "split graph eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=c1, out=h, workspace=ws1)
+        M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=c2, out=y, workspace=ws2)
+    for rep in range(4):
+        h.fill_(0)
+        y.fill_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(h), ref_h, err_msg=f"replay {rep}")
+        np.testing.assert_array_equal(bits(y), ref_y, err_msg=f"replay {rep}")
+        _ = (P.d_x.float() @ P.d_x.float().t()).sum().item()   # unrelated eager work

@@ -28,10 +28,14 @@ def _indexed_full(P, name):
     cfg1 = M.select(T, k, sh.E_glob, sh.E_loc, sh.N1, sh.K1)
     r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, cfg1.block_m)
     canary = torch.full((T * k, sh.N1), -3.0, dtype=torch.bfloat16, device="cuda")
-    h = M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=cfg1, out=canary)
-    y = M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=cfg1)
+    # cfg=None: each projection runs the library's own choice for the routing
+    # (block_m fixed by the routing; split_k per projection)
+    h = M.moe_w4a16_gemm(P.d_x, P.p1, r, out=canary)
+    y = M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w)
     torch.cuda.synchronize()
-    log(name, "config", cfg1, "ntp", int(r.num_tokens_padded.item()))
+    assert M.indexed_config(r, P.p1).split_k == cfg1.split_k
+    log(name, "gate/up", M.indexed_config(r, P.p1), "down", M.indexed_config(r, P.p2),
+        "ntp", int(r.num_tokens_padded.item()))
     flat = P.topk_ids.reshape(-1)
     ok = (flat >= sh.first) & (flat < sh.first + sh.E_loc)
     d_ok = torch.from_numpy(ok).cuda()

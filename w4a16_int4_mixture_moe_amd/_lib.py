@@ -36,15 +36,17 @@ class WeightDesc(ctypes.Structure):
 DESC_GATE_UP = 1            # W4A16_DESC_GATE_UP
 DESC_MXFP4 = 2              # W4A16_DESC_MXFP4
 A_TOKEN, A_SLOT, A_SORTED = 0, 1, 2   # W4A16_A_TOKEN / _SLOT / _SORTED
+ROUTE_INDEXED, ROUTE_CONTIGUOUS, ROUTE_MASKED = 0, 1, 2   # W4A16_ROUTE_*
 
 
 class Config(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int32), ("nr", ctypes.c_int32),
-                ("waves", ctypes.c_int32), ("split_k", ctypes.c_int32), ("stages", ctypes.c_int32)]
+                ("waves", ctypes.c_int32), ("split_k", ctypes.c_int32), ("stages", ctypes.c_int32),
+                ("kind", ctypes.c_int32)]
 
     def __repr__(self):
         return (f"Config(block_m={self.block_m}, nr={self.nr}, waves={self.waves}, "
-                f"split_k={self.split_k}, stages={self.stages})")
+                f"split_k={self.split_k}, stages={self.stages}, kind={self.kind})")
 
 
 class IndexedRouting(ctypes.Structure):
@@ -53,6 +55,7 @@ class IndexedRouting(ctypes.Structure):
         ("num_tokens_padded", ctypes.c_void_p), ("capacity", ctypes.c_int64),
         ("block_m", ctypes.c_int32), ("T", ctypes.c_int32), ("topk", ctypes.c_int32),
         ("topk_ids", ctypes.c_void_p), ("first_expert", ctypes.c_int32), ("E_loc", ctypes.c_int32),
+        ("E_glob", ctypes.c_int32),
     ]
 
 
@@ -70,10 +73,10 @@ SIGNATURES = {
     "w4a16_pack_w4": (_I32, [_P, _P, ctypes.POINTER(WeightDesc), _P, _P, _P]),
     "w4a16_align_capacity": (_I64, [_I32, _I32, _I32, _I32]),
     "w4a16_moe_align": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P]),
-    "w4a16_select": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(Config)]),
+    "w4a16_select": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(Config)]),
     "w4a16_mxfp4_select": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(Config)]),
-    "w4a16_indexed_config": (_I32, [_I32, ctypes.POINTER(Config)]),
-    "w4a16_moe_gemm_workspace_bytes": (_SZ, [ctypes.POINTER(WeightDesc), _I32, _I32, _I32,
+    "w4a16_indexed_config": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(Config)]),
+    "w4a16_moe_gemm_workspace_bytes": (_SZ, [ctypes.POINTER(WeightDesc), ctypes.POINTER(IndexedRouting), _I32,
                                              ctypes.POINTER(Config)]),
     "w4a16_moe_gemm": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I64, _I32,
                               ctypes.POINTER(IndexedRouting), _P, _P, ctypes.POINTER(Config),
@@ -81,9 +84,10 @@ SIGNATURES = {
     "w4a16_moe_gate_up_silu": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I64,
                                       ctypes.POINTER(IndexedRouting), _P, ctypes.POINTER(Config), _P]),
     "w4a16_grouped_contiguous": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I64, _P, _P,
-                                        ctypes.POINTER(Config), _P]),
+                                        ctypes.POINTER(Config), _P, _SZ, _P]),
     "w4a16_grouped_masked": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I32, _P, _I32, _P,
-                                    ctypes.POINTER(Config), _P]),
+                                    ctypes.POINTER(Config), _P, _SZ, _P]),
+    "w4a16_grouped_workspace_bytes": (_SZ, [ctypes.POINTER(WeightDesc), _I32, _I64, _I32, ctypes.POINTER(Config)]),
     "w4a16_mxfp4_weight_desc_init": (_I32, [_I32, _I32, _I32, ctypes.POINTER(WeightDesc)]),
     "w4a16_mxfp4_weight_desc_init_gate_up": (_I32, [_I32, _I32, _I32, ctypes.POINTER(WeightDesc)]),
     "w4a16_mxfp4_gate_up_silu": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _P, _I64,

@@ -25,8 +25,8 @@ from typing import Optional
 
 import torch
 
-from ._lib import (A_SLOT, A_SORTED, A_TOKEN, DESC_GATE_UP, DESC_MXFP4, Config, IndexedRouting,
-                   W4A16Error, WeightDesc, check, load)
+from ._lib import (A_SLOT, A_SORTED, A_TOKEN, DESC_GATE_UP, DESC_MXFP4, ROUTE_CONTIGUOUS, ROUTE_INDEXED,
+                   ROUTE_MASKED, Config, IndexedRouting, W4A16Error, WeightDesc, check, load)
 
 
 def _stream(dev: torch.device) -> ctypes.c_void_p:
@@ -128,7 +128,7 @@ class Routing:
         return IndexedRouting(self.sorted_ids.data_ptr(), self.expert_ids.data_ptr(),
                               self.num_tokens_padded.data_ptr(), self.capacity, self.block_m,
                               self.T, self.topk, self.topk_ids.data_ptr(), self.first_expert,
-                              self.E_loc)
+                              self.E_loc, self.E_glob)
 
 
 def align_capacity(T: int, topk: int, E_loc: int, block_m: int) -> int:
@@ -154,30 +154,55 @@ def moe_align(topk_ids: torch.Tensor, E_glob: int, first_expert: int, E_loc: int
     return Routing(sorted_ids, expert_ids, ntp, block_m, topk_ids, E_glob, first_expert, E_loc)
 
 
-def select(T: int, topk: int, E_glob: int, E_loc: int, N: int, K: int) -> Config:
+_KINDS = {"indexed": ROUTE_INDEXED, "contiguous": ROUTE_CONTIGUOUS, "masked": ROUTE_MASKED}
+
+
+def select(T: int, topk: int, E_glob: int, E_loc: int, N: int, K: int, kind: str = "indexed",
+           expected_m: int = 0) -> Config:
+    """The library's tile choice (w4a16_select).  kind "indexed": T tokens,
+    top-k of E_glob experts, E_loc local; "contiguous": T = rows of the
+    layout, E_loc experts; "masked": T = max_m, E_loc groups, expected_m."""
     c = Config()
-    check(load().w4a16_select(T, topk, E_glob, E_loc, N, K, ctypes.byref(c)))
+    check(load().w4a16_select(T, topk, E_glob, E_loc, N, K, _KINDS[kind], expected_m, ctypes.byref(c)))
     return c
 
 
-def config(block_m: int, nr: int, waves: int = 4, split_k: int = 1, stages: int = 2) -> Config:
-    """split_k = 1: one workgroup per tile; 0: stream-K over resident workgroups.
+def config(block_m: int, nr: int, waves: int = 4, split_k: int = 1, stages: int = 2,
+           kind: str = "indexed") -> Config:
+    """split_k = 1: one workgroup per tile; 2, 4, 8, 16: K slices per tile,
+    reduced in slice order; 0: stream-K over resident workgroups.
     stages: K chunks of weights in flight per wave (2, or 4 for small tiles)."""
-    return Config(block_m, nr, waves, split_k, stages)
+    return Config(block_m, nr, waves, split_k, stages, _KINDS[kind])
 
 
-def indexed_config(block_m: int) -> Config:
-    """The config moe_w4a16_gemm uses by default for routing aligned to block_m."""
+def indexed_config(routing: "Routing", packed: PackedW4) -> Config:
+    """The config moe_w4a16_gemm uses when cfg is None: the selector's choice
+    for the routing's shape with the routing's block_m."""
     c = Config()
-    check(load().w4a16_indexed_config(block_m, ctypes.byref(c)))
+    check(load().w4a16_indexed_config(routing.T, routing.topk, routing.E_glob, routing.E_loc, packed.N, packed.K,
+                                      routing.block_m, ctypes.byref(c)))
     return c
 
 
-def workspace_bytes(packed: PackedW4, T: int, topk: int, combine: bool,
-                    cfg: Optional[Config] = None) -> int:
+def workspace_bytes(packed: PackedW4, routing: "Routing", combine: bool, cfg: Optional[Config] = None) -> int:
+    """Workspace bytes of moe_w4a16_gemm (zero-fill it once before first use)."""
+    r = routing.as_c()
     return int(load().w4a16_moe_gemm_workspace_bytes(
-        ctypes.byref(packed.desc), T, topk, int(bool(combine)),
+        ctypes.byref(packed.desc), ctypes.byref(r), int(bool(combine)),
         None if cfg is None else ctypes.byref(cfg)))
+
+
+def grouped_workspace_bytes(packed: PackedW4, kind: str, rows: int, expected_m: int = 0,
+                            cfg: Optional[Config] = None) -> int:
+    """Workspace bytes of a grouped call ("contiguous": rows = m_rows;
+    "masked": rows = max_m, with its expected_m)."""
+    return int(load().w4a16_grouped_workspace_bytes(ctypes.byref(packed.desc), _KINDS[kind], rows, expected_m,
+                                                    None if cfg is None else ctypes.byref(cfg)))
+
+
+def _workspace(nbytes: int, dev: torch.device) -> Optional[torch.Tensor]:
+    # zero-filled: split-K arrival counters start at zero (calls leave them so)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
 
 
 _A_LAYOUTS = {"token": A_TOKEN, "slot": A_SLOT, "sorted": A_SORTED}
@@ -213,12 +238,8 @@ def moe_w4a16_gemm(a: torch.Tensor, packed: PackedW4, routing: Routing,
         _need(out, "out", _BF16, 2)
         if out.shape[0] < rows or out.shape[1] != packed.N:
             raise ValueError(f"out must be [{rows}, {packed.N}]")
-    if cfg is None:
-        cfg = indexed_config(routing.block_m)
     if workspace is None:
-        nws = workspace_bytes(packed, T, k, combine, cfg)
-        if nws:
-            workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+        workspace = _workspace(workspace_bytes(packed, routing, combine, cfg), dev)
     r = routing.as_c()
     check(load().w4a16_moe_gemm(ctypes.byref(packed.desc), packed.w.data_ptr(), packed.s.data_ptr(),
                                 a.data_ptr(), a.shape[0], _A_LAYOUTS[a_layout], ctypes.byref(r),
@@ -245,19 +266,19 @@ def moe_gate_up_silu(x: torch.Tensor, packed: PackedW4, routing: Routing,
         _need(out, "out", _BF16, 2)
         if out.shape[0] < routing.capacity or out.shape[1] != packed.N // 2:
             raise ValueError(f"out must be [{routing.capacity}, {packed.N // 2}]")
-    if cfg is None:
-        cfg = indexed_config(routing.block_m)
     r = routing.as_c()
     check(load().w4a16_moe_gate_up_silu(ctypes.byref(packed.desc), packed.w.data_ptr(), packed.s.data_ptr(),
                                         x.data_ptr(), x.shape[0], ctypes.byref(r), out.data_ptr(),
-                                        ctypes.byref(cfg), _stream(x.device)))
+                                        None if cfg is None else ctypes.byref(cfg), _stream(x.device)))
     return out
 
 
 def grouped_contiguous(a: torch.Tensor, packed: PackedW4, m_indices: torch.Tensor,
-                       cfg: Optional[Config] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                       cfg: Optional[Config] = None, out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """a [m, K] (experts' rows back to back, 128-row aligned segments),
-    m_indices int32 [m] (-1 on padding) -> out [m, N]."""
+    m_indices int32 [m] (-1 on padding) -> out [m, N].  cfg: None (the
+    call's own selection) or select(..., kind="contiguous")."""
     _need(a, "a", _BF16, 2)
     _need(m_indices, "m_indices", (torch.int32,), 1)
     m = a.shape[0]
@@ -265,16 +286,22 @@ def grouped_contiguous(a: torch.Tensor, packed: PackedW4, m_indices: torch.Tenso
         raise ValueError("a / m_indices / weight shapes disagree")
     if out is None:
         out = torch.zeros(m, packed.N, dtype=torch.bfloat16, device=a.device)
+    if workspace is None:
+        workspace = _workspace(grouped_workspace_bytes(packed, "contiguous", m, 0, cfg), a.device)
     check(load().w4a16_grouped_contiguous(ctypes.byref(packed.desc), packed.w.data_ptr(),
                                           packed.s.data_ptr(), a.data_ptr(), m, m_indices.data_ptr(),
                                           out.data_ptr(), None if cfg is None else ctypes.byref(cfg),
+                                          _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                           _stream(a.device)))
     return out
 
 
 def grouped_masked(a: torch.Tensor, packed: PackedW4, masked_m: torch.Tensor, expected_m: int,
-                   cfg: Optional[Config] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """a [E, max_m, K], masked_m int32 [E] -> out flat [E * max_m, N]."""
+                   cfg: Optional[Config] = None, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """a [E, max_m, K], masked_m int32 [E] -> out flat [E * max_m, N].
+    cfg: None (the call's own selection from expected_m) or
+    select(..., kind="masked")."""
     _need(a, "a", _BF16, 3)
     _need(masked_m, "masked_m", (torch.int32,), 1)
     G, max_m, K = a.shape
@@ -282,16 +309,21 @@ def grouped_masked(a: torch.Tensor, packed: PackedW4, masked_m: torch.Tensor, ex
         raise ValueError("a / masked_m / weight shapes disagree")
     if out is None:
         out = torch.zeros(G * max_m, packed.N, dtype=torch.bfloat16, device=a.device)
+    if workspace is None:
+        workspace = _workspace(grouped_workspace_bytes(packed, "masked", max_m, int(expected_m), cfg), a.device)
     check(load().w4a16_grouped_masked(ctypes.byref(packed.desc), packed.w.data_ptr(),
                                       packed.s.data_ptr(), a.data_ptr(), max_m, masked_m.data_ptr(),
                                       int(expected_m), out.data_ptr(),
-                                      None if cfg is None else ctypes.byref(cfg), _stream(a.device)))
+                                      None if cfg is None else ctypes.byref(cfg),
+                                      _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                      _stream(a.device)))
     return out
 
 
 __all__ = [
     "W4A16Error", "PackedW4", "Routing", "Config", "weight_desc", "pack_w4", "align_capacity",
-    "moe_align", "select", "config", "indexed_config", "workspace_bytes", "moe_w4a16_gemm", "moe_gate_up_silu",
+    "moe_align", "select", "config", "indexed_config", "workspace_bytes", "grouped_workspace_bytes", "moe_w4a16_gemm",
+    "moe_gate_up_silu",
     "grouped_contiguous",
     "grouped_masked",
 ]

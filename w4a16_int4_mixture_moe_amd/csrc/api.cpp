@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -121,15 +122,25 @@ bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm =
 // Chord W4A16 MoE post, section "H200 prefill and TP8": block_m is chosen from
 // tokens per expert tok_e = routed rows / experts; below about 80 a search
 // minimises the total number of blocks on sampled routing, above it the
-// padded expert rows are fitted under a maximum block_m.  On gfx950 the
-// kernel skips 16-row token tiles that hold no valid row, so MFMA work
-// follows valid rows whatever block_m is, while every extra block of an
-// expert re-reads and re-dequantises its weights.  So:
+// padded expert rows are fitted under a maximum block_m; K is split only
+// where the plain grid leaves the machine underfilled.  On gfx950 the kernel
+// skips 16-row token tiles that hold no valid row, so MFMA work follows valid
+// rows whatever block_m is, while every extra block of an expert re-reads and
+// re-dequantises its weights.  So:
 //   - decode side (tok_e < kPrefillTokE): sample per-expert counts, pick the
 //     smallest block_m whose total block count is within 2 % of the minimum
 //     (smaller blocks keep fewer accumulators live and more waves resident);
 //   - prefill side: block_m 128 (largest tile the accumulators allow), two
-//     weight tiles per wave (measured faster than four at 128 rows).
+//     weight tiles per wave (measured faster than four at 128 rows);
+//   - split_k doubles while the doubled grid stays within 4/5 of one round
+//     of resident workgroups and each slice keeps kMinSliceChunks chunks
+//     (measured on MI355X, gate/up K = 7168: TP8 T = 1, 32 tiles, 32.3 us
+//     unsplit, 13.1 us at 8 slices; EP32 decode, 384 tiles, 47.7 -> 40.2 us
+//     at 2, slower at 4; EP16 decode, 768 tiles, and TP8 T = 16, 456 tiles,
+//     no faster split).
+// The machine model is fixed (256 CUs, resident workgroups per CU of each
+// tile from its register use), so the choice is deterministic and available
+// without a device.
 constexpr double kPrefillTokE = 48.0;
 // A4W4: above this many rows per expert the MXFP4 GEMM takes 64-row blocks
 // where the W4A16 rule gives 128 (measured on MI355X, step time: EP8 / EP16
@@ -137,9 +148,17 @@ constexpr double kPrefillTokE = 48.0;
 // 128 stays 6 % faster, since 64 would split most experts into two blocks
 // that each stream the expert's weights).
 constexpr double kMxHalfTileTokE = 128.0;
+constexpr int kCUs = 256;
+constexpr int kMinSliceChunks = 4;    // 512 K elements per slice at least
+constexpr int kMaxSplit = 16;
+// split-K slices are kept for at most this many tiles per call (a tile past
+// it runs whole in one workgroup); the selector splits only grids below one
+// round of resident workgroups, so real grids stay well under it
+constexpr int kSplitTileCap = 2048;
 
 std::mutex g_cache_mu;
-std::map<std::tuple<int, int, int, int, int, int>, w4a16_config> g_cache;
+typedef std::tuple<int, int, int, int, int, int, int, int> SelectKey;
+std::map<SelectKey, w4a16_config> g_cache;
 
 int64_t sampled_blocks(const std::vector<int>& counts, int bm) {
   int64_t b = 0;
@@ -147,23 +166,53 @@ int64_t sampled_blocks(const std::vector<int>& counts, int bm) {
   return b;
 }
 
-int resident_workgroups(const w4a16_config& c, int epi);
+// Resident workgroups per CU of the one-workgroup-per-tile kernel with this
+// tile (four waves; register use of the gfx950 build: 16- and 32-row blocks
+// fit four workgroups per CU, 64-row blocks three, 128-row blocks two).
+int resident_per_cu(int block_m) { return block_m <= 32 ? 4 : block_m == 64 ? 3 : 2; }
 
-w4a16_config select_config(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc) {
-  w4a16_config c;
-  c.waves = 4;
-  c.split_k = 1;
-  c.stages = 2;
-  const double tok_e = (double)T * topk / std::max(E_glob, 1);
-  // sampled routing: each of T*topk slots lands on one of E_glob experts
-  // uniformly; keep the local ones (fixed seed: deterministic choice)
+int n_tiles_of(int N, int nr, int waves) {
+  const int tiles_per_wg = nr * waves;
+  return (N / 16 + tiles_per_wg - 1) / tiles_per_wg;
+}
+
+int chunks_of(int K) { return (K + 127) / 128; }
+
+// split_k for a grid of `tiles` one-workgroup tiles over K
+int choose_split(int64_t tiles, int block_m, int K) {
+  const int64_t resident = (int64_t)kCUs * resident_per_cu(block_m);
+  const int KC = chunks_of(K);
+  int split = 1;
+  while (split < kMaxSplit && tiles * split * 2 * 5 <= resident * 4 && KC / (2 * split) >= kMinSliceChunks)
+    split *= 2;
+  return split;
+}
+
+// per-expert counts of a seeded multinomial sample of the routing: each of
+// T * topk slots lands on one of E_glob experts uniformly; the local ones kept
+std::vector<int> sampled_counts(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc) {
   std::mt19937 rng(12345u);
   std::vector<int> counts(std::max(E_loc, 1), 0);
   std::binomial_distribution<int> bin(std::max(T, 0) * std::max(topk, 1), 1.0 / std::max(E_glob, 1));
   for (int e = 0; e < E_loc; ++e) counts[e] = bin(rng);
-  if (tok_e >= kPrefillTokE) {
+  return counts;
+}
+
+// Indexed config; block_m chosen by the tok_e rule, or forced (> 0) when the
+// routing buffers already fix it.
+w4a16_config select_indexed(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N, int32_t K,
+                            int32_t force_block_m) {
+  w4a16_config c;
+  c.kind = W4A16_ROUTE_INDEXED;
+  c.waves = 4;
+  c.stages = 2;
+  c.nr = 2;  // measured: two 16-row weight tiles per wave beat four at 128 rows
+  const double tok_e = (double)T * topk / std::max(E_glob, 1);
+  const std::vector<int> counts = sampled_counts(T, topk, E_glob, E_loc);
+  if (force_block_m > 0) {
+    c.block_m = force_block_m;
+  } else if (tok_e >= kPrefillTokE) {
     c.block_m = 128;
-    c.nr = 2;  // measured: two 16-row weight tiles per wave beat four at 128 rows
   } else {
     const int cands[3] = {16, 32, 64};
     int64_t best = INT64_MAX;
@@ -174,16 +223,46 @@ w4a16_config select_config(int32_t T, int32_t topk, int32_t E_glob, int32_t E_lo
         c.block_m = bm;
         break;
       }
-    c.nr = 2;
   }
-  // One workgroup per tile throughout.  Stream-K (split_k = 0) stays
-  // available as an explicit config; the post gates it by shape (section
-  // "H200 prefill and TP8"), but measured on MI355X against the current
-  // one-workgroup kernel it no longer wins anywhere on the step: TP8 T = 1
-  // 0.051 vs 0.059 ms, TP8 T = 16 0.095 vs 0.118, EP32 decode 0.089 vs
-  // 0.104 (one workgroup per tile first), the down projection losing most
-  // (its fix-up pass and per-segment pipeline restarts against K = 256 or
-  // 2048).
+  const int64_t tiles = sampled_blocks(counts, c.block_m) * n_tiles_of(N, c.nr, c.waves);
+  c.split_k = choose_split(tiles, c.block_m, K);
+  return c;
+}
+
+// Contiguous grouped layout: 128-row blocks when their grid fills the
+// machine, else 64 (post, section "Grouped SM90 kernels": BM128 for large
+// grids, BM64 for small concatenated problems so M tiles still fill).
+w4a16_config select_contiguous(int64_t m_rows, int32_t E, int32_t N, int32_t K) {
+  (void)E;
+  w4a16_config c;
+  c.kind = W4A16_ROUTE_CONTIGUOUS;
+  c.nr = 2;
+  c.waves = 4;
+  c.stages = 2;
+  const int nt = n_tiles_of(N, c.nr, c.waves);
+  const int64_t grid128 = (m_rows + 127) / 128 * nt;
+  c.block_m = grid128 >= (int64_t)kCUs * resident_per_cu(128) ? 128 : 64;
+  c.split_k = choose_split((m_rows + c.block_m - 1) / c.block_m * nt, c.block_m, K);
+  return c;
+}
+
+// Masked grouped layout (post, section "Grouped SM90 kernels"): a group that
+// spills into a second M tile re-reads all of K, so deep-K projections cover
+// about 1.3 x expected_m rows; short-K ones take the leaner
+// ceil(1.25 x expected_m, 8).  Rounded up to a built block (at most 128).
+// Buffered K follows latency: 512 elements (four 128-K stages) for decode-size
+// blocks, two stages for larger ones.
+w4a16_config select_masked(int32_t max_m, int32_t E, int32_t N, int32_t K, int32_t expected_m) {
+  w4a16_config c;
+  c.kind = W4A16_ROUTE_MASKED;
+  c.nr = 2;
+  c.waves = 4;
+  const int em = std::max(1, std::min(expected_m, max_m));
+  const int want = K >= 4096 ? (int)std::ceil(1.3 * em) : (int)round_up((int64_t)std::ceil(1.25 * em), 8);
+  c.block_m = want <= 16 ? 16 : want <= 32 ? 32 : want <= 64 ? 64 : 128;
+  c.stages = c.block_m <= 32 ? 4 : 2;
+  const int64_t blocks = (int64_t)E * ((std::min(em, max_m) + c.block_m - 1) / c.block_m);
+  c.split_k = choose_split(blocks * n_tiles_of(N, c.nr, c.waves), c.block_m, K);
   return c;
 }
 
@@ -192,20 +271,41 @@ const char* env_str(const char* name) {
   return (v && *v) ? v : nullptr;
 }
 
-// W4A16_BLOCK_M / W4A16_NR / W4A16_WAVES / W4A16_SPLIT_K / W4A16_STAGES override the selector (read on
-// every call; the memoised result is the selector's, overrides are applied on top).
-void apply_env_overrides(w4a16_config* c) {
-  if (const char* v = env_str("W4A16_BLOCK_M")) c->block_m = std::atoi(v);
+const char* const kOverrideVars[5] = {"W4A16_BLOCK_M", "W4A16_NR", "W4A16_WAVES", "W4A16_SPLIT_K", "W4A16_STAGES"};
+
+// W4A16_BLOCK_M / W4A16_NR / W4A16_WAVES / W4A16_SPLIT_K / W4A16_STAGES override the indexed selector
+// (read on every call; the memoised result is the selector's, overrides are applied on top).
+// block_m is left alone when the routing already fixes it.
+void apply_env_overrides(w4a16_config* c, bool block_m_free) {
+  if (const char* v = env_str("W4A16_BLOCK_M"))
+    if (block_m_free) c->block_m = std::atoi(v);
   if (const char* v = env_str("W4A16_NR")) c->nr = std::atoi(v);
   if (const char* v = env_str("W4A16_WAVES")) c->waves = std::atoi(v);
   if (const char* v = env_str("W4A16_SPLIT_K")) c->split_k = std::atoi(v);
   if (const char* v = env_str("W4A16_STAGES")) c->stages = std::atoi(v);
 }
 
-w4a16_status check_config(const w4a16_config& c, int route, int epi) {
+// the first tuning override set in the environment, or NULL
+const char* env_override_present() {
+  for (const char* name : kOverrideVars)
+    if (env_str(name)) return name;
+  return nullptr;
+}
+
+bool valid_split(int split) { return split == 0 || split == 1 || split == 2 || split == 4 || split == 8 || split == 16; }
+
+w4a16_status check_config(const w4a16_config& c, int route, int epi, int K) {
+  if (c.kind != route)
+    return fail(W4A16_ERR_ARG, "config was chosen for routing kind %d, this call is kind %d (%s)", c.kind, route,
+                route == W4A16_ROUTE_INDEXED ? "indexed" : "grouped calls choose their own tiles");
   if (!valid_block_m(c.block_m)) return fail(W4A16_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128}", c.block_m);
-  if (c.split_k != 0 && c.split_k != 1)
-    return fail(W4A16_ERR_UNSUPPORTED, "split_k %d: 0 (stream-K) or 1 (one workgroup per tile)", c.split_k);
+  if (!valid_split(c.split_k))
+    return fail(W4A16_ERR_UNSUPPORTED, "split_k %d: 1 (one workgroup per tile), 2, 4, 8, 16 (K slices) or 0 (stream-K)",
+                c.split_k);
+  if (c.split_k == 0 && route != W4A16_ROUTE_INDEXED)
+    return fail(W4A16_ERR_UNSUPPORTED, "stream-K (split_k = 0) is built for indexed routing only");
+  if (c.split_k > 1 && c.split_k > chunks_of(K))
+    return fail(W4A16_ERR_UNSUPPORTED, "split_k %d exceeds the %d 128-K chunks of K = %d", c.split_k, chunks_of(K), K);
   if (!w4a16::gemm_config_supported(route, epi, c.block_m / 16, c.nr, c.waves, c.stages))
     return fail(W4A16_ERR_UNSUPPORTED, "tile config block_m=%d nr=%d waves=%d stages=%d not built", c.block_m,
                 c.nr, c.waves, c.stages);
@@ -224,40 +324,93 @@ w4a16::GemmParams base_params(const w4a16_weight_desc* d, const void* pw, const 
   p.K = d->K;
   p.NT = d->N / 16;
   p.KC = d->K_pad / 128;
-  const int tiles_per_wg = nr * waves;
-  p.n_tiles = (p.NT + tiles_per_wg - 1) / tiles_per_wg;
+  p.n_tiles = n_tiles_of(d->N, nr, waves);
   p.gated = (d->flags & W4A16_DESC_GATE_UP) != 0;
   p.out = out;
+  p.split = 1;
   return p;
 }
 
-// Workspace carve-up: [combine partials, fp32 T*topk*N][stream-K partial tiles]
-size_t combine_region(int32_t T, int32_t topk, int32_t N, bool combine) {
-  return combine ? (size_t)round_up((int64_t)T * topk * N * (int64_t)sizeof(float), 256) : 0;
+// Workspace carve-up (each region 256-byte aligned):
+//   [split counters, 4 B per splittable tile][split slices][combine partials, fp32 T*topk*N][stream-K partials]
+struct Workspace {
+  size_t counters = 0, slices = 0, combine = 0, streamk = 0;
+  int split_tiles = 0;
+  size_t total() const { return counters + slices + combine + streamk; }
+};
+
+size_t al256(size_t v) { return (v + 255) / 256 * 256; }
+
+int resident_workgroups(const w4a16_config& c, int epi);
+
+// tiles: an upper bound of the call's tiles (routed blocks x N tiles)
+Workspace workspace_layout(const w4a16_config& c, int epi, int64_t tiles, int32_t N, int32_t T, int32_t topk,
+                           bool combine) {
+  Workspace w;
+  if (c.split_k > 1) {
+    w.split_tiles = (int)std::min<int64_t>(std::max<int64_t>(tiles, 0), kSplitTileCap);
+    w.counters = al256((size_t)w.split_tiles * 4);
+    w.slices = al256((size_t)w.split_tiles * c.split_k * w4a16::split_slice_bytes(c.block_m / 16, c.nr, c.waves));
+  }
+  if (combine) w.combine = al256((size_t)T * topk * N * sizeof(float));
+  if (c.split_k == 0) {
+    const int wgs = resident_workgroups(c, epi);
+    if (wgs > 0) w.streamk = w4a16::streamk_partial_bytes(c.block_m / 16, c.nr, c.waves, wgs);
+  }
+  return w;
 }
 
-size_t streamk_region(const w4a16_config& c, int epi) {
-  if (c.split_k != 0) return 0;
-  const int wgs = resident_workgroups(c, epi);
-  if (wgs <= 0) return 0;
-  return w4a16::streamk_partial_bytes(c.block_m / 16, c.nr, c.waves, wgs);
+void attach_split(w4a16::GemmParams& p, const w4a16_config& c, const Workspace& w, char* ws) {
+  p.split = std::max(c.split_k, 1);
+  if (c.split_k > 1) {
+    p.split_tiles = w.split_tiles;
+    p.split_count = reinterpret_cast<uint32_t*>(ws);
+    p.split_partial = reinterpret_cast<float*>(ws + w.counters);
+  }
 }
 
-w4a16_config default_indexed_config(int32_t block_m) {
-  w4a16_config c;
-  c.block_m = block_m;
-  c.nr = 2;
-  c.waves = 4;
-  c.split_k = 1;
-  c.stages = 2;
-  apply_env_overrides(&c);
-  return c;
+// Upper bound of the routed blocks of an indexed call: every local expert with
+// rows adds at most one partial block, and there are at most T * topk local
+// slots (so at most that many experts with rows).
+int64_t indexed_block_bound(const w4a16_indexed_routing& r) {
+  const int64_t slots = (int64_t)r.T * r.topk;
+  return std::min<int64_t>(r.capacity / std::max(r.block_m, 1),
+                           (slots + r.block_m - 1) / r.block_m + std::min<int64_t>(r.E_loc, slots));
 }
 
 // Workgroups of this config the current device keeps resident (stream-K
 // grid); 0 when no device is visible or the config is not built.
 int resident_workgroups(const w4a16_config& c, int epi) {
   return w4a16::streamk_workgroups(w4a16::kRouteIndexed, epi, c.block_m / 16, c.nr, c.waves, c.stages);
+}
+
+// select_indexed, memoised per argument set (no environment overrides)
+w4a16_config cached_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N, int32_t K,
+                           int32_t kind, int32_t expected_m, int32_t force_block_m) {
+  const SelectKey key = std::make_tuple(T, topk, E_glob, E_loc, N, K, kind * 1024 + force_block_m, expected_m);
+  {
+    std::lock_guard<std::mutex> g(g_cache_mu);
+    auto it = g_cache.find(key);
+    if (it != g_cache.end()) return it->second;
+  }
+  w4a16_config c;
+  if (kind == W4A16_ROUTE_CONTIGUOUS)
+    c = select_contiguous(T, E_loc, N, K);
+  else if (kind == W4A16_ROUTE_MASKED)
+    c = select_masked(T, E_loc, N, K, expected_m);
+  else
+    c = select_indexed(T, topk, E_glob, E_loc, N, K, force_block_m);
+  std::lock_guard<std::mutex> g(g_cache_mu);
+  g_cache[key] = c;
+  return c;
+}
+
+// An activation / output tensor the kernels address with 32-bit byte offsets.
+w4a16_status check_offset_range(int64_t rows, int32_t K, const char* what) {
+  if (rows > 0 && rows * (int64_t)K * 2 > ((int64_t)1 << 32))
+    return fail(W4A16_ERR_SHAPE, "%s: %lld rows x K = %d x 2 bytes exceed the 4 GiB the kernels address", what,
+                (long long)rows, K);
+  return W4A16_OK;
 }
 
 }  // namespace
@@ -339,35 +492,78 @@ w4a16_status w4a16_moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, i
   return W4A16_OK;
 }
 
-w4a16_status w4a16_indexed_config(int32_t block_m, w4a16_config* out) {
-  if (!out) return fail(W4A16_ERR_ARG, "out is NULL");
-  if (!valid_block_m(block_m)) return fail(W4A16_ERR_ARG, "block_m %d not in {16, 32, 64, 128}", block_m);
-  *out = default_indexed_config(block_m);
+}  // extern "C"
+
+namespace {
+
+// The indexed config of a call: cfg, or the selector's choice for the
+// routing's shape and block_m with environment overrides applied.
+w4a16_status indexed_call_config(const w4a16_indexed_routing& r, const w4a16_weight_desc* d, const w4a16_config* cfg,
+                                 w4a16_config* out) {
+  if (cfg) {
+    *out = *cfg;
+    return W4A16_OK;
+  }
+  if (r.E_glob <= 0) return fail(W4A16_ERR_ARG, "routing.E_glob must be positive (it steers the config when cfg is NULL)");
+  *out = cached_select(r.T, r.topk, r.E_glob, r.E_loc, d->N, d->K, W4A16_ROUTE_INDEXED, 0, r.block_m);
+  apply_env_overrides(out, false);
   return W4A16_OK;
 }
 
-// select_config, memoised per argument set of the public call (no
-// environment overrides)
-w4a16_config cached_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N, int32_t K) {
-  const auto key = std::make_tuple(T, topk, E_glob, E_loc, N, K);
-  {
-    std::lock_guard<std::mutex> g(g_cache_mu);
-    auto it = g_cache.find(key);
-    if (it != g_cache.end()) return it->second;
-  }
-  const w4a16_config c = select_config(T, topk, E_glob, E_loc);
-  std::lock_guard<std::mutex> g(g_cache_mu);
-  g_cache[key] = c;
-  return c;
+// Checks shared by the indexed W4A16 calls; fills the activation rows the
+// call may read.
+w4a16_status check_indexed_call(const w4a16_weight_desc* desc, const void* packed_w, const void* packed_s,
+                                const void* a, const void* out, const w4a16_indexed_routing* routing) {
+  w4a16_status st = check_int4_desc(desc);
+  if (st != W4A16_OK) return st;
+  if (!routing) return fail(W4A16_ERR_ARG, "routing is NULL");
+  const w4a16_indexed_routing& r = *routing;
+  if (!packed_w || !packed_s || !r.sorted_ids || !r.expert_ids || !r.num_tokens_padded)
+    return fail(W4A16_ERR_ARG, "NULL pointer argument");
+  if (r.T < 0 || r.topk <= 0 || r.capacity < 0 || r.E_loc <= 0) return fail(W4A16_ERR_ARG, "bad routing sizes");
+  if (r.T > 0 && (!a || !out)) return fail(W4A16_ERR_ARG, "activations or output are NULL");
+  if (!aligned16(packed_w) || !aligned16(packed_s) || !aligned16(a) || !aligned16(out))
+    return fail(W4A16_ERR_ARG, "packed weights, activations and output must be 16-byte aligned");
+  if (r.E_loc != desc->E)
+    return fail(W4A16_ERR_LAYOUT, "routing has E_loc=%d but the packed weight holds %d experts", r.E_loc, desc->E);
+  if (!valid_block_m(r.block_m)) return fail(W4A16_ERR_ARG, "routing.block_m %d not in {16, 32, 64, 128}", r.block_m);
+  if ((int64_t)r.T * r.topk >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "T*topk too large");
+  if (r.capacity % r.block_m) return fail(W4A16_ERR_CAPACITY, "capacity not a multiple of block_m");
+  if (r.capacity / r.block_m > INT32_MAX / 2) return fail(W4A16_ERR_CAPACITY, "capacity too large");
+  return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+w4a16_status w4a16_indexed_config(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N, int32_t K,
+                                  int32_t block_m, w4a16_config* out) {
+  if (!out) return fail(W4A16_ERR_ARG, "out is NULL");
+  if (!valid_block_m(block_m)) return fail(W4A16_ERR_ARG, "block_m %d not in {16, 32, 64, 128}", block_m);
+  if (T < 0 || topk <= 0 || E_glob <= 0 || E_loc <= 0 || N <= 0 || K <= 0)
+    return fail(W4A16_ERR_ARG, "bad sizes for indexed_config");
+  *out = cached_select(T, topk, E_glob, E_loc, N, K, W4A16_ROUTE_INDEXED, 0, block_m);
+  apply_env_overrides(out, false);
+  return W4A16_OK;
 }
 
 w4a16_status w4a16_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N,
-                          int32_t K, w4a16_config* out) {
+                          int32_t K, int32_t kind, int32_t expected_m, w4a16_config* out) {
   if (!out) return fail(W4A16_ERR_ARG, "out is NULL");
-  if (T < 0 || topk <= 0 || E_glob <= 0 || E_loc <= 0 || N <= 0 || K <= 0)
-    return fail(W4A16_ERR_ARG, "bad sizes for select");
-  *out = cached_select(T, topk, E_glob, E_loc, N, K);
-  apply_env_overrides(out);
+  if (T < 0 || E_loc <= 0 || N <= 0 || K <= 0) return fail(W4A16_ERR_ARG, "bad sizes for select");
+  if (kind == W4A16_ROUTE_INDEXED) {
+    if (topk <= 0 || E_glob <= 0) return fail(W4A16_ERR_ARG, "bad sizes for select");
+    *out = cached_select(T, topk, E_glob, E_loc, N, K, kind, 0, 0);
+    apply_env_overrides(out, true);
+    return W4A16_OK;
+  }
+  if (kind != W4A16_ROUTE_CONTIGUOUS && kind != W4A16_ROUTE_MASKED)
+    return fail(W4A16_ERR_ARG, "kind %d is not a W4A16_ROUTE_* value", kind);
+  if (const char* v = env_override_present())
+    return fail(W4A16_ERR_ARG, "%s is set: tuning overrides apply to indexed routing only; grouped calls choose their own tiles", v);
+  if (kind == W4A16_ROUTE_MASKED && expected_m <= 0) return fail(W4A16_ERR_ARG, "expected_m must be positive");
+  *out = cached_select(T, 1, 1, E_loc, N, K, kind, kind == W4A16_ROUTE_MASKED ? expected_m : 0, 0);
   return W4A16_OK;
 }
 
@@ -376,7 +572,7 @@ w4a16_status w4a16_mxfp4_select(int32_t T, int32_t topk, int32_t E_glob, int32_t
   if (!out) return fail(W4A16_ERR_ARG, "out is NULL");
   if (T < 0 || topk <= 0 || E_glob <= 0 || E_loc <= 0 || N <= 0 || K <= 0)
     return fail(W4A16_ERR_ARG, "bad sizes for select");
-  w4a16_config c = cached_select(T, topk, E_glob, E_loc, N, K);
+  w4a16_config c = cached_select(T, topk, E_glob, E_loc, N, K, W4A16_ROUTE_INDEXED, 0, 0);
   const double tok_e = (double)T * topk / E_glob;
   if (c.block_m == 128 && tok_e >= kMxHalfTileTokE) c.block_m = 64;
   c.nr = 4;
@@ -384,38 +580,38 @@ w4a16_status w4a16_mxfp4_select(int32_t T, int32_t topk, int32_t E_glob, int32_t
   c.split_k = 1;
   c.stages = c.block_m <= 32 ? 4 : 2;
   *out = c;
-  apply_env_overrides(out);
+  apply_env_overrides(out, true);
   return W4A16_OK;
 }
 
-size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, int32_t T, int32_t topk,
+size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, const w4a16_indexed_routing* routing,
                                       int32_t combine, const w4a16_config* cfg) {
-  if (check_int4_desc(desc) != W4A16_OK || T < 0 || topk <= 0) return 0;
-  const w4a16_config c = cfg ? *cfg : default_indexed_config(16);
+  if (check_int4_desc(desc) != W4A16_OK || !routing) return 0;
+  const w4a16_indexed_routing& r = *routing;
+  if (r.T < 0 || r.topk <= 0 || r.E_loc <= 0 || !valid_block_m(r.block_m) || r.capacity < 0) return 0;
+  w4a16_config c;
+  if (indexed_call_config(r, desc, cfg, &c) != W4A16_OK) return 0;
   const int epi = combine ? w4a16::kEpiWeighted : w4a16::kEpiStore;
-  if (check_config(c, w4a16::kRouteIndexed, epi) != W4A16_OK) return 0;
-  return combine_region(T, topk, desc->N, combine != 0) + streamk_region(c, epi);
+  if (check_config(c, W4A16_ROUTE_INDEXED, epi, desc->K) != W4A16_OK) return 0;
+  const int64_t tiles = indexed_block_bound(r) * n_tiles_of(desc->N, c.nr, c.waves);
+  return workspace_layout(c, epi, tiles, desc->N, r.T, r.topk, combine != 0).total();
 }
 
-w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
-                            const void* packed_s, const uint16_t* a, int64_t a_rows,
-                            int32_t a_layout, const w4a16_indexed_routing* routing,
-                            const float* topk_weights, uint16_t* out,
-                            const w4a16_config* cfg, void* workspace, size_t workspace_bytes,
-                            w4a16_stream_t stream) {
-  w4a16_status st = check_int4_desc(desc);
+}  // extern "C"
+
+namespace {
+
+// The indexed GEMM.
+w4a16_status moe_gemm_impl(const w4a16_weight_desc* desc, const void* packed_w, const void* packed_s,
+                           const uint16_t* a, int64_t a_rows, int32_t a_layout, const w4a16_indexed_routing* routing,
+                           const float* topk_weights, uint16_t* out, const w4a16_config* cfg, void* workspace,
+                           size_t workspace_bytes, w4a16_stream_t stream) {
+  w4a16_status st = check_indexed_call(desc, packed_w, packed_s, a, out, routing);
   if (st != W4A16_OK) return st;
-  if (!routing) return fail(W4A16_ERR_ARG, "routing is NULL");
   const w4a16_indexed_routing& r = *routing;
   const bool combine = topk_weights != nullptr;
-  if (!packed_w || !packed_s || !r.sorted_ids || !r.expert_ids || !r.num_tokens_padded)
-    return fail(W4A16_ERR_ARG, "NULL pointer argument");
-  if (r.T < 0 || r.topk <= 0 || r.capacity < 0) return fail(W4A16_ERR_ARG, "bad routing sizes");
-  if (r.T > 0 && (!a || !out)) return fail(W4A16_ERR_ARG, "activations or output are NULL");
-  if (!aligned16(packed_w) || !aligned16(packed_s) || !aligned16(a) || !aligned16(out))
-    return fail(W4A16_ERR_ARG, "packed weights, activations and output must be 16-byte aligned");
-  if (r.E_loc != desc->E)
-    return fail(W4A16_ERR_LAYOUT, "routing has E_loc=%d but the packed weight holds %d experts", r.E_loc, desc->E);
+  if (combine && (desc->flags & W4A16_DESC_GATE_UP))
+    return fail(W4A16_ERR_LAYOUT, "a gate/up interleaved weight cannot take the top-k combine (it belongs to the down projection)");
   if (a_layout != W4A16_A_TOKEN && a_layout != W4A16_A_SLOT && a_layout != W4A16_A_SORTED)
     return fail(W4A16_ERR_ARG, "a_layout %d is not W4A16_A_TOKEN, W4A16_A_SLOT or W4A16_A_SORTED", a_layout);
   const int64_t need_rows = a_layout == W4A16_A_TOKEN  ? (int64_t)r.T
@@ -423,32 +619,31 @@ w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
                                                        : r.capacity;
   if (a_rows < need_rows)
     return fail(W4A16_ERR_SHAPE, "activations have %lld rows, need %lld", (long long)a_rows, (long long)need_rows);
-  if ((int64_t)r.T * r.topk >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "T*topk too large");
+  st = check_offset_range(need_rows, desc->K, "activations");
+  if (st != W4A16_OK) return st;
   const int epi = combine ? w4a16::kEpiWeighted : w4a16::kEpiStore;
   w4a16_config c;
-  if (cfg) {
-    c = *cfg;
-  } else {
-    c = default_indexed_config(r.block_m);   // the routing buffers fix block_m
-  }
-  st = check_config(c, w4a16::kRouteIndexed, epi);
+  st = indexed_call_config(r, desc, cfg, &c);
+  if (st != W4A16_OK) return st;
+  st = check_config(c, W4A16_ROUTE_INDEXED, epi, desc->K);
   if (st != W4A16_OK) return st;
   if (c.block_m != r.block_m)
     return fail(W4A16_ERR_LAYOUT, "config block_m=%d differs from the routing's block_m=%d", c.block_m, r.block_m);
-  if (r.capacity % r.block_m) return fail(W4A16_ERR_CAPACITY, "capacity not a multiple of block_m");
   if (combine && !r.topk_ids) return fail(W4A16_ERR_ARG, "combine needs routing.topk_ids");
-  const size_t comb_bytes = combine_region(r.T, r.topk, desc->N, combine);
-  const size_t sk_bytes = streamk_region(c, epi);
-  if (c.split_k == 0 && sk_bytes == 0)
+  const int64_t tiles = indexed_block_bound(r) * n_tiles_of(desc->N, c.nr, c.waves);
+  const Workspace wl = workspace_layout(c, epi, tiles, desc->N, r.T, r.topk, combine);
+  if (c.split_k == 0 && wl.streamk == 0)
     return fail(W4A16_ERR_HIP, "stream-K: could not query the device's resident workgroups");
-  const size_t need = comb_bytes + sk_bytes;
+  const size_t need = wl.total();
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(W4A16_ERR_WORKSPACE, "this call needs %zu bytes of 16-byte aligned workspace, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
   if (r.T == 0) return W4A16_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  w4a16::GemmParams p = base_params(desc, packed_w, packed_s, a, combine ? (void*)ws : (void*)out, c.nr, c.waves);
+  hipError_t e;
+  float* comb = combine ? reinterpret_cast<float*>(ws + wl.counters + wl.slices) : nullptr;
+  w4a16::GemmParams p = base_params(desc, packed_w, packed_s, a, combine ? (void*)comb : (void*)out, c.nr, c.waves);
   p.sorted_ids = r.sorted_ids;
   p.expert_ids = r.expert_ids;
   p.num_tokens_padded = r.num_tokens_padded;
@@ -456,52 +651,59 @@ w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
   p.a_row_div = a_layout == W4A16_A_TOKEN ? r.topk : a_layout == W4A16_A_SLOT ? 1 : 0;
   p.slot_weight = topk_weights;
   p.grid_blocks = (int32_t)(r.capacity / r.block_m);
-  hipError_t e;
   if (c.split_k == 0) {
-    p.sk_partial = reinterpret_cast<float*>(ws + comb_bytes);
+    p.sk_partial = reinterpret_cast<float*>(ws + wl.counters + wl.slices + wl.combine);
     const int wgs = resident_workgroups(c, epi);
     e = w4a16::launch_gemm_streamk(w4a16::kRouteIndexed, epi, c.block_m / 16, c.nr, c.waves, c.stages, p,
                                    wgs, s);
   } else {
+    attach_split(p, c, wl, ws);
     e = w4a16::launch_gemm(w4a16::kRouteIndexed, epi, c.block_m / 16, c.nr, c.waves, c.stages, p, s);
   }
   if (e != hipSuccess) return hip_fail(e, "moe_gemm launch");
   if (combine) {
-    e = w4a16::launch_combine(static_cast<const float*>(workspace), r.topk_ids, r.T, r.topk,
-                              r.first_expert, r.E_loc, desc->N, out, s);
+    e = w4a16::launch_combine(comb, r.topk_ids, r.T, r.topk, r.first_expert, r.E_loc, desc->N, out, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
   }
   return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
+                            const void* packed_s, const uint16_t* a, int64_t a_rows,
+                            int32_t a_layout, const w4a16_indexed_routing* routing,
+                            const float* topk_weights, uint16_t* out,
+                            const w4a16_config* cfg, void* workspace, size_t workspace_bytes,
+                            w4a16_stream_t stream) {
+  return moe_gemm_impl(desc, packed_w, packed_s, a, a_rows, a_layout, routing, topk_weights, out, cfg, workspace,
+                       workspace_bytes, stream);
 }
 
 w4a16_status w4a16_moe_gate_up_silu(const w4a16_weight_desc* desc, const void* packed_w,
                                     const void* packed_s, const uint16_t* x, int64_t x_rows,
                                     const w4a16_indexed_routing* routing, uint16_t* out,
                                     const w4a16_config* cfg, w4a16_stream_t stream) {
-  w4a16_status st = check_int4_desc(desc);
+  w4a16_status st = check_indexed_call(desc, packed_w, packed_s, x, out, routing);
   if (st != W4A16_OK) return st;
   if (desc->flags != W4A16_DESC_GATE_UP)
     return fail(W4A16_ERR_LAYOUT, "the fused SiLU gate/up call needs a weight packed with w4a16_weight_desc_init_gate_up");
-  if (!routing) return fail(W4A16_ERR_ARG, "routing is NULL");
   const w4a16_indexed_routing& r = *routing;
-  if (!packed_w || !packed_s || !r.sorted_ids || !r.expert_ids || !r.num_tokens_padded)
-    return fail(W4A16_ERR_ARG, "NULL pointer argument");
-  if (r.T < 0 || r.topk <= 0 || r.capacity < 0) return fail(W4A16_ERR_ARG, "bad routing sizes");
-  if (r.T > 0 && (!x || !out)) return fail(W4A16_ERR_ARG, "activations or output are NULL");
-  if (!aligned16(packed_w) || !aligned16(packed_s) || !aligned16(x) || !aligned16(out))
-    return fail(W4A16_ERR_ARG, "packed weights, activations and output must be 16-byte aligned");
-  if (r.E_loc != desc->E)
-    return fail(W4A16_ERR_LAYOUT, "routing has E_loc=%d but the packed weight holds %d experts", r.E_loc, desc->E);
   if (x_rows < r.T) return fail(W4A16_ERR_SHAPE, "activations have %lld rows, need %d", (long long)x_rows, r.T);
-  if ((int64_t)r.T * r.topk >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "T*topk too large");
-  w4a16_config c = cfg ? *cfg : default_indexed_config(r.block_m);
+  st = check_offset_range(r.T, desc->K, "activations");
+  if (st != W4A16_OK) return st;
+  w4a16_config c;
+  st = indexed_call_config(r, desc, cfg, &c);
+  if (st != W4A16_OK) return st;
+  if (!cfg) c.split_k = 1;  // the fused epilogue runs whole tiles
   if (c.split_k != 1) return fail(W4A16_ERR_UNSUPPORTED, "the fused SiLU gate/up call runs one workgroup per tile (split_k = 1)");
   if (c.nr % 2) return fail(W4A16_ERR_UNSUPPORTED, "the fused SiLU gate/up call needs an even nr (gate and up tiles in pairs)");
-  st = check_config(c, w4a16::kRouteIndexed, w4a16::kEpiSilu);
+  st = check_config(c, W4A16_ROUTE_INDEXED, w4a16::kEpiSilu, desc->K);
   if (st != W4A16_OK) return st;
   if (c.block_m != r.block_m)
     return fail(W4A16_ERR_LAYOUT, "config block_m=%d differs from the routing's block_m=%d", c.block_m, r.block_m);
-  if (r.capacity % r.block_m) return fail(W4A16_ERR_CAPACITY, "capacity not a multiple of block_m");
   if (r.T == 0) return W4A16_OK;
   w4a16::GemmParams p = base_params(desc, packed_w, packed_s, x, out, c.nr, c.waves);
   p.sorted_ids = r.sorted_ids;
@@ -516,10 +718,68 @@ w4a16_status w4a16_moe_gate_up_silu(const w4a16_weight_desc* desc, const void* p
   return W4A16_OK;
 }
 
+namespace {
+
+// The config of a grouped call: NULL -> its own selection; otherwise a config
+// of its kind (an indexed config is refused by check_config).  Tuning
+// overrides in the environment are refused either way.
+w4a16_status grouped_call_config(int kind, const w4a16_weight_desc* d, int64_t rows, int32_t expected_m,
+                                 const w4a16_config* cfg, w4a16_config* out) {
+  if (const char* v = env_override_present())
+    return fail(W4A16_ERR_ARG, "%s is set: tuning overrides apply to indexed routing only; grouped calls choose their own tiles", v);
+  if (cfg) {
+    *out = *cfg;
+    return W4A16_OK;
+  }
+  if (kind == W4A16_ROUTE_MASKED && expected_m <= 0) return fail(W4A16_ERR_ARG, "expected_m must be positive");
+  if (rows > INT32_MAX) return fail(W4A16_ERR_SHAPE, "too many rows");
+  *out = cached_select((int32_t)rows, 1, 1, d->E, d->N, d->K, kind, kind == W4A16_ROUTE_MASKED ? expected_m : 0, 0);
+  return W4A16_OK;
+}
+
+// routed blocks of a grouped call's grid
+int64_t grouped_blocks(int kind, const w4a16_weight_desc* d, int64_t rows, const w4a16_config& c) {
+  if (kind == W4A16_ROUTE_CONTIGUOUS) return rows / c.block_m;
+  return (int64_t)d->E * ((rows + c.block_m - 1) / c.block_m);
+}
+
+}  // namespace
+
+size_t w4a16_grouped_workspace_bytes(const w4a16_weight_desc* desc, int32_t kind, int64_t rows, int32_t expected_m,
+                                     const w4a16_config* cfg) {
+  if (check_int4_desc(desc) != W4A16_OK || rows < 0) return 0;
+  if (kind != W4A16_ROUTE_CONTIGUOUS && kind != W4A16_ROUTE_MASKED) return 0;
+  w4a16_config c;
+  if (grouped_call_config(kind, desc, rows, expected_m, cfg, &c) != W4A16_OK) return 0;
+  if (check_config(c, kind, w4a16::kEpiStore, desc->K) != W4A16_OK) return 0;
+  const int64_t tiles = grouped_blocks(kind, desc, rows, c) * n_tiles_of(desc->N, c.nr, c.waves);
+  return workspace_layout(c, w4a16::kEpiStore, tiles, desc->N, 0, 1, false).total();
+}
+
+namespace {
+
+w4a16_status launch_grouped(int kind, const w4a16_weight_desc* desc, const w4a16_config& c, w4a16::GemmParams& p,
+                            int64_t rows, void* workspace, size_t workspace_bytes, hipStream_t s, const char* what) {
+  const int64_t tiles = grouped_blocks(kind, desc, rows, c) * n_tiles_of(desc->N, c.nr, c.waves);
+  const Workspace wl = workspace_layout(c, w4a16::kEpiStore, tiles, desc->N, 0, 1, false);
+  const size_t need = wl.total();
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(W4A16_ERR_WORKSPACE, "this call needs %zu bytes of 16-byte aligned workspace, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  attach_split(p, c, wl, static_cast<char*>(workspace));
+  hipError_t e = w4a16::launch_gemm(kind == W4A16_ROUTE_CONTIGUOUS ? w4a16::kRouteContiguous : w4a16::kRouteMasked,
+                                    w4a16::kEpiStore, c.block_m / 16, c.nr, c.waves, c.stages, p, s);
+  if (e != hipSuccess) return hip_fail(e, what);
+  return W4A16_OK;
+}
+
+}  // namespace
+
 w4a16_status w4a16_grouped_contiguous(const w4a16_weight_desc* desc, const void* packed_w,
                                       const void* packed_s, const uint16_t* a, int64_t m_rows,
                                       const int32_t* m_indices, uint16_t* out,
-                                      const w4a16_config* cfg, w4a16_stream_t stream) {
+                                      const w4a16_config* cfg, void* workspace, size_t workspace_bytes,
+                                      w4a16_stream_t stream) {
   w4a16_status st = check_int4_desc(desc);
   if (st != W4A16_OK) return st;
   if (m_rows < 0) return fail(W4A16_ERR_ARG, "m_rows < 0");
@@ -527,33 +787,28 @@ w4a16_status w4a16_grouped_contiguous(const w4a16_weight_desc* desc, const void*
   if (!packed_w || !packed_s) return fail(W4A16_ERR_ARG, "NULL pointer argument");
   if (!aligned16(packed_w) || !aligned16(packed_s) || !aligned16(a) || !aligned16(out))
     return fail(W4A16_ERR_ARG, "packed weights, activations and output must be 16-byte aligned");
-  w4a16_config c;
-  if (cfg) {
-    c = *cfg;
-  } else {
-    c.block_m = 128; c.nr = 2; c.waves = 4; c.split_k = 1; c.stages = 2;
-    apply_env_overrides(&c);
-  }
-  st = check_config(c, w4a16::kRouteContiguous, w4a16::kEpiStore);
+  st = check_offset_range(m_rows, desc->K, "activations");
   if (st != W4A16_OK) return st;
-  if (c.split_k != 1) return fail(W4A16_ERR_UNSUPPORTED, "grouped calls run split_k = 1 only");
+  w4a16_config c;
+  st = grouped_call_config(W4A16_ROUTE_CONTIGUOUS, desc, m_rows, 0, cfg, &c);
+  if (st != W4A16_OK) return st;
+  st = check_config(c, W4A16_ROUTE_CONTIGUOUS, w4a16::kEpiStore, desc->K);
+  if (st != W4A16_OK) return st;
   if (128 % c.block_m) return fail(W4A16_ERR_UNSUPPORTED, "contiguous layout needs block_m dividing 128");
   if (m_rows % c.block_m) return fail(W4A16_ERR_SHAPE, "m_rows=%lld is not a multiple of block_m=%d (segments are 128-row aligned)", (long long)m_rows, c.block_m);
-  if (m_rows >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "m_rows too large");
   if (m_rows == 0) return W4A16_OK;
   w4a16::GemmParams p = base_params(desc, packed_w, packed_s, a, out, c.nr, c.waves);
   p.m_indices = m_indices;
   p.grid_blocks = (int32_t)(m_rows / c.block_m);
-  hipError_t e = w4a16::launch_gemm(w4a16::kRouteContiguous, w4a16::kEpiStore, c.block_m / 16, c.nr,
-                                    c.waves, c.stages, p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "grouped_contiguous launch");
-  return W4A16_OK;
+  return launch_grouped(W4A16_ROUTE_CONTIGUOUS, desc, c, p, m_rows, workspace, workspace_bytes,
+                        static_cast<hipStream_t>(stream), "grouped_contiguous launch");
 }
 
 w4a16_status w4a16_grouped_masked(const w4a16_weight_desc* desc, const void* packed_w,
                                   const void* packed_s, const uint16_t* a, int32_t max_m,
                                   const int32_t* masked_m, int32_t expected_m, uint16_t* out,
-                                  const w4a16_config* cfg, w4a16_stream_t stream) {
+                                  const w4a16_config* cfg, void* workspace, size_t workspace_bytes,
+                                  w4a16_stream_t stream) {
   w4a16_status st = check_int4_desc(desc);
   if (st != W4A16_OK) return st;
   if (max_m <= 0) return fail(W4A16_ERR_ARG, "max_m must be positive");
@@ -561,33 +816,20 @@ w4a16_status w4a16_grouped_masked(const w4a16_weight_desc* desc, const void* pac
   if (!aligned16(packed_w) || !aligned16(packed_s) || !aligned16(a) || !aligned16(out))
     return fail(W4A16_ERR_ARG, "packed weights, activations and output must be 16-byte aligned");
   if ((int64_t)desc->E * max_m >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "E * max_m too large");
-  w4a16_config c;
-  if (cfg) {
-    c = *cfg;
-  } else {
-    if (expected_m <= 0) return fail(W4A16_ERR_ARG, "expected_m must be positive");
-    // chosen from the expected rows per group (post, section "Grouped SM90
-    // kernels": masked decode picks BLOCK_M from the expected tokens per expert)
-    const int want = (int)round_up(std::min(expected_m, 128), 16);
-    c.block_m = want <= 16 ? 16 : want <= 32 ? 32 : want <= 64 ? 64 : 128;
-    c.nr = 2;
-    c.waves = 4;
-    c.split_k = 1;
-    c.stages = 2;
-    apply_env_overrides(&c);
-  }
-  st = check_config(c, w4a16::kRouteMasked, w4a16::kEpiStore);
+  st = check_offset_range((int64_t)desc->E * max_m, desc->K, "activations");
   if (st != W4A16_OK) return st;
-  if (c.split_k != 1) return fail(W4A16_ERR_UNSUPPORTED, "grouped calls run split_k = 1 only");
+  w4a16_config c;
+  st = grouped_call_config(W4A16_ROUTE_MASKED, desc, max_m, expected_m, cfg, &c);
+  if (st != W4A16_OK) return st;
+  st = check_config(c, W4A16_ROUTE_MASKED, w4a16::kEpiStore, desc->K);
+  if (st != W4A16_OK) return st;
   w4a16::GemmParams p = base_params(desc, packed_w, packed_s, a, out, c.nr, c.waves);
   p.masked_m = masked_m;
   p.max_m = max_m;
   p.blocks_per_group = (max_m + c.block_m - 1) / c.block_m;
   p.grid_blocks = desc->E * p.blocks_per_group;
-  hipError_t e = w4a16::launch_gemm(w4a16::kRouteMasked, w4a16::kEpiStore, c.block_m / 16, c.nr,
-                                    c.waves, c.stages, p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "grouped_masked launch");
-  return W4A16_OK;
+  return launch_grouped(W4A16_ROUTE_MASKED, desc, c, p, max_m, workspace, workspace_bytes,
+                        static_cast<hipStream_t>(stream), "grouped_masked launch");
 }
 
 // ------------------------------------------------------------ A4W4 (MXFP4)
@@ -655,7 +897,7 @@ w4a16_status w4a16_mxfp4_quant_local_slots(const uint16_t* x, const int32_t* top
 size_t w4a16_mxfp4_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, int32_t T, int32_t topk,
                                             int32_t combine) {
   if (check_mx_desc(desc) != W4A16_OK || T < 0 || topk <= 0) return 0;
-  return combine_region(T, topk, desc->N, combine != 0);
+  return combine ? al256((size_t)T * topk * desc->N * sizeof(float)) : 0;
 }
 
 w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w, const void* packed_s,
@@ -696,8 +938,10 @@ w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* pac
     c.waves = 4;
     c.split_k = 1;
     c.stages = r.block_m <= 32 ? 4 : 2;
-    apply_env_overrides(&c);
+    c.kind = W4A16_ROUTE_INDEXED;
+    apply_env_overrides(&c, false);
   }
+  if (c.kind != W4A16_ROUTE_INDEXED) return fail(W4A16_ERR_ARG, "config was chosen for a grouped routing kind");
   if (!valid_block_m(c.block_m)) return fail(W4A16_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128}", c.block_m);
   if (c.split_k != 1) return fail(W4A16_ERR_UNSUPPORTED, "the MXFP4 GEMM runs one workgroup per tile (split_k = 1)");
   if (!w4a16::mx_gemm_config_supported(epi, c.block_m / 16, c.nr, c.waves, c.stages))
@@ -707,7 +951,7 @@ w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* pac
     return fail(W4A16_ERR_LAYOUT, "config block_m=%d differs from the routing's block_m=%d", c.block_m, r.block_m);
   if (r.capacity % r.block_m) return fail(W4A16_ERR_CAPACITY, "capacity not a multiple of block_m");
   if (combine && !r.topk_ids) return fail(W4A16_ERR_ARG, "combine needs routing.topk_ids");
-  const size_t need = combine_region(r.T, r.topk, desc->N, combine);
+  const size_t need = combine ? al256((size_t)r.T * r.topk * desc->N * sizeof(float)) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(W4A16_ERR_WORKSPACE, "this call needs %zu bytes of 16-byte aligned workspace, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -765,8 +1009,10 @@ w4a16_status w4a16_mxfp4_gate_up_silu(const w4a16_weight_desc* desc, const void*
     c.waves = 4;
     c.split_k = 1;
     c.stages = r.block_m <= 32 ? 4 : 2;
-    apply_env_overrides(&c);
+    c.kind = W4A16_ROUTE_INDEXED;
+    apply_env_overrides(&c, false);
   }
+  if (c.kind != W4A16_ROUTE_INDEXED) return fail(W4A16_ERR_ARG, "config was chosen for a grouped routing kind");
   if (!valid_block_m(c.block_m)) return fail(W4A16_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128}", c.block_m);
   if (c.split_k != 1 || c.nr != 4)
     return fail(W4A16_ERR_UNSUPPORTED, "the fused A4W4 gate/up call runs one workgroup per tile with nr = 4");

@@ -66,6 +66,7 @@ struct TileSmem {
   int row[16 * MT];                     // activation row per block row, -1 = padding
   int out[16 * MT];                     // output row per block row, -1 = not stored
   float w[16 * MT];                     // top-k weight per block row (weighted epilogue)
+  int last;                             // split-K: this workgroup reduces the tile
 };
 
 #ifndef W4A16_PIPELINED_DEQUANT
@@ -414,20 +415,112 @@ __device__ __forceinline__ void epilogue_weighted_staged(const GemmParams& p, Ti
   }
 }
 
+// Split-K reduce (the post gates splitting by shape, section "H200 prefill
+// and TP8"; here a plain split of K into p.split slices for grids that would
+// leave the machine underfilled).  Every slice's workgroup stores its fp32
+// accumulators, then counts its arrival on the tile's counter; the last to
+// arrive sums all slices in slice order 0, 1, ..., so the result does not
+// depend on which workgroup came last, resets the counter for the next call
+// and returns true with the sum in tot.  No workgroup waits for another.
+//
+// Coherence without whole-cache maintenance: the eight XCDs' L2 caches are
+// not coherent with each other, and an agent-scope fence writes back or
+// invalidates a whole L2 (measured: TP8 T = 16 gate/up 51 -> 349 us with a
+// fence per workgroup).  So the slices are written and read with agent-scope
+// relaxed atomic accesses, which the gfx950 code generator issues with the
+// device-coherence cache bit (write-through / re-fetch at the coherence
+// point); each workgroup waits for its stores' completion before it counts
+// its arrival, and the counter is itself an agent-scope atomic.
+template <int MT, int NR, int NW>
+__device__ __forceinline__ bool split_reduce(const GemmParams& p, TileSmem<MT>& sm, int tile, int s, uint32_t tmask,
+                                             const f32x4_t (&acc)[NR][MT], f32x4_t (&tot)[NR][MT]) {
+  constexpr int NTHR = NW * kWave;
+  constexpr int SLICE = NR * MT * NTHR * 2;          // 64-bit words per slice
+  uint64_t* base = reinterpret_cast<uint64_t*>(p.split_partial) + (int64_t)tile * p.split * SLICE;
+  uint64_t* mine = base + (int64_t)s * SLICE;
+  auto pair = [](float a, float b) {
+    return (uint64_t)__builtin_bit_cast(uint32_t, a) | ((uint64_t)__builtin_bit_cast(uint32_t, b) << 32);
+  };
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      if ((tmask >> t) & 1u) {
+        const f32x4_t v = acc[r][t];
+        uint64_t* d = mine + 2 * ((r * MT + t) * NTHR + threadIdx.x);
+        __hip_atomic_store(d, pair(v[0], v[1]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(d + 1, pair(v[2], v[3]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);                     // this thread's slice stores have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();                                    // ... for every thread of the workgroup
+  if (threadIdx.x == 0) {
+    const uint32_t before = __hip_atomic_fetch_add(p.split_count + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = before == (uint32_t)p.split - 1u;
+    if (last) __hip_atomic_store(p.split_count + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.last = last;
+  }
+  __syncthreads();
+  if (!sm.last) return false;
+  auto lo = [](uint64_t w) { return __builtin_bit_cast(float, (uint32_t)w); };
+  auto hi = [](uint64_t w) { return __builtin_bit_cast(float, (uint32_t)(w >> 32)); };
+  for (int q = 0; q < p.split; ++q) {
+    const uint64_t* src = base + (int64_t)q * SLICE;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        if ((tmask >> t) & 1u) {
+          f32x4_t v;
+          if (q == s) {
+            v = acc[r][t];
+          } else {
+            const uint64_t* d = src + 2 * ((r * MT + t) * NTHR + threadIdx.x);
+            const uint64_t w0 = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t w1 = __hip_atomic_load(d + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v = f32x4_t{lo(w0), hi(w0), lo(w1), hi(w1)};
+          }
+          tot[r][t] = q == 0 ? v : tot[r][t] + v;
+        }
+  }
+  return true;
+}
+
 template <int MT, int NR, int NW, int D, int ROUTE, int EPI>
 __global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) TileSmem<MT> sm;
-  const int mb = blockIdx.x / p.n_tiles;
-  const int nt = blockIdx.x - mb * p.n_tiles;
+  // workgroup -> (tile, K slice); consecutive workgroups are the slices of
+  // one tile, then the N tiles of one routed block
+  int tile = blockIdx.x, s = 0;
+  const int S = p.split;
+  if (S > 1) {
+    tile = blockIdx.x / S;
+    s = blockIdx.x - tile * S;
+  }
+  const bool split = S > 1 && tile < p.split_tiles;   // else slice 0 runs the whole K
+  if (S > 1 && !split && s != 0) return;
+  const int mb = tile / p.n_tiles;
+  const int nt = tile - mb * p.n_tiles;
   const int expert = setup_rows<MT, NW, ROUTE, EPI>(p, mb, sm);
   if (expert < 0) return;
   __syncthreads();
   const uint32_t tmask = active_tiles<MT>(sm);
-  run_tile<MT, NR, NW, D>(p, sm, expert, nt, tmask, 0, p.KC, [&](const f32x4_t(&acc)[NR][MT], uint32_t tm) {
+  const int c0 = split ? (int)((int64_t)s * p.KC / S) : 0;
+  const int c1 = split ? (int)((int64_t)(s + 1) * p.KC / S) : p.KC;
+  auto store = [&](const f32x4_t(&acc)[NR][MT], uint32_t tm) {
     if constexpr (EPI == kEpiWeighted && 16 * NR * NW <= 128)
       epilogue_weighted_staged<MT, NR, NW>(p, sm, nt, tm, acc);
     else
       epilogue<MT, NR, NW, EPI>(p, sm, nt, tm, acc);
+  };
+  run_tile<MT, NR, NW, D>(p, sm, expert, nt, tmask, c0, c1, [&](const f32x4_t(&acc)[NR][MT], uint32_t tm) {
+    if (split) {
+      f32x4_t tot[NR][MT];
+      if (split_reduce<MT, NR, NW>(p, sm, tile, s, tm, acc, tot)) store(tot, tm);
+    } else {
+      store(acc, tm);
+    }
   });
 }
 
@@ -639,12 +732,16 @@ hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves, 
   // over all eight L2s.  (Keeping a block's N tiles on one XCD, which saves
   // the repeated activation fetch, measured several times slower: all its
   // workgroups then request the same lines from one L2 at once.)
-  const int64_t grid = (int64_t)p.grid_blocks * p.n_tiles;
+  const int64_t grid = (int64_t)p.grid_blocks * p.n_tiles * std::max(p.split, 1);
   if (grid <= 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+  if (p.split > 1 && (p.split > p.KC || (p.split_tiles > 0 && (!p.split_partial || !p.split_count))))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(k.classic, dim3((unsigned)grid), dim3(waves * kWave), 0, stream, p);
   return hipGetLastError();
 }
+
+size_t split_slice_bytes(int m_tiles, int nr, int waves) { return (size_t)nr * m_tiles * waves * kWave * 16; }
 
 int streamk_workgroups(int route, int epilogue, int m_tiles, int nr, int waves, int stages) {
   const KernelSet k = find_kernels(route, epilogue, m_tiles, nr, waves, stages);

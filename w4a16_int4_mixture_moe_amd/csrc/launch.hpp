@@ -53,6 +53,15 @@ struct GemmParams {
   int32_t grid_blocks;
   // stream-K: fp32 partial tiles, two slots per persistent workgroup
   float* sk_partial;
+  // split-K: `split` workgroups per tile, each over an equal share of the K
+  // chunks; tiles with index below split_tiles leave their fp32 slices in
+  // split_partial ([tile][slice][NR * MT * threads] float4) and count their
+  // arrival in split_count[tile] (zero at entry, reset to zero by the last
+  // arriver); tiles past split_tiles run whole in their slice-0 workgroup
+  int32_t split;
+  int32_t split_tiles;
+  float* split_partial;
+  uint32_t* split_count;
 };
 
 // m_tiles: 16-row token tiles per block (block_m / 16); nr: 16-row weight
@@ -60,7 +69,8 @@ struct GemmParams {
 // flight per wave (2 or 3).
 bool gemm_config_supported(int route, int epilogue, int m_tiles, int nr, int waves, int stages);
 
-// One workgroup per (routed block, N tile), full K each.
+// One workgroup per (routed block, N tile), full K each; with p.split > 1,
+// p.split workgroups per tile, each over a share of K, reduced in slice order.
 hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves, int stages,
                        const GemmParams& p, hipStream_t stream);
 
@@ -74,6 +84,9 @@ hipError_t launch_gemm_streamk(int route, int epilogue, int m_tiles, int nr, int
 // workgroups per CU x CUs), and the partial-tile bytes they need.
 int streamk_workgroups(int route, int epilogue, int m_tiles, int nr, int waves, int stages);
 size_t streamk_partial_bytes(int m_tiles, int nr, int waves, int workgroups);
+
+// Bytes of one K slice of one tile in split_partial.
+size_t split_slice_bytes(int m_tiles, int nr, int waves);
 
 // ---- combine of weighted per-slot partials (gemm.hip)
 hipError_t launch_combine(const float* partial, const int32_t* topk_ids, int32_t T, int32_t topk,
