@@ -301,6 +301,25 @@ w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
                             const w4a16_config* cfg, void* workspace, size_t workspace_bytes,
                             w4a16_stream_t stream);
 
+/* w4a16_moe_gemm for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, outputs and errors as w4a16_moe_gemm, without the workspace:
+ * the call uses the library's own scratch array instead, W4A16_SCRATCH_BYTES
+ * per GPU (allocated with the library's code on each device it runs on and
+ * held until the process ends; the call itself allocates nothing).  A call
+ * needing more scratch than that (w4a16_moe_gemm_workspace_bytes) returns
+ * ERR_WORKSPACE: 128 MiB covers, for example, the top-k combine of 576
+ * tokens x top-8 x N = 7168.  All calls on one GPU share its array and each
+ * starts by clearing the part it needs zeroed, so calls that overlap on one
+ * GPU (different streams, or threads) race and give wrong results: order
+ * them on one stream.  The first call on a device looks up the array's
+ * device address (no device work). */
+#define W4A16_SCRATCH_BYTES ((size_t)128 << 20)
+w4a16_status w4a16_moe_gemm_noalloc(const w4a16_weight_desc* desc, const void* packed_w, const void* packed_s,
+                                    const uint16_t* a, int64_t a_rows, int32_t a_layout,
+                                    const w4a16_indexed_routing* routing, const float* topk_weights, uint16_t* out,
+                                    const w4a16_config* cfg, w4a16_stream_t stream);
+
 /* Gate/up projection with the activation between the two projections
  * fused into its epilogue, written in sorted order for the down projection.
  * (The post's layer numbers exclude the activation, section "Measurement";

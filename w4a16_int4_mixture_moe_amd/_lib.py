@@ -81,6 +81,8 @@ SIGNATURES = {
     "w4a16_moe_gemm": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I64, _I32,
                               ctypes.POINTER(IndexedRouting), _P, _P, ctypes.POINTER(Config),
                               _P, _SZ, _P]),
+    "w4a16_moe_gemm_noalloc": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I64, _I32,
+                                      ctypes.POINTER(IndexedRouting), _P, _P, ctypes.POINTER(Config), _P]),
     "w4a16_moe_gate_up_silu": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I64,
                                       ctypes.POINTER(IndexedRouting), _P, ctypes.POINTER(Config), _P]),
     "w4a16_grouped_contiguous": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I64, _P, _P,

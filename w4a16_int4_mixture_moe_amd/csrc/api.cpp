@@ -601,11 +601,15 @@ size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, const w4a16
 
 namespace {
 
-// The indexed GEMM.
+// The indexed GEMM with its workspace already chosen.  With no_alloc, the
+// workspace is the library's own scratch array of `workspace_bytes` bytes:
+// a call needing more is refused, and the split-K arrival counters are
+// cleared first (the array keeps whatever the previous call on the device
+// left in it).
 w4a16_status moe_gemm_impl(const w4a16_weight_desc* desc, const void* packed_w, const void* packed_s,
                            const uint16_t* a, int64_t a_rows, int32_t a_layout, const w4a16_indexed_routing* routing,
                            const float* topk_weights, uint16_t* out, const w4a16_config* cfg, void* workspace,
-                           size_t workspace_bytes, w4a16_stream_t stream) {
+                           size_t workspace_bytes, w4a16_stream_t stream, bool no_alloc) {
   w4a16_status st = check_indexed_call(desc, packed_w, packed_s, a, out, routing);
   if (st != W4A16_OK) return st;
   const w4a16_indexed_routing& r = *routing;
@@ -635,6 +639,9 @@ w4a16_status moe_gemm_impl(const w4a16_weight_desc* desc, const void* packed_w, 
   if (c.split_k == 0 && wl.streamk == 0)
     return fail(W4A16_ERR_HIP, "stream-K: could not query the device's resident workgroups");
   const size_t need = wl.total();
+  if (no_alloc && need > workspace_bytes)
+    return fail(W4A16_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the library's scratch array holds %zu "
+                "(use w4a16_moe_gemm with a caller workspace)", need, workspace_bytes);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(W4A16_ERR_WORKSPACE, "this call needs %zu bytes of 16-byte aligned workspace, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -642,6 +649,10 @@ w4a16_status moe_gemm_impl(const w4a16_weight_desc* desc, const void* packed_w, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   hipError_t e;
+  if (no_alloc && wl.counters > 0) {
+    e = w4a16::launch_zero_words(reinterpret_cast<uint32_t*>(ws), (int64_t)(wl.counters / 4), s);
+    if (e != hipSuccess) return hip_fail(e, "scratch counter clear launch");
+  }
   float* comb = combine ? reinterpret_cast<float*>(ws + wl.counters + wl.slices) : nullptr;
   w4a16::GemmParams p = base_params(desc, packed_w, packed_s, a, combine ? (void*)comb : (void*)out, c.nr, c.waves);
   p.sorted_ids = r.sorted_ids;
@@ -668,6 +679,33 @@ w4a16_status moe_gemm_impl(const w4a16_weight_desc* desc, const void* packed_w, 
   return W4A16_OK;
 }
 
+// The library's own scratch for w4a16_moe_gemm_noalloc: one array per GPU,
+// held until the process ends.  Host code never passes `scratch` itself to a
+// kernel (in host code the name is a host-side stand-in, not a device
+// address); it passes the device address hipGetSymbolAddress returns for the
+// current device, looked up once per device on the first call there.
+static __device__ __align__(256) unsigned char scratch[W4A16_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+w4a16_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(W4A16_ERR_HIP, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return W4A16_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -679,7 +717,18 @@ w4a16_status w4a16_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w,
                             const w4a16_config* cfg, void* workspace, size_t workspace_bytes,
                             w4a16_stream_t stream) {
   return moe_gemm_impl(desc, packed_w, packed_s, a, a_rows, a_layout, routing, topk_weights, out, cfg, workspace,
-                       workspace_bytes, stream);
+                       workspace_bytes, stream, false);
+}
+
+w4a16_status w4a16_moe_gemm_noalloc(const w4a16_weight_desc* desc, const void* packed_w, const void* packed_s,
+                                    const uint16_t* a, int64_t a_rows, int32_t a_layout,
+                                    const w4a16_indexed_routing* routing, const float* topk_weights, uint16_t* out,
+                                    const w4a16_config* cfg, w4a16_stream_t stream) {
+  void* ws = nullptr;
+  w4a16_status st = scratch_of_current_device(&ws);
+  if (st != W4A16_OK) return st;
+  return moe_gemm_impl(desc, packed_w, packed_s, a, a_rows, a_layout, routing, topk_weights, out, cfg, ws,
+                       W4A16_SCRATCH_BYTES, stream, true);
 }
 
 w4a16_status w4a16_moe_gate_up_silu(const w4a16_weight_desc* desc, const void* packed_w,

@@ -651,6 +651,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<uint4*>(out + t * N + n) = o;
 }
 
+// Zero `words` 32-bit words (a kernel, not hipMemsetAsync, so the call can
+// sit in a captured HIP graph).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t stream) {
+  if (words <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((words + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, words);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const float* partial, const int32_t* topk_ids, int32_t T, int32_t topk,
                           int32_t first, int32_t E_loc, int32_t N, uint16_t* out,
                           hipStream_t stream) {

@@ -88,6 +88,9 @@ size_t streamk_partial_bytes(int m_tiles, int nr, int waves, int workgroups);
 // Bytes of one K slice of one tile in split_partial.
 size_t split_slice_bytes(int m_tiles, int nr, int waves);
 
+// ---- zero fill of 32-bit words, graph-capturable (gemm.hip)
+hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t stream);
+
 // ---- combine of weighted per-slot partials (gemm.hip)
 hipError_t launch_combine(const float* partial, const int32_t* topk_ids, int32_t T, int32_t topk,
                           int32_t first, int32_t E_loc, int32_t N, uint16_t* out,
