@@ -263,7 +263,8 @@ def test_selector_follows_tokens_per_expert(L):
     one = W.select(16, 8, 384, 384, 512, 7168)             # ~0.3 rows/expert
     assert one.block_m == 16
     pre = W.select(8192, 8, 384, 48, 4096, 7168)           # ~171 rows/expert
-    assert pre.block_m == 128 and pre.nr == 2
+    assert pre.block_m == 128 and pre.nr == 4                  # the prefill tile (K % 128 == 0)
+    assert W.select(8192, 8, 384, 48, 4096, 7200).nr == 2     # ragged K: the general kernel
     # tok_e, not total tokens: same T, 8x more experts -> decode side
     assert W.select(8192, 8, 3072, 48, 4096, 7168).block_m < 128
     assert W.select(576, 8, 384, 48, 4096, 7168).block_m == dec.block_m   # memoised, stable

@@ -545,3 +545,49 @@ def test_split_k_graph_replays_match_eager():
         np.testing.assert_array_equal(bits(h), ref_h, err_msg=f"replay {rep}")
         np.testing.assert_array_equal(bits(y), ref_y, err_msg=f"replay {rep}")
         _ = (P.d_x.float() @ P.d_x.float().t()).sum().item()   # unrelated eager work
+
+
+# ------------------------------------------------------------ prefill tile
+
+def test_prefill_tile_bit_identical_to_the_general_kernel():
+    """The 128 x 256 prefill tile (block_m 128, nr 4: LDS-DMA staging, K a
+    multiple of 128) sums every output in the same order as the general
+    kernel's 128-row tiles, so their bits agree, for odd and even chunk
+    counts, every active-tile count (skewed routing), a ragged last N tile,
+    and every epilogue and row source; both within tolerance of the oracle."""
+    sh = W.MoEShape(name="prefill_tile", E_glob=12, E_loc=6, first=3, topk=4, T=400, K1=1152, N1=512,
+                    K2=1024, N2=272, zipf_s=1.0, seed=4242)
+    P = Problem(sh).upload()
+    r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, 128)
+    flat = P.topk_ids.reshape(-1)
+    counts = np.bincount(flat[(flat >= sh.first) & (flat < sh.first + sh.E_loc)] - sh.first, minlength=sh.E_loc)
+    log("rows per local expert", counts.tolist())
+    out = {}
+    for nr in (4, 2):
+        c = M.config(128, nr)
+        h = M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=c)
+        y = M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=c)
+        torch.cuda.synchronize()
+        out[nr] = (bits(h), bits(y))
+        _check_indexed(P, h, y, f"prefill tile check nr={nr}")
+    np.testing.assert_array_equal(out[4][0], out[2][0], err_msg="gate/up: prefill tile vs general kernel")
+    np.testing.assert_array_equal(out[4][1], out[2][1], err_msg="down+combine: prefill tile vs general kernel")
+    # fused SiLU epilogue on the interleaved gate/up weight
+    p1g = M.pack_w4(to_dev(P.c1), to_dev_bf16(P.s1), gate_up=True)
+    inter = {nr: bits(M.moe_gate_up_silu(P.d_x, p1g, r, cfg=M.config(128, nr))) for nr in (4, 2)}
+    valid = r.sorted_ids.cpu().numpy() < sh.T * sh.topk
+    np.testing.assert_array_equal(inter[4][valid], inter[2][valid], err_msg="fused SiLU: prefill tile")
+    # grouped row sources
+    A, mi, _ = W.contiguous_layout(P.topk_ids, P.x, sh.first, sh.E_loc, pad=128, pad_fill=0x7FC0)
+    oc = {nr: bits(M.grouped_contiguous(to_dev_bf16(A), P.p1, to_dev(mi), cfg=M.config(128, nr, kind="contiguous")))
+          for nr in (4, 2)}
+    ok = mi >= 0
+    np.testing.assert_array_equal(oc[4][ok], oc[2][ok], err_msg="contiguous: prefill tile")
+    ref, vr = O.grouped_contiguous(A, P.c1, P.s1, mi)
+    assert_close(oc[4][vr], ref[vr], "contiguous prefill tile")
+    A3, mm, _, _ = W.masked_layout(P.topk_ids, P.x, sh.first, sh.E_loc, 200, pad_fill=0x7FC0)
+    om = {nr: bits(M.grouped_masked(to_dev_bf16(A3), P.p1, to_dev(mm), 100, cfg=M.config(128, nr, kind="masked")))
+          for nr in (4, 2)}
+    refm, vm = O.grouped_masked(A3, P.c1, P.s1, mm)
+    np.testing.assert_array_equal(om[4][vm], om[2][vm], err_msg="masked: prefill tile")
+    assert_close(om[4][vm], refm[vm], "masked prefill tile")

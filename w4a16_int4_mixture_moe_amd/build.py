@@ -24,7 +24,7 @@ LIBNAME = "libw4a16moe.so"
 OBJDIR = os.path.join(ROOT, "_build", "w4a16moe")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "align.hip", "pack.hip", "gemm.hip", "mx.hip"]
+SOURCES = ["api.cpp", "align.hip", "pack.hip", "gemm.hip", "prefill.hip", "mx.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

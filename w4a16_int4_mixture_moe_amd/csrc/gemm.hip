@@ -738,6 +738,8 @@ bool gemm_config_supported(int route, int epilogue, int m_tiles, int nr, int wav
 
 hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves, int stages,
                        const GemmParams& p, hipStream_t stream) {
+  if (prefill_applies(route, epilogue, m_tiles, nr, waves, stages, p))
+    return launch_gemm_prefill(route, epilogue, p, stream);
   const KernelSet k = find_kernels(route, epilogue, m_tiles, nr, waves, stages);
   if (k.classic == nullptr) return hipErrorInvalidValue;
   // Consecutive workgroups (the N tiles of one block) go to different XCDs

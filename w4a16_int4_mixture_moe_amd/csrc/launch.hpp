@@ -74,6 +74,13 @@ bool gemm_config_supported(int route, int epilogue, int m_tiles, int nr, int wav
 hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves, int stages,
                        const GemmParams& p, hipStream_t stream);
 
+// The prefill tile (prefill.hip): 128 routed rows x 256 weight rows per
+// workgroup, activations staged by LDS-DMA.  Serves the (m_tiles 8, nr 4,
+// waves 4, stages 2) configuration when K is a multiple of 128 and K is not
+// split; launch_gemm dispatches to it.
+bool prefill_applies(int route, int epilogue, int m_tiles, int nr, int waves, int stages, const GemmParams& p);
+hipError_t launch_gemm_prefill(int route, int epilogue, const GemmParams& p, hipStream_t stream);
+
 // Stream-K: `workgroups` persistent workgroups each take an equal contiguous
 // range of (tile, 128-K chunk) units; tiles cut by a range boundary leave
 // fp32 partials in p.sk_partial that a fix-up kernel sums in range order.

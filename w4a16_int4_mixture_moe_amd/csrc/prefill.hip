@@ -1,0 +1,285 @@
+// Prefill-side W4A16 MoE GEMM tile for gfx950: 128 routed rows x 256 weight
+// rows per workgroup.
+//
+// Why a separate kernel.  Large routed blocks are MFMA-bound, and on gfx950
+// what limits the MFMA rate in this GEMM is the LDS and register traffic per
+// MFMA, not the MFMA unit.  Each wave here owns four 16-row weight tiles
+// (64 weight rows) and all eight 16-row token tiles of the block, so every
+// activation fragment read from LDS feeds four MFMAs, and the dequantised
+// weights (VALU work, subtract-then-scale of the Chord post's "H200 and
+// Blackwell indexed decode" section) are amortised over 128 rows.  The
+// accumulators (4 x 8 MFMA tiles, 128 registers) stay in ordinary VGPRs and
+// the whole wave fits 256 registers, so two workgroups (two waves per SIMD)
+// share a CU.  That needs the activation staging to cost no registers: the
+// block's rows are copied HBM -> LDS with global_load_lds_dwordx4 (16 bytes
+// per lane, straight into LDS), one 128-wide K chunk ahead of the MFMAs,
+// double buffered.
+//
+// LDS layout.  A staged chunk is 128 rows x 256 bytes (128 bf16 of K).  The
+// LDS-DMA writes each instruction's 64 lanes to 1 KB of consecutive LDS (four
+// rows), so rows cannot be padded; instead the sixteen 16-byte granules of
+// row r are stored XOR-swizzled, granule q at position q ^ (r % 16).  The
+// MFMA operand read of lane l (row 16 t + l % 16, granule 4 (l / 16) + j)
+// then touches sixteen different positions in each group of sixteen lanes:
+// conflict-free (measured at the rate of linear reads; unswizzled rows run at
+// half that rate).
+//
+// Arithmetic is that of moe_gemm_kernel: the same packed weights and scales,
+// dequant8, v_mfma_f32_16x16x32_bf16 with the weights as the A operand, K
+// chunks in order and the four 32-wide MFMA steps of a chunk in order, so the
+// outputs are bit-identical to every other tile configuration.  K must be a
+// multiple of 128 (the DMA copies whole chunks; other K use the general
+// kernel).
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+#include "tile_common.hpp"
+
+namespace w4a16 {
+
+namespace {
+
+constexpr int kPfMT = 8;            // token tiles per block (128 rows)
+constexpr int kPfNR = 4;            // weight tiles per wave
+constexpr int kPfNW = 4;            // waves per workgroup
+constexpr int kPfBM = 16 * kPfMT;
+constexpr int kPfChunkBytes = kPfBM * kChunk * 2;   // one staged chunk: 32 KB
+
+struct PfSmem {
+  uint16_t xs[2][kPfBM * kChunk];   // two staged chunks, granules swizzled by row
+  int row[kPfBM];                   // activation row per block row, -1 = padding
+  int out[kPfBM];                   // output row per block row, -1 = not stored
+  float w[kPfBM];                   // top-k weight per block row (weighted epilogue)
+  uint32_t xoff[kPfBM];             // byte offset of the LDS-DMA source granule per block row
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at dst + 16 l (dst wave-uniform).  (Kept out of templates: the host pass
+// rejects the builtin's pointer arguments inside one.)
+__device__ __forceinline__ void dma16(gptr_t src, lds_ptr_t dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// Wait until at most n vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at
+// their maxima, i.e. not waited for).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// acc += this wave's 64 weight rows x the block's first 16 NA rows over all K.
+template <int NA>
+__device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int expert, int nt,
+                                            f32x4_t (&acc)[kPfNR][kPfMT]) {
+  static_assert(NA >= 1 && NA <= kPfMT, "active tile count");
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int KC = p.KC;
+
+  // LDS-DMA of a chunk: instruction i (of 4 NA) writes block rows 4 i .. 4 i + 3;
+  // this wave issues i = wave + 4 k, k < NA.  Lane l lands at row
+  // 4 i + l / 16, position l % 16, so it loads granule (l % 16) ^ (row % 16)
+  // of that row, the same granule for every k (16 k leaves row % 16 alone).
+  // (the per-lane source offsets are kept in LDS, sm.xoff, not in registers)
+  {
+    const int fallback_row = sm.row[0];   // always valid
+    for (int i = tid; i < kPfBM; i += kPfNW * kWave) {
+      const int r = sm.row[i];
+      sm.xoff[i] = (uint32_t)(r >= 0 ? r : fallback_row) * (uint32_t)(p.K * 2);
+    }
+  }
+  __syncthreads();
+  const uint32_t gran = (uint32_t)(((lane & 15) ^ ((4 * wave + (lane >> 4)) & 15)) * 16);
+  const int xrow = 4 * wave + (lane >> 4);
+  const gptr_t xbase = uniform_ptr(p.a);
+  auto issue_x = [&](int c, int buf) {
+    const gptr_t base = xbase + (int64_t)c * (kChunk * 2) + gran;
+#pragma unroll
+    for (int k = 0; k < NA; ++k)
+      dma16(base + sm.xoff[xrow + 16 * k], (lds_ptr_t)(reinterpret_cast<char*>(&sm.xs[buf][0]) + (wave + 4 * k) * 1024));
+  };
+
+  // weights and scales: a ring of two chunks per wave, as in moe_gemm_kernel
+  const int rt_base = nt * (kPfNW * kPfNR) + wave * kPfNR;
+  gptr_t wbase[kPfNR];
+  gptr_t sbase[kPfNR];
+#pragma unroll
+  for (int r = 0; r < kPfNR; ++r) {
+    const int rt = min(rt_base + r, p.NT - 1);
+    const int64_t tile = (int64_t)expert * p.NT + rt;
+    wbase[r] = uniform_ptr(p.packed_w + tile * p.KC * kWave);
+    sbase[r] = uniform_ptr(p.packed_s + tile * ((p.KC + 1) / 2) * kWave);
+  }
+  const uint32_t woff = (uint32_t)lane * 16u;
+  const uint32_t soff = (uint32_t)lane * 4u;
+  auto issue_w = [&](int c, u32x4_t (&w)[kPfNR]) {
+#pragma unroll
+    for (int r = 0; r < kPfNR; ++r) w[r] = gload_u32x4(wbase[r] + (int64_t)c * (kWave * 16) + woff);
+  };
+  // the scale words of a chunk pair (low half: even chunk, high half: odd)
+  auto issue_s = [&](int c, uint32_t (&sc)[kPfNR]) {
+#pragma unroll
+    for (int r = 0; r < kPfNR; ++r) sc[r] = gload_u32(sbase[r] + (int64_t)(c >> 1) * (kWave * 4) + soff);
+  };
+
+  const DequantMasks masks = make_dequant_masks();
+  // weights and scales of the current chunk and of the next one (a ring of
+  // two register sets: the second wave on each SIMD covers the rest of the
+  // load latency)
+  u32x4_t wr[2][kPfNR];
+  uint32_t sr[2][kPfNR];            // scale words of the current and the next chunk pair
+
+  // prologue: chunk 0 to LDS, weights and scales of chunk 0 in flight
+  issue_x(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_w(0, wr[0]);
+  issue_s(0, sr[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<2 * kPfNR>();          // this wave's DMA of chunk 0 has landed
+  __syncthreads();                  // ... and every wave's
+
+  // one chunk at ring position P: DMA of chunk c + 1 into the other LDS
+  // buffer and the weights of chunk c + 1 into the other register set, then
+  // dequant + MFMAs of chunk c, then wait for the DMA and synchronise.
+  // has_next: chunk c + 1 exists.
+  auto chunk = [&](auto P_, int c, bool has_next) {
+    constexpr int P = decltype(P_)::value;
+    const int buf = c & 1;
+    // P is the chunk's parity: register set P holds its weights, and its
+    // scales sit in the low (P = 0) or high (P = 1) half of the pair's word
+    if (has_next) {
+      issue_x(c + 1, buf ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_w(c + 1, wr[P ^ 1]);
+      if (P == 1) issue_s(c + 1, sr[((c + 1) >> 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const char* xs = reinterpret_cast<const char*>(&sm.xs[buf][0]);
+    const int spair = (c >> 1) & 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8_t A[kPfNR];
+#pragma unroll
+      for (int r = 0; r < kPfNR; ++r) {
+        const uint32_t word = spair ? sr[1][r] : sr[0][r];
+        const float sv = __builtin_bit_cast(float, P ? (word & 0xFFFF0000u) : (word << 16));
+        A[r] = dequant8(wr[P][r][j], sv, -1032.0f * sv, 0.0625f * sv, -72.0f * sv, masks);
+      }
+      const uint32_t rowoff = (uint32_t)(lane & 15) * 256u;
+      const uint32_t goff = (uint32_t)((((lane >> 4) * 4 + j) ^ (lane & 15)) * 16);
+#pragma unroll
+      for (int t = 0; t < NA; ++t) {
+        const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(xs + t * 4096 + rowoff + goff);
+#pragma unroll
+        for (int r = 0; r < kPfNR; ++r)
+          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r], B, acc[r][t], 0, 0, 0);
+      }
+      // keep each 32-K step's operands to itself: hoisting the next step's
+      // dequant or operand reads above these MFMAs needs more registers than
+      // two waves per SIMD leave (the second wave covers the latency instead)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (has_next) {
+      // the DMA of chunk c + 1 was issued before its weights (and, after an
+      // odd chunk, the next pair's scales)
+      if (P == 1)
+        wait_vmcnt<2 * kPfNR>();
+      else
+        wait_vmcnt<kPfNR>();
+    }
+    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  int c = 0;
+  for (; c + 2 < KC; c += 2) {
+    chunk(I0{}, c, true);
+    chunk(I1{}, c + 1, true);
+  }
+  // the last one or two chunks
+  if (c < KC) chunk(I0{}, c, c + 1 < KC);
+  if (c + 1 < KC) chunk(I1{}, c + 1, false);
+}
+
+// The block's tiles: the main loop specialised for its active token tiles
+// (a prefix, rounded up to an even count: at most one tile of padding rows
+// multiplied), then the epilogue.
+template <int EPI>
+__device__ __forceinline__ void pf_run(const GemmParams& p, PfSmem& sm, int expert, int nt, uint32_t tmask) {
+  const int na = 32 - __clz(tmask);
+  auto go = [&](auto NA_) {
+    constexpr int NA = decltype(NA_)::value;
+    f32x4_t acc[kPfNR][kPfMT];
+#pragma unroll
+    for (int r = 0; r < kPfNR; ++r)
+#pragma unroll
+      for (int t = 0; t < kPfMT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    pf_mainloop<NA>(p, sm, expert, nt, acc);
+    epilogue<kPfMT, kPfNR, kPfNW, EPI>(p, sm, nt, (1u << NA) - 1u, acc);
+  };
+  if (na <= 2)
+    go(std::integral_constant<int, 2>{});
+  else if (na <= 4)
+    go(std::integral_constant<int, 4>{});
+  else if (na <= 6)
+    go(std::integral_constant<int, 6>{});
+  else
+    go(std::integral_constant<int, 8>{});
+}
+
+template <int ROUTE, int EPI>
+__global__ __launch_bounds__(kPfNW * kWave, 2) void moe_gemm_prefill_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(16))) PfSmem sm;
+  // work item (routed block, N tile), block-major: consecutive workgroups
+  // (the N tiles of one block) go to different XCDs.  Measured against
+  // orders that keep a block's N tiles on one XCD (its activation rows then
+  // come from HBM once): all sixteen side by side there, 4.8x slower (one
+  // L2 serving the same lines to sixteen CUs at once); spread over time
+  // (N-tile-major), 1-8 % slower.
+  const int mb = blockIdx.x / p.n_tiles;
+  const int nt = blockIdx.x - mb * p.n_tiles;
+  const int expert = setup_rows<kPfMT, kPfNW, ROUTE, EPI>(p, mb, sm);
+  if (expert < 0) return;
+  __syncthreads();
+  pf_run<EPI>(p, sm, expert, nt, active_tiles<kPfMT>(sm));
+}
+
+typedef void (*PfKernel)(const GemmParams);
+
+PfKernel pick_prefill(int route, int epi) {
+  if (route == kRouteIndexed) {
+    if (epi == kEpiStore) return moe_gemm_prefill_kernel<kRouteIndexed, kEpiStore>;
+    if (epi == kEpiWeighted) return moe_gemm_prefill_kernel<kRouteIndexed, kEpiWeighted>;
+    if (epi == kEpiSilu) return moe_gemm_prefill_kernel<kRouteIndexed, kEpiSilu>;
+    return nullptr;
+  }
+  if (epi != kEpiStore) return nullptr;
+  if (route == kRouteContiguous) return moe_gemm_prefill_kernel<kRouteContiguous, kEpiStore>;
+  if (route == kRouteMasked) return moe_gemm_prefill_kernel<kRouteMasked, kEpiStore>;
+  return nullptr;
+}
+
+}  // namespace
+
+bool prefill_applies(int route, int epilogue, int m_tiles, int nr, int waves, int stages, const GemmParams& p) {
+  return m_tiles == kPfMT && nr == kPfNR && waves == kPfNW && stages == 2 && p.K % kChunk == 0 && p.split <= 1 &&
+         pick_prefill(route, epilogue) != nullptr;
+}
+
+hipError_t launch_gemm_prefill(int route, int epilogue, const GemmParams& p, hipStream_t stream) {
+  const PfKernel k = pick_prefill(route, epilogue);
+  if (k == nullptr || p.K % kChunk) return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)p.grid_blocks * p.n_tiles;
+  if (grid <= 0) return hipSuccess;
+  if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kPfNW * kWave), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace w4a16
