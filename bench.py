@@ -97,10 +97,15 @@ def cfg_tag(cfg) -> str:
     return f"bm{cfg.block_m} nr{cfg.nr} waves{cfg.waves} split_k{cfg.split_k} stages{cfg.stages}"
 
 
-def kernel_name(cfg, route: int, epi: int, mx: bool = False) -> str:
-    """The GEMM kernel's name as the rocprofv3 kernel trace shows it."""
+def kernel_name(cfg, route: int, epi: int, K: int, mx: bool = False) -> str:
+    """The GEMM kernel's name as the rocprofv3 kernel trace shows it (the
+    library runs the 128-row, 4-tiles-per-wave, unsplit configurations on its
+    prefill tile when K is a multiple of 128)."""
     if mx:
         return f"mx_gemm_kernel<{cfg.block_m // 16}, {cfg.nr}, {cfg.waves}, {cfg.stages}, {epi}>"
+    if (cfg.block_m == 128 and cfg.nr == 4 and cfg.waves == 4 and cfg.stages == 2 and cfg.split_k <= 1
+            and K % 128 == 0):
+        return f"moe_gemm_prefill_kernel<{cfg.waves}, {route}, {epi}>"
     return f"moe_gemm_kernel<{cfg.block_m // 16}, {cfg.nr}, {cfg.waves}, {cfg.stages}, {route}, {epi}>"
 
 
@@ -278,6 +283,7 @@ class IndexedStep:
         else:
             self.cfg1 = override(M.indexed_config(self.routing, self.p1))
             self.cfg2 = override(M.indexed_config(self.routing, self.p2))
+            self.cfg2.combine_cols = args.combine_cols
             if self.fused:
                 self.cfg1.split_k = 1
         self.h = torch.empty(T * k, sh.N1, dtype=torch.bfloat16, device=dev)
@@ -389,10 +395,10 @@ class IndexedStep:
         peak = FP4_PEAK_TFLOPS if self.mx else BF16_PEAK_TFLOPS
         rec = {"gate_up": gemm_record(st_gu[0], s["wb1"], s["flops1"], s["rows_per_expert"],
                                       kernel_name(self.cfg1, ROUTE_INDEXED, 3 if self.mx and self.fused else
-                                                  (2 if self.fused else EPI_STORE), self.mx),
+                                                  (2 if self.fused else EPI_STORE), self.sh.K1, self.mx),
                                       self.cfg1, s["total1"], peak, st_gu),
                "down_combine": gemm_record(st_dn[0], s["wb2"], s["flops2"], s["rows_per_expert"],
-                                           kernel_name(self.cfg2, ROUTE_INDEXED, EPI_WEIGHTED, self.mx),
+                                           kernel_name(self.cfg2, ROUTE_INDEXED, EPI_WEIGHTED, self.sh.K2, self.mx),
                                            self.cfg2, s["total2"], peak, st_dn)}
         if st_align is not None:
             rec["align_us"] = round(st_align[0], 2)
@@ -421,7 +427,7 @@ class GroupedStep:
     contiguous layout (each expert's rows padded to 128, m_indices -1 on
     padding) and the masked one ([E, max_m, K] with masked_m counts)."""
 
-    def __init__(self, torch, M, W, sh, dev):
+    def __init__(self, torch, M, W, sh, dev, args=None):
         self.torch, self.M, self.sh = torch, M, sh
         t_gen = time.perf_counter()
         ids, _ = W.routing_for(sh)
@@ -444,17 +450,27 @@ class GroupedStep:
         self.expected_m = max(1, int(round(float(self.mm.mean()))))
         self.cfg_c = M.select(self.rows_c, 1, 1, sh.E_loc, sh.N1, sh.K1, kind="contiguous")
         self.cfg_m = M.select(sh.max_m, 1, 1, sh.E_loc, sh.N1, sh.K1, kind="masked", expected_m=self.expected_m)
+        # --nr / --waves overrides: the calls then take the changed configs
+        self.explicit = bool(args is not None and (args.nr or args.waves))
+        if self.explicit:
+            for c in (self.cfg_c, self.cfg_m):
+                c.nr = args.nr or c.nr
+                c.waves = args.waves or c.waves
         z = lambda n: torch.zeros(max(16, n), dtype=torch.uint8, device=dev)
-        self.ws_c = z(M.grouped_workspace_bytes(self.p1, "contiguous", self.rows_c))
-        self.ws_m = z(M.grouped_workspace_bytes(self.p1, "masked", sh.max_m, self.expected_m))
+        self.ws_c = z(M.grouped_workspace_bytes(self.p1, "contiguous", self.rows_c,
+                                                cfg=self.cfg_c if self.explicit else None))
+        self.ws_m = z(M.grouped_workspace_bytes(self.p1, "masked", sh.max_m, self.expected_m,
+                                                cfg=self.cfg_m if self.explicit else None))
         self.out_c = torch.empty(self.rows_c, sh.N1, dtype=torch.bfloat16, device=dev)
         self.out_m = torch.empty(sh.E_loc * sh.max_m, sh.N1, dtype=torch.bfloat16, device=dev)
 
     def contiguous(self):
-        self.M.grouped_contiguous(self.d_A, self.p1, self.d_mi, out=self.out_c, workspace=self.ws_c)
+        self.M.grouped_contiguous(self.d_A, self.p1, self.d_mi, out=self.out_c, workspace=self.ws_c,
+                                  cfg=self.cfg_c if self.explicit else None)
 
     def masked(self):
-        self.M.grouped_masked(self.d_A3, self.p1, self.d_mm, self.expected_m, out=self.out_m, workspace=self.ws_m)
+        self.M.grouped_masked(self.d_A3, self.p1, self.d_mm, self.expected_m, out=self.out_m, workspace=self.ws_m,
+                              cfg=self.cfg_m if self.explicit else None)
 
     def step(self):
         self.contiguous()
@@ -468,12 +484,12 @@ class GroupedStep:
         touched = int(sum(1 for c in self.mm if c > 0))
         wb = weight_bytes(touched, sh.N1, sh.K1)
         rpe_c = valid_c / max(touched, 1)
-        rec_c = gemm_record(st_c[0], wb, valid_c * fl_row, rpe_c, kernel_name(self.cfg_c, ROUTE_CONTIGUOUS, EPI_STORE),
+        rec_c = gemm_record(st_c[0], wb, valid_c * fl_row, rpe_c, kernel_name(self.cfg_c, ROUTE_CONTIGUOUS, EPI_STORE, sh.K1),
                             self.cfg_c, stats=st_c)
         rec_c["TFLOPs_padded_rows"] = round(self.rows_c * fl_row / (st_c[0] * 1e-6) / 1e12, 2)
         rec_c.update(rows=self.rows_c, valid_rows=valid_c)
         rec_m = gemm_record(st_m[0], wb, valid_m * fl_row, valid_m / max(touched, 1),
-                            kernel_name(self.cfg_m, ROUTE_MASKED, EPI_STORE), self.cfg_m, stats=st_m)
+                            kernel_name(self.cfg_m, ROUTE_MASKED, EPI_STORE, sh.K1), self.cfg_m, stats=st_m)
         rec_m["TFLOPs_all_rows"] = round(sh.E_loc * sh.max_m * fl_row / (st_m[0] * 1e-6) / 1e12, 2)
         rec_m.update(max_m=int(sh.max_m), valid_rows=valid_m, dropped_rows=int(self.dropped),
                      expected_m=self.expected_m)
@@ -605,6 +621,8 @@ def main() -> int:
     ap.add_argument("--split-k", type=int, default=-1, help="override: 1 one workgroup per tile, 2/4/8/16 K slices, "
                                                              "0 stream-K")
     ap.add_argument("--stages", type=int, default=0, help="override: K chunks of weights in flight per wave")
+    ap.add_argument("--combine-cols", type=int, default=0,
+                    help="override: output columns per down-projection + combine pass (a multiple of 16)")
     ap.add_argument("--cpu-experts", type=int, default=4, help="experts in the CPU-baseline sample (0: skip)")
     ap.add_argument("--eager", action="store_true", help="launch the step eagerly instead of replaying a HIP graph")
     ap.add_argument("--fused", action="store_true",
@@ -637,7 +655,7 @@ def main() -> int:
         if args.mx or args.fused:
             print("the grouped layouts run the W4A16 gate/up GEMM only (no --mx / --fused)", file=sys.stderr)
             return 2
-        gs = GroupedStep(torch, M, W, sh, dev)
+        gs = GroupedStep(torch, M, W, sh, dev, args)
         rec = measure_grouped(timer, gs, args.ramp_ms, max(8, args.steps // 2))
         for _ in range(args.warmup):
             gs.step()
@@ -789,7 +807,7 @@ def main() -> int:
             torch.cuda.empty_cache()
         configs["3_tp8"] = sweep
         del w3
-        gs = GroupedStep(torch, M, W, W.WORKLOADS["grouped_skewed"], dev)
+        gs = GroupedStep(torch, M, W, W.WORKLOADS["grouped_skewed"], dev, args)
         configs["4_grouped_skewed"] = measure_grouped(timer, gs, args.ramp_ms, sub_reps)
         del gs
         torch.cuda.empty_cache()

@@ -58,7 +58,7 @@ typedef enum {
 const char* w4a16_last_error(void);
 
 /* ABI version of this header (W4A16_ABI_VERSION). */
-#define W4A16_ABI_VERSION 5
+#define W4A16_ABI_VERSION 6
 int32_t w4a16_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -199,6 +199,16 @@ typedef struct {
                         for block_m <= 32 with nr = 2 */
   int32_t kind;      /* W4A16_ROUTE_*: the routing the config is for.  A call
                         given a config of another kind returns ERR_ARG */
+  int32_t combine_cols; /* top-k combine only: output columns per pass.  The
+                        call runs the GEMM and the combine over one range of
+                        this many columns after another, so the fp32 per-slot
+                        partials of a pass (T * topk * combine_cols * 4
+                        bytes of workspace) can stay in the last-level cache
+                        between the two.  0: the library's choice (all of N
+                        when the expected local partials fit 240 MiB, else the
+                        fewest passes that do, in whole workgroup tiles); else
+                        a multiple of 16 (ERR_ARG otherwise).  Results do not
+                        depend on it.  Selection returns 0. */
 } w4a16_config;
 
 /* The config w4a16_select gives for indexed routing aligned to block_m (the
@@ -255,7 +265,9 @@ typedef struct {
  * combine flag and config (NULL: the config the call would choose):
  *   - split_k > 1: 4 bytes of arrival counter per tile that may be split,
  *     then that many tiles' fp32 slices;
- *   - combine != 0: the fp32 per-slot partials, T * topk * N * 4 bytes;
+ *   - combine != 0: the fp32 per-slot partials of one pass,
+ *     T * topk * cols * 4 bytes (cols: the config's combine_cols, or the
+ *     library's choice for it);
  *   - split_k = 0: two partial tiles per resident workgroup of the current
  *     device.
  * The workspace must be zero-filled once before its first use (the arrival

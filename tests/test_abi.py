@@ -38,7 +38,7 @@ def test_every_declared_function_is_exported_and_bound(L):
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(_lib.WeightDesc) == 64
     assert _lib.WeightDesc.flags.offset == 32 and _lib.WeightDesc.w_bytes.offset == 40
-    assert ctypes.sizeof(_lib.Config) == 24 and _lib.Config.kind.offset == 20
+    assert ctypes.sizeof(_lib.Config) == 28 and _lib.Config.kind.offset == 20 and _lib.Config.combine_cols.offset == 24
     assert ctypes.sizeof(_lib.IndexedRouting) == 72 and _lib.IndexedRouting.E_glob.offset == 64
     assert _lib.IndexedRouting.capacity.offset == 24
 
@@ -82,11 +82,11 @@ def test_header_compiles_as_c_and_matches_the_binding(tmp_path):
             got[("const", "W4A16_A_SORTED")]) == (_lib.A_TOKEN, _lib.A_SLOT, _lib.A_SORTED)
     assert (got[("const", "W4A16_ROUTE_INDEXED")], got[("const", "W4A16_ROUTE_CONTIGUOUS")],
             got[("const", "W4A16_ROUTE_MASKED")]) == (_lib.ROUTE_INDEXED, _lib.ROUTE_CONTIGUOUS, _lib.ROUTE_MASKED)
-    assert got[("const", "W4A16_ABI_VERSION")] == 5
+    assert got[("const", "W4A16_ABI_VERSION")] == 6
 
 
 def test_version_and_desc(L):
-    assert L.w4a16_abi_version() == 5
+    assert L.w4a16_abi_version() == 6
     d = W.weight_desc(48, 4096, 7168)
     assert (d.K_pad, d.chunks, d.group) == (7168, 56, 32)
     assert d.w_bytes == 48 * 4096 * 7168 // 2
@@ -162,6 +162,35 @@ def test_capacity_and_workspace(L):
     assert L.w4a16_indexed_config(10, 8, 384, 4, 7168, 2048, 32, ctypes.byref(c)) == 0
     assert (c.block_m, c.nr, c.waves, c.stages, c.kind) == (32, 2, 4, 2, 0)
     assert _ws(d, r, True) == _ws(d, r, True, c)
+    assert c.combine_cols == 0
+
+
+def test_combine_passes_size_the_workspace(L):
+    """The combine's workspace holds one pass of fp32 per-slot partials:
+    T * topk * cols * 4 bytes, cols = the config's combine_cols or the
+    library's choice (all of N while the expected local partials fit 128 MB,
+    else the fewest passes that do, in whole workgroup tiles)."""
+    d = W.weight_desc(4, 7168, 2048)
+    r = _routing(10, 8, 4, 32)
+    assert _ws(d, r, True, W.config(32, 2, combine_cols=1024)) == 10 * 8 * 1024 * 4
+    assert _ws(d, r, True, W.config(32, 2, combine_cols=16)) == -(-(10 * 8 * 16 * 4) // 256) * 256
+    assert _ws(d, r, True, W.config(32, 2, combine_cols=8192)) == 10 * 8 * 7168 * 4   # capped at N
+    assert _ws(d, r, True, W.config(32, 2, combine_cols=24)) == 0       # not a multiple of 16
+    assert _ws(d, r, True, W.config(32, 2, combine_cols=-16)) == 0
+    assert _ws(d, r, False, W.config(32, 2, combine_cols=1024)) == 0    # no combine, no partials
+    # TP8-like down projection, every expert local: T = 4096, top-8, N = 7168
+    # -> 940 MB of partials in one pass; the library's choice is 4 passes of
+    # 1792 columns (7 workgroup tiles of 256)
+    d2 = W.weight_desc(384, 7168, 256)
+    r2 = _lib.IndexedRouting(None, None, None, 40960, 128, 4096, 8, None, 0, 384, 384)
+    assert _ws(d2, r2, True, W.config(128, 4)) == 4096 * 8 * 1792 * 4
+    # T = 1024: 235 MB fits one pass
+    r4 = _lib.IndexedRouting(None, None, None, 10240, 32, 1024, 8, None, 0, 384, 384)
+    assert _ws(d2, r4, True, W.config(32, 2)) == 1024 * 8 * 7168 * 4
+    # an EP8 share (1 in 8 slots local) of T = 576 stays one pass
+    d3 = W.weight_desc(48, 7168, 2048)
+    r3 = _lib.IndexedRouting(None, None, None, 6144, 32, 576, 8, None, 0, 48, 384)
+    assert _ws(d3, r3, True, W.config(32, 2)) == 576 * 8 * 7168 * 4
 
 
 def test_align_argument_errors(L):
@@ -191,6 +220,7 @@ def test_gemm_argument_errors(L, monkeypatch):
     assert call(cfg=ctypes.byref(W.config(32, 2, split_k=4))) == -4     # more slices than the 2 K chunks
     assert call(cfg=ctypes.byref(W.config(32, 2, split_k=2))) == -8     # split needs workspace
     assert call(cfg=ctypes.byref(W.config(32, 2, kind="contiguous"))) == -1   # config of another kind
+    assert call(cfg=ctypes.byref(W.config(32, 2, combine_cols=40)), w=P) == -1  # pass width not a multiple of 16
     bad = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 4, 64)
     assert call(r=bad) == -3                                             # E_loc != weight experts
     no_eg = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 8, 0)

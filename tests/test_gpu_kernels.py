@@ -549,45 +549,81 @@ def test_split_k_graph_replays_match_eager():
 
 # ------------------------------------------------------------ prefill tile
 
-def test_prefill_tile_bit_identical_to_the_general_kernel():
-    """The 128 x 256 prefill tile (block_m 128, nr 4: LDS-DMA staging, K a
-    multiple of 128) sums every output in the same order as the general
-    kernel's 128-row tiles, so their bits agree, for odd and even chunk
-    counts, every active-tile count (skewed routing), a ragged last N tile,
-    and every epilogue and row source; both within tolerance of the oracle."""
-    sh = W.MoEShape(name="prefill_tile", E_glob=12, E_loc=6, first=3, topk=4, T=400, K1=1152, N1=512,
-                    K2=1024, N2=272, zipf_s=1.0, seed=4242)
+# (K of the gate/up, K of the down): chunk counts of 128 that leave 0, 1, 2
+# and 3 chunks past the prefill tile's four-chunk steps, and counts below four
+PREFILL_K = [(1152, 1024), (1280, 896), (384, 256), (512, 128)]
+
+
+@pytest.mark.parametrize("K1,K2", PREFILL_K)
+def test_prefill_tile_bit_identical_to_the_general_kernel(K1, K2):
+    """The prefill tile (block_m 128, nr 4: LDS-DMA staging, K a multiple of
+    128) sums every output in the same order as the general kernel's 128-row
+    tiles, so their bits agree, for every chunk count modulo four (the tile's
+    main loop takes four chunks a step), every active-tile count (skewed
+    routing), a ragged last N tile, and every epilogue and row source; both
+    within tolerance of the oracle."""
+    sh = W.MoEShape(name="prefill_tile", E_glob=12, E_loc=6, first=3, topk=4, T=400, K1=K1, N1=512,
+                    K2=K2, N2=272, zipf_s=1.0, seed=4242)
     P = Problem(sh).upload()
     r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, 128)
     flat = P.topk_ids.reshape(-1)
     counts = np.bincount(flat[(flat >= sh.first) & (flat < sh.first + sh.E_loc)] - sh.first, minlength=sh.E_loc)
-    log("rows per local expert", counts.tolist())
+    log(f"K1={K1} K2={K2} rows per local expert", counts.tolist())
+    tiles = {"prefill": (4, 4), "general": (2, 4)}     # (nr, waves)
     out = {}
-    for nr in (4, 2):
-        c = M.config(128, nr)
+    for name, (nr, waves) in tiles.items():
+        c = M.config(128, nr, waves)
         h = M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=c)
         y = M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=c)
         torch.cuda.synchronize()
-        out[nr] = (bits(h), bits(y))
-        _check_indexed(P, h, y, f"prefill tile check nr={nr}")
-    np.testing.assert_array_equal(out[4][0], out[2][0], err_msg="gate/up: prefill tile vs general kernel")
-    np.testing.assert_array_equal(out[4][1], out[2][1], err_msg="down+combine: prefill tile vs general kernel")
+        out[name] = (bits(h), bits(y))
+        if name == "prefill":
+            _check_indexed(P, h, y, f"prefill tile check K1={K1} K2={K2}")
+    for name in ("prefill",):
+        np.testing.assert_array_equal(out[name][0], out["general"][0], err_msg=f"gate/up: {name} vs general kernel")
+        np.testing.assert_array_equal(out[name][1], out["general"][1], err_msg=f"down+combine: {name} vs general kernel")
     # fused SiLU epilogue on the interleaved gate/up weight
     p1g = M.pack_w4(to_dev(P.c1), to_dev_bf16(P.s1), gate_up=True)
-    inter = {nr: bits(M.moe_gate_up_silu(P.d_x, p1g, r, cfg=M.config(128, nr))) for nr in (4, 2)}
+    inter = {name: bits(M.moe_gate_up_silu(P.d_x, p1g, r, cfg=M.config(128, nr, waves)))
+             for name, (nr, waves) in tiles.items()}
     valid = r.sorted_ids.cpu().numpy() < sh.T * sh.topk
-    np.testing.assert_array_equal(inter[4][valid], inter[2][valid], err_msg="fused SiLU: prefill tile")
+    for name in ("prefill",):
+        np.testing.assert_array_equal(inter[name][valid], inter["general"][valid], err_msg=f"fused SiLU: {name}")
     # grouped row sources
     A, mi, _ = W.contiguous_layout(P.topk_ids, P.x, sh.first, sh.E_loc, pad=128, pad_fill=0x7FC0)
-    oc = {nr: bits(M.grouped_contiguous(to_dev_bf16(A), P.p1, to_dev(mi), cfg=M.config(128, nr, kind="contiguous")))
-          for nr in (4, 2)}
+    oc = {name: bits(M.grouped_contiguous(to_dev_bf16(A), P.p1, to_dev(mi),
+                                          cfg=M.config(128, nr, waves, kind="contiguous")))
+          for name, (nr, waves) in tiles.items()}
     ok = mi >= 0
-    np.testing.assert_array_equal(oc[4][ok], oc[2][ok], err_msg="contiguous: prefill tile")
     ref, vr = O.grouped_contiguous(A, P.c1, P.s1, mi)
-    assert_close(oc[4][vr], ref[vr], "contiguous prefill tile")
     A3, mm, _, _ = W.masked_layout(P.topk_ids, P.x, sh.first, sh.E_loc, 200, pad_fill=0x7FC0)
-    om = {nr: bits(M.grouped_masked(to_dev_bf16(A3), P.p1, to_dev(mm), 100, cfg=M.config(128, nr, kind="masked")))
-          for nr in (4, 2)}
+    om = {name: bits(M.grouped_masked(to_dev_bf16(A3), P.p1, to_dev(mm), 100,
+                                      cfg=M.config(128, nr, waves, kind="masked")))
+          for name, (nr, waves) in tiles.items()}
     refm, vm = O.grouped_masked(A3, P.c1, P.s1, mm)
-    np.testing.assert_array_equal(om[4][vm], om[2][vm], err_msg="masked: prefill tile")
-    assert_close(om[4][vm], refm[vm], "masked prefill tile")
+    for name in ("prefill",):
+        np.testing.assert_array_equal(oc[name][ok], oc["general"][ok], err_msg=f"contiguous: {name}")
+        np.testing.assert_array_equal(om[name][vm], om["general"][vm], err_msg=f"masked: {name}")
+    assert_close(oc["prefill"][vr], ref[vr], "contiguous prefill tile")
+    assert_close(om["prefill"][vm], refm[vm], "masked prefill tile")
+
+
+def test_combine_passes_bit_identical():
+    """The down projection + combine over column passes (combine_cols) gives
+    the same bits as one pass over all N: each pass runs the GEMM over its
+    column range of the weights and combines those columns.  Pass widths
+    that cut a workgroup tile, leave a ragged last pass, or take one 16-column
+    tile; on the general kernel, the prefill tile, K slices and stream-K."""
+    sh = W.MoEShape(name="combine_passes", E_glob=12, E_loc=6, first=3, topk=4, T=300, K1=256, N1=64,
+                    K2=1024, N2=272, zipf_s=1.0, seed=515)
+    P = Problem(sh).upload()
+    ref = O.indexed_down_combine(P.a, P.c2, P.s2, P.topk_ids, P.topk_w, sh.first, sh.E_loc)
+    for bm, nr, split in ((32, 2, 1), (128, 4, 1), (32, 2, 2), (64, 2, 0)):
+        r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, bm)
+        one = bits(M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=M.config(bm, nr, split_k=split)))
+        assert_close(one, ref, f"down+combine bm={bm} nr={nr} split={split}")
+        for cols in (16, 64, 112, 256, 272):
+            got = bits(M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w,
+                                        cfg=M.config(bm, nr, split_k=split, combine_cols=cols)))
+            np.testing.assert_array_equal(got, one, err_msg=f"bm={bm} nr={nr} split={split} combine_cols={cols}")
+        log(f"bm={bm} nr={nr} split={split}: passes of 16..272 columns bit-identical to one pass")

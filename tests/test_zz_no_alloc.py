@@ -69,10 +69,16 @@ def test_noalloc_refuses_calls_beyond_its_scratch():
                     N2=7168, seed=99)
     P = Problem(sh).upload()
     r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, 32)
-    need = M.workspace_bytes(P.p2, r, True, M.config(32, 2))
-    assert need > 128 << 20                 # 640 x 8 x 7168 x 4 bytes of combine partials
+    one_pass = M.config(32, 2, combine_cols=sh.N2)
+    need = M.workspace_bytes(P.p2, r, True, one_pass)
+    assert need > 128 << 20                 # 640 x 8 x 7168 x 4 bytes of combine partials in one pass
     y = torch.full((sh.T, sh.N2), 3.0, dtype=torch.bfloat16, device=dev())
-    st = _call("noalloc", P, P.p2, P.d_a, _lib.A_SLOT, r, P.d_w, y, M.config(32, 2))
+    st = _call("noalloc", P, P.p2, P.d_a, _lib.A_SLOT, r, P.d_w, y, one_pass)
     assert st == -8 and b"scratch" in M.load().w4a16_last_error()
     torch.cuda.synchronize()
     assert bool((y.float() == 3.0).all()), "a refused call wrote its output"
+    # the same combine in two passes of 3584 columns fits the scratch array:
+    # same bits as the workspace call
+    two_passes = M.config(32, 2, combine_cols=3584)
+    assert M.workspace_bytes(P.p2, r, True, two_passes) == 640 * 8 * 3584 * 4
+    _compare(P, sh.T, M.config(32, 2), two_passes)

@@ -42,11 +42,12 @@ ROUTE_INDEXED, ROUTE_CONTIGUOUS, ROUTE_MASKED = 0, 1, 2   # W4A16_ROUTE_*
 class Config(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int32), ("nr", ctypes.c_int32),
                 ("waves", ctypes.c_int32), ("split_k", ctypes.c_int32), ("stages", ctypes.c_int32),
-                ("kind", ctypes.c_int32)]
+                ("kind", ctypes.c_int32), ("combine_cols", ctypes.c_int32)]
 
     def __repr__(self):
         return (f"Config(block_m={self.block_m}, nr={self.nr}, waves={self.waves}, "
-                f"split_k={self.split_k}, stages={self.stages}, kind={self.kind})")
+                f"split_k={self.split_k}, stages={self.stages}, kind={self.kind}, "
+                f"combine_cols={self.combine_cols})")
 
 
 class IndexedRouting(ctypes.Structure):

@@ -168,11 +168,13 @@ def select(T: int, topk: int, E_glob: int, E_loc: int, N: int, K: int, kind: str
 
 
 def config(block_m: int, nr: int, waves: int = 4, split_k: int = 1, stages: int = 2,
-           kind: str = "indexed") -> Config:
+           kind: str = "indexed", combine_cols: int = 0) -> Config:
     """split_k = 1: one workgroup per tile; 2, 4, 8, 16: K slices per tile,
     reduced in slice order; 0: stream-K over resident workgroups.
-    stages: K chunks of weights in flight per wave (2, or 4 for small tiles)."""
-    return Config(block_m, nr, waves, split_k, stages, _KINDS[kind])
+    stages: K chunks of weights in flight per wave (2, or 4 for small tiles).
+    combine_cols: output columns per GEMM + combine pass of a top-k combine
+    (0: the library's choice; else a multiple of 16)."""
+    return Config(block_m, nr, waves, split_k, stages, _KINDS[kind], combine_cols)
 
 
 def indexed_config(routing: "Routing", packed: PackedW4) -> Config:

@@ -202,7 +202,7 @@ std::vector<int> sampled_counts(int32_t T, int32_t topk, int32_t E_glob, int32_t
 // routing buffers already fix it.
 w4a16_config select_indexed(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N, int32_t K,
                             int32_t force_block_m) {
-  w4a16_config c;
+  w4a16_config c{};
   c.kind = W4A16_ROUTE_INDEXED;
   c.waves = 4;
   c.stages = 2;
@@ -239,7 +239,7 @@ w4a16_config select_indexed(int32_t T, int32_t topk, int32_t E_glob, int32_t E_l
 // grids, BM64 for small concatenated problems so M tiles still fill).
 w4a16_config select_contiguous(int64_t m_rows, int32_t E, int32_t N, int32_t K) {
   (void)E;
-  w4a16_config c;
+  w4a16_config c{};
   c.kind = W4A16_ROUTE_CONTIGUOUS;
   c.nr = 2;
   c.waves = 4;
@@ -258,7 +258,7 @@ w4a16_config select_contiguous(int64_t m_rows, int32_t E, int32_t N, int32_t K) 
 // Buffered K follows latency: 512 elements (four 128-K stages) for decode-size
 // blocks, two stages for larger ones.
 w4a16_config select_masked(int32_t max_m, int32_t E, int32_t N, int32_t K, int32_t expected_m) {
-  w4a16_config c;
+  w4a16_config c{};
   c.kind = W4A16_ROUTE_MASKED;
   c.nr = 2;
   c.waves = 4;
@@ -305,6 +305,9 @@ w4a16_status check_config(const w4a16_config& c, int route, int epi, int K) {
     return fail(W4A16_ERR_ARG, "config was chosen for routing kind %d, this call is kind %d (%s)", c.kind, route,
                 route == W4A16_ROUTE_INDEXED ? "indexed" : "grouped calls choose their own tiles");
   if (!valid_block_m(c.block_m)) return fail(W4A16_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128}", c.block_m);
+  if (c.combine_cols < 0 || c.combine_cols % 16)
+    return fail(W4A16_ERR_ARG, "combine_cols %d: 0 (the library's choice) or a positive multiple of 16",
+                c.combine_cols);
   if (!valid_split(c.split_k))
     return fail(W4A16_ERR_UNSUPPORTED, "split_k %d: 1 (one workgroup per tile), 2, 4, 8, 16 (K slices) or 0 (stream-K)",
                 c.split_k);
@@ -329,6 +332,7 @@ w4a16::GemmParams base_params(const w4a16_weight_desc* d, const void* pw, const 
   p.N = d->N;
   p.K = d->K;
   p.NT = d->N / 16;
+  p.w_tiles = d->N / 16;
   p.KC = d->K_pad / 128;
   p.n_tiles = n_tiles_of(d->N, nr, waves);
   p.gated = (d->flags & W4A16_DESC_GATE_UP) != 0;
@@ -338,7 +342,7 @@ w4a16::GemmParams base_params(const w4a16_weight_desc* d, const void* pw, const 
 }
 
 // Workspace carve-up (each region 256-byte aligned):
-//   [split counters, 4 B per splittable tile][split slices][combine partials, fp32 T*topk*N][stream-K partials]
+//   [split counters, 4 B per splittable tile][split slices][combine partials, fp32 T*topk*cols][stream-K partials]
 struct Workspace {
   size_t counters = 0, slices = 0, combine = 0, streamk = 0;
   int split_tiles = 0;
@@ -349,8 +353,33 @@ size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 
 int resident_workgroups(const w4a16_config& c, int epi);
 
-// tiles: an upper bound of the call's tiles (routed blocks x N tiles)
-Workspace workspace_layout(const w4a16_config& c, int epi, int64_t tiles, int32_t N, int32_t T, int32_t topk,
+// Output columns per pass of the down projection + combine.  A pass's fp32
+// per-slot partials are written by the GEMM and read back by the combine;
+// when they fit the last-level cache (256 MB) the combine reads them without
+// HBM write-backs competing.  Measured on MI355X: a buffer of up to 256 MB
+// written by one kernel reads back at 6.5 TB/s, a 1 GB one at 4.3 TB/s; TP8
+// T = 4096 (940 MB of partials) combines in 238 us in one pass, 145 us in
+// four.  Every extra pass costs the GEMM a fetch of each block's activation
+// rows per XCD (down GEMM 354 us in one pass, 391 us in four), so the
+// library's choice is the fewest passes whose expected partials (local slots
+// under uniform routing x columns x 4 bytes) stay within kCombinePassBytes,
+// in whole workgroup tiles; an explicit config's combine_cols wins.
+constexpr double kCombinePassBytes = 240.0 * (1 << 20);
+
+int32_t combine_cols_of(const w4a16_config& c, int32_t N, int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc) {
+  if (c.combine_cols > 0) return std::min(c.combine_cols, N);
+  const double local = E_glob > 0 ? std::min(1.0, (double)E_loc / E_glob) : 1.0;
+  const double bytes = (double)std::max(T, 0) * topk * local * N * 4.0;
+  if (bytes <= kCombinePassBytes) return N;
+  const int64_t passes = (int64_t)std::ceil(bytes / kCombinePassBytes);
+  const int64_t wg_n = 16 * (int64_t)c.nr * c.waves;
+  const int64_t cols = ((N + passes - 1) / passes + wg_n - 1) / wg_n * wg_n;
+  return (int32_t)std::min<int64_t>(cols, N);
+}
+
+// tiles: an upper bound of the call's tiles (routed blocks x N tiles);
+// cols: output columns per combine pass (combine_cols_of)
+Workspace workspace_layout(const w4a16_config& c, int epi, int64_t tiles, int32_t cols, int32_t T, int32_t topk,
                            bool combine) {
   Workspace w;
   if (c.split_k > 1) {
@@ -358,7 +387,7 @@ Workspace workspace_layout(const w4a16_config& c, int epi, int64_t tiles, int32_
     w.counters = al256((size_t)w.split_tiles * 4);
     w.slices = al256((size_t)w.split_tiles * c.split_k * w4a16::split_slice_bytes(c.block_m / 16, c.nr, c.waves));
   }
-  if (combine) w.combine = al256((size_t)T * topk * N * sizeof(float));
+  if (combine) w.combine = al256((size_t)T * topk * cols * sizeof(float));
   if (c.split_k == 0) {
     const int wgs = resident_workgroups(c, epi);
     if (wgs > 0) w.streamk = w4a16::streamk_partial_bytes(c.block_m / 16, c.nr, c.waves, wgs);
@@ -399,7 +428,7 @@ w4a16_config cached_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_lo
     auto it = g_cache.find(key);
     if (it != g_cache.end()) return it->second;
   }
-  w4a16_config c;
+  w4a16_config c{};
   if (kind == W4A16_ROUTE_CONTIGUOUS)
     c = select_contiguous(T, E_loc, N, K);
   else if (kind == W4A16_ROUTE_MASKED)
@@ -595,12 +624,13 @@ size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, const w4a16
   if (check_int4_desc(desc) != W4A16_OK || !routing) return 0;
   const w4a16_indexed_routing& r = *routing;
   if (r.T < 0 || r.topk <= 0 || r.E_loc <= 0 || !valid_block_m(r.block_m) || r.capacity < 0) return 0;
-  w4a16_config c;
+  w4a16_config c{};
   if (indexed_call_config(r, desc, cfg, &c) != W4A16_OK) return 0;
   const int epi = combine ? w4a16::kEpiWeighted : w4a16::kEpiStore;
   if (check_config(c, W4A16_ROUTE_INDEXED, epi, desc->K) != W4A16_OK) return 0;
   const int64_t tiles = indexed_block_bound(r) * n_tiles_of(desc->N, c.nr, c.waves);
-  return workspace_layout(c, epi, tiles, desc->N, r.T, r.topk, combine != 0).total();
+  const int32_t cols = combine_cols_of(c, desc->N, r.T, r.topk, r.E_glob, r.E_loc);
+  return workspace_layout(c, epi, tiles, cols, r.T, r.topk, combine != 0).total();
 }
 
 }  // extern "C"
@@ -632,7 +662,7 @@ w4a16_status moe_gemm_impl(const w4a16_weight_desc* desc, const void* packed_w, 
   st = check_offset_range(need_rows, desc->K, "activations");
   if (st != W4A16_OK) return st;
   const int epi = combine ? w4a16::kEpiWeighted : w4a16::kEpiStore;
-  w4a16_config c;
+  w4a16_config c{};
   st = indexed_call_config(r, desc, cfg, &c);
   if (st != W4A16_OK) return st;
   st = check_config(c, W4A16_ROUTE_INDEXED, epi, desc->K);
@@ -641,7 +671,8 @@ w4a16_status moe_gemm_impl(const w4a16_weight_desc* desc, const void* packed_w, 
     return fail(W4A16_ERR_LAYOUT, "config block_m=%d differs from the routing's block_m=%d", c.block_m, r.block_m);
   if (combine && !r.topk_ids) return fail(W4A16_ERR_ARG, "combine needs routing.topk_ids");
   const int64_t tiles = indexed_block_bound(r) * n_tiles_of(desc->N, c.nr, c.waves);
-  const Workspace wl = workspace_layout(c, epi, tiles, desc->N, r.T, r.topk, combine);
+  const int32_t cols = combine ? combine_cols_of(c, desc->N, r.T, r.topk, r.E_glob, r.E_loc) : desc->N;
+  const Workspace wl = workspace_layout(c, epi, tiles, cols, r.T, r.topk, combine);
   if (c.split_k == 0 && wl.streamk == 0)
     return fail(W4A16_ERR_HIP, "stream-K: could not query the device's resident workgroups");
   const size_t need = wl.total();
@@ -668,19 +699,30 @@ w4a16_status moe_gemm_impl(const w4a16_weight_desc* desc, const void* packed_w, 
   p.a_row_div = a_layout == W4A16_A_TOKEN ? r.topk : a_layout == W4A16_A_SLOT ? 1 : 0;
   p.slot_weight = topk_weights;
   p.grid_blocks = (int32_t)(r.capacity / r.block_m);
-  if (c.split_k == 0) {
-    p.sk_partial = reinterpret_cast<float*>(ws + wl.counters + wl.slices + wl.combine);
-    const int wgs = resident_workgroups(c, epi);
-    e = w4a16::launch_gemm_streamk(w4a16::kRouteIndexed, epi, c.block_m / 16, c.nr, c.waves, c.stages, p,
-                                   wgs, s);
-  } else {
-    attach_split(p, c, wl, ws);
-    e = w4a16::launch_gemm(w4a16::kRouteIndexed, epi, c.block_m / 16, c.nr, c.waves, c.stages, p, s);
-  }
-  if (e != hipSuccess) return hip_fail(e, "moe_gemm launch");
-  if (combine) {
-    e = w4a16::launch_combine(comb, r.topk_ids, r.T, r.topk, r.first_expert, r.E_loc, desc->N, out, s);
-    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  if (c.split_k == 0) p.sk_partial = reinterpret_cast<float*>(ws + wl.counters + wl.slices + wl.combine);
+  else attach_split(p, c, wl, ws);
+  // one pass per `cols` output columns (all of N without the combine): the
+  // GEMM over that column range of the weights, then its combine
+  const int64_t kc2 = (p.KC + 1) / 2;
+  for (int32_t n0 = 0; n0 < desc->N; n0 += cols) {
+    const int32_t nc = std::min(cols, desc->N - n0);
+    w4a16::GemmParams q = p;
+    q.packed_w = p.packed_w + (int64_t)(n0 / 16) * p.KC * 64;
+    q.packed_s = p.packed_s + (int64_t)(n0 / 16) * kc2 * 64;
+    q.N = nc;
+    q.NT = nc / 16;
+    q.n_tiles = n_tiles_of(nc, c.nr, c.waves);
+    if (c.split_k == 0) {
+      e = w4a16::launch_gemm_streamk(w4a16::kRouteIndexed, epi, c.block_m / 16, c.nr, c.waves, c.stages, q,
+                                     resident_workgroups(c, epi), s);
+    } else {
+      e = w4a16::launch_gemm(w4a16::kRouteIndexed, epi, c.block_m / 16, c.nr, c.waves, c.stages, q, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "moe_gemm launch");
+    if (combine) {
+      e = w4a16::launch_combine(comb, r.topk_ids, r.T, r.topk, r.first_expert, r.E_loc, nc, out + n0, desc->N, s);
+      if (e != hipSuccess) return hip_fail(e, "combine launch");
+    }
   }
   return W4A16_OK;
 }
@@ -749,7 +791,7 @@ w4a16_status w4a16_moe_gate_up_silu(const w4a16_weight_desc* desc, const void* p
   if (x_rows < r.T) return fail(W4A16_ERR_SHAPE, "activations have %lld rows, need %d", (long long)x_rows, r.T);
   st = check_offset_range(r.T, desc->K, "activations");
   if (st != W4A16_OK) return st;
-  w4a16_config c;
+  w4a16_config c{};
   st = indexed_call_config(r, desc, cfg, &c);
   if (st != W4A16_OK) return st;
   if (!cfg) c.split_k = 1;  // the fused epilogue runs whole tiles
@@ -804,7 +846,7 @@ size_t w4a16_grouped_workspace_bytes(const w4a16_weight_desc* desc, int32_t kind
                                      const w4a16_config* cfg) {
   if (check_int4_desc(desc) != W4A16_OK || rows < 0) return 0;
   if (kind != W4A16_ROUTE_CONTIGUOUS && kind != W4A16_ROUTE_MASKED) return 0;
-  w4a16_config c;
+  w4a16_config c{};
   if (grouped_call_config(kind, desc, rows, expected_m, cfg, &c) != W4A16_OK) return 0;
   if (check_config(c, kind, w4a16::kEpiStore, desc->K) != W4A16_OK) return 0;
   const int64_t tiles = grouped_blocks(kind, desc, rows, c) * n_tiles_of(desc->N, c.nr, c.waves);
@@ -844,7 +886,7 @@ w4a16_status w4a16_grouped_contiguous(const w4a16_weight_desc* desc, const void*
     return fail(W4A16_ERR_ARG, "packed weights, activations and output must be 16-byte aligned");
   st = check_offset_range(m_rows, desc->K, "activations");
   if (st != W4A16_OK) return st;
-  w4a16_config c;
+  w4a16_config c{};
   st = grouped_call_config(W4A16_ROUTE_CONTIGUOUS, desc, m_rows, 0, cfg, &c);
   if (st != W4A16_OK) return st;
   st = check_config(c, W4A16_ROUTE_CONTIGUOUS, w4a16::kEpiStore, desc->K);
@@ -873,7 +915,7 @@ w4a16_status w4a16_grouped_masked(const w4a16_weight_desc* desc, const void* pac
   if ((int64_t)desc->E * max_m >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "E * max_m too large");
   st = check_offset_range((int64_t)desc->E * max_m, desc->K, "activations");
   if (st != W4A16_OK) return st;
-  w4a16_config c;
+  w4a16_config c{};
   st = grouped_call_config(W4A16_ROUTE_MASKED, desc, max_m, expected_m, cfg, &c);
   if (st != W4A16_OK) return st;
   st = check_config(c, W4A16_ROUTE_MASKED, w4a16::kEpiStore, desc->K);
@@ -984,7 +1026,7 @@ w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* pac
   if (a_rows * (int64_t)(desc->K / 2) >= ((int64_t)1 << 32))
     return fail(W4A16_ERR_SHAPE, "activation codes exceed 4 GiB (32-bit row offsets)");
   const int epi = combine ? w4a16::kEpiWeighted : w4a16::kEpiStore;
-  w4a16_config c;
+  w4a16_config c{};
   if (cfg) {
     c = *cfg;
   } else {
@@ -1026,7 +1068,7 @@ w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* pac
   if (e != hipSuccess) return hip_fail(e, "mxfp4_moe_gemm launch");
   if (combine) {
     e = w4a16::launch_combine(static_cast<const float*>(workspace), r.topk_ids, r.T, r.topk, r.first_expert,
-                              r.E_loc, desc->N, out, s);
+                              r.E_loc, desc->N, out, desc->N, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
   }
   return W4A16_OK;
@@ -1055,7 +1097,7 @@ w4a16_status w4a16_mxfp4_gate_up_silu(const w4a16_weight_desc* desc, const void*
   if ((int64_t)r.T * r.topk >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "T*topk too large");
   if (x_rows * (int64_t)(desc->K / 2) >= ((int64_t)1 << 32))
     return fail(W4A16_ERR_SHAPE, "activation codes exceed 4 GiB (32-bit row offsets)");
-  w4a16_config c;
+  w4a16_config c{};
   if (cfg) {
     c = *cfg;
   } else {

@@ -124,7 +124,7 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const int rt = min(rt_base + r, p.NT - 1);
-    const int64_t tile = (int64_t)expert * p.NT + rt;
+    const int64_t tile = (int64_t)expert * p.w_tiles + rt;
     wbase[r] = uniform_ptr(p.packed_w + tile * p.KC * kWave);
     sbase[r] = uniform_ptr(p.packed_s + tile * ((p.KC + 1) / 2) * kWave);
   }
@@ -623,32 +623,60 @@ __global__ __launch_bounds__(NW * kWave) void streamk_fixup_kernel(const GemmPar
 }
 
 // Top-k combine: out[t, n] = bf16(sum over local j, in j order, of
-// partial[t*k + j, n]); tokens with no local slot get 0.
+// partial[t*k + j, n]); tokens with no local slot get 0.  One thread per
+// 8 columns of a token.  For topk <= KMAX every load (the token's ids, then
+// the partial rows of its local slots) is issued before the first add, so
+// the slots' latencies overlap instead of adding up; the sum still runs in
+// j order and skips non-local slots (an add of zero would turn -0 into +0).
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partial,
                                                       const int32_t* __restrict__ topk_ids,
                                                       int32_t T, int32_t topk, int32_t first,
                                                       int32_t E_loc, int32_t N,
-                                                      uint16_t* __restrict__ out) {
+                                                      uint16_t* __restrict__ out, int32_t ldo) {
   const int n8 = N / 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)T * n8) return;
   const int64_t t = idx / n8;
   const int n = (int)(idx - t * n8) * 8;
   float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < topk; ++j) {
-    const int e = topk_ids[t * topk + j] - first;
-    if ((unsigned)e >= (unsigned)E_loc) continue;
-    const float4* src = reinterpret_cast<const float4*>(partial + (t * topk + j) * (int64_t)N + n);
-    const float4 u = src[0], v = src[1];
+  auto add = [&](const float4& u, const float4& v) {
     a[0] += u.x; a[1] += u.y; a[2] += u.z; a[3] += u.w;
     a[4] += v.x; a[5] += v.y; a[6] += v.z; a[7] += v.w;
+  };
+  if (topk <= KMAX) {
+    // the id loads are unconditional (clamped index) so they issue together
+    int32_t id[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) id[j] = topk_ids[t * topk + (j < topk ? j : topk - 1)];
+    bool loc[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) loc[j] = j < topk && (unsigned)(id[j] - first) < (unsigned)E_loc;
+    float4 u[KMAX], v[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (loc[j]) {
+        const float4* src = reinterpret_cast<const float4*>(partial + (t * topk + j) * (int64_t)N + n);
+        u[j] = src[0];
+        v[j] = src[1];
+      }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (loc[j]) add(u[j], v[j]);
+  } else {
+    for (int j = 0; j < topk; ++j) {
+      const int e = topk_ids[t * topk + j] - first;
+      if ((unsigned)e >= (unsigned)E_loc) continue;
+      const float4* src = reinterpret_cast<const float4*>(partial + (t * topk + j) * (int64_t)N + n);
+      add(src[0], src[1]);
+    }
   }
   uint4 o;
   o.x = pack_bf16x2(a[0], a[1]);
   o.y = pack_bf16x2(a[2], a[3]);
   o.z = pack_bf16x2(a[4], a[5]);
   o.w = pack_bf16x2(a[6], a[7]);
-  *reinterpret_cast<uint4*>(out + t * N + n) = o;
+  *reinterpret_cast<uint4*>(out + t * ldo + n) = o;
 }
 
 // Zero `words` 32-bit words (a kernel, not hipMemsetAsync, so the call can
@@ -665,12 +693,17 @@ hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const float* partial, const int32_t* topk_ids, int32_t T, int32_t topk,
-                          int32_t first, int32_t E_loc, int32_t N, uint16_t* out,
+                          int32_t first, int32_t E_loc, int32_t cols, uint16_t* out, int32_t ldo,
                           hipStream_t stream) {
-  const int64_t threads = (int64_t)T * (N / 8);
+  const int64_t threads = (int64_t)T * (cols / 8);
   if (threads == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
-                     partial, topk_ids, T, topk, first, E_loc, N, out);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (topk <= 8)
+    hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(256), 0, stream, partial, topk_ids, T, topk, first, E_loc, cols,
+                       out, ldo);
+  else
+    hipLaunchKernelGGL(combine_kernel<16>, grid, dim3(256), 0, stream, partial, topk_ids, T, topk, first, E_loc, cols,
+                       out, ldo);
   return hipGetLastError();
 }
 

@@ -28,7 +28,9 @@ struct GemmParams {
   const uint32_t* packed_s;     // [E][NT][KC2][64], bf16 scale pairs (MXFP4: [E][NT][KC][64] E8M0 bytes)
   const uint16_t* a;            // bf16 activations, row stride K (MXFP4: E2M1 codes, two per byte, row stride K/2 bytes)
   const uint8_t* a_scale;       // MXFP4 activations: E8M0 scales, row stride K/32 bytes
-  int32_t E, N, K, NT, KC;
+  int32_t E, N, K, NT, KC;      // N, NT: the output columns (16-row weight tiles) this call covers
+  int32_t w_tiles;              // 16-row tiles per expert in packed_w / packed_s (>= NT: a call may
+                                // cover a column range, packed_w / packed_s then point at its first tile)
   int32_t n_tiles;              // workgroup tiles along N
   // indexed
   const int32_t* sorted_ids;
@@ -98,9 +100,10 @@ size_t split_slice_bytes(int m_tiles, int nr, int waves);
 // ---- zero fill of 32-bit words, graph-capturable (gemm.hip)
 hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t stream);
 
-// ---- combine of weighted per-slot partials (gemm.hip)
+// ---- combine of weighted per-slot partials (gemm.hip): partial [T*topk][cols]
+// fp32 -> out[t * ldo + c] bf16 for c < cols
 hipError_t launch_combine(const float* partial, const int32_t* topk_ids, int32_t T, int32_t topk,
-                          int32_t first, int32_t E_loc, int32_t N, uint16_t* out,
+                          int32_t first, int32_t E_loc, int32_t cols, uint16_t* out, int32_t ldo,
                           hipStream_t stream);
 
 // ---- A4W4: MXFP4 activations x MXFP4 weights (mx.hip)

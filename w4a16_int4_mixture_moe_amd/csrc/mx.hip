@@ -209,7 +209,7 @@ __device__ __forceinline__ void mx_mainloop(const GemmParams& p, const MxSmem<MT
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const int rt = min(rt_base + r, p.NT - 1);
-    const int64_t tile = (int64_t)expert * p.NT + rt;
+    const int64_t tile = (int64_t)expert * p.w_tiles + rt;
     wbase[r] = uniform_ptr(p.packed_w + tile * KC * kWave);
     sbase[r] = uniform_ptr(reinterpret_cast<const uint8_t*>(p.packed_s) + tile * KC * kWave);
   }
@@ -305,7 +305,7 @@ __device__ __forceinline__ void mx_mainloop_staged(const GemmParams& p, MxStaged
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const int rt = min(rt_base + r, p.NT - 1);
-    const int64_t tile = (int64_t)expert * p.NT + rt;
+    const int64_t tile = (int64_t)expert * p.w_tiles + rt;
     wbase[r] = uniform_ptr(p.packed_w + tile * KC * kWave);
     sbase[r] = uniform_ptr(reinterpret_cast<const uint8_t*>(p.packed_s) + tile * KC * kWave);
   }

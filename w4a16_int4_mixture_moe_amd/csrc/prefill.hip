@@ -10,7 +10,11 @@
 // Blackwell indexed decode" section) are amortised over 128 rows.  The
 // accumulators (4 x 8 MFMA tiles, 128 registers) stay in ordinary VGPRs and
 // the whole wave fits 256 registers, so two workgroups (two waves per SIMD)
-// share a CU.  That needs the activation staging to cost no registers: the
+// share a CU.  (One eight-wave workgroup of 512 weight rows per CU, which
+// stages each activation chunk once for twice the weight rows, measured 3-19 %
+// slower: its eight waves meet at every chunk barrier together, where two
+// independent workgroups cover each other's waits.)  That needs the
+// activation staging to cost no registers: the
 // block's rows are copied HBM -> LDS with global_load_lds_dwordx4 (16 bytes
 // per lane, straight into LDS), one 128-wide K chunk ahead of the MFMAs,
 // double buffered.
@@ -112,7 +116,7 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
 #pragma unroll
   for (int r = 0; r < kPfNR; ++r) {
     const int rt = min(rt_base + r, p.NT - 1);
-    const int64_t tile = (int64_t)expert * p.NT + rt;
+    const int64_t tile = (int64_t)expert * p.w_tiles + rt;
     wbase[r] = uniform_ptr(p.packed_w + tile * p.KC * kWave);
     sbase[r] = uniform_ptr(p.packed_s + tile * ((p.KC + 1) / 2) * kWave);
   }
@@ -148,26 +152,29 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
   // buffer and the weights of chunk c + 1 into the other register set, then
   // dequant + MFMAs of chunk c, then wait for the DMA and synchronise.
   // has_next: chunk c + 1 exists.
-  auto chunk = [&](auto P_, int c, bool has_next) {
+  //
+  // P = c % 2 and Q = (c / 2) % 2 are compile-time constants, so every ring
+  // index below is static (a run-time index puts the ring in scratch memory).
+  // P: the LDS buffer and weight register set of chunk c, and which half of
+  // the pair's scale word holds its scales (low for P = 0); Q: the scale
+  // register set of the chunk pair.
+  auto chunk = [&](auto P_, auto Q_, int c, bool has_next) {
     constexpr int P = decltype(P_)::value;
-    const int buf = c & 1;
-    // P is the chunk's parity: register set P holds its weights, and its
-    // scales sit in the low (P = 0) or high (P = 1) half of the pair's word
+    constexpr int Q = decltype(Q_)::value;
     if (has_next) {
-      issue_x(c + 1, buf ^ 1);
+      issue_x(c + 1, P ^ 1);
       __builtin_amdgcn_sched_barrier(0);
       issue_w(c + 1, wr[P ^ 1]);
-      if (P == 1) issue_s(c + 1, sr[((c + 1) >> 1) & 1]);
+      if (P == 1) issue_s(c + 1, sr[Q ^ 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    const char* xs = reinterpret_cast<const char*>(&sm.xs[buf][0]);
-    const int spair = (c >> 1) & 1;
+    const char* xs = reinterpret_cast<const char*>(&sm.xs[P][0]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bf16x8_t A[kPfNR];
 #pragma unroll
       for (int r = 0; r < kPfNR; ++r) {
-        const uint32_t word = spair ? sr[1][r] : sr[0][r];
+        const uint32_t word = sr[Q][r];
         const float sv = __builtin_bit_cast(float, P ? (word & 0xFFFF0000u) : (word << 16));
         A[r] = dequant8(wr[P][r][j], sv, -1032.0f * sv, 0.0625f * sv, -72.0f * sv, masks);
       }
@@ -198,13 +205,17 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   int c = 0;
-  for (; c + 2 < KC; c += 2) {
-    chunk(I0{}, c, true);
-    chunk(I1{}, c + 1, true);
+  for (; c + 4 < KC; c += 4) {
+    chunk(I0{}, I0{}, c, true);
+    chunk(I1{}, I0{}, c + 1, true);
+    chunk(I0{}, I1{}, c + 2, true);
+    chunk(I1{}, I1{}, c + 3, true);
   }
-  // the last one or two chunks
-  if (c < KC) chunk(I0{}, c, c + 1 < KC);
-  if (c + 1 < KC) chunk(I1{}, c + 1, false);
+  // the last one to four chunks (c is a multiple of four here)
+  if (c < KC) chunk(I0{}, I0{}, c, c + 1 < KC);
+  if (c + 1 < KC) chunk(I1{}, I0{}, c + 1, c + 2 < KC);
+  if (c + 2 < KC) chunk(I0{}, I1{}, c + 2, c + 3 < KC);
+  if (c + 3 < KC) chunk(I1{}, I1{}, c + 3, false);
 }
 
 // The block's tiles: the main loop specialised for its active token tiles
