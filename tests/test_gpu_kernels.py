@@ -627,3 +627,45 @@ def test_combine_passes_bit_identical():
                                         cfg=M.config(bm, nr, split_k=split, combine_cols=cols)))
             np.testing.assert_array_equal(got, one, err_msg=f"bm={bm} nr={nr} split={split} combine_cols={cols}")
         log(f"bm={bm} nr={nr} split={split}: passes of 16..272 columns bit-identical to one pass")
+
+
+def test_prefill_tile_n_tile_loop_bit_identical():
+    """K of at most 256 on the prefill tile: when the grid is large enough a
+    workgroup keeps its block's activation rows in LDS and runs several N
+    tiles (here 445 routed-block slots x 7 N tiles: two tiles per workgroup,
+    the last group one tile).  Bits equal the general kernel's for the per-slot
+    store, the weighted combine, the fused SiLU epilogue and the contiguous
+    layout; sampled outputs within tolerance of the oracle."""
+    sh = W.MoEShape(name="pf_loop", E_glob=384, E_loc=384, first=0, topk=8, T=1024, K1=256, N1=1792,
+                    K2=256, N2=1792, seed=4343)
+    P = Problem(sh).upload()
+    r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, 128)
+    assert r.capacity // 128 == 445
+    out = {}
+    for name, nr in (("prefill", 4), ("general", 2)):
+        c = M.config(128, nr)
+        h = M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=c)
+        y = M.moe_w4a16_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=c)
+        torch.cuda.synchronize()
+        out[name] = (bits(h), bits(y))
+    np.testing.assert_array_equal(out["prefill"][0], out["general"][0], err_msg="gate/up: N-tile loop")
+    np.testing.assert_array_equal(out["prefill"][1], out["general"][1], err_msg="down+combine: N-tile loop")
+    rng = np.random.default_rng(7)
+    flat = P.topk_ids.reshape(-1)
+    slots = rng.choice(len(flat), 64, replace=False)
+    cols = np.unique(np.concatenate([rng.choice(sh.N1, 64, replace=False), [0, sh.N1 - 1]]))
+    ref, _ = O.indexed_gate_up(P.x, P.c1, P.s1, P.topk_ids, sh.first, sh.E_loc, slots=slots, cols=cols)
+    assert_close(out["prefill"][0][slots][:, cols], ref, "N-tile loop gate/up")
+    toks = rng.choice(sh.T, 48, replace=False)
+    ref2 = O.indexed_down_combine(P.a, P.c2, P.s2, P.topk_ids, P.topk_w, sh.first, sh.E_loc, tokens=toks, cols=cols)
+    assert_close(out["prefill"][1][toks][:, cols], ref2, "N-tile loop down+combine")
+    p1g = M.pack_w4(to_dev(P.c1), to_dev_bf16(P.s1), gate_up=True)
+    inter = {nr: bits(M.moe_gate_up_silu(P.d_x, p1g, r, cfg=M.config(128, nr))) for nr in (4, 2)}
+    valid = r.sorted_ids.cpu().numpy() < sh.T * sh.topk
+    np.testing.assert_array_equal(inter[4][valid], inter[2][valid], err_msg="fused SiLU: N-tile loop")
+    A, mi, _ = W.contiguous_layout(P.topk_ids, P.x, sh.first, sh.E_loc, pad=128, pad_fill=0x7FC0)
+    dA, dmi = to_dev_bf16(A), to_dev(mi)
+    oc = {nr: bits(M.grouped_contiguous(dA, P.p1, dmi, cfg=M.config(128, nr, kind="contiguous"))) for nr in (4, 2)}
+    ok = mi >= 0
+    np.testing.assert_array_equal(oc[4][ok], oc[2][ok], err_msg="contiguous: N-tile loop")
+    log("N-tile loop: bit-identical to the general kernel; rows", int(ok.sum()))

@@ -77,9 +77,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // acc += this wave's 64 weight rows x the block's first 16 NA rows over all K.
-template <int NA>
+// SHORT: K is at most two chunks.  resident (SHORT only): the block's
+// activation rows are already in LDS from the previous N tile (two chunks
+// fill both buffers); nothing is staged.
+template <int NA, bool SHORT>
 __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int expert, int nt,
-                                            f32x4_t (&acc)[kPfNR][kPfMT]) {
+                                            f32x4_t (&acc)[kPfNR][kPfMT], bool resident) {
   static_assert(NA >= 1 && NA <= kPfMT, "active tile count");
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -91,7 +94,7 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
   // 4 i + l / 16, position l % 16, so it loads granule (l % 16) ^ (row % 16)
   // of that row, the same granule for every k (16 k leaves row % 16 alone).
   // (the per-lane source offsets are kept in LDS, sm.xoff, not in registers)
-  {
+  if (!resident) {
     const int fallback_row = sm.row[0];   // always valid
     for (int i = tid; i < kPfBM; i += kPfNW * kWave) {
       const int r = sm.row[i];
@@ -103,6 +106,7 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
   const int xrow = 4 * wave + (lane >> 4);
   const gptr_t xbase = uniform_ptr(p.a);
   auto issue_x = [&](int c, int buf) {
+    if (resident) return;
     const gptr_t base = xbase + (int64_t)c * (kChunk * 2) + gran;
 #pragma unroll
     for (int k = 0; k < NA; ++k)
@@ -204,35 +208,52 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  int c = 0;
-  for (; c + 4 < KC; c += 4) {
-    chunk(I0{}, I0{}, c, true);
-    chunk(I1{}, I0{}, c + 1, true);
-    chunk(I0{}, I1{}, c + 2, true);
-    chunk(I1{}, I1{}, c + 3, true);
+  if constexpr (SHORT) {
+    chunk(I0{}, I0{}, 0, KC > 1);
+    if (KC > 1) chunk(I1{}, I0{}, 1, false);
+  } else {
+    int c = 0;
+    for (; c + 4 < KC; c += 4) {
+      chunk(I0{}, I0{}, c, true);
+      chunk(I1{}, I0{}, c + 1, true);
+      chunk(I0{}, I1{}, c + 2, true);
+      chunk(I1{}, I1{}, c + 3, true);
+    }
+    // the last one to four chunks (c is a multiple of four here)
+    if (c < KC) chunk(I0{}, I0{}, c, c + 1 < KC);
+    if (c + 1 < KC) chunk(I1{}, I0{}, c + 1, c + 2 < KC);
+    if (c + 2 < KC) chunk(I0{}, I1{}, c + 2, c + 3 < KC);
+    if (c + 3 < KC) chunk(I1{}, I1{}, c + 3, false);
   }
-  // the last one to four chunks (c is a multiple of four here)
-  if (c < KC) chunk(I0{}, I0{}, c, c + 1 < KC);
-  if (c + 1 < KC) chunk(I1{}, I0{}, c + 1, c + 2 < KC);
-  if (c + 2 < KC) chunk(I0{}, I1{}, c + 2, c + 3 < KC);
-  if (c + 3 < KC) chunk(I1{}, I1{}, c + 3, false);
 }
 
 // The block's tiles: the main loop specialised for its active token tiles
 // (a prefix, rounded up to an even count: at most one tile of padding rows
 // multiplied), then the epilogue.
-template <int EPI>
-__device__ __forceinline__ void pf_run(const GemmParams& p, PfSmem& sm, int expert, int nt, uint32_t tmask) {
+// N tiles nt0 .. nt1 - 1 of the block, one after another.  LOOP (a kernel
+// of its own, so the registers of the one-tile kernels are unaffected): more
+// than one tile, K fits the two LDS buffers and the later tiles reuse the
+// staged rows.
+template <int EPI, bool LOOP>
+__device__ __forceinline__ void pf_run(const GemmParams& p, PfSmem& sm, int expert, int nt0, int nt1,
+                                       uint32_t tmask) {
   const int na = 32 - __clz(tmask);
   auto go = [&](auto NA_) {
     constexpr int NA = decltype(NA_)::value;
-    f32x4_t acc[kPfNR][kPfMT];
+    auto tile = [&](int nt, bool resident) {
+      f32x4_t acc[kPfNR][kPfMT];
 #pragma unroll
-    for (int r = 0; r < kPfNR; ++r)
+      for (int r = 0; r < kPfNR; ++r)
 #pragma unroll
-      for (int t = 0; t < kPfMT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    pf_mainloop<NA>(p, sm, expert, nt, acc);
-    epilogue<kPfMT, kPfNR, kPfNW, EPI>(p, sm, nt, (1u << NA) - 1u, acc);
+        for (int t = 0; t < kPfMT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      pf_mainloop<NA, LOOP>(p, sm, expert, nt, acc, resident);
+      epilogue<kPfMT, kPfNR, kPfNW, EPI>(p, sm, nt, (1u << NA) - 1u, acc);
+    };
+    if constexpr (LOOP) {
+      for (int nt = nt0; nt < nt1; ++nt) tile(nt, nt != nt0);
+    } else {
+      tile(nt0, false);
+    }
   };
   if (na <= 2)
     go(std::integral_constant<int, 2>{});
@@ -244,36 +265,44 @@ __device__ __forceinline__ void pf_run(const GemmParams& p, PfSmem& sm, int expe
     go(std::integral_constant<int, 8>{});
 }
 
-template <int ROUTE, int EPI>
-__global__ __launch_bounds__(kPfNW * kWave, 2) void moe_gemm_prefill_kernel(const GemmParams p) {
+// One workgroup per (routed block, group of n_loop consecutive N tiles);
+// n_loop > 1 only when K fits the two LDS buffers.
+template <int ROUTE, int EPI, bool LOOP>
+__global__ __launch_bounds__(kPfNW * kWave, 2) void moe_gemm_prefill_kernel(const GemmParams p, int n_loop) {
   __shared__ __attribute__((aligned(16))) PfSmem sm;
-  // work item (routed block, N tile), block-major: consecutive workgroups
-  // (the N tiles of one block) go to different XCDs.  Measured against
-  // orders that keep a block's N tiles on one XCD (its activation rows then
-  // come from HBM once): all sixteen side by side there, 4.8x slower (one
-  // L2 serving the same lines to sixteen CUs at once); spread over time
-  // (N-tile-major), 1-8 % slower.
-  const int mb = blockIdx.x / p.n_tiles;
-  const int nt = blockIdx.x - mb * p.n_tiles;
+  // work item (routed block, N-tile group), block-major: consecutive
+  // workgroups (the N tiles of one block) go to different XCDs.  Measured
+  // against orders that keep a block's N tiles on one XCD (its activation
+  // rows then come from HBM once): all sixteen side by side there, 4.8x
+  // slower (one L2 serving the same lines to sixteen CUs at once); spread
+  // over time (N-tile-major), 1-8 % slower.
+  const int groups = (p.n_tiles + n_loop - 1) / n_loop;
+  const int mb = blockIdx.x / groups;
+  const int nt0 = (blockIdx.x - mb * groups) * n_loop;
   const int expert = setup_rows<kPfMT, kPfNW, ROUTE, EPI>(p, mb, sm);
   if (expert < 0) return;
   __syncthreads();
-  pf_run<EPI>(p, sm, expert, nt, active_tiles<kPfMT>(sm));
+  pf_run<EPI, LOOP>(p, sm, expert, nt0, min(nt0 + n_loop, p.n_tiles), active_tiles<kPfMT>(sm));
 }
 
-typedef void (*PfKernel)(const GemmParams);
+typedef void (*PfKernel)(const GemmParams, int);
 
-PfKernel pick_prefill(int route, int epi) {
+template <bool LOOP>
+PfKernel pick_prefill_loop(int route, int epi) {
   if (route == kRouteIndexed) {
-    if (epi == kEpiStore) return moe_gemm_prefill_kernel<kRouteIndexed, kEpiStore>;
-    if (epi == kEpiWeighted) return moe_gemm_prefill_kernel<kRouteIndexed, kEpiWeighted>;
-    if (epi == kEpiSilu) return moe_gemm_prefill_kernel<kRouteIndexed, kEpiSilu>;
+    if (epi == kEpiStore) return moe_gemm_prefill_kernel<kRouteIndexed, kEpiStore, LOOP>;
+    if (epi == kEpiWeighted) return moe_gemm_prefill_kernel<kRouteIndexed, kEpiWeighted, LOOP>;
+    if (epi == kEpiSilu) return moe_gemm_prefill_kernel<kRouteIndexed, kEpiSilu, LOOP>;
     return nullptr;
   }
   if (epi != kEpiStore) return nullptr;
-  if (route == kRouteContiguous) return moe_gemm_prefill_kernel<kRouteContiguous, kEpiStore>;
-  if (route == kRouteMasked) return moe_gemm_prefill_kernel<kRouteMasked, kEpiStore>;
+  if (route == kRouteContiguous) return moe_gemm_prefill_kernel<kRouteContiguous, kEpiStore, LOOP>;
+  if (route == kRouteMasked) return moe_gemm_prefill_kernel<kRouteMasked, kEpiStore, LOOP>;
   return nullptr;
+}
+
+PfKernel pick_prefill(int route, int epi, bool loop = false) {
+  return loop ? pick_prefill_loop<true>(route, epi) : pick_prefill_loop<false>(route, epi);
 }
 
 }  // namespace
@@ -283,13 +312,33 @@ bool prefill_applies(int route, int epilogue, int m_tiles, int nr, int waves, in
          pick_prefill(route, epilogue) != nullptr;
 }
 
+// N tiles per workgroup.  With K of at most two chunks (K <= 256, the down
+// projection of a TP8 share) a block's 128 activation rows (64 KB at K = 256)
+// outweigh an N tile's weights (36 KB with scales), and every N tile's
+// workgroup fetches them again; a workgroup that keeps them in LDS and runs
+// several N tiles fetches them once.  As many tiles per workgroup as keep the
+// grid at kPfLoopMinWorkgroups or more (the routed-block bound counts every
+// block).  Measured on MI355X, TP8 T = 4096 down + combine in four passes of
+// seven N tiles: one tile per workgroup 541 us; 2, 3, 7 tiles 513, 501,
+// 515 us; 4 tiles (two workgroups per block) 684 us.
+constexpr int64_t kPfLoopMinWorkgroups = 1536;
+
+int prefill_n_loop(const GemmParams& p) {
+  if (p.KC > 2) return 1;
+  int best = 1;
+  for (int l = 2; l <= p.n_tiles; ++l)
+    if ((int64_t)p.grid_blocks * ((p.n_tiles + l - 1) / l) >= kPfLoopMinWorkgroups) best = l;
+  return best;
+}
+
 hipError_t launch_gemm_prefill(int route, int epilogue, const GemmParams& p, hipStream_t stream) {
-  const PfKernel k = pick_prefill(route, epilogue);
+  const int n_loop = prefill_n_loop(p);
+  const PfKernel k = pick_prefill(route, epilogue, n_loop > 1);
   if (k == nullptr || p.K % kChunk) return hipErrorInvalidValue;
-  const int64_t grid = (int64_t)p.grid_blocks * p.n_tiles;
+  const int64_t grid = (int64_t)p.grid_blocks * ((p.n_tiles + n_loop - 1) / n_loop);
   if (grid <= 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kPfNW * kWave), 0, stream, p);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kPfNW * kWave), 0, stream, p, n_loop);
   return hipGetLastError();
 }
 
