@@ -100,12 +100,13 @@ def cfg_tag(cfg) -> str:
 def kernel_name(cfg, route: int, epi: int, K: int, mx: bool = False) -> str:
     """The GEMM kernel's name as the rocprofv3 kernel trace shows it (the
     library runs the 128-row, 4-tiles-per-wave, unsplit configurations on its
-    prefill tile when K is a multiple of 128)."""
+    prefill tile when K is a multiple of 128, in its N-tile-loop form for
+    K <= 256 on the grids measured here)."""
     if mx:
         return f"mx_gemm_kernel<{cfg.block_m // 16}, {cfg.nr}, {cfg.waves}, {cfg.stages}, {epi}>"
     if (cfg.block_m == 128 and cfg.nr == 4 and cfg.waves == 4 and cfg.stages == 2 and cfg.split_k <= 1
             and K % 128 == 0):
-        return f"moe_gemm_prefill_kernel<{cfg.waves}, {route}, {epi}>"
+        return f"moe_gemm_prefill_kernel<{route}, {epi}, {'true' if K <= 256 else 'false'}>"
     return f"moe_gemm_kernel<{cfg.block_m // 16}, {cfg.nr}, {cfg.waves}, {cfg.stages}, {route}, {epi}>"
 
 

@@ -22,11 +22,17 @@
 // LDS layout.  A staged chunk is 128 rows x 256 bytes (128 bf16 of K).  The
 // LDS-DMA writes each instruction's 64 lanes to 1 KB of consecutive LDS (four
 // rows), so rows cannot be padded; instead the sixteen 16-byte granules of
-// row r are stored XOR-swizzled, granule q at position q ^ (r % 16).  The
-// MFMA operand read of lane l (row 16 t + l % 16, granule 4 (l / 16) + j)
-// then touches sixteen different positions in each group of sixteen lanes:
-// conflict-free (measured at the rate of linear reads; unswizzled rows run at
-// half that rate).
+// row r are permuted, granule q at position q ^ swz(r) with
+// swz(r) = (r % 4) ^ (12 if bit 2 of r is set).  The MFMA operand read of
+// lane l (row 16 t + l % 16, granule 4 (l / 16) + j) is then free of bank
+// conflicts.  Measured on MI355X with SQ_LDS_BANK_CONFLICT (a wave's
+// ds_read_b128 takes 4 LDS cycles when linear): q ^ swz(r) 4 cycles;
+// q ^ (r % 16), q ^ (r % 8), and 272-byte padded rows 8 cycles each.  gfx950
+// serves the 64 lanes of a b128 read 16 at a time, and the lanes that share
+// a cycle are not a run of 16 consecutive lanes (that model would make
+// q ^ (r % 16) conflict-free); swz was chosen to be conflict-free under every
+// lane grouping and 64-bank mapping consistent with a set of measured read
+// patterns, and measured so.
 //
 // Arithmetic is that of moe_gemm_kernel: the same packed weights and scales,
 // dequant8, v_mfma_f32_16x16x32_bf16 with the weights as the A operand, K
@@ -91,7 +97,7 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
 
   // LDS-DMA of a chunk: instruction i (of 4 NA) writes block rows 4 i .. 4 i + 3;
   // this wave issues i = wave + 4 k, k < NA.  Lane l lands at row
-  // 4 i + l / 16, position l % 16, so it loads granule (l % 16) ^ (row % 16)
+  // 4 i + l / 16, position l % 16, so it loads granule (l % 16) ^ swz(row)
   // of that row, the same granule for every k (16 k leaves row % 16 alone).
   // (the per-lane source offsets are kept in LDS, sm.xoff, not in registers)
   if (!resident) {
@@ -102,7 +108,8 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
     }
   }
   __syncthreads();
-  const uint32_t gran = (uint32_t)(((lane & 15) ^ ((4 * wave + (lane >> 4)) & 15)) * 16);
+  // row % 16 = 4 wave + l / 16: swz = l / 16 ^ (12 if wave is odd)
+  const uint32_t gran = (uint32_t)(((lane & 15) ^ (lane >> 4) ^ ((wave & 1) * 12)) * 16);
   const int xrow = 4 * wave + (lane >> 4);
   const gptr_t xbase = uniform_ptr(p.a);
   auto issue_x = [&](int c, int buf) {
@@ -183,7 +190,7 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
         A[r] = dequant8(wr[P][r][j], sv, -1032.0f * sv, 0.0625f * sv, -72.0f * sv, masks);
       }
       const uint32_t rowoff = (uint32_t)(lane & 15) * 256u;
-      const uint32_t goff = (uint32_t)((((lane >> 4) * 4 + j) ^ (lane & 15)) * 16);
+      const uint32_t goff = (uint32_t)((((lane >> 4) * 4 + j) ^ (lane & 3) ^ (((lane >> 2) & 1) * 12)) * 16);
 #pragma unroll
       for (int t = 0; t < NA; ++t) {
         const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(xs + t * 4096 + rowoff + goff);
