@@ -267,7 +267,8 @@ typedef struct {
  *     then that many tiles' fp32 slices;
  *   - combine != 0: the fp32 per-slot partials of one pass,
  *     T * topk * cols * 4 bytes (cols: the config's combine_cols, or the
- *     library's choice for it);
+ *     library's choice for it), then T bytes of local-slot counts per token
+ *     (each region rounded up to 256 bytes);
  *   - split_k = 0: two partial tiles per resident workgroup of the current
  *     device.
  * The workspace must be zero-filled once before its first use (the arrival
@@ -292,7 +293,9 @@ size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, const w4a16
  *  topk_weights != NULL (float32 [T, topk]): top-k-weighted combine,
  *               out[t] = bf16(sum over local j of w[t][j] * (a_row . W[e]^T))
  *               with fp32 products, summed in j order, one rounding; tokens
- *               without local slots get 0; every row of out[T, N] written.
+ *               without local slots get 0; every row of out[T, N] written
+ *               (a token with one local slot is written by the GEMM itself:
+ *               bf16 of that one product).
  *               Needs workspace (fp32 partials per slot).
  *               A weight packed with interleaved gate/up tiles
  *               (W4A16_DESC_GATE_UP) is rejected here (ERR_LAYOUT): the

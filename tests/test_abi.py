@@ -141,10 +141,11 @@ def test_capacity_and_workspace(L):
     d = W.weight_desc(4, 7168, 2048)
     r = _routing(10, 8, 4, 32)
     one_wg_per_tile = W.config(32, 2, split_k=1)
-    assert _ws(d, r, True, one_wg_per_tile) == 10 * 8 * 7168 * 4
+    tok = 256                                          # local-slot counts of the 10 tokens, one 256-byte region
+    assert _ws(d, r, True, one_wg_per_tile) == 10 * 8 * 7168 * 4 + tok
     assert _ws(d, r, False, one_wg_per_tile) == 0
     assert _ws(d, r, True, W.config(32, 3)) == 0                     # unsupported config
-    assert _ws(d, r, True, W.config(32, 2, stages=4)) == 10 * 8 * 7168 * 4
+    assert _ws(d, r, True, W.config(32, 2, stages=4)) == 10 * 8 * 7168 * 4 + tok
     assert _ws(d, r, True, W.config(64, 4, stages=4)) == 0           # not built
     assert _ws(d, r, True, W.config(32, 2, stages=3)) == 0           # odd depth: not built
     assert _ws(d, r, True, W.config(32, 2, kind="masked")) == 0      # config of another routing kind
@@ -155,7 +156,7 @@ def test_capacity_and_workspace(L):
     tiles = blocks * (7168 // 16 // 8)
     al = lambda v: -(-v // 256) * 256
     slices = tiles * 4 * (2 * 2 * 256 * 16)
-    assert _ws(d, r, True, W.config(32, 2, split_k=4)) == al(tiles * 4) + al(slices) + 10 * 8 * 7168 * 4
+    assert _ws(d, r, True, W.config(32, 2, split_k=4)) == al(tiles * 4) + al(slices) + 10 * 8 * 7168 * 4 + tok
     assert _ws(d, r, True, W.config(32, 2, split_k=32)) == 0         # not a split count
     # cfg NULL: the selector's config for the routing's block_m
     c = _lib.Config()
@@ -172,9 +173,10 @@ def test_combine_passes_size_the_workspace(L):
     else the fewest passes that do, in whole workgroup tiles)."""
     d = W.weight_desc(4, 7168, 2048)
     r = _routing(10, 8, 4, 32)
-    assert _ws(d, r, True, W.config(32, 2, combine_cols=1024)) == 10 * 8 * 1024 * 4
-    assert _ws(d, r, True, W.config(32, 2, combine_cols=16)) == -(-(10 * 8 * 16 * 4) // 256) * 256
-    assert _ws(d, r, True, W.config(32, 2, combine_cols=8192)) == 10 * 8 * 7168 * 4   # capped at N
+    tok = 256                                          # local-slot counts per token, rounded to 256 bytes
+    assert _ws(d, r, True, W.config(32, 2, combine_cols=1024)) == 10 * 8 * 1024 * 4 + tok
+    assert _ws(d, r, True, W.config(32, 2, combine_cols=16)) == -(-(10 * 8 * 16 * 4) // 256) * 256 + tok
+    assert _ws(d, r, True, W.config(32, 2, combine_cols=8192)) == 10 * 8 * 7168 * 4 + tok   # capped at N
     assert _ws(d, r, True, W.config(32, 2, combine_cols=24)) == 0       # not a multiple of 16
     assert _ws(d, r, True, W.config(32, 2, combine_cols=-16)) == 0
     assert _ws(d, r, False, W.config(32, 2, combine_cols=1024)) == 0    # no combine, no partials
@@ -183,14 +185,14 @@ def test_combine_passes_size_the_workspace(L):
     # 1792 columns (7 workgroup tiles of 256)
     d2 = W.weight_desc(384, 7168, 256)
     r2 = _lib.IndexedRouting(None, None, None, 40960, 128, 4096, 8, None, 0, 384, 384)
-    assert _ws(d2, r2, True, W.config(128, 4)) == 4096 * 8 * 1792 * 4
+    assert _ws(d2, r2, True, W.config(128, 4)) == 4096 * 8 * 1792 * 4 + 4096
     # T = 1024: 235 MB fits one pass
     r4 = _lib.IndexedRouting(None, None, None, 10240, 32, 1024, 8, None, 0, 384, 384)
-    assert _ws(d2, r4, True, W.config(32, 2)) == 1024 * 8 * 7168 * 4
+    assert _ws(d2, r4, True, W.config(32, 2)) == 1024 * 8 * 7168 * 4 + 1024
     # an EP8 share (1 in 8 slots local) of T = 576 stays one pass
     d3 = W.weight_desc(48, 7168, 2048)
     r3 = _lib.IndexedRouting(None, None, None, 6144, 32, 576, 8, None, 0, 48, 384)
-    assert _ws(d3, r3, True, W.config(32, 2)) == 576 * 8 * 7168 * 4
+    assert _ws(d3, r3, True, W.config(32, 2)) == 576 * 8 * 7168 * 4 + 768
 
 
 def test_align_argument_errors(L):

@@ -80,5 +80,5 @@ def test_noalloc_refuses_calls_beyond_its_scratch():
     # the same combine in two passes of 3584 columns fits the scratch array:
     # same bits as the workspace call
     two_passes = M.config(32, 2, combine_cols=3584)
-    assert M.workspace_bytes(P.p2, r, True, two_passes) == 640 * 8 * 3584 * 4
+    assert M.workspace_bytes(P.p2, r, True, two_passes) == 640 * 8 * 3584 * 4 + 768   # + local-slot counts
     _compare(P, sh.T, M.config(32, 2), two_passes)

@@ -342,11 +342,12 @@ w4a16::GemmParams base_params(const w4a16_weight_desc* d, const void* pw, const 
 }
 
 // Workspace carve-up (each region 256-byte aligned):
-//   [split counters, 4 B per splittable tile][split slices][combine partials, fp32 T*topk*cols][stream-K partials]
+//   [split counters, 4 B per splittable tile][split slices][combine partials, fp32 T*topk*cols]
+//   [stream-K partials][local slots per token, T bytes (combine)]
 struct Workspace {
-  size_t counters = 0, slices = 0, combine = 0, streamk = 0;
+  size_t counters = 0, slices = 0, combine = 0, streamk = 0, tokens = 0;
   int split_tiles = 0;
-  size_t total() const { return counters + slices + combine + streamk; }
+  size_t total() const { return counters + slices + combine + streamk + tokens; }
 };
 
 size_t al256(size_t v) { return (v + 255) / 256 * 256; }
@@ -366,10 +367,18 @@ int resident_workgroups(const w4a16_config& c, int epi);
 // in whole workgroup tiles; an explicit config's combine_cols wins.
 constexpr double kCombinePassBytes = 240.0 * (1 << 20);
 
+// fp32 per-slot partials of the local slots under uniform routing
+double expected_partial_bytes(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N) {
+  const double local = E_glob > 0 ? std::min(1.0, (double)E_loc / E_glob) : 1.0;
+  return (double)std::max(T, 0) * topk * local * N * 4.0;
+}
+
+// Partials from which tokens with one local slot bypass them (see moe_gemm_impl).
+constexpr double kDirectMinBytes = 64.0 * (1 << 20);
+
 int32_t combine_cols_of(const w4a16_config& c, int32_t N, int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc) {
   if (c.combine_cols > 0) return std::min(c.combine_cols, N);
-  const double local = E_glob > 0 ? std::min(1.0, (double)E_loc / E_glob) : 1.0;
-  const double bytes = (double)std::max(T, 0) * topk * local * N * 4.0;
+  const double bytes = expected_partial_bytes(T, topk, E_glob, E_loc, N);
   if (bytes <= kCombinePassBytes) return N;
   const int64_t passes = (int64_t)std::ceil(bytes / kCombinePassBytes);
   const int64_t wg_n = 16 * (int64_t)c.nr * c.waves;
@@ -387,7 +396,10 @@ Workspace workspace_layout(const w4a16_config& c, int epi, int64_t tiles, int32_
     w.counters = al256((size_t)w.split_tiles * 4);
     w.slices = al256((size_t)w.split_tiles * c.split_k * w4a16::split_slice_bytes(c.block_m / 16, c.nr, c.waves));
   }
-  if (combine) w.combine = al256((size_t)T * topk * cols * sizeof(float));
+  if (combine) {
+    w.combine = al256((size_t)T * topk * cols * sizeof(float));
+    w.tokens = al256((size_t)std::max(T, 0));
+  }
   if (c.split_k == 0) {
     const int wgs = resident_workgroups(c, epi);
     if (wgs > 0) w.streamk = w4a16::streamk_partial_bytes(c.block_m / 16, c.nr, c.waves, wgs);
@@ -701,6 +713,24 @@ w4a16_status moe_gemm_impl(const w4a16_weight_desc* desc, const void* packed_w, 
   p.grid_blocks = (int32_t)(r.capacity / r.block_m);
   if (c.split_k == 0) p.sk_partial = reinterpret_cast<float*>(ws + wl.counters + wl.slices + wl.combine);
   else attach_split(p, c, wl, ws);
+  // Tokens with exactly one local slot: the GEMM stores bf16(w * acc) as their
+  // output and the combine leaves them alone (the sum of one term), which
+  // saves their fp32 round trip at the cost of a small counting launch.
+  // Used where the partials are large (measured on MI355X, down + combine:
+  // EP8 prefill 360-373 -> 354 us, EP16 prefill 228 -> 219 us; EP8 decode
+  // 90 -> 93 us, so not there); skipped when every expert is local and
+  // top-k >= 2, where no token has one.
+  const bool direct = combine && !(r.first_expert == 0 && r.E_loc >= r.E_glob && r.topk >= 2) &&
+                      expected_partial_bytes(r.T, r.topk, r.E_glob, r.E_loc, desc->N) >= kDirectMinBytes;
+  uint8_t* token_local = combine ? reinterpret_cast<uint8_t*>(ws + wl.counters + wl.slices + wl.combine + wl.streamk)
+                                 : nullptr;
+  if (direct) {
+    e = w4a16::launch_token_local(r.topk_ids, r.T, r.topk, r.first_expert, r.E_loc, token_local, s);
+    if (e != hipSuccess) return hip_fail(e, "token count launch");
+    p.token_local = token_local;
+    p.topk = r.topk;
+    p.direct_ld = desc->N;
+  }
   // one pass per `cols` output columns (all of N without the combine): the
   // GEMM over that column range of the weights, then its combine
   const int64_t kc2 = (p.KC + 1) / 2;
@@ -712,6 +742,7 @@ w4a16_status moe_gemm_impl(const w4a16_weight_desc* desc, const void* packed_w, 
     q.N = nc;
     q.NT = nc / 16;
     q.n_tiles = n_tiles_of(nc, c.nr, c.waves);
+    if (direct) q.direct_out = out + n0;
     if (c.split_k == 0) {
       e = w4a16::launch_gemm_streamk(w4a16::kRouteIndexed, epi, c.block_m / 16, c.nr, c.waves, c.stages, q,
                                      resident_workgroups(c, epi), s);
@@ -720,7 +751,8 @@ w4a16_status moe_gemm_impl(const w4a16_weight_desc* desc, const void* packed_w, 
     }
     if (e != hipSuccess) return hip_fail(e, "moe_gemm launch");
     if (combine) {
-      e = w4a16::launch_combine(comb, r.topk_ids, r.T, r.topk, r.first_expert, r.E_loc, nc, out + n0, desc->N, s);
+      e = w4a16::launch_combine(comb, r.topk_ids, r.T, r.topk, r.first_expert, r.E_loc, nc, out + n0, desc->N,
+                                direct ? token_local : nullptr, s);
       if (e != hipSuccess) return hip_fail(e, "combine launch");
     }
   }
@@ -1068,7 +1100,7 @@ w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* pac
   if (e != hipSuccess) return hip_fail(e, "mxfp4_moe_gemm launch");
   if (combine) {
     e = w4a16::launch_combine(static_cast<const float*>(workspace), r.topk_ids, r.T, r.topk, r.first_expert,
-                              r.E_loc, desc->N, out, desc->N, s);
+                              r.E_loc, desc->N, out, desc->N, nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
   }
   return W4A16_OK;

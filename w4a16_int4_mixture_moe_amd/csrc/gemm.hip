@@ -409,9 +409,16 @@ __device__ __forceinline__ void epilogue_weighted_staged(const GemmParams& p, Ti
     const int i = idx / (BN / 4);
     const int c = 4 * (idx - i * (BN / 4));
     const int orow = sm.out[i];
-    if (orow < 0 || n0 + c >= p.N) continue;
-    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (int64_t)orow * p.N + n0 + c) =
-        *reinterpret_cast<const float4*>(tile + i * LD + c);
+    if (orow == -1 || n0 + c >= p.N) continue;
+    const float4 v = *reinterpret_cast<const float4*>(tile + i * LD + c);
+    if (orow < 0) {               // the token's only local slot: its combined output
+      uint2 o;
+      o.x = pack_bf16x2(v.x, v.y);
+      o.y = pack_bf16x2(v.z, v.w);
+      *reinterpret_cast<uint2*>(p.direct_out + (int64_t)(-orow - 2) * p.direct_ld + n0 + c) = o;
+      continue;
+    }
+    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (int64_t)orow * p.N + n0 + c) = v;
   }
 }
 
@@ -628,17 +635,21 @@ __global__ __launch_bounds__(NW * kWave) void streamk_fixup_kernel(const GemmPar
 // the partial rows of its local slots) is issued before the first add, so
 // the slots' latencies overlap instead of adding up; the sum still runs in
 // j order and skips non-local slots (an add of zero would turn -0 into +0).
+// token_local != nullptr: tokens with exactly one local slot were stored by
+// the GEMM and are left alone.
 template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partial,
                                                       const int32_t* __restrict__ topk_ids,
                                                       int32_t T, int32_t topk, int32_t first,
                                                       int32_t E_loc, int32_t N,
-                                                      uint16_t* __restrict__ out, int32_t ldo) {
+                                                      uint16_t* __restrict__ out, int32_t ldo,
+                                                      const uint8_t* __restrict__ token_local) {
   const int n8 = N / 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)T * n8) return;
   const int64_t t = idx / n8;
   const int n = (int)(idx - t * n8) * 8;
+  if (token_local != nullptr && token_local[t] == 1) return;
   float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   auto add = [&](const float4& u, const float4& v) {
     a[0] += u.x; a[1] += u.y; a[2] += u.z; a[3] += u.w;
@@ -694,16 +705,35 @@ hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t stream) {
 
 hipError_t launch_combine(const float* partial, const int32_t* topk_ids, int32_t T, int32_t topk,
                           int32_t first, int32_t E_loc, int32_t cols, uint16_t* out, int32_t ldo,
-                          hipStream_t stream) {
+                          const uint8_t* token_local, hipStream_t stream) {
   const int64_t threads = (int64_t)T * (cols / 8);
   if (threads == 0) return hipSuccess;
   const dim3 grid((unsigned)((threads + 255) / 256));
   if (topk <= 8)
     hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(256), 0, stream, partial, topk_ids, T, topk, first, E_loc, cols,
-                       out, ldo);
+                       out, ldo, token_local);
   else
     hipLaunchKernelGGL(combine_kernel<16>, grid, dim3(256), 0, stream, partial, topk_ids, T, topk, first, E_loc, cols,
-                       out, ldo);
+                       out, ldo, token_local);
+  return hipGetLastError();
+}
+
+// Local slots of each token (saturated at 255), one thread per token.
+__global__ __launch_bounds__(256) void token_local_kernel(const int32_t* __restrict__ topk_ids, int32_t T,
+                                                          int32_t topk, int32_t first, int32_t E_loc,
+                                                          uint8_t* __restrict__ cnt) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  int c = 0;
+  for (int j = 0; j < topk; ++j) c += (unsigned)(topk_ids[t * topk + j] - first) < (unsigned)E_loc;
+  cnt[t] = (uint8_t)min(c, 255);
+}
+
+hipError_t launch_token_local(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t first, int32_t E_loc,
+                              uint8_t* cnt, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(token_local_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, stream, topk_ids, T, topk,
+                     first, E_loc, cnt);
   return hipGetLastError();
 }
 

@@ -40,6 +40,14 @@ struct GemmParams {
   int32_t a_row_div;            // topk (rows per token), 1 (rows per slot), 0 (rows per sorted position)
   int32_t gated;                // packed tiles alternate gate / up (output columns remapped)
   const float* slot_weight;     // weighted epilogue: topk weights, one per slot
+  // weighted epilogue, optional (token_local != nullptr): local slots per
+  // token (saturated at 255); the rows of tokens with exactly one local slot
+  // are stored as bf16(w * acc) to direct_out[token * direct_ld + column]
+  // instead of as fp32 partials (their combine is that one term)
+  const uint8_t* token_local;
+  int32_t topk;
+  uint16_t* direct_out;
+  int32_t direct_ld;
   // contiguous
   const int32_t* m_indices;
   // masked
@@ -101,10 +109,14 @@ size_t split_slice_bytes(int m_tiles, int nr, int waves);
 hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t stream);
 
 // ---- combine of weighted per-slot partials (gemm.hip): partial [T*topk][cols]
-// fp32 -> out[t * ldo + c] bf16 for c < cols
+// fp32 -> out[t * ldo + c] bf16 for c < cols; token_local != nullptr: tokens
+// with exactly one local slot are skipped (the GEMM stored them)
 hipError_t launch_combine(const float* partial, const int32_t* topk_ids, int32_t T, int32_t topk,
                           int32_t first, int32_t E_loc, int32_t cols, uint16_t* out, int32_t ldo,
-                          hipStream_t stream);
+                          const uint8_t* token_local, hipStream_t stream);
+// local slots of each token: cnt[t] = min(#{j : first <= ids[t*topk + j] < first + E_loc}, 255)
+hipError_t launch_token_local(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t first, int32_t E_loc,
+                              uint8_t* cnt, hipStream_t stream);
 
 // ---- A4W4: MXFP4 activations x MXFP4 weights (mx.hip)
 // bf16 [rows][K] -> E2M1 codes [rows][K/2] (two per byte, low nibble first)

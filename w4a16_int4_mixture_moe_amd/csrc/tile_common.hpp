@@ -42,7 +42,14 @@ __device__ __forceinline__ int setup_rows(const GemmParams& p, int mb, Smem& sm)
       // or the sorted position itself (0: rows already in sorted order)
       sm.row[i] = v ? (p.a_row_div > 0 ? s / p.a_row_div : pos) : -1;
       sm.out[i] = v ? (EPI == kEpiSilu || EPI == kEpiSiluMx ? pos : s) : -1;
-      if constexpr (EPI == kEpiWeighted) sm.w[i] = v ? p.slot_weight[s] : 0.f;
+      if constexpr (EPI == kEpiWeighted) {
+        sm.w[i] = v ? p.slot_weight[s] : 0.f;
+        // a token with one local slot: out = -(token + 2), stored directly as bf16
+        if (v && p.token_local != nullptr) {
+          const int t = s / p.topk;
+          if (p.token_local[t] == 1) sm.out[i] = -(t + 2);
+        }
+      }
     }
   } else if constexpr (ROUTE == kRouteContiguous) {
     const int r0 = mb * BM;
@@ -140,8 +147,18 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const Smem& sm, in
       if (!((tmask >> t) & 1u)) continue;
       const int i = 16 * t + (lane & 15);
       const int orow = sm.out[i];
-      if (orow < 0) continue;
+      if (EPI == kEpiWeighted ? orow == -1 : orow < 0) continue;
       const f32x4_t v = acc[r][t];
+      if constexpr (EPI == kEpiWeighted) {
+        const float w = sm.w[i];
+        if (orow < 0) {            // the token's only local slot: its combined output
+          uint2 o;
+          o.x = pack_bf16x2(w * v[0], w * v[1]);
+          o.y = pack_bf16x2(w * v[2], w * v[3]);
+          *reinterpret_cast<uint2*>(p.direct_out + (int64_t)(-orow - 2) * p.direct_ld + n) = o;
+          continue;
+        }
+      }
       if constexpr (EPI == kEpiStore) {
         uint2 o;
         o.x = pack_bf16x2(v[0], v[1]);
