@@ -15,8 +15,12 @@
 // * 16 weight rows; each wave owns NR 16-row weight tiles and every token
 // tile of the block.  Per 128-wide K chunk:
 //   - activations: BM rows x 256 B staged global -> registers -> LDS
-//     (double buffered, rows padded to 272 B so the 16-byte operand reads
-//     of 16 different rows fall in different LDS banks);
+//     (double buffered, rows padded to 272 B; on gfx950 the operand reads
+//     of this layout are 2-way bank-conflicted, 8 LDS cycles per wave read
+//     against 4 for a conflict-free one, measured with
+//     SQ_LDS_BANK_CONFLICT; the kernels this template serves are bound by
+//     their weight stream, and the prefill tile, where the reads matter
+//     more, uses a conflict-free permutation of unpadded rows);
 //   - weights: one 16-byte load per lane per weight tile straight from HBM
 //     into registers (the packed layout is the operand layout) plus the
 //     lane's one bf16 scale, both requested two or three chunks ahead;
@@ -507,8 +511,8 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p
   }
   const bool split = S > 1 && tile < p.split_tiles;   // else slice 0 runs the whole K
   if (S > 1 && !split && s != 0) return;
-  const int mb = tile / p.n_tiles;
-  const int nt = tile - mb * p.n_tiles;
+  int mb, nt;
+  if (!block_of(p, tile, p.n_tiles, mb, nt)) return;
   const int expert = setup_rows<MT, NW, ROUTE, EPI>(p, mb, sm);
   if (expert < 0) return;
   __syncthreads();
@@ -799,23 +803,29 @@ bool gemm_config_supported(int route, int epilogue, int m_tiles, int nr, int wav
   return find_kernels(route, epilogue, m_tiles, nr, waves, stages).classic != nullptr;
 }
 
+// The N tiles of a block share an XCD (block_of) when K is not split and a
+// block has 2 .. kXcdGroupMaxTiles of them.
+int xcd_group_for(int split, int per_block) { return split <= 1 && per_block >= 2 && per_block <= kXcdGroupMaxTiles; }
+
 hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves, int stages,
                        const GemmParams& p, hipStream_t stream) {
   if (prefill_applies(route, epilogue, m_tiles, nr, waves, stages, p))
     return launch_gemm_prefill(route, epilogue, p, stream);
   const KernelSet k = find_kernels(route, epilogue, m_tiles, nr, waves, stages);
   if (k.classic == nullptr) return hipErrorInvalidValue;
-  // Consecutive workgroups (the N tiles of one block) go to different XCDs
-  // (round robin), so the L2 requests for a block's activation rows spread
-  // over all eight L2s.  (Keeping a block's N tiles on one XCD, which saves
-  // the repeated activation fetch, measured several times slower: all its
-  // workgroups then request the same lines from one L2 at once.)
-  const int64_t grid = (int64_t)p.grid_blocks * p.n_tiles * std::max(p.split, 1);
+  // Block-major order spreads a block's N tiles over the XCDs (round robin);
+  // blocks with few N tiles keep them on one XCD instead (block_of).
+  // Keeping many tiles of a block on one XCD measured several times slower:
+  // all its workgroups then request the same activation lines from one L2
+  // at once.
+  GemmParams q = p;
+  q.xcd_group = xcd_group_for(p.split, p.n_tiles);
+  const int64_t grid = grid_of(q, q.n_tiles) * std::max(q.split, 1);
   if (grid <= 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
-  if (p.split > 1 && (p.split > p.KC || (p.split_tiles > 0 && (!p.split_partial || !p.split_count))))
+  if (q.split > 1 && (q.split > q.KC || (q.split_tiles > 0 && (!q.split_partial || !q.split_count))))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k.classic, dim3((unsigned)grid), dim3(waves * kWave), 0, stream, p);
+  hipLaunchKernelGGL(k.classic, dim3((unsigned)grid), dim3(waves * kWave), 0, stream, q);
   return hipGetLastError();
 }
 

@@ -32,6 +32,7 @@ struct GemmParams {
   int32_t w_tiles;              // 16-row tiles per expert in packed_w / packed_s (>= NT: a call may
                                 // cover a column range, packed_w / packed_s then point at its first tile)
   int32_t n_tiles;              // workgroup tiles along N
+  int32_t xcd_group;            // 1: a block's N tiles run on one XCD (see block_of), else block-major
   // indexed
   const int32_t* sorted_ids;
   const int32_t* expert_ids;
@@ -73,6 +74,11 @@ struct GemmParams {
   float* split_partial;
   uint32_t* split_count;
 };
+
+// XCD-grouped block order (block_of in tile_common.hpp) for blocks with
+// 2 .. kXcdGroupMaxTiles N tiles (or N-tile groups) and K not split.
+constexpr int kXcdGroupMaxTiles = 4;
+int xcd_group_for(int split, int per_block);
 
 // m_tiles: 16-row token tiles per block (block_m / 16); nr: 16-row weight
 // tiles per wave; waves: waves per workgroup; stages: chunks of weights in

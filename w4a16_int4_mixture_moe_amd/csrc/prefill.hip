@@ -277,15 +277,17 @@ __device__ __forceinline__ void pf_run(const GemmParams& p, PfSmem& sm, int expe
 template <int ROUTE, int EPI, bool LOOP>
 __global__ __launch_bounds__(kPfNW * kWave, 2) void moe_gemm_prefill_kernel(const GemmParams p, int n_loop) {
   __shared__ __attribute__((aligned(16))) PfSmem sm;
-  // work item (routed block, N-tile group), block-major: consecutive
-  // workgroups (the N tiles of one block) go to different XCDs.  Measured
-  // against orders that keep a block's N tiles on one XCD (its activation
-  // rows then come from HBM once): all sixteen side by side there, 4.8x
-  // slower (one L2 serving the same lines to sixteen CUs at once); spread
-  // over time (N-tile-major), 1-8 % slower.
+  // work item (routed block, N-tile group), block-major (consecutive
+  // workgroups, the N tiles of one block, go to different XCDs) unless the
+  // block has few groups (block_of).  Measured against orders that keep a
+  // block's sixteen N tiles on one XCD (its activation rows then come from
+  // HBM once): all sixteen side by side there, 4.8x slower (one L2 serving
+  // the same lines to sixteen CUs at once); spread over time (N-tile-major),
+  // 1-8 % slower.
   const int groups = (p.n_tiles + n_loop - 1) / n_loop;
-  const int mb = blockIdx.x / groups;
-  const int nt0 = (blockIdx.x - mb * groups) * n_loop;
+  int mb, g;
+  if (!block_of(p, blockIdx.x, groups, mb, g)) return;
+  const int nt0 = g * n_loop;
   const int expert = setup_rows<kPfMT, kPfNW, ROUTE, EPI>(p, mb, sm);
   if (expert < 0) return;
   __syncthreads();
@@ -342,10 +344,13 @@ hipError_t launch_gemm_prefill(int route, int epilogue, const GemmParams& p, hip
   const int n_loop = prefill_n_loop(p);
   const PfKernel k = pick_prefill(route, epilogue, n_loop > 1);
   if (k == nullptr || p.K % kChunk) return hipErrorInvalidValue;
-  const int64_t grid = (int64_t)p.grid_blocks * ((p.n_tiles + n_loop - 1) / n_loop);
+  const int groups = (p.n_tiles + n_loop - 1) / n_loop;
+  GemmParams q = p;
+  q.xcd_group = xcd_group_for(1, groups);
+  const int64_t grid = grid_of(q, groups);
   if (grid <= 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kPfNW * kWave), 0, stream, p, n_loop);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kPfNW * kWave), 0, stream, q, n_loop);
   return hipGetLastError();
 }
 

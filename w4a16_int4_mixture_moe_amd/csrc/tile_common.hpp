@@ -22,6 +22,34 @@ __device__ __forceinline__ int live_blocks(const GemmParams& p) {
     return p.grid_blocks;
 }
 
+// Routed block mb and per-block item j (N tile, or group of N tiles) of work
+// item w, for `per` items per block.  Block-major by default: consecutive
+// items are one block's, and the hardware's round-robin dispatch sends
+// consecutive workgroups to different XCDs, so each XCD fetches the block's
+// activation rows into its own L2.  p.xcd_group: items of one block are 8
+// apart, i.e. on one XCD, which then fetches the rows once; w runs over
+// groups of 8 blocks x per items (the launcher rounds the grid up to whole
+// groups) and items past the last block return false.  Used for few items
+// per block only: many workgroups asking one L2 for the same lines at once
+// were measured several times slower.
+__device__ __forceinline__ bool block_of(const GemmParams& p, int w, int per, int& mb, int& j) {
+  if (!p.xcd_group) {
+    mb = w / per;
+    j = w - mb * per;
+    return true;
+  }
+  const int k = w >> 3;
+  const int grp = k / per;
+  j = k - grp * per;
+  mb = grp * 8 + (w & 7);
+  return mb < p.grid_blocks;
+}
+
+// Grid of a launch with `per` items per routed block (see block_of).
+inline int64_t grid_of(const GemmParams& p, int per) {
+  return p.xcd_group ? ((int64_t)p.grid_blocks + 7) / 8 * 8 * per : (int64_t)p.grid_blocks * per;
+}
+
 // Fill the block's row tables; returns the block's expert (wave-uniform) or
 // -1 when the block has no work.  The caller synchronises afterwards.
 template <int MT, int NW, int ROUTE, int EPI, typename Smem>
