@@ -99,14 +99,16 @@ def cfg_tag(cfg) -> str:
 
 def kernel_name(cfg, route: int, epi: int, K: int, mx: bool = False) -> str:
     """The GEMM kernel's name as the rocprofv3 kernel trace shows it (the
-    library runs the 128-row, 4-tiles-per-wave, unsplit configurations on its
-    prefill tile when K is a multiple of 128, in its N-tile-loop form for
-    K <= 256 on the grids measured here)."""
+    library runs the unsplit 128-row, 4-tiles-per-wave, 4-wave and 256-row,
+    2-tiles-per-wave, 8-wave configurations on its prefill tiles when K is a
+    multiple of 128, the first in its N-tile-loop form for K <= 256 on the
+    grids measured here)."""
     if mx:
         return f"mx_gemm_kernel<{cfg.block_m // 16}, {cfg.nr}, {cfg.waves}, {cfg.stages}, {epi}>"
-    if (cfg.block_m == 128 and cfg.nr == 4 and cfg.waves == 4 and cfg.stages == 2 and cfg.split_k <= 1
-            and K % 128 == 0):
-        return f"moe_gemm_prefill_kernel<{route}, {epi}, {'true' if K <= 256 else 'false'}>"
+    tile = (cfg.block_m, cfg.nr, cfg.waves)
+    if tile in ((128, 4, 4), (256, 2, 8)) and cfg.stages == 2 and cfg.split_k <= 1 and K % 128 == 0:
+        loop = "true" if K <= 256 and tile == (128, 4, 4) else "false"
+        return f"moe_gemm_prefill_kernel<{cfg.block_m // 16}, {cfg.nr}, {cfg.waves}, {route}, {epi}, {loop}>"
     return f"moe_gemm_kernel<{cfg.block_m // 16}, {cfg.nr}, {cfg.waves}, {cfg.stages}, {route}, {epi}>"
 
 
@@ -283,7 +285,7 @@ class IndexedStep:
             self.cfg2 = self.cfg1
         else:
             self.cfg1 = override(M.indexed_config(self.routing, self.p1))
-            self.cfg2 = override(M.indexed_config(self.routing, self.p2))
+            self.cfg2 = override(M.indexed_config(self.routing, self.p2, combine=True))
             self.cfg2.combine_cols = args.combine_cols
             if self.fused:
                 self.cfg1.split_k = 1
@@ -451,10 +453,14 @@ class GroupedStep:
         self.expected_m = max(1, int(round(float(self.mm.mean()))))
         self.cfg_c = M.select(self.rows_c, 1, 1, sh.E_loc, sh.N1, sh.K1, kind="contiguous")
         self.cfg_m = M.select(sh.max_m, 1, 1, sh.E_loc, sh.N1, sh.K1, kind="masked", expected_m=self.expected_m)
-        # --nr / --waves overrides: the calls then take the changed configs
-        self.explicit = bool(args is not None and (args.nr or args.waves))
+        # --block-m / --nr / --waves overrides: the calls then take the
+        # changed configs (block_m on the contiguous layout only where it
+        # divides the layout's 128-row segments)
+        self.explicit = bool(args is not None and (args.nr or args.waves or args.block_m))
         if self.explicit:
             for c in (self.cfg_c, self.cfg_m):
+                if args.block_m and (c is self.cfg_m or 128 % args.block_m == 0):
+                    c.block_m = args.block_m
                 c.nr = args.nr or c.nr
                 c.waves = args.waves or c.waves
         z = lambda n: torch.zeros(max(16, n), dtype=torch.uint8, device=dev)

@@ -58,7 +58,7 @@ typedef enum {
 const char* w4a16_last_error(void);
 
 /* ABI version of this header (W4A16_ABI_VERSION). */
-#define W4A16_ABI_VERSION 6
+#define W4A16_ABI_VERSION 7
 int32_t w4a16_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -150,7 +150,7 @@ w4a16_status w4a16_pack_w4(const uint8_t* codes, const uint16_t* scales,
  * [0, E_glob) are treated as not local.
  *
  * capacity = length of sorted_ids, >= w4a16_align_capacity(); expert_ids has
- * capacity / block_m entries.  block_m in {16, 32, 64, 128}.  E_loc <= 1024.
+ * capacity / block_m entries.  block_m in {16, 32, 64, 128, 256}.  E_loc <= 1024.
  * validate != 0 synchronises: topk_ids are copied to the host and checked
  * to lie in [0, E_glob) before anything is enqueued (ERR_ROUTING otherwise).
  * Errors: ERR_ARG, ERR_SHAPE, ERR_CAPACITY, ERR_ROUTING, ERR_HIP. */
@@ -179,7 +179,9 @@ w4a16_status w4a16_moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, i
 #define W4A16_ROUTE_MASKED 2      /* grouped, masked_m */
 
 typedef struct {
-  int32_t block_m;   /* rows per routed block: 16, 32, 64 or 128 */
+  int32_t block_m;   /* rows per tile: 16, 32, 64, 128 or 256.  Indexed
+                        calls: the routing's block_m or a divisor of it (a
+                        tile then covers part of a routed block) */
   int32_t nr;        /* 16-row weight tiles per wave: 2 or 4 */
   int32_t waves;     /* waves per workgroup: 4 (8 for some tiles) */
   int32_t split_k;   /* 1: one workgroup per (block, N tile), whole K;
@@ -213,11 +215,14 @@ typedef struct {
 
 /* The config w4a16_select gives for indexed routing aligned to block_m (the
  * routing buffers fix block_m; the rest is chosen as w4a16_select does):
- * what w4a16_moe_gemm uses when its cfg is NULL.  Host only; environment
- * overrides W4A16_NR, W4A16_WAVES, W4A16_SPLIT_K, W4A16_STAGES applied.
+ * what w4a16_moe_gemm (combine != 0: with topk_weights) and
+ * w4a16_moe_gate_up_silu (combine = 0) use when their cfg is NULL.  A 256-row
+ * routing gives the 256-row tile without the combine and 128-row tiles with
+ * it (or when K is not a multiple of 128).  Host only; environment overrides
+ * W4A16_NR, W4A16_WAVES, W4A16_SPLIT_K, W4A16_STAGES applied.
  * Errors: ERR_ARG. */
 w4a16_status w4a16_indexed_config(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N,
-                                  int32_t K, int32_t block_m, w4a16_config* out);
+                                  int32_t K, int32_t block_m, int32_t combine, w4a16_config* out);
 
 /* Choose a config (host only; memoised per argument set, so repeated calls
  * cost about a microsecond).
@@ -225,7 +230,11 @@ w4a16_status w4a16_indexed_config(int32_t T, int32_t topk, int32_t E_glob, int32
  *    E_loc are held here, projection [N, K]; expected_m ignored.
  *    tok_e = T * topk / E_glob.  Below 48 rows per expert block_m minimises
  *    the total block count over {16, 32, 64} on a seeded multinomial sample
- *    of the routing (ties to the smaller block); from 48 on, 128.  split_k
+ *    of the routing (ties to the smaller block); from 48 on, 128 (with K a
+ *    multiple of 128: the prefill tile, nr 4); from 128 on with K a
+ *    multiple of 128, 256 (the 256-row tile: nr 2, eight waves, split_k 1;
+ *    the call with the top-k combine then runs 128-row tiles on the same
+ *    routing, see w4a16_indexed_config).  split_k
  *    doubles from 1 while the sampled grid (routed blocks x N tiles x
  *    split_k) stays below one round of resident workgroups on 256 CUs and
  *    each slice keeps at least four 128-K chunks.
@@ -253,7 +262,7 @@ typedef struct {
   const int32_t* expert_ids;
   const int32_t* num_tokens_padded;  /* device scalar */
   int64_t capacity;                  /* length of sorted_ids */
-  int32_t block_m;                   /* must equal the config's block_m */
+  int32_t block_m;                   /* a multiple of the config's block_m */
   int32_t T, topk;                   /* sentinel is T * topk */
   const int32_t* topk_ids;           /* [T, topk]; read only by the combine */
   int32_t first_expert, E_loc;       /* local expert range; read only by the combine */
@@ -471,8 +480,8 @@ w4a16_status w4a16_mxfp4_quant_local_slots(const uint16_t* x, const int32_t* top
 
 /* Choose a config for the A4W4 GEMM (host only; arguments, memoisation and
  * environment overrides as w4a16_select): block_m as w4a16_select, except
- * that where it gives 128 and tokens per expert T * topk / E_glob are at
- * least 128, 64 (the MXFP4 kernel keeps more waves resident on 64-row
+ * that where it gives 128 or 256 and tokens per expert T * topk / E_glob are
+ * at least 128, 64 (the MXFP4 kernel keeps more waves resident on 64-row
  * blocks and measured faster there); nr 4, waves 4, one workgroup per
  * tile, stages 4 for block_m <= 32, else 2.  Errors: ERR_ARG. */
 w4a16_status w4a16_mxfp4_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc,
@@ -490,11 +499,13 @@ size_t w4a16_mxfp4_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, int32
  * per-slot bf16 rows (topk_weights NULL) or the top-k-weighted combine into
  * out[T, N] with fp32 partials summed in j order and rounded once.
  * Accumulation is fp32 (the MFMA's); each output is rounded once to bf16.
- *  cfg : NULL: block_m from the routing, nr 4, four waves, stages 4 for
- *        block_m <= 32 else 2; split_k must be 1.
+ *  cfg : NULL: block_m from the routing (64 on a 256-row routing), nr 4,
+ *        four waves, stages 4 for block_m <= 32 else 2; split_k must be 1.
+ *        A config's block_m divides the routing's.
  * Pointers: packed_w, packed_s, a_codes, out, workspace 16-byte aligned.
- * Errors: ERR_ARG, ERR_LAYOUT (not an MXFP4 weight, E_loc or block_m
- * mismatch), ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP. */
+ * Errors: ERR_ARG, ERR_LAYOUT (not an MXFP4 weight, E_loc mismatch, or a
+ * block_m that does not divide the routing's), ERR_SHAPE, ERR_UNSUPPORTED,
+ * ERR_WORKSPACE, ERR_HIP. */
 w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* packed_w, const void* packed_s,
                                   const uint8_t* a_codes, const uint8_t* a_scales, int64_t a_rows,
                                   int32_t a_layout, const w4a16_indexed_routing* routing,
@@ -510,11 +521,12 @@ w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* pac
  * slot: out_codes[p] ([capacity, I/2] bytes), out_scales[p] ([capacity,
  * I/32]).  Padding positions are left unwritten; the down projection reads
  * the rows with a_layout = W4A16_A_SORTED.
- *  cfg : NULL: block_m from the routing, nr 4, four waves; nr must be 4 and
- *        split_k 1.
+ *  cfg : NULL: block_m from the routing (64 on a 256-row routing), nr 4,
+ *        four waves; nr must be 4 and split_k 1, and block_m divide the
+ *        routing's.
  * Pointers: packed_w, packed_s, x_codes, out_codes 16-byte aligned.
- * Errors: ERR_ARG, ERR_LAYOUT (not an MXFP4 gate/up weight), ERR_SHAPE,
- * ERR_UNSUPPORTED, ERR_HIP. */
+ * Errors: ERR_ARG, ERR_LAYOUT (not an MXFP4 gate/up weight, or block_m not
+ * dividing the routing's), ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP. */
 w4a16_status w4a16_mxfp4_gate_up_silu(const w4a16_weight_desc* desc, const void* packed_w, const void* packed_s,
                                       const uint8_t* x_codes, const uint8_t* x_scales, int64_t x_rows,
                                       const w4a16_indexed_routing* routing, uint8_t* out_codes,

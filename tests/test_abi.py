@@ -82,11 +82,11 @@ def test_header_compiles_as_c_and_matches_the_binding(tmp_path):
             got[("const", "W4A16_A_SORTED")]) == (_lib.A_TOKEN, _lib.A_SLOT, _lib.A_SORTED)
     assert (got[("const", "W4A16_ROUTE_INDEXED")], got[("const", "W4A16_ROUTE_CONTIGUOUS")],
             got[("const", "W4A16_ROUTE_MASKED")]) == (_lib.ROUTE_INDEXED, _lib.ROUTE_CONTIGUOUS, _lib.ROUTE_MASKED)
-    assert got[("const", "W4A16_ABI_VERSION")] == 6
+    assert got[("const", "W4A16_ABI_VERSION")] == 7
 
 
 def test_version_and_desc(L):
-    assert L.w4a16_abi_version() == 6
+    assert L.w4a16_abi_version() == 7
     d = W.weight_desc(48, 4096, 7168)
     assert (d.K_pad, d.chunks, d.group) == (7168, 56, 32)
     assert d.w_bytes == 48 * 4096 * 7168 // 2
@@ -160,10 +160,33 @@ def test_capacity_and_workspace(L):
     assert _ws(d, r, True, W.config(32, 2, split_k=32)) == 0         # not a split count
     # cfg NULL: the selector's config for the routing's block_m
     c = _lib.Config()
-    assert L.w4a16_indexed_config(10, 8, 384, 4, 7168, 2048, 32, ctypes.byref(c)) == 0
+    assert L.w4a16_indexed_config(10, 8, 384, 4, 7168, 2048, 32, 1, ctypes.byref(c)) == 0
     assert (c.block_m, c.nr, c.waves, c.stages, c.kind) == (32, 2, 4, 2, 0)
     assert _ws(d, r, True) == _ws(d, r, True, c)
     assert c.combine_cols == 0
+
+
+def test_wide_tile_selection(L):
+    """From 128 routed rows per expert (K a multiple of 128) the selector
+    aligns the routing to 256 rows: the gate/up runs the 256-row tile (nr 2,
+    eight waves, unsplit), the down projection with the combine 128-row
+    tiles over the same routing, and a workspace sized for those tiles."""
+    ep8 = W.select(8192, 8, 384, 48, 4096, 7168)
+    assert (ep8.block_m, ep8.nr, ep8.waves, ep8.split_k) == (256, 2, 8, 1)
+    assert W.select(4096, 8, 384, 384, 512, 7168).block_m == 128        # 85 rows per expert
+    assert W.select(8192, 8, 384, 48, 4096, 7000).block_m == 128        # K not a multiple of 128
+    assert W.mxfp4_select(8192, 8, 384, 48, 4096, 7168).block_m == 64   # the A4W4 rule is unchanged
+    c = _lib.Config()
+    assert L.w4a16_indexed_config(8192, 8, 384, 48, 4096, 7168, 256, 0, ctypes.byref(c)) == 0
+    assert (c.block_m, c.nr, c.waves, c.split_k) == (256, 2, 8, 1)
+    assert L.w4a16_indexed_config(8192, 8, 384, 48, 7168, 2048, 256, 1, ctypes.byref(c)) == 0
+    assert (c.block_m, c.nr, c.waves) == (128, 4, 4)
+    assert L.w4a16_indexed_config(8192, 8, 384, 48, 7168, 2000, 256, 0, ctypes.byref(c)) == 0
+    assert c.block_m == 128                                             # K not a multiple of 128
+    d = W.weight_desc(48, 7168, 2048)
+    r = _routing(8192, 8, 48, 256)
+    assert _ws(d, r, True) == _ws(d, r, True, W.config(128, 4))
+    assert _ws(d, r, False) == 0
 
 
 def test_combine_passes_size_the_workspace(L):
@@ -215,7 +238,7 @@ def test_gemm_argument_errors(L, monkeypatch):
                                          kw.get("wsb", 0), None)
     assert call(a=P + 2) == -1                                           # misaligned activations
     assert call(rows=10) == -2                                           # too few activation rows
-    assert call(cfg=ctypes.byref(W.config(64, 2))) == -3                 # block_m disagrees with routing
+    assert call(cfg=ctypes.byref(W.config(64, 2))) == -3                 # block_m does not divide the routing's
     assert call(cfg=ctypes.byref(W.config(32, 3))) == -4                 # tile config not built
     assert call(w=P) == -8                                               # combine without workspace
     assert call(cfg=ctypes.byref(W.config(32, 2, split_k=3))) == -4     # not a split count
@@ -243,6 +266,7 @@ def test_gemm_argument_errors(L, monkeypatch):
                                                                 None, 0, None)
     assert gc(100) == -2
     assert gc(128, ctypes.byref(W.config(64, 2))) == -1                  # indexed config on a grouped call
+    assert gc(256, ctypes.byref(W.config(256, 2, 8, kind="contiguous"))) == -4   # 256-row blocks straddle 128-row segments
     assert gc(300032, None, W.weight_desc(8, 64, 7168)) == -2            # 300032 x 7168 x 2 B > 4 GiB
     # tuning overrides belong to indexed routing: grouped calls and grouped selection refuse them
     monkeypatch.setenv("W4A16_BLOCK_M", "64")
@@ -268,16 +292,16 @@ def test_gate_up_silu_argument_errors(L):
     assert call(plain, W.config(32, 2)) == -3                            # weight not gate/up packed
     assert call(gated, W.config(32, 2, split_k=0)) == -4                 # one workgroup per tile only
     assert call(gated, W.config(32, 2, split_k=2)) == -4
-    assert call(gated, W.config(16, 2)) == -3                            # block_m disagrees with routing
+    assert call(gated, W.config(64, 2)) == -3                            # block_m does not divide the routing's
     assert call(gated, W.config(32, 2, kind="masked")) == -1             # config of another kind
 
 
 def test_mxfp4_selector_halves_large_prefill_blocks(L):
-    """A4W4 takes 64-row blocks where the W4A16 rule gives 128 at >= 128 rows
-    per expert, keeps 128 below that, follows the W4A16 block_m elsewhere,
+    """A4W4 takes 64-row blocks where the W4A16 rule gives 128 or 256 at >= 128
+    rows per expert, keeps 128 below that, follows the W4A16 block_m elsewhere,
     and always uses one workgroup per tile with four weight tiles per wave."""
     pre = W.mxfp4_select(8192, 8, 384, 48, 4096, 7168)          # ~171 rows/expert
-    assert W.select(8192, 8, 384, 48, 4096, 7168).block_m == 128
+    assert W.select(8192, 8, 384, 48, 4096, 7168).block_m == 256
     assert (pre.block_m, pre.nr, pre.waves, pre.split_k, pre.stages) == (64, 4, 4, 1, 2)
     tp = W.mxfp4_select(4096, 8, 384, 384, 512, 7168)           # ~85 rows/expert
     assert W.select(4096, 8, 384, 384, 512, 7168).block_m == 128 and tp.block_m == 128
@@ -295,8 +319,11 @@ def test_selector_follows_tokens_per_expert(L):
     one = W.select(16, 8, 384, 384, 512, 7168)             # ~0.3 rows/expert
     assert one.block_m == 16
     pre = W.select(8192, 8, 384, 48, 4096, 7168)           # ~171 rows/expert
-    assert pre.block_m == 128 and pre.nr == 4                  # the prefill tile (K % 128 == 0)
-    assert W.select(8192, 8, 384, 48, 4096, 7200).nr == 2     # ragged K: the general kernel
+    assert pre.block_m == 256 and pre.nr == 2 and pre.waves == 8   # the 256-row tile (K % 128 == 0)
+    mid = W.select(4096, 8, 384, 48, 4096, 7168)           # ~85 rows/expert
+    assert mid.block_m == 128 and mid.nr == 4                  # the 128-row prefill tile
+    ragged = W.select(8192, 8, 384, 48, 4096, 7200)           # ragged K: the general kernel
+    assert ragged.block_m == 128 and ragged.nr == 2
     # tok_e, not total tokens: same T, 8x more experts -> decode side
     assert W.select(8192, 8, 3072, 48, 4096, 7168).block_m < 128
     assert W.select(576, 8, 384, 48, 4096, 7168).block_m == dec.block_m   # memoised, stable
@@ -366,7 +393,7 @@ def test_mxfp4_descriptor_and_errors(L):
     assert call(rows=10) == -2                                           # too few rows
     assert call(c=W.mxfp4_config(32, 3)) == -4                           # not built
     assert call(c=W.config(32, 4, split_k=0, stages=4)) == -4            # one workgroup per tile
-    assert call(c=W.mxfp4_config(64, 4)) == -3                           # block_m disagrees with routing
+    assert call(c=W.mxfp4_config(64, 4)) == -3                           # block_m does not divide the routing's
     assert call(w=P) == -8                                               # combine without workspace
     assert L.w4a16_mxfp4_moe_gemm_workspace_bytes(ctypes.byref(mx), 10, 8, 1) == 10 * 8 * 64 * 4
     assert L.w4a16_mxfp4_quant(P, 4, 48, P, P, None) == -2               # K % 32
@@ -392,6 +419,6 @@ def test_mxfp4_gate_up_silu_errors(L):
     assert call(plain, W.mxfp4_config(32, 4)) == -3                      # not a gate/up MXFP4 weight
     assert call(W.weight_desc(8, 128, 256, gate_up=True), W.mxfp4_config(32, 4)) == -3   # INT4 weight
     assert call(gated, W.mxfp4_config(32, 2)) == -4                      # nr must be 4
-    assert call(gated, W.mxfp4_config(64, 4)) == -3                      # block_m disagrees with routing
+    assert call(gated, W.mxfp4_config(64, 4)) == -3                      # block_m does not divide the routing's
     # the INT4 calls reject the combined flags too
     assert L.w4a16_pack_w4(P, P, ctypes.byref(gated), P, P, None) == -3

@@ -37,7 +37,7 @@ def test_align_bit_exact_small_random():
     n = 0
     for T, k, E_glob in [(1, 1, 1), (3, 2, 5), (37, 3, 11), (64, 2, 8), (200, 8, 64), (513, 6, 7)]:
         for (first, E_loc), bm in itertools.product([(0, E_glob), (E_glob // 3, max(1, E_glob // 2))],
-                                                    (16, 32, 64, 128)):
+                                                    (16, 32, 64, 128, 256)):
             topk = rng.integers(0, E_glob, (T, k)).astype(np.int32)
             _align_case(topk, E_glob, first, E_loc, bm)
             n += 1
@@ -561,7 +561,9 @@ def test_prefill_tile_bit_identical_to_the_general_kernel(K1, K2):
     tiles, so their bits agree, for every chunk count modulo four (the tile's
     main loop takes four chunks a step), every active-tile count (skewed
     routing), a ragged last N tile, and every epilogue and row source; both
-    within tolerance of the oracle."""
+    within tolerance of the oracle.  So does the 256-row tile (nr 2, eight
+    waves) on a 256-row routing, and so do 128- and 64-row tiles over that
+    routing."""
     sh = W.MoEShape(name="prefill_tile", E_glob=12, E_loc=6, first=3, topk=4, T=400, K1=K1, N1=512,
                     K2=K2, N2=272, zipf_s=1.0, seed=4242)
     P = Problem(sh).upload()
@@ -579,9 +581,34 @@ def test_prefill_tile_bit_identical_to_the_general_kernel(K1, K2):
         out[name] = (bits(h), bits(y))
         if name == "prefill":
             _check_indexed(P, h, y, f"prefill tile check K1={K1} K2={K2}")
-    for name in ("prefill",):
+    # the 256-row tile (block_m 256, nr 2, eight waves) on its own routing
+    r256 = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, 256)
+    wide = M.config(256, 2, 8)
+    out["wide"] = (bits(M.moe_w4a16_gemm(P.d_x, P.p1, r256, cfg=wide)),
+                   bits(M.moe_w4a16_gemm(P.d_a, P.p2, r256, topk_weights=P.d_w, cfg=wide)))
+    for name in ("prefill", "wide"):
         np.testing.assert_array_equal(out[name][0], out["general"][0], err_msg=f"gate/up: {name} vs general kernel")
         np.testing.assert_array_equal(out[name][1], out["general"][1], err_msg=f"down+combine: {name} vs general kernel")
+    # tiles of 128 and 64 rows over the 256-row routing (a tile looks its
+    # expert up from the routed block it falls in; a tile of padding only
+    # exits), as the down + combine runs after a 256-row gate/up
+    for c in (M.config(128, 4), M.config(128, 2), M.config(64, 2)):
+        tag = f"bm{c.block_m} nr{c.nr}"
+        y = bits(M.moe_w4a16_gemm(P.d_a, P.p2, r256, topk_weights=P.d_w, cfg=c))
+        np.testing.assert_array_equal(y, out["general"][1], err_msg=f"down+combine on the 256-row routing, {tag}")
+        h = bits(M.moe_w4a16_gemm(P.d_x, P.p1, r256, cfg=c))
+        np.testing.assert_array_equal(h, out["general"][0], err_msg=f"gate/up on the 256-row routing, {tag}")
+    # the calls' own choice (cfg None: the 256-row tile for the gate/up,
+    # 128-row tiles, K-split on this small grid, for the down), K slices and
+    # stream-K over the 256-row routing: within the oracle's tolerance
+    h = M.moe_w4a16_gemm(P.d_x, P.p1, r256)
+    np.testing.assert_array_equal(bits(h), out["general"][0], err_msg="gate/up on the 256-row routing, cfg None")
+    _check_indexed(P, h, M.moe_w4a16_gemm(P.d_a, P.p2, r256, topk_weights=P.d_w),
+                   f"256-row routing, cfg None, K1={K1} K2={K2}")
+    for c in ((M.config(64, 2, split_k=2),) if K2 >= 256 else ()) + (M.config(128, 2, split_k=0),):
+        _check_indexed(P, M.moe_w4a16_gemm(P.d_x, P.p1, r256, cfg=c),
+                       M.moe_w4a16_gemm(P.d_a, P.p2, r256, topk_weights=P.d_w, cfg=c),
+                       f"256-row routing bm{c.block_m} split_k={c.split_k} K1={K1} K2={K2}")
     # fused SiLU epilogue on the interleaved gate/up weight
     p1g = M.pack_w4(to_dev(P.c1), to_dev_bf16(P.s1), gate_up=True)
     inter = {name: bits(M.moe_gate_up_silu(P.d_x, p1g, r, cfg=M.config(128, nr, waves)))
@@ -589,6 +616,16 @@ def test_prefill_tile_bit_identical_to_the_general_kernel(K1, K2):
     valid = r.sorted_ids.cpu().numpy() < sh.T * sh.topk
     for name in ("prefill",):
         np.testing.assert_array_equal(inter[name][valid], inter["general"][valid], err_msg=f"fused SiLU: {name}")
+    # fused SiLU on the 256-row routing (the 256-row tile, and 128-row tiles):
+    # rows in that routing's sorted order, compared per slot
+    s128, s256 = r.sorted_ids.cpu().numpy(), r256.sorted_ids.cpu().numpy()
+    v256 = s256 < sh.T * sh.topk
+    for c in (wide, M.config(128, 4), None):
+        iw = bits(M.moe_gate_up_silu(P.d_x, p1g, r256, cfg=c))
+        by_slot = np.zeros((sh.T * sh.topk, iw.shape[1]), iw.dtype)
+        by_slot[s256[v256]] = iw[v256]
+        np.testing.assert_array_equal(by_slot[s128[valid]], inter["general"][valid],
+                                      err_msg=f"fused SiLU on the 256-row routing, {c}")
     # grouped row sources
     A, mi, _ = W.contiguous_layout(P.topk_ids, P.x, sh.first, sh.E_loc, pad=128, pad_fill=0x7FC0)
     oc = {name: bits(M.grouped_contiguous(to_dev_bf16(A), P.p1, to_dev(mi),
@@ -601,8 +638,10 @@ def test_prefill_tile_bit_identical_to_the_general_kernel(K1, K2):
                                       cfg=M.config(128, nr, waves, kind="masked")))
           for name, (nr, waves) in tiles.items()}
     refm, vm = O.grouped_masked(A3, P.c1, P.s1, mm)
+    om["wide"] = bits(M.grouped_masked(to_dev_bf16(A3), P.p1, to_dev(mm), 100, cfg=M.config(256, 2, 8, kind="masked")))
     for name in ("prefill",):
         np.testing.assert_array_equal(oc[name][ok], oc["general"][ok], err_msg=f"contiguous: {name}")
+    for name in ("prefill", "wide"):
         np.testing.assert_array_equal(om[name][vm], om["general"][vm], err_msg=f"masked: {name}")
     assert_close(oc["prefill"][vr], ref[vr], "contiguous prefill tile")
     assert_close(om["prefill"][vm], refm[vm], "masked prefill tile")

@@ -115,7 +115,7 @@ w4a16_status check_mx_desc(const w4a16_weight_desc* d) {
   return W4A16_OK;
 }
 
-bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
 
 // ---------------------------------------------------------------- selection
 //
@@ -142,6 +142,15 @@ bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm =
 // tile from its register use), so the choice is deterministic and available
 // without a device.
 constexpr double kPrefillTokE = 48.0;
+// Routed rows per expert from which the routing takes 256-row blocks: the
+// gate/up runs the 256-row prefill tile (an expert of up to 256 rows streams
+// its weights once), the down projection + combine 128-row tiles over the
+// same routing.  Measured on MI355X at 171 rows per expert (T = 8192, top-8
+// of 384, Zipf-skewed), against 128-row blocks: gate/up EP8 595 -> 544 us,
+// EP16 384 -> 356 us, EP32 180 -> 144 us; the down + combine on the 256-row
+// tile was 5-7 % slower than on the 128-row one, and grouped masked calls
+// (up to 512 rows per group) 20 % slower, so neither takes it.
+constexpr double kWideTokE = 128.0;
 // A4W4: above this many rows per expert the MXFP4 GEMM takes 64-row blocks
 // where the W4A16 rule gives 128 (measured on MI355X, step time: EP8 / EP16
 // prefill shares 5 % / 9 % faster at 64; at 85 rows per expert, TP8 T = 4096,
@@ -168,8 +177,9 @@ int64_t sampled_blocks(const std::vector<int>& counts, int bm) {
 
 // Resident workgroups per CU of the one-workgroup-per-tile kernel with this
 // tile (four waves; register use of the gfx950 build: 16- and 32-row blocks
-// fit four workgroups per CU, 64-row blocks three, 128-row blocks two).
-int resident_per_cu(int block_m) { return block_m <= 32 ? 4 : block_m == 64 ? 3 : 2; }
+// fit four workgroups per CU, 64-row blocks three, 128-row blocks two; the
+// eight-wave 256-row tile one).
+int resident_per_cu(int block_m) { return block_m <= 32 ? 4 : block_m == 64 ? 3 : block_m == 128 ? 2 : 1; }
 
 int n_tiles_of(int N, int nr, int waves) {
   const int tiles_per_wg = nr * waves;
@@ -198,10 +208,11 @@ std::vector<int> sampled_counts(int32_t T, int32_t topk, int32_t E_glob, int32_t
   return counts;
 }
 
-// Indexed config; block_m chosen by the tok_e rule, or forced (> 0) when the
-// routing buffers already fix it.
+// Indexed config; block_m chosen by the tok_e rule, or, when the routing
+// buffers already fix their block_m (force_block_m > 0), that block_m or
+// (256-row routing under a top-k combine) the 128-row tile.
 w4a16_config select_indexed(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N, int32_t K,
-                            int32_t force_block_m) {
+                            int32_t force_block_m, bool combine) {
   w4a16_config c{};
   c.kind = W4A16_ROUTE_INDEXED;
   c.waves = 4;
@@ -211,6 +222,9 @@ w4a16_config select_indexed(int32_t T, int32_t topk, int32_t E_glob, int32_t E_l
   const std::vector<int> counts = sampled_counts(T, topk, E_glob, E_loc);
   if (force_block_m > 0) {
     c.block_m = force_block_m;
+    if (c.block_m == 256 && (combine || K % 128)) c.block_m = 128;
+  } else if (tok_e >= kWideTokE && K % 128 == 0) {
+    c.block_m = 256;
   } else if (tok_e >= kPrefillTokE) {
     c.block_m = 128;
   } else {
@@ -229,6 +243,13 @@ w4a16_config select_indexed(int32_t T, int32_t topk, int32_t E_glob, int32_t E_l
   // per wave: EP8 prefill gate/up 629 -> 604 us, down 413 -> 401 us, TP8
   // T = 4096 gate/up 378 -> 362 us, down 637 -> 616 us, bit-identical outputs
   if (c.block_m == 128 && K % 128 == 0) c.nr = 4;
+  // 256-row blocks (only when the routing fixes them): the wide prefill tile,
+  // two weight tiles per wave over eight waves, unsplit
+  if (c.block_m == 256) {
+    c.waves = 8;
+    c.split_k = 1;
+    return c;
+  }
   const int64_t tiles = sampled_blocks(counts, c.block_m) * n_tiles_of(N, c.nr, c.waves);
   c.split_k = choose_split(tiles, c.block_m, K);
   return c;
@@ -304,7 +325,7 @@ w4a16_status check_config(const w4a16_config& c, int route, int epi, int K) {
   if (c.kind != route)
     return fail(W4A16_ERR_ARG, "config was chosen for routing kind %d, this call is kind %d (%s)", c.kind, route,
                 route == W4A16_ROUTE_INDEXED ? "indexed" : "grouped calls choose their own tiles");
-  if (!valid_block_m(c.block_m)) return fail(W4A16_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128}", c.block_m);
+  if (!valid_block_m(c.block_m)) return fail(W4A16_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128, 256}", c.block_m);
   if (c.combine_cols < 0 || c.combine_cols % 16)
     return fail(W4A16_ERR_ARG, "combine_cols %d: 0 (the library's choice) or a positive multiple of 16",
                 c.combine_cols);
@@ -419,10 +440,10 @@ void attach_split(w4a16::GemmParams& p, const w4a16_config& c, const Workspace& 
 // Upper bound of the routed blocks of an indexed call: every local expert with
 // rows adds at most one partial block, and there are at most T * topk local
 // slots (so at most that many experts with rows).
-int64_t indexed_block_bound(const w4a16_indexed_routing& r) {
+int64_t indexed_block_bound(const w4a16_indexed_routing& r, int32_t block_m) {
   const int64_t slots = (int64_t)r.T * r.topk;
-  return std::min<int64_t>(r.capacity / std::max(r.block_m, 1),
-                           (slots + r.block_m - 1) / r.block_m + std::min<int64_t>(r.E_loc, slots));
+  return std::min<int64_t>(r.capacity / std::max(block_m, 1),
+                           (slots + block_m - 1) / block_m + std::min<int64_t>(r.E_loc, slots));
 }
 
 // Workgroups of this config the current device keeps resident (stream-K
@@ -433,8 +454,9 @@ int resident_workgroups(const w4a16_config& c, int epi) {
 
 // select_indexed, memoised per argument set (no environment overrides)
 w4a16_config cached_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N, int32_t K,
-                           int32_t kind, int32_t expected_m, int32_t force_block_m) {
-  const SelectKey key = std::make_tuple(T, topk, E_glob, E_loc, N, K, kind * 1024 + force_block_m, expected_m);
+                           int32_t kind, int32_t expected_m, int32_t force_block_m, bool combine = false) {
+  const SelectKey key =
+      std::make_tuple(T, topk, E_glob, E_loc, N, K, kind * 1024 + (combine ? 512 : 0) + force_block_m, expected_m);
   {
     std::lock_guard<std::mutex> g(g_cache_mu);
     auto it = g_cache.find(key);
@@ -446,7 +468,7 @@ w4a16_config cached_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_lo
   else if (kind == W4A16_ROUTE_MASKED)
     c = select_masked(T, E_loc, N, K, expected_m);
   else
-    c = select_indexed(T, topk, E_glob, E_loc, N, K, force_block_m);
+    c = select_indexed(T, topk, E_glob, E_loc, N, K, force_block_m, combine);
   std::lock_guard<std::mutex> g(g_cache_mu);
   g_cache[key] = c;
   return c;
@@ -517,7 +539,7 @@ w4a16_status w4a16_moe_align(const int32_t* topk_ids, int32_t T, int32_t topk, i
   if ((int64_t)first_expert + E_loc > E_glob)
     return fail(W4A16_ERR_ARG, "local experts [%d, %d) exceed E_glob=%d", first_expert, first_expert + E_loc, E_glob);
   if (E_loc > 1024) return fail(W4A16_ERR_SHAPE, "E_loc=%d > 1024 not supported", E_loc);
-  if (!valid_block_m(block_m)) return fail(W4A16_ERR_SHAPE, "block_m %d not in {16, 32, 64, 128}", block_m);
+  if (!valid_block_m(block_m)) return fail(W4A16_ERR_SHAPE, "block_m %d not in {16, 32, 64, 128, 256}", block_m);
   if ((int64_t)T * topk >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "T*topk too large");
   const int64_t need = w4a16_align_capacity(T, topk, E_loc, block_m);
   if (capacity < need || capacity % block_m)
@@ -546,15 +568,35 @@ namespace {
 // The indexed config of a call: cfg, or the selector's choice for the
 // routing's shape and block_m with environment overrides applied.
 w4a16_status indexed_call_config(const w4a16_indexed_routing& r, const w4a16_weight_desc* d, const w4a16_config* cfg,
-                                 w4a16_config* out) {
+                                 bool combine, w4a16_config* out) {
   if (cfg) {
     *out = *cfg;
     return W4A16_OK;
   }
   if (r.E_glob <= 0) return fail(W4A16_ERR_ARG, "routing.E_glob must be positive (it steers the config when cfg is NULL)");
-  *out = cached_select(r.T, r.topk, r.E_glob, r.E_loc, d->N, d->K, W4A16_ROUTE_INDEXED, 0, r.block_m);
+  *out = cached_select(r.T, r.topk, r.E_glob, r.E_loc, d->N, d->K, W4A16_ROUTE_INDEXED, 0, r.block_m, combine);
   apply_env_overrides(out, false);
   return W4A16_OK;
+}
+
+// An indexed call's tile rows: the routing's block_m or a divisor of it (a
+// 256-row routing also serves 128-row tiles; the tiles then look their
+// expert up as expert_ids[tile >> shift]).
+w4a16_status check_tile_rows(const w4a16_config& c, const w4a16_indexed_routing& r) {
+  if (c.block_m > r.block_m || r.block_m % c.block_m)
+    return fail(W4A16_ERR_LAYOUT, "config block_m=%d does not divide the routing's block_m=%d", c.block_m, r.block_m);
+  return W4A16_OK;
+}
+
+// The A4W4 calls' tile rows when cfg is NULL: the routing's block_m, except
+// that a 256-row routing (which the W4A16 selector gives from 128 rows per
+// expert) takes 64-row tiles, the A4W4 choice at those token counts.
+int32_t mx_tile_rows(const w4a16_indexed_routing& r) { return r.block_m == 256 ? 64 : r.block_m; }
+
+int32_t tile_shift(const w4a16_config& c, const w4a16_indexed_routing& r) {
+  int32_t s = 0;
+  while ((c.block_m << s) < r.block_m) ++s;
+  return s;
 }
 
 // Checks shared by the indexed W4A16 calls; fills the activation rows the
@@ -573,7 +615,7 @@ w4a16_status check_indexed_call(const w4a16_weight_desc* desc, const void* packe
     return fail(W4A16_ERR_ARG, "packed weights, activations and output must be 16-byte aligned");
   if (r.E_loc != desc->E)
     return fail(W4A16_ERR_LAYOUT, "routing has E_loc=%d but the packed weight holds %d experts", r.E_loc, desc->E);
-  if (!valid_block_m(r.block_m)) return fail(W4A16_ERR_ARG, "routing.block_m %d not in {16, 32, 64, 128}", r.block_m);
+  if (!valid_block_m(r.block_m)) return fail(W4A16_ERR_ARG, "routing.block_m %d not in {16, 32, 64, 128, 256}", r.block_m);
   if ((int64_t)r.T * r.topk >= INT32_MAX / 2) return fail(W4A16_ERR_SHAPE, "T*topk too large");
   if (r.capacity % r.block_m) return fail(W4A16_ERR_CAPACITY, "capacity not a multiple of block_m");
   if (r.capacity / r.block_m > INT32_MAX / 2) return fail(W4A16_ERR_CAPACITY, "capacity too large");
@@ -585,12 +627,12 @@ w4a16_status check_indexed_call(const w4a16_weight_desc* desc, const void* packe
 extern "C" {
 
 w4a16_status w4a16_indexed_config(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N, int32_t K,
-                                  int32_t block_m, w4a16_config* out) {
+                                  int32_t block_m, int32_t combine, w4a16_config* out) {
   if (!out) return fail(W4A16_ERR_ARG, "out is NULL");
-  if (!valid_block_m(block_m)) return fail(W4A16_ERR_ARG, "block_m %d not in {16, 32, 64, 128}", block_m);
+  if (!valid_block_m(block_m)) return fail(W4A16_ERR_ARG, "block_m %d not in {16, 32, 64, 128, 256}", block_m);
   if (T < 0 || topk <= 0 || E_glob <= 0 || E_loc <= 0 || N <= 0 || K <= 0)
     return fail(W4A16_ERR_ARG, "bad sizes for indexed_config");
-  *out = cached_select(T, topk, E_glob, E_loc, N, K, W4A16_ROUTE_INDEXED, 0, block_m);
+  *out = cached_select(T, topk, E_glob, E_loc, N, K, W4A16_ROUTE_INDEXED, 0, block_m, combine != 0);
   apply_env_overrides(out, false);
   return W4A16_OK;
 }
@@ -621,7 +663,7 @@ w4a16_status w4a16_mxfp4_select(int32_t T, int32_t topk, int32_t E_glob, int32_t
     return fail(W4A16_ERR_ARG, "bad sizes for select");
   w4a16_config c = cached_select(T, topk, E_glob, E_loc, N, K, W4A16_ROUTE_INDEXED, 0, 0);
   const double tok_e = (double)T * topk / E_glob;
-  if (c.block_m == 128 && tok_e >= kMxHalfTileTokE) c.block_m = 64;
+  if (c.block_m >= 128 && tok_e >= kMxHalfTileTokE) c.block_m = 64;
   c.nr = 4;
   c.waves = 4;
   c.split_k = 1;
@@ -637,10 +679,10 @@ size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, const w4a16
   const w4a16_indexed_routing& r = *routing;
   if (r.T < 0 || r.topk <= 0 || r.E_loc <= 0 || !valid_block_m(r.block_m) || r.capacity < 0) return 0;
   w4a16_config c{};
-  if (indexed_call_config(r, desc, cfg, &c) != W4A16_OK) return 0;
+  if (indexed_call_config(r, desc, cfg, combine != 0, &c) != W4A16_OK) return 0;
   const int epi = combine ? w4a16::kEpiWeighted : w4a16::kEpiStore;
   if (check_config(c, W4A16_ROUTE_INDEXED, epi, desc->K) != W4A16_OK) return 0;
-  const int64_t tiles = indexed_block_bound(r) * n_tiles_of(desc->N, c.nr, c.waves);
+  const int64_t tiles = indexed_block_bound(r, c.block_m) * n_tiles_of(desc->N, c.nr, c.waves);
   const int32_t cols = combine_cols_of(c, desc->N, r.T, r.topk, r.E_glob, r.E_loc);
   return workspace_layout(c, epi, tiles, cols, r.T, r.topk, combine != 0).total();
 }
@@ -675,14 +717,14 @@ w4a16_status moe_gemm_impl(const w4a16_weight_desc* desc, const void* packed_w, 
   if (st != W4A16_OK) return st;
   const int epi = combine ? w4a16::kEpiWeighted : w4a16::kEpiStore;
   w4a16_config c{};
-  st = indexed_call_config(r, desc, cfg, &c);
+  st = indexed_call_config(r, desc, cfg, combine, &c);
   if (st != W4A16_OK) return st;
   st = check_config(c, W4A16_ROUTE_INDEXED, epi, desc->K);
   if (st != W4A16_OK) return st;
-  if (c.block_m != r.block_m)
-    return fail(W4A16_ERR_LAYOUT, "config block_m=%d differs from the routing's block_m=%d", c.block_m, r.block_m);
+  st = check_tile_rows(c, r);
+  if (st != W4A16_OK) return st;
   if (combine && !r.topk_ids) return fail(W4A16_ERR_ARG, "combine needs routing.topk_ids");
-  const int64_t tiles = indexed_block_bound(r) * n_tiles_of(desc->N, c.nr, c.waves);
+  const int64_t tiles = indexed_block_bound(r, c.block_m) * n_tiles_of(desc->N, c.nr, c.waves);
   const int32_t cols = combine ? combine_cols_of(c, desc->N, r.T, r.topk, r.E_glob, r.E_loc) : desc->N;
   const Workspace wl = workspace_layout(c, epi, tiles, cols, r.T, r.topk, combine);
   if (c.split_k == 0 && wl.streamk == 0)
@@ -710,7 +752,8 @@ w4a16_status moe_gemm_impl(const w4a16_weight_desc* desc, const void* packed_w, 
   p.sentinel = r.T * r.topk;
   p.a_row_div = a_layout == W4A16_A_TOKEN ? r.topk : a_layout == W4A16_A_SLOT ? 1 : 0;
   p.slot_weight = topk_weights;
-  p.grid_blocks = (int32_t)(r.capacity / r.block_m);
+  p.expert_shift = tile_shift(c, r);
+  p.grid_blocks = (int32_t)(r.capacity / c.block_m);
   if (c.split_k == 0) p.sk_partial = reinterpret_cast<float*>(ws + wl.counters + wl.slices + wl.combine);
   else attach_split(p, c, wl, ws);
   // Tokens with exactly one local slot: the GEMM stores bf16(w * acc) as their
@@ -824,15 +867,15 @@ w4a16_status w4a16_moe_gate_up_silu(const w4a16_weight_desc* desc, const void* p
   st = check_offset_range(r.T, desc->K, "activations");
   if (st != W4A16_OK) return st;
   w4a16_config c{};
-  st = indexed_call_config(r, desc, cfg, &c);
+  st = indexed_call_config(r, desc, cfg, false, &c);
   if (st != W4A16_OK) return st;
   if (!cfg) c.split_k = 1;  // the fused epilogue runs whole tiles
   if (c.split_k != 1) return fail(W4A16_ERR_UNSUPPORTED, "the fused SiLU gate/up call runs one workgroup per tile (split_k = 1)");
   if (c.nr % 2) return fail(W4A16_ERR_UNSUPPORTED, "the fused SiLU gate/up call needs an even nr (gate and up tiles in pairs)");
   st = check_config(c, W4A16_ROUTE_INDEXED, w4a16::kEpiSilu, desc->K);
   if (st != W4A16_OK) return st;
-  if (c.block_m != r.block_m)
-    return fail(W4A16_ERR_LAYOUT, "config block_m=%d differs from the routing's block_m=%d", c.block_m, r.block_m);
+  st = check_tile_rows(c, r);
+  if (st != W4A16_OK) return st;
   if (r.T == 0) return W4A16_OK;
   w4a16::GemmParams p = base_params(desc, packed_w, packed_s, x, out, c.nr, c.waves);
   p.sorted_ids = r.sorted_ids;
@@ -840,7 +883,8 @@ w4a16_status w4a16_moe_gate_up_silu(const w4a16_weight_desc* desc, const void* p
   p.num_tokens_padded = r.num_tokens_padded;
   p.sentinel = r.T * r.topk;
   p.a_row_div = r.topk;
-  p.grid_blocks = (int32_t)(r.capacity / r.block_m);
+  p.expert_shift = tile_shift(c, r);
+  p.grid_blocks = (int32_t)(r.capacity / c.block_m);
   hipError_t e = w4a16::launch_gemm(w4a16::kRouteIndexed, w4a16::kEpiSilu, c.block_m / 16, c.nr, c.waves,
                                     c.stages, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gate_up_silu launch");
@@ -1062,22 +1106,22 @@ w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* pac
   if (cfg) {
     c = *cfg;
   } else {
-    c.block_m = r.block_m;            // the routing buffers fix block_m
+    c.block_m = mx_tile_rows(r);      // the routing buffers fix block_m
     c.nr = 4;
     c.waves = 4;
     c.split_k = 1;
-    c.stages = r.block_m <= 32 ? 4 : 2;
+    c.stages = c.block_m <= 32 ? 4 : 2;
     c.kind = W4A16_ROUTE_INDEXED;
     apply_env_overrides(&c, false);
   }
   if (c.kind != W4A16_ROUTE_INDEXED) return fail(W4A16_ERR_ARG, "config was chosen for a grouped routing kind");
-  if (!valid_block_m(c.block_m)) return fail(W4A16_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128}", c.block_m);
+  if (!valid_block_m(c.block_m)) return fail(W4A16_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128, 256}", c.block_m);
   if (c.split_k != 1) return fail(W4A16_ERR_UNSUPPORTED, "the MXFP4 GEMM runs one workgroup per tile (split_k = 1)");
   if (!w4a16::mx_gemm_config_supported(epi, c.block_m / 16, c.nr, c.waves, c.stages))
     return fail(W4A16_ERR_UNSUPPORTED, "MXFP4 tile config block_m=%d nr=%d waves=%d stages=%d not built", c.block_m,
                 c.nr, c.waves, c.stages);
-  if (c.block_m != r.block_m)
-    return fail(W4A16_ERR_LAYOUT, "config block_m=%d differs from the routing's block_m=%d", c.block_m, r.block_m);
+  st = check_tile_rows(c, r);
+  if (st != W4A16_OK) return st;
   if (r.capacity % r.block_m) return fail(W4A16_ERR_CAPACITY, "capacity not a multiple of block_m");
   if (combine && !r.topk_ids) return fail(W4A16_ERR_ARG, "combine needs routing.topk_ids");
   const size_t need = combine ? al256((size_t)r.T * r.topk * desc->N * sizeof(float)) : 0;
@@ -1095,7 +1139,8 @@ w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* pac
   p.sentinel = r.T * r.topk;
   p.a_row_div = a_layout == W4A16_A_TOKEN ? r.topk : a_layout == W4A16_A_SLOT ? 1 : 0;
   p.slot_weight = topk_weights;
-  p.grid_blocks = (int32_t)(r.capacity / r.block_m);
+  p.expert_shift = tile_shift(c, r);
+  p.grid_blocks = (int32_t)(r.capacity / c.block_m);
   hipError_t e = w4a16::launch_mx_gemm(epi, c.block_m / 16, c.nr, c.waves, c.stages, p, s);
   if (e != hipSuccess) return hip_fail(e, "mxfp4_moe_gemm launch");
   if (combine) {
@@ -1133,23 +1178,23 @@ w4a16_status w4a16_mxfp4_gate_up_silu(const w4a16_weight_desc* desc, const void*
   if (cfg) {
     c = *cfg;
   } else {
-    c.block_m = r.block_m;
+    c.block_m = mx_tile_rows(r);
     c.nr = 4;
     c.waves = 4;
     c.split_k = 1;
-    c.stages = r.block_m <= 32 ? 4 : 2;
+    c.stages = c.block_m <= 32 ? 4 : 2;
     c.kind = W4A16_ROUTE_INDEXED;
     apply_env_overrides(&c, false);
   }
   if (c.kind != W4A16_ROUTE_INDEXED) return fail(W4A16_ERR_ARG, "config was chosen for a grouped routing kind");
-  if (!valid_block_m(c.block_m)) return fail(W4A16_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128}", c.block_m);
+  if (!valid_block_m(c.block_m)) return fail(W4A16_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128, 256}", c.block_m);
   if (c.split_k != 1 || c.nr != 4)
     return fail(W4A16_ERR_UNSUPPORTED, "the fused A4W4 gate/up call runs one workgroup per tile with nr = 4");
   if (!w4a16::mx_gemm_config_supported(w4a16::kEpiSiluMx, c.block_m / 16, c.nr, c.waves, c.stages))
     return fail(W4A16_ERR_UNSUPPORTED, "MXFP4 tile config block_m=%d nr=%d waves=%d stages=%d not built", c.block_m,
                 c.nr, c.waves, c.stages);
-  if (c.block_m != r.block_m)
-    return fail(W4A16_ERR_LAYOUT, "config block_m=%d differs from the routing's block_m=%d", c.block_m, r.block_m);
+  st = check_tile_rows(c, r);
+  if (st != W4A16_OK) return st;
   if (r.capacity % r.block_m) return fail(W4A16_ERR_CAPACITY, "capacity not a multiple of block_m");
   if (r.T == 0) return W4A16_OK;
   w4a16::GemmParams p = base_params(desc, packed_w, packed_s, reinterpret_cast<const uint16_t*>(x_codes),
@@ -1161,7 +1206,8 @@ w4a16_status w4a16_mxfp4_gate_up_silu(const w4a16_weight_desc* desc, const void*
   p.num_tokens_padded = r.num_tokens_padded;
   p.sentinel = r.T * r.topk;
   p.a_row_div = r.topk;
-  p.grid_blocks = (int32_t)(r.capacity / r.block_m);
+  p.expert_shift = tile_shift(c, r);
+  p.grid_blocks = (int32_t)(r.capacity / c.block_m);
   hipError_t e = w4a16::launch_mx_gemm(w4a16::kEpiSiluMx, c.block_m / 16, c.nr, c.waves, c.stages, p,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mxfp4_gate_up_silu launch");

@@ -359,16 +359,17 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, TileSmem<MT>& sm, 
     else
       go(std::integral_constant<int, 4>{});
   } else {
-    static_assert(MT == 8, "token tiles per block: 1, 2, 4 or 8");
+    static_assert(MT == 8 || MT == 16, "token tiles per block: 1, 2, 4, 8 or 16");
+    constexpr int Q = MT / 4;                        // active tiles rounded up to a multiple of Q
     const int na = 32 - __clz(tmask);               // tmask is a prefix
-    if (na <= 2)
-      go(std::integral_constant<int, 2>{});
-    else if (na <= 4)
-      go(std::integral_constant<int, 4>{});
-    else if (na <= 6)
-      go(std::integral_constant<int, 6>{});
+    if (na <= Q)
+      go(std::integral_constant<int, Q>{});
+    else if (na <= 2 * Q)
+      go(std::integral_constant<int, 2 * Q>{});
+    else if (na <= 3 * Q)
+      go(std::integral_constant<int, 3 * Q>{});
     else
-      go(std::integral_constant<int, 8>{});
+      go(std::integral_constant<int, 4 * Q>{});
   }
 }
 
@@ -794,7 +795,7 @@ static KernelSet find_kernels(int route, int epi, int m_tiles, int nr, int waves
   W4A16_CASE(1, 2, 4, 2) W4A16_CASE(2, 2, 4, 2) W4A16_CASE(4, 2, 4, 2) W4A16_CASE(8, 2, 4, 2)
   W4A16_CASE(1, 4, 4, 2) W4A16_CASE(2, 4, 4, 2) W4A16_CASE(4, 4, 4, 2) W4A16_CASE(8, 4, 4, 2)
   W4A16_CASE(1, 2, 4, 4) W4A16_CASE(2, 2, 4, 4)
-  W4A16_CASE(1, 2, 8, 2) W4A16_CASE(2, 2, 8, 2) W4A16_CASE(8, 2, 8, 2)
+  W4A16_CASE(1, 2, 8, 2) W4A16_CASE(2, 2, 8, 2) W4A16_CASE(8, 2, 8, 2) W4A16_CASE(16, 2, 8, 2)
 #undef W4A16_CASE
   return KernelSet{};
 }
@@ -810,7 +811,7 @@ int xcd_group_for(int split, int per_block) { return split <= 1 && per_block >= 
 hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves, int stages,
                        const GemmParams& p, hipStream_t stream) {
   if (prefill_applies(route, epilogue, m_tiles, nr, waves, stages, p))
-    return launch_gemm_prefill(route, epilogue, p, stream);
+    return launch_gemm_prefill(route, epilogue, m_tiles, nr, waves, p, stream);
   const KernelSet k = find_kernels(route, epilogue, m_tiles, nr, waves, stages);
   if (k.classic == nullptr) return hipErrorInvalidValue;
   // Block-major order spreads a block's N tiles over the XCDs (round robin);

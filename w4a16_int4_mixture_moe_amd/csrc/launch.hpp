@@ -36,6 +36,7 @@ struct GemmParams {
   // indexed
   const int32_t* sorted_ids;
   const int32_t* expert_ids;
+  int32_t expert_shift;         // log2(routing block_m / tile rows): tile b reads expert_ids[b >> shift]
   const int32_t* num_tokens_padded;
   int32_t sentinel;             // T * topk
   int32_t a_row_div;            // topk (rows per token), 1 (rows per slot), 0 (rows per sorted position)
@@ -90,12 +91,13 @@ bool gemm_config_supported(int route, int epilogue, int m_tiles, int nr, int wav
 hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves, int stages,
                        const GemmParams& p, hipStream_t stream);
 
-// The prefill tile (prefill.hip): 128 routed rows x 256 weight rows per
-// workgroup, activations staged by LDS-DMA.  Serves the (m_tiles 8, nr 4,
-// waves 4, stages 2) configuration when K is a multiple of 128 and K is not
-// split; launch_gemm dispatches to it.
+// The prefill tiles (prefill.hip): 128 or 256 routed rows x 256 weight rows
+// per workgroup, activations staged by LDS-DMA.  Serve the (m_tiles 8, nr 4,
+// waves 4) and (m_tiles 16, nr 2, waves 8) configurations with stages 2 when
+// K is a multiple of 128 and K is not split; launch_gemm dispatches to them.
 bool prefill_applies(int route, int epilogue, int m_tiles, int nr, int waves, int stages, const GemmParams& p);
-hipError_t launch_gemm_prefill(int route, int epilogue, const GemmParams& p, hipStream_t stream);
+hipError_t launch_gemm_prefill(int route, int epilogue, int m_tiles, int nr, int waves, const GemmParams& p,
+                               hipStream_t stream);
 
 // Stream-K: `workgroups` persistent workgroups each take an equal contiguous
 // range of (tile, 128-K chunk) units; tiles cut by a range boundary leave

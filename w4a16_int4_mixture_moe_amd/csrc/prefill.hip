@@ -1,5 +1,8 @@
-// Prefill-side W4A16 MoE GEMM tile for gfx950: 128 routed rows x 256 weight
-// rows per workgroup.
+// Prefill-side W4A16 MoE GEMM tiles for gfx950: 128 routed rows x 256 weight
+// rows per workgroup (four waves, two workgroups per CU), or 256 routed rows x
+// 256 weight rows (eight waves, one workgroup per CU).  The description below
+// is the 128-row tile's; the 256-row one gives each wave two weight tiles of
+// all sixteen token tiles instead of four of eight.
 //
 // Why a separate kernel.  Large routed blocks are MFMA-bound, and on gfx950
 // what limits the MFMA rate in this GEMM is the LDS and register traffic per
@@ -50,18 +53,30 @@ namespace w4a16 {
 
 namespace {
 
-constexpr int kPfMT = 8;            // token tiles per block (128 rows)
-constexpr int kPfNR = 4;            // weight tiles per wave
-constexpr int kPfNW = 4;            // waves per workgroup
-constexpr int kPfBM = 16 * kPfMT;
-constexpr int kPfChunkBytes = kPfBM * kChunk * 2;   // one staged chunk: 32 KB
+// Tile shapes: MT token tiles per block (BM = 16 MT rows), NR weight tiles
+// per wave, NW waves per workgroup; every wave covers all MT token tiles, so
+// a wave holds NR x MT accumulator tiles (128 registers in both shapes) and
+// two waves run per SIMD.
+template <int MT_, int NR_, int NW_>
+struct PfCfg {
+  static constexpr int MT = MT_, NR = NR_, NW = NW_, BM = 16 * MT_;
+  static constexpr int kPerCU = 8 / NW_;   // resident workgroups per CU
+};
+// 128 rows x 256 weight rows, two workgroups per CU
+using PfNarrow = PfCfg<8, 4, 4>;
+// 256 rows x 256 weight rows, one workgroup per CU: each dequantised weight
+// fragment feeds 16 token tiles (half the dequantisation and weight traffic
+// per MFMA of the narrow tile) and an expert of up to 256 rows reads its
+// weights once; LDS holds two 64 KB chunks
+using PfWide = PfCfg<16, 2, 8>;
 
+template <int BM>
 struct PfSmem {
-  uint16_t xs[2][kPfBM * kChunk];   // two staged chunks, granules swizzled by row
-  int row[kPfBM];                   // activation row per block row, -1 = padding
-  int out[kPfBM];                   // output row per block row, -1 = not stored
-  float w[kPfBM];                   // top-k weight per block row (weighted epilogue)
-  uint32_t xoff[kPfBM];             // byte offset of the LDS-DMA source granule per block row
+  uint16_t xs[2][BM * kChunk];      // two staged chunks, granules permuted by row
+  int row[BM];                      // activation row per block row, -1 = padding
+  int out[BM];                      // output row per block row, -1 = not stored
+  float w[BM];                      // top-k weight per block row (weighted epilogue)
+  uint32_t xoff[BM];                // byte offset of the LDS-DMA source granule per block row
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -82,33 +97,35 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
-// acc += this wave's 64 weight rows x the block's first 16 NA rows over all K.
-// SHORT: K is at most two chunks.  resident (SHORT only): the block's
+// acc += this wave's 16 NR weight rows x the block's first 16 NA rows over
+// all K.  SHORT: K is at most two chunks.  resident (SHORT only): the block's
 // activation rows are already in LDS from the previous N tile (two chunks
 // fill both buffers); nothing is staged.
-template <int NA, bool SHORT>
-__device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int expert, int nt,
-                                            f32x4_t (&acc)[kPfNR][kPfMT], bool resident) {
-  static_assert(NA >= 1 && NA <= kPfMT, "active tile count");
+template <class C, int NA, bool SHORT>
+__device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem<C::BM>& sm, int expert, int nt,
+                                            f32x4_t (&acc)[C::NR][C::MT], bool resident) {
+  constexpr int NR = C::NR, NW = C::NW;
+  static_assert(NA >= 1 && NA <= C::MT && (4 * NA) % NW == 0, "active tile count");
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int KC = p.KC;
 
   // LDS-DMA of a chunk: instruction i (of 4 NA) writes block rows 4 i .. 4 i + 3;
-  // this wave issues i = wave + 4 k, k < NA.  Lane l lands at row
+  // this wave issues i = wave + NW k, k < 4 NA / NW.  Lane l lands at row
   // 4 i + l / 16, position l % 16, so it loads granule (l % 16) ^ swz(row)
-  // of that row, the same granule for every k (16 k leaves row % 16 alone).
+  // of that row, the same granule for every k (4 NW k leaves row % 16 alone).
   // (the per-lane source offsets are kept in LDS, sm.xoff, not in registers)
   if (!resident) {
     const int fallback_row = sm.row[0];   // always valid
-    for (int i = tid; i < kPfBM; i += kPfNW * kWave) {
+    for (int i = tid; i < C::BM; i += NW * kWave) {
       const int r = sm.row[i];
       sm.xoff[i] = (uint32_t)(r >= 0 ? r : fallback_row) * (uint32_t)(p.K * 2);
     }
   }
   __syncthreads();
-  // row % 16 = 4 wave + l / 16: swz = l / 16 ^ (12 if wave is odd)
+  // row % 16 = (4 wave + l / 16) % 16: swz = l / 16 ^ (12 if wave is odd)
   const uint32_t gran = (uint32_t)(((lane & 15) ^ (lane >> 4) ^ ((wave & 1) * 12)) * 16);
   const int xrow = 4 * wave + (lane >> 4);
   const gptr_t xbase = uniform_ptr(p.a);
@@ -116,16 +133,17 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
     if (resident) return;
     const gptr_t base = xbase + (int64_t)c * (kChunk * 2) + gran;
 #pragma unroll
-    for (int k = 0; k < NA; ++k)
-      dma16(base + sm.xoff[xrow + 16 * k], (lds_ptr_t)(reinterpret_cast<char*>(&sm.xs[buf][0]) + (wave + 4 * k) * 1024));
+    for (int k = 0; k < 4 * NA / NW; ++k)
+      dma16(base + sm.xoff[xrow + 4 * NW * k],
+            (lds_ptr_t)(reinterpret_cast<char*>(&sm.xs[buf][0]) + (wave + NW * k) * 1024));
   };
 
   // weights and scales: a ring of two chunks per wave, as in moe_gemm_kernel
-  const int rt_base = nt * (kPfNW * kPfNR) + wave * kPfNR;
-  gptr_t wbase[kPfNR];
-  gptr_t sbase[kPfNR];
+  const int rt_base = nt * (NW * NR) + wave * NR;
+  gptr_t wbase[NR];
+  gptr_t sbase[NR];
 #pragma unroll
-  for (int r = 0; r < kPfNR; ++r) {
+  for (int r = 0; r < NR; ++r) {
     const int rt = min(rt_base + r, p.NT - 1);
     const int64_t tile = (int64_t)expert * p.w_tiles + rt;
     wbase[r] = uniform_ptr(p.packed_w + tile * p.KC * kWave);
@@ -133,22 +151,22 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
   }
   const uint32_t woff = (uint32_t)lane * 16u;
   const uint32_t soff = (uint32_t)lane * 4u;
-  auto issue_w = [&](int c, u32x4_t (&w)[kPfNR]) {
+  auto issue_w = [&](int c, u32x4_t (&w)[NR]) {
 #pragma unroll
-    for (int r = 0; r < kPfNR; ++r) w[r] = gload_u32x4(wbase[r] + (int64_t)c * (kWave * 16) + woff);
+    for (int r = 0; r < NR; ++r) w[r] = gload_u32x4(wbase[r] + (int64_t)c * (kWave * 16) + woff);
   };
   // the scale words of a chunk pair (low half: even chunk, high half: odd)
-  auto issue_s = [&](int c, uint32_t (&sc)[kPfNR]) {
+  auto issue_s = [&](int c, uint32_t (&sc)[NR]) {
 #pragma unroll
-    for (int r = 0; r < kPfNR; ++r) sc[r] = gload_u32(sbase[r] + (int64_t)(c >> 1) * (kWave * 4) + soff);
+    for (int r = 0; r < NR; ++r) sc[r] = gload_u32(sbase[r] + (int64_t)(c >> 1) * (kWave * 4) + soff);
   };
 
   const DequantMasks masks = make_dequant_masks();
   // weights and scales of the current chunk and of the next one (a ring of
   // two register sets: the second wave on each SIMD covers the rest of the
   // load latency)
-  u32x4_t wr[2][kPfNR];
-  uint32_t sr[2][kPfNR];            // scale words of the current and the next chunk pair
+  u32x4_t wr[2][NR];
+  uint32_t sr[2][NR];               // scale words of the current and the next chunk pair
 
   // prologue: chunk 0 to LDS, weights and scales of chunk 0 in flight
   issue_x(0, 0);
@@ -156,7 +174,7 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
   issue_w(0, wr[0]);
   issue_s(0, sr[0]);
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<2 * kPfNR>();          // this wave's DMA of chunk 0 has landed
+  wait_vmcnt<2 * NR>();             // this wave's DMA of chunk 0 has landed
   __syncthreads();                  // ... and every wave's
 
   // one chunk at ring position P: DMA of chunk c + 1 into the other LDS
@@ -182,9 +200,9 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
     const char* xs = reinterpret_cast<const char*>(&sm.xs[P][0]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bf16x8_t A[kPfNR];
+      bf16x8_t A[NR];
 #pragma unroll
-      for (int r = 0; r < kPfNR; ++r) {
+      for (int r = 0; r < NR; ++r) {
         const uint32_t word = sr[Q][r];
         const float sv = __builtin_bit_cast(float, P ? (word & 0xFFFF0000u) : (word << 16));
         A[r] = dequant8(wr[P][r][j], sv, -1032.0f * sv, 0.0625f * sv, -72.0f * sv, masks);
@@ -195,7 +213,7 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
       for (int t = 0; t < NA; ++t) {
         const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(xs + t * 4096 + rowoff + goff);
 #pragma unroll
-        for (int r = 0; r < kPfNR; ++r)
+        for (int r = 0; r < NR; ++r)
           acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r], B, acc[r][t], 0, 0, 0);
       }
       // keep each 32-K step's operands to itself: hoisting the next step's
@@ -207,9 +225,9 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
       // the DMA of chunk c + 1 was issued before its weights (and, after an
       // odd chunk, the next pair's scales)
       if (P == 1)
-        wait_vmcnt<2 * kPfNR>();
+        wait_vmcnt<2 * NR>();
       else
-        wait_vmcnt<kPfNR>();
+        wait_vmcnt<NR>();
     }
     __syncthreads();
   };
@@ -241,20 +259,20 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem& sm, int
 // of its own, so the registers of the one-tile kernels are unaffected): more
 // than one tile, K fits the two LDS buffers and the later tiles reuse the
 // staged rows.
-template <int EPI, bool LOOP>
-__device__ __forceinline__ void pf_run(const GemmParams& p, PfSmem& sm, int expert, int nt0, int nt1,
+template <class C, int EPI, bool LOOP>
+__device__ __forceinline__ void pf_run(const GemmParams& p, PfSmem<C::BM>& sm, int expert, int nt0, int nt1,
                                        uint32_t tmask) {
   const int na = 32 - __clz(tmask);
   auto go = [&](auto NA_) {
     constexpr int NA = decltype(NA_)::value;
     auto tile = [&](int nt, bool resident) {
-      f32x4_t acc[kPfNR][kPfMT];
+      f32x4_t acc[C::NR][C::MT];
 #pragma unroll
-      for (int r = 0; r < kPfNR; ++r)
+      for (int r = 0; r < C::NR; ++r)
 #pragma unroll
-        for (int t = 0; t < kPfMT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      pf_mainloop<NA, LOOP>(p, sm, expert, nt, acc, resident);
-      epilogue<kPfMT, kPfNR, kPfNW, EPI>(p, sm, nt, (1u << NA) - 1u, acc);
+        for (int t = 0; t < C::MT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      pf_mainloop<C, NA, LOOP>(p, sm, expert, nt, acc, resident);
+      epilogue<C::MT, C::NR, C::NW, EPI>(p, sm, nt, (1u << NA) - 1u, acc);
     };
     if constexpr (LOOP) {
       for (int nt = nt0; nt < nt1; ++nt) tile(nt, nt != nt0);
@@ -262,21 +280,27 @@ __device__ __forceinline__ void pf_run(const GemmParams& p, PfSmem& sm, int expe
       tile(nt0, false);
     }
   };
-  if (na <= 2)
-    go(std::integral_constant<int, 2>{});
-  else if (na <= 4)
-    go(std::integral_constant<int, 4>{});
-  else if (na <= 6)
-    go(std::integral_constant<int, 6>{});
+  // active tiles rounded up to a multiple of C::MT / 4 (two for the narrow
+  // tile, four for the wide one)
+  constexpr int Q = C::MT / 4;
+  if (na <= Q)
+    go(std::integral_constant<int, Q>{});
+  else if (na <= 2 * Q)
+    go(std::integral_constant<int, 2 * Q>{});
+  else if (na <= 3 * Q)
+    go(std::integral_constant<int, 3 * Q>{});
   else
-    go(std::integral_constant<int, 8>{});
+    go(std::integral_constant<int, 4 * Q>{});
 }
 
 // One workgroup per (routed block, group of n_loop consecutive N tiles);
 // n_loop > 1 only when K fits the two LDS buffers.
-template <int ROUTE, int EPI, bool LOOP>
-__global__ __launch_bounds__(kPfNW * kWave, 2) void moe_gemm_prefill_kernel(const GemmParams p, int n_loop) {
-  __shared__ __attribute__((aligned(16))) PfSmem sm;
+// (Template arguments are the tile's sizes rather than its PfCfg so that the
+// kernel's name in a trace reads like the general kernel's.)
+template <int MT, int NR, int NW, int ROUTE, int EPI, bool LOOP>
+__global__ __launch_bounds__(NW * kWave, 8 / NW) void moe_gemm_prefill_kernel(const GemmParams p, int n_loop) {
+  using C = PfCfg<MT, NR, NW>;
+  __shared__ __attribute__((aligned(16))) PfSmem<C::BM> sm;
   // work item (routed block, N-tile group), block-major (consecutive
   // workgroups, the N tiles of one block, go to different XCDs) unless the
   // block has few groups (block_of).  Measured against orders that keep a
@@ -288,37 +312,43 @@ __global__ __launch_bounds__(kPfNW * kWave, 2) void moe_gemm_prefill_kernel(cons
   int mb, g;
   if (!block_of(p, blockIdx.x, groups, mb, g)) return;
   const int nt0 = g * n_loop;
-  const int expert = setup_rows<kPfMT, kPfNW, ROUTE, EPI>(p, mb, sm);
+  const int expert = setup_rows<C::MT, C::NW, ROUTE, EPI>(p, mb, sm);
   if (expert < 0) return;
   __syncthreads();
-  pf_run<EPI, LOOP>(p, sm, expert, nt0, min(nt0 + n_loop, p.n_tiles), active_tiles<kPfMT>(sm));
+  pf_run<C, EPI, LOOP>(p, sm, expert, nt0, min(nt0 + n_loop, p.n_tiles), active_tiles<C::MT>(sm));
 }
 
 typedef void (*PfKernel)(const GemmParams, int);
 
-template <bool LOOP>
-PfKernel pick_prefill_loop(int route, int epi) {
+template <class C, bool LOOP>
+PfKernel pick_prefill_of(int route, int epi) {
   if (route == kRouteIndexed) {
-    if (epi == kEpiStore) return moe_gemm_prefill_kernel<kRouteIndexed, kEpiStore, LOOP>;
-    if (epi == kEpiWeighted) return moe_gemm_prefill_kernel<kRouteIndexed, kEpiWeighted, LOOP>;
-    if (epi == kEpiSilu) return moe_gemm_prefill_kernel<kRouteIndexed, kEpiSilu, LOOP>;
+    if (epi == kEpiStore) return moe_gemm_prefill_kernel<C::MT, C::NR, C::NW, kRouteIndexed, kEpiStore, LOOP>;
+    if (epi == kEpiWeighted) return moe_gemm_prefill_kernel<C::MT, C::NR, C::NW, kRouteIndexed, kEpiWeighted, LOOP>;
+    if (epi == kEpiSilu) return moe_gemm_prefill_kernel<C::MT, C::NR, C::NW, kRouteIndexed, kEpiSilu, LOOP>;
     return nullptr;
   }
   if (epi != kEpiStore) return nullptr;
-  if (route == kRouteContiguous) return moe_gemm_prefill_kernel<kRouteContiguous, kEpiStore, LOOP>;
-  if (route == kRouteMasked) return moe_gemm_prefill_kernel<kRouteMasked, kEpiStore, LOOP>;
+  if (route == kRouteContiguous) return moe_gemm_prefill_kernel<C::MT, C::NR, C::NW, kRouteContiguous, kEpiStore, LOOP>;
+  if (route == kRouteMasked) return moe_gemm_prefill_kernel<C::MT, C::NR, C::NW, kRouteMasked, kEpiStore, LOOP>;
   return nullptr;
 }
 
-PfKernel pick_prefill(int route, int epi, bool loop = false) {
-  return loop ? pick_prefill_loop<true>(route, epi) : pick_prefill_loop<false>(route, epi);
+// The prefill tile of a configuration (m_tiles, nr, waves), or nullptr; the
+// N-tile loop exists for the narrow tile only.
+PfKernel pick_prefill(int m_tiles, int nr, int waves, int route, int epi, bool loop) {
+  if (m_tiles == PfNarrow::MT && nr == PfNarrow::NR && waves == PfNarrow::NW)
+    return loop ? pick_prefill_of<PfNarrow, true>(route, epi) : pick_prefill_of<PfNarrow, false>(route, epi);
+  if (m_tiles == PfWide::MT && nr == PfWide::NR && waves == PfWide::NW && !loop)
+    return pick_prefill_of<PfWide, false>(route, epi);
+  return nullptr;
 }
 
 }  // namespace
 
 bool prefill_applies(int route, int epilogue, int m_tiles, int nr, int waves, int stages, const GemmParams& p) {
-  return m_tiles == kPfMT && nr == kPfNR && waves == kPfNW && stages == 2 && p.K % kChunk == 0 && p.split <= 1 &&
-         pick_prefill(route, epilogue) != nullptr;
+  return stages == 2 && p.K % kChunk == 0 && p.split <= 1 &&
+         pick_prefill(m_tiles, nr, waves, route, epilogue, false) != nullptr;
 }
 
 // N tiles per workgroup.  With K of at most two chunks (K <= 256, the down
@@ -332,17 +362,18 @@ bool prefill_applies(int route, int epilogue, int m_tiles, int nr, int waves, in
 // 515 us; 4 tiles (two workgroups per block) 684 us.
 constexpr int64_t kPfLoopMinWorkgroups = 1536;
 
-int prefill_n_loop(const GemmParams& p) {
-  if (p.KC > 2) return 1;
+int prefill_n_loop(const GemmParams& p, int m_tiles) {
+  if (p.KC > 2 || m_tiles != PfNarrow::MT) return 1;
   int best = 1;
   for (int l = 2; l <= p.n_tiles; ++l)
     if ((int64_t)p.grid_blocks * ((p.n_tiles + l - 1) / l) >= kPfLoopMinWorkgroups) best = l;
   return best;
 }
 
-hipError_t launch_gemm_prefill(int route, int epilogue, const GemmParams& p, hipStream_t stream) {
-  const int n_loop = prefill_n_loop(p);
-  const PfKernel k = pick_prefill(route, epilogue, n_loop > 1);
+hipError_t launch_gemm_prefill(int route, int epilogue, int m_tiles, int nr, int waves, const GemmParams& p,
+                               hipStream_t stream) {
+  const int n_loop = prefill_n_loop(p, m_tiles);
+  const PfKernel k = pick_prefill(m_tiles, nr, waves, route, epilogue, n_loop > 1);
   if (k == nullptr || p.K % kChunk) return hipErrorInvalidValue;
   const int groups = (p.n_tiles + n_loop - 1) / n_loop;
   GemmParams q = p;
@@ -350,7 +381,7 @@ hipError_t launch_gemm_prefill(int route, int epilogue, const GemmParams& p, hip
   const int64_t grid = grid_of(q, groups);
   if (grid <= 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kPfNW * kWave), 0, stream, q, n_loop);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(waves * kWave), 0, stream, q, n_loop);
   return hipGetLastError();
 }
 

@@ -60,8 +60,11 @@ __device__ __forceinline__ int setup_rows(const GemmParams& p, int mb, Smem& sm)
   int expert;
   if constexpr (ROUTE == kRouteIndexed) {
     if (mb * BM >= *p.num_tokens_padded) return -1;
-    expert = p.expert_ids[mb];
+    expert = p.expert_ids[mb >> p.expert_shift];
     if ((unsigned)expert >= (unsigned)p.E) return -1;   // -1 (unused block) or foreign id
+    // tiles smaller than the routing's blocks: an expert's padding sits at the
+    // end of its segment, so a tile whose first row is padding has no rows
+    if (p.expert_shift && (unsigned)p.sorted_ids[mb * BM] >= (unsigned)p.sentinel) return -1;
     for (int i = tid; i < BM; i += NTHR) {
       const int pos = mb * BM + i;                         // sorted position
       const int s = p.sorted_ids[pos];
