@@ -76,10 +76,14 @@ struct PfSmem {
   int row[BM];                      // activation row per block row, -1 = padding
   int out[BM];                      // output row per block row, -1 = not stored
   float w[BM];                      // top-k weight per block row (weighted epilogue)
-  uint32_t xoff[BM];                // byte offset of the LDS-DMA source granule per block row
+  // byte offsets of the LDS-DMA source rows, in the order the DMA reads them:
+  // entry 8 g + k is block row g + (BM / 8) k (see pf_mainloop)
+  uint32_t xoff[BM];
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(3))) char* lds_cptr_t;
+typedef const __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land
 // at dst + 16 l (dst wave-uniform).  (Kept out of templates: the host pass
@@ -116,12 +120,17 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem<C::BM>& 
   // this wave issues i = wave + NW k, k < 4 NA / NW.  Lane l lands at row
   // 4 i + l / 16, position l % 16, so it loads granule (l % 16) ^ swz(row)
   // of that row, the same granule for every k (4 NW k leaves row % 16 alone).
-  // (the per-lane source offsets are kept in LDS, sm.xoff, not in registers)
+  // The per-lane source offsets of rows g + 4 NW k (g = 4 wave + l / 16,
+  // k < 8; 8 x 4 NW = BM rows) sit in LDS as 8 consecutive words per g, so a
+  // lane fetches its offsets with two 16-byte reads and one wait (read one by
+  // one, each DMA waited on its own LDS round trip).
+  static_assert(8 * 4 * NW == C::BM, "eight DMA rows per lane cover the block");
+  constexpr int KX = 4 * NA / NW;        // DMA instructions per wave per chunk (<= 8)
   if (!resident) {
     const int fallback_row = sm.row[0];   // always valid
     for (int i = tid; i < C::BM; i += NW * kWave) {
       const int r = sm.row[i];
-      sm.xoff[i] = (uint32_t)(r >= 0 ? r : fallback_row) * (uint32_t)(p.K * 2);
+      sm.xoff[(i % (4 * NW)) * 8 + i / (4 * NW)] = (uint32_t)(r >= 0 ? r : fallback_row) * (uint32_t)(p.K * 2);
     }
   }
   __syncthreads();
@@ -132,10 +141,19 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem<C::BM>& 
   auto issue_x = [&](int c, int buf) {
     if (resident) return;
     const gptr_t base = xbase + (int64_t)c * (kChunk * 2) + gran;
+    const u32x4_t* xq = reinterpret_cast<const u32x4_t*>(&sm.xoff[xrow * 8]);
+    uint32_t xo[8];
+    const u32x4_t lo = xq[0];
 #pragma unroll
-    for (int k = 0; k < 4 * NA / NW; ++k)
-      dma16(base + sm.xoff[xrow + 4 * NW * k],
-            (lds_ptr_t)(reinterpret_cast<char*>(&sm.xs[buf][0]) + (wave + NW * k) * 1024));
+    for (int k = 0; k < 4; ++k) xo[k] = lo[k];
+    if constexpr (KX > 4) {
+      const u32x4_t hi = xq[1];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) xo[4 + k] = hi[k];
+    }
+#pragma unroll
+    for (int k = 0; k < KX; ++k)
+      dma16(base + xo[k], (lds_ptr_t)(reinterpret_cast<char*>(&sm.xs[buf][0]) + (wave + NW * k) * 1024));
   };
 
   // weights and scales: a ring of two chunks per wave, as in moe_gemm_kernel
@@ -198,28 +216,100 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem<C::BM>& 
       __builtin_amdgcn_sched_barrier(0);
     }
     const char* xs = reinterpret_cast<const char*>(&sm.xs[P][0]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8_t A[NR];
+    const uint32_t rowoff = (uint32_t)(lane & 15) * 256u;
+    // this wave's weight fragments of 32-K step j, dequantised
+    auto dequant_step = [&](int j, bf16x8_t (&A)[NR]) {
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         const uint32_t word = sr[Q][r];
         const float sv = __builtin_bit_cast(float, P ? (word & 0xFFFF0000u) : (word << 16));
         A[r] = dequant8(wr[P][r][j], sv, -1032.0f * sv, 0.0625f * sv, -72.0f * sv, masks);
       }
-      const uint32_t rowoff = (uint32_t)(lane & 15) * 256u;
-      const uint32_t goff = (uint32_t)((((lane >> 4) * 4 + j) ^ (lane & 3) ^ (((lane >> 2) & 1) * 12)) * 16);
+    };
+    // the activation fragment of token tile t at step j
+    auto goff = [&](int j) {
+      return (uint32_t)((((lane >> 4) * 4 + j) ^ (lane & 3) ^ (((lane >> 2) & 1) * 12)) * 16);
+    };
+    auto operand = [&](int j, int t) {
+      return *reinterpret_cast<const bf16x8_t*>(xs + t * 4096 + rowoff + goff(j));
+    };
+    if constexpr (NR == 2) {
+      // two weight tiles per wave leave registers for a pipeline: the
+      // fragments of the next two token tiles are read while the MFMAs of
+      // the current two run, and the next step's weights are dequantised
+      // under the current step's MFMAs (the order of every accumulator's
+      // MFMAs is unchanged).  Measured on MI355X against reading each pair
+      // and waiting for it: gate/up EP8 prefill 540 -> 518 us, EP32 145 ->
+      // 135 us.  (Loading the weights two chunks ahead gained 1 % more: it
+      // needs a barrier without __syncthreads' wait for every load, and the
+      // compiler then waits for all loads wherever a register load is used
+      // after an LDS-DMA was issued, so it was not kept.)
+      // LDS byte address of this lane's row of step j in chunk c's buffer,
+      // opaque to the optimiser: the token tiles' offsets (t x 4 KB) then stay
+      // in the reads' immediate field (a folded 64 KB buffer offset would
+      // overflow it and cost an address register per tile and step)
+      uint32_t xb[4];
 #pragma unroll
-      for (int t = 0; t < NA; ++t) {
-        const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(xs + t * 4096 + rowoff + goff);
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r], B, acc[r][t], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        xb[j] = (uint32_t)(uintptr_t)(lds_cptr_t)xs + rowoff + goff(j);
+        __asm__ volatile("" : "+v"(xb[j]));
       }
-      // keep each 32-K step's operands to itself: hoisting the next step's
-      // dequant or operand reads above these MFMAs needs more registers than
-      // two waves per SIMD leave (the second wave covers the latency instead)
-      __builtin_amdgcn_sched_barrier(0);
+      auto operand2 = [&](int j, int t) {
+        return *reinterpret_cast<const lds_bf16x8_t*>((lds_cptr_t)(uintptr_t)xb[j] + t * 4096);
+      };
+      bf16x8_t A[NR], An[NR];
+      dequant_step(0, A);
+      bf16x8_t B0 = operand2(0, 0), B1 = operand2(0, 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int tp = 0; tp < NA / 2; ++tp) {
+          bf16x8_t N0 = B0, N1 = B1;
+          if (tp + 1 < NA / 2) {
+            N0 = operand2(j, 2 * tp + 2);
+            N1 = operand2(j, 2 * tp + 3);
+          } else if (j < 3) {
+            N0 = operand2(j + 1, 0);
+            N1 = operand2(j + 1, 1);
+          }
+          if (tp < NR && j < 3) {   // weight tile tp of the next step
+            const uint32_t word = sr[Q][tp];
+            const float sv = __builtin_bit_cast(float, P ? (word & 0xFFFF0000u) : (word << 16));
+            An[tp] = dequant8(wr[P][tp][j + 1], sv, -1032.0f * sv, 0.0625f * sv, -72.0f * sv, masks);
+          }
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            acc[r][2 * tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r], B0, acc[r][2 * tp], 0, 0, 0);
+            acc[r][2 * tp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r], B1, acc[r][2 * tp + 1], 0, 0, 0);
+          }
+          B0 = N0;
+          B1 = N1;
+          // one pair per scheduling region (a wider one lets the scheduler
+          // hoist later pairs' reads and dequant work, which spills)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (j < 3)
+#pragma unroll
+          for (int r = 0; r < NR; ++r) A[r] = An[r];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x8_t A[NR];
+        dequant_step(j, A);
+#pragma unroll
+        for (int t = 0; t < NA; ++t) {
+          const bf16x8_t B = operand(j, t);
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r], B, acc[r][t], 0, 0, 0);
+        }
+        // keep each 32-K step's operands to itself: with four weight tiles
+        // per wave, hoisting the next step's dequant or operand reads above
+        // these MFMAs needs more registers than two waves per SIMD leave (the
+        // second wave covers the latency instead)
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (has_next) {
       // the DMA of chunk c + 1 was issued before its weights (and, after an
