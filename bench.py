@@ -98,13 +98,15 @@ def cfg_tag(cfg) -> str:
 
 
 def kernel_name(cfg, route: int, epi: int, K: int, mx: bool = False) -> str:
-    """The GEMM kernel's name as the rocprofv3 kernel trace shows it (the
-    library runs the unsplit 128-row, 4-tiles-per-wave, 4-wave and 256-row,
-    2-tiles-per-wave, 8-wave configurations on its prefill tiles when K is a
-    multiple of 128, the first in its N-tile-loop form for K <= 256 on the
-    grids measured here)."""
+    """The GEMM kernel's name as the rocprofv3 kernel trace shows it.  nr 1 is
+    the tile whose waves split K; the library runs the unsplit 128-row,
+    4-tiles-per-wave, 4-wave and 256-row, 2-tiles-per-wave, 8-wave
+    configurations on its prefill tiles when K is a multiple of 128, the
+    first in its N-tile-loop form for K <= 256 on the grids measured here."""
     if mx:
         return f"mx_gemm_kernel<{cfg.block_m // 16}, {cfg.nr}, {cfg.waves}, {cfg.stages}, {epi}>"
+    if cfg.nr == 1:
+        return f"moe_gemm_kwave_kernel<{cfg.waves}, {epi}>"
     tile = (cfg.block_m, cfg.nr, cfg.waves)
     if tile in ((128, 4, 4), (256, 2, 8)) and cfg.stages == 2 and cfg.split_k <= 1 and K % 128 == 0:
         loop = "true" if K <= 256 and tile == (128, 4, 4) else "false"
@@ -288,7 +290,11 @@ class IndexedStep:
             self.cfg2 = override(M.indexed_config(self.routing, self.p2, combine=True))
             self.cfg2.combine_cols = args.combine_cols
             if self.fused:
+                # what the fused call chooses for itself: whole tiles, gate /
+                # up tiles in pairs (nr 1 falls back to the two-tile kernel)
                 self.cfg1.split_k = 1
+                if self.cfg1.nr == 1 and not args.nr:
+                    self.cfg1.nr, self.cfg1.waves = 2, 4
         self.h = torch.empty(T * k, sh.N1, dtype=torch.bfloat16, device=dev)
         self.y = torch.empty(T, sh.N2, dtype=torch.bfloat16, device=dev)
         z = lambda n: torch.zeros(max(16, n), dtype=torch.uint8, device=dev)

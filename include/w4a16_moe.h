@@ -182,7 +182,11 @@ typedef struct {
   int32_t block_m;   /* rows per tile: 16, 32, 64, 128 or 256.  Indexed
                         calls: the routing's block_m or a divisor of it (a
                         tile then covers part of a routed block) */
-  int32_t nr;        /* 16-row weight tiles per wave: 2 or 4 */
+  int32_t nr;        /* 16-row weight tiles per wave: 2 or 4; or 1: one
+                        16-row weight tile per workgroup whose waves (8)
+                        split K and sum their partials in LDS (block_m 16,
+                        split_k 1, K a multiple of 128, indexed routing,
+                        per-slot or combine epilogue) */
   int32_t waves;     /* waves per workgroup: 4 (8 for some tiles) */
   int32_t split_k;   /* 1: one workgroup per (block, N tile), whole K;
                         2, 4, 8, 16: that many workgroups per tile, each over
@@ -237,7 +241,9 @@ w4a16_status w4a16_indexed_config(int32_t T, int32_t topk, int32_t E_glob, int32
  *    routing, see w4a16_indexed_config).  split_k
  *    doubles from 1 while the sampled grid (routed blocks x N tiles x
  *    split_k) stays below one round of resident workgroups on 256 CUs and
- *    each slice keeps at least four 128-K chunks.
+ *    each slice keeps at least four 128-K chunks; a block_m 16 grid that
+ *    would split K four or more ways (K a multiple of 128) takes nr 1 with
+ *    eight waves splitting K instead, split_k 1.
  *  kind W4A16_ROUTE_CONTIGUOUS: T = rows of the contiguous layout, E_loc =
  *    experts, [N, K]; topk, E_glob and expected_m ignored.  block_m 128 when
  *    the grid of 128-row blocks fills the machine, else 64.

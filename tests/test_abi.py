@@ -338,7 +338,9 @@ def test_selector_splits_k_only_for_underfilled_grids(L):
     assert W.select(576, 8, 384, 12, 4096, 7168).split_k == 2     # EP32 decode: 384 tiles
     assert W.select(16, 8, 384, 384, 512, 7168).split_k == 2      # TP8 T=16: ~400 sampled tiles
     t1 = W.select(1, 8, 384, 384, 512, 7168)                      # TP8 T=1: 8 blocks x 4 tiles
-    assert t1.split_k == 8                                        # 56 chunks: 7 per slice
+    # it would split 8 ways (56 chunks: 7 per slice); the waves split K instead
+    assert (t1.block_m, t1.nr, t1.waves, t1.split_k) == (16, 1, 8, 1)
+    assert W.select(1, 8, 384, 384, 512, 7000).split_k == 8       # K not a multiple of 128: K slices
     assert W.select(1, 8, 384, 384, 7168, 256).split_k == 1       # its down projection: K = 256, 2 chunks
     assert W.select(4096, 8, 384, 384, 512, 7168).split_k == 1    # prefill-side grids fill the machine
     assert W.select(8192, 8, 384, 48, 4096, 7168).split_k == 1

@@ -189,6 +189,30 @@ def test_ragged_shapes():
         _check_indexed(P, h, y, f"ragged bm={bm} waves=8")
 
 
+def test_sparse_routing_launches_only_possible_tiles():
+    """The launch grid covers the tiles that can hold routed rows (T * topk
+    slots plus one rounding per expert with rows), not the over-allocated
+    capacity: a few tokens over many experts (every slot its own expert, the
+    most padding per row) at every block size, tiles dividing a 256-row
+    routing, K slices and stream-K, against the oracle."""
+    for T in (1, 3, 48):
+        sh = W.MoEShape(name=f"sparse_t{T}", E_glob=384, E_loc=384, first=0, topk=8, T=T, K1=256, N1=64,
+                        K2=256, N2=96, seed=600 + T)
+        P = Problem(sh).upload()
+        for bm in (16, 32, 64, 128):
+            _, h, y = _run_indexed(P, bm)
+            _check_indexed(P, h, y, f"sparse T={T} bm={bm}")
+        r256 = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, 256)
+        _, h, y = _run_indexed(P, 16, nr=1, waves=8)
+        _check_indexed(P, h, y, f"sparse T={T} bm=16 nr=1 (waves splitting K)")
+        for c in (M.config(256, 2, 8), M.config(128, 4), M.config(64, 2), M.config(16, 2, split_k=2),
+                  M.config(16, 2, split_k=0), M.config(16, 1, 8)):
+            h = M.moe_w4a16_gemm(P.d_x, P.p1, r256, cfg=c)
+            y = M.moe_w4a16_gemm(P.d_a, P.p2, r256, topk_weights=P.d_w, cfg=c)
+            torch.cuda.synchronize()
+            _check_indexed(P, h, y, f"sparse T={T} 256-row routing bm={c.block_m} split_k={c.split_k}")
+
+
 def test_multi_chunk_k():
     """K spanning many 128-wide chunks (steady-state loop plus its tail, both
     prefetch depths), ragged and not, against the oracle; depths agree bit

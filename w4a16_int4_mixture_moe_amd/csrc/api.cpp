@@ -182,7 +182,7 @@ int64_t sampled_blocks(const std::vector<int>& counts, int bm) {
 int resident_per_cu(int block_m) { return block_m <= 32 ? 4 : block_m == 64 ? 3 : block_m == 128 ? 2 : 1; }
 
 int n_tiles_of(int N, int nr, int waves) {
-  const int tiles_per_wg = nr * waves;
+  const int tiles_per_wg = nr == 1 ? 1 : nr * waves;   // nr 1: the waves split K, not N
   return (N / 16 + tiles_per_wg - 1) / tiles_per_wg;
 }
 
@@ -252,6 +252,17 @@ w4a16_config select_indexed(int32_t T, int32_t topk, int32_t E_glob, int32_t E_l
   }
   const int64_t tiles = sampled_blocks(counts, c.block_m) * n_tiles_of(N, c.nr, c.waves);
   c.split_k = choose_split(tiles, c.block_m, K);
+  // A grid this small would split K four or more ways: one 16-row weight
+  // tile per workgroup with its waves splitting K instead (partials meet in
+  // LDS, no global reduction).  Measured on MI355X, TP8 gate/up (N = 512,
+  // K = 7168): T = 1 14.6 -> 9.0 us (K split 8 ways -> waves splitting K);
+  // T = 16 (split 2) 49 against 79 us and T = 128 146 against 288 us, so
+  // only where the split would reach 4.
+  if (c.block_m == 16 && c.split_k >= 4 && K % 128 == 0) {
+    c.nr = 1;
+    c.waves = w4a16::kKwWaves;
+    c.split_k = 1;
+  }
   return c;
 }
 
@@ -336,6 +347,8 @@ w4a16_status check_config(const w4a16_config& c, int route, int epi, int K) {
     return fail(W4A16_ERR_UNSUPPORTED, "stream-K (split_k = 0) is built for indexed routing only");
   if (c.split_k > 1 && c.split_k > chunks_of(K))
     return fail(W4A16_ERR_UNSUPPORTED, "split_k %d exceeds the %d 128-K chunks of K = %d", c.split_k, chunks_of(K), K);
+  if (c.nr == 1 && (c.split_k != 1 || K % 128))
+    return fail(W4A16_ERR_UNSUPPORTED, "nr = 1 (waves splitting K) needs split_k = 1 and K a multiple of 128");
   if (!w4a16::gemm_config_supported(route, epi, c.block_m / 16, c.nr, c.waves, c.stages))
     return fail(W4A16_ERR_UNSUPPORTED, "tile config block_m=%d nr=%d waves=%d stages=%d not built", c.block_m,
                 c.nr, c.waves, c.stages);
@@ -437,13 +450,20 @@ void attach_split(w4a16::GemmParams& p, const w4a16_config& c, const Workspace& 
   }
 }
 
-// Upper bound of the routed blocks of an indexed call: every local expert with
-// rows adds at most one partial block, and there are at most T * topk local
-// slots (so at most that many experts with rows).
+// Upper bound of the tiles of block_m rows that hold routed rows in an
+// indexed call: the align writes the experts' segments from position 0, each
+// rounded up to the routing's block_m R, so num_tokens_padded is at most
+// slots + (R - 1) per expert with rows, and there are at most T * topk local
+// slots (so at most that many experts with rows).  Every tile past it is
+// padding, so it also bounds the launch grid: the over-allocated capacity
+// (one block of padding per local expert) would otherwise launch mostly
+// empty workgroups -- 361 blocks for the 8 rows of one token over 384
+// experts.
 int64_t indexed_block_bound(const w4a16_indexed_routing& r, int32_t block_m) {
   const int64_t slots = (int64_t)r.T * r.topk;
-  return std::min<int64_t>(r.capacity / std::max(block_m, 1),
-                           (slots + block_m - 1) / block_m + std::min<int64_t>(r.E_loc, slots));
+  const int64_t b = std::max(block_m, 1);
+  const int64_t per_expert = std::max<int64_t>(r.block_m / b, 1);   // tiles of one routed block
+  return std::min<int64_t>(r.capacity / b, (slots + b - 1) / b + per_expert * std::min<int64_t>(r.E_loc, slots));
 }
 
 // Workgroups of this config the current device keeps resident (stream-K
@@ -753,7 +773,7 @@ w4a16_status moe_gemm_impl(const w4a16_weight_desc* desc, const void* packed_w, 
   p.a_row_div = a_layout == W4A16_A_TOKEN ? r.topk : a_layout == W4A16_A_SLOT ? 1 : 0;
   p.slot_weight = topk_weights;
   p.expert_shift = tile_shift(c, r);
-  p.grid_blocks = (int32_t)(r.capacity / c.block_m);
+  p.grid_blocks = (int32_t)indexed_block_bound(r, c.block_m);
   if (c.split_k == 0) p.sk_partial = reinterpret_cast<float*>(ws + wl.counters + wl.slices + wl.combine);
   else attach_split(p, c, wl, ws);
   // Tokens with exactly one local slot: the GEMM stores bf16(w * acc) as their
@@ -869,7 +889,13 @@ w4a16_status w4a16_moe_gate_up_silu(const w4a16_weight_desc* desc, const void* p
   w4a16_config c{};
   st = indexed_call_config(r, desc, cfg, false, &c);
   if (st != W4A16_OK) return st;
-  if (!cfg) c.split_k = 1;  // the fused epilogue runs whole tiles
+  if (!cfg) {
+    c.split_k = 1;  // the fused epilogue runs whole tiles
+    if (c.nr == 1) {  // ... in gate / up pairs: the two-tile general kernel
+      c.nr = 2;
+      c.waves = 4;
+    }
+  }
   if (c.split_k != 1) return fail(W4A16_ERR_UNSUPPORTED, "the fused SiLU gate/up call runs one workgroup per tile (split_k = 1)");
   if (c.nr % 2) return fail(W4A16_ERR_UNSUPPORTED, "the fused SiLU gate/up call needs an even nr (gate and up tiles in pairs)");
   st = check_config(c, W4A16_ROUTE_INDEXED, w4a16::kEpiSilu, desc->K);
@@ -884,7 +910,7 @@ w4a16_status w4a16_moe_gate_up_silu(const w4a16_weight_desc* desc, const void* p
   p.sentinel = r.T * r.topk;
   p.a_row_div = r.topk;
   p.expert_shift = tile_shift(c, r);
-  p.grid_blocks = (int32_t)(r.capacity / c.block_m);
+  p.grid_blocks = (int32_t)indexed_block_bound(r, c.block_m);
   hipError_t e = w4a16::launch_gemm(w4a16::kRouteIndexed, w4a16::kEpiSilu, c.block_m / 16, c.nr, c.waves,
                                     c.stages, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gate_up_silu launch");
@@ -1140,7 +1166,7 @@ w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* pac
   p.a_row_div = a_layout == W4A16_A_TOKEN ? r.topk : a_layout == W4A16_A_SLOT ? 1 : 0;
   p.slot_weight = topk_weights;
   p.expert_shift = tile_shift(c, r);
-  p.grid_blocks = (int32_t)(r.capacity / c.block_m);
+  p.grid_blocks = (int32_t)indexed_block_bound(r, c.block_m);
   hipError_t e = w4a16::launch_mx_gemm(epi, c.block_m / 16, c.nr, c.waves, c.stages, p, s);
   if (e != hipSuccess) return hip_fail(e, "mxfp4_moe_gemm launch");
   if (combine) {
@@ -1207,7 +1233,7 @@ w4a16_status w4a16_mxfp4_gate_up_silu(const w4a16_weight_desc* desc, const void*
   p.sentinel = r.T * r.topk;
   p.a_row_div = r.topk;
   p.expert_shift = tile_shift(c, r);
-  p.grid_blocks = (int32_t)(r.capacity / c.block_m);
+  p.grid_blocks = (int32_t)indexed_block_bound(r, c.block_m);
   hipError_t e = w4a16::launch_mx_gemm(w4a16::kEpiSiluMx, c.block_m / 16, c.nr, c.waves, c.stages, p,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mxfp4_gate_up_silu launch");

@@ -79,6 +79,9 @@ struct GemmParams {
 // XCD-grouped block order (block_of in tile_common.hpp) for blocks with
 // 2 .. kXcdGroupMaxTiles N tiles (or N-tile groups) and K not split.
 constexpr int kXcdGroupMaxTiles = 4;
+// waves of the K-split tile (nr = 1: one 16-row weight tile per workgroup,
+// its waves splitting K; moe_gemm_kwave_kernel)
+constexpr int kKwWaves = 8;
 int xcd_group_for(int split, int per_block);
 
 // m_tiles: 16-row token tiles per block (block_m / 16); nr: 16-row weight
