@@ -174,6 +174,12 @@ def test_wide_tile_selection(L):
     ep8 = W.select(8192, 8, 384, 48, 4096, 7168)
     assert (ep8.block_m, ep8.nr, ep8.waves, ep8.split_k) == (256, 2, 8, 1)
     assert W.select(4096, 8, 384, 384, 512, 7168).block_m == 128        # 85 rows per expert
+    # the padded-rows fit: 127.1 rows fit one 128-row block, 130 need 144 rows -> the 256-row tile;
+    # 300 rows fit two blocks of 160 (-> 256), as do 512 (two of 256)
+    assert W.select(6100, 8, 384, 48, 4096, 7168).block_m == 128
+    assert W.select(6240, 8, 384, 48, 4096, 7168).block_m == 256
+    assert W.select(14400, 8, 384, 48, 4096, 7168).block_m == 256
+    assert W.select(24576, 8, 384, 48, 4096, 7168).block_m == 256
     assert W.select(8192, 8, 384, 48, 4096, 7000).block_m == 128        # K not a multiple of 128
     assert W.mxfp4_select(8192, 8, 384, 48, 4096, 7168).block_m == 64   # the A4W4 rule is unchanged
     c = _lib.Config()

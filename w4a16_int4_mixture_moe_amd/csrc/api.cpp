@@ -130,8 +130,10 @@ bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm =
 //   - decode side (tok_e < kPrefillTokE): sample per-expert counts, pick the
 //     smallest block_m whose total block count is within 2 % of the minimum
 //     (smaller blocks keep fewer accumulators live and more waves resident);
-//   - prefill side: block_m 128 (largest tile the accumulators allow), two
-//     weight tiles per wave (measured faster than four at 128 rows);
+//   - prefill side: the padded expert rows fitted under the largest tile
+//     (fit_padded_rows: the fewest blocks per expert of at most that many
+//     rows, each block's rows rounded up to 16), rounded up to a built tile:
+//     128 rows, or 256 where K allows the 256-row prefill tile;
 //   - split_k doubles while the doubled grid stays within 4/5 of one round
 //     of resident workgroups and each slice keeps kMinSliceChunks chunks
 //     (measured on MI355X, gate/up K = 7168: TP8 T = 1, 32 tiles, 32.3 us
@@ -151,6 +153,15 @@ constexpr double kPrefillTokE = 48.0;
 // tile was 5-7 % slower than on the 128-row one, and grouped masked calls
 // (up to 512 rows per group) 20 % slower, so neither takes it.
 constexpr double kWideTokE = 128.0;
+
+// Rows per block when an expert's tok_e rows are split into the fewest
+// blocks of at most max_rows rows, each rounded up to the 16-row token tile
+// (the post's padded-rows fit, section "H200 prefill and TP8").
+int fit_padded_rows(double tok_e, int max_rows) {
+  const int rows = std::max(1, (int)std::ceil(tok_e));
+  const int blocks = (rows + max_rows - 1) / max_rows;
+  return (int)round_up((rows + blocks - 1) / blocks, 16);
+}
 // A4W4: above this many rows per expert the MXFP4 GEMM takes 64-row blocks
 // where the W4A16 rule gives 128 (measured on MI355X, step time: EP8 / EP16
 // prefill shares 5 % / 9 % faster at 64; at 85 rows per expert, TP8 T = 4096,
@@ -223,10 +234,12 @@ w4a16_config select_indexed(int32_t T, int32_t topk, int32_t E_glob, int32_t E_l
   if (force_block_m > 0) {
     c.block_m = force_block_m;
     if (c.block_m == 256 && (combine || K % 128)) c.block_m = 128;
-  } else if (tok_e >= kWideTokE && K % 128 == 0) {
-    c.block_m = 256;
   } else if (tok_e >= kPrefillTokE) {
-    c.block_m = 128;
+    // the fitted rows rounded up to a built tile: above 128 rows the 256-row
+    // tile, whose lower bound is kWideTokE (the fit exceeds 128 rows exactly
+    // when tok_e does, up to 256)
+    const int max_rows = K % 128 == 0 ? 256 : 128;
+    c.block_m = fit_padded_rows(tok_e, max_rows) > 128 && tok_e >= kWideTokE ? 256 : 128;
   } else {
     const int cands[3] = {16, 32, 64};
     int64_t best = INT64_MAX;
