@@ -290,11 +290,7 @@ class IndexedStep:
             self.cfg2 = override(M.indexed_config(self.routing, self.p2, combine=True))
             self.cfg2.combine_cols = args.combine_cols
             if self.fused:
-                # what the fused call chooses for itself: whole tiles, gate /
-                # up tiles in pairs (nr 1 falls back to the two-tile kernel)
-                self.cfg1.split_k = 1
-                if self.cfg1.nr == 1 and not args.nr:
-                    self.cfg1.nr, self.cfg1.waves = 2, 4
+                self.cfg1.split_k = 1   # what the fused call chooses for itself: whole tiles
         self.h = torch.empty(T * k, sh.N1, dtype=torch.bfloat16, device=dev)
         self.y = torch.empty(T, sh.N2, dtype=torch.bfloat16, device=dev)
         z = lambda n: torch.zeros(max(16, n), dtype=torch.uint8, device=dev)
@@ -313,8 +309,9 @@ class IndexedStep:
         self.inter_mx = (M.MXRows(torch.zeros(cap, sh.N1 // 4, dtype=torch.uint8, device=dev),
                                   torch.zeros(cap, sh.N1 // 64, dtype=torch.uint8, device=dev))
                          if self.fused and self.mx else None)
-        if self.fused and (sh.K2 != sh.N1 // 2 or self.cfg1.nr % 2 or (self.mx and self.cfg1.nr != 4)):
-            raise SystemExit("--fused needs K2 = N1 / 2 and an even nr (4 with --mx)")
+        if self.fused and (sh.K2 != sh.N1 // 2 or (self.cfg1.nr % 2 and self.cfg1.nr != 1)
+                           or (self.mx and self.cfg1.nr != 4)):
+            raise SystemExit("--fused needs K2 = N1 / 2 and an even nr or 1 (4 with --mx)")
         self.L = M.load()
         self._ctypes = ctypes
 

@@ -185,8 +185,9 @@ typedef struct {
   int32_t nr;        /* 16-row weight tiles per wave: 2 or 4; or 1: one
                         16-row weight tile per workgroup whose waves (8)
                         split K and sum their partials in LDS (block_m 16,
-                        split_k 1, K a multiple of 128, indexed routing,
-                        per-slot or combine epilogue) */
+                        split_k 1, K a multiple of 128, indexed routing; in
+                        the fused SiLU call one gate / up tile pair per
+                        workgroup) */
   int32_t waves;     /* waves per workgroup: 4 (8 for some tiles) */
   int32_t split_k;   /* 1: one workgroup per (block, N tile), whole K;
                         2, 4, 8, 16: that many workgroups per tile, each over
@@ -366,8 +367,8 @@ w4a16_status w4a16_moe_gemm_noalloc(const w4a16_weight_desc* desc, const void* p
  *               uses them).
  *  cfg        : NULL: w4a16_indexed_config for the routing's shape and
  *               block_m, without splitting; one workgroup per tile
- *               (split_k = 1), nr even.  A config of another routing kind:
- *               ERR_ARG.
+ *               (split_k = 1), nr even or 1.  A config of another routing
+ *               kind: ERR_ARG.
  * Sizes: x_rows * K * 2 bytes at most 4 GiB (ERR_SHAPE).
  * Pointers 16-byte aligned.
  * Errors: ERR_ARG, ERR_LAYOUT (not a gate/up weight), ERR_SHAPE,

@@ -252,6 +252,11 @@ def test_gemm_argument_errors(L, monkeypatch):
     assert call(cfg=ctypes.byref(W.config(32, 2, split_k=2))) == -8     # split needs workspace
     assert call(cfg=ctypes.byref(W.config(32, 2, kind="contiguous"))) == -1   # config of another kind
     assert call(cfg=ctypes.byref(W.config(32, 2, combine_cols=40)), w=P) == -1  # pass width not a multiple of 16
+    # nr 1 (waves splitting K): block_m 16, eight waves, split_k 1, K a multiple of 128
+    assert call(cfg=ctypes.byref(W.config(16, 1, 8, split_k=2))) == -4
+    assert call(cfg=ctypes.byref(W.config(16, 1, 4))) == -4
+    assert call(cfg=ctypes.byref(W.config(32, 1, 8))) == -4
+    assert call(d=W.weight_desc(8, 64, 224), cfg=ctypes.byref(W.config(16, 1, 8))) == -4
     bad = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 4, 64)
     assert call(r=bad) == -3                                             # E_loc != weight experts
     no_eg = _lib.IndexedRouting(P, P, P, 1024, 32, 64, 2, P, 0, 8, 0)
@@ -298,6 +303,7 @@ def test_gate_up_silu_argument_errors(L):
     assert call(plain, W.config(32, 2)) == -3                            # weight not gate/up packed
     assert call(gated, W.config(32, 2, split_k=0)) == -4                 # one workgroup per tile only
     assert call(gated, W.config(32, 2, split_k=2)) == -4
+    assert call(gated, W.config(32, 3)) == -4                            # odd nr other than 1
     assert call(gated, W.config(64, 2)) == -3                            # block_m does not divide the routing's
     assert call(gated, W.config(32, 2, kind="masked")) == -1             # config of another kind
 

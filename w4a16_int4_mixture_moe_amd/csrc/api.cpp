@@ -902,15 +902,10 @@ w4a16_status w4a16_moe_gate_up_silu(const w4a16_weight_desc* desc, const void* p
   w4a16_config c{};
   st = indexed_call_config(r, desc, cfg, false, &c);
   if (st != W4A16_OK) return st;
-  if (!cfg) {
-    c.split_k = 1;  // the fused epilogue runs whole tiles
-    if (c.nr == 1) {  // ... in gate / up pairs: the two-tile general kernel
-      c.nr = 2;
-      c.waves = 4;
-    }
-  }
+  if (!cfg) c.split_k = 1;  // the fused epilogue runs whole tiles
   if (c.split_k != 1) return fail(W4A16_ERR_UNSUPPORTED, "the fused SiLU gate/up call runs one workgroup per tile (split_k = 1)");
-  if (c.nr % 2) return fail(W4A16_ERR_UNSUPPORTED, "the fused SiLU gate/up call needs an even nr (gate and up tiles in pairs)");
+  if (c.nr != 1 && c.nr % 2)
+    return fail(W4A16_ERR_UNSUPPORTED, "the fused SiLU gate/up call needs an even nr, or 1 (gate and up tiles in pairs)");
   st = check_config(c, W4A16_ROUTE_INDEXED, w4a16::kEpiSilu, desc->K);
   if (st != W4A16_OK) return st;
   st = check_tile_rows(c, r);
@@ -924,6 +919,7 @@ w4a16_status w4a16_moe_gate_up_silu(const w4a16_weight_desc* desc, const void* p
   p.a_row_div = r.topk;
   p.expert_shift = tile_shift(c, r);
   p.grid_blocks = (int32_t)indexed_block_bound(r, c.block_m);
+  if (c.nr == 1) p.n_tiles = p.NT / 2;   // one (gate, up) tile pair per workgroup
   hipError_t e = w4a16::launch_gemm(w4a16::kRouteIndexed, w4a16::kEpiSilu, c.block_m / 16, c.nr, c.waves,
                                     c.stages, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gate_up_silu launch");

@@ -537,30 +537,31 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p
 }
 
 // Few routed rows (block_m 16) and a grid too small for the machine: one
-// 16-row weight tile of one routed block per workgroup, its NW waves
-// splitting K (wave w takes chunks [w KC / NW, (w + 1) KC / NW)).  Each wave
-// keeps up to kKwBatch chunks of weights, scales and activation fragments in
-// flight straight into registers (no LDS staging: the B operand of lane l is
-// 64 contiguous bytes of its token row per chunk), and the waves' partial
-// sums meet in LDS, summed in wave order, so no global split-K reduction
-// (slices, arrival counter, second pass) sits on the path.  The product is
-// the MFMA kernel's: bf16 weights dequantised by dequant8, fp32
-// accumulation, one rounding at the store; only the order of the K sums
-// differs from the other tiles (per wave, then over waves).  Indexed routing,
-// per-slot or weighted epilogue.
-constexpr int kKwBatch = 8;
-
-template <int NW>
+// 16-row weight tile of one routed block per workgroup (two, gate and up,
+// for the fused SiLU epilogue), its NW waves splitting K (wave w takes
+// chunks [w KC / NW, (w + 1) KC / NW)).  Each wave keeps a batch of chunks of
+// weights, scales and activation fragments in flight straight into
+// registers (no LDS staging: the B operand of lane l is 64 contiguous bytes
+// of its token row per chunk), and the waves' partial sums meet in LDS,
+// summed in wave order, so no global split-K reduction (slices, arrival
+// counter, second pass) sits on the path.  The product is the MFMA
+// kernel's: bf16 weights dequantised by dequant8, fp32 accumulation, one
+// rounding at the store; only the order of the K sums differs from the
+// other tiles (per wave, then over waves).  Indexed routing; per-slot,
+// weighted or fused SiLU epilogue.
+template <int NT, int NW>
 struct KwSmem {
   int row[16];
   int out[16];
   float w[16];
-  f32x4_t red[NW][kWave];
+  f32x4_t red[NW][NT][kWave];
 };
 
 template <int NW, int EPI>
 __global__ __launch_bounds__(NW * kWave) void moe_gemm_kwave_kernel(const GemmParams p) {
-  __shared__ __attribute__((aligned(16))) KwSmem<NW> sm;
+  constexpr int NT = EPI == kEpiSilu ? 2 : 1;     // weight tiles per workgroup
+  constexpr int KB = 8 / NT;                       // chunks in flight per wave
+  __shared__ __attribute__((aligned(16))) KwSmem<NT, NW> sm;
   int mb, nt;
   if (!block_of(p, blockIdx.x, p.n_tiles, mb, nt)) return;
   const int expert = setup_rows<1, NW, kRouteIndexed, EPI>(p, mb, sm);
@@ -570,50 +571,66 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_kwave_kernel(const GemmPa
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int KC = p.KC;
   const int c0 = (int)((int64_t)wave * KC / NW), c1 = (int)((int64_t)(wave + 1) * KC / NW);
-  const int64_t tile = (int64_t)expert * p.w_tiles + nt;
-  const gptr_t wbase = uniform_ptr(p.packed_w + tile * KC * kWave) + lane * 16;
-  const gptr_t sbase = uniform_ptr(p.packed_s + tile * ((KC + 1) / 2) * kWave) + lane * 4;
+  gptr_t wbase[NT], sbase[NT];
+#pragma unroll
+  for (int r = 0; r < NT; ++r) {
+    const int64_t tile = (int64_t)expert * p.w_tiles + min(NT * nt + r, p.NT - 1);
+    wbase[r] = uniform_ptr(p.packed_w + tile * KC * kWave) + lane * 16;
+    sbase[r] = uniform_ptr(p.packed_s + tile * ((KC + 1) / 2) * kWave) + lane * 4;
+  }
   // B operand: lane l supplies token row l % 16 at K 32 (l / 16) .. + 31 of
   // each chunk, the same K positions its weight words cover (step j: bytes
   // 16 j .. 16 j + 15 of those 64)
   const int arow = sm.row[lane & 15];
   const gptr_t abase = uniform_ptr(p.a) + (int64_t)max(arow, 0) * p.K * 2 + (lane >> 4) * 64;
   const DequantMasks masks = make_dequant_masks();
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int cb = c0; cb < c1; cb += kKwBatch) {
-    u32x4_t w[kKwBatch];
-    uint32_t sw[kKwBatch];
-    bf16x8_t x[kKwBatch][4];
+  f32x4_t acc[NT];
 #pragma unroll
-    for (int i = 0; i < kKwBatch; ++i) {
+  for (int r = 0; r < NT; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int cb = c0; cb < c1; cb += KB) {
+    u32x4_t w[KB][NT];
+    uint32_t sw[KB][NT];
+    bf16x8_t x[KB][4];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
       const int c = min(cb + i, c1 - 1);          // past c1: a repeated load, not used
-      w[i] = gload_u32x4(wbase + (int64_t)c * (kWave * 16));
-      sw[i] = gload_u32(sbase + (int64_t)(c >> 1) * (kWave * 4));
+#pragma unroll
+      for (int r = 0; r < NT; ++r) {
+        w[i][r] = gload_u32x4(wbase[r] + (int64_t)c * (kWave * 16));
+        sw[i][r] = gload_u32(sbase[r] + (int64_t)(c >> 1) * (kWave * 4));
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         x[i][j] = arow >= 0 ? __builtin_bit_cast(bf16x8_t, gload_u32x4(abase + (int64_t)c * (kChunk * 2) + 16 * j))
                             : bf16x8_t{};
     }
 #pragma unroll
-    for (int i = 0; i < kKwBatch; ++i) {
+    for (int i = 0; i < KB; ++i) {
       const int c = cb + i;
       if (c >= c1) break;
-      const float sv = __builtin_bit_cast(float, (c & 1) ? (sw[i] & 0xFFFF0000u) : (sw[i] << 16));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8_t A = dequant8(w[i][j], sv, -1032.0f * sv, 0.0625f * sv, -72.0f * sv, masks);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, x[i][j], acc, 0, 0, 0);
+      for (int r = 0; r < NT; ++r) {
+        const float sv = __builtin_bit_cast(float, (c & 1) ? (sw[i][r] & 0xFFFF0000u) : (sw[i][r] << 16));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8_t A = dequant8(w[i][r][j], sv, -1032.0f * sv, 0.0625f * sv, -72.0f * sv, masks);
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, x[i][j], acc[r], 0, 0, 0);
+        }
       }
     }
   }
-  sm.red[wave][lane] = acc;
+#pragma unroll
+  for (int r = 0; r < NT; ++r) sm.red[wave][r][lane] = acc[r];
   __syncthreads();
   if (wave != 0) return;
-  f32x4_t tot = sm.red[0][lane];
+  f32x4_t tot[NT][1];
 #pragma unroll
-  for (int v = 1; v < NW; ++v) tot += sm.red[v][lane];
-  const f32x4_t t1[1][1] = {{tot}};
-  epilogue<1, 1, 1, EPI>(p, sm, nt, 1u, t1);
+  for (int r = 0; r < NT; ++r) {
+    tot[r][0] = sm.red[0][r][lane];
+#pragma unroll
+    for (int v = 1; v < NW; ++v) tot[r][0] += sm.red[v][r][lane];
+  }
+  epilogue<1, NT, 1, EPI>(p, sm, nt, 1u, tot);
 }
 
 // Work partition shared by the stream-K kernel and its fix-up: `units`
@@ -875,6 +892,7 @@ static KernelSet find_kernels(int route, int epi, int m_tiles, int nr, int waves
     KernelSet k;
     if (epi == kEpiStore) k.classic = moe_gemm_kwave_kernel<kKwWaves, kEpiStore>;
     if (epi == kEpiWeighted) k.classic = moe_gemm_kwave_kernel<kKwWaves, kEpiWeighted>;
+    if (epi == kEpiSilu) k.classic = moe_gemm_kwave_kernel<kKwWaves, kEpiSilu>;
     return k;
   }
 #define W4A16_CASE(MT_, NR_, NW_, D_) \
