@@ -299,22 +299,49 @@ __device__ __forceinline__ void pf_mainloop(const GemmParams& p, PfSmem<C::BM>& 
           for (int r = 0; r < NR; ++r) A[r] = An[r];
       }
     } else {
+      // four weight tiles per wave: registers for one activation fragment
+      // read ahead (the next token tile's, under the current one's four
+      // MFMAs), not for the next step's dequant.  Measured against reading
+      // each fragment where it is used: TP8 T = 4096 gate/up 320 -> 306 us,
+      // grouped contiguous / masked 880 / 962 -> 858 / 940 us; the N-tile-loop
+      // form (SHORT) spills with it and stays as it was (its down + combine
+      // 486 against 501 us)
+      if constexpr (!SHORT) {
+        bf16x8_t B = operand(0, 0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x8_t A[NR];
-        dequant_step(j, A);
+        for (int j = 0; j < 4; ++j) {
+          bf16x8_t A[NR];
+          dequant_step(j, A);
 #pragma unroll
-        for (int t = 0; t < NA; ++t) {
-          const bf16x8_t B = operand(j, t);
+          for (int t = 0; t < NA; ++t) {
+            bf16x8_t Bn = B;
+            if (t + 1 < NA)
+              Bn = operand(j, t + 1);
+            else if (j < 3)
+              Bn = operand(j + 1, 0);
 #pragma unroll
-          for (int r = 0; r < NR; ++r)
-            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r], B, acc[r][t], 0, 0, 0);
+            for (int r = 0; r < NR; ++r)
+              acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r], B, acc[r][t], 0, 0, 0);
+            B = Bn;
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
-        // keep each 32-K step's operands to itself: with four weight tiles
-        // per wave, hoisting the next step's dequant or operand reads above
-        // these MFMAs needs more registers than two waves per SIMD leave (the
-        // second wave covers the latency instead)
-        __builtin_amdgcn_sched_barrier(0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x8_t A[NR];
+          dequant_step(j, A);
+#pragma unroll
+          for (int t = 0; t < NA; ++t) {
+            const bf16x8_t B = operand(j, t);
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+              acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r], B, acc[r][t], 0, 0, 0);
+          }
+          // keep each 32-K step's operands to itself (more registers than
+          // two waves per SIMD leave otherwise)
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     if (has_next) {
