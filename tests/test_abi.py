@@ -354,6 +354,11 @@ def test_selector_splits_k_only_for_underfilled_grids(L):
     assert (t1.block_m, t1.nr, t1.waves, t1.split_k) == (16, 1, 8, 1)
     assert W.select(1, 8, 384, 384, 512, 7000).split_k == 8       # K not a multiple of 128: K slices
     assert W.select(1, 8, 384, 384, 7168, 256).split_k == 1       # its down projection: K = 256, 2 chunks
+    # 16-row blocks over K = 256 take four weight tiles per wave while the grid keeps 2 per CU
+    assert W.select(1, 8, 384, 384, 7168, 256).nr == 2            # 9 blocks x 28 tiles: too few
+    assert W.select(16, 8, 384, 384, 7168, 256).nr == 4
+    assert W.select(128, 8, 384, 384, 7168, 256).nr == 4
+    assert W.select(1024, 8, 384, 384, 7168, 256).nr == 2         # 32-row blocks
     assert W.select(4096, 8, 384, 384, 512, 7168).split_k == 1    # prefill-side grids fill the machine
     assert W.select(8192, 8, 384, 48, 4096, 7168).split_k == 1
 

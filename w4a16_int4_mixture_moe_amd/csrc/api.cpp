@@ -265,6 +265,14 @@ w4a16_config select_indexed(int32_t T, int32_t topk, int32_t E_glob, int32_t E_l
   }
   const int64_t tiles = sampled_blocks(counts, c.block_m) * n_tiles_of(N, c.nr, c.waves);
   c.split_k = choose_split(tiles, c.block_m, K);
+  // 16-row blocks over a short K (at most two chunks: the down projection of
+  // a TP8 share): four weight tiles per wave spread each block's staging over
+  // twice the weight rows, while the grid keeps two workgroups per CU.
+  // Measured on MI355X, TP8 down (N = 7168, K = 256): T = 16 35.9 -> 34.3 us,
+  // T = 128 107.5 -> 99.6 us; T = 1 (252 workgroups) 10.5 against 11.0 us.
+  if (c.block_m == 16 && K <= 256 && c.split_k == 1 &&
+      sampled_blocks(counts, 16) * n_tiles_of(N, 4, c.waves) >= 2 * (int64_t)kCUs)
+    c.nr = 4;
   // A grid this small would split K four or more ways: one 16-row weight
   // tile per workgroup with its waves splitting K instead (partials meet in
   // LDS, no global reduction).  Measured on MI355X, TP8 gate/up (N = 512,
