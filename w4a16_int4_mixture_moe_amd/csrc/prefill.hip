@@ -1,8 +1,10 @@
 // Prefill-side W4A16 MoE GEMM tiles for gfx950: 128 routed rows x 256 weight
 // rows per workgroup (four waves, two workgroups per CU), or 256 routed rows x
-// 256 weight rows (eight waves, one workgroup per CU).  The description below
-// is the 128-row tile's; the 256-row one gives each wave two weight tiles of
-// all sixteen token tiles instead of four of eight.
+// 256 weight rows (eight waves, one workgroup per CU; an expert of up to 256
+// rows then streams its weights once).  The description below is the
+// 128-row tile's; the 256-row one gives each wave two weight tiles of all
+// sixteen token tiles instead of four of eight, which leaves registers for a
+// software-pipelined step (see pf_mainloop).
 //
 // Why a separate kernel.  Large routed blocks are MFMA-bound, and on gfx950
 // what limits the MFMA rate in this GEMM is the LDS and register traffic per
@@ -40,7 +42,8 @@
 // Arithmetic is that of moe_gemm_kernel: the same packed weights and scales,
 // dequant8, v_mfma_f32_16x16x32_bf16 with the weights as the A operand, K
 // chunks in order and the four 32-wide MFMA steps of a chunk in order, so the
-// outputs are bit-identical to every other tile configuration.  K must be a
+// outputs are bit-identical to the general kernel's tile configurations
+// (only the tile whose waves split K sums in another order).  K must be a
 // multiple of 128 (the DMA copies whole chunks; other K use the general
 // kernel).
 #include <type_traits>
