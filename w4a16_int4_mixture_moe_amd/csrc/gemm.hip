@@ -926,6 +926,15 @@ hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves, 
   // at once.
   GemmParams q = p;
   q.xcd_group = xcd_group_for(p.split, p.n_tiles);
+  // decode tiles (at most 32 rows) of a block with 32 or more N tiles: groups
+  // of kXcdDecodeGroup N tiles per XCD, so the block's activation rows land in
+  // min(8, n_tiles / 16) L2s instead of all eight (measured on MI355X, EP8
+  // decode gate/up: 2% faster, HBM bytes 1.089x -> 1.030x the weight and
+  // scale bytes).  Not the K-split tile (nr 1): it runs on small grids, where
+  // rounding up to whole groups leaves workgroups idle (T = 1: 0.5 us slower).
+  if (nr > 1 && p.split <= 1 && m_tiles <= 2 && q.n_tiles >= 2 * kXcdDecodeGroup &&
+      q.n_tiles % kXcdDecodeGroup == 0)
+    q.xcd_group = kXcdDecodeGroup;
   const int64_t grid = grid_of(q, q.n_tiles) * std::max(q.split, 1);
   if (grid <= 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidConfiguration;

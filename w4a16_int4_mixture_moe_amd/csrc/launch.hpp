@@ -79,6 +79,8 @@ struct GemmParams {
 // XCD-grouped block order (block_of in tile_common.hpp) for blocks with
 // 2 .. kXcdGroupMaxTiles N tiles (or N-tile groups) and K not split.
 constexpr int kXcdGroupMaxTiles = 4;
+// N tiles of a decode block kept together on one XCD (see launch_gemm)
+constexpr int kXcdDecodeGroup = 16;
 // waves of the K-split tile (nr = 1: one 16-row weight tile per workgroup,
 // its waves splitting K; moe_gemm_kwave_kernel)
 constexpr int kKwWaves = 8;

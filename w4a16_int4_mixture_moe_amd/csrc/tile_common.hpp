@@ -27,27 +27,37 @@ __device__ __forceinline__ int live_blocks(const GemmParams& p) {
 // items are one block's, and the hardware's round-robin dispatch sends
 // consecutive workgroups to different XCDs, so each XCD fetches the block's
 // activation rows into its own L2.  p.xcd_group: items of one block are 8
-// apart, i.e. on one XCD, which then fetches the rows once; w runs over
-// groups of 8 blocks x per items (the launcher rounds the grid up to whole
-// groups) and items past the last block return false.  Used for few items
-// per block only: many workgroups asking one L2 for the same lines at once
-// were measured several times slower.
+// apart, i.e. on one XCD, which then fetches the rows once (1: all `per`
+// items of a block; > 1: groups of xcd_group items, so a block spans
+// per / xcd_group XCDs); w runs over groups of 8 (block, group) pairs x the
+// group's items (the launcher rounds the grid up to whole groups) and items
+// past the last block return false.  Not for many items on one XCD: many
+// workgroups asking one L2 for the same lines at once were measured several
+// times slower (all 32 N tiles of a decode block: 3x).
 __device__ __forceinline__ bool block_of(const GemmParams& p, int w, int per, int& mb, int& j) {
   if (!p.xcd_group) {
     mb = w / per;
     j = w - mb * per;
     return true;
   }
+  // groups of tq consecutive items of a block share an XCD (tq = per: the
+  // whole block; xcd_group > 1: tq = xcd_group, dividing per)
+  const int tq = p.xcd_group == 1 ? per : p.xcd_group;
+  const int parts = per / tq;
   const int k = w >> 3;
-  const int grp = k / per;
-  j = k - grp * per;
-  mb = grp * 8 + (w & 7);
+  const int g = k / tq;
+  const int t = k - g * tq;
+  const int q = g * 8 + (w & 7);
+  mb = q / parts;
+  j = (q - mb * parts) * tq + t;
   return mb < p.grid_blocks;
 }
 
 // Grid of a launch with `per` items per routed block (see block_of).
 inline int64_t grid_of(const GemmParams& p, int per) {
-  return p.xcd_group ? ((int64_t)p.grid_blocks + 7) / 8 * 8 * per : (int64_t)p.grid_blocks * per;
+  if (!p.xcd_group) return (int64_t)p.grid_blocks * per;
+  const int tq = p.xcd_group == 1 ? per : p.xcd_group;
+  return ((int64_t)p.grid_blocks * (per / tq) + 7) / 8 * 8 * tq;
 }
 
 // Fill the block's row tables; returns the block's expert (wave-uniform) or
