@@ -287,7 +287,7 @@ class IndexedStep:
             self.cfg2 = self.cfg1
         else:
             self.cfg1 = override(M.indexed_config(self.routing, self.p1))
-            self.cfg2 = override(M.indexed_config(self.routing, self.p2, combine=True))
+            self.cfg2 = override(M.indexed_config(self.routing, self.p2))
             self.cfg2.combine_cols = args.combine_cols
             if self.fused:
                 self.cfg1.split_k = 1   # what the fused call chooses for itself: whole tiles

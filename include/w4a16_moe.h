@@ -58,7 +58,7 @@ typedef enum {
 const char* w4a16_last_error(void);
 
 /* ABI version of this header (W4A16_ABI_VERSION). */
-#define W4A16_ABI_VERSION 7
+#define W4A16_ABI_VERSION 8
 int32_t w4a16_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -220,14 +220,13 @@ typedef struct {
 
 /* The config w4a16_select gives for indexed routing aligned to block_m (the
  * routing buffers fix block_m; the rest is chosen as w4a16_select does):
- * what w4a16_moe_gemm (combine != 0: with topk_weights) and
- * w4a16_moe_gate_up_silu (combine = 0) use when their cfg is NULL.  A 256-row
- * routing gives the 256-row tile without the combine and 128-row tiles with
- * it (or when K is not a multiple of 128).  Host only; environment overrides
- * W4A16_NR, W4A16_WAVES, W4A16_SPLIT_K, W4A16_STAGES applied.
+ * what w4a16_moe_gemm and w4a16_moe_gate_up_silu use when their cfg is NULL.
+ * A 256-row routing gives the 256-row tile (128-row tiles when K is not a
+ * multiple of 128).  Host only; environment overrides W4A16_NR, W4A16_WAVES,
+ * W4A16_SPLIT_K, W4A16_STAGES applied.
  * Errors: ERR_ARG. */
 w4a16_status w4a16_indexed_config(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N,
-                                  int32_t K, int32_t block_m, int32_t combine, w4a16_config* out);
+                                  int32_t K, int32_t block_m, w4a16_config* out);
 
 /* Choose a config (host only; memoised per argument set, so repeated calls
  * cost about a microsecond).
@@ -237,10 +236,8 @@ w4a16_status w4a16_indexed_config(int32_t T, int32_t topk, int32_t E_glob, int32
  *    the total block count over {16, 32, 64} on a seeded multinomial sample
  *    of the routing (ties to the smaller block); from 48 on, 128 (with K a
  *    multiple of 128: the prefill tile, nr 4); from 128 on with K a
- *    multiple of 128, 256 (the 256-row tile: nr 2, eight waves, split_k 1;
- *    the call with the top-k combine then runs 128-row tiles on the same
- *    routing, see w4a16_indexed_config).  split_k
- *    doubles from 1 while the sampled grid (routed blocks x N tiles x
+ *    multiple of 128, 256 (the 256-row tile: nr 2, eight waves, split_k
+ *    1).  split_k doubles from 1 while the sampled grid (routed blocks x N tiles x
  *    split_k) stays below one round of resident workgroups on 256 CUs and
  *    each slice keeps at least four 128-K chunks; a block_m 16 grid that
  *    would split K four or more ways (K a multiple of 128) takes nr 1 with

@@ -82,11 +82,11 @@ def test_header_compiles_as_c_and_matches_the_binding(tmp_path):
             got[("const", "W4A16_A_SORTED")]) == (_lib.A_TOKEN, _lib.A_SLOT, _lib.A_SORTED)
     assert (got[("const", "W4A16_ROUTE_INDEXED")], got[("const", "W4A16_ROUTE_CONTIGUOUS")],
             got[("const", "W4A16_ROUTE_MASKED")]) == (_lib.ROUTE_INDEXED, _lib.ROUTE_CONTIGUOUS, _lib.ROUTE_MASKED)
-    assert got[("const", "W4A16_ABI_VERSION")] == 7
+    assert got[("const", "W4A16_ABI_VERSION")] == 8
 
 
 def test_version_and_desc(L):
-    assert L.w4a16_abi_version() == 7
+    assert L.w4a16_abi_version() == 8
     d = W.weight_desc(48, 4096, 7168)
     assert (d.K_pad, d.chunks, d.group) == (7168, 56, 32)
     assert d.w_bytes == 48 * 4096 * 7168 // 2
@@ -160,7 +160,7 @@ def test_capacity_and_workspace(L):
     assert _ws(d, r, True, W.config(32, 2, split_k=32)) == 0         # not a split count
     # cfg NULL: the selector's config for the routing's block_m
     c = _lib.Config()
-    assert L.w4a16_indexed_config(10, 8, 384, 4, 7168, 2048, 32, 1, ctypes.byref(c)) == 0
+    assert L.w4a16_indexed_config(10, 8, 384, 4, 7168, 2048, 32, ctypes.byref(c)) == 0
     assert (c.block_m, c.nr, c.waves, c.stages, c.kind) == (32, 2, 4, 2, 0)
     assert _ws(d, r, True) == _ws(d, r, True, c)
     assert c.combine_cols == 0
@@ -168,9 +168,9 @@ def test_capacity_and_workspace(L):
 
 def test_wide_tile_selection(L):
     """From 128 routed rows per expert (K a multiple of 128) the selector
-    aligns the routing to 256 rows: the gate/up runs the 256-row tile (nr 2,
-    eight waves, unsplit), the down projection with the combine 128-row
-    tiles over the same routing, and a workspace sized for those tiles."""
+    aligns the routing to 256 rows: both projections run the 256-row tile
+    (nr 2, eight waves, unsplit), the down projection with the combine on a
+    workspace sized for that tile."""
     ep8 = W.select(8192, 8, 384, 48, 4096, 7168)
     assert (ep8.block_m, ep8.nr, ep8.waves, ep8.split_k) == (256, 2, 8, 1)
     assert W.select(4096, 8, 384, 384, 512, 7168).block_m == 128        # 85 rows per expert
@@ -183,15 +183,15 @@ def test_wide_tile_selection(L):
     assert W.select(8192, 8, 384, 48, 4096, 7000).block_m == 128        # K not a multiple of 128
     assert W.mxfp4_select(8192, 8, 384, 48, 4096, 7168).block_m == 64   # the A4W4 rule is unchanged
     c = _lib.Config()
-    assert L.w4a16_indexed_config(8192, 8, 384, 48, 4096, 7168, 256, 0, ctypes.byref(c)) == 0
+    assert L.w4a16_indexed_config(8192, 8, 384, 48, 4096, 7168, 256, ctypes.byref(c)) == 0
     assert (c.block_m, c.nr, c.waves, c.split_k) == (256, 2, 8, 1)
-    assert L.w4a16_indexed_config(8192, 8, 384, 48, 7168, 2048, 256, 1, ctypes.byref(c)) == 0
-    assert (c.block_m, c.nr, c.waves) == (128, 4, 4)
-    assert L.w4a16_indexed_config(8192, 8, 384, 48, 7168, 2000, 256, 0, ctypes.byref(c)) == 0
+    assert L.w4a16_indexed_config(8192, 8, 384, 48, 7168, 2048, 256, ctypes.byref(c)) == 0
+    assert (c.block_m, c.nr, c.waves, c.split_k) == (256, 2, 8, 1)
+    assert L.w4a16_indexed_config(8192, 8, 384, 48, 7168, 2000, 256, ctypes.byref(c)) == 0
     assert c.block_m == 128                                             # K not a multiple of 128
     d = W.weight_desc(48, 7168, 2048)
     r = _routing(8192, 8, 48, 256)
-    assert _ws(d, r, True) == _ws(d, r, True, W.config(128, 4))
+    assert _ws(d, r, True) == _ws(d, r, True, W.config(256, 2, 8))
     assert _ws(d, r, False) == 0
 
 

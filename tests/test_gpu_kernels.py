@@ -622,13 +622,14 @@ def test_prefill_tile_bit_identical_to_the_general_kernel(K1, K2):
         np.testing.assert_array_equal(y, out["general"][1], err_msg=f"down+combine on the 256-row routing, {tag}")
         h = bits(M.moe_w4a16_gemm(P.d_x, P.p1, r256, cfg=c))
         np.testing.assert_array_equal(h, out["general"][0], err_msg=f"gate/up on the 256-row routing, {tag}")
-    # the calls' own choice (cfg None: the 256-row tile for the gate/up,
-    # 128-row tiles, K-split on this small grid, for the down), K slices and
-    # stream-K over the 256-row routing: within the oracle's tolerance
+    # the calls' own choice (cfg None: the 256-row tile, unsplit, for both
+    # projections), bit-identical; K slices and stream-K over the 256-row
+    # routing: within the oracle's tolerance
     h = M.moe_w4a16_gemm(P.d_x, P.p1, r256)
+    y = M.moe_w4a16_gemm(P.d_a, P.p2, r256, topk_weights=P.d_w)
     np.testing.assert_array_equal(bits(h), out["general"][0], err_msg="gate/up on the 256-row routing, cfg None")
-    _check_indexed(P, h, M.moe_w4a16_gemm(P.d_a, P.p2, r256, topk_weights=P.d_w),
-                   f"256-row routing, cfg None, K1={K1} K2={K2}")
+    np.testing.assert_array_equal(bits(y), out["general"][1], err_msg="down+combine on the 256-row routing, cfg None")
+    _check_indexed(P, h, y, f"256-row routing, cfg None, K1={K1} K2={K2}")
     for c in ((M.config(64, 2, split_k=2),) if K2 >= 256 else ()) + (M.config(128, 2, split_k=0),):
         _check_indexed(P, M.moe_w4a16_gemm(P.d_x, P.p1, r256, cfg=c),
                        M.moe_w4a16_gemm(P.d_a, P.p2, r256, topk_weights=P.d_w, cfg=c),

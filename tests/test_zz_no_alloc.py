@@ -62,8 +62,9 @@ def test_noalloc_matches_the_workspace_entry_point_on_two_calls():
     _compare(P, 77, split, M.config(32, 2, split_k=2))   # second call, smaller input
     _compare(P, 300, plain, plain)
     _compare(P, 41, plain, plain)
-    # a 256-row routing (256-row gate/up tile, 128-row down tiles over it) and
-    # the tile whose waves split K
+    # a 256-row routing (the 256-row tile for both projections; 128-row down
+    # tiles over it) and the tile whose waves split K
+    _compare(P, 300, M.config(256, 2, 8), M.config(256, 2, 8))
     _compare(P, 300, M.config(256, 2, 8), M.config(128, 4))
     _compare(P, 41, M.config(16, 1, 8), M.config(16, 1, 8))
 

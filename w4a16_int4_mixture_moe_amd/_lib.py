@@ -76,7 +76,7 @@ SIGNATURES = {
     "w4a16_moe_align": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P]),
     "w4a16_select": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(Config)]),
     "w4a16_mxfp4_select": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(Config)]),
-    "w4a16_indexed_config": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(Config)]),
+    "w4a16_indexed_config": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(Config)]),
     "w4a16_moe_gemm_workspace_bytes": (_SZ, [ctypes.POINTER(WeightDesc), ctypes.POINTER(IndexedRouting), _I32,
                                              ctypes.POINTER(Config)]),
     "w4a16_moe_gemm": (_I32, [ctypes.POINTER(WeightDesc), _P, _P, _P, _I64, _I32,

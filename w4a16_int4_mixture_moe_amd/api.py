@@ -177,14 +177,13 @@ def config(block_m: int, nr: int, waves: int = 4, split_k: int = 1, stages: int 
     return Config(block_m, nr, waves, split_k, stages, _KINDS[kind], combine_cols)
 
 
-def indexed_config(routing: "Routing", packed: PackedW4, combine: bool = False) -> Config:
-    """The config moe_w4a16_gemm (combine: with topk_weights) and
-    moe_gate_up_silu use when cfg is None: the selector's choice for the
-    routing's shape with the routing's block_m (a 256-row routing takes
-    128-row tiles under the combine)."""
+def indexed_config(routing: "Routing", packed: PackedW4) -> Config:
+    """The config moe_w4a16_gemm and moe_gate_up_silu use when cfg is None:
+    the selector's choice for the routing's shape with the routing's
+    block_m."""
     c = Config()
     check(load().w4a16_indexed_config(routing.T, routing.topk, routing.E_glob, routing.E_loc, packed.N, packed.K,
-                                      routing.block_m, int(bool(combine)), ctypes.byref(c)))
+                                      routing.block_m, ctypes.byref(c)))
     return c
 
 

@@ -144,14 +144,15 @@ bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm =
 // tile from its register use), so the choice is deterministic and available
 // without a device.
 constexpr double kPrefillTokE = 48.0;
-// Routed rows per expert from which the routing takes 256-row blocks: the
-// gate/up runs the 256-row prefill tile (an expert of up to 256 rows streams
-// its weights once), the down projection + combine 128-row tiles over the
-// same routing.  Measured on MI355X at 171 rows per expert (T = 8192, top-8
-// of 384, Zipf-skewed), against 128-row blocks: gate/up EP8 595 -> 544 us,
-// EP16 384 -> 356 us, EP32 180 -> 144 us; the down + combine on the 256-row
-// tile was 5-7 % slower than on the 128-row one, and grouped masked calls
-// (up to 512 rows per group) 20 % slower, so neither takes it.
+// Routed rows per expert from which the routing takes 256-row blocks: both
+// projections run the 256-row prefill tile (an expert of up to 256 rows
+// streams its weights once).  Measured on MI355X at 171 rows per expert
+// (T = 8192, top-8 of 384, Zipf-skewed), against 128-row blocks: gate/up
+// EP8 595 -> 544 us, EP16 384 -> 356 us, EP32 180 -> 144 us; on the
+// software-pipelined 256-row tile the down + combine against 128-row tiles
+// on the same routing: EP8 352 -> 344 us, EP16 221 -> 210 us, EP32 135 ->
+// 133 us.  Grouped masked calls (up to 512 rows per group) were 20 % slower
+// on it, so they keep 128.
 constexpr double kWideTokE = 128.0;
 
 // Rows per block when an expert's tok_e rows are split into the fewest
@@ -220,10 +221,10 @@ std::vector<int> sampled_counts(int32_t T, int32_t topk, int32_t E_glob, int32_t
 }
 
 // Indexed config; block_m chosen by the tok_e rule, or, when the routing
-// buffers already fix their block_m (force_block_m > 0), that block_m or
-// (256-row routing under a top-k combine) the 128-row tile.
+// buffers already fix their block_m (force_block_m > 0), that block_m (a
+// 256-row routing with K not a multiple of 128: the 128-row tile).
 w4a16_config select_indexed(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N, int32_t K,
-                            int32_t force_block_m, bool combine) {
+                            int32_t force_block_m) {
   w4a16_config c{};
   c.kind = W4A16_ROUTE_INDEXED;
   c.waves = 4;
@@ -233,7 +234,7 @@ w4a16_config select_indexed(int32_t T, int32_t topk, int32_t E_glob, int32_t E_l
   const std::vector<int> counts = sampled_counts(T, topk, E_glob, E_loc);
   if (force_block_m > 0) {
     c.block_m = force_block_m;
-    if (c.block_m == 256 && (combine || K % 128)) c.block_m = 128;
+    if (c.block_m == 256 && K % 128) c.block_m = 128;
   } else if (tok_e >= kPrefillTokE) {
     // the fitted rows rounded up to a built tile: above 128 rows the 256-row
     // tile, whose lower bound is kWideTokE (the fit exceeds 128 rows exactly
@@ -495,9 +496,8 @@ int resident_workgroups(const w4a16_config& c, int epi) {
 
 // select_indexed, memoised per argument set (no environment overrides)
 w4a16_config cached_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N, int32_t K,
-                           int32_t kind, int32_t expected_m, int32_t force_block_m, bool combine = false) {
-  const SelectKey key =
-      std::make_tuple(T, topk, E_glob, E_loc, N, K, kind * 1024 + (combine ? 512 : 0) + force_block_m, expected_m);
+                           int32_t kind, int32_t expected_m, int32_t force_block_m) {
+  const SelectKey key = std::make_tuple(T, topk, E_glob, E_loc, N, K, kind * 1024 + force_block_m, expected_m);
   {
     std::lock_guard<std::mutex> g(g_cache_mu);
     auto it = g_cache.find(key);
@@ -509,7 +509,7 @@ w4a16_config cached_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_lo
   else if (kind == W4A16_ROUTE_MASKED)
     c = select_masked(T, E_loc, N, K, expected_m);
   else
-    c = select_indexed(T, topk, E_glob, E_loc, N, K, force_block_m, combine);
+    c = select_indexed(T, topk, E_glob, E_loc, N, K, force_block_m);
   std::lock_guard<std::mutex> g(g_cache_mu);
   g_cache[key] = c;
   return c;
@@ -609,13 +609,13 @@ namespace {
 // The indexed config of a call: cfg, or the selector's choice for the
 // routing's shape and block_m with environment overrides applied.
 w4a16_status indexed_call_config(const w4a16_indexed_routing& r, const w4a16_weight_desc* d, const w4a16_config* cfg,
-                                 bool combine, w4a16_config* out) {
+                                 w4a16_config* out) {
   if (cfg) {
     *out = *cfg;
     return W4A16_OK;
   }
   if (r.E_glob <= 0) return fail(W4A16_ERR_ARG, "routing.E_glob must be positive (it steers the config when cfg is NULL)");
-  *out = cached_select(r.T, r.topk, r.E_glob, r.E_loc, d->N, d->K, W4A16_ROUTE_INDEXED, 0, r.block_m, combine);
+  *out = cached_select(r.T, r.topk, r.E_glob, r.E_loc, d->N, d->K, W4A16_ROUTE_INDEXED, 0, r.block_m);
   apply_env_overrides(out, false);
   return W4A16_OK;
 }
@@ -668,12 +668,12 @@ w4a16_status check_indexed_call(const w4a16_weight_desc* desc, const void* packe
 extern "C" {
 
 w4a16_status w4a16_indexed_config(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc, int32_t N, int32_t K,
-                                  int32_t block_m, int32_t combine, w4a16_config* out) {
+                                  int32_t block_m, w4a16_config* out) {
   if (!out) return fail(W4A16_ERR_ARG, "out is NULL");
   if (!valid_block_m(block_m)) return fail(W4A16_ERR_ARG, "block_m %d not in {16, 32, 64, 128, 256}", block_m);
   if (T < 0 || topk <= 0 || E_glob <= 0 || E_loc <= 0 || N <= 0 || K <= 0)
     return fail(W4A16_ERR_ARG, "bad sizes for indexed_config");
-  *out = cached_select(T, topk, E_glob, E_loc, N, K, W4A16_ROUTE_INDEXED, 0, block_m, combine != 0);
+  *out = cached_select(T, topk, E_glob, E_loc, N, K, W4A16_ROUTE_INDEXED, 0, block_m);
   apply_env_overrides(out, false);
   return W4A16_OK;
 }
@@ -720,7 +720,7 @@ size_t w4a16_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, const w4a16
   const w4a16_indexed_routing& r = *routing;
   if (r.T < 0 || r.topk <= 0 || r.E_loc <= 0 || !valid_block_m(r.block_m) || r.capacity < 0) return 0;
   w4a16_config c{};
-  if (indexed_call_config(r, desc, cfg, combine != 0, &c) != W4A16_OK) return 0;
+  if (indexed_call_config(r, desc, cfg, &c) != W4A16_OK) return 0;
   const int epi = combine ? w4a16::kEpiWeighted : w4a16::kEpiStore;
   if (check_config(c, W4A16_ROUTE_INDEXED, epi, desc->K) != W4A16_OK) return 0;
   const int64_t tiles = indexed_block_bound(r, c.block_m) * n_tiles_of(desc->N, c.nr, c.waves);
@@ -758,7 +758,7 @@ w4a16_status moe_gemm_impl(const w4a16_weight_desc* desc, const void* packed_w, 
   if (st != W4A16_OK) return st;
   const int epi = combine ? w4a16::kEpiWeighted : w4a16::kEpiStore;
   w4a16_config c{};
-  st = indexed_call_config(r, desc, cfg, combine, &c);
+  st = indexed_call_config(r, desc, cfg, &c);
   if (st != W4A16_OK) return st;
   st = check_config(c, W4A16_ROUTE_INDEXED, epi, desc->K);
   if (st != W4A16_OK) return st;
@@ -908,7 +908,7 @@ w4a16_status w4a16_moe_gate_up_silu(const w4a16_weight_desc* desc, const void* p
   st = check_offset_range(r.T, desc->K, "activations");
   if (st != W4A16_OK) return st;
   w4a16_config c{};
-  st = indexed_call_config(r, desc, cfg, false, &c);
+  st = indexed_call_config(r, desc, cfg, &c);
   if (st != W4A16_OK) return st;
   if (!cfg) c.split_k = 1;  // the fused epilogue runs whole tiles
   if (c.split_k != 1) return fail(W4A16_ERR_UNSUPPORTED, "the fused SiLU gate/up call runs one workgroup per tile (split_k = 1)");

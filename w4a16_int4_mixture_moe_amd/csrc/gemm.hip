@@ -921,9 +921,6 @@ hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves, 
   if (k.classic == nullptr) return hipErrorInvalidValue;
   // Block-major order spreads a block's N tiles over the XCDs (round robin);
   // blocks with few N tiles keep them on one XCD instead (block_of).
-  // Keeping many tiles of a block on one XCD measured several times slower:
-  // all its workgroups then request the same activation lines from one L2
-  // at once.
   GemmParams q = p;
   q.xcd_group = xcd_group_for(p.split, p.n_tiles);
   // decode tiles (at most 32 rows) of a block with 32 or more N tiles: groups

@@ -31,9 +31,10 @@ __device__ __forceinline__ int live_blocks(const GemmParams& p) {
 // items of a block; > 1: groups of xcd_group items, so a block spans
 // per / xcd_group XCDs); w runs over groups of 8 (block, group) pairs x the
 // group's items (the launcher rounds the grid up to whole groups) and items
-// past the last block return false.  Not for many items on one XCD: many
-// workgroups asking one L2 for the same lines at once were measured several
-// times slower (all 32 N tiles of a decode block: 3x).
+// past the last block return false.  Group sizes are measured choices: an
+// early decode kernel ran 3x slower with all 32 N tiles of a block on one XCD
+// (its workgroups asked one L2 for the same lines at once); the current one
+// takes groups of 16 at no cost.
 __device__ __forceinline__ bool block_of(const GemmParams& p, int w, int per, int& mb, int& j) {
   if (!p.xcd_group) {
     mb = w / per;
