@@ -191,13 +191,14 @@ typedef struct {
   int32_t waves;     /* waves per workgroup: 4 (8 for some tiles) */
   int32_t split_k;   /* 1: one workgroup per (block, N tile), whole K;
                         2, 4, 8, 16: that many workgroups per tile, each over
-                        an equal share of the 128-K chunks (at least one
-                        chunk each); each leaves fp32 partials in workspace
+                        an equal share of the pairs of 128-K chunks (at most
+                        one slice per pair); each leaves fp32 partials in workspace
                         and the last to finish sums them in slice order
                         (results independent of timing, but not bit-identical
                         to split_k = 1);
                         0: stream-K -- the workgroups the device keeps resident
-                        each take an equal share of (tile, 128-K chunk) units;
+                        each take an equal share of (tile, pair of 128-K
+                        chunks) units;
                         tiles cut between two workgroups are finished from
                         fp32 partials in workspace, summed in K order (results
                         then depend on the device's CU count, not on timing);

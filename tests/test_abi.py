@@ -248,8 +248,11 @@ def test_gemm_argument_errors(L, monkeypatch):
     assert call(cfg=ctypes.byref(W.config(32, 3))) == -4                 # tile config not built
     assert call(w=P) == -8                                               # combine without workspace
     assert call(cfg=ctypes.byref(W.config(32, 2, split_k=3))) == -4     # not a split count
-    assert call(cfg=ctypes.byref(W.config(32, 2, split_k=4))) == -4     # more slices than the 2 K chunks
-    assert call(cfg=ctypes.byref(W.config(32, 2, split_k=2))) == -8     # split needs workspace
+    # slices are whole pairs of 128-K chunks: K = 256 has one pair, K = 512 two
+    assert call(cfg=ctypes.byref(W.config(32, 2, split_k=2))) == -4     # more slices than the 1 chunk pair
+    d4 = W.weight_desc(8, 64, 512)
+    assert call(d=d4, cfg=ctypes.byref(W.config(32, 2, split_k=4))) == -4   # more slices than the 2 pairs
+    assert call(d=d4, cfg=ctypes.byref(W.config(32, 2, split_k=2))) == -8   # split needs workspace
     assert call(cfg=ctypes.byref(W.config(32, 2, kind="contiguous"))) == -1   # config of another kind
     assert call(cfg=ctypes.byref(W.config(32, 2, combine_cols=40)), w=P) == -1  # pass width not a multiple of 16
     # nr 1 (waves splitting K): block_m 16, eight waves, split_k 1, K a multiple of 128

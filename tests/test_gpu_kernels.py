@@ -196,8 +196,8 @@ def test_sparse_routing_launches_only_possible_tiles():
     most padding per row) at every block size, tiles dividing a 256-row
     routing, K slices and stream-K, against the oracle."""
     for T in (1, 3, 48):
-        sh = W.MoEShape(name=f"sparse_t{T}", E_glob=384, E_loc=384, first=0, topk=8, T=T, K1=256, N1=64,
-                        K2=256, N2=96, seed=600 + T)
+        sh = W.MoEShape(name=f"sparse_t{T}", E_glob=384, E_loc=384, first=0, topk=8, T=T, K1=512, N1=64,
+                        K2=512, N2=96, seed=600 + T)
         P = Problem(sh).upload()
         for bm in (16, 32, 64, 128):
             _, h, y = _run_indexed(P, bm)
@@ -364,7 +364,7 @@ def test_dense_special_case_matches_library_matmul():
 # ------------------------------------------------------------ grouped layouts
 
 def test_grouped_contiguous_and_masked_small():
-    sh = W.scaled(W.WORKLOADS["grouped_skewed"], T=300, K1=256, N1=96, E_glob=24, E_loc=6,
+    sh = W.scaled(W.WORKLOADS["grouped_skewed"], T=300, K1=512, N1=96, E_glob=24, E_loc=6,
                   first=3, max_m=48, n_zero_experts=1)
     P = Problem(sh, with_down=False).upload()
     A, mi, slots = W.contiguous_layout(P.topk_ids, P.x, sh.first, sh.E_loc, pad=128, pad_fill=0x7FC0)
@@ -381,7 +381,7 @@ def test_grouped_contiguous_and_masked_small():
         assert_close(out[valid], ref[valid], f"masked bm={bm} waves={nw}")
     out = bits(M.grouped_masked(to_dev_bf16(A3), P.p1, to_dev(mm), expected_m=max(1, int(mm.mean()))))
     assert_close(out[valid], ref[valid], "masked auto config")
-    # split K on the grouped layouts (K = 256: two slices of one chunk)
+    # split K on the grouped layouts (K = 512: two slices of one chunk pair)
     out = bits(M.grouped_contiguous(to_dev_bf16(A), P.p1, to_dev(mi), cfg=M.config(32, 2, split_k=2, kind="contiguous")))
     ref_c, valid_c = O.grouped_contiguous(A, P.c1, P.s1, mi)
     assert_close(out[valid_c], ref_c[valid_c], "contiguous split_k=2")
@@ -479,30 +479,34 @@ def test_streamk_matches_oracle_and_is_deterministic(name, T):
 # ------------------------------------------------------------ split K
 
 def _split_shapes():
-    return [W.WORKLOADS["tiny"],
-            W.MoEShape(name="ragged", E_glob=9, E_loc=5, first=2, topk=3, T=37, K1=96, N1=48,
-                       K2=160, N2=80, seed=77),
+    # K slices are whole pairs of 128-K chunks: K of at least two pairs, and
+    # ragged ones (a last chunk of 96 and of 32 columns)
+    return [W.scaled(W.WORKLOADS["tiny"], K1=1024, K2=512),
+            W.MoEShape(name="ragged", E_glob=9, E_loc=5, first=2, topk=3, T=37, K1=608, N1=48,
+                       K2=672, N2=80, seed=77),
             W.MoEShape(name="k1312", E_glob=8, E_loc=6, first=1, topk=2, T=40, K1=1312, N1=96,
                        K2=1024, N2=80, seed=91)]
 
 
 @pytest.mark.parametrize("shape", _split_shapes(), ids=lambda s: s.name)
 def test_split_k_matches_oracle_is_deterministic_and_leaves_counters_zero(shape):
-    """split_k = S: S workgroups per tile over equal shares of the K chunks,
-    the last to finish summing the fp32 slices in slice order.  Within
-    tolerance of the oracle for every S the shape allows, bit-identical across
-    repeated calls on one workspace (whichever workgroup finishes last), and
-    the arrival counters are back at zero after every call."""
+    """split_k = S: S workgroups per tile over equal shares of the pairs of
+    K chunks, the last to finish summing the fp32 slices in slice order.
+    Within tolerance of the oracle for every S the shape allows (at most one
+    slice per chunk pair), bit-identical across repeated calls on one
+    workspace (whichever workgroup finishes last), and the arrival counters
+    are back at zero after every call."""
     P = Problem(shape).upload()
     sh = P.sh
+    pairs = lambda K: -(-K // 256)
     for bm in (16, 32, 128):
         r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, bm)
         for S in (2, 4, 8):
-            if S > -(-sh.K1 // 128) and S > -(-sh.K2 // 128):
+            if S > pairs(sh.K1) and S > pairs(sh.K2):
                 continue
             outs = []
-            c1 = M.config(bm, 2, split_k=S if S <= -(-sh.K1 // 128) else 1)
-            c2 = M.config(bm, 2, split_k=S if S <= -(-sh.K2 // 128) else 1)
+            c1 = M.config(bm, 2, split_k=S if S <= pairs(sh.K1) else 1)
+            c2 = M.config(bm, 2, split_k=S if S <= pairs(sh.K2) else 1)
             ws1 = torch.zeros(max(16, M.workspace_bytes(P.p1, r, False, c1)), dtype=torch.uint8, device=dev())
             ws2 = torch.zeros(max(16, M.workspace_bytes(P.p2, r, True, c2)), dtype=torch.uint8, device=dev())
             for rep in range(3):
@@ -543,7 +547,7 @@ def test_split_k_graph_replays_match_eager():
     """A split-K call captured in a HIP graph: every replay reproduces the
     eager bits (the counters it leaves at zero let the next replay split
     again), with eager work and poisoned outputs between replays."""
-    P = Problem(W.scaled(W.WORKLOADS["tiny"], K1=1024, K2=512)).upload()
+    P = Problem(W.scaled(W.WORKLOADS["tiny"], K1=2048, K2=1024)).upload()
     sh = P.sh
     r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, 16)
     c1, c2 = M.config(16, 2, split_k=8), M.config(16, 2, split_k=4)
@@ -630,7 +634,7 @@ def test_prefill_tile_bit_identical_to_the_general_kernel(K1, K2):
     np.testing.assert_array_equal(bits(h), out["general"][0], err_msg="gate/up on the 256-row routing, cfg None")
     np.testing.assert_array_equal(bits(y), out["general"][1], err_msg="down+combine on the 256-row routing, cfg None")
     _check_indexed(P, h, y, f"256-row routing, cfg None, K1={K1} K2={K2}")
-    for c in ((M.config(64, 2, split_k=2),) if K2 >= 256 else ()) + (M.config(128, 2, split_k=0),):
+    for c in ((M.config(64, 2, split_k=2),) if K2 >= 512 else ()) + (M.config(128, 2, split_k=0),):
         _check_indexed(P, M.moe_w4a16_gemm(P.d_x, P.p1, r256, cfg=c),
                        M.moe_w4a16_gemm(P.d_a, P.p2, r256, topk_weights=P.d_w, cfg=c),
                        f"256-row routing bm{c.block_m} split_k={c.split_k} K1={K1} K2={K2}")

@@ -367,8 +367,9 @@ w4a16_status check_config(const w4a16_config& c, int route, int epi, int K) {
                 c.split_k);
   if (c.split_k == 0 && route != W4A16_ROUTE_INDEXED)
     return fail(W4A16_ERR_UNSUPPORTED, "stream-K (split_k = 0) is built for indexed routing only");
-  if (c.split_k > 1 && c.split_k > chunks_of(K))
-    return fail(W4A16_ERR_UNSUPPORTED, "split_k %d exceeds the %d 128-K chunks of K = %d", c.split_k, chunks_of(K), K);
+  if (c.split_k > 1 && c.split_k > (chunks_of(K) + 1) / 2)
+    return fail(W4A16_ERR_UNSUPPORTED, "split_k %d exceeds the %d pairs of 128-K chunks of K = %d", c.split_k,
+                (chunks_of(K) + 1) / 2, K);
   if (c.nr == 1 && (c.split_k != 1 || K % 128))
     return fail(W4A16_ERR_UNSUPPORTED, "nr = 1 (waves splitting K) needs split_k = 1 and K a multiple of 128");
   if (!w4a16::gemm_config_supported(route, epi, c.block_m / 16, c.nr, c.waves, c.stages))

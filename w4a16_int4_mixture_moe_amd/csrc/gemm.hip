@@ -35,7 +35,7 @@
 // fully dynamic one):
 //   classic   one workgroup per (routed block, N tile);
 //   stream-K  as many workgroups as the device keeps resident, each taking
-//             an equal contiguous range of (tile, chunk) units, so a grid of
+//             an equal contiguous range of (tile, chunk pair) units, so a grid of
 //             1.5 "waves" of tiles no longer idles half the machine at the
 //             end; a tile cut by a range boundary leaves fp32 partials
 //             (one slot per contributor) that streamk_fixup_kernel sums in
@@ -156,13 +156,19 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
         *reinterpret_cast<u32x4_t*>(&sm.xs[buf][piece_row(i)][xcol]) = v;
       }
   };
-  auto issue_w = [&](int c, u32x4_t (&w)[NR], uint32_t (&sc)[NR]) {
+  // weights of chunk c and, for an even chunk (withs), the scale word of
+  // its chunk pair, which the odd chunk after it reuses: a range starts on
+  // an even chunk (split-K slices and stream-K units are whole chunk
+  // pairs), so even ring positions hold even chunks
+  auto issue_w = [&](int c, u32x4_t (&w)[NR], uint32_t (&sc)[NR], auto withs) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       w[r] = gload_u32x4(wbase[r] + (int64_t)c * (kWave * 16) + woff);
-      sc[r] = gload_u32(sbase[r] + (int64_t)(c >> 1) * (kWave * 4) + soff);
+      if constexpr (decltype(withs)::value) sc[r] = gload_u32(sbase[r] + (int64_t)(c >> 1) * (kWave * 4) + soff);
     }
   };
+  using WithS = std::integral_constant<bool, true>;
+  using NoS = std::integral_constant<bool, false>;
 
   // Weights and scales: a ring of D register sets (the config's prefetch
   // stages); chunk c0 + m*D + P uses set P, and the set is refilled with
@@ -178,7 +184,8 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
   // value stays one register tuple that the allocator can keep in place
   u32x4_t xr[PPT];
   u32x4_t wr[D][NR];
-  uint32_t sr[D][NR];
+  uint32_t sr[D][NR];   // scale words: even ring positions only
+  uint32_t spair[NR];   // the current pair's word, kept for its odd chunk
 
   // c0 < c1 (both callers).  Unconditional, clamped (a set past the range
   // re-reads the last chunk and is never used) and in ring order: the waits
@@ -188,7 +195,10 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     __builtin_amdgcn_sched_barrier(0);
-    issue_w(min(c0 + i, c1 - 1), wr[i], sr[i]);
+    if (i % 2 == 0)
+      issue_w(min(c0 + i, c1 - 1), wr[i], sr[i], WithS{});
+    else
+      issue_w(min(c0 + i, c1 - 1), wr[i], sr[i], NoS{});
   }
   __builtin_amdgcn_sched_barrier(0);
   store_x(0, c0, xr, true);
@@ -239,8 +249,29 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
 #pragma unroll
     for (int r = 0; r < NR; ++r) asm volatile("" ::"v"(A[r]));
     __builtin_amdgcn_sched_barrier(0);
-    issue_w(c + D, wr[P], sr[P]);
+    if constexpr (P % 2 == 0)
+      issue_w(c + D, wr[P], sr[P], WithS{});
+    else
+      issue_w(c + D, wr[P], sr[P], NoS{});
     __builtin_amdgcn_sched_barrier(0);
+  };
+  // an even chunk hands its pair's scale word to the odd chunk after it,
+  // before its refill overwrites the word (a copy of a value that arrived
+  // long ago: it waits for nothing)
+  auto keep_pair = [&](auto P_) {
+    constexpr int P = decltype(P_)::value;
+    if constexpr (P % 2 == 0) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) spair[r] = sr[P][r];
+    }
+  };
+  // the scale word of the chunk at ring position P
+  auto word_of = [&](auto P_) -> const uint32_t(&)[NR] {
+    constexpr int P = decltype(P_)::value;
+    if constexpr (P % 2 == 0)
+      return sr[P];
+    else
+      return spair;
   };
 
   // Pipelined form: fragment j + 1 is dequantised
@@ -255,6 +286,8 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
     scale_consts(sr[0], c0, kcur);
     dequant_set(wr[0], 0, kcur, Acur);
   }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) spair[r] = 0u;
 
   // one chunk at ring position P (c - c0 = P mod D).  STEADY: chunks c + 1
   // and c + D exist and c + 1 is not the ragged last chunk, so every
@@ -270,11 +303,12 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
         bf16x8_t Anext[NR];
         if (j < 3) {
           dequant_set(wr[P], j + 1, kcur, Anext);
+          if (j == 2) keep_pair(P_);
           if (j == 2 && (STEADY || c + D < c1)) refill(P_, c, Anext);
         } else if (STEADY || c + 1 < c1) {
-          constexpr int PN = (P + 1) % D;
-          scale_consts(sr[PN], c + 1, kcur);
-          dequant_set(wr[PN], 0, kcur, Anext);
+          using PN = std::integral_constant<int, (P + 1) % D>;
+          scale_consts(word_of(PN{}), c + 1, kcur);
+          dequant_set(wr[PN::value], 0, kcur, Anext);
         }
         mfmas(buf, j, Acur);
 #pragma unroll
@@ -282,7 +316,8 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, TileSmem<MT>& sm, 
       }
     } else {
       float k[NR][4];
-      scale_consts(sr[P], c, k);
+      scale_consts(word_of(P_), c, k);
+      keep_pair(P_);
       // one 8-wide K fragment at a time: dequantise it, read the matching
       // activation fragments, issue its MFMAs
 #pragma unroll
@@ -518,8 +553,11 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_kernel(const GemmParams p
   if (expert < 0) return;
   __syncthreads();
   const uint32_t tmask = active_tiles<MT>(sm);
-  const int c0 = split ? (int)((int64_t)s * p.KC / S) : 0;
-  const int c1 = split ? (int)((int64_t)(s + 1) * p.KC / S) : p.KC;
+  // slices of whole chunk pairs (the main loop's ranges start on an even
+  // chunk); split <= (KC + 1) / 2, so none is empty
+  const int KC2 = (p.KC + 1) / 2;
+  const int c0 = split ? 2 * (int)((int64_t)s * KC2 / S) : 0;
+  const int c1 = split ? min(p.KC, 2 * (int)((int64_t)(s + 1) * KC2 / S)) : p.KC;
   auto store = [&](const f32x4_t(&acc)[NR][MT], uint32_t tm) {
     if constexpr (EPI == kEpiWeighted && 16 * NR * NW <= 128)
       epilogue_weighted_staged<MT, NR, NW>(p, sm, nt, tm, acc);
@@ -634,14 +672,15 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_kwave_kernel(const GemmPa
 }
 
 // Work partition shared by the stream-K kernel and its fix-up: `units`
-// (tile, chunk) units split into ranges of `per` units, one per workgroup.
+// (tile, chunk pair) units split into ranges of `per` units, one per
+// workgroup (whole pairs: the main loop's ranges start on an even chunk).
 struct SkPartition {
   int64_t units, per;
 };
 
 template <int MT, int ROUTE>
 __device__ __forceinline__ SkPartition sk_partition(const GemmParams& p, int64_t workgroups) {
-  const int64_t units = (int64_t)live_blocks<MT, ROUTE>(p) * p.n_tiles * p.KC;
+  const int64_t units = (int64_t)live_blocks<MT, ROUTE>(p) * p.n_tiles * ((p.KC + 1) / 2);
   return SkPartition{units, (units + workgroups - 1) / workgroups};
 }
 
@@ -653,11 +692,14 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_streamk_kernel(const Gemm
   const int64_t g = blockIdx.x;
   const int64_t end = min(part.units, (g + 1) * part.per);
   const int KC = p.KC;
+  const int KC2 = (KC + 1) / 2;
   bool first = true;
   for (int64_t u = g * part.per; u < end;) {
-    const int64_t item = u / KC;
-    const int c0 = (int)(u - item * KC);
-    const int c1 = (int)min((int64_t)KC, c0 + (end - u));
+    const int64_t item = u / KC2;
+    const int q0 = (int)(u - item * KC2);
+    const int q1 = (int)min((int64_t)KC2, q0 + (end - u));
+    const int c0 = 2 * q0;
+    const int c1 = min(KC, 2 * q1);
     const int mb = (int)(item / p.n_tiles);
     const int nt = (int)(item - (int64_t)mb * p.n_tiles);
     __syncthreads();                       // previous tile's LDS readers are done
@@ -683,7 +725,7 @@ __global__ __launch_bounds__(NW * kWave) void moe_gemm_streamk_kernel(const Gemm
       });
     }
     first = false;
-    u += c1 - c0;
+    u += q1 - q0;
   }
 }
 
@@ -695,12 +737,12 @@ __global__ __launch_bounds__(NW * kWave) void streamk_fixup_kernel(const GemmPar
   __shared__ __attribute__((aligned(16))) TileSmem<MT> sm;
   constexpr int NTHR = NW * kWave;
   const SkPartition part = sk_partition<MT, ROUTE>(p, sk_grid);
-  const int KC = p.KC;
+  const int KC2 = (p.KC + 1) / 2;                  // units (chunk pairs) per tile
   const int64_t g = (int64_t)blockIdx.x + 1;       // boundary between ranges g-1 and g
   const int64_t b = g * part.per;
-  if (b >= part.units || b % KC == 0) return;      // boundary at a tile edge: nothing cut
-  const int64_t item = b / KC;
-  if ((g - 1) * part.per > item * KC) return;      // an earlier boundary inside this tile owns it
+  if (b >= part.units || b % KC2 == 0) return;     // boundary at a tile edge: nothing cut
+  const int64_t item = b / KC2;
+  if ((g - 1) * part.per > item * KC2) return;     // an earlier boundary inside this tile owns it
   const int mb = (int)(item / p.n_tiles);
   const int nt = (int)(item - (int64_t)mb * p.n_tiles);
   const int expert = setup_rows<MT, NW, ROUTE, EPI>(p, mb, sm);
@@ -712,9 +754,9 @@ __global__ __launch_bounds__(NW * kWave) void streamk_fixup_kernel(const GemmPar
   for (int r = 0; r < NR; ++r)
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int64_t h0 = item * KC / part.per, h1 = ((item + 1) * KC - 1) / part.per;
+  const int64_t h0 = item * KC2 / part.per, h1 = ((item + 1) * KC2 - 1) / part.per;
   for (int64_t h = h0; h <= h1; ++h) {
-    const int64_t slot = (h * part.per) / KC == item ? 2 * h : 2 * h + 1;
+    const int64_t slot = (h * part.per) / KC2 == item ? 2 * h : 2 * h + 1;
     const float4* src = partial_slot<MT, NR, NW>(p, slot);
 #pragma unroll
     for (int r = 0; r < NR; ++r)
@@ -935,7 +977,7 @@ hipError_t launch_gemm(int route, int epilogue, int m_tiles, int nr, int waves, 
   const int64_t grid = grid_of(q, q.n_tiles) * std::max(q.split, 1);
   if (grid <= 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
-  if (q.split > 1 && (q.split > q.KC || (q.split_tiles > 0 && (!q.split_partial || !q.split_count))))
+  if (q.split > 1 && (q.split > (q.KC + 1) / 2 || (q.split_tiles > 0 && (!q.split_partial || !q.split_count))))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(k.classic, dim3((unsigned)grid), dim3(waves * kWave), 0, stream, q);
   return hipGetLastError();
