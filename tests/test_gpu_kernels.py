@@ -213,6 +213,26 @@ def test_sparse_routing_launches_only_possible_tiles():
             _check_indexed(P, h, y, f"sparse T={T} 256-row routing bm={c.block_m} split_k={c.split_k}")
 
 
+def test_decode_xcd_groups_cover_every_tile():
+    """Decode tiles of a block with 32 or more N tiles run in groups of 16 N
+    tiles per XCD (the grid rounded up to whole rounds of eight groups;
+    workgroups past the last block exit).  Gate/up N = 4096 on block_m 32,
+    nr 2 (32 N tiles per block: grouped) gives the same bits as nr 4 (16 N
+    tiles: block-major), whose outputs are summed in the same order, and
+    matches the oracle; with a grid that needs idle groups and one that
+    does not."""
+    for T, seed in ((40, 31), (57, 32)):
+        sh = W.MoEShape(name=f"xcd_t{T}", E_glob=8, E_loc=5, first=1, topk=2, T=T, K1=256, N1=4096,
+                        K2=256, N2=64, seed=seed)
+        P = Problem(sh, with_down=False).upload()
+        r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, 32)
+        hg = M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=M.config(32, 2))
+        hb = M.moe_w4a16_gemm(P.d_x, P.p1, r, cfg=M.config(32, 4))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(hg), bits(hb), err_msg=f"T={T}: grouped vs block-major")
+        _check_indexed(P, hg, None, f"xcd groups T={T}")
+
+
 def test_multi_chunk_k():
     """K spanning many 128-wide chunks (steady-state loop plus its tail, both
     prefetch depths), ragged and not, against the oracle; depths agree bit
