@@ -104,6 +104,8 @@ def kernel_name(cfg, route: int, epi: int, K: int, mx: bool = False) -> str:
     configurations on its prefill tiles when K is a multiple of 128, the
     first in its N-tile-loop form for K <= 256 on the grids measured here."""
     if mx:
+        if cfg.nr == 1:
+            return f"mx_kwave_kernel<{cfg.waves}, {epi}>"
         return f"mx_gemm_kernel<{cfg.block_m // 16}, {cfg.nr}, {cfg.waves}, {cfg.stages}, {epi}>"
     if cfg.nr == 1:
         return f"moe_gemm_kwave_kernel<{cfg.waves}, {epi}>"
@@ -283,8 +285,12 @@ class IndexedStep:
             return cfg
 
         if self.mx:
-            self.cfg1 = M.mxfp4_config(bm, args.nr or 4, args.stages or None)
-            self.cfg2 = self.cfg1
+            # per projection, as the selector gives it (the fused chain's
+            # epilogue needs four weight tiles per wave)
+            c2 = M.mxfp4_select(T, k, sh.E_glob, sh.E_loc, sh.N2, sh.K2)
+            nr_of = lambda cc: 4 if cc.nr == 1 and (bm != 16 or self.fused) else cc.nr
+            self.cfg1 = M.mxfp4_config(bm, args.nr or nr_of(c), args.stages or None)
+            self.cfg2 = M.mxfp4_config(bm, args.nr or (4 if c2.nr == 1 and bm != 16 else c2.nr), args.stages or None)
         else:
             self.cfg1 = override(M.indexed_config(self.routing, self.p1))
             self.cfg2 = override(M.indexed_config(self.routing, self.p2))

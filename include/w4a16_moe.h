@@ -488,7 +488,9 @@ w4a16_status w4a16_mxfp4_quant_local_slots(const uint16_t* x, const int32_t* top
  * that where it gives 128 or 256 and tokens per expert T * topk / E_glob are
  * at least 128, 64 (the MXFP4 kernel keeps more waves resident on 64-row
  * blocks and measured faster there); nr 4, waves 4, one workgroup per
- * tile, stages 4 for block_m <= 32, else 2.  Errors: ERR_ARG. */
+ * tile, stages 4 for block_m <= 32, else 2 -- except where w4a16_select
+ * gives the tile whose waves split K (block_m 16, nr 1): there the A4W4
+ * K-split tile, nr 1 with eight waves.  Errors: ERR_ARG. */
 w4a16_status w4a16_mxfp4_select(int32_t T, int32_t topk, int32_t E_glob, int32_t E_loc,
                                 int32_t N, int32_t K, w4a16_config* out);
 
@@ -505,8 +507,10 @@ size_t w4a16_mxfp4_moe_gemm_workspace_bytes(const w4a16_weight_desc* desc, int32
  * out[T, N] with fp32 partials summed in j order and rounded once.
  * Accumulation is fp32 (the MFMA's); each output is rounded once to bf16.
  *  cfg : NULL: block_m from the routing (64 on a 256-row routing), nr 4,
- *        four waves, stages 4 for block_m <= 32 else 2; split_k must be 1.
- *        A config's block_m divides the routing's.
+ *        four waves, stages 4 for block_m <= 32 else 2 -- or, on a 16-row
+ *        routing where w4a16_mxfp4_select takes it, nr 1 with eight waves
+ *        (one 16-row weight tile per workgroup, its waves splitting K);
+ *        split_k must be 1.  A config's block_m divides the routing's.
  * Pointers: packed_w, packed_s, a_codes, out, workspace 16-byte aligned.
  * Errors: ERR_ARG, ERR_LAYOUT (not an MXFP4 weight, E_loc mismatch, or a
  * block_m that does not divide the routing's), ERR_SHAPE, ERR_UNSUPPORTED,

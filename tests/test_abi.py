@@ -314,7 +314,8 @@ def test_gate_up_silu_argument_errors(L):
 def test_mxfp4_selector_halves_large_prefill_blocks(L):
     """A4W4 takes 64-row blocks where the W4A16 rule gives 128 or 256 at >= 128
     rows per expert, keeps 128 below that, follows the W4A16 block_m elsewhere,
-    and always uses one workgroup per tile with four weight tiles per wave."""
+    and uses one workgroup per tile with four weight tiles per wave, or its
+    K-split tile where the W4A16 rule takes one."""
     pre = W.mxfp4_select(8192, 8, 384, 48, 4096, 7168)          # ~171 rows/expert
     assert W.select(8192, 8, 384, 48, 4096, 7168).block_m == 256
     assert (pre.block_m, pre.nr, pre.waves, pre.split_k, pre.stages) == (64, 4, 4, 1, 2)
@@ -324,6 +325,12 @@ def test_mxfp4_selector_halves_large_prefill_blocks(L):
         c, w = W.mxfp4_select(*args), W.select(*args)
         assert c.block_m == w.block_m and c.split_k == 1 and c.nr == 4
         assert c.stages == (4 if c.block_m <= 32 else 2)
+    # where the W4A16 rule takes the tile whose waves split K (TP8 T = 1
+    # gate/up), A4W4 takes its own K-split tile; the short-K down keeps nr 4
+    t1, w1 = W.mxfp4_select(1, 8, 384, 384, 512, 7168), W.select(1, 8, 384, 384, 512, 7168)
+    assert w1.nr == 1 and (t1.block_m, t1.nr, t1.waves, t1.split_k) == (16, 1, 8, 1)
+    d1 = W.mxfp4_select(1, 8, 384, 384, 7168, 256)
+    assert (d1.block_m, d1.nr, d1.waves) == (16, 4, 4)
     with pytest.raises(W.W4A16Error):
         W.mxfp4_select(16, 0, 384, 48, 4096, 7168)
 

@@ -164,6 +164,35 @@ def test_mx_gemm_vs_oracle(shape):
         log(sh.name, f"bm={bm} nr={nr}", dict(gu_err=e1, gu_exact=x1, dn_err=e2, dn_exact=x2))
 
 
+def test_mx_kwave_tile_vs_oracle():
+    """The A4W4 K-split tile (block_m 16, nr 1: eight waves share a 16-row
+    weight tile's K chunks and sum in wave order): within tolerance of the
+    oracle for the per-slot store and the top-k combine, with two batches of
+    chunks per wave (K = 10240: ten chunks each), one or two chunks per wave
+    (K = 1152, 640), and waves without chunks (K = 256); non-local rows
+    untouched; and the call's own choice on a 16-row routing."""
+    for K1, K2, seed in ((10240, 256, 61), (1152, 640, 62)):
+        sh = W.MoEShape(name=f"mx_kwave_{K1}", E_glob=8, E_loc=5, first=2, topk=2, T=21, K1=K1, N1=64,
+                        K2=K2, N2=48, seed=seed)
+        P = MxProblem(sh).upload()
+        T, k = P.T, sh.topk
+        h_ref, ok = X.mx_indexed_gate_up(*P.xq, X.unpack_nibbles(P.w1), P.s1, P.topk_ids, sh.first, sh.E_loc)
+        y_ref = X.mx_indexed_down_combine(*P.aq, X.unpack_nibbles(P.w2), P.s2, P.topk_ids, P.topk_w,
+                                          sh.first, sh.E_loc)
+        r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, 16)
+        for cfg in (M.mxfp4_config(16, 1), None):
+            canary = torch.full((T * k, sh.N1), 0x7F81, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+            h = M.moe_mxfp4_gemm(P.d_x, P.p1, r, cfg=cfg, out=canary)
+            y = M.moe_mxfp4_gemm(P.d_a, P.p2, r, topk_weights=P.d_w, cfg=cfg)
+            torch.cuda.synchronize()
+            hb, yb = bits(h), bits(y)
+            what = f"{sh.name} {'nr 1' if cfg is not None else 'cfg None'}"
+            assert (hb[~ok] == 0x7F81).all(), "non-local per-slot rows were written"
+            e1, x1 = assert_close(hb[ok], h_ref[ok], what + " gate/up")
+            e2, x2 = assert_close(yb, y_ref, what + " down+combine")
+            log(what, dict(gu_err=e1, gu_exact=x1, dn_err=e2, dn_exact=x2))
+
+
 def test_mx_one_hot_reads_weights_exactly():
     sh = W.MoEShape(name="onehot_mx", E_glob=6, E_loc=4, first=1, topk=2, T=40, K1=512, N1=64,
                     K2=128, N2=32, seed=55)

@@ -423,7 +423,10 @@ def mxfp4_select(T: int, topk: int, E_glob: int, E_loc: int, N: int, K: int) -> 
 
 
 def mxfp4_config(block_m: int, nr: int = 4, stages: Optional[int] = None) -> Config:
-    return config(block_m, nr, waves=4, split_k=1, stages=(4 if block_m <= 32 else 2) if stages is None else stages)
+    """An A4W4 tile config: nr 2 or 4 weight tiles per wave on four waves, or
+    nr 1 (block_m 16): the K-split tile, whose eight waves split K."""
+    return config(block_m, nr, waves=8 if nr == 1 else 4, split_k=1,
+                  stages=(4 if block_m <= 32 else 2) if stages is None else stages)
 
 
 def moe_mxfp4_gemm(a: MXRows, packed: PackedW4, routing: Routing,

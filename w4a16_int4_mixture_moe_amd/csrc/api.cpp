@@ -706,8 +706,11 @@ w4a16_status w4a16_mxfp4_select(int32_t T, int32_t topk, int32_t E_glob, int32_t
   w4a16_config c = cached_select(T, topk, E_glob, E_loc, N, K, W4A16_ROUTE_INDEXED, 0, 0);
   const double tok_e = (double)T * topk / E_glob;
   if (c.block_m >= 128 && tok_e >= kMxHalfTileTokE) c.block_m = 64;
-  c.nr = 4;
-  c.waves = 4;
+  // the K-split tile where the W4A16 rule takes it (block_m 16, a grid that
+  // would split K four or more ways), else four weight tiles per wave
+  const bool kwave = c.nr == 1;
+  c.nr = kwave ? 1 : 4;
+  c.waves = kwave ? w4a16::kKwWaves : 4;
   c.split_k = 1;
   c.stages = c.block_m <= 32 ? 4 : 2;
   *out = c;
@@ -1151,8 +1154,12 @@ w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* pac
     c = *cfg;
   } else {
     c.block_m = mx_tile_rows(r);      // the routing buffers fix block_m
-    c.nr = 4;
-    c.waves = 4;
+    // the K-split tile on a 16-row routing where the selector takes it
+    const bool kwave = c.block_m == 16 && r.E_glob > 0 &&
+                       cached_select(r.T, r.topk, r.E_glob, r.E_loc, desc->N, desc->K, W4A16_ROUTE_INDEXED, 0,
+                                     r.block_m).nr == 1;
+    c.nr = kwave ? 1 : 4;
+    c.waves = kwave ? w4a16::kKwWaves : 4;
     c.split_k = 1;
     c.stages = c.block_m <= 32 ? 4 : 2;
     c.kind = W4A16_ROUTE_INDEXED;

@@ -489,6 +489,74 @@ __global__ __launch_bounds__(NW * kWave) void mx_gemm_kernel(const GemmParams p)
   }
 }
 
+// Few routed rows (block_m 16) and a grid too small for the machine: one
+// 16-row weight tile per workgroup, its NW waves splitting K (wave w takes
+// chunks [w KC / NW, (w + 1) KC / NW)).  Each wave loads a batch of its
+// chunks' weight and activation fragments and scale bytes straight into
+// registers (the activation rows need no staging, as above), one MFMA per
+// chunk, and the waves' partial sums meet in LDS, summed in wave order.
+// Store or weighted epilogue; the W4A16 K-split tile's scheme, on the
+// scaled FP4 MFMA.
+constexpr int kMxKwBatch = 8;                     // chunks in flight per wave
+
+template <int NW>
+struct MxKwSmem : MxSmem<1> {
+  f32x4_t red[NW][kWave];
+};
+
+template <int NW, int EPI>
+__global__ __launch_bounds__(NW * kWave) void mx_kwave_kernel(const GemmParams p) {
+  __shared__ MxKwSmem<NW> sm;
+  const int mb = blockIdx.x / p.n_tiles;
+  const int nt = blockIdx.x - mb * p.n_tiles;
+  const int expert = setup_rows<1, NW, kRouteIndexed, EPI>(p, mb, sm);
+  if (expert < 0) return;
+  __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int KC = p.KC;
+  const int c0 = (int)((int64_t)wave * KC / NW), c1 = (int)((int64_t)(wave + 1) * KC / NW);
+  const int64_t tile = (int64_t)expert * p.w_tiles + min(nt, p.NT - 1);
+  const gptr_t wbase = uniform_ptr(p.packed_w + tile * KC * kWave) + lane * 16;
+  const gptr_t sbase = uniform_ptr(reinterpret_cast<const uint8_t*>(p.packed_s) + tile * KC * kWave) + lane;
+  // B operand: lane l supplies token row l % 16, block l / 16 of each chunk
+  const int r = sm.row[lane & 15];
+  const int64_t row = r >= 0 ? r : sm.row[0];     // padding reads a valid row, never stored
+  const gptr_t abase = uniform_ptr(p.a) + row * (p.K / 2) + 16 * (lane >> 4);
+  const gptr_t asbase = uniform_ptr(p.a_scale) + row * (p.K / 32) + (lane >> 4);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int cb = c0; cb < c1; cb += kMxKwBatch) {
+    u32x4_t w[kMxKwBatch], x[kMxKwBatch];
+    uint32_t ws[kMxKwBatch], xs[kMxKwBatch];
+#pragma unroll
+    for (int i = 0; i < kMxKwBatch; ++i) {
+      const int c = min(cb + i, c1 - 1);          // past c1: a repeated load, not used
+      w[i] = gload_u32x4(wbase + (int64_t)c * (kWave * 16));
+      ws[i] = gload_u8(sbase + (int64_t)c * kWave);
+      x[i] = gload_u32x4(abase + (int64_t)c * 64);
+      xs[i] = gload_u8(asbase + (int64_t)c * 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);            // the whole batch in flight before the first MFMA
+    // every MFMA of the batch is issued (a conditional one would let the
+    // compiler sink its loads behind the branch, one round trip per chunk);
+    // past c1 the activation operand is zero (FP4 has no Inf or NaN, so the
+    // products are exact zeros)
+#pragma unroll
+    for (int i = 0; i < kMxKwBatch; ++i) {
+      const u32x4_t xb = cb + i < c1 ? x[i] : u32x4_t{0u, 0u, 0u, 0u};
+      acc = mx_mfma(w[i], ws[i], xb, xs[i], acc);
+    }
+  }
+  sm.red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  f32x4_t tot[1][1];
+  tot[0][0] = sm.red[0][lane];
+#pragma unroll
+  for (int v = 1; v < NW; ++v) tot[0][0] += sm.red[v][lane];
+  epilogue<1, 1, 1, EPI>(p, sm, nt, 1u, tot);
+}
+
 typedef void (*MxKernel)(const GemmParams);
 
 template <int MT, int NR, int NW, int D>
@@ -502,8 +570,14 @@ static MxKernel mx_pick(int epi) {
 
 // Built tile configurations (MT, NR, waves, stages): four waves; NR = 2 or 4
 // weight tiles per wave; four stages for the decode tiles (MT <= 2), two for
-// the larger blocks.
+// the larger blocks; and the K-split tile (MT 1, NR 1, kKwWaves waves).
 static MxKernel find_mx_kernel(int epi, int m_tiles, int nr, int waves, int stages) {
+  if (nr == 1) {  // the K-split tile: block_m 16, kKwWaves waves (stages do not apply)
+    if (m_tiles != 1 || waves != kKwWaves) return nullptr;
+    if (epi == kEpiStore) return mx_kwave_kernel<kKwWaves, kEpiStore>;
+    if (epi == kEpiWeighted) return mx_kwave_kernel<kKwWaves, kEpiWeighted>;
+    return nullptr;
+  }
 #define W4A16_MX_CASE(MT_, NR_, NW_, D_) \
   if (m_tiles == MT_ && nr == NR_ && waves == NW_ && stages == D_) return mx_pick<MT_, NR_, NW_, D_>(epi);
   W4A16_MX_CASE(1, 2, 4, 4) W4A16_MX_CASE(2, 2, 4, 4) W4A16_MX_CASE(4, 2, 4, 2) W4A16_MX_CASE(8, 2, 4, 2)
