@@ -285,10 +285,9 @@ class IndexedStep:
             return cfg
 
         if self.mx:
-            # per projection, as the selector gives it (the fused chain's
-            # epilogue needs four weight tiles per wave)
+            # per projection, as the selector gives it
             c2 = M.mxfp4_select(T, k, sh.E_glob, sh.E_loc, sh.N2, sh.K2)
-            nr_of = lambda cc: 4 if cc.nr == 1 and (bm != 16 or self.fused) else cc.nr
+            nr_of = lambda cc: 4 if cc.nr == 1 and bm != 16 else cc.nr
             self.cfg1 = M.mxfp4_config(bm, args.nr or nr_of(c), args.stages or None)
             self.cfg2 = M.mxfp4_config(bm, args.nr or (4 if c2.nr == 1 and bm != 16 else c2.nr), args.stages or None)
         else:
@@ -316,8 +315,8 @@ class IndexedStep:
                                   torch.zeros(cap, sh.N1 // 64, dtype=torch.uint8, device=dev))
                          if self.fused and self.mx else None)
         if self.fused and (sh.K2 != sh.N1 // 2 or (self.cfg1.nr % 2 and self.cfg1.nr != 1)
-                           or (self.mx and self.cfg1.nr != 4)):
-            raise SystemExit("--fused needs K2 = N1 / 2 and an even nr or 1 (4 with --mx)")
+                           or (self.mx and self.cfg1.nr not in (1, 4))):
+            raise SystemExit("--fused needs K2 = N1 / 2 and an even nr or 1 (4 or 1 with --mx)")
         self.L = M.load()
         self._ctypes = ctypes
 

@@ -531,8 +531,10 @@ w4a16_status w4a16_mxfp4_moe_gemm(const w4a16_weight_desc* desc, const void* pac
  * I/32]).  Padding positions are left unwritten; the down projection reads
  * the rows with a_layout = W4A16_A_SORTED.
  *  cfg : NULL: block_m from the routing (64 on a 256-row routing), nr 4,
- *        four waves; nr must be 4 and split_k 1, and block_m divide the
- *        routing's.
+ *        four waves -- or, on a 16-row routing where w4a16_mxfp4_select
+ *        takes it, nr 1 with eight waves (the K-split tile, here four packed
+ *        tiles, one activation block, per workgroup); nr must be 4 or 1 and
+ *        split_k 1, and block_m divide the routing's.
  * Pointers: packed_w, packed_s, x_codes, out_codes 16-byte aligned.
  * Errors: ERR_ARG, ERR_LAYOUT (not an MXFP4 gate/up weight, or block_m not
  * dividing the routing's), ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP. */

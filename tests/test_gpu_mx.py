@@ -299,14 +299,15 @@ def test_mx_fused_silu_quant_and_sorted_down(shape):
     a_ref[ok] = O.silu_mul(h_ref[ok])
     y_ref = X.mx_indexed_down_combine(*X.mx_quantize(a_ref), X.unpack_nibbles(P.w2), P.s2, P.topk_ids, P.topk_w,
                                       sh.first, sh.E_loc)
-    for bm in (16, 32, 64, 128):
+    # nr 1: the K-split tile (four packed tiles per workgroup in the fused call)
+    for bm, nr in ((16, 4), (32, 4), (64, 4), (128, 4), (16, 1)):
         r = M.moe_align(P.d_ids, sh.E_glob, sh.first, sh.E_loc, bm)
-        cfg = M.mxfp4_config(bm, 4)
+        cfg = M.mxfp4_config(bm, nr)
         h = M.moe_mxfp4_gemm(P.d_x, P.p1, r, cfg=cfg)
         hg = M.moe_mxfp4_gemm(P.d_x, p1g, r, cfg=cfg)
         inter = M.moe_mxfp4_gate_up_silu(P.d_x, p1g, r, cfg=cfg)
         torch.cuda.synchronize()
-        np.testing.assert_array_equal(bits(hg), bits(h), err_msg=f"interleaved packing changed bits, bm={bm}")
+        np.testing.assert_array_equal(bits(hg), bits(h), err_msg=f"interleaved packing changed bits, bm={bm} nr={nr}")
         sid = r.sorted_ids.cpu().numpy()
         valid = sid < T * k
         # the oracle's activation and quantiser on the GPU's per-slot values
@@ -323,7 +324,7 @@ def test_mx_fused_silu_quant_and_sorted_down(shape):
         # fp64 in the oracle) can move a code by one step or the block scale
         # by one binade: at most one step of the coarser E2M1 spacing (2 X)
         bound = 2.0 * np.repeat(np.maximum(X.e8m0_to_f64(gs), X.e8m0_to_f64(rs)), 32, axis=1)
-        assert np.all(np.abs(got_v - ref_v) <= bound), f"bm={bm}"
+        assert np.all(np.abs(got_v - ref_v) <= bound), f"bm={bm} nr={nr}"
         assert same_s.mean() > 0.99 and same_c.mean() > 0.99, (same_s.mean(), same_c.mean())
         # down on sorted rows == down on the same rows gathered per slot
         slot_rows = M.MXRows(torch.zeros(T * k, sh.K2 // 2, dtype=torch.uint8, device="cuda"),
@@ -335,9 +336,9 @@ def test_mx_fused_silu_quant_and_sorted_down(shape):
         y_sorted = M.moe_mxfp4_gemm(inter, P.p2, r, topk_weights=P.d_w, a_layout="sorted", cfg=cfg)
         y_slot = M.moe_mxfp4_gemm(slot_rows, P.p2, r, topk_weights=P.d_w, a_layout="slot", cfg=cfg)
         torch.cuda.synchronize()
-        np.testing.assert_array_equal(bits(y_sorted), bits(y_slot), err_msg=f"bm={bm}")
-        e, x_ = assert_close(bits(y_sorted), y_ref, f"{sh.name} A4W4 chain bm={bm}")
-        log(sh.name, f"bm={bm}", dict(chain_err=e, chain_exact=x_, codes_exact=float(same_c.mean()),
+        np.testing.assert_array_equal(bits(y_sorted), bits(y_slot), err_msg=f"bm={bm} nr={nr}")
+        e, x_ = assert_close(bits(y_sorted), y_ref, f"{sh.name} A4W4 chain bm={bm} nr={nr}")
+        log(sh.name, f"bm={bm} nr={nr}", dict(chain_err=e, chain_exact=x_, codes_exact=float(same_c.mean()),
                                       scales_exact=float(same_s.mean())))
 
 

@@ -1230,8 +1230,12 @@ w4a16_status w4a16_mxfp4_gate_up_silu(const w4a16_weight_desc* desc, const void*
     c = *cfg;
   } else {
     c.block_m = mx_tile_rows(r);
-    c.nr = 4;
-    c.waves = 4;
+    // the K-split tile on a 16-row routing where the selector takes it
+    const bool kwave = c.block_m == 16 && r.E_glob > 0 &&
+                       cached_select(r.T, r.topk, r.E_glob, r.E_loc, desc->N, desc->K, W4A16_ROUTE_INDEXED, 0,
+                                     r.block_m).nr == 1;
+    c.nr = kwave ? 1 : 4;
+    c.waves = kwave ? w4a16::kKwWaves : 4;
     c.split_k = 1;
     c.stages = c.block_m <= 32 ? 4 : 2;
     c.kind = W4A16_ROUTE_INDEXED;
@@ -1239,8 +1243,9 @@ w4a16_status w4a16_mxfp4_gate_up_silu(const w4a16_weight_desc* desc, const void*
   }
   if (c.kind != W4A16_ROUTE_INDEXED) return fail(W4A16_ERR_ARG, "config was chosen for a grouped routing kind");
   if (!valid_block_m(c.block_m)) return fail(W4A16_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128, 256}", c.block_m);
-  if (c.split_k != 1 || c.nr != 4)
-    return fail(W4A16_ERR_UNSUPPORTED, "the fused A4W4 gate/up call runs one workgroup per tile with nr = 4");
+  if (c.split_k != 1 || (c.nr != 4 && c.nr != 1))
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "the fused A4W4 gate/up call runs one workgroup per tile with nr = 4 (or 1: the K-split tile)");
   if (!w4a16::mx_gemm_config_supported(w4a16::kEpiSiluMx, c.block_m / 16, c.nr, c.waves, c.stages))
     return fail(W4A16_ERR_UNSUPPORTED, "MXFP4 tile config block_m=%d nr=%d waves=%d stages=%d not built", c.block_m,
                 c.nr, c.waves, c.stages);
@@ -1250,6 +1255,7 @@ w4a16_status w4a16_mxfp4_gate_up_silu(const w4a16_weight_desc* desc, const void*
   if (r.T == 0) return W4A16_OK;
   w4a16::GemmParams p = base_params(desc, packed_w, packed_s, reinterpret_cast<const uint16_t*>(x_codes),
                                     out_codes, c.nr, c.waves);
+  if (c.nr == 1) p.n_tiles = p.NT / 4;   // the K-split tile: four packed tiles (one activation block) each
   p.a_scale = x_scales;
   p.out_scale = out_scales;
   p.sorted_ids = r.sorted_ids;

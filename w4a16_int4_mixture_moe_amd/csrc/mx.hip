@@ -490,23 +490,24 @@ __global__ __launch_bounds__(NW * kWave) void mx_gemm_kernel(const GemmParams p)
 }
 
 // Few routed rows (block_m 16) and a grid too small for the machine: one
-// 16-row weight tile per workgroup, its NW waves splitting K (wave w takes
-// chunks [w KC / NW, (w + 1) KC / NW)).  Each wave loads a batch of its
-// chunks' weight and activation fragments and scale bytes straight into
-// registers (the activation rows need no staging, as above), one MFMA per
-// chunk, and the waves' partial sums meet in LDS, summed in wave order.
-// Store or weighted epilogue; the W4A16 K-split tile's scheme, on the
-// scaled FP4 MFMA.
-constexpr int kMxKwBatch = 8;                     // chunks in flight per wave
-
-template <int NW>
+// 16-row weight tile per workgroup (four, gate t / up t / gate t+1 / up t+1,
+// for the fused SiLU and quantisation epilogue, which needs one whole
+// 32-column activation block per token), its NW waves splitting K (wave w
+// takes chunks [w KC / NW, (w + 1) KC / NW)).  Each wave loads a batch of
+// its chunks' weight and activation fragments and scale bytes straight into
+// registers (the activation rows need no staging, as above), and the waves'
+// partial sums meet in LDS, summed in wave order.  The W4A16 K-split tile's
+// scheme, on the scaled FP4 MFMA.
+template <int NW, int NT>
 struct MxKwSmem : MxSmem<1> {
-  f32x4_t red[NW][kWave];
+  f32x4_t red[NW][NT][kWave];
 };
 
 template <int NW, int EPI>
 __global__ __launch_bounds__(NW * kWave) void mx_kwave_kernel(const GemmParams p) {
-  __shared__ MxKwSmem<NW> sm;
+  constexpr int NT = EPI == kEpiSiluMx ? 4 : 1;   // weight tiles per workgroup
+  constexpr int KB = 8 / NT;                       // chunks in flight per wave
+  __shared__ MxKwSmem<NW, NT> sm;
   const int mb = blockIdx.x / p.n_tiles;
   const int nt = blockIdx.x - mb * p.n_tiles;
   const int expert = setup_rows<1, NW, kRouteIndexed, EPI>(p, mb, sm);
@@ -516,23 +517,32 @@ __global__ __launch_bounds__(NW * kWave) void mx_kwave_kernel(const GemmParams p
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int KC = p.KC;
   const int c0 = (int)((int64_t)wave * KC / NW), c1 = (int)((int64_t)(wave + 1) * KC / NW);
-  const int64_t tile = (int64_t)expert * p.w_tiles + min(nt, p.NT - 1);
-  const gptr_t wbase = uniform_ptr(p.packed_w + tile * KC * kWave) + lane * 16;
-  const gptr_t sbase = uniform_ptr(reinterpret_cast<const uint8_t*>(p.packed_s) + tile * KC * kWave) + lane;
+  gptr_t wbase[NT], sbase[NT];
+#pragma unroll
+  for (int r = 0; r < NT; ++r) {
+    const int64_t tile = (int64_t)expert * p.w_tiles + min(NT * nt + r, p.NT - 1);
+    wbase[r] = uniform_ptr(p.packed_w + tile * KC * kWave) + lane * 16;
+    sbase[r] = uniform_ptr(reinterpret_cast<const uint8_t*>(p.packed_s) + tile * KC * kWave) + lane;
+  }
   // B operand: lane l supplies token row l % 16, block l / 16 of each chunk
-  const int r = sm.row[lane & 15];
-  const int64_t row = r >= 0 ? r : sm.row[0];     // padding reads a valid row, never stored
+  const int r16 = sm.row[lane & 15];
+  const int64_t row = r16 >= 0 ? r16 : sm.row[0];  // padding reads a valid row, never stored
   const gptr_t abase = uniform_ptr(p.a) + row * (p.K / 2) + 16 * (lane >> 4);
   const gptr_t asbase = uniform_ptr(p.a_scale) + row * (p.K / 32) + (lane >> 4);
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int cb = c0; cb < c1; cb += kMxKwBatch) {
-    u32x4_t w[kMxKwBatch], x[kMxKwBatch];
-    uint32_t ws[kMxKwBatch], xs[kMxKwBatch];
+  f32x4_t acc[NT];
 #pragma unroll
-    for (int i = 0; i < kMxKwBatch; ++i) {
+  for (int r = 0; r < NT; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int cb = c0; cb < c1; cb += KB) {
+    u32x4_t w[KB][NT], x[KB];
+    uint32_t ws[KB][NT], xs[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
       const int c = min(cb + i, c1 - 1);          // past c1: a repeated load, not used
-      w[i] = gload_u32x4(wbase + (int64_t)c * (kWave * 16));
-      ws[i] = gload_u8(sbase + (int64_t)c * kWave);
+#pragma unroll
+      for (int r = 0; r < NT; ++r) {
+        w[i][r] = gload_u32x4(wbase[r] + (int64_t)c * (kWave * 16));
+        ws[i][r] = gload_u8(sbase[r] + (int64_t)c * kWave);
+      }
       x[i] = gload_u32x4(abase + (int64_t)c * 64);
       xs[i] = gload_u8(asbase + (int64_t)c * 4);
     }
@@ -542,19 +552,27 @@ __global__ __launch_bounds__(NW * kWave) void mx_kwave_kernel(const GemmParams p
     // past c1 the activation operand is zero (FP4 has no Inf or NaN, so the
     // products are exact zeros)
 #pragma unroll
-    for (int i = 0; i < kMxKwBatch; ++i) {
+    for (int i = 0; i < KB; ++i) {
       const u32x4_t xb = cb + i < c1 ? x[i] : u32x4_t{0u, 0u, 0u, 0u};
-      acc = mx_mfma(w[i], ws[i], xb, xs[i], acc);
+#pragma unroll
+      for (int r = 0; r < NT; ++r) acc[r] = mx_mfma(w[i][r], ws[i][r], xb, xs[i], acc[r]);
     }
   }
-  sm.red[wave][lane] = acc;
+#pragma unroll
+  for (int r = 0; r < NT; ++r) sm.red[wave][r][lane] = acc[r];
   __syncthreads();
   if (wave != 0) return;
-  f32x4_t tot[1][1];
-  tot[0][0] = sm.red[0][lane];
+  f32x4_t tot[NT][1];
 #pragma unroll
-  for (int v = 1; v < NW; ++v) tot[0][0] += sm.red[v][lane];
-  epilogue<1, 1, 1, EPI>(p, sm, nt, 1u, tot);
+  for (int r = 0; r < NT; ++r) {
+    tot[r][0] = sm.red[0][r][lane];
+#pragma unroll
+    for (int v = 1; v < NW; ++v) tot[r][0] += sm.red[v][r][lane];
+  }
+  if constexpr (EPI == kEpiSiluMx)
+    mx_silu_epilogue<1, NT, 1>(p, sm, nt, 1u, tot);
+  else
+    epilogue<1, NT, 1, EPI>(p, sm, nt, 1u, tot);
 }
 
 typedef void (*MxKernel)(const GemmParams);
@@ -576,6 +594,7 @@ static MxKernel find_mx_kernel(int epi, int m_tiles, int nr, int waves, int stag
     if (m_tiles != 1 || waves != kKwWaves) return nullptr;
     if (epi == kEpiStore) return mx_kwave_kernel<kKwWaves, kEpiStore>;
     if (epi == kEpiWeighted) return mx_kwave_kernel<kKwWaves, kEpiWeighted>;
+    if (epi == kEpiSiluMx) return mx_kwave_kernel<kKwWaves, kEpiSiluMx>;
     return nullptr;
   }
 #define W4A16_MX_CASE(MT_, NR_, NW_, D_) \
