@@ -447,7 +447,8 @@ def test_mxfp4_gate_up_silu_errors(L):
                                                      ctypes.byref(cfg), None)
     assert call(plain, W.mxfp4_config(32, 4)) == -3                      # not a gate/up MXFP4 weight
     assert call(W.weight_desc(8, 128, 256, gate_up=True), W.mxfp4_config(32, 4)) == -3   # INT4 weight
-    assert call(gated, W.mxfp4_config(32, 2)) == -4                      # nr must be 4
+    assert call(gated, W.mxfp4_config(32, 2)) == -4                      # nr must be 4 or 1
+    assert call(gated, W.mxfp4_config(32, 1)) == -4                      # nr 1 only on block_m 16
     assert call(gated, W.mxfp4_config(64, 4)) == -3                      # block_m does not divide the routing's
     # the INT4 calls reject the combined flags too
     assert L.w4a16_pack_w4(P, P, ctypes.byref(gated), P, P, None) == -3
